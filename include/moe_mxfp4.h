@@ -1,0 +1,218 @@
+/*
+ * moe_mxfp4.h -- C ABI of the MXFP4 routed-expert mixture-of-experts layer
+ * for AMD MI355X (gfx950).
+ *
+ * The layer (InferenceX "MI355X Qwen3.5 SGLang v0.5.12" post, section on the
+ * specific optimisations; VibeSys "Qwen3.5-397B on 4x MI300A" post, sections
+ * "Goal" and "Baseline"; MiniMax M3 on MI355X post, sections "Local shape
+ * and tiling" and "Shared expert fusion"):
+ *
+ *   1. softmax top-K routing over E experts, the shared expert folded in as
+ *      expert E in slot K                              moe_route_topk
+ *   2. permute: group the (token, slot) assignments by expert   moe_align_sort
+ *   3. (W4A4 only) MXFP4-quantise the activations      moe_mxfp4_quantize
+ *   4. grouped gate/up GEMM on MXFP4 weights + SwiGLU  moe_expert_gate_up
+ *   5. grouped down GEMM                               moe_expert_down
+ *   6. weighted combine back into token order          moe_combine
+ *   all six in one call                                moe_mxfp4_forward
+ *
+ * Conventions for every entry point:
+ *   - Data pointers are DEVICE pointers (HBM of the current HIP device),
+ *     owned by the caller; the library reads/writes them only during the
+ *     enqueued work and keeps no reference.  Scalars are passed by value.
+ *   - `stream` is a hipStream_t (NULL = the default stream).  Every call
+ *     only enqueues work on it and returns; it never synchronises, never
+ *     allocates device memory and never reads device memory on the host, so
+ *     a call can be captured in a HIP graph.  Faults inside kernels surface
+ *     at the caller's next synchronisation.
+ *   - All argument checks happen before anything is enqueued; on an error
+ *     nothing is enqueued and no output is touched.  T = 0 is valid and
+ *     enqueues nothing (moe_align_sort still writes its zero tables).
+ *   - Vector-loaded buffers (activations, packed weights, y, quantiser
+ *     input and output) must be 16-byte aligned.
+ *   - Shapes: H and I multiples of 128; E <= 1024; K + shared <= 32.
+ *
+ * MXFP4 (OCP Microscaling v1.0): per 32 consecutive elements along the
+ * reduction axis one E8M0 scale byte b (value 2^(b-127)) and 32 E2M1 codes
+ * (s|ee|m, values +-{0, .5, 1, 1.5, 2, 3, 4, 6}), two codes per byte with
+ * element 2j in the low nibble.  Scale bytes 1..254 are supported; 0 only
+ * for all-zero blocks; 255 (NaN) is outside the contract.
+ *
+ * Weight layout (expert e in [0, E'), E' = E + shared; the shared expert is
+ * expert E):
+ *   w13       uint8 [E', 2I, H/2]  rows [0, I) gate, rows [I, 2I) up
+ *   w13_scale uint8 [E', 2I, H/32]
+ *   w2        uint8 [E', H, I/2]
+ *   w2_scale  uint8 [E', H, I/32]
+ */
+#ifndef MOE_MXFP4_H
+#define MOE_MXFP4_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#if defined(__GNUC__)
+#define MOE_API __attribute__((visibility("default")))
+#else
+#define MOE_API
+#endif
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_ERR_INVALID_ARGUMENT = 1,   /* null pointer, negative size, bad flag, misaligned buffer */
+  MOE_ERR_UNSUPPORTED = 2,        /* a shape outside the compiled kernels' range */
+  MOE_ERR_WORKSPACE_TOO_SMALL = 3,
+  MOE_ERR_DEVICE = 4              /* a HIP launch error (hipGetLastError) */
+} moe_status;
+
+typedef enum { MOE_ACT_BF16 = 0 /* W4A16 */, MOE_ACT_MXFP4 = 1 /* W4A4 */ } moe_act_fmt;
+typedef enum { MOE_SRC_F32 = 0, MOE_SRC_BF16 = 1 } moe_src_dtype;
+
+/* Rows per tile of the grouped GEMMs (the 32-row tiles of the VibeSys post,
+ * section "Prefill, cache and speculation"). */
+#define MOE_TILE_M 32
+
+/* Human-readable name of a status code (static string). */
+MOE_API const char *moe_status_string(moe_status s);
+
+/*
+ * Softmax top-K routing (InferenceX Qwen3.5 post, fused_topk bullet:
+ * softmax-scored top-K selection, E = 512, K = 10; shared-expert bullet: the
+ * shared expert as expert top-K+1 of one dispatch).
+ *   logits        fp32 [T, E] row-major, router logits
+ *   gate_logits   fp32 [T] shared-expert gate logits; required iff shared = 1
+ *   topk_ids      out int32 [T, K'] (K' = K + shared)
+ *   topk_weights  out fp32  [T, K']
+ * Slots 0..K-1: the K experts with the largest logits, ordered by (logit
+ * descending, index ascending), -0.0 equal to +0.0.  Weight of slot k:
+ * exp(l_k - l_max) / sum exp(l - l_max), the sum over the K selected when
+ * renormalize = 1, over all E when 0.  Slot K when shared = 1: expert E with
+ * weight 1 / (1 + exp(-g_t)).  NaN or infinite logits are outside the contract.
+ * Errors: INVALID_ARGUMENT (null pointers, T < 0, K < 1, K > E, flags not 0/1),
+ * UNSUPPORTED (E > 1024, K' > 32).
+ */
+MOE_API moe_status moe_route_topk(const float *logits, const float *gate_logits, int32_t T, int32_t E,
+                          int32_t K, int32_t shared, int32_t renormalize, int32_t *topk_ids,
+                          float *topk_weights, void *stream);
+
+/* Scratch bytes moe_align_sort needs for A = T * Kp assignments over Ep experts. */
+MOE_API size_t moe_align_workspace_size(int32_t T, int32_t Kp, int32_t Ep);
+
+/*
+ * Group the flat assignments a = t*Kp + k by expert id (the "one MoE
+ * dispatch" of the InferenceX post's shared-expert bullet; 32-row tiles of
+ * the VibeSys post).  A histogram / prefix-scan permute; the result is
+ * unique: stable, ascending a inside each expert's group.
+ *   topk_ids       int32 [T, Kp], every id in [0, Ep) (other ids are skipped)
+ *   expert_counts  out int32 [Ep]      rows per expert
+ *   expert_offsets out int32 [Ep + 1]  exclusive scan of counts, last = T*Kp
+ *   sorted_assign  out int32 [T*Kp]    flat ids grouped by expert
+ *   inv_assign     out int32 [T*Kp] or NULL: position of flat id a in sorted_assign
+ *   tile_table     out int32 [ceil(T*Kp/tile_m) + Ep][2] or NULL: (expert,
+ *                  first row) of each tile_m-row tile, expert-major, rows ascending
+ *   num_tiles      out int32 [1]
+ *   workspace      device scratch of moe_align_workspace_size bytes
+ * Errors: INVALID_ARGUMENT (null required pointer, T < 0, Kp < 1, Ep < 1,
+ * tile_m < 1), UNSUPPORTED (Ep > 2048), WORKSPACE_TOO_SMALL.
+ */
+MOE_API moe_status moe_align_sort(const int32_t *topk_ids, int32_t T, int32_t Kp, int32_t Ep,
+                          int32_t tile_m, int32_t *expert_counts, int32_t *expert_offsets,
+                          int32_t *sorted_assign, int32_t *inv_assign, int32_t *tile_table,
+                          int32_t *num_tiles, void *workspace, size_t workspace_bytes,
+                          void *stream);
+
+/*
+ * MXFP4-quantise rows x cols values (OpenRelay "Gemma 4 31B on MI355X" post,
+ * sections "Optimisation 3" and "Optimisation 4": activation quantisation to
+ * MXFP4 in its own fused kernel).  Per 32-block: X = floor(log2 amax) - 2,
+ * clamped to [-127, 127] (-127 for an all-zero block); scale byte X + 127;
+ * each v / 2^X rounded to the nearest E2M1 value, ties to the even code,
+ * saturating at 6, sign kept.  Used for W4A4 activations and to pack
+ * float weights.
+ *   src        fp32 or bf16 [rows, cols] (src_dtype), 16-byte aligned
+ *   packed     out uint8 [rows, cols/2], 16-byte aligned
+ *   scales     out uint8 [rows, cols/32]
+ * Errors: INVALID_ARGUMENT (null pointers, rows < 0, cols < 0, bad dtype,
+ * misaligned), UNSUPPORTED (cols not a multiple of 32).
+ */
+MOE_API moe_status moe_mxfp4_quantize(const void *src, int32_t src_dtype, int64_t rows, int64_t cols,
+                              uint8_t *packed, uint8_t *scales, void *stream);
+
+/*
+ * Grouped gate/up GEMM with SwiGLU (VibeSys post, section "Baseline": the
+ * fused HIP MoE kernel dequantises MXFP4 weights in registers).
+ * For every sorted row r of expert e (token t = sorted_assign[r] / Kp):
+ *   acc[n] = sum_h a[t, h] * W13[e, n, h]   (fp32 accumulation), n < 2I
+ *   h[r, i] = bf16( silu(acc[i]) * acc[I + i] )
+ *   act_fmt = MOE_ACT_BF16:  act = x bf16 [T, H], act_scale = NULL
+ *   act_fmt = MOE_ACT_MXFP4: act = packed uint8 [T, H/2], act_scale uint8 [T, H/32]
+ *   sorted_assign, expert_offsets, tile_table, num_tiles: moe_align_sort's
+ *     outputs with tile_m = MOE_TILE_M; max_tiles = ceil(T*Kp/32) + Ep
+ *   h          out bf16 [T*Kp, I], sorted row order
+ * Errors: INVALID_ARGUMENT, UNSUPPORTED (H or I not a multiple of 128).
+ */
+MOE_API moe_status moe_expert_gate_up(const void *act, const uint8_t *act_scale, int32_t act_fmt,
+                              const int32_t *sorted_assign, const int32_t *expert_offsets,
+                              const int32_t *tile_table, const int32_t *num_tiles,
+                              const uint8_t *w13, const uint8_t *w13_scale, int32_t T, int32_t H,
+                              int32_t I, int32_t Ep, int32_t Kp, uint16_t *h, void *stream);
+
+/*
+ * Grouped down GEMM: y[r, j] = sum_i h[r, i] * W2[e, j, i] (fp32 accumulation).
+ *   act_fmt = MOE_ACT_BF16:  h bf16 [A, I], h_scale = NULL
+ *   act_fmt = MOE_ACT_MXFP4: h packed uint8 [A, I/2], h_scale uint8 [A, I/32]
+ *   y          out fp32 [A, H], sorted row order (A = T*Kp)
+ * Errors: INVALID_ARGUMENT, UNSUPPORTED (H or I not a multiple of 128).
+ */
+MOE_API moe_status moe_expert_down(const void *h, const uint8_t *h_scale, int32_t act_fmt,
+                           const int32_t *expert_offsets, const int32_t *tile_table,
+                           const int32_t *num_tiles, const uint8_t *w2, const uint8_t *w2_scale,
+                           int32_t T, int32_t H, int32_t I, int32_t Ep, int32_t Kp, float *y,
+                           void *stream);
+
+/*
+ * Weighted combine back into token order (the shared expert is slot K, so
+ * no separate dense MLP is added: MiniMax M3 post, section "Shared expert
+ * fusion"):  out[t, j] = bf16( sum_{k < Kp} w[t, k] * y[inv[t*Kp + k], j] ),
+ * slots summed in order in fp32.
+ *   y fp32 [T*Kp, H]; topk_weights fp32 [T, Kp]; inv_assign int32 [T*Kp];
+ *   out bf16 [T, H]
+ * Errors: INVALID_ARGUMENT, UNSUPPORTED (H not a multiple of 128).
+ */
+MOE_API moe_status moe_combine(const float *y, const float *topk_weights, const int32_t *inv_assign,
+                       int32_t T, int32_t H, int32_t Kp, uint16_t *out, void *stream);
+
+/* Workspace bytes moe_mxfp4_forward needs (0 for T = 0). */
+MOE_API size_t moe_mxfp4_workspace_size(int32_t T, int32_t H, int32_t I, int32_t E, int32_t K,
+                                int32_t shared, int32_t act_fmt);
+
+/*
+ * The whole layer in one call: route, align, [quantise x], gate/up + SwiGLU,
+ * [quantise h], down, combine, all enqueued on `stream`.
+ *   x              bf16 [T, H]
+ *   router_logits  fp32 [T, E];  shared_gate_logits fp32 [T] (shared = 1) or NULL
+ *   w13, w13_scale, w2, w2_scale: the MXFP4 weights of E + shared experts
+ *   act_fmt        MOE_ACT_BF16 (W4A16) or MOE_ACT_MXFP4 (W4A4: x and h are
+ *                  MXFP4-quantised before their GEMM)
+ *   out            out bf16 [T, H]
+ *   topk_ids_out, topk_weights_out: optional copies of the routing [T, K']
+ *   workspace      caller-owned device scratch of moe_mxfp4_workspace_size bytes
+ * Errors: any of the stage errors, WORKSPACE_TOO_SMALL.
+ */
+MOE_API moe_status moe_mxfp4_forward(const uint16_t *x, const float *router_logits,
+                             const float *shared_gate_logits, const uint8_t *w13,
+                             const uint8_t *w13_scale, const uint8_t *w2, const uint8_t *w2_scale,
+                             int32_t T, int32_t H, int32_t I, int32_t E, int32_t K, int32_t shared,
+                             int32_t act_fmt, uint16_t *out, int32_t *topk_ids_out,
+                             float *topk_weights_out, void *workspace, size_t workspace_bytes,
+                             void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_MXFP4_H */

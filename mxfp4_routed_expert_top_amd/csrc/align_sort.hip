@@ -1,0 +1,162 @@
+// Group the flat assignments a = t*K' + k by expert: a histogram / prefix-scan
+// permute that is stable (ascending a inside each expert's group) with no
+// atomic deciding any order, plus the table of tile_m-row tiles that drive
+// the grouped GEMMs (VibeSys "Qwen3.5-397B on 4x MI300A" post, section
+// "Prefill, cache and speculation": 32-row tiles in the MoE kernel; the
+// InferenceX Qwen3.5 post's shared-expert bullet: one MoE dispatch covers
+// the routed experts and the shared one).
+//
+// Three launches over chunks of kChunk assignments:
+//   1. per-chunk histograms            hist[b][e]
+//   2. one block: column scans over chunks, the exclusive scan over experts
+//      (offsets), per-chunk base positions and the tile table
+//   3. per-chunk stable scatter: inside a chunk, wave by wave in order, each
+//      lane's rank among the earlier lanes with the same expert
+#include "common.h"
+#include "kernels.h"
+
+namespace {
+
+constexpr int kChunk = 2048;      // assignments per block in passes 1 and 3
+constexpr int kScanThreads = 1024;
+
+__global__ __launch_bounds__(256) void align_hist_kernel(const int32_t* __restrict__ ids, int A,
+                                                         int Ep, int32_t* __restrict__ hist) {
+  extern __shared__ int32_t sh[];
+  for (int e = threadIdx.x; e < Ep; e += blockDim.x) sh[e] = 0;
+  __syncthreads();
+  const int a0 = blockIdx.x * kChunk;
+  const int a1 = min(A, a0 + kChunk);
+  for (int a = a0 + threadIdx.x; a < a1; a += blockDim.x) {
+    const int e = ids[a];
+    if ((unsigned)e < (unsigned)Ep) atomicAdd(&sh[e], 1);   // ids outside [0, Ep) are skipped
+  }
+  __syncthreads();
+  for (int e = threadIdx.x; e < Ep; e += blockDim.x) hist[(size_t)blockIdx.x * Ep + e] = sh[e];
+}
+
+// Exclusive scan of one value per thread over a 1024-thread block.
+__device__ int block_exclusive_scan(int v, int* tmp /* >= 16 ints */, int* total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int x = v;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    int y = __shfl_up(x, d, MOE_WAVE);
+    if (lane >= d) x += y;
+  }
+  if (lane == 63) tmp[wave] = x;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    int run = 0;
+    for (int w = 0; w < (int)(blockDim.x >> 6); ++w) {
+      int c = tmp[w];
+      tmp[w] = run;
+      run += c;
+    }
+    tmp[16] = run;
+  }
+  __syncthreads();
+  int r = x - v + tmp[wave];
+  *total = tmp[16];
+  __syncthreads();
+  return r;
+}
+
+__global__ __launch_bounds__(kScanThreads) void align_scan_kernel(
+    int32_t* __restrict__ hist, int nb, int A, int Ep, int tile_m, int32_t* __restrict__ counts,
+    int32_t* __restrict__ offsets, int32_t* __restrict__ tiles, int32_t* __restrict__ num_tiles) {
+  __shared__ int tmp[17];
+  // Each thread owns experts e = 2*tid and 2*tid + 1 (Ep <= 2048).
+  int cnt[2] = {0, 0};
+  for (int q = 0; q < 2; ++q) {
+    int e = 2 * threadIdx.x + q;
+    if (e < Ep) {
+      int run = 0;
+      for (int b = 0; b < nb; ++b) {
+        int32_t* p = hist + (size_t)b * Ep + e;
+        int c = *p;
+        *p = run;          // exclusive prefix over chunks
+        run += c;
+      }
+      cnt[q] = run;
+    }
+  }
+  int total;
+  int base = block_exclusive_scan(cnt[0] + cnt[1], tmp, &total);
+  int off[2] = {base, base + cnt[0]};
+  int nt[2] = {(cnt[0] + tile_m - 1) / tile_m, (cnt[1] + tile_m - 1) / tile_m};
+  int ttotal;
+  int tbase = block_exclusive_scan(nt[0] + nt[1], tmp, &ttotal);
+  int toff[2] = {tbase, tbase + nt[0]};
+  for (int q = 0; q < 2; ++q) {
+    int e = 2 * threadIdx.x + q;
+    if (e < Ep) {
+      counts[e] = cnt[q];
+      offsets[e] = off[q];
+      for (int b = 0; b < nb; ++b) hist[(size_t)b * Ep + e] += off[q];
+      if (tiles)
+        for (int j = 0; j < nt[q]; ++j) {
+          tiles[2 * (toff[q] + j)] = e;
+          tiles[2 * (toff[q] + j) + 1] = off[q] + j * tile_m;
+        }
+    }
+  }
+  if (threadIdx.x == 0) {
+    offsets[Ep] = A;
+    *num_tiles = ttotal;
+  }
+}
+
+__global__ __launch_bounds__(256) void align_scatter_kernel(
+    const int32_t* __restrict__ ids, int A, int Ep, const int32_t* __restrict__ base,
+    int32_t* __restrict__ sorted, int32_t* __restrict__ inv) {
+  extern __shared__ int32_t pos[];
+  for (int e = threadIdx.x; e < Ep; e += blockDim.x) pos[e] = base[(size_t)blockIdx.x * Ep + e];
+  __syncthreads();
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int a0 = blockIdx.x * kChunk;
+  for (int r = 0; r < kChunk; r += 256) {
+    const int a = a0 + r + threadIdx.x;
+    int e = (a < A) ? ids[a] : -1;
+    if ((unsigned)e >= (unsigned)Ep) e = -1;
+    int rank = 0, same = 0;
+    for (int j = 0; j < 64; ++j) {
+      int ej = __shfl(e, j, MOE_WAVE);
+      if (ej == e) {
+        same++;
+        if (j < lane) rank++;
+      }
+    }
+    for (int w = 0; w < 4; ++w) {
+      if (w == wave && e >= 0) {
+        int p = pos[e] + rank;
+        sorted[p] = a;
+        if (inv) inv[a] = p;
+        if (rank == same - 1) pos[e] = p + 1;    // the last lane of this expert advances it
+      }
+      __syncthreads();
+    }
+  }
+}
+
+}  // namespace
+
+size_t align_scratch_bytes(int A, int Ep) {
+  int nb = (A + kChunk - 1) / kChunk;
+  return (size_t)(nb > 0 ? nb : 1) * Ep * sizeof(int32_t);
+}
+
+hipError_t launch_align_sort(const int32_t* ids, int A, int Ep, int tile_m, int32_t* counts,
+                             int32_t* offsets, int32_t* sorted, int32_t* inv, int32_t* tiles,
+                             int32_t* num_tiles, int32_t* scratch, hipStream_t stream) {
+  const int nb = (A + kChunk - 1) / kChunk;
+  const size_t lds = (size_t)Ep * sizeof(int32_t);
+  if (nb > 0)
+    hipLaunchKernelGGL(align_hist_kernel, dim3(nb), dim3(256), lds, stream, ids, A, Ep, scratch);
+  hipLaunchKernelGGL(align_scan_kernel, dim3(1), dim3(kScanThreads), 0, stream, scratch, nb, A, Ep,
+                     tile_m, counts, offsets, tiles, num_tiles);
+  if (nb > 0)
+    hipLaunchKernelGGL(align_scatter_kernel, dim3(nb), dim3(256), lds, stream, ids, A, Ep, scratch,
+                       sorted, inv);
+  return hipGetLastError();
+}

@@ -1,0 +1,67 @@
+// Device helpers shared by the HIP kernels of the MXFP4 MoE layer (gfx950).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float floatx4_t __attribute__((ext_vector_type(4)));
+typedef int int32x8_t __attribute__((ext_vector_type(8)));
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+
+#define MOE_WAVE 64
+
+// float32 -> bf16 bits, round to nearest even (finite inputs).
+__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) {
+  return __uint_as_float(((uint32_t)b) << 16);
+}
+
+// E8M0 scale byte -> float 2^(b-127).  Bytes 1..254 are exact normals; byte 0
+// gives 2^-127 (a float32 subnormal); byte 255 (NaN) is outside the contract.
+__device__ __forceinline__ float e8m0_to_f32(uint32_t b) {
+  return b ? __uint_as_float(b << 23) : __uint_as_float(0x00400000u);
+}
+
+// SiLU(g) * u in fp32.
+__device__ __forceinline__ float swiglu(float g, float u) {
+  return g / (1.0f + __expf(-g)) * u;
+}
+
+// Eight E2M1 codes (one dword, element 2j in the low nibble of byte j) times
+// a power-of-two scale -> eight bf16 values, exact.  Uses the gfx950 scaled
+// FP4 -> BF16 converter; op_sel picks the byte.
+__device__ __forceinline__ bf16x8_t dequant8_bf16(uint32_t q, float scale) {
+  bf16x2_t p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(q, scale, 0);
+  bf16x2_t p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(q, scale, 1);
+  bf16x2_t p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(q, scale, 2);
+  bf16x2_t p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(q, scale, 3);
+  bf16x8_t r = {p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
+  return r;
+}
+
+__device__ __forceinline__ floatx4_t mfma_bf16_16x16x32(bf16x8_t a, bf16x8_t b, floatx4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// Scaled MFMA, both operands FP4 (E2M1): lane l supplies row (l % 16), K-block
+// (l / 16) as 32 codes in four dwords plus that block's E8M0 byte.
+__device__ __forceinline__ floatx4_t mfma_fp4_16x16x128(u32x4_t a, uint32_t sa, u32x4_t b,
+                                                        uint32_t sb, floatx4_t c) {
+  int32x8_t av = {(int)a[0], (int)a[1], (int)a[2], (int)a[3], 0, 0, 0, 0};
+  int32x8_t bv = {(int)b[0], (int)b[1], (int)b[2], (int)b[3], 0, 0, 0, 0};
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, bv, c, 4, 4, 0, (int)sa, 0, (int)sb);
+}
+
+__device__ __forceinline__ u32x4_t load16(const void* p) {
+  return *reinterpret_cast<const u32x4_t*>(p);
+}
+
+__device__ __forceinline__ bf16x8_t load_bf16x8(const void* p) {
+  return *reinterpret_cast<const bf16x8_t*>(p);
+}

@@ -1,0 +1,30 @@
+// Host-side launchers of the HIP kernels (internal to the library).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+hipError_t launch_route_topk(const float* logits, const float* gate, int T, int E, int K,
+                             int shared, int renormalize, int32_t* ids, float* weights,
+                             hipStream_t stream);
+
+size_t align_scratch_bytes(int A, int Ep);
+hipError_t launch_align_sort(const int32_t* ids, int A, int Ep, int tile_m, int32_t* counts,
+                             int32_t* offsets, int32_t* sorted, int32_t* inv, int32_t* tiles,
+                             int32_t* num_tiles, int32_t* scratch, hipStream_t stream);
+
+hipError_t launch_mxfp4_quant(const void* src, int src_is_bf16, int64_t rows, int64_t cols,
+                              uint8_t* packed, uint8_t* scales, hipStream_t stream);
+
+int expert_gemm_tile_m();
+hipError_t launch_gate_up(int act_fmt, const void* act, const uint8_t* act_scale,
+                          const int32_t* sorted, const int32_t* offsets, const int32_t* tiles,
+                          const int32_t* num_tiles, int max_tiles, const uint8_t* w13,
+                          const uint8_t* w13s, int T, int H, int I, int Kp, uint16_t* h,
+                          hipStream_t stream);
+hipError_t launch_down(int act_fmt, const void* h, const uint8_t* h_scale, const int32_t* offsets,
+                       const int32_t* tiles, const int32_t* num_tiles, int max_tiles,
+                       const uint8_t* w2, const uint8_t* w2s, int H, int I, float* y,
+                       hipStream_t stream);
+hipError_t launch_combine(const float* y, const float* w, const int32_t* inv, int T, int H, int Kp,
+                          uint16_t* out, hipStream_t stream);

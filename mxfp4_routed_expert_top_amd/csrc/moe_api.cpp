@@ -1,0 +1,264 @@
+// C ABI of the MXFP4 routed-expert MoE layer: argument checks, workspace
+// carving and the launch sequence.  Every check runs before the first
+// enqueue; nothing here allocates, synchronises or reads device memory.
+#include "../../include/moe_mxfp4.h"
+
+#include <hip/hip_runtime.h>
+
+#include "kernels.h"
+
+namespace {
+
+constexpr int kMaxE = 1024;
+constexpr int kMaxKp = 32;
+constexpr size_t kAlign = 256;
+
+inline size_t round_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+inline bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+inline hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
+inline moe_status from_hip(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_DEVICE; }
+
+inline int64_t max_tiles_for(int64_t A, int64_t Ep) {
+  return (A + MOE_TILE_M - 1) / MOE_TILE_M + Ep;
+}
+
+moe_status check_shape_HI(int32_t H, int32_t I) {
+  if (H <= 0 || I <= 0) return MOE_ERR_INVALID_ARGUMENT;
+  if (H % 128 || I % 128) return MOE_ERR_UNSUPPORTED;
+  return MOE_OK;
+}
+
+// Forward workspace layout, in this order, each piece 256-byte aligned.
+struct FwdLayout {
+  size_t ids, w, counts, offsets, sorted, inv, tiles, ntiles, scratch, xq, xs, h, hq, hs, y, total;
+};
+
+FwdLayout forward_layout(int64_t T, int64_t H, int64_t I, int64_t E, int64_t K, int64_t shared,
+                         int32_t act_fmt) {
+  const int64_t Kp = K + shared, Ep = E + shared, A = T * Kp;
+  FwdLayout L{};
+  size_t p = 0;
+  auto take = [&](size_t bytes) {
+    size_t at = p;
+    p += round_up(bytes);
+    return at;
+  };
+  L.ids = take(A * 4);
+  L.w = take(A * 4);
+  L.counts = take(Ep * 4);
+  L.offsets = take((Ep + 1) * 4);
+  L.sorted = take(A * 4);
+  L.inv = take(A * 4);
+  L.tiles = take(max_tiles_for(A, Ep) * 2 * 4);
+  L.ntiles = take(4);
+  L.scratch = take(align_scratch_bytes((int)A, (int)Ep));
+  const bool q = act_fmt == MOE_ACT_MXFP4;
+  L.xq = take(q ? T * H / 2 : 0);
+  L.xs = take(q ? T * H / 32 : 0);
+  L.h = take(A * I * 2);
+  L.hq = take(q ? A * I / 2 : 0);
+  L.hs = take(q ? A * I / 32 : 0);
+  L.y = take(A * H * 4);
+  L.total = p;
+  return L;
+}
+
+moe_status check_route(const float* logits, const float* gate, int32_t T, int32_t E, int32_t K,
+                       int32_t shared, int32_t renormalize) {
+  if (T < 0 || E < 1 || K < 1 || K > E || (shared != 0 && shared != 1) ||
+      (renormalize != 0 && renormalize != 1))
+    return MOE_ERR_INVALID_ARGUMENT;
+  if (T > 0 && (!logits || (shared && !gate))) return MOE_ERR_INVALID_ARGUMENT;
+  if (E > kMaxE || K + shared > kMaxKp) return MOE_ERR_UNSUPPORTED;
+  return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* moe_status_string(moe_status s) {
+  switch (s) {
+    case MOE_OK: return "MOE_OK";
+    case MOE_ERR_INVALID_ARGUMENT: return "MOE_ERR_INVALID_ARGUMENT";
+    case MOE_ERR_UNSUPPORTED: return "MOE_ERR_UNSUPPORTED";
+    case MOE_ERR_WORKSPACE_TOO_SMALL: return "MOE_ERR_WORKSPACE_TOO_SMALL";
+    case MOE_ERR_DEVICE: return "MOE_ERR_DEVICE";
+  }
+  return "MOE_ERR_UNKNOWN";
+}
+
+moe_status moe_route_topk(const float* logits, const float* gate_logits, int32_t T, int32_t E,
+                          int32_t K, int32_t shared, int32_t renormalize, int32_t* topk_ids,
+                          float* topk_weights, void* stream) {
+  moe_status st = check_route(logits, gate_logits, T, E, K, shared, renormalize);
+  if (st != MOE_OK) return st;
+  if (T > 0 && (!topk_ids || !topk_weights)) return MOE_ERR_INVALID_ARGUMENT;
+  if (T == 0) return MOE_OK;
+  return from_hip(launch_route_topk(logits, gate_logits, T, E, K, shared, renormalize, topk_ids,
+                                    topk_weights, as_stream(stream)));
+}
+
+size_t moe_align_workspace_size(int32_t T, int32_t Kp, int32_t Ep) {
+  if (T < 0 || Kp < 1 || Ep < 1) return 0;
+  return align_scratch_bytes((int)((int64_t)T * Kp), Ep);
+}
+
+moe_status moe_align_sort(const int32_t* topk_ids, int32_t T, int32_t Kp, int32_t Ep,
+                          int32_t tile_m, int32_t* expert_counts, int32_t* expert_offsets,
+                          int32_t* sorted_assign, int32_t* inv_assign, int32_t* tile_table,
+                          int32_t* num_tiles, void* workspace, size_t workspace_bytes,
+                          void* stream) {
+  if (T < 0 || Kp < 1 || Ep < 1 || tile_m < 1) return MOE_ERR_INVALID_ARGUMENT;
+  if (Ep > 2048) return MOE_ERR_UNSUPPORTED;
+  const int64_t A = (int64_t)T * Kp;
+  if (A > INT32_MAX / 2) return MOE_ERR_UNSUPPORTED;
+  if (!expert_counts || !expert_offsets || !num_tiles || (A > 0 && (!topk_ids || !sorted_assign)))
+    return MOE_ERR_INVALID_ARGUMENT;
+  const size_t need = align_scratch_bytes((int)A, Ep);
+  if (workspace_bytes < need) return MOE_ERR_WORKSPACE_TOO_SMALL;
+  if (!workspace) return MOE_ERR_INVALID_ARGUMENT;
+  return from_hip(launch_align_sort(topk_ids, (int)A, Ep, tile_m, expert_counts, expert_offsets,
+                                    sorted_assign, inv_assign, tile_table, num_tiles,
+                                    (int32_t*)workspace, as_stream(stream)));
+}
+
+moe_status moe_mxfp4_quantize(const void* src, int32_t src_dtype, int64_t rows, int64_t cols,
+                              uint8_t* packed, uint8_t* scales, void* stream) {
+  if (rows < 0 || cols < 0 || (src_dtype != MOE_SRC_F32 && src_dtype != MOE_SRC_BF16))
+    return MOE_ERR_INVALID_ARGUMENT;
+  if (cols % 32) return MOE_ERR_UNSUPPORTED;
+  if (rows == 0 || cols == 0) return MOE_OK;
+  if (!src || !packed || !scales || !aligned16(src) || !aligned16(packed))
+    return MOE_ERR_INVALID_ARGUMENT;
+  if (rows * (cols / 32) / 256 >= (int64_t)UINT32_MAX) return MOE_ERR_UNSUPPORTED;
+  return from_hip(launch_mxfp4_quant(src, src_dtype == MOE_SRC_BF16, rows, cols, packed, scales,
+                                     as_stream(stream)));
+}
+
+moe_status moe_expert_gate_up(const void* act, const uint8_t* act_scale, int32_t act_fmt,
+                              const int32_t* sorted_assign, const int32_t* expert_offsets,
+                              const int32_t* tile_table, const int32_t* num_tiles,
+                              const uint8_t* w13, const uint8_t* w13_scale, int32_t T, int32_t H,
+                              int32_t I, int32_t Ep, int32_t Kp, uint16_t* h, void* stream) {
+  if (T < 0 || Ep < 1 || Kp < 1 || (act_fmt != MOE_ACT_BF16 && act_fmt != MOE_ACT_MXFP4))
+    return MOE_ERR_INVALID_ARGUMENT;
+  moe_status st = check_shape_HI(H, I);
+  if (st != MOE_OK) return st;
+  if (Ep > 2048) return MOE_ERR_UNSUPPORTED;
+  if (T == 0) return MOE_OK;
+  if (!act || !sorted_assign || !expert_offsets || !tile_table || !num_tiles || !w13 ||
+      !w13_scale || !h || (act_fmt == MOE_ACT_MXFP4 && !act_scale))
+    return MOE_ERR_INVALID_ARGUMENT;
+  if (!aligned16(act) || !aligned16(w13)) return MOE_ERR_INVALID_ARGUMENT;
+  const int64_t mt = max_tiles_for((int64_t)T * Kp, Ep);
+  if (mt * (I / 64) >= INT32_MAX) return MOE_ERR_UNSUPPORTED;
+  return from_hip(launch_gate_up(act_fmt, act, act_scale, sorted_assign, expert_offsets, tile_table,
+                                 num_tiles, (int)mt, w13, w13_scale, T, H, I, Kp, h,
+                                 as_stream(stream)));
+}
+
+moe_status moe_expert_down(const void* h, const uint8_t* h_scale, int32_t act_fmt,
+                           const int32_t* expert_offsets, const int32_t* tile_table,
+                           const int32_t* num_tiles, const uint8_t* w2, const uint8_t* w2_scale,
+                           int32_t T, int32_t H, int32_t I, int32_t Ep, int32_t Kp, float* y,
+                           void* stream) {
+  if (T < 0 || Ep < 1 || Kp < 1 || (act_fmt != MOE_ACT_BF16 && act_fmt != MOE_ACT_MXFP4))
+    return MOE_ERR_INVALID_ARGUMENT;
+  moe_status st = check_shape_HI(H, I);
+  if (st != MOE_OK) return st;
+  if (Ep > 2048) return MOE_ERR_UNSUPPORTED;
+  if (T == 0) return MOE_OK;
+  if (!h || !expert_offsets || !tile_table || !num_tiles || !w2 || !w2_scale || !y ||
+      (act_fmt == MOE_ACT_MXFP4 && !h_scale))
+    return MOE_ERR_INVALID_ARGUMENT;
+  if (!aligned16(h) || !aligned16(w2)) return MOE_ERR_INVALID_ARGUMENT;
+  const int64_t mt = max_tiles_for((int64_t)T * Kp, Ep);
+  if (mt * (H / 128) >= INT32_MAX) return MOE_ERR_UNSUPPORTED;
+  return from_hip(launch_down(act_fmt, h, h_scale, expert_offsets, tile_table, num_tiles, (int)mt,
+                              w2, w2_scale, H, I, y, as_stream(stream)));
+}
+
+moe_status moe_combine(const float* y, const float* topk_weights, const int32_t* inv_assign,
+                       int32_t T, int32_t H, int32_t Kp, uint16_t* out, void* stream) {
+  if (T < 0 || H <= 0 || Kp < 1) return MOE_ERR_INVALID_ARGUMENT;
+  if (H % 128) return MOE_ERR_UNSUPPORTED;
+  if (T == 0) return MOE_OK;
+  if (!y || !topk_weights || !inv_assign || !out || !aligned16(y) || !aligned16(out))
+    return MOE_ERR_INVALID_ARGUMENT;
+  return from_hip(launch_combine(y, topk_weights, inv_assign, T, H, Kp, out, as_stream(stream)));
+}
+
+size_t moe_mxfp4_workspace_size(int32_t T, int32_t H, int32_t I, int32_t E, int32_t K,
+                                int32_t shared, int32_t act_fmt) {
+  if (T <= 0 || H <= 0 || I <= 0 || E < 1 || K < 1 || shared < 0 || shared > 1) return 0;
+  return forward_layout(T, H, I, E, K, shared, act_fmt).total;
+}
+
+moe_status moe_mxfp4_forward(const uint16_t* x, const float* router_logits,
+                             const float* shared_gate_logits, const uint8_t* w13,
+                             const uint8_t* w13_scale, const uint8_t* w2, const uint8_t* w2_scale,
+                             int32_t T, int32_t H, int32_t I, int32_t E, int32_t K, int32_t shared,
+                             int32_t act_fmt, uint16_t* out, int32_t* topk_ids_out,
+                             float* topk_weights_out, void* workspace, size_t workspace_bytes,
+                             void* stream) {
+  moe_status st = check_route(router_logits, shared_gate_logits, T, E, K, shared, 1);
+  if (st != MOE_OK) return st;
+  if (act_fmt != MOE_ACT_BF16 && act_fmt != MOE_ACT_MXFP4) return MOE_ERR_INVALID_ARGUMENT;
+  st = check_shape_HI(H, I);
+  if (st != MOE_OK) return st;
+  if (T == 0) return MOE_OK;
+  if (!x || !w13 || !w13_scale || !w2 || !w2_scale || !out) return MOE_ERR_INVALID_ARGUMENT;
+  if (!aligned16(x) || !aligned16(w13) || !aligned16(w2) || !aligned16(out))
+    return MOE_ERR_INVALID_ARGUMENT;
+  const int Kp = K + shared, Ep = E + shared;
+  const int64_t A = (int64_t)T * Kp;
+  if (A * (int64_t)H >= ((int64_t)1 << 40) || A > INT32_MAX / 2) return MOE_ERR_UNSUPPORTED;
+  const FwdLayout L = forward_layout(T, H, I, E, K, shared, act_fmt);
+  if (workspace_bytes < L.total) return MOE_ERR_WORKSPACE_TOO_SMALL;
+  if (!workspace) return MOE_ERR_INVALID_ARGUMENT;
+
+  char* ws = (char*)workspace;
+  int32_t* ids = topk_ids_out ? topk_ids_out : (int32_t*)(ws + L.ids);
+  float* wts = topk_weights_out ? topk_weights_out : (float*)(ws + L.w);
+  int32_t* counts = (int32_t*)(ws + L.counts);
+  int32_t* offsets = (int32_t*)(ws + L.offsets);
+  int32_t* sorted = (int32_t*)(ws + L.sorted);
+  int32_t* inv = (int32_t*)(ws + L.inv);
+  int32_t* tiles = (int32_t*)(ws + L.tiles);
+  int32_t* ntiles = (int32_t*)(ws + L.ntiles);
+  int32_t* scratch = (int32_t*)(ws + L.scratch);
+  uint8_t* xq = (uint8_t*)(ws + L.xq);
+  uint8_t* xs = (uint8_t*)(ws + L.xs);
+  uint16_t* h = (uint16_t*)(ws + L.h);
+  uint8_t* hq = (uint8_t*)(ws + L.hq);
+  uint8_t* hs = (uint8_t*)(ws + L.hs);
+  float* y = (float*)(ws + L.y);
+  hipStream_t s = as_stream(stream);
+  const int mt = (int)max_tiles_for(A, Ep);
+
+  hipError_t e = launch_route_topk(router_logits, shared_gate_logits, T, E, K, shared, 1, ids, wts, s);
+  if (e != hipSuccess) return MOE_ERR_DEVICE;
+  e = launch_align_sort(ids, (int)A, Ep, MOE_TILE_M, counts, offsets, sorted, inv, tiles, ntiles,
+                        scratch, s);
+  if (e != hipSuccess) return MOE_ERR_DEVICE;
+  if (act_fmt == MOE_ACT_BF16) {
+    e = launch_gate_up(0, x, nullptr, sorted, offsets, tiles, ntiles, mt, w13, w13_scale, T, H, I,
+                       Kp, h, s);
+    if (e != hipSuccess) return MOE_ERR_DEVICE;
+    e = launch_down(0, h, nullptr, offsets, tiles, ntiles, mt, w2, w2_scale, H, I, y, s);
+  } else {
+    e = launch_mxfp4_quant(x, 1, T, H, xq, xs, s);
+    if (e != hipSuccess) return MOE_ERR_DEVICE;
+    e = launch_gate_up(1, xq, xs, sorted, offsets, tiles, ntiles, mt, w13, w13_scale, T, H, I, Kp,
+                       h, s);
+    if (e != hipSuccess) return MOE_ERR_DEVICE;
+    e = launch_mxfp4_quant(h, 1, A, I, hq, hs, s);
+    if (e != hipSuccess) return MOE_ERR_DEVICE;
+    e = launch_down(1, hq, hs, offsets, tiles, ntiles, mt, w2, w2_scale, H, I, y, s);
+  }
+  if (e != hipSuccess) return MOE_ERR_DEVICE;
+  return from_hip(launch_combine(y, wts, inv, T, H, Kp, out, s));
+}
+
+}  // extern "C"

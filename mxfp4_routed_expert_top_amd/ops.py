@@ -1,0 +1,290 @@
+"""Python binding of libmoe_mxfp4.so (ctypes): argument marshalling only.
+
+Every function has the name of the C entry point it calls (without the
+``moe_`` prefix), takes torch tensors that live on the GPU, passes their
+device pointers and the current HIP stream, and raises ``MoeError`` on a
+non-OK status.  Nothing here computes any step of the layer; there is no
+CPU fallback: if the library is missing, loading it raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libmoe_mxfp4.so")
+
+MOE_OK, MOE_ERR_INVALID_ARGUMENT, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE_TOO_SMALL, MOE_ERR_DEVICE = range(5)
+ACT_BF16, ACT_MXFP4 = 0, 1
+SRC_F32, SRC_BF16 = 0, 1
+TILE_M = 32
+
+_lib = None
+
+_P = ctypes.c_void_p
+_I32 = ctypes.c_int32
+_I64 = ctypes.c_int64
+_SZ = ctypes.c_size_t
+
+_SIGS = {
+    "moe_status_string": (ctypes.c_char_p, [_I32]),
+    "moe_route_topk": (_I32, [_P, _P, _I32, _I32, _I32, _I32, _I32, _P, _P, _P]),
+    "moe_align_workspace_size": (_SZ, [_I32, _I32, _I32]),
+    "moe_align_sort": (_I32, [_P, _I32, _I32, _I32, _I32, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
+    "moe_mxfp4_quantize": (_I32, [_P, _I32, _I64, _I64, _P, _P, _P]),
+    "moe_expert_gate_up": (_I32, [_P, _P, _I32, _P, _P, _P, _P, _P, _P, _I32, _I32, _I32, _I32,
+                                  _I32, _P, _P]),
+    "moe_expert_down": (_I32, [_P, _P, _I32, _P, _P, _P, _P, _P, _I32, _I32, _I32, _I32, _I32,
+                               _P, _P]),
+    "moe_combine": (_I32, [_P, _P, _P, _I32, _I32, _I32, _P, _P]),
+    "moe_mxfp4_workspace_size": (_SZ, [_I32, _I32, _I32, _I32, _I32, _I32, _I32]),
+    "moe_mxfp4_forward": (_I32, [_P, _P, _P, _P, _P, _P, _P, _I32, _I32, _I32, _I32, _I32, _I32,
+                                 _I32, _P, _P, _P, _P, _SZ, _P]),
+}
+EXPORTS = tuple(_SIGS)
+
+
+class MoeError(RuntimeError):
+    def __init__(self, fn, status):
+        self.status = status
+        super().__init__(f"{fn} returned {status_string(status)} ({status})")
+
+
+def lib() -> ctypes.CDLL:
+    """Load libmoe_mxfp4.so once (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "`python -m mxfp4_routed_expert_top_amd.build`")
+        l = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGS.items():
+            f = getattr(l, name)
+            f.restype, f.argtypes = res, args
+        _lib = l
+    return _lib
+
+
+def status_string(status: int) -> str:
+    return lib().moe_status_string(int(status)).decode()
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("expected a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError("expected a contiguous tensor")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream=None):
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _check(fn, status):
+    if status != MOE_OK:
+        raise MoeError(fn, status)
+
+
+def _dt(t, dtype, name):
+    if t is not None and t.dtype != dtype:
+        raise TypeError(f"{name}: expected {dtype}, got {t.dtype}")
+
+
+# ------------------------------------------------------------------ stages --
+
+def route_topk(logits, gate_logits, K: int, shared: int, renormalize: int = 1,
+               topk_ids=None, topk_weights=None, stream=None):
+    """moe_route_topk: logits fp32 [T, E], gate fp32 [T] -> (ids int32 [T, K'], w fp32 [T, K'])."""
+    _dt(logits, torch.float32, "logits")
+    _dt(gate_logits, torch.float32, "gate_logits")
+    T, E = logits.shape
+    Kp = K + shared
+    if topk_ids is None:
+        topk_ids = torch.empty(T, Kp, dtype=torch.int32, device=logits.device)
+    if topk_weights is None:
+        topk_weights = torch.empty(T, Kp, dtype=torch.float32, device=logits.device)
+    _check("moe_route_topk", lib().moe_route_topk(
+        _ptr(logits), _ptr(gate_logits), T, E, K, shared, renormalize, _ptr(topk_ids),
+        _ptr(topk_weights), _stream(stream)))
+    return topk_ids, topk_weights
+
+
+def align_workspace_size(T: int, Kp: int, Ep: int) -> int:
+    return int(lib().moe_align_workspace_size(T, Kp, Ep))
+
+
+def align_sort(topk_ids, Ep: int, tile_m: int = TILE_M, out=None, stream=None):
+    """moe_align_sort -> dict(counts, offsets, sorted, inv, tiles, num_tiles, workspace).
+    `out` may hold preallocated tensors of those names (see alloc_align)."""
+    _dt(topk_ids, torch.int32, "topk_ids")
+    T, Kp = topk_ids.shape
+    A = T * Kp
+    if out is None:
+        out = alloc_align(T, Kp, Ep, topk_ids.device, tile_m)
+    _check("moe_align_sort", lib().moe_align_sort(
+        _ptr(topk_ids), T, Kp, Ep, tile_m, _ptr(out["counts"]), _ptr(out["offsets"]),
+        _ptr(out["sorted"]) if A else None, _ptr(out["inv"]) if A else None,
+        _ptr(out["tiles"]), _ptr(out["num_tiles"]), _ptr(out["workspace"]),
+        out["workspace"].numel(), _stream(stream)))
+    return out
+
+
+def alloc_align(T: int, Kp: int, Ep: int, device, tile_m: int = TILE_M) -> dict:
+    A = T * Kp
+    i32 = dict(dtype=torch.int32, device=device)
+    ws_bytes = align_workspace_size(T, Kp, Ep)
+    return dict(counts=torch.empty(Ep, **i32), offsets=torch.empty(Ep + 1, **i32),
+                sorted=torch.empty(max(A, 1), **i32)[:A], inv=torch.empty(max(A, 1), **i32)[:A],
+                tiles=torch.empty((A + tile_m - 1) // tile_m + Ep, 2, **i32),
+                num_tiles=torch.empty(1, **i32),
+                workspace=torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=device))
+
+
+def mxfp4_quantize(src, packed=None, scales=None, stream=None):
+    """moe_mxfp4_quantize: fp32 or bf16 [..., cols] -> (packed uint8 [..., cols/2], scales uint8 [..., cols/32])."""
+    if src.dtype == torch.float32:
+        dt = SRC_F32
+    elif src.dtype == torch.bfloat16:
+        dt = SRC_BF16
+    else:
+        raise TypeError("src must be float32 or bfloat16")
+    cols = src.shape[-1]
+    rows = src.numel() // cols if cols else 0
+    lead = src.shape[:-1]
+    if packed is None:
+        packed = torch.empty(*lead, cols // 2, dtype=torch.uint8, device=src.device)
+    if scales is None:
+        scales = torch.empty(*lead, cols // 32, dtype=torch.uint8, device=src.device)
+    _check("moe_mxfp4_quantize", lib().moe_mxfp4_quantize(
+        _ptr(src), dt, rows, cols, _ptr(packed), _ptr(scales), _stream(stream)))
+    return packed, scales
+
+
+def expert_gate_up(act, act_scale, act_fmt: int, align: dict, w13, w13_scale, T: int, H: int,
+                   I: int, Ep: int, Kp: int, h=None, stream=None):
+    """moe_expert_gate_up -> h bf16 [T*Kp, I] in sorted row order."""
+    if h is None:
+        h = torch.empty(T * Kp, I, dtype=torch.bfloat16, device=w13.device)
+    _check("moe_expert_gate_up", lib().moe_expert_gate_up(
+        _ptr(act), _ptr(act_scale), act_fmt, _ptr(align["sorted"]), _ptr(align["offsets"]),
+        _ptr(align["tiles"]), _ptr(align["num_tiles"]), _ptr(w13), _ptr(w13_scale), T, H, I, Ep,
+        Kp, _ptr(h), _stream(stream)))
+    return h
+
+
+def expert_down(h, h_scale, act_fmt: int, align: dict, w2, w2_scale, T: int, H: int, I: int,
+                Ep: int, Kp: int, y=None, stream=None):
+    """moe_expert_down -> y fp32 [T*Kp, H] in sorted row order."""
+    if y is None:
+        y = torch.empty(T * Kp, H, dtype=torch.float32, device=w2.device)
+    _check("moe_expert_down", lib().moe_expert_down(
+        _ptr(h), _ptr(h_scale), act_fmt, _ptr(align["offsets"]), _ptr(align["tiles"]),
+        _ptr(align["num_tiles"]), _ptr(w2), _ptr(w2_scale), T, H, I, Ep, Kp, _ptr(y),
+        _stream(stream)))
+    return y
+
+
+def combine(y, topk_weights, inv, T: int, H: int, Kp: int, out=None, stream=None):
+    """moe_combine -> out bf16 [T, H]."""
+    if out is None:
+        out = torch.empty(T, H, dtype=torch.bfloat16, device=y.device)
+    _check("moe_combine", lib().moe_combine(
+        _ptr(y), _ptr(topk_weights), _ptr(inv), T, H, Kp, _ptr(out), _stream(stream)))
+    return out
+
+
+# ------------------------------------------------------------ whole layer --
+
+def workspace_size(T, H, I, E, K, shared, act_fmt) -> int:
+    return int(lib().moe_mxfp4_workspace_size(T, H, I, E, K, shared, act_fmt))
+
+
+def mxfp4_forward(x, router_logits, shared_gate_logits, w13, w13_scale, w2, w2_scale, I: int,
+                  E: int, K: int, shared: int, act_fmt: int = ACT_BF16, out=None, topk_ids=None,
+                  topk_weights=None, workspace=None, stream=None):
+    """moe_mxfp4_forward: the whole layer.  x bf16 [T, H] -> out bf16 [T, H]."""
+    _dt(x, torch.bfloat16, "x")
+    _dt(router_logits, torch.float32, "router_logits")
+    T, H = x.shape
+    if out is None:
+        out = torch.empty(T, H, dtype=torch.bfloat16, device=x.device)
+    need = workspace_size(T, H, I, E, K, shared, act_fmt)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=x.device)
+    _check("moe_mxfp4_forward", lib().moe_mxfp4_forward(
+        _ptr(x), _ptr(router_logits), _ptr(shared_gate_logits), _ptr(w13), _ptr(w13_scale),
+        _ptr(w2), _ptr(w2_scale), T, H, I, E, K, shared, act_fmt, _ptr(out), _ptr(topk_ids),
+        _ptr(topk_weights), _ptr(workspace), workspace.numel(), _stream(stream)))
+    return out
+
+
+def alloc_stages(T: int, H: int, I: int, E: int, K: int, shared: int, act_fmt: int,
+                 device) -> dict:
+    """Preallocated outputs of every stage of one pass (for forward_stages)."""
+    Kp, Ep, A = K + shared, E + shared, T * (K + shared)
+    b = dict(ids=torch.empty(T, Kp, dtype=torch.int32, device=device),
+             w=torch.empty(T, Kp, dtype=torch.float32, device=device),
+             align=alloc_align(T, Kp, Ep, device),
+             h=torch.empty(A, I, dtype=torch.bfloat16, device=device),
+             y=torch.empty(A, H, dtype=torch.float32, device=device),
+             out=torch.empty(T, H, dtype=torch.bfloat16, device=device))
+    if act_fmt == ACT_MXFP4:
+        u8 = dict(dtype=torch.uint8, device=device)
+        b.update(xq=torch.empty(T, H // 2, **u8), xs=torch.empty(T, H // 32, **u8),
+                 hq=torch.empty(A, I // 2, **u8), hs=torch.empty(A, I // 32, **u8))
+    return b
+
+
+def forward_stages(x, router_logits, shared_gate_logits, w13, w13_scale, w2, w2_scale, I: int,
+                   E: int, K: int, shared: int, act_fmt: int = ACT_BF16, bufs=None, stream=None,
+                   events=None):
+    """The same pass as mxfp4_forward, one C entry point per stage, keeping
+    every intermediate (in `bufs` if given, see alloc_stages).  `events`, if
+    given, maps a stage name (route, align, quant_x, gate_up, quant_h, down,
+    combine) to a (start, end) pair of torch.cuda.Event recorded around it."""
+    T, H = x.shape
+    Kp, Ep = K + shared, E + shared
+    b = alloc_stages(T, H, I, E, K, shared, act_fmt, x.device) if bufs is None else bufs
+    st = torch.cuda.current_stream() if stream is None else stream
+
+    def rec(name, i):
+        if events and name in events:
+            events[name][i].record(st)
+
+    rec("route", 0)
+    route_topk(router_logits, shared_gate_logits, K, shared, topk_ids=b["ids"],
+               topk_weights=b["w"], stream=stream)
+    rec("route", 1)
+    rec("align", 0)
+    align_sort(b["ids"], Ep, out=b["align"], stream=stream)
+    rec("align", 1)
+    act, act_s = x, None
+    if act_fmt == ACT_MXFP4:
+        rec("quant_x", 0)
+        mxfp4_quantize(x, b["xq"], b["xs"], stream=stream)
+        rec("quant_x", 1)
+        act, act_s = b["xq"], b["xs"]
+    rec("gate_up", 0)
+    expert_gate_up(act, act_s, act_fmt, b["align"], w13, w13_scale, T, H, I, Ep, Kp, h=b["h"],
+                   stream=stream)
+    rec("gate_up", 1)
+    hin, hin_s = b["h"], None
+    if act_fmt == ACT_MXFP4:
+        rec("quant_h", 0)
+        mxfp4_quantize(b["h"], b["hq"], b["hs"], stream=stream)
+        rec("quant_h", 1)
+        hin, hin_s = b["hq"], b["hs"]
+    rec("down", 0)
+    expert_down(hin, hin_s, act_fmt, b["align"], w2, w2_scale, T, H, I, Ep, Kp, y=b["y"],
+                stream=stream)
+    rec("down", 1)
+    rec("combine", 0)
+    combine(b["y"], b["w"], b["align"]["inv"], T, H, Kp, out=b["out"], stream=stream)
+    rec("combine", 1)
+    return b

@@ -1,0 +1,134 @@
+"""The C-ABI library without a GPU: it loads, it exports every entry point the
+header declares, and every argument check returns its status before any
+HIP call (no call here reaches a kernel launch)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from mxfp4_routed_expert_top_amd import ops
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe_mxfp4.h")
+
+OK, INVALID, UNSUPPORTED, WS_SMALL = (ops.MOE_OK, ops.MOE_ERR_INVALID_ARGUMENT,
+                                      ops.MOE_ERR_UNSUPPORTED, ops.MOE_ERR_WORKSPACE_TOO_SMALL)
+FAKE = ctypes.c_void_p(0x100000)        # never dereferenced: every call below fails validation
+MIS = ctypes.c_void_p(0x100004)          # not 16-byte aligned
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"MOE_API\s+[\w\s\*]+?\b(moe_\w+)\s*\(", text)))
+
+
+def test_library_loads_and_exports_every_declared_symbol():
+    lib = ops.lib()
+    names = declared_functions()
+    assert len(names) == 10
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) == set(ops.EXPORTS)
+
+
+def test_status_strings():
+    assert ops.status_string(0) == "MOE_OK"
+    assert ops.status_string(4) == "MOE_ERR_DEVICE"
+    assert ops.status_string(99) == "MOE_ERR_UNKNOWN"
+
+
+def test_route_topk_argument_errors():
+    f = ops.lib().moe_route_topk
+    assert f(None, None, 4, 8, 2, 0, 1, FAKE, FAKE, None) == INVALID        # null logits
+    assert f(FAKE, None, 4, 8, 2, 1, 1, FAKE, FAKE, None) == INVALID        # shared without gate
+    assert f(FAKE, None, -1, 8, 2, 0, 1, FAKE, FAKE, None) == INVALID       # T < 0
+    assert f(FAKE, None, 4, 8, 0, 0, 1, FAKE, FAKE, None) == INVALID        # K < 1
+    assert f(FAKE, None, 4, 8, 9, 0, 1, FAKE, FAKE, None) == INVALID        # K > E
+    assert f(FAKE, None, 4, 8, 2, 2, 1, FAKE, FAKE, None) == INVALID        # shared flag
+    assert f(FAKE, None, 4, 8, 2, 0, 3, FAKE, FAKE, None) == INVALID        # renormalize flag
+    assert f(FAKE, None, 4, 8, 2, 0, 1, None, FAKE, None) == INVALID        # null output
+    assert f(FAKE, None, 4, 2048, 2, 0, 1, FAKE, FAKE, None) == UNSUPPORTED  # E > 1024
+    assert f(FAKE, FAKE, 4, 64, 32, 1, 1, FAKE, FAKE, None) == UNSUPPORTED   # K' > 32
+    assert f(None, None, 0, 8, 2, 0, 1, None, None, None) == OK             # T = 0: nothing to do
+
+
+def test_align_sort_argument_errors():
+    f = ops.lib().moe_align_sort
+    ws = ops.align_workspace_size(10, 3, 7)
+    assert ws > 0
+    args = lambda **kw: [kw.get("ids", FAKE), kw.get("T", 10), kw.get("Kp", 3), kw.get("Ep", 7),
+                         kw.get("tm", 32), kw.get("cnt", FAKE), kw.get("off", FAKE),
+                         kw.get("srt", FAKE), None, None, kw.get("nt", FAKE), kw.get("ws", FAKE),
+                         kw.get("wsb", ws), None]
+    assert f(*args(ids=None)) == INVALID
+    assert f(*args(T=-1)) == INVALID
+    assert f(*args(Kp=0)) == INVALID
+    assert f(*args(Ep=0)) == INVALID
+    assert f(*args(tm=0)) == INVALID
+    assert f(*args(cnt=None)) == INVALID
+    assert f(*args(nt=None)) == INVALID
+    assert f(*args(Ep=4096)) == UNSUPPORTED
+    assert f(*args(wsb=ws - 1)) == WS_SMALL
+    assert f(*args(ws=None)) == INVALID
+
+
+def test_quantize_argument_errors():
+    f = ops.lib().moe_mxfp4_quantize
+    assert f(FAKE, 0, 4, 48, FAKE, FAKE, None) == UNSUPPORTED      # cols % 32
+    assert f(FAKE, 2, 4, 64, FAKE, FAKE, None) == INVALID          # dtype
+    assert f(FAKE, 0, -1, 64, FAKE, FAKE, None) == INVALID
+    assert f(None, 0, 4, 64, FAKE, FAKE, None) == INVALID
+    assert f(MIS, 0, 4, 64, FAKE, FAKE, None) == INVALID           # misaligned source
+    assert f(FAKE, 0, 0, 64, FAKE, FAKE, None) == OK               # empty
+
+
+def test_gemm_and_combine_argument_errors():
+    gu = ops.lib().moe_expert_gate_up
+    base = [FAKE, None, 0, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 8, 256, 128, 16, 2, FAKE, None]
+    def call(f, a, **over):
+        a = list(a)
+        for i, v in over.items():
+            a[int(i[1:])] = v
+        return f(*a)
+    assert call(gu, base, a0=None) == INVALID
+    assert call(gu, base, a2=1) == INVALID                 # MXFP4 activations need scales
+    assert call(gu, base, a2=7) == INVALID
+    assert call(gu, base, a10=200) == UNSUPPORTED          # H % 128
+    assert call(gu, base, a11=96) == UNSUPPORTED           # I % 128
+    assert call(gu, base, a0=MIS) == INVALID
+    assert call(gu, base, a9=0) == OK
+    dn = ops.lib().moe_expert_down
+    based = [FAKE, None, 0, FAKE, FAKE, FAKE, FAKE, FAKE, 8, 256, 128, 16, 2, FAKE, None]
+    assert call(dn, based, a13=None) == INVALID
+    assert call(dn, based, a9=100) == UNSUPPORTED
+    assert call(dn, based, a8=0) == OK
+    cb = ops.lib().moe_combine
+    assert cb(None, FAKE, FAKE, 4, 256, 3, FAKE, None) == INVALID
+    assert cb(FAKE, FAKE, FAKE, 4, 200, 3, FAKE, None) == UNSUPPORTED
+    assert cb(FAKE, FAKE, FAKE, 0, 256, 3, FAKE, None) == OK
+
+
+def test_forward_argument_errors_and_workspace():
+    f = ops.lib().moe_mxfp4_forward
+    need = ops.workspace_size(8, 256, 128, 16, 2, 0, 0)
+    assert need > 0 and ops.workspace_size(0, 256, 128, 16, 2, 0, 0) == 0
+    assert ops.workspace_size(8, 256, 128, 16, 2, 0, 1) > need      # W4A4 adds the quantised copies
+    base = [FAKE, FAKE, None, FAKE, FAKE, FAKE, FAKE, 8, 256, 128, 16, 2, 0, 0, FAKE, None, None,
+            FAKE, need, None]
+    def call(**over):
+        a = list(base)
+        for i, v in over.items():
+            a[int(i[1:])] = v
+        return f(*a)
+    assert call(a18=need - 1) == WS_SMALL
+    assert call(a17=None) == INVALID
+    assert call(a0=None) == INVALID
+    assert call(a14=None) == INVALID
+    assert call(a12=1) == INVALID                          # shared without gate logits
+    assert call(a13=5) == INVALID
+    assert call(a11=17) == INVALID                         # K > E
+    assert call(a8=96) == UNSUPPORTED
+    assert call(a10=2048) == UNSUPPORTED
+    assert call(a3=MIS) == INVALID
+    assert call(a7=0, a0=None, a17=None, a18=0) == OK      # T = 0

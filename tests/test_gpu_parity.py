@@ -1,0 +1,282 @@
+"""Parity of the HIP path (through the C ABI) with the CPU oracle.
+
+Bit-exact: MXFP4 packing, routing ids, the grouping tables.  Within
+tolerance: routing weights (1e-6 absolute), h (bf16, rare one-ulp flips),
+and the layer output (relative L2 <= 5e-3 for W4A16, <= 2e-2 for W4A4; max
+abs <= 2e-2 x RMS of the oracle output)."""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import synth
+from oracle import moe, mxfp4
+from tests.helpers import (DEV, MAX_ABS_RMS, REL_L2, W_ATOL, Problem, bits, max_abs_over_rms,
+                           rel_l2)
+
+pytestmark = pytest.mark.gpu
+
+
+def _say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _lib():
+    from mxfp4_routed_expert_top_amd import ops
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    ops.lib()
+
+
+def ops():
+    from mxfp4_routed_expert_top_amd import ops as o
+    return o
+
+
+SMALL = {
+    "tiny": synth.CONFIGS["tiny"],
+    # several 32-row tiles per expert with ragged tails; H, I span several K steps
+    "ragged": synth.custom_config("ragged", T=50, H=512, I=256, E=32, K=4, shared=1),
+    "no_shared_k1": synth.custom_config("no_shared_k1", T=33, H=256, I=128, E=8, K=1, shared=0),
+    "one_expert": synth.custom_config("one_expert", T=7, H=128, I=128, E=1, K=1, shared=0),
+    "single_token": synth.custom_config("single_token", T=1, H=384, I=256, E=64, K=6, shared=1),
+    "sparse": synth.custom_config("sparse", T=3, H=256, I=128, E=300, K=2, shared=1),
+    "w4a4_small": synth.custom_config("w4a4_small", T=40, H=256, I=128, E=16, K=3, shared=1,
+                                      act_fmt=synth.ACT_MXFP4, outlier_p=0.01),
+    "w4a4_ragged": synth.custom_config("w4a4_ragged", T=70, H=384, I=256, E=12, K=2, shared=1,
+                                       act_fmt=synth.ACT_MXFP4, outlier_p=0.001),
+}
+
+
+# ------------------------------------------------------------- quantiser --
+
+def _special_blocks():
+    """Blocks with ties at every midpoint, saturation, signed zeros, tiny and
+    huge magnitudes, all-zero blocks."""
+    mids = np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0, 6.5, 7.0, 0.0, -0.0, 4.0])
+    rows = []
+    for X in [-127, -120, -7, -1, 0, 3, 100]:
+        blk = np.zeros(32)
+        blk[0] = 4.0
+        blk[1:1 + mids.size] = mids
+        blk[20:20 + mids.size] = -mids
+        rows.append(blk * 2.0 ** X)
+    rows.append(np.zeros(32))
+    rows.append(-np.zeros(32))
+    return np.array(rows, np.float32)
+
+
+@pytest.mark.parametrize("kind", ["weights_f32", "act_bf16", "special_f32", "special_bf16"])
+def test_quantize_bit_exact(kind):
+    _say("quantize", kind)
+    g = torch.Generator().manual_seed(11)
+    if kind == "weights_f32":
+        v = torch.randn(512, 1024, generator=g) * 0.02
+    elif kind == "act_bf16":
+        v = torch.randn(300, 2048, generator=g)
+        v = torch.where(torch.rand(300, 2048, generator=g) < 0.01, v * 50, v).to(torch.bfloat16)
+    else:
+        v = torch.from_numpy(_special_blocks())
+        if kind == "special_bf16":
+            v = v.to(torch.bfloat16)           # every special value is bf16-exact
+    p, s = ops().mxfp4_quantize(v.to(DEV))
+    want_p, want_s = mxfp4.quantize(v.double().numpy())
+    assert np.array_equal(s.cpu().numpy(), want_s)
+    assert np.array_equal(p.cpu().numpy(), want_p)
+
+
+# ---------------------------------------------------------------- routing --
+
+ROUTE_CASES = [("tiny", None), ("ragged", None), ("ties", None), ("decode", None),
+               ("prefill_skewed", None), ("w4a4", None), ("full_softmax", 0)]
+
+
+@pytest.mark.parametrize("name,renorm", ROUTE_CASES)
+def test_route_topk(name, renorm):
+    _say("route", name)
+    if name == "ties":
+        T, E, K, shared = 257, 96, 7, 1
+        logits = synth.ties_logits(T, E, 3)
+        gate = torch.randn(T, generator=torch.Generator().manual_seed(4))
+    elif name == "full_softmax":
+        T, E, K, shared = 64, 40, 40, 0
+        logits = torch.randn(T, E, generator=torch.Generator().manual_seed(5)) * 3
+        gate = None
+    else:
+        cfg = SMALL.get(name) or synth.CONFIGS[name]
+        T, E, K, shared = cfg.T, cfg.E, cfg.K, cfg.shared
+        logits, gate = synth.router_logits(cfg), synth.gate_logits(cfg)
+    renormalize = 1 if renorm is None else renorm
+    ids, w = ops().route_topk(logits.to(DEV), None if gate is None else gate.to(DEV), K, shared,
+                              renormalize)
+    want_ids, want_w = moe.route(logits.numpy(), None if gate is None else gate.numpy(), K,
+                                 shared, bool(renormalize))
+    assert np.array_equal(ids.cpu().numpy(), want_ids)
+    assert np.max(np.abs(w.cpu().numpy() - want_w)) <= W_ATOL
+    if renormalize:
+        assert np.all(np.abs(w[:, :K].double().sum(1).cpu().numpy() - 1) <= 1e-6)
+
+
+# ------------------------------------------------------------------ align --
+
+def _check_align(got, want, with_tiles=True):
+    counts, offsets, srt, inv, tiles, n = want
+    assert np.array_equal(got["counts"].cpu().numpy(), counts)
+    assert np.array_equal(got["offsets"].cpu().numpy(), offsets)
+    assert np.array_equal(got["sorted"].cpu().numpy(), srt)
+    assert np.array_equal(got["inv"].cpu().numpy(), inv)
+    assert int(got["num_tiles"].item()) == n
+    if with_tiles:
+        assert np.array_equal(got["tiles"][:n].cpu().numpy(), tiles)
+
+
+def test_align_golden_tile_m_2():
+    ids = torch.tensor([[1, 0], [1, 2], [0, 1]], dtype=torch.int32)
+    got = ops().align_sort(ids.to(DEV), 3, tile_m=2)
+    _check_align(got, moe.align(ids.numpy(), 3, 2))
+    assert got["tiles"][:4].cpu().tolist() == [[0, 0], [1, 2], [1, 4], [2, 5]]
+
+
+@pytest.mark.parametrize("name", ["tiny", "ragged", "sparse", "decode", "prefill",
+                                  "prefill_skewed", "w4a4", "one_hot", "big_a"])
+def test_align_sort(name):
+    _say("align", name)
+    if name == "one_hot":                  # every assignment to one expert: many tiles
+        T, Kp, Ep = 3000, 1, 40
+        ids = torch.full((T, Kp), 17, dtype=torch.int32)
+    elif name == "big_a":                  # many chunks, random ids, a ragged last chunk
+        T, Kp, Ep = 12345, 9, 1025
+        ids = torch.randint(0, Ep, (T, Kp), generator=torch.Generator().manual_seed(9),
+                            dtype=torch.int32)
+    else:
+        cfg = SMALL.get(name) or synth.CONFIGS[name]
+        Kp, Ep = cfg.Kp, cfg.Ep
+        ids = torch.from_numpy(moe.route(synth.router_logits(cfg).numpy(),
+                                         None if not cfg.shared else synth.gate_logits(cfg).numpy(),
+                                         cfg.K, cfg.shared)[0])
+    got = ops().align_sort(ids.to(DEV), Ep)
+    _check_align(got, moe.align(ids.numpy(), Ep, 32))
+
+
+def test_align_empty():
+    ids = torch.empty(0, 3, dtype=torch.int32, device=DEV)
+    got = ops().align_sort(ids, 5)
+    assert got["counts"].cpu().tolist() == [0] * 5
+    assert got["offsets"].cpu().tolist() == [0] * 6
+    assert int(got["num_tiles"].item()) == 0
+
+
+# -------------------------------------------------------------- the layer --
+
+def _oracle_h(prob, res):
+    """Oracle h (bf16 values, fp64) for every sorted row."""
+    c = prob.cfg
+    x = bits(prob.x_cpu)
+    a_all = (mxfp4.decode(*moe.quantize_activations(x)) if c.act_fmt == synth.ACT_MXFP4
+             else mxfp4.bf16_to_f64(x))
+    h = np.zeros((c.A, c.I))
+    for e in range(c.Ep):
+        lo, hi = res["offsets"][e], res["offsets"][e + 1]
+        if hi > lo:
+            toks = res["sorted"][lo:hi] // c.Kp
+            _, h[lo:hi] = moe.expert_mlp(a_all[toks], *prob.oracle_weights(e), c.I, c.act_fmt,
+                                         return_h=True)
+    return h
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+def test_layer_small(name):
+    _say("layer", name)
+    prob = Problem(SMALL[name])
+    c = prob.cfg
+    r = prob.stages()
+    out = prob.forward()
+    torch.cuda.synchronize()
+    want = prob.oracle()
+    # the one-call forward and the per-stage calls produce the same bits
+    assert np.array_equal(bits(out), bits(r["out"]))
+    assert np.array_equal(r["ids"].cpu().numpy(), want["ids"])
+    assert np.max(np.abs(r["w"].cpu().numpy() - want["w"])) <= W_ATOL
+    _check_align(r["align"], (want["counts"], want["offsets"], want["sorted"], want["inv"],
+                              want["tiles"], want["n_tiles"]))
+    if c.act_fmt == synth.ACT_MXFP4:
+        xq, xs = moe.quantize_activations(bits(prob.x_cpu))
+        assert np.array_equal(r["xq"].cpu().numpy(), xq)
+        assert np.array_equal(r["xs"].cpu().numpy(), xs)
+    h = mxfp4.bf16_to_f64(bits(r["h"]))
+    hw = _oracle_h(prob, want)
+    assert np.linalg.norm(h - hw) / np.linalg.norm(hw) <= 2e-3
+    e_rel = rel_l2(bits(out), want["out"])
+    e_max = max_abs_over_rms(bits(out), want["out"])
+    _say(f"  {name}: rel_l2 {e_rel:.2e}  max_abs/rms {e_max:.2e}")
+    assert e_rel <= REL_L2[c.act_fmt]
+    assert e_max <= MAX_ABS_RMS
+
+
+def test_layer_all_tokens_one_expert():
+    cfg = synth.custom_config("hot", T=100, H=256, I=128, E=16, K=3, shared=1)
+    logits = synth.router_logits(cfg)
+    logits[:, 5] += 100.0                  # expert 5 first for every token: 4 tiles of 32
+    prob = Problem(cfg, logits=logits)
+    out = prob.forward()
+    want = prob.oracle()
+    assert want["counts"][5] == cfg.T
+    assert rel_l2(bits(out), want["out"]) <= REL_L2[cfg.act_fmt]
+    assert max_abs_over_rms(bits(out), want["out"]) <= MAX_ABS_RMS
+
+
+def test_layer_deterministic_and_reentrant():
+    prob = Problem(SMALL["ragged"])
+    a = bits(prob.forward())
+    b = bits(prob.forward())
+    ws = torch.full((ops().workspace_size(prob.cfg.T, prob.cfg.H, prob.cfg.I, prob.cfg.E,
+                                          prob.cfg.K, prob.cfg.shared, prob.cfg.act_fmt),),
+                    0xFF, dtype=torch.uint8, device=DEV)        # dirty workspace
+    c = bits(prob.forward(workspace=ws))
+    assert np.array_equal(a, b) and np.array_equal(a, c)
+
+
+def test_layer_empty_batch():
+    cfg = synth.custom_config("empty", T=1)
+    prob = Problem(cfg)
+    x = torch.empty(0, cfg.H, dtype=torch.bfloat16, device=DEV)
+    l = torch.empty(0, cfg.E, dtype=torch.float32, device=DEV)
+    g = torch.empty(0, dtype=torch.float32, device=DEV)
+    out = ops().mxfp4_forward(x, l, g, prob.w13, prob.w13s, prob.w2, prob.w2s, cfg.I, cfg.E,
+                              cfg.K, cfg.shared, cfg.act_fmt)
+    assert out.shape == (0, cfg.H)
+
+
+FULL = ["decode", "prefill", "prefill_skewed", "w4a4"]
+
+
+@pytest.mark.parametrize("name", FULL)
+def test_layer_full_size_sampled(name):
+    """Full-size workloads in the launch configuration the bench times: routing
+    and grouping bit-exact for every token, the output of sampled tokens
+    against the oracle."""
+    cfg = synth.CONFIGS[name]
+    _say("full", name, "T", cfg.T, "H", cfg.H, "I", cfg.I, "E", cfg.E, "K", cfg.K)
+    prob = Problem(cfg)
+    ids = torch.empty(cfg.T, cfg.Kp, dtype=torch.int32, device=DEV)
+    w = torch.empty(cfg.T, cfg.Kp, dtype=torch.float32, device=DEV)
+    out = prob.forward(topk_ids=ids, topk_weights=w)
+    torch.cuda.synchronize()
+    _say("  forward done")
+    rng = np.random.default_rng(cfg.seed_act)
+    tokens = np.sort(rng.choice(cfg.T, size=2, replace=False))
+    want = prob.oracle(tokens=tokens)
+    _say("  oracle done for tokens", tokens.tolist())
+    assert np.array_equal(ids.cpu().numpy(), want["ids"])
+    assert np.max(np.abs(w.cpu().numpy() - want["w"])) <= W_ATOL
+    if cfg.skew:
+        assert int((want["counts"] == 0).sum()) == 3
+    got = bits(out)[tokens]
+    e_rel = rel_l2(got, want["out"])
+    e_max = max_abs_over_rms(got, want["out"])
+    _say(f"  {name}: rel_l2 {e_rel:.2e}  max_abs/rms {e_max:.2e}")
+    assert e_rel <= REL_L2[cfg.act_fmt]
+    assert e_max <= MAX_ABS_RMS
+    assert torch.isfinite(out.float()).all()
