@@ -107,14 +107,14 @@ def expert_mlp(a: np.ndarray, w13_e, w13s_e, w2_e, w2s_e, I: int, act_fmt: int,
     """One expert on rows a (fp64 [n, H], already bf16 / MXFP4-exact values).
 
     acc = a . dq(W13)^T (fp64); h = bf16(silu(acc[:, :I]) * acc[:, I:]);
-    for W4A4 h is MXFP4-quantised along I and decoded; y = h . dq(W2)^T."""
+    for W4A4 h is MXFP4-quantised along I and decoded; y = h . dq(W2)^T.
+    With return_h, also returns the bf16 h (before any MXFP4 step)."""
     W13 = mxfp4.decode(w13_e, w13s_e)              # [2I, H]
     acc = a @ W13.T                                # [n, 2I]
     h = mxfp4.round_bf16(silu(acc[:, :I]) * acc[:, I:])
-    if act_fmt == ACT_MXFP4:
-        h = mxfp4.decode(*mxfp4.quantize(h))
+    hin = mxfp4.decode(*mxfp4.quantize(h)) if act_fmt == ACT_MXFP4 else h
     W2 = mxfp4.decode(w2_e, w2s_e)                 # [H, I]
-    y = h @ W2.T                                   # [n, H]
+    y = hin @ W2.T                                 # [n, H]
     return (y, h) if return_h else y
 
 
