@@ -58,6 +58,25 @@ __device__ __forceinline__ floatx4_t mfma_fp4_16x16x128(u32x4_t a, uint32_t sa, 
   return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, bv, c, 4, 4, 0, (int)sa, 0, (int)sb);
 }
 
+// Raw buffer loads: a wave-uniform resource (base, size in bytes) plus a
+// per-lane byte offset and a wave-uniform byte offset.  Reads past the
+// resource's size return zeros instead of touching memory.
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+#define MOE_BUFFER_FLAGS 0x00020000  // gfx9 raw buffer: 32-bit data format, no swizzle
+
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                           MOE_BUFFER_FLAGS);
+}
+
+__device__ __forceinline__ u32x4_t bload16(rsrc_t r, uint32_t voff, uint32_t soff) {
+  return __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, (int)soff, 0));
+}
+
+__device__ __forceinline__ uint32_t bload1(rsrc_t r, uint32_t voff, uint32_t soff) {
+  return (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(r, (int)voff, (int)soff, 0);
+}
+
 __device__ __forceinline__ u32x4_t load16(const void* p) {
   return *reinterpret_cast<const u32x4_t*>(p);
 }

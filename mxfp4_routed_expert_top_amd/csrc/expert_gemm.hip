@@ -28,8 +28,16 @@
 
 namespace {
 
+// Tuning constants: the widest pipeline phase (in 128-element chunks) and
+// the waves per SIMD the register allocation of the GEMM kernels aims for.
+#ifndef MOE_GEMM_PH_MAX
+#define MOE_GEMM_PH_MAX 2
+#endif
+#ifndef MOE_GEMM_WAVES_PER_EU
+#define MOE_GEMM_WAVES_PER_EU 3
+#endif
+
 constexpr int kTileM = 32;        // rows per workgroup (= the tile table's tile_m)
-constexpr int kMT = kTileM / 16;  // 16-row MFMA subtiles per tile
 
 struct TileInfo {
   int expert, row0, rows;
@@ -44,260 +52,268 @@ __device__ __forceinline__ bool load_tile(const int32_t* tiles, const int32_t* n
   return true;
 }
 
-// ---------------------------------------------------------------- W4A16 ----
+// A wave computes two 16-row strips of weights against the activation rows of
+// its tile over the whole K, in phases of PH chunks of 128 K-elements.  In
+// chunk c, lane (row l%16, group g = l/16) holds bytes [64 c + 16 g, +16) of
+// its weight row (32 codes) and the scale byte of block 4 c + g.
+//
+// Software pipeline: phases alternate between two register sets; the loads
+// of phase p+1 (weights and activations together) are issued before phase p
+// is computed, so the wave always has one phase in flight and waits only for
+// the older one (vmcnt counts in issue order).
+//
+// Operands are read with buffer loads: one resource per tensor (wave-uniform)
+// and per-lane byte offsets, so a chunk's position is a scalar offset.  The
+// weight scales of the workgroup's rows are first copied to LDS with 16-byte
+// loads (one byte per lane per chunk would cost a load instruction per 1 KiB
+// of weights); lanes of padded tile rows get an out-of-range activation
+// offset, so their loads return zeros without touching memory.
+constexpr uint32_t kOutOfRange = 0x80000000u;
 
-__global__ __launch_bounds__(256) void gate_up_w4a16_kernel(
-    const uint16_t* __restrict__ x, const int32_t* __restrict__ sorted,
-    const int32_t* __restrict__ offsets, const int32_t* __restrict__ tiles,
-    const int32_t* __restrict__ num_tiles, const uint8_t* __restrict__ w13,
-    const uint8_t* __restrict__ w13s, int T, int H, int I, int Kp, int nsl,
-    uint16_t* __restrict__ h) {
+struct Operands {
+  rsrc_t w, a, as;         // weights, activations, activation scales (MXFP4)
+  uint32_t wo[2];          // lane offsets of its two weight rows (+16 g)
+  uint32_t lso[2];         // LDS offsets of its two weight rows' scales (+g)
+  uint32_t ao, aso;        // lane offset of its activation row (+32 g elements or +16 g bytes)
+  const uint8_t* lds;      // the workgroup's weight scales
+  const uint8_t* ldx;      // bf16 activation rows staged in LDS (small tiles), lane row + 64 g
+  bool xvalid;             // the lane's activation row exists (padded rows read zeros)
+};
+
+template <int PH, bool kFP4A, bool XL>
+struct Phase {
+  u32x4_t q[2][PH];
+  u32x4_t a[PH][(kFP4A || XL) ? 1 : 4];
+  uint32_t as[PH];
+
+  __device__ __forceinline__ void load(const Operands& o, int c0) {
+#pragma unroll
+    for (int j = 0; j < PH; ++j)
+#pragma unroll
+      for (int si = 0; si < 2; ++si) q[si][j] = bload16(o.w, o.wo[si], 64 * (c0 + j));
+#pragma unroll
+    for (int j = 0; j < PH; ++j) {
+      if constexpr (kFP4A) {
+        a[j][0] = bload16(o.a, o.ao, 64 * (c0 + j));
+        as[j] = bload1(o.as, o.aso, 4 * (c0 + j));
+      } else if constexpr (!XL) {
+#pragma unroll
+        for (int qq = 0; qq < 4; ++qq) a[j][qq] = bload16(o.a, o.ao + 16 * qq, 256 * (c0 + j));
+      }
+    }
+  }
+
+  __device__ __forceinline__ void compute(const Operands& o, int c0, floatx4_t (&acc)[2]) const {
+#pragma unroll
+    for (int j = 0; j < PH; ++j) {
+      uint32_t sw[2];
+#pragma unroll
+      for (int si = 0; si < 2; ++si) sw[si] = o.lds[o.lso[si] + 4 * (c0 + j)];
+      if constexpr (kFP4A) {
+#pragma unroll
+        for (int si = 0; si < 2; ++si)
+          acc[si] = mfma_fp4_16x16x128(a[j][0], as[j], q[si][j], sw[si], acc[si]);
+      } else {
+        u32x4_t x[4];
+#pragma unroll
+        for (int qq = 0; qq < 4; ++qq) {
+          if constexpr (XL) {
+            const u32x4_t v = *reinterpret_cast<const u32x4_t*>(o.ldx + 256 * (c0 + j) + 16 * qq);
+            x[qq] = o.xvalid ? v : (u32x4_t){0u, 0u, 0u, 0u};
+          } else {
+            x[qq] = a[j][qq];
+          }
+        }
+#pragma unroll
+        for (int si = 0; si < 2; ++si) {
+          const float sc = e8m0_to_f32(sw[si]);
+#pragma unroll
+          for (int qq = 0; qq < 4; ++qq)
+            acc[si] = mfma_bf16_16x16x32(__builtin_bit_cast(bf16x8_t, x[qq]),
+                                         dequant8_bf16(q[si][j][qq], sc), acc[si]);
+        }
+      }
+    }
+  }
+};
+
+template <int PH, bool kFP4A, bool XL>
+__device__ __forceinline__ void wave_gemm(const Operands& o, int nph, floatx4_t (&acc)[2]) {
+  Phase<PH, kFP4A, XL> A, B;
+  int p = 0;
+  if (nph & 1) {                 // an odd phase first, unpipelined
+    A.load(o, 0);
+    A.compute(o, 0, acc);
+    p = 1;
+  }
+  if (p < nph) {
+    A.load(o, PH * p);
+    B.load(o, PH * (p + 1));
+    for (; p + 2 < nph; p += 2) {
+      A.compute(o, PH * p, acc);
+      A.load(o, PH * (p + 2));
+      B.compute(o, PH * (p + 1), acc);
+      B.load(o, PH * (p + 3));
+    }
+    A.compute(o, PH * p, acc);
+    B.compute(o, PH * (p + 1), acc);
+  }
+}
+
+// Tiles of at most kXR rows take their bf16 activation rows from LDS (one
+// cooperative copy per workgroup instead of 4 loads per lane per chunk).
+constexpr int kXR = 4;
+
+// Copy `bytes` (a multiple of 16) of weight scales starting at byte `off` of
+// resource r into LDS, 16 bytes per lane per step.
+__device__ __forceinline__ void scales_to_lds(rsrc_t r, uint32_t off, uint32_t bytes,
+                                              uint8_t* lds) {
+  for (uint32_t v = threadIdx.x * 16; v < bytes; v += blockDim.x * 16)
+    *reinterpret_cast<u32x4_t*>(lds + v) = bload16(r, off + v, 0);
+}
+
+// gate_up: a workgroup (4 waves) owns one tile and 64 intermediate columns;
+// wave w owns columns i in [16 w, 16 w + 16) of them: 16 gate rows and 16 up
+// rows of W13 over the whole K = H.  The tile's 16-row subtiles run one after
+// the other (the second re-reads the weights, from L2): decode tiles mostly
+// have 1-3 rows and this keeps a single subtile's registers live.  SwiGLU in
+// registers, bf16 h stored in sorted row order.
+template <int PH, bool kFP4A>
+__global__ __launch_bounds__(256)
+__attribute__((amdgpu_waves_per_eu(MOE_GEMM_WAVES_PER_EU))) void gate_up_kernel(
+    const void* __restrict__ act, const uint8_t* __restrict__ act_scale,
+    const int32_t* __restrict__ sorted, const int32_t* __restrict__ offsets,
+    const int32_t* __restrict__ tiles, const int32_t* __restrict__ num_tiles,
+    const uint8_t* __restrict__ w13, const uint8_t* __restrict__ w13s, int T, int H, int I, int Kp,
+    int nsl, uint16_t* __restrict__ h) {
   TileInfo ti;
   if (!load_tile(tiles, num_tiles, offsets, blockIdx.x / nsl, &ti)) return;
   const int s = blockIdx.x % nsl;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int nl = lane & 15, g = lane >> 4;
   const int i = s * 64 + wave * 16 + nl;
-  const size_t rb = (size_t)H / 2, rs = (size_t)H / 32;
-  const size_t erow = (size_t)ti.expert * 2 * I;
-  const uint8_t* wg = w13 + (erow + i) * rb + 16 * g;
-  const uint8_t* wu = w13 + (erow + I + i) * rb + 16 * g;
-  const uint8_t* sg = w13s + (erow + i) * rs + g;
-  const uint8_t* su = w13s + (erow + I + i) * rs + g;
-
-  const uint16_t* xr[kMT];
-#pragma unroll
-  for (int mt = 0; mt < kMT; ++mt) {
-    const int m = min(16 * mt + nl, ti.rows - 1);          // padded rows reuse a valid row
-    const int tok = min((unsigned)(sorted[ti.row0 + m] / Kp), (unsigned)(T - 1));
-    xr[mt] = x + (size_t)tok * H + 32 * g;
+  const uint32_t rb = H / 2, rs = H / 32;
+  const size_t wbytes = (size_t)2 * I * rb, sbytes = (size_t)2 * I * rs;
+  extern __shared__ uint8_t lds_scales[];                  // [2][64 rows][rs]: gate, up
+  Operands o;
+  o.lds = lds_scales;
+  o.w = make_rsrc(w13 + ti.expert * wbytes, (uint32_t)wbytes);
+  o.wo[0] = i * rb + 16 * g;
+  o.wo[1] = (I + i) * rb + 16 * g;
+  o.lso[0] = (wave * 16 + nl) * rs + g;
+  o.lso[1] = (64 + wave * 16 + nl) * rs + g;
+  if (kFP4A) {
+    o.a = make_rsrc(act, (uint32_t)((size_t)T * rb));
+    o.as = make_rsrc(act_scale, (uint32_t)((size_t)T * rs));
+  } else {
+    o.a = make_rsrc(act, (uint32_t)((size_t)T * H * 2));
   }
-  const int mtn = (ti.rows + 15) / 16;
-
-  floatx4_t accg[kMT], accu[kMT];
-#pragma unroll
-  for (int mt = 0; mt < kMT; ++mt) accg[mt] = accu[mt] = (floatx4_t){0.f, 0.f, 0.f, 0.f};
-
-  for (int k0 = 0; k0 < H; k0 += 128) {
-    const u32x4_t qg = load16(wg + k0 / 2);
-    const u32x4_t qu = load16(wu + k0 / 2);
-    const float scg = e8m0_to_f32(sg[k0 / 32]);
-    const float scu = e8m0_to_f32(su[k0 / 32]);
-    bf16x8_t a[kMT][4];
-#pragma unroll
-    for (int mt = 0; mt < kMT; ++mt)
-      if (mt < mtn)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) a[mt][j] = load_bf16x8(xr[mt] + k0 + 8 * j);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const bf16x8_t bg = dequant8_bf16(qg[j], scg);
-      const bf16x8_t bu = dequant8_bf16(qu[j], scu);
-#pragma unroll
-      for (int mt = 0; mt < kMT; ++mt)
-        if (mt < mtn) {
-          accg[mt] = mfma_bf16_16x16x32(a[mt][j], bg, accg[mt]);
-          accu[mt] = mfma_bf16_16x16x32(a[mt][j], bu, accu[mt]);
-        }
+  {
+    const rsrc_t rsc = make_rsrc(w13s + ti.expert * sbytes, (uint32_t)sbytes);
+    scales_to_lds(rsc, (uint32_t)(s * 64) * rs, 64 * rs, lds_scales);
+    scales_to_lds(rsc, (uint32_t)(I + s * 64) * rs, 64 * rs, lds_scales + 64 * rs);
+  }
+  uint8_t* lds_x = lds_scales + 128 * rs;                  // [kXR rows][H] bf16 (small tiles)
+  const bool xl = !kFP4A && ti.rows <= kXR;
+  if (xl) {
+    const uint32_t rowb = (uint32_t)H * 2;
+    for (uint32_t v = threadIdx.x * 16; v < ti.rows * rowb; v += blockDim.x * 16) {
+      const uint32_t r = v / rowb;
+      const uint32_t tok = min((unsigned)(sorted[ti.row0 + r] / Kp), (unsigned)(T - 1));
+      *reinterpret_cast<u32x4_t*>(lds_x + v) = bload16(o.a, tok * rowb + (v - r * rowb), 0);
     }
   }
-
-#pragma unroll
-  for (int mt = 0; mt < kMT; ++mt)
+  __syncthreads();
+  const int mtn = (ti.rows + 15) / 16;
+  for (int mt = 0; mt < mtn; ++mt) {
+    const int m = 16 * mt + nl;
+    floatx4_t acc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+    if (xl) {
+      o.ldx = lds_x + min(m, kXR - 1) * H * 2 + 64 * g;
+      o.xvalid = m < ti.rows;
+      wave_gemm<PH, kFP4A, true>(o, H / 128 / PH, acc);
+    } else {
+      const uint32_t tok = min((unsigned)(sorted[ti.row0 + min(m, ti.rows - 1)] / Kp),
+                               (unsigned)(T - 1));
+      o.ao = m >= ti.rows ? kOutOfRange : (kFP4A ? tok * rb + 16 * g : tok * H * 2 + 64 * g);
+      o.aso = m >= ti.rows ? kOutOfRange : tok * rs + g;
+      wave_gemm<PH, kFP4A, false>(o, H / 128 / PH, acc);
+    }
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const int m = 16 * mt + 4 * g + r;
-      if (m < ti.rows)
-        h[(size_t)(ti.row0 + m) * I + i] = f32_to_bf16_rne(swiglu(accg[mt][r], accu[mt][r]));
+      const int mm = 16 * mt + 4 * g + r;
+      if (mm < ti.rows)
+        h[(size_t)(ti.row0 + mm) * I + i] = f32_to_bf16_rne(swiglu(acc[0][r], acc[1][r]));
     }
+  }
 }
 
-__global__ __launch_bounds__(256) void down_w4a16_kernel(
-    const uint16_t* __restrict__ h, const int32_t* __restrict__ offsets,
-    const int32_t* __restrict__ tiles, const int32_t* __restrict__ num_tiles,
-    const uint8_t* __restrict__ w2, const uint8_t* __restrict__ w2s, int H, int I, int nsl,
-    float* __restrict__ y) {
+// down: a workgroup (4 waves) owns one tile and 128 output columns j; wave w
+// owns [32 w, 32 w + 32) of them (two 16-row strips of W2) over K = I.  y is
+// stored as fp32 in sorted row order.
+template <int PH, bool kFP4A>
+__global__ __launch_bounds__(256)
+__attribute__((amdgpu_waves_per_eu(MOE_GEMM_WAVES_PER_EU))) void down_kernel(
+    const void* __restrict__ hin, const uint8_t* __restrict__ hscale,
+    const int32_t* __restrict__ offsets, const int32_t* __restrict__ tiles,
+    const int32_t* __restrict__ num_tiles, const uint8_t* __restrict__ w2,
+    const uint8_t* __restrict__ w2s, int A, int H, int I, int nsl, float* __restrict__ y) {
   TileInfo ti;
   if (!load_tile(tiles, num_tiles, offsets, blockIdx.x / nsl, &ti)) return;
   const int s = blockIdx.x % nsl;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int nl = lane & 15, g = lane >> 4;
   const int j0 = s * 128 + wave * 32 + nl;                 // strip 0; strip 1 is j0 + 16
-  const size_t rb = (size_t)I / 2, rs = (size_t)I / 32;
-  const size_t erow = (size_t)ti.expert * H;
-  const uint8_t* w0 = w2 + (erow + j0) * rb + 16 * g;
-  const uint8_t* w1 = w2 + (erow + j0 + 16) * rb + 16 * g;
-  const uint8_t* s0 = w2s + (erow + j0) * rs + g;
-  const uint8_t* s1 = w2s + (erow + j0 + 16) * rs + g;
-
-  const uint16_t* hr[kMT];
-#pragma unroll
-  for (int mt = 0; mt < kMT; ++mt) {
-    const int m = min(16 * mt + nl, ti.rows - 1);
-    hr[mt] = h + (size_t)(ti.row0 + m) * I + 32 * g;
+  const uint32_t rb = I / 2, rs = I / 32;
+  const size_t wbytes = (size_t)H * rb, sbytes = (size_t)H * rs;
+  extern __shared__ uint8_t lds_scales[];                  // [128 rows][rs]
+  Operands o;
+  o.lds = lds_scales;
+  o.w = make_rsrc(w2 + ti.expert * wbytes, (uint32_t)wbytes);
+  o.wo[0] = j0 * rb + 16 * g;
+  o.wo[1] = (j0 + 16) * rb + 16 * g;
+  o.lso[0] = (wave * 32 + nl) * rs + g;
+  o.lso[1] = (wave * 32 + 16 + nl) * rs + g;
+  if (kFP4A) {
+    o.a = make_rsrc(hin, (uint32_t)((size_t)A * rb));
+    o.as = make_rsrc(hscale, (uint32_t)((size_t)A * rs));
+  } else {
+    o.a = make_rsrc(hin, (uint32_t)((size_t)A * I * 2));
   }
+  scales_to_lds(make_rsrc(w2s + ti.expert * sbytes, (uint32_t)sbytes), (uint32_t)(s * 128) * rs,
+                128 * rs, lds_scales);
+  uint8_t* lds_x = lds_scales + 128 * rs;                  // [kXR rows][I] bf16 (small tiles)
+  const bool xl = !kFP4A && ti.rows <= kXR;
+  if (xl) {
+    const uint32_t rowb = (uint32_t)I * 2;
+    for (uint32_t v = threadIdx.x * 16; v < ti.rows * rowb; v += blockDim.x * 16)
+      *reinterpret_cast<u32x4_t*>(lds_x + v) = bload16(o.a, ti.row0 * rowb + v, 0);
+  }
+  __syncthreads();
   const int mtn = (ti.rows + 15) / 16;
-
-  floatx4_t acc0[kMT], acc1[kMT];
-#pragma unroll
-  for (int mt = 0; mt < kMT; ++mt) acc0[mt] = acc1[mt] = (floatx4_t){0.f, 0.f, 0.f, 0.f};
-
-  for (int k0 = 0; k0 < I; k0 += 128) {
-    const u32x4_t q0 = load16(w0 + k0 / 2);
-    const u32x4_t q1 = load16(w1 + k0 / 2);
-    const float sc0 = e8m0_to_f32(s0[k0 / 32]);
-    const float sc1 = e8m0_to_f32(s1[k0 / 32]);
-    bf16x8_t a[kMT][4];
-#pragma unroll
-    for (int mt = 0; mt < kMT; ++mt)
-      if (mt < mtn)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) a[mt][j] = load_bf16x8(hr[mt] + k0 + 8 * j);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const bf16x8_t b0 = dequant8_bf16(q0[j], sc0);
-      const bf16x8_t b1 = dequant8_bf16(q1[j], sc1);
-#pragma unroll
-      for (int mt = 0; mt < kMT; ++mt)
-        if (mt < mtn) {
-          acc0[mt] = mfma_bf16_16x16x32(a[mt][j], b0, acc0[mt]);
-          acc1[mt] = mfma_bf16_16x16x32(a[mt][j], b1, acc1[mt]);
-        }
+  for (int mt = 0; mt < mtn; ++mt) {
+    const int m = 16 * mt + nl;
+    floatx4_t acc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+    if (xl) {
+      o.ldx = lds_x + min(m, kXR - 1) * I * 2 + 64 * g;
+      o.xvalid = m < ti.rows;
+      wave_gemm<PH, kFP4A, true>(o, I / 128 / PH, acc);
+    } else {
+      const uint32_t row = ti.row0 + m;
+      o.ao = m >= ti.rows ? kOutOfRange : (kFP4A ? row * rb + 16 * g : row * I * 2 + 64 * g);
+      o.aso = m >= ti.rows ? kOutOfRange : row * rs + g;
+      wave_gemm<PH, kFP4A, false>(o, I / 128 / PH, acc);
     }
-  }
-
-#pragma unroll
-  for (int mt = 0; mt < kMT; ++mt)
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const int m = 16 * mt + 4 * g + r;
-      if (m < ti.rows) {
-        float* yr = y + (size_t)(ti.row0 + m) * H;
-        yr[j0] = acc0[mt][r];
-        yr[j0 + 16] = acc1[mt][r];
+      const int mm = 16 * mt + 4 * g + r;
+      if (mm < ti.rows) {
+        float* yr = y + (size_t)(ti.row0 + mm) * H;
+        yr[j0] = acc[0][r];
+        yr[j0 + 16] = acc[1][r];
       }
     }
-}
-
-// ----------------------------------------------------------------- W4A4 ----
-
-__global__ __launch_bounds__(256) void gate_up_w4a4_kernel(
-    const uint8_t* __restrict__ xq, const uint8_t* __restrict__ xs,
-    const int32_t* __restrict__ sorted, const int32_t* __restrict__ offsets,
-    const int32_t* __restrict__ tiles, const int32_t* __restrict__ num_tiles,
-    const uint8_t* __restrict__ w13, const uint8_t* __restrict__ w13s, int T, int H, int I,
-    int Kp, int nsl, uint16_t* __restrict__ h) {
-  TileInfo ti;
-  if (!load_tile(tiles, num_tiles, offsets, blockIdx.x / nsl, &ti)) return;
-  const int s = blockIdx.x % nsl;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int nl = lane & 15, g = lane >> 4;
-  const int i = s * 64 + wave * 16 + nl;
-  const size_t rb = (size_t)H / 2, rs = (size_t)H / 32;
-  const size_t erow = (size_t)ti.expert * 2 * I;
-  const uint8_t* wg = w13 + (erow + i) * rb + 16 * g;
-  const uint8_t* wu = w13 + (erow + I + i) * rb + 16 * g;
-  const uint8_t* sg = w13s + (erow + i) * rs + g;
-  const uint8_t* su = w13s + (erow + I + i) * rs + g;
-
-  const uint8_t* ar[kMT];
-  const uint8_t* asr[kMT];
-#pragma unroll
-  for (int mt = 0; mt < kMT; ++mt) {
-    const int m = min(16 * mt + nl, ti.rows - 1);
-    const int tok = min((unsigned)(sorted[ti.row0 + m] / Kp), (unsigned)(T - 1));
-    ar[mt] = xq + (size_t)tok * rb + 16 * g;
-    asr[mt] = xs + (size_t)tok * rs + g;
   }
-  const int mtn = (ti.rows + 15) / 16;
-
-  floatx4_t accg[kMT], accu[kMT];
-#pragma unroll
-  for (int mt = 0; mt < kMT; ++mt) accg[mt] = accu[mt] = (floatx4_t){0.f, 0.f, 0.f, 0.f};
-
-  for (int k0 = 0; k0 < H; k0 += 128) {
-    const u32x4_t qg = load16(wg + k0 / 2);
-    const u32x4_t qu = load16(wu + k0 / 2);
-    const uint32_t scg = sg[k0 / 32];
-    const uint32_t scu = su[k0 / 32];
-#pragma unroll
-    for (int mt = 0; mt < kMT; ++mt)
-      if (mt < mtn) {
-        const u32x4_t qa = load16(ar[mt] + k0 / 2);
-        const uint32_t sa = asr[mt][k0 / 32];
-        accg[mt] = mfma_fp4_16x16x128(qa, sa, qg, scg, accg[mt]);
-        accu[mt] = mfma_fp4_16x16x128(qa, sa, qu, scu, accu[mt]);
-      }
-  }
-
-#pragma unroll
-  for (int mt = 0; mt < kMT; ++mt)
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int m = 16 * mt + 4 * g + r;
-      if (m < ti.rows)
-        h[(size_t)(ti.row0 + m) * I + i] = f32_to_bf16_rne(swiglu(accg[mt][r], accu[mt][r]));
-    }
-}
-
-__global__ __launch_bounds__(256) void down_w4a4_kernel(
-    const uint8_t* __restrict__ hq, const uint8_t* __restrict__ hs,
-    const int32_t* __restrict__ offsets, const int32_t* __restrict__ tiles,
-    const int32_t* __restrict__ num_tiles, const uint8_t* __restrict__ w2,
-    const uint8_t* __restrict__ w2s, int H, int I, int nsl, float* __restrict__ y) {
-  TileInfo ti;
-  if (!load_tile(tiles, num_tiles, offsets, blockIdx.x / nsl, &ti)) return;
-  const int s = blockIdx.x % nsl;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int nl = lane & 15, g = lane >> 4;
-  const int j0 = s * 128 + wave * 32 + nl;
-  const size_t rb = (size_t)I / 2, rs = (size_t)I / 32;
-  const size_t erow = (size_t)ti.expert * H;
-  const uint8_t* w0 = w2 + (erow + j0) * rb + 16 * g;
-  const uint8_t* w1 = w2 + (erow + j0 + 16) * rb + 16 * g;
-  const uint8_t* s0 = w2s + (erow + j0) * rs + g;
-  const uint8_t* s1 = w2s + (erow + j0 + 16) * rs + g;
-
-  const uint8_t* ar[kMT];
-  const uint8_t* asr[kMT];
-#pragma unroll
-  for (int mt = 0; mt < kMT; ++mt) {
-    const int m = min(16 * mt + nl, ti.rows - 1);
-    ar[mt] = hq + (size_t)(ti.row0 + m) * rb + 16 * g;
-    asr[mt] = hs + (size_t)(ti.row0 + m) * rs + g;
-  }
-  const int mtn = (ti.rows + 15) / 16;
-
-  floatx4_t acc0[kMT], acc1[kMT];
-#pragma unroll
-  for (int mt = 0; mt < kMT; ++mt) acc0[mt] = acc1[mt] = (floatx4_t){0.f, 0.f, 0.f, 0.f};
-
-  for (int k0 = 0; k0 < I; k0 += 128) {
-    const u32x4_t q0 = load16(w0 + k0 / 2);
-    const u32x4_t q1 = load16(w1 + k0 / 2);
-    const uint32_t sc0 = s0[k0 / 32];
-    const uint32_t sc1 = s1[k0 / 32];
-#pragma unroll
-    for (int mt = 0; mt < kMT; ++mt)
-      if (mt < mtn) {
-        const u32x4_t qa = load16(ar[mt] + k0 / 2);
-        const uint32_t sa = asr[mt][k0 / 32];
-        acc0[mt] = mfma_fp4_16x16x128(qa, sa, q0, sc0, acc0[mt]);
-        acc1[mt] = mfma_fp4_16x16x128(qa, sa, q1, sc1, acc1[mt]);
-      }
-  }
-
-#pragma unroll
-  for (int mt = 0; mt < kMT; ++mt)
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int m = 16 * mt + 4 * g + r;
-      if (m < ti.rows) {
-        float* yr = y + (size_t)(ti.row0 + m) * H;
-        yr[j0] = acc0[mt][r];
-        yr[j0 + 16] = acc1[mt][r];
-      }
-    }
 }
 
 // -------------------------------------------------------------- combine ----
@@ -329,35 +345,72 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
 
 int expert_gemm_tile_m() { return kTileM; }
 
+// Phase width (chunks of 128 K-elements per pipeline stage): 2 when the chunk
+// count is even, else 1.
+int expert_gemm_phase(int nch) { return (MOE_GEMM_PH_MAX >= 2 && nch % 2 == 0) ? 2 : 1; }
+
+namespace {
+template <int PH, bool kFP4A>
+struct GateUpLaunch {
+  static hipError_t run(dim3 grid, hipStream_t stream, const void* act, const uint8_t* act_scale,
+                        const int32_t* sorted, const int32_t* offsets, const int32_t* tiles,
+                        const int32_t* num_tiles, const uint8_t* w13, const uint8_t* w13s, int T,
+                        int H, int I, int Kp, int nsl, uint16_t* h) {
+    const size_t lds = (size_t)128 * (H / 32) + (kFP4A ? 0 : (size_t)kXR * H * 2);
+    hipLaunchKernelGGL((gate_up_kernel<PH, kFP4A>), grid, dim3(256), lds, stream,
+                       act, act_scale,
+                       sorted, offsets, tiles, num_tiles, w13, w13s, T, H, I, Kp, nsl, h);
+    return hipGetLastError();
+  }
+};
+
+template <int PH, bool kFP4A>
+struct DownLaunch {
+  static hipError_t run(dim3 grid, hipStream_t stream, const void* hin, const uint8_t* hscale,
+                        const int32_t* offsets, const int32_t* tiles, const int32_t* num_tiles,
+                        const uint8_t* w2, const uint8_t* w2s, int A, int H, int I, int nsl,
+                        float* y) {
+    const size_t lds = (size_t)128 * (I / 32) + (kFP4A ? 0 : (size_t)kXR * I * 2);
+    hipLaunchKernelGGL((down_kernel<PH, kFP4A>), grid, dim3(256), lds, stream,
+                       hin, hscale, offsets,
+                       tiles, num_tiles, w2, w2s, A, H, I, nsl, y);
+    return hipGetLastError();
+  }
+};
+
+template <template <int, bool> class Launch, bool kFP4A, typename... Args>
+hipError_t dispatch_ph(int ph, Args... args) {
+  return ph == 2 ? Launch<2, kFP4A>::run(args...) : Launch<1, kFP4A>::run(args...);
+}
+}  // namespace
+
 hipError_t launch_gate_up(int act_fmt, const void* act, const uint8_t* act_scale,
                           const int32_t* sorted, const int32_t* offsets, const int32_t* tiles,
                           const int32_t* num_tiles, int max_tiles, const uint8_t* w13,
                           const uint8_t* w13s, int T, int H, int I, int Kp, uint16_t* h,
                           hipStream_t stream) {
   const int nsl = I / 64;
-  dim3 grid((unsigned)(max_tiles * nsl)), block(256);
+  const int ph = expert_gemm_phase(H / 128);
+  dim3 grid((unsigned)(max_tiles * nsl));
   if (act_fmt == 0)
-    hipLaunchKernelGGL(gate_up_w4a16_kernel, grid, block, 0, stream, (const uint16_t*)act, sorted,
-                       offsets, tiles, num_tiles, w13, w13s, T, H, I, Kp, nsl, h);
-  else
-    hipLaunchKernelGGL(gate_up_w4a4_kernel, grid, block, 0, stream, (const uint8_t*)act, act_scale,
-                       sorted, offsets, tiles, num_tiles, w13, w13s, T, H, I, Kp, nsl, h);
-  return hipGetLastError();
+    return dispatch_ph<GateUpLaunch, false>(ph, grid, stream, act, act_scale, sorted, offsets,
+                                            tiles, num_tiles, w13, w13s, T, H, I, Kp, nsl, h);
+  return dispatch_ph<GateUpLaunch, true>(ph, grid, stream, act, act_scale, sorted, offsets, tiles,
+                                         num_tiles, w13, w13s, T, H, I, Kp, nsl, h);
 }
 
 hipError_t launch_down(int act_fmt, const void* h, const uint8_t* h_scale, const int32_t* offsets,
                        const int32_t* tiles, const int32_t* num_tiles, int max_tiles,
-                       const uint8_t* w2, const uint8_t* w2s, int H, int I, float* y,
+                       const uint8_t* w2, const uint8_t* w2s, int A, int H, int I, float* y,
                        hipStream_t stream) {
   const int nsl = H / 128;
-  dim3 grid((unsigned)(max_tiles * nsl)), block(256);
+  const int ph = expert_gemm_phase(I / 128);
+  dim3 grid((unsigned)(max_tiles * nsl));
   if (act_fmt == 0)
-    hipLaunchKernelGGL(down_w4a16_kernel, grid, block, 0, stream, (const uint16_t*)h, offsets, tiles,
-                       num_tiles, w2, w2s, H, I, nsl, y);
-  else
-    hipLaunchKernelGGL(down_w4a4_kernel, grid, block, 0, stream, (const uint8_t*)h, h_scale, offsets,
-                       tiles, num_tiles, w2, w2s, H, I, nsl, y);
-  return hipGetLastError();
+    return dispatch_ph<DownLaunch, false>(ph, grid, stream, h, h_scale, offsets, tiles, num_tiles,
+                                          w2, w2s, A, H, I, nsl, y);
+  return dispatch_ph<DownLaunch, true>(ph, grid, stream, h, h_scale, offsets, tiles, num_tiles, w2,
+                                       w2s, A, H, I, nsl, y);
 }
 
 hipError_t launch_combine(const float* y, const float* w, const int32_t* inv, int T, int H, int Kp,

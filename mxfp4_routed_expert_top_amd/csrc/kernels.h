@@ -17,6 +17,7 @@ hipError_t launch_mxfp4_quant(const void* src, int src_is_bf16, int64_t rows, in
                               uint8_t* packed, uint8_t* scales, hipStream_t stream);
 
 int expert_gemm_tile_m();
+int expert_gemm_phase(int nch);
 hipError_t launch_gate_up(int act_fmt, const void* act, const uint8_t* act_scale,
                           const int32_t* sorted, const int32_t* offsets, const int32_t* tiles,
                           const int32_t* num_tiles, int max_tiles, const uint8_t* w13,
@@ -24,7 +25,7 @@ hipError_t launch_gate_up(int act_fmt, const void* act, const uint8_t* act_scale
                           hipStream_t stream);
 hipError_t launch_down(int act_fmt, const void* h, const uint8_t* h_scale, const int32_t* offsets,
                        const int32_t* tiles, const int32_t* num_tiles, int max_tiles,
-                       const uint8_t* w2, const uint8_t* w2s, int H, int I, float* y,
+                       const uint8_t* w2, const uint8_t* w2s, int A, int H, int I, float* y,
                        hipStream_t stream);
 hipError_t launch_combine(const float* y, const float* w, const int32_t* inv, int T, int H, int Kp,
                           uint16_t* out, hipStream_t stream);

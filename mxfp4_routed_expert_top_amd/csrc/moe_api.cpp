@@ -176,7 +176,7 @@ moe_status moe_expert_down(const void* h, const uint8_t* h_scale, int32_t act_fm
   const int64_t mt = max_tiles_for((int64_t)T * Kp, Ep);
   if (mt * (H / 128) >= INT32_MAX) return MOE_ERR_UNSUPPORTED;
   return from_hip(launch_down(act_fmt, h, h_scale, expert_offsets, tile_table, num_tiles, (int)mt,
-                              w2, w2_scale, H, I, y, as_stream(stream)));
+                              w2, w2_scale, T * Kp, H, I, y, as_stream(stream)));
 }
 
 moe_status moe_combine(const float* y, const float* topk_weights, const int32_t* inv_assign,
@@ -246,7 +246,7 @@ moe_status moe_mxfp4_forward(const uint16_t* x, const float* router_logits,
     e = launch_gate_up(0, x, nullptr, sorted, offsets, tiles, ntiles, mt, w13, w13_scale, T, H, I,
                        Kp, h, s);
     if (e != hipSuccess) return MOE_ERR_DEVICE;
-    e = launch_down(0, h, nullptr, offsets, tiles, ntiles, mt, w2, w2_scale, H, I, y, s);
+    e = launch_down(0, h, nullptr, offsets, tiles, ntiles, mt, w2, w2_scale, (int)A, H, I, y, s);
   } else {
     e = launch_mxfp4_quant(x, 1, T, H, xq, xs, s);
     if (e != hipSuccess) return MOE_ERR_DEVICE;
@@ -255,7 +255,7 @@ moe_status moe_mxfp4_forward(const uint16_t* x, const float* router_logits,
     if (e != hipSuccess) return MOE_ERR_DEVICE;
     e = launch_mxfp4_quant(h, 1, A, I, hq, hs, s);
     if (e != hipSuccess) return MOE_ERR_DEVICE;
-    e = launch_down(1, hq, hs, offsets, tiles, ntiles, mt, w2, w2_scale, H, I, y, s);
+    e = launch_down(1, hq, hs, offsets, tiles, ntiles, mt, w2, w2_scale, (int)A, H, I, y, s);
   }
   if (e != hipSuccess) return MOE_ERR_DEVICE;
   return from_hip(launch_combine(y, wts, inv, T, H, Kp, out, s));
