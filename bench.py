@@ -35,7 +35,7 @@ def parse():
     p.add_argument("--steps", type=int, default=50)
     p.add_argument("--warmup", type=int, default=10)
     p.add_argument("--workload", default="decode", choices=list(synth.CONFIGS))
-    p.add_argument("--cpu-tokens", type=int, default=3,
+    p.add_argument("--cpu-tokens", type=int, default=32,
                    help="tokens of the batch the CPU oracle is timed on")
     p.add_argument("--no-cpu", action="store_true", help="skip the cpu_baseline leg")
     return p.parse_args()
@@ -76,32 +76,46 @@ def algorithmic(cfg, counts):
                 flops=cfg.A * 6 * cfg.H * cfg.I, gate_up_flops=cfg.A * 4 * cfg.H * cfg.I)
 
 
-def cpu_baseline(cfg, w13_dev_fn, n_tokens):
-    """Time the oracle (as it stands) on n_tokens of the batch."""
-    from oracle import moe, mxfp4
-    from threadpoolctl import threadpool_info
+def _pack_expert(args):
+    """Draw one expert's float weights on the CPU and pack them with the
+    oracle's quantiser (input preparation for the cpu_baseline leg)."""
+    from oracle import mxfp4
+    cfg, e = args
+    torch.set_num_threads(1)
+    a = mxfp4.quantize(synth.expert_w13(cfg, e).double().numpy())
+    b = mxfp4.quantize(synth.expert_w2(cfg, e).double().numpy())
+    return e, (a[0], a[1], b[0], b[1])
+
+
+def cpu_baseline(cfg, n_tokens):
+    """Time the oracle, as it stands, on the first n_tokens tokens of the
+    batch (route + align over all tokens, expert MLPs + combine for the
+    sample), single-threaded.  Its weights are the same distribution drawn on
+    the CPU and packed beforehand by the oracle's own quantiser in a process
+    pool (not timed)."""
+    import multiprocessing as mp
+    from threadpoolctl import threadpool_limits
+    from oracle import moe
     x_bits = synth.activations(cfg).view(torch.int16).numpy().view(np.uint16)
     logits = synth.router_logits(cfg).numpy()
     gate = synth.gate_logits(cfg)
     gate = None if gate is None else gate.numpy()
-    tokens = np.arange(n_tokens)
+    tokens = np.arange(min(n_tokens, cfg.T))
     ids, _ = moe.route(logits, gate, cfg.K, cfg.shared)
     need = sorted(set(ids[tokens].reshape(-1).tolist()))
-    log(f"cpu_baseline: packing {len(need)} experts with the oracle's quantiser")
-    packed = {}
-    for e in need:
-        a = mxfp4.quantize(synth.expert_w13(cfg, e, "cuda").cpu().double().numpy())
-        b = mxfp4.quantize(synth.expert_w2(cfg, e, "cuda").cpu().double().numpy())
-        packed[e] = (a[0], a[1], b[0], b[1])
-    t0 = time.perf_counter()
-    moe.forward(x_bits, logits, gate, lambda e: packed[e], cfg.I, cfg.E, cfg.K, cfg.shared,
-                cfg.act_fmt, tokens=tokens)
-    dt = time.perf_counter() - t0
-    blas = [p.get("num_threads", 1) for p in threadpool_info() if p.get("user_api") == "blas"]
-    return {"value": n_tokens / dt, "unit": "tokens/s", "cores": max(blas + [1]),
-            "kind": "oracle", "seconds": dt,
-            "sample": f"first {n_tokens} of the {cfg.T} tokens ({len(need)} experts), "
-                      "routing and grouping over all tokens; numpy fp64, BLAS threads = cores"}
+    procs = max(1, min(16, len(os.sched_getaffinity(0))))
+    log(f"cpu_baseline: packing {len(need)} experts with the oracle's quantiser ({procs} procs)")
+    with mp.get_context("spawn").Pool(procs) as pool:
+        packed = dict(pool.map(_pack_expert, [(cfg, e) for e in need], chunksize=4))
+    with threadpool_limits(1):
+        t0 = time.perf_counter()
+        moe.forward(x_bits, logits, gate, lambda e: packed[e], cfg.I, cfg.E, cfg.K, cfg.shared,
+                    cfg.act_fmt, tokens=tokens)
+        dt = time.perf_counter() - t0
+    return {"value": round(len(tokens) / dt, 3), "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "seconds": round(dt, 2),
+            "sample": f"{len(tokens)} of the batch's {cfg.T} tokens ({len(need)} experts decoded); "
+                      "numpy fp64 oracle on one host core"}
 
 
 def main():
@@ -116,11 +130,17 @@ def main():
         f"shared={cfg.shared} act={'mxfp4' if cfg.act_fmt else 'bf16'}")
     x, logits, gate, w13, w13s, w2, w2s = make_inputs(cfg)
     bufs = ops.alloc_stages(cfg.T, cfg.H, cfg.I, cfg.E, cfg.K, cfg.shared, cfg.act_fmt, "cuda")
-    names = ["route", "align", "gate_up", "down", "combine"]
-    if cfg.act_fmt == ops.ACT_MXFP4:
-        names += ["quant_x", "quant_h"]
+    ws = torch.empty(ops.workspace_size(cfg.T, cfg.H, cfg.I, cfg.E, cfg.K, cfg.shared, cfg.act_fmt),
+                     dtype=torch.uint8, device="cuda")
+    out = torch.empty(cfg.T, cfg.H, dtype=torch.bfloat16, device="cuda")
+    stream = torch.cuda.current_stream()
 
-    def step(events=None):
+    def step():
+        # the whole layer, one C call: route, align, [quant x], gate/up+SwiGLU, [quant h], down, combine
+        ops.mxfp4_forward(x, logits, gate, w13, w13s, w2, w2s, cfg.I, cfg.E, cfg.K, cfg.shared,
+                          cfg.act_fmt, out=out, workspace=ws)
+
+    def step_stages(events):
         ops.forward_stages(x, logits, gate, w13, w13s, w2, w2s, cfg.I, cfg.E, cfg.K, cfg.shared,
                            cfg.act_fmt, bufs=bufs, events=events)
 
@@ -129,17 +149,31 @@ def main():
     torch.cuda.synchronize()
     log("warmup done")
 
-    ev = [{n: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for n in names} for _ in range(args.steps)]
+    # timed region 1: whole-layer throughput (no events inside the steps)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for i in range(args.steps):
-        step(ev[i])
+    for _ in range(args.steps):
+        step()
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms = (t1 - t0) * 1e3 / args.steps
+
+    # timed region 2: the same pass stage by stage, HIP events on the launch
+    # stream around the GEMM kernels (the dominant ones) for their durations
+    names = ["gate_up", "down"]
+    ev = [{n: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for n in names} for _ in range(args.steps)]
+    for _ in range(2):
+        step_stages(None)
+    torch.cuda.synchronize()
+    for i in range(args.steps):
+        step_stages(ev[i])
+    torch.cuda.synchronize()
     stage_ms = {n: float(np.mean([e[n][0].elapsed_time(e[n][1]) for e in ev])) for n in names}
-    log("stage ms:", json.dumps({k: round(v, 4) for k, v in stage_ms.items()}))
+    log("kernel ms:", json.dumps({k: round(v, 4) for k, v in stage_ms.items()}),
+        "step ms:", round(ms, 4))
+    if not torch.equal(out, bufs["out"]):
+        raise RuntimeError("one-call forward and per-stage pass disagree")
 
     counts = bufs["align"]["counts"].cpu().numpy()
     alg = algorithmic(cfg, counts)
@@ -151,13 +185,15 @@ def main():
                 "kernel": "gate_up_w4a16_kernel" if cfg.act_fmt == 0 else "gate_up_w4a4_kernel",
                 "algorithmic_bytes": alg["w13_bytes"], "kernel_ms": round(stage_ms["gate_up"], 4)}
     layer = {"bytes": alg["layer_bytes"], "flops": alg["flops"], "touched_experts": alg["touched"],
+             "hbm_gbs": round(alg["layer_bytes"] / layer_s / 1e9, 1),
              "hbm_frac": round(alg["layer_bytes"] / layer_s / 1e9 / HBM_PEAK_GBS, 4),
              "mxfp4_mfma_frac": round(alg["flops"] / layer_s / 1e12 / MXFP4_PEAK_TFLOPS, 5),
              "bf16_mfma_frac": round(alg["flops"] / layer_s / 1e12 / BF16_PEAK_TFLOPS, 5),
-             "stage_ms": {k: round(v, 4) for k, v in stage_ms.items()}}
+             "kernel_ms": {k: round(v, 4) for k, v in stage_ms.items()},
+             "down_gbs": round(alg["w2_bytes"] / (stage_ms["down"] / 1e3) / 1e9, 1)}
     cpu = None
     if not args.no_cpu:
-        cpu = cpu_baseline(cfg, None, args.cpu_tokens)
+        cpu = cpu_baseline(cfg, args.cpu_tokens)
     res = {"metric": METRIC, "value": round(cfg.T / layer_s, 1), "unit": "tokens/s",
            "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
            "higher_is_better": True, "scaling": "weak", "vs_baseline": None,

@@ -6,12 +6,15 @@
 // InferenceX Qwen3.5 post's shared-expert bullet: one MoE dispatch covers
 // the routed experts and the shared one).
 //
-// Three launches over chunks of kChunk assignments:
+// Up to kSmallA assignments: one workgroup does everything in LDS.  Beyond:
+// three launches over chunks of kChunk assignments:
 //   1. per-chunk histograms            hist[b][e]
 //   2. one block: column scans over chunks, the exclusive scan over experts
 //      (offsets), per-chunk base positions and the tile table
 //   3. per-chunk stable scatter: inside a chunk, wave by wave in order, each
 //      lane's rank among the earlier lanes with the same expert
+// A lane's rank among equal experts in its wave comes from ballots: one
+// round per distinct expert in the wave (at most 64), no data exchange.
 #include "common.h"
 #include "kernels.h"
 
@@ -19,6 +22,26 @@ namespace {
 
 constexpr int kChunk = 2048;      // assignments per block in passes 1 and 3
 constexpr int kScanThreads = 1024;
+constexpr int kSmallA = 8192;     // single-workgroup path up to this many assignments
+
+// Rank of this lane among the lanes of its wave holding the same expert e
+// (lower lanes first) and the number of such lanes; e < 0 takes no part.
+__device__ __forceinline__ void wave_match_rank(int e, int* rank, int* same) {
+  const int lane = threadIdx.x & 63;
+  uint64_t todo = __ballot(e >= 0);
+  *rank = 0;
+  *same = 0;
+  while (todo) {
+    const int leader = __ffsll((unsigned long long)todo) - 1;
+    const int el = __builtin_amdgcn_readlane(e, leader);
+    const uint64_t m = __ballot(e == el);
+    if (e == el) {
+      *rank = __popcll(m & ((1ull << lane) - 1ull));
+      *same = __popcll(m);
+    }
+    todo &= ~m;
+  }
+}
 
 __global__ __launch_bounds__(256) void align_hist_kernel(const int32_t* __restrict__ ids, int A,
                                                          int Ep, int32_t* __restrict__ hist) {
@@ -113,26 +136,88 @@ __global__ __launch_bounds__(256) void align_scatter_kernel(
   extern __shared__ int32_t pos[];
   for (int e = threadIdx.x; e < Ep; e += blockDim.x) pos[e] = base[(size_t)blockIdx.x * Ep + e];
   __syncthreads();
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wave = threadIdx.x >> 6;
   const int a0 = blockIdx.x * kChunk;
-  for (int r = 0; r < kChunk; r += 256) {
-    const int a = a0 + r + threadIdx.x;
+  const int a1 = min(A, a0 + kChunk);
+  for (int r = a0; r < a1; r += 256) {
+    const int a = r + threadIdx.x;
     int e = (a < A) ? ids[a] : -1;
     if ((unsigned)e >= (unsigned)Ep) e = -1;
-    int rank = 0, same = 0;
-    for (int j = 0; j < 64; ++j) {
-      int ej = __shfl(e, j, MOE_WAVE);
-      if (ej == e) {
-        same++;
-        if (j < lane) rank++;
-      }
-    }
+    int rank, same;
+    wave_match_rank(e, &rank, &same);
     for (int w = 0; w < 4; ++w) {
       if (w == wave && e >= 0) {
         int p = pos[e] + rank;
         sorted[p] = a;
         if (inv) inv[a] = p;
         if (rank == same - 1) pos[e] = p + 1;    // the last lane of this expert advances it
+      }
+      __syncthreads();
+    }
+  }
+}
+
+
+// Everything for A <= kSmallA in one workgroup of kScanThreads threads.
+__global__ __launch_bounds__(kScanThreads) void align_small_kernel(
+    const int32_t* __restrict__ ids, int A, int Ep, int tile_m, int32_t* __restrict__ counts,
+    int32_t* __restrict__ offsets, int32_t* __restrict__ sorted, int32_t* __restrict__ inv,
+    int32_t* __restrict__ tiles, int32_t* __restrict__ num_tiles) {
+  extern __shared__ int32_t sh[];          // cnt[Ep], then pos[Ep]
+  __shared__ int tmp[17];
+  int32_t* cnt = sh;
+  int32_t* pos = sh + Ep;
+  for (int e = threadIdx.x; e < Ep; e += blockDim.x) cnt[e] = 0;
+  __syncthreads();
+  for (int a = threadIdx.x; a < A; a += blockDim.x) {
+    const int e = ids[a];
+    if ((unsigned)e < (unsigned)Ep) atomicAdd(&cnt[e], 1);
+  }
+  __syncthreads();
+  int c[2] = {0, 0};
+  for (int q = 0; q < 2; ++q) {
+    const int e = 2 * threadIdx.x + q;
+    if (e < Ep) c[q] = cnt[e];
+  }
+  int total;
+  const int base = block_exclusive_scan(c[0] + c[1], tmp, &total);
+  const int off[2] = {base, base + c[0]};
+  const int nt[2] = {(c[0] + tile_m - 1) / tile_m, (c[1] + tile_m - 1) / tile_m};
+  int ttotal;
+  const int tbase = block_exclusive_scan(nt[0] + nt[1], tmp, &ttotal);
+  const int toff[2] = {tbase, tbase + nt[0]};
+  for (int q = 0; q < 2; ++q) {
+    const int e = 2 * threadIdx.x + q;
+    if (e < Ep) {
+      counts[e] = c[q];
+      offsets[e] = off[q];
+      pos[e] = off[q];
+      if (tiles)
+        for (int j = 0; j < nt[q]; ++j) {
+          tiles[2 * (toff[q] + j)] = e;
+          tiles[2 * (toff[q] + j) + 1] = off[q] + j * tile_m;
+        }
+    }
+  }
+  if (threadIdx.x == 0) {
+    offsets[Ep] = A;
+    *num_tiles = ttotal;
+  }
+  __syncthreads();
+  const int wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
+  for (int r = 0; r < A; r += blockDim.x) {
+    const int a = r + threadIdx.x;
+    int e = (a < A) ? ids[a] : -1;
+    if ((unsigned)e >= (unsigned)Ep) e = -1;
+    int rank, same;
+    wave_match_rank(e, &rank, &same);
+    const int nwr = min(nw, (A - r + 63) / 64);            // waves holding elements this round
+    for (int w = 0; w < nwr; ++w) {
+      if (w == wave && e >= 0) {
+        const int p = pos[e] + rank;
+        sorted[p] = a;
+        if (inv) inv[a] = p;
+        if (rank == same - 1) pos[e] = p + 1;
       }
       __syncthreads();
     }
@@ -149,14 +234,18 @@ size_t align_scratch_bytes(int A, int Ep) {
 hipError_t launch_align_sort(const int32_t* ids, int A, int Ep, int tile_m, int32_t* counts,
                              int32_t* offsets, int32_t* sorted, int32_t* inv, int32_t* tiles,
                              int32_t* num_tiles, int32_t* scratch, hipStream_t stream) {
+  if (A <= kSmallA) {
+    hipLaunchKernelGGL(align_small_kernel, dim3(1), dim3(kScanThreads),
+                       (size_t)2 * Ep * sizeof(int32_t), stream, ids, A, Ep, tile_m, counts, offsets,
+                       sorted, inv, tiles, num_tiles);
+    return hipGetLastError();
+  }
   const int nb = (A + kChunk - 1) / kChunk;
   const size_t lds = (size_t)Ep * sizeof(int32_t);
-  if (nb > 0)
-    hipLaunchKernelGGL(align_hist_kernel, dim3(nb), dim3(256), lds, stream, ids, A, Ep, scratch);
+  hipLaunchKernelGGL(align_hist_kernel, dim3(nb), dim3(256), lds, stream, ids, A, Ep, scratch);
   hipLaunchKernelGGL(align_scan_kernel, dim3(1), dim3(kScanThreads), 0, stream, scratch, nb, A, Ep,
                      tile_m, counts, offsets, tiles, num_tiles);
-  if (nb > 0)
-    hipLaunchKernelGGL(align_scatter_kernel, dim3(nb), dim3(256), lds, stream, ids, A, Ep, scratch,
-                       sorted, inv);
+  hipLaunchKernelGGL(align_scatter_kernel, dim3(nb), dim3(256), lds, stream, ids, A, Ep, scratch,
+                     sorted, inv);
   return hipGetLastError();
 }

@@ -30,15 +30,29 @@ __device__ __forceinline__ float key_value(uint64_t key) {
   return __uint_as_float(u);
 }
 
+// Wave-wide maximum of a 64-bit key held as (hi, lo), with DPP lane moves
+// (no LDS round trip): quad swaps, half-row and row mirrors, then row
+// broadcasts; lane 63 ends with the maximum, which is read back as a scalar.
+template <int CTRL, int ROWMASK>
+__device__ __forceinline__ void dpp_max_step(uint32_t& hi, uint32_t& lo) {
+  const uint32_t h2 = (uint32_t)__builtin_amdgcn_update_dpp((int)hi, (int)hi, CTRL, ROWMASK, 0xF, false);
+  const uint32_t l2 = (uint32_t)__builtin_amdgcn_update_dpp((int)lo, (int)lo, CTRL, ROWMASK, 0xF, false);
+  const bool gt = (h2 > hi) || (h2 == hi && l2 > lo);
+  hi = gt ? h2 : hi;
+  lo = gt ? l2 : lo;
+}
+
 __device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) {
-    uint32_t lo = __shfl_xor((unsigned)(v & 0xFFFFFFFFu), m, MOE_WAVE);
-    uint32_t hi = __shfl_xor((unsigned)(v >> 32), m, MOE_WAVE);
-    uint64_t o = ((uint64_t)hi << 32) | lo;
-    v = o > v ? o : v;
-  }
-  return v;
+  uint32_t hi = (uint32_t)(v >> 32), lo = (uint32_t)v;
+  dpp_max_step<0xB1, 0xF>(hi, lo);    // quad_perm [1,0,3,2]
+  dpp_max_step<0x4E, 0xF>(hi, lo);    // quad_perm [2,3,0,1]
+  dpp_max_step<0x141, 0xF>(hi, lo);   // row_half_mirror
+  dpp_max_step<0x140, 0xF>(hi, lo);   // row_mirror
+  dpp_max_step<0x142, 0xA>(hi, lo);   // row_bcast:15 into rows 1, 3
+  dpp_max_step<0x143, 0xC>(hi, lo);   // row_bcast:31 into rows 2, 3
+  hi = (uint32_t)__builtin_amdgcn_readlane((int)hi, 63);
+  lo = (uint32_t)__builtin_amdgcn_readlane((int)lo, 63);
+  return ((uint64_t)hi << 32) | lo;
 }
 
 __device__ __forceinline__ float wave_sum_f32(float v) {
@@ -63,7 +77,10 @@ __global__ __launch_bounds__(256) void route_topk_kernel(
     key[j] = (e < E) ? route_key(row[e], e) : 0ull;    // 0 = never selected
   }
 
-  float lmax = 0.f, sel_val = 0.f;
+  // K rounds: the wave-wide best key is the next slot; its owner retires it.
+  // Selected values are wave-uniform, so every lane accumulates the
+  // renormalised denominator itself, in slot order.
+  float lmax = 0.f, den = 0.f, num = 0.f;
   int sel_e = 0;
   for (int k = 0; k < K; ++k) {
     uint64_t best = 0ull;
@@ -78,15 +95,15 @@ __global__ __launch_bounds__(256) void route_topk_kernel(
         if (j == (e >> 6)) key[j] = 0ull;
     }
     if (k == 0) lmax = v;
-    if (lane == k) { sel_e = e; sel_val = v; }
+    const float ek = expf(v - lmax);
+    den += ek;
+    if (lane == k) {
+      sel_e = e;
+      num = ek;
+    }
   }
 
-  // Denominator: over the K selected (renormalised) or over all E.
-  float num = (lane < K) ? expf(sel_val - lmax) : 0.f;
-  float den;
-  if (renormalize) {
-    den = wave_sum_f32(num);
-  } else {
+  if (!renormalize) {
     float s = 0.f;
     for (int e = lane; e < E; e += 64) s += expf(row[e] - lmax);
     den = wave_sum_f32(s);

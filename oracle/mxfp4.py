@@ -77,13 +77,22 @@ def decode(packed: np.ndarray, scales: np.ndarray) -> np.ndarray:
 def _nearest_code_magnitude(mag: np.ndarray) -> np.ndarray:
     """Index 0..7 of the GRID value nearest to mag; on a tie between two grid
     values the even index (mantissa bit 0) wins.  Values above 6 land on 6,
-    which is the nearest grid value, so saturation needs no separate rule."""
-    dist = np.abs(mag[..., None] - GRID)
-    best = dist.min(axis=-1, keepdims=True)
-    cand = dist == best
-    even = cand & (np.arange(8) % 2 == 0)
-    has_even = even.any(axis=-1)
-    return np.where(has_even, even.argmax(axis=-1), cand.argmax(axis=-1)).astype(np.uint8)
+    which is the nearest grid value, so saturation needs no separate rule.
+    Brute force over the 8 candidates, keeping the best so far (elementwise;
+    evaluated in slices of 2^16 elements to stay in cache)."""
+    flat = mag.reshape(-1)
+    out = np.empty(flat.shape, dtype=np.uint8)
+    for lo in range(0, flat.size, 1 << 16):
+        m = flat[lo:lo + (1 << 16)]
+        best_code = np.zeros(m.shape, dtype=np.uint8)
+        best_dist = np.abs(m - GRID[0])
+        for c in range(1, 8):
+            d = np.abs(m - GRID[c])
+            take = (d < best_dist) | ((d == best_dist) & (c % 2 == 0))
+            np.putmask(best_code, take, c)
+            np.putmask(best_dist, take, d)
+        out[lo:lo + (1 << 16)] = best_code
+    return out.reshape(mag.shape)
 
 
 def quantize(v: np.ndarray):

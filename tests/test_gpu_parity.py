@@ -286,3 +286,32 @@ def test_layer_full_size_sampled(name):
     assert e_rel <= REL_L2[cfg.act_fmt]
     assert e_max <= MAX_ABS_RMS
     assert torch.isfinite(out.float()).all()
+
+
+def test_forward_capturable_in_hip_graph():
+    """The one-call forward only enqueues work on the caller's stream: captured
+    in a HIP graph, every replay (with eager work and synchronisations in
+    between) equals the eager result."""
+    prob = Problem(SMALL["ragged"])
+    c = prob.cfg
+    o = ops()
+    ws = torch.empty(o.workspace_size(c.T, c.H, c.I, c.E, c.K, c.shared, c.act_fmt),
+                     dtype=torch.uint8, device=DEV)
+    out = torch.empty(c.T, c.H, dtype=torch.bfloat16, device=DEV)
+    eager = bits(prob.forward())
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        prob.forward(out=out, workspace=ws)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=s):
+            prob.forward(out=out, workspace=ws)
+    torch.cuda.synchronize()
+    for rep in range(4):
+        out.fill_(0)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(bits(out), eager), f"replay {rep}"
+        prob.forward()                      # eager work between replays
+        torch.cuda.synchronize()
