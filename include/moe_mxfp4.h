@@ -72,8 +72,9 @@ typedef enum {
 typedef enum { MOE_ACT_BF16 = 0 /* W4A16 */, MOE_ACT_MXFP4 = 1 /* W4A4 */ } moe_act_fmt;
 typedef enum { MOE_SRC_F32 = 0, MOE_SRC_BF16 = 1 } moe_src_dtype;
 
-/* Rows per tile of the grouped GEMMs (the 32-row tiles of the VibeSys post,
- * section "Prefill, cache and speculation"). */
+/* Rows per tile of the weight-streaming (decode) GEMMs: the 32-row tiles of
+ * the VibeSys post, section "Prefill, cache and speculation".  The LDS-tiled
+ * (prefill) GEMMs take 64- or 128-row tiles. */
 #define MOE_TILE_M 32
 
 /* Human-readable name of a status code (static string). */
@@ -151,13 +152,17 @@ MOE_API moe_status moe_mxfp4_quantize(const void *src, int32_t src_dtype, int64_
  *   act_fmt = MOE_ACT_BF16:  act = x bf16 [T, H], act_scale = NULL
  *   act_fmt = MOE_ACT_MXFP4: act = packed uint8 [T, H/2], act_scale uint8 [T, H/32]
  *   sorted_assign, expert_offsets, tile_table, num_tiles: moe_align_sort's
- *     outputs with tile_m = MOE_TILE_M; max_tiles = ceil(T*Kp/32) + Ep
+ *     outputs built with the same tile_m
+ *   tile_m     rows per tile: 32 selects the weight-streaming kernel (small
+ *              groups, decode); 64 or 128 the LDS-tiled kernel (large
+ *              groups, prefill; needs H a multiple of 256)
  *   h          out bf16 [T*Kp, I], sorted row order
- * Errors: INVALID_ARGUMENT, UNSUPPORTED (H or I not a multiple of 128).
+ * Errors: INVALID_ARGUMENT, UNSUPPORTED (H or I not a multiple of 128, or a
+ * tile_m / shape the kernels do not cover).
  */
 MOE_API moe_status moe_expert_gate_up(const void *act, const uint8_t *act_scale, int32_t act_fmt,
                               const int32_t *sorted_assign, const int32_t *expert_offsets,
-                              const int32_t *tile_table, const int32_t *num_tiles,
+                              const int32_t *tile_table, const int32_t *num_tiles, int32_t tile_m,
                               const uint8_t *w13, const uint8_t *w13_scale, int32_t T, int32_t H,
                               int32_t I, int32_t Ep, int32_t Kp, uint16_t *h, void *stream);
 
@@ -165,14 +170,16 @@ MOE_API moe_status moe_expert_gate_up(const void *act, const uint8_t *act_scale,
  * Grouped down GEMM: y[r, j] = sum_i h[r, i] * W2[e, j, i] (fp32 accumulation).
  *   act_fmt = MOE_ACT_BF16:  h bf16 [A, I], h_scale = NULL
  *   act_fmt = MOE_ACT_MXFP4: h packed uint8 [A, I/2], h_scale uint8 [A, I/32]
+ *   tile_m     as for moe_expert_gate_up
  *   y          out fp32 [A, H], sorted row order (A = T*Kp)
- * Errors: INVALID_ARGUMENT, UNSUPPORTED (H or I not a multiple of 128).
+ * Errors: INVALID_ARGUMENT, UNSUPPORTED (H or I not a multiple of 128, or a
+ * tile_m / shape the kernels do not cover).
  */
 MOE_API moe_status moe_expert_down(const void *h, const uint8_t *h_scale, int32_t act_fmt,
                            const int32_t *expert_offsets, const int32_t *tile_table,
-                           const int32_t *num_tiles, const uint8_t *w2, const uint8_t *w2_scale,
-                           int32_t T, int32_t H, int32_t I, int32_t Ep, int32_t Kp, float *y,
-                           void *stream);
+                           const int32_t *num_tiles, int32_t tile_m, const uint8_t *w2,
+                           const uint8_t *w2_scale, int32_t T, int32_t H, int32_t I, int32_t Ep,
+                           int32_t Kp, float *y, void *stream);
 
 /*
  * Weighted combine back into token order (the shared expert is slot K, so
@@ -186,13 +193,20 @@ MOE_API moe_status moe_expert_down(const void *h, const uint8_t *h_scale, int32_
 MOE_API moe_status moe_combine(const float *y, const float *topk_weights, const int32_t *inv_assign,
                        int32_t T, int32_t H, int32_t Kp, uint16_t *out, void *stream);
 
+/* The tile_m moe_mxfp4_forward uses for these shapes (A = T*Kp assignments
+ * over Ep experts): 32, 64 or 128 (see moe_expert_gate_up). */
+MOE_API int32_t moe_gemm_tile_m(int32_t T, int32_t Kp, int32_t Ep, int32_t H, int32_t I);
+
 /* Workspace bytes moe_mxfp4_forward needs (0 for T = 0). */
 MOE_API size_t moe_mxfp4_workspace_size(int32_t T, int32_t H, int32_t I, int32_t E, int32_t K,
                                 int32_t shared, int32_t act_fmt);
 
 /*
  * The whole layer in one call: route, align, [quantise x], gate/up + SwiGLU,
- * [quantise h], down, combine, all enqueued on `stream`.
+ * [quantise h], down, combine, all enqueued on `stream`.  The GEMM kernels
+ * are chosen on the host from the shapes alone (no device read): average
+ * rows per expert T*K'/E' <= 8 -> 32-row weight-streaming tiles, <= 48 ->
+ * 64-row LDS-tiled, else 128-row LDS-tiled (when H is a multiple of 256).
  *   x              bf16 [T, H]
  *   router_logits  fp32 [T, E];  shared_gate_logits fp32 [T] (shared = 1) or NULL
  *   w13, w13_scale, w2, w2_scale: the MXFP4 weights of E + shared experts

@@ -18,8 +18,21 @@ inline bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 inline hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
 inline moe_status from_hip(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_DEVICE; }
 
-inline int64_t max_tiles_for(int64_t A, int64_t Ep) {
-  return (A + MOE_TILE_M - 1) / MOE_TILE_M + Ep;
+inline int64_t max_tiles_for(int64_t A, int64_t Ep, int64_t tile_m = MOE_TILE_M) {
+  return (A + tile_m - 1) / tile_m + Ep;
+}
+
+// Rows per GEMM tile for a call, from the shapes alone: small groups stream
+// weights through 32-row tiles; larger groups use the LDS-tiled kernels.
+int choose_tile_m(int64_t A, int64_t Ep, int H, int I) {
+  const int64_t avg = A / Ep;
+  if (avg <= 8) return MOE_TILE_M;
+  const int tm = avg <= 48 ? 64 : 128;
+  return expert_gemm_tiled_supported(tm, H, I) ? tm : MOE_TILE_M;
+}
+
+bool tile_m_ok(int32_t tile_m, int32_t H, int32_t I) {
+  return tile_m == MOE_TILE_M || expert_gemm_tiled_supported(tile_m, H, I);
 }
 
 moe_status check_shape_HI(int32_t H, int32_t I) {
@@ -138,45 +151,53 @@ moe_status moe_mxfp4_quantize(const void* src, int32_t src_dtype, int64_t rows, 
 
 moe_status moe_expert_gate_up(const void* act, const uint8_t* act_scale, int32_t act_fmt,
                               const int32_t* sorted_assign, const int32_t* expert_offsets,
-                              const int32_t* tile_table, const int32_t* num_tiles,
+                              const int32_t* tile_table, const int32_t* num_tiles, int32_t tile_m,
                               const uint8_t* w13, const uint8_t* w13_scale, int32_t T, int32_t H,
                               int32_t I, int32_t Ep, int32_t Kp, uint16_t* h, void* stream) {
   if (T < 0 || Ep < 1 || Kp < 1 || (act_fmt != MOE_ACT_BF16 && act_fmt != MOE_ACT_MXFP4))
     return MOE_ERR_INVALID_ARGUMENT;
   moe_status st = check_shape_HI(H, I);
   if (st != MOE_OK) return st;
-  if (Ep > 2048) return MOE_ERR_UNSUPPORTED;
+  if (Ep > 2048 || !tile_m_ok(tile_m, H, I)) return MOE_ERR_UNSUPPORTED;
   if (T == 0) return MOE_OK;
   if (!act || !sorted_assign || !expert_offsets || !tile_table || !num_tiles || !w13 ||
       !w13_scale || !h || (act_fmt == MOE_ACT_MXFP4 && !act_scale))
     return MOE_ERR_INVALID_ARGUMENT;
   if (!aligned16(act) || !aligned16(w13)) return MOE_ERR_INVALID_ARGUMENT;
-  const int64_t mt = max_tiles_for((int64_t)T * Kp, Ep);
-  if (mt * (I / 64) >= INT32_MAX) return MOE_ERR_UNSUPPORTED;
+  const int64_t mt = max_tiles_for((int64_t)T * Kp, Ep, tile_m);
+  if (mt * (I / 16) >= INT32_MAX) return MOE_ERR_UNSUPPORTED;
+  hipStream_t s = as_stream(stream);
+  if (tile_m != MOE_TILE_M)
+    return from_hip(launch_gate_up_tiled(tile_m, act_fmt, act, act_scale, sorted_assign,
+                                         expert_offsets, tile_table, num_tiles, (int)mt, w13,
+                                         w13_scale, T, H, I, Kp, h, s));
   return from_hip(launch_gate_up(act_fmt, act, act_scale, sorted_assign, expert_offsets, tile_table,
-                                 num_tiles, (int)mt, w13, w13_scale, T, H, I, Kp, h,
-                                 as_stream(stream)));
+                                 num_tiles, (int)mt, w13, w13_scale, T, H, I, Kp, h, s));
 }
 
 moe_status moe_expert_down(const void* h, const uint8_t* h_scale, int32_t act_fmt,
                            const int32_t* expert_offsets, const int32_t* tile_table,
-                           const int32_t* num_tiles, const uint8_t* w2, const uint8_t* w2_scale,
-                           int32_t T, int32_t H, int32_t I, int32_t Ep, int32_t Kp, float* y,
-                           void* stream) {
+                           const int32_t* num_tiles, int32_t tile_m, const uint8_t* w2,
+                           const uint8_t* w2_scale, int32_t T, int32_t H, int32_t I, int32_t Ep,
+                           int32_t Kp, float* y, void* stream) {
   if (T < 0 || Ep < 1 || Kp < 1 || (act_fmt != MOE_ACT_BF16 && act_fmt != MOE_ACT_MXFP4))
     return MOE_ERR_INVALID_ARGUMENT;
   moe_status st = check_shape_HI(H, I);
   if (st != MOE_OK) return st;
-  if (Ep > 2048) return MOE_ERR_UNSUPPORTED;
+  if (Ep > 2048 || !tile_m_ok(tile_m, H, I)) return MOE_ERR_UNSUPPORTED;
   if (T == 0) return MOE_OK;
   if (!h || !expert_offsets || !tile_table || !num_tiles || !w2 || !w2_scale || !y ||
       (act_fmt == MOE_ACT_MXFP4 && !h_scale))
     return MOE_ERR_INVALID_ARGUMENT;
   if (!aligned16(h) || !aligned16(w2)) return MOE_ERR_INVALID_ARGUMENT;
-  const int64_t mt = max_tiles_for((int64_t)T * Kp, Ep);
+  const int64_t mt = max_tiles_for((int64_t)T * Kp, Ep, tile_m);
   if (mt * (H / 128) >= INT32_MAX) return MOE_ERR_UNSUPPORTED;
+  hipStream_t s = as_stream(stream);
+  if (tile_m != MOE_TILE_M)
+    return from_hip(launch_down_tiled(tile_m, act_fmt, h, h_scale, expert_offsets, tile_table,
+                                      num_tiles, (int)mt, w2, w2_scale, T * Kp, H, I, y, s));
   return from_hip(launch_down(act_fmt, h, h_scale, expert_offsets, tile_table, num_tiles, (int)mt,
-                              w2, w2_scale, T * Kp, H, I, y, as_stream(stream)));
+                              w2, w2_scale, T * Kp, H, I, y, s));
 }
 
 moe_status moe_combine(const float* y, const float* topk_weights, const int32_t* inv_assign,
@@ -187,6 +208,11 @@ moe_status moe_combine(const float* y, const float* topk_weights, const int32_t*
   if (!y || !topk_weights || !inv_assign || !out || !aligned16(y) || !aligned16(out))
     return MOE_ERR_INVALID_ARGUMENT;
   return from_hip(launch_combine(y, topk_weights, inv_assign, T, H, Kp, out, as_stream(stream)));
+}
+
+int32_t moe_gemm_tile_m(int32_t T, int32_t Kp, int32_t Ep, int32_t H, int32_t I) {
+  if (T <= 0 || Kp < 1 || Ep < 1 || H <= 0 || I <= 0) return MOE_TILE_M;
+  return choose_tile_m((int64_t)T * Kp, Ep, H, I);
 }
 
 size_t moe_mxfp4_workspace_size(int32_t T, int32_t H, int32_t I, int32_t E, int32_t K,
@@ -235,28 +261,37 @@ moe_status moe_mxfp4_forward(const uint16_t* x, const float* router_logits,
   uint8_t* hs = (uint8_t*)(ws + L.hs);
   float* y = (float*)(ws + L.y);
   hipStream_t s = as_stream(stream);
-  const int mt = (int)max_tiles_for(A, Ep);
+  const int tm = choose_tile_m(A, Ep, H, I);
+  const int mt = (int)max_tiles_for(A, Ep, tm);
 
   hipError_t e = launch_route_topk(router_logits, shared_gate_logits, T, E, K, shared, 1, ids, wts, s);
   if (e != hipSuccess) return MOE_ERR_DEVICE;
-  e = launch_align_sort(ids, (int)A, Ep, MOE_TILE_M, counts, offsets, sorted, inv, tiles, ntiles,
-                        scratch, s);
+  e = launch_align_sort(ids, (int)A, Ep, tm, counts, offsets, sorted, inv, tiles, ntiles, scratch, s);
   if (e != hipSuccess) return MOE_ERR_DEVICE;
-  if (act_fmt == MOE_ACT_BF16) {
-    e = launch_gate_up(0, x, nullptr, sorted, offsets, tiles, ntiles, mt, w13, w13_scale, T, H, I,
-                       Kp, h, s);
-    if (e != hipSuccess) return MOE_ERR_DEVICE;
-    e = launch_down(0, h, nullptr, offsets, tiles, ntiles, mt, w2, w2_scale, (int)A, H, I, y, s);
-  } else {
+  const bool q = act_fmt == MOE_ACT_MXFP4;
+  if (q) {
     e = launch_mxfp4_quant(x, 1, T, H, xq, xs, s);
     if (e != hipSuccess) return MOE_ERR_DEVICE;
-    e = launch_gate_up(1, xq, xs, sorted, offsets, tiles, ntiles, mt, w13, w13_scale, T, H, I, Kp,
-                       h, s);
-    if (e != hipSuccess) return MOE_ERR_DEVICE;
+  }
+  const void* a1 = q ? (const void*)xq : (const void*)x;
+  const uint8_t* a1s = q ? xs : nullptr;
+  e = tm != MOE_TILE_M
+          ? launch_gate_up_tiled(tm, act_fmt, a1, a1s, sorted, offsets, tiles, ntiles, mt, w13,
+                                 w13_scale, T, H, I, Kp, h, s)
+          : launch_gate_up(act_fmt, a1, a1s, sorted, offsets, tiles, ntiles, mt, w13, w13_scale, T,
+                           H, I, Kp, h, s);
+  if (e != hipSuccess) return MOE_ERR_DEVICE;
+  if (q) {
     e = launch_mxfp4_quant(h, 1, A, I, hq, hs, s);
     if (e != hipSuccess) return MOE_ERR_DEVICE;
-    e = launch_down(1, hq, hs, offsets, tiles, ntiles, mt, w2, w2_scale, (int)A, H, I, y, s);
   }
+  const void* a2 = q ? (const void*)hq : (const void*)h;
+  const uint8_t* a2s = q ? hs : nullptr;
+  e = tm != MOE_TILE_M
+          ? launch_down_tiled(tm, act_fmt, a2, a2s, offsets, tiles, ntiles, mt, w2, w2_scale,
+                              (int)A, H, I, y, s)
+          : launch_down(act_fmt, a2, a2s, offsets, tiles, ntiles, mt, w2, w2_scale, (int)A, H, I, y,
+                        s);
   if (e != hipSuccess) return MOE_ERR_DEVICE;
   return from_hip(launch_combine(y, wts, inv, T, H, Kp, out, s));
 }

@@ -34,11 +34,12 @@ _SIGS = {
     "moe_align_workspace_size": (_SZ, [_I32, _I32, _I32]),
     "moe_align_sort": (_I32, [_P, _I32, _I32, _I32, _I32, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
     "moe_mxfp4_quantize": (_I32, [_P, _I32, _I64, _I64, _P, _P, _P]),
-    "moe_expert_gate_up": (_I32, [_P, _P, _I32, _P, _P, _P, _P, _P, _P, _I32, _I32, _I32, _I32,
-                                  _I32, _P, _P]),
-    "moe_expert_down": (_I32, [_P, _P, _I32, _P, _P, _P, _P, _P, _I32, _I32, _I32, _I32, _I32,
-                               _P, _P]),
+    "moe_expert_gate_up": (_I32, [_P, _P, _I32, _P, _P, _P, _P, _I32, _P, _P, _I32, _I32, _I32,
+                                  _I32, _I32, _P, _P]),
+    "moe_expert_down": (_I32, [_P, _P, _I32, _P, _P, _P, _I32, _P, _P, _I32, _I32, _I32, _I32,
+                               _I32, _P, _P]),
     "moe_combine": (_I32, [_P, _P, _P, _I32, _I32, _I32, _P, _P]),
+    "moe_gemm_tile_m": (_I32, [_I32, _I32, _I32, _I32, _I32]),
     "moe_mxfp4_workspace_size": (_SZ, [_I32, _I32, _I32, _I32, _I32, _I32, _I32]),
     "moe_mxfp4_forward": (_I32, [_P, _P, _P, _P, _P, _P, _P, _I32, _I32, _I32, _I32, _I32, _I32,
                                  _I32, _P, _P, _P, _P, _SZ, _P]),
@@ -127,6 +128,9 @@ def align_sort(topk_ids, Ep: int, tile_m: int = TILE_M, out=None, stream=None):
     A = T * Kp
     if out is None:
         out = alloc_align(T, Kp, Ep, topk_ids.device, tile_m)
+    if out["tiles"].shape[0] < (A + tile_m - 1) // tile_m + Ep:
+        raise ValueError("tile table too small for this tile_m")
+    out["tile_m"] = tile_m
     _check("moe_align_sort", lib().moe_align_sort(
         _ptr(topk_ids), T, Kp, Ep, tile_m, _ptr(out["counts"]), _ptr(out["offsets"]),
         _ptr(out["sorted"]) if A else None, _ptr(out["inv"]) if A else None,
@@ -166,15 +170,20 @@ def mxfp4_quantize(src, packed=None, scales=None, stream=None):
     return packed, scales
 
 
+def gemm_tile_m(T: int, Kp: int, Ep: int, H: int, I: int) -> int:
+    """moe_gemm_tile_m: the GEMM tile rows mxfp4_forward uses for these shapes."""
+    return int(lib().moe_gemm_tile_m(T, Kp, Ep, H, I))
+
+
 def expert_gate_up(act, act_scale, act_fmt: int, align: dict, w13, w13_scale, T: int, H: int,
                    I: int, Ep: int, Kp: int, h=None, stream=None):
-    """moe_expert_gate_up -> h bf16 [T*Kp, I] in sorted row order."""
+    """moe_expert_gate_up -> h bf16 [T*Kp, I] in sorted row order (align["tile_m"]-row tiles)."""
     if h is None:
         h = torch.empty(T * Kp, I, dtype=torch.bfloat16, device=w13.device)
     _check("moe_expert_gate_up", lib().moe_expert_gate_up(
         _ptr(act), _ptr(act_scale), act_fmt, _ptr(align["sorted"]), _ptr(align["offsets"]),
-        _ptr(align["tiles"]), _ptr(align["num_tiles"]), _ptr(w13), _ptr(w13_scale), T, H, I, Ep,
-        Kp, _ptr(h), _stream(stream)))
+        _ptr(align["tiles"]), _ptr(align["num_tiles"]), align["tile_m"], _ptr(w13),
+        _ptr(w13_scale), T, H, I, Ep, Kp, _ptr(h), _stream(stream)))
     return h
 
 
@@ -185,8 +194,8 @@ def expert_down(h, h_scale, act_fmt: int, align: dict, w2, w2_scale, T: int, H: 
         y = torch.empty(T * Kp, H, dtype=torch.float32, device=w2.device)
     _check("moe_expert_down", lib().moe_expert_down(
         _ptr(h), _ptr(h_scale), act_fmt, _ptr(align["offsets"]), _ptr(align["tiles"]),
-        _ptr(align["num_tiles"]), _ptr(w2), _ptr(w2_scale), T, H, I, Ep, Kp, _ptr(y),
-        _stream(stream)))
+        _ptr(align["num_tiles"]), align["tile_m"], _ptr(w2), _ptr(w2_scale), T, H, I, Ep, Kp,
+        _ptr(y), _stream(stream)))
     return y
 
 
@@ -262,7 +271,7 @@ def forward_stages(x, router_logits, shared_gate_logits, w13, w13_scale, w2, w2_
                topk_weights=b["w"], stream=stream)
     rec("route", 1)
     rec("align", 0)
-    align_sort(b["ids"], Ep, out=b["align"], stream=stream)
+    align_sort(b["ids"], Ep, tile_m=gemm_tile_m(T, Kp, Ep, H, I), out=b["align"], stream=stream)
     rec("align", 1)
     act, act_s = x, None
     if act_fmt == ACT_MXFP4:

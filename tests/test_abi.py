@@ -26,7 +26,7 @@ def declared_functions():
 def test_library_loads_and_exports_every_declared_symbol():
     lib = ops.lib()
     names = declared_functions()
-    assert len(names) == 10
+    assert len(names) == 11
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(ops.EXPORTS)
@@ -85,7 +85,7 @@ def test_quantize_argument_errors():
 
 def test_gemm_and_combine_argument_errors():
     gu = ops.lib().moe_expert_gate_up
-    base = [FAKE, None, 0, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 8, 256, 128, 16, 2, FAKE, None]
+    base = [FAKE, None, 0, FAKE, FAKE, FAKE, FAKE, 32, FAKE, FAKE, 8, 256, 128, 16, 2, FAKE, None]
     def call(f, a, **over):
         a = list(a)
         for i, v in over.items():
@@ -94,19 +94,30 @@ def test_gemm_and_combine_argument_errors():
     assert call(gu, base, a0=None) == INVALID
     assert call(gu, base, a2=1) == INVALID                 # MXFP4 activations need scales
     assert call(gu, base, a2=7) == INVALID
-    assert call(gu, base, a10=200) == UNSUPPORTED          # H % 128
-    assert call(gu, base, a11=96) == UNSUPPORTED           # I % 128
+    assert call(gu, base, a11=200) == UNSUPPORTED          # H % 128
+    assert call(gu, base, a12=96) == UNSUPPORTED           # I % 128
+    assert call(gu, base, a7=48) == UNSUPPORTED            # no kernel for 48-row tiles
+    assert call(gu, base, a7=128, a11=384) == UNSUPPORTED  # tiled kernels need H % 256
     assert call(gu, base, a0=MIS) == INVALID
-    assert call(gu, base, a9=0) == OK
+    assert call(gu, base, a10=0) == OK
     dn = ops.lib().moe_expert_down
-    based = [FAKE, None, 0, FAKE, FAKE, FAKE, FAKE, FAKE, 8, 256, 128, 16, 2, FAKE, None]
-    assert call(dn, based, a13=None) == INVALID
-    assert call(dn, based, a9=100) == UNSUPPORTED
-    assert call(dn, based, a8=0) == OK
+    based = [FAKE, None, 0, FAKE, FAKE, FAKE, 32, FAKE, FAKE, 8, 256, 128, 16, 2, FAKE, None]
+    assert call(dn, based, a14=None) == INVALID
+    assert call(dn, based, a10=100) == UNSUPPORTED
+    assert call(dn, based, a6=64, a10=384) == UNSUPPORTED
+    assert call(dn, based, a9=0) == OK
     cb = ops.lib().moe_combine
     assert cb(None, FAKE, FAKE, 4, 256, 3, FAKE, None) == INVALID
     assert cb(FAKE, FAKE, FAKE, 4, 200, 3, FAKE, None) == UNSUPPORTED
     assert cb(FAKE, FAKE, FAKE, 0, 256, 3, FAKE, None) == OK
+
+
+def test_gemm_tile_choice():
+    # decode-like groups stream weights; larger groups use the LDS-tiled kernels
+    assert ops.gemm_tile_m(64, 11, 513, 4096, 1024) == 32
+    assert ops.gemm_tile_m(1536, 11, 513, 4096, 1024) == 64
+    assert ops.gemm_tile_m(8192, 11, 513, 4096, 1024) == 128
+    assert ops.gemm_tile_m(8192, 11, 513, 384, 1024) == 32      # H % 256 != 0
 
 
 def test_forward_argument_errors_and_workspace():

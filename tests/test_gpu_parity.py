@@ -47,6 +47,11 @@ SMALL = {
                                       act_fmt=synth.ACT_MXFP4, outlier_p=0.01),
     "w4a4_ragged": synth.custom_config("w4a4_ragged", T=70, H=384, I=256, E=12, K=2, shared=1,
                                        act_fmt=synth.ACT_MXFP4, outlier_p=0.001),
+    # enough rows per expert for the LDS-tiled kernels (64- and 128-row tiles)
+    "tiled64": synth.custom_config("tiled64", T=200, H=256, I=128, E=24, K=4, shared=1),
+    "tiled128": synth.custom_config("tiled128", T=300, H=512, I=256, E=16, K=3, shared=1),
+    "tiled128_w4a4": synth.custom_config("tiled128_w4a4", T=300, H=512, I=256, E=16, K=3,
+                                         shared=1, act_fmt=synth.ACT_MXFP4, outlier_p=0.002),
 }
 
 
@@ -199,8 +204,7 @@ def test_layer_small(name):
     assert np.array_equal(bits(out), bits(r["out"]))
     assert np.array_equal(r["ids"].cpu().numpy(), want["ids"])
     assert np.max(np.abs(r["w"].cpu().numpy() - want["w"])) <= W_ATOL
-    _check_align(r["align"], (want["counts"], want["offsets"], want["sorted"], want["inv"],
-                              want["tiles"], want["n_tiles"]))
+    _check_align(r["align"], moe.align(want["ids"], c.Ep, r["align"]["tile_m"]))
     if c.act_fmt == synth.ACT_MXFP4:
         xq, xs = moe.quantize_activations(bits(prob.x_cpu))
         assert np.array_equal(r["xq"].cpu().numpy(), xq)
@@ -315,3 +319,34 @@ def test_forward_capturable_in_hip_graph():
         assert np.array_equal(bits(out), eager), f"replay {rep}"
         prob.forward()                      # eager work between replays
         torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("tile_m", [32, 64, 128])
+@pytest.mark.parametrize("act", [synth.ACT_BF16, synth.ACT_MXFP4])
+def test_gemm_kernels_for_every_tile_size(tile_m, act):
+    """The staged entry points with each tile size (weight-streaming 32-row
+    tiles, LDS-tiled 64- and 128-row tiles) against the oracle."""
+    cfg = synth.custom_config("tiles", T=150, H=512, I=256, E=8, K=3, shared=1, act_fmt=act,
+                              outlier_p=0.002 if act else 0.0)
+    _say("tile_m", tile_m, "act", act)
+    prob = Problem(cfg)
+    c = prob.cfg
+    o = ops()
+    ids, w = o.route_topk(prob.logits, prob.gate, c.K, c.shared)
+    al = o.align_sort(ids, c.Ep, tile_m=tile_m)
+    if act == synth.ACT_MXFP4:
+        xq, xs = o.mxfp4_quantize(prob.x)
+        h = o.expert_gate_up(xq, xs, act, al, prob.w13, prob.w13s, c.T, c.H, c.I, c.Ep, c.Kp)
+        hq, hs = o.mxfp4_quantize(h)
+        y = o.expert_down(hq, hs, act, al, prob.w2, prob.w2s, c.T, c.H, c.I, c.Ep, c.Kp)
+    else:
+        h = o.expert_gate_up(prob.x, None, act, al, prob.w13, prob.w13s, c.T, c.H, c.I, c.Ep, c.Kp)
+        y = o.expert_down(h, None, act, al, prob.w2, prob.w2s, c.T, c.H, c.I, c.Ep, c.Kp)
+    out = o.combine(y, w, al["inv"], c.T, c.H, c.Kp)
+    torch.cuda.synchronize()
+    want = prob.oracle()
+    _check_align(al, moe.align(want["ids"], c.Ep, tile_m))
+    e_rel = rel_l2(bits(out), want["out"])
+    e_max = max_abs_over_rms(bits(out), want["out"])
+    _say(f"  tile_m {tile_m}: rel_l2 {e_rel:.2e}  max_abs/rms {e_max:.2e}")
+    assert e_rel <= REL_L2[act] and e_max <= MAX_ABS_RMS
