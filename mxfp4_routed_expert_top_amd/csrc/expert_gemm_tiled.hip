@@ -36,133 +36,149 @@ __device__ __forceinline__ int xcd_logical(int b, int nblocks) {
   return (b & 7) * (nblocks >> 3) + (b >> 3);
 }
 
-// LDS bytes of one activation row of one chunk (+16 bytes of padding so that
-// 16 consecutive rows fall in different banks).
-template <bool kFP4A>
-constexpr int lds_row_bytes() {
-  return kFP4A ? 64 + 16 : 256 + 16;
+// The K loop as an NS-stage pipeline.  Stage u holds one 128-element chunk:
+// the tile's activation rows in LDS (written by direct-to-LDS buffer loads,
+// no registers) and each wave's four weight strips (16 bytes per lane) plus
+// their scale bytes in registers.  Iteration c waits for stage c % NS,
+// meets the other waves at the barrier (which also retires every read of
+// the stage about to be refilled), issues chunk c + NS - 1 into that stage
+// and runs the MFMAs of chunk c; NS - 1 chunks stay in flight.
+//
+// Activation layout per stage, rows of the tile in order:
+//   bf16:  256 bytes per row, 16-byte slot p of row r holds piece p ^ (r & 15)
+//   MXFP4: 64 bytes of codes per row, slot p holds piece p ^ ((r >> 2) & 3);
+//          then 4 scale bytes per row (1 KiB reserved)
+// (the XOR swizzle spreads the 16 rows an MFMA operand read touches over all
+// LDS banks).  Loads beyond the tile's rows or past the last chunk use an
+// out-of-range offset: they move no data and every wave issues the same
+// number of loads per stage, so the wait counts are constants.
+template <int BM, bool kFP4A>
+constexpr int x_bytes() {
+  return kFP4A ? BM * 64 + 1024 : BM * 256;
 }
 
+// Each stage ends with the chunk's weight scales of the workgroup's 256
+// weight rows: one dword per row (the row's four scale blocks of the chunk),
+// wave w's 64 rows at [256 w, 256 w + 256).
 template <int BM, bool kFP4A>
-constexpr int lds_buf_bytes() {
-  return BM * lds_row_bytes<kFP4A>() + (kFP4A ? BM * 4 : 0);
+constexpr int stage_bytes() {
+  return x_bytes<BM, kFP4A>() + 1024;
 }
 
-// One wave's GEMM over the tile: acc[mt][st] for 16-row subtile mt and
-// 16-row weight strip st.  `rows_act` are the activation rows staged per
-// chunk; `fill` gathers chunk c into an LDS buffer.
-template <int BM, bool kFP4A>
+// s_waitcnt vmcnt(n) with the other counters left alone (gfx9 encoding).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// Workgroup barrier without the release fence of __syncthreads: the fence
+// would wait for every direct-to-LDS load still in flight, i.e. for the
+// stages being prefetched.  Each wave waits for its own loads of the stage
+// it is about to read (wait_vmcnt) before the barrier, and every LDS read of
+// a stage has returned (its MFMAs consumed it) before the barrier that
+// precedes the stage's refill; the "memory" clobber keeps the compiler from
+// moving memory accesses across.
+__device__ __forceinline__ void stage_barrier() { asm volatile("s_barrier" ::: "memory"); }
+
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+__device__ __forceinline__ void load_to_lds16(rsrc_t r, uint32_t voff, uint32_t soff, void* lds) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)lds, 16, (int)voff, (int)soff, 0, 0);
+}
+
+__device__ __forceinline__ void load_to_lds4(rsrc_t r, uint32_t voff, uint32_t soff, void* lds) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)lds, 4, (int)voff, (int)soff, 0, 0);
+}
+
+template <int BM, bool kFP4A, int NS>
 struct TiledGemm {
   static constexpr int MT = BM / 16;
-  static constexpr int RB = lds_row_bytes<kFP4A>();
-  static constexpr int NQ = kFP4A ? (BM * 5 + 255) / 256 : BM / 16;   // 16-byte pieces per thread
+  static constexpr int XI = kFP4A ? BM / 64 : BM / 16;   // code / row loads per wave per stage
+  static constexpr int LPS = XI + (kFP4A ? 1 : 0) + 5;     // vmem ops per wave per stage
+  static constexpr int SB = stage_bytes<BM, kFP4A>();
 
-  // weights
-  rsrc_t w, ws;
-  uint32_t wo[4], so[4];
-  // activations: per thread, NQ pieces of the chunk (offset of the piece in
-  // the source row per chunk, or kOOR), and where each lands in LDS
-  rsrc_t a, as;
-  uint32_t src[NQ];
-  uint32_t dst[NQ];
-  bool is_scale[NQ];
+  rsrc_t w, ws, a, as;
+  uint32_t wo[4];               // lane's weight row offsets (+16 g)
+  uint32_t wso;                 // scale dword of weight row (64 w + l) of the workgroup
+  uint32_t xo[XI];              // lane's activation source offsets (or kOOR)
+  uint32_t xso;                 // MXFP4 activation scale source offset (or kOOR)
+  int wave, lane, nl, g, nch;
 
-  __device__ __forceinline__ void load_w(int c, u32x4_t (&q)[4], uint32_t (&s)[4]) const {
+  // Issue chunk c into a stage (weight codes into registers q).
+  __device__ __forceinline__ void issue(uint8_t* base, int c, u32x4_t (&q)[4]) const {
+    const bool ok = c < nch;
+    const uint32_t oor = ok ? 0u : kOOR;
+    const uint32_t cc = ok ? (uint32_t)c : 0u;
+    if constexpr (kFP4A) {
 #pragma unroll
-    for (int st = 0; st < 4; ++st) {
-      q[st] = bload16(w, wo[st], 64 * c);
-      s[st] = bload1(ws, so[st], 4 * c);
+      for (int i = 0; i < XI; ++i)
+        load_to_lds16(a, xo[i] | oor, 64 * cc, base + (wave * XI + i) * 1024);
+      load_to_lds4(as, xso | oor, 4 * cc, base + BM * 64 + wave * 256);
+    } else {
+#pragma unroll
+      for (int i = 0; i < XI; ++i)
+        load_to_lds16(a, xo[i] | oor, 256 * cc, base + (wave * XI + i) * 1024);
     }
+    load_to_lds4(ws, wso | oor, 4 * cc, base + x_bytes<BM, kFP4A>() + wave * 256);
+#pragma unroll
+    for (int t = 0; t < 4; ++t) q[t] = bload16(w, wo[t] | oor, 64 * cc);
   }
 
-  __device__ __forceinline__ void load_x(int c, u32x4_t (&v)[NQ]) const {
-#pragma unroll
-    for (int q = 0; q < NQ; ++q) {
-      if constexpr (kFP4A) {
-        // codes: 64 B per row per chunk; scales: 4 B per row per chunk (one dword)
-        if (is_scale[q]) {
-          v[q] = (u32x4_t){(uint32_t)__builtin_amdgcn_raw_buffer_load_b32(as, (int)src[q], 4 * c, 0),
-                           0u, 0u, 0u};
-        } else {
-          v[q] = bload16(a, src[q], 64 * c);
-        }
-      } else {
-        v[q] = bload16(a, src[q], 256 * c);
-      }
-    }
-  }
-
-  __device__ __forceinline__ void store_x(uint8_t* buf, const u32x4_t (&v)[NQ]) const {
-#pragma unroll
-    for (int q = 0; q < NQ; ++q) {
-      if (dst[q] == 0xFFFFFFFFu) continue;
-      if (kFP4A && is_scale[q])
-        *reinterpret_cast<uint32_t*>(buf + dst[q]) = v[q][0];
-      else
-        *reinterpret_cast<u32x4_t*>(buf + dst[q]) = v[q];
-    }
-  }
-
-  __device__ __forceinline__ void compute(const uint8_t* buf, const u32x4_t (&q)[4],
-                                          const uint32_t (&s)[4], int nl, int g,
+  __device__ __forceinline__ void compute(const uint8_t* x, const u32x4_t (&q)[4],
                                           floatx4_t (&acc)[MT][4]) const {
+    uint32_t s[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) s[t] = x[x_bytes<BM, kFP4A>() + wave * 256 + (16 * t + nl) * 4 + g];
     if constexpr (kFP4A) {
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
         const int r = 16 * mt + nl;
-        const u32x4_t av = *reinterpret_cast<const u32x4_t*>(buf + r * RB + 16 * g);
-        const uint32_t sa = buf[BM * RB + r * 4 + g];
+        const u32x4_t av =
+            *reinterpret_cast<const u32x4_t*>(x + r * 64 + 16 * (g ^ ((r >> 2) & 3)));
+        const uint32_t sa = x[BM * 64 + r * 4 + g];
 #pragma unroll
-        for (int st = 0; st < 4; ++st)
-          acc[mt][st] = mfma_fp4_16x16x128(av, sa, q[st], s[st], acc[mt][st]);
+        for (int t = 0; t < 4; ++t) acc[mt][t] = mfma_fp4_16x16x128(av, sa, q[t], s[t], acc[mt][t]);
       }
     } else {
       float sc[4];
 #pragma unroll
-      for (int st = 0; st < 4; ++st) sc[st] = e8m0_to_f32(s[st]);
+      for (int t = 0; t < 4; ++t) sc[t] = e8m0_to_f32(s[t]);
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         bf16x8_t b[4];
 #pragma unroll
-        for (int st = 0; st < 4; ++st) b[st] = dequant8_bf16(q[st][j], sc[st]);
+        for (int t = 0; t < 4; ++t) b[t] = dequant8_bf16(q[t][j], sc[t]);
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) {
           const int r = 16 * mt + nl;
-          const bf16x8_t av = *reinterpret_cast<const bf16x8_t*>(buf + r * RB + 64 * g + 16 * j);
+          const bf16x8_t av = *reinterpret_cast<const bf16x8_t*>(
+              x + r * 256 + 16 * ((4 * g + j) ^ (r & 15)));
 #pragma unroll
-          for (int st = 0; st < 4; ++st) acc[mt][st] = mfma_bf16_16x16x32(av, b[st], acc[mt][st]);
+          for (int t = 0; t < 4; ++t) acc[mt][t] = mfma_bf16_16x16x32(av, b[t], acc[mt][t]);
         }
       }
     }
   }
 
-  // The K loop: chunk c+1's weights and activations are loaded while chunk c
-  // is computed; the activations go to the other LDS buffer after the MFMAs.
-  __device__ __forceinline__ void run(uint8_t* lds, int nch, int nl, int g,
+  // stages[u]: one LDS array per stage (separate objects, so the compiler's
+  // wait before reading stage u only covers the loads into stage u).
+  __device__ __forceinline__ void run(uint8_t* const (&stages)[NS],
                                       floatx4_t (&acc)[MT][4]) const {
-    constexpr int BUF = lds_buf_bytes<BM, kFP4A>();
-    u32x4_t q[4], qn[4];
-    uint32_t s[4], sn[4];
-    u32x4_t v[NQ];
-    load_x(0, v);
-    load_w(0, q, s);
-    store_x(lds, v);
-    __syncthreads();
-    for (int c = 0; c < nch; ++c) {
-      const bool more = c + 1 < nch;
-      if (more) {
-        load_w(c + 1, qn, sn);
-        load_x(c + 1, v);
-      }
-      compute(lds + (c & 1) * BUF, q, s, nl, g, acc);
-      if (more) store_x(lds + ((c + 1) & 1) * BUF, v);
-      __syncthreads();
+    u32x4_t q[NS][4];
 #pragma unroll
-      for (int st = 0; st < 4; ++st) {
-        q[st] = qn[st];
-        s[st] = sn[st];
+    for (int u = 0; u < NS - 1; ++u) issue(stages[u], u, q[u]);
+    for (int c0 = 0; c0 < nch; c0 += NS) {
+#pragma unroll
+      for (int u = 0; u < NS; ++u) {
+        const int c = c0 + u;
+        wait_vmcnt<LPS * (NS - 2)>();
+        stage_barrier();
+        issue(stages[(u + NS - 1) % NS], c + NS - 1, q[(u + NS - 1) % NS]);
+        if (c < nch) compute(stages[u], q[u], acc);
       }
     }
+    wait_vmcnt<0>();
   }
 };
 
@@ -176,60 +192,54 @@ __device__ __forceinline__ bool tile_of(const int32_t* tiles, const int32_t* num
   return true;
 }
 
-// Per-thread activation pieces of a chunk.  bf16: BM rows x 16 pieces of 16
-// bytes; thread t takes rows t/16 + 16 q, piece t % 16.  MXFP4: BM rows x 4
-// code pieces, then BM scale dwords; thread t takes items t + 256 q.
-template <int BM, bool kFP4A>
-__device__ __forceinline__ void plan_x(TiledGemm<BM, kFP4A>& G, const int32_t* sorted, int Kp,
+// The lane's activation source offsets for every stage: row r of the tile
+// comes from source row src_row(r) (a token for gate/up, a sorted row for down).
+template <int BM, bool kFP4A, int NS>
+__device__ __forceinline__ void plan_x(TiledGemm<BM, kFP4A, NS>& G, const int32_t* sorted, int Kp,
                                        int T, const TileT& ti, bool gather, uint32_t row_bytes,
                                        uint32_t scale_bytes) {
-  constexpr int RB = lds_row_bytes<kFP4A>();
-  const int t = threadIdx.x;
+  auto src_row = [&](int r) -> uint32_t {
+    return gather ? min((unsigned)(sorted[ti.row0 + r] / Kp), (unsigned)(T - 1))
+                  : (uint32_t)(ti.row0 + r);
+  };
 #pragma unroll
-  for (int q = 0; q < G.NQ; ++q) {
+  for (int i = 0; i < G.XI; ++i) {
+    const int k = G.wave * G.XI + i;
     int r, piece;
-    bool sc = false;
     if (kFP4A) {
-      const int item = t + 256 * q;
-      if (item < BM * 4) {
-        r = item >> 2;
-        piece = item & 3;
-      } else {
-        r = item - BM * 4;
-        piece = 0;
-        sc = true;
-      }
+      r = 16 * k + (G.lane >> 2);
+      const int p = G.lane & 3;
+      piece = p ^ ((r >> 2) & 3);
     } else {
-      r = (t >> 4) + 16 * q;
-      piece = t & 15;
+      r = 4 * k + (G.lane >> 4);
+      const int p = G.lane & 15;
+      piece = p ^ (r & 15);
     }
-    G.is_scale[q] = sc;
-    if (r >= BM) {
-      G.src[q] = kOOR;
-      G.dst[q] = 0xFFFFFFFFu;
-      continue;
-    }
-    G.dst[q] = sc ? (uint32_t)(BM * RB + r * 4) : (uint32_t)(r * RB + 16 * piece);
-    if (r >= ti.rows) {
-      G.src[q] = kOOR;                     // padded row: zeros
-      continue;
-    }
-    const uint32_t srow = gather ? min((unsigned)(sorted[ti.row0 + r] / Kp), (unsigned)(T - 1))
-                                 : (uint32_t)(ti.row0 + r);
-    G.src[q] = sc ? srow * scale_bytes : srow * row_bytes + 16 * piece;
+    G.xo[i] = r < ti.rows ? src_row(r) * row_bytes + 16 * piece : kOOR;
+  }
+  if (kFP4A) {
+    const int r = 64 * G.wave + G.lane;
+    G.xso = r < ti.rows ? src_row(r) * scale_bytes : kOOR;
+  } else {
+    G.xso = kOOR;
   }
 }
 
 // gate/up + SwiGLU: weight rows gate [i0, i0 + 128) and up [I + i0, I + i0 + 128),
 // i0 = 128 s; wave w owns i in [i0 + 32 w, i0 + 32 w + 32): strips gate lo/hi, up lo/hi.
-template <int BM, bool kFP4A>
+template <int BM, bool kFP4A, int NS>
 __global__ __launch_bounds__(256) void gate_up_tiled_kernel(
     const void* __restrict__ act, const uint8_t* __restrict__ act_scale,
     const int32_t* __restrict__ sorted, const int32_t* __restrict__ offsets,
     const int32_t* __restrict__ tiles, const int32_t* __restrict__ num_tiles,
     const uint8_t* __restrict__ w13, const uint8_t* __restrict__ w13s, int T, int H, int I, int Kp,
     int max_tiles, uint16_t* __restrict__ h) {
-  __shared__ __align__(16) uint8_t lds[2 * lds_buf_bytes<BM, kFP4A>()];
+  __shared__ __align__(16) uint8_t st0[stage_bytes<BM, kFP4A>()];
+  __shared__ __align__(16) uint8_t st1[stage_bytes<BM, kFP4A>()];
+  __shared__ __align__(16) uint8_t st2[stage_bytes<BM, kFP4A>()];
+  __shared__ __align__(16) uint8_t st3[stage_bytes<BM, kFP4A>()];
+  static_assert(NS == 4, "four LDS stages");
+  uint8_t* const stages[NS] = {st0, st1, st2, st3};
   const int L = xcd_logical(blockIdx.x, gridDim.x);
   const int s = L / max_tiles;
   if (s >= I / 128) return;
@@ -239,15 +249,21 @@ __global__ __launch_bounds__(256) void gate_up_tiled_kernel(
   const int nl = lane & 15, g = lane >> 4;
   const uint32_t rb = H / 2, rs = H / 32;
   const size_t wbytes = (size_t)2 * I * rb, sbytes = (size_t)2 * I * rs;
-  TiledGemm<BM, kFP4A> G;
+  TiledGemm<BM, kFP4A, NS> G;
+  G.wave = wave;
+  G.lane = lane;
+  G.nl = nl;
+  G.g = g;
   G.w = make_rsrc(w13 + ti.expert * wbytes, (uint32_t)wbytes);
   G.ws = make_rsrc(w13s + ti.expert * sbytes, (uint32_t)sbytes);
   const int i0 = s * 128 + wave * 32;
   const int rows4[4] = {i0 + nl, i0 + 16 + nl, I + i0 + nl, I + i0 + 16 + nl};
 #pragma unroll
-  for (int st = 0; st < 4; ++st) {
-    G.wo[st] = rows4[st] * rb + 16 * g;
-    G.so[st] = rows4[st] * rs + g;
+  for (int st = 0; st < 4; ++st) G.wo[st] = rows4[st] * rb + 16 * g;
+  {
+    const int t = lane >> 4, rr = lane & 15;                // scale row (16 t + rr) of the wave
+    const int row = (t < 2 ? i0 : I + i0) + 16 * (t & 1) + rr;
+    G.wso = row * rs;
   }
   if (kFP4A) {
     G.a = make_rsrc(act, (uint32_t)((size_t)T * rb));
@@ -255,14 +271,15 @@ __global__ __launch_bounds__(256) void gate_up_tiled_kernel(
   } else {
     G.a = make_rsrc(act, (uint32_t)((size_t)T * H * 2));
   }
-  plan_x<BM, kFP4A>(G, sorted, Kp, T, ti, true, kFP4A ? rb : (uint32_t)H * 2, rs);
+  G.nch = H / 128;
+  plan_x<BM, kFP4A, NS>(G, sorted, Kp, T, ti, true, kFP4A ? rb : (uint32_t)H * 2, rs);
 
   floatx4_t acc[BM / 16][4];
 #pragma unroll
   for (int mt = 0; mt < BM / 16; ++mt)
 #pragma unroll
     for (int st = 0; st < 4; ++st) acc[mt][st] = (floatx4_t){0.f, 0.f, 0.f, 0.f};
-  G.run(lds, H / 128, nl, g, acc);
+  G.run(stages, acc);
 
 #pragma unroll
   for (int mt = 0; mt < BM / 16; ++mt)
@@ -278,13 +295,18 @@ __global__ __launch_bounds__(256) void gate_up_tiled_kernel(
 }
 
 // down: weight rows j in [256 s, 256 s + 256); wave w owns [256 s + 64 w, +64).
-template <int BM, bool kFP4A>
+template <int BM, bool kFP4A, int NS>
 __global__ __launch_bounds__(256) void down_tiled_kernel(
     const void* __restrict__ hin, const uint8_t* __restrict__ hscale,
     const int32_t* __restrict__ offsets, const int32_t* __restrict__ tiles,
     const int32_t* __restrict__ num_tiles, const uint8_t* __restrict__ w2,
     const uint8_t* __restrict__ w2s, int A, int H, int I, int max_tiles, float* __restrict__ y) {
-  __shared__ __align__(16) uint8_t lds[2 * lds_buf_bytes<BM, kFP4A>()];
+  __shared__ __align__(16) uint8_t st0[stage_bytes<BM, kFP4A>()];
+  __shared__ __align__(16) uint8_t st1[stage_bytes<BM, kFP4A>()];
+  __shared__ __align__(16) uint8_t st2[stage_bytes<BM, kFP4A>()];
+  __shared__ __align__(16) uint8_t st3[stage_bytes<BM, kFP4A>()];
+  static_assert(NS == 4, "four LDS stages");
+  uint8_t* const stages[NS] = {st0, st1, st2, st3};
   const int L = xcd_logical(blockIdx.x, gridDim.x);
   const int s = L / max_tiles;
   if (s >= H / 256) return;
@@ -294,29 +316,32 @@ __global__ __launch_bounds__(256) void down_tiled_kernel(
   const int nl = lane & 15, g = lane >> 4;
   const uint32_t rb = I / 2, rs = I / 32;
   const size_t wbytes = (size_t)H * rb, sbytes = (size_t)H * rs;
-  TiledGemm<BM, kFP4A> G;
+  TiledGemm<BM, kFP4A, NS> G;
+  G.wave = wave;
+  G.lane = lane;
+  G.nl = nl;
+  G.g = g;
   G.w = make_rsrc(w2 + ti.expert * wbytes, (uint32_t)wbytes);
   G.ws = make_rsrc(w2s + ti.expert * sbytes, (uint32_t)sbytes);
   const int j0 = s * 256 + wave * 64;
 #pragma unroll
-  for (int st = 0; st < 4; ++st) {
-    G.wo[st] = (j0 + 16 * st + nl) * rb + 16 * g;
-    G.so[st] = (j0 + 16 * st + nl) * rs + g;
-  }
+  for (int st = 0; st < 4; ++st) G.wo[st] = (j0 + 16 * st + nl) * rb + 16 * g;
+  G.wso = (j0 + lane) * rs;                                   // scale row 16 t + rr = lane
   if (kFP4A) {
     G.a = make_rsrc(hin, (uint32_t)((size_t)A * rb));
     G.as = make_rsrc(hscale, (uint32_t)((size_t)A * rs));
   } else {
     G.a = make_rsrc(hin, (uint32_t)((size_t)A * I * 2));
   }
-  plan_x<BM, kFP4A>(G, nullptr, 1, A, ti, false, kFP4A ? rb : (uint32_t)I * 2, rs);
+  G.nch = I / 128;
+  plan_x<BM, kFP4A, NS>(G, nullptr, 1, A, ti, false, kFP4A ? rb : (uint32_t)I * 2, rs);
 
   floatx4_t acc[BM / 16][4];
 #pragma unroll
   for (int mt = 0; mt < BM / 16; ++mt)
 #pragma unroll
     for (int st = 0; st < 4; ++st) acc[mt][st] = (floatx4_t){0.f, 0.f, 0.f, 0.f};
-  G.run(lds, I / 128, nl, g, acc);
+  G.run(stages, acc);
 
 #pragma unroll
   for (int mt = 0; mt < BM / 16; ++mt)
@@ -331,6 +356,12 @@ __global__ __launch_bounds__(256) void down_tiled_kernel(
     }
 }
 
+// Pipeline depth: 4 stages (128 KiB of LDS for 128-row bf16 tiles).
+template <int BM, bool kFP4A>
+constexpr int tiled_stages() {
+  return 4;
+}
+
 template <int BM, bool kFP4A>
 hipError_t launch_gate_up_bm(const void* act, const uint8_t* act_scale, const int32_t* sorted,
                              const int32_t* offsets, const int32_t* tiles,
@@ -339,7 +370,8 @@ hipError_t launch_gate_up_bm(const void* act, const uint8_t* act_scale, const in
                              hipStream_t stream) {
   const long n = (long)max_tiles * (I / 128);
   const unsigned grid = (unsigned)((n + 7) / 8 * 8);
-  hipLaunchKernelGGL((gate_up_tiled_kernel<BM, kFP4A>), dim3(grid), dim3(256), 0, stream, act,
+  hipLaunchKernelGGL((gate_up_tiled_kernel<BM, kFP4A, tiled_stages<BM, kFP4A>()>), dim3(grid),
+                     dim3(256), 0, stream, act,
                      act_scale, sorted, offsets, tiles, num_tiles, w13, w13s, T, H, I, Kp,
                      max_tiles, h);
   return hipGetLastError();
@@ -352,7 +384,8 @@ hipError_t launch_down_bm(const void* h, const uint8_t* h_scale, const int32_t* 
                           hipStream_t stream) {
   const long n = (long)max_tiles * (H / 256);
   const unsigned grid = (unsigned)((n + 7) / 8 * 8);
-  hipLaunchKernelGGL((down_tiled_kernel<BM, kFP4A>), dim3(grid), dim3(256), 0, stream, h,
+  hipLaunchKernelGGL((down_tiled_kernel<BM, kFP4A, tiled_stages<BM, kFP4A>()>), dim3(grid),
+                     dim3(256), 0, stream, h,
                      h_scale, offsets, tiles, num_tiles, w2, w2s, A, H, I, max_tiles, y);
   return hipGetLastError();
 }
