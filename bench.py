@@ -38,6 +38,9 @@ def parse():
     p.add_argument("--cpu-tokens", type=int, default=32,
                    help="tokens of the batch the CPU oracle is timed on")
     p.add_argument("--no-cpu", action="store_true", help="skip the cpu_baseline leg")
+    p.add_argument("--pmc-calibrate", action="store_true",
+                   help="first run a plain 1 GiB kernel (torch.bitwise_not) whose HBM bytes are "
+                        "known, for scaling FETCH_SIZE / WRITE_SIZE counter passes")
     return p.parse_args()
 
 
@@ -66,14 +69,30 @@ def make_inputs(cfg):
 
 def algorithmic(cfg, counts):
     """Bytes the layer must move and FLOPs it must do, given the realised
-    per-expert counts (weights of experts that got no token are not counted)."""
+    per-expert counts (weights of experts that got no token are not counted;
+    intermediates such as h and y are implementation traffic, not counted).
+    gate_up's own figure: the touched experts' W13 codes + scales and the
+    activations it reads (bf16 x, or its MXFP4 codes + scales for W4A4)."""
     touched = int((counts > 0).sum())
     w13_e = 2 * cfg.I * cfg.H // 2 + 2 * cfg.I * cfg.H // 32
     w2_e = cfg.H * cfg.I // 2 + cfg.H * cfg.I // 32
     io = cfg.T * cfg.H * 2 + cfg.T * cfg.E * 4 + cfg.T * 4 * cfg.shared + cfg.T * cfg.H * 2
+    x_gu = cfg.T * cfg.H * 2 if cfg.act_fmt == 0 else cfg.T * (cfg.H // 2 + cfg.H // 32)
     return dict(touched=touched, w13_bytes=touched * w13_e, w2_bytes=touched * w2_e,
+                gate_up_bytes=touched * w13_e + x_gu,
                 layer_bytes=touched * (w13_e + w2_e) + io,
                 flops=cfg.A * 6 * cfg.H * cfg.I, gate_up_flops=cfg.A * 4 * cfg.H * cfg.I)
+
+
+def gate_up_kernel_name(cfg, tile_m):
+    """The gate/up kernel's name as rocprofv3 reports it for this shape."""
+    a = "true" if cfg.act_fmt else "false"
+    return f"gate_up_kernel<2, {a}>" if tile_m == 32 else f"gate_up_tiled_kernel<{tile_m}, {a}>"
+
+
+def traffic_path(cfg):
+    return os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles",
+                        f"{cfg.name}_T{cfg.T}_traffic.json")
 
 
 def _pack_expert(args):
@@ -128,6 +147,12 @@ def main():
     cfg = synth.CONFIGS[args.workload]
     log(f"workload {cfg.name}: T={cfg.T} H={cfg.H} I={cfg.I} E={cfg.E} K={cfg.K} "
         f"shared={cfg.shared} act={'mxfp4' if cfg.act_fmt else 'bf16'}")
+    if args.pmc_calibrate:
+        a = torch.zeros(1 << 28, dtype=torch.int32, device="cuda")      # 1 GiB
+        torch.bitwise_not(a, out=torch.empty_like(a))
+        torch.cuda.synchronize()
+        del a
+        torch.cuda.empty_cache()
     x, logits, gate, w13, w13s, w2, w2s = make_inputs(cfg)
     bufs = ops.alloc_stages(cfg.T, cfg.H, cfg.I, cfg.E, cfg.K, cfg.shared, cfg.act_fmt, "cuda")
     ws = torch.empty(ops.workspace_size(cfg.T, cfg.H, cfg.I, cfg.E, cfg.K, cfg.shared, cfg.act_fmt),
@@ -177,18 +202,34 @@ def main():
 
     counts = bufs["align"]["counts"].cpu().numpy()
     alg = algorithmic(cfg, counts)
+    from mxfp4_routed_expert_top_amd import profiling
+    tile_m = ops.gemm_tile_m(cfg.T, cfg.Kp, cfg.Ep, cfg.H, cfg.I, cfg.act_fmt)
+    kname = gate_up_kernel_name(cfg, tile_m)
     gu_s = stage_ms["gate_up"] / 1e3
-    achieved = alg["w13_bytes"] / gu_s / 1e9
+    mfma_peak = BF16_PEAK_TFLOPS if cfg.act_fmt == 0 else MXFP4_PEAK_TFLOPS
+    t_hbm = alg["gate_up_bytes"] / (HBM_PEAK_GBS * 1e9)
+    t_mfma = alg["gate_up_flops"] / (mfma_peak * 1e12)
+    traffic = profiling.load_traffic(traffic_path(cfg), kname)
+    if t_hbm >= t_mfma:
+        achieved = alg["gate_up_bytes"] / gu_s / 1e9
+        roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                    "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4)}
+    else:
+        achieved = alg["gate_up_flops"] / gu_s / 1e12
+        roofline = {"bound": "mfma", "achieved": round(achieved, 1), "peak": mfma_peak,
+                    "unit": "TFLOP/s", "frac": round(achieved / mfma_peak, 4)}
+    roofline.update({"traffic": traffic, "kernel": kname,
+                     "algorithmic_bytes": alg["gate_up_bytes"],
+                     "algorithmic_flops": alg["gate_up_flops"],
+                     "kernel_ms": round(stage_ms["gate_up"], 4)})
     layer_s = ms / 1e3
-    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
-                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
-                "kernel": "gate_up_w4a16_kernel" if cfg.act_fmt == 0 else "gate_up_w4a4_kernel",
-                "algorithmic_bytes": alg["w13_bytes"], "kernel_ms": round(stage_ms["gate_up"], 4)}
+    t_bind = max(alg["layer_bytes"] / (HBM_PEAK_GBS * 1e9), alg["flops"] / (mfma_peak * 1e12))
     layer = {"bytes": alg["layer_bytes"], "flops": alg["flops"], "touched_experts": alg["touched"],
              "hbm_gbs": round(alg["layer_bytes"] / layer_s / 1e9, 1),
              "hbm_frac": round(alg["layer_bytes"] / layer_s / 1e9 / HBM_PEAK_GBS, 4),
              "mxfp4_mfma_frac": round(alg["flops"] / layer_s / 1e12 / MXFP4_PEAK_TFLOPS, 5),
              "bf16_mfma_frac": round(alg["flops"] / layer_s / 1e12 / BF16_PEAK_TFLOPS, 5),
+             "binding_roofline_frac": round(t_bind / layer_s, 4),
              "kernel_ms": {k: round(v, 4) for k, v in stage_ms.items()},
              "down_gbs": round(alg["w2_bytes"] / (stage_ms["down"] / 1e3) / 1e9, 1)}
     cpu = None

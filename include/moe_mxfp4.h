@@ -155,7 +155,10 @@ MOE_API moe_status moe_mxfp4_quantize(const void *src, int32_t src_dtype, int64_
  *     outputs built with the same tile_m
  *   tile_m     rows per tile: 32 selects the weight-streaming kernel (small
  *              groups, decode); 64 or 128 the LDS-tiled kernel (large
- *              groups, prefill; needs H a multiple of 256)
+ *              groups, prefill; needs H a multiple of 256 and H, I at most
+ *              4096 for bf16 activations, 6144 (64-row) or 8192 (128-row)
+ *              for MXFP4 ones: the weight scales of a workgroup's rows sit
+ *              in LDS for the whole reduction)
  *   h          out bf16 [T*Kp, I], sorted row order
  * Errors: INVALID_ARGUMENT, UNSUPPORTED (H or I not a multiple of 128, or a
  * tile_m / shape the kernels do not cover).
@@ -193,9 +196,11 @@ MOE_API moe_status moe_expert_down(const void *h, const uint8_t *h_scale, int32_
 MOE_API moe_status moe_combine(const float *y, const float *topk_weights, const int32_t *inv_assign,
                        int32_t T, int32_t H, int32_t Kp, uint16_t *out, void *stream);
 
-/* The tile_m moe_mxfp4_forward uses for these shapes (A = T*Kp assignments
- * over Ep experts): 32, 64 or 128 (see moe_expert_gate_up). */
-MOE_API int32_t moe_gemm_tile_m(int32_t T, int32_t Kp, int32_t Ep, int32_t H, int32_t I);
+/* The tile_m moe_mxfp4_forward uses for these shapes and activation format
+ * (A = T*Kp assignments over Ep experts): 32, 64 or 128 (see
+ * moe_expert_gate_up). */
+MOE_API int32_t moe_gemm_tile_m(int32_t T, int32_t Kp, int32_t Ep, int32_t H, int32_t I,
+                                int32_t act_fmt);
 
 /* Workspace bytes moe_mxfp4_forward needs (0 for T = 0). */
 MOE_API size_t moe_mxfp4_workspace_size(int32_t T, int32_t H, int32_t I, int32_t E, int32_t K,
@@ -206,7 +211,8 @@ MOE_API size_t moe_mxfp4_workspace_size(int32_t T, int32_t H, int32_t I, int32_t
  * [quantise h], down, combine, all enqueued on `stream`.  The GEMM kernels
  * are chosen on the host from the shapes alone (no device read): average
  * rows per expert T*K'/E' <= 8 -> 32-row weight-streaming tiles, <= 48 ->
- * 64-row LDS-tiled, else 128-row LDS-tiled (when H is a multiple of 256).
+ * 64-row LDS-tiled, else 128-row LDS-tiled (when the shapes fit the tiled
+ * kernels, see moe_expert_gate_up; otherwise 32).
  *   x              bf16 [T, H]
  *   router_logits  fp32 [T, E];  shared_gate_logits fp32 [T] (shared = 1) or NULL
  *   w13, w13_scale, w2, w2_scale: the MXFP4 weights of E + shared experts

@@ -5,13 +5,15 @@
 // for small-M decode and large-M prefill GEMMs and reorder grouped-MoE
 // programs so that neighbours reuse expert-weight tiles from cache (MiniMax
 // M3 on MI355X post, section "Local shape and tiling"); here the block order
-// is remapped so that each XCD (own L2) walks consecutive tiles of one
-// weight slice.
+// is remapped so that each XCD (own L2) runs every weight slice of a tile
+// together and an expert's tiles back to back.
 //
-// Per 128-element K chunk: every wave loads its four strips' codes (16 bytes
-// per lane = one scale block) and scale bytes from HBM, the workgroup
-// gathers the tile's activation chunk into LDS (double-buffered, one barrier
-// per chunk, the next chunk's loads in flight during the MFMAs).
+// The weight scales of the workgroup's rows (whole K) go to LDS once, up
+// front.  Per 128-element K chunk: every wave loads its four strips' codes
+// (16 bytes per lane = one scale block) from HBM into registers and the
+// workgroup gathers the tile's activation chunk into LDS (a 3- or 4-stage
+// pipeline, one barrier per chunk, later chunks' loads in flight during the
+// MFMAs).
 //   W4A16: codes -> bf16 via v_cvt_scalef32_pk_bf16_fp4, v_mfma_f32_16x16x32_bf16,
 //          activations bf16 [rows][128] per chunk in LDS.
 //   W4A4:  codes and E8M0 scales straight into v_mfma_scale_f32_16x16x128_f8f6f4,
@@ -30,39 +32,55 @@ struct TileT {
   int expert, row0, rows;
 };
 
-// Logical block index: the blocks an XCD receives (b = x, x+8, x+16, ...)
-// take consecutive logical indices.  The grid is a multiple of 8.
-__device__ __forceinline__ int xcd_logical(int b, int nblocks) {
-  return (b & 7) * (nblocks >> 3) + (b >> 3);
+// Block -> (tile, weight slice).  The hardware hands workgroup b to XCD
+// b % 8.  The num_tiles * nslices live (tile, slice) pairs, tile-major, are
+// cut into 8 contiguous runs, one per XCD, so that an XCD runs all slices of
+// a tile together (the tile's activation rows are fetched into its L2 once,
+// not once per slice) and consecutive tiles of one expert back to back (its
+// weight slices are re-read from L2).  Blocks past the live pairs exit.
+__device__ __forceinline__ bool tile_slice(int b, int num_tiles, int nslices, int* tile,
+                                           int* slice) {
+  const int live = num_tiles * nslices;
+  const int per = (live + 7) >> 3;
+  const int j = b >> 3;
+  const int L = (b & 7) * per + j;
+  if (j >= per || L >= live) return false;
+  *tile = L / nslices;
+  *slice = L - *tile * nslices;
+  return true;
 }
 
-// The K loop as an NS-stage pipeline.  Stage u holds one 128-element chunk:
-// the tile's activation rows in LDS (written by direct-to-LDS buffer loads,
-// no registers) and each wave's four weight strips (16 bytes per lane) plus
-// their scale bytes in registers.  Iteration c waits for stage c % NS,
-// meets the other waves at the barrier (which also retires every read of
-// the stage about to be refilled), issues chunk c + NS - 1 into that stage
-// and runs the MFMAs of chunk c; NS - 1 chunks stay in flight.
-//
-// Activation layout per stage, rows of the tile in order:
-//   bf16:  256 bytes per row, 16-byte slot p of row r holds piece p ^ (r & 15)
-//   MXFP4: 64 bytes of codes per row, slot p holds piece p ^ ((r >> 2) & 3);
-//          then 4 scale bytes per row (1 KiB reserved)
-// (the XOR swizzle spreads the 16 rows an MFMA operand read touches over all
-// LDS banks).  Loads beyond the tile's rows or past the last chunk use an
-// out-of-range offset: they move no data and every wave issues the same
-// number of loads per stage, so the wait counts are constants.
+// Per-configuration constants.  NS: pipeline stages.  KMAX: the largest
+// reduction length whose weight scales fit the LDS left over by the stages
+// (256 rows x KMAX/32 bytes).  Totals: bf16 128-row 160 KiB (one workgroup
+// per CU), bf16 64-row 80 KiB (two per CU), MXFP4 128-row 100 KiB, MXFP4
+// 64-row 68 KiB (two per CU).
 template <int BM, bool kFP4A>
-constexpr int x_bytes() {
-  return kFP4A ? BM * 64 + 1024 : BM * 256;
-}
+struct TileCfg {
+  static constexpr int NS = (BM == 64 && !kFP4A) ? 3 : 4;
+  static constexpr int KMAX = kFP4A ? (BM == 128 ? 8192 : 6144) : 4096;
+  static constexpr int SCB = 256 * (KMAX / 32);
+  // activation bytes per stage:
+  //   bf16:  256 bytes per row, 16-byte slot p of row r holds piece p ^ (r & 15)
+  //   MXFP4: 64 bytes of codes per row, slot p holds piece p ^ ((r >> 2) & 3);
+  //          then 4 scale bytes per row (1 KiB reserved)
+  // (the XOR swizzle spreads the 16 rows an MFMA operand read touches over all
+  // LDS banks)
+  static constexpr int XB = kFP4A ? BM * 64 + 1024 : BM * 256;
+};
 
-// Each stage ends with the chunk's weight scales of the workgroup's 256
-// weight rows: one dword per row (the row's four scale blocks of the chunk),
-// wave w's 64 rows at [256 w, 256 w + 256).
-template <int BM, bool kFP4A>
-constexpr int stage_bytes() {
-  return x_bytes<BM, kFP4A>() + 1024;
+// Weight scales in LDS: the workgroup's 256 weight rows (wave w's strips are
+// rows [64 w, 64 w + 64)), each Q = K/128 dwords for the whole K, dword c
+// holding chunk c's four scale bytes (K-groups 0..3).  They are loaded once,
+// before the K loop (one request per cache line), not per chunk.  Dword c of
+// row r sits at slot c ^ scale_swizzle(r): the 16 rows one read touches then
+// fall in 16 different banks whatever Q is (for Q = 2^v * odd the rows'
+// natural offsets already differ mod 64 when v <= 2; otherwise the XOR
+// separates the rows that would share a bank).
+__device__ __forceinline__ int scale_swizzle(int r, int Q) {
+  const int v = __builtin_ctz(Q);
+  const int rr = r & 15;
+  return v <= 2 ? 0 : (v < 6 ? rr >> (6 - v) : rr);
 }
 
 // s_waitcnt vmcnt(n) with the other counters left alone (gfx9 encoding).
@@ -91,19 +109,49 @@ __device__ __forceinline__ void load_to_lds4(rsrc_t r, uint32_t voff, uint32_t s
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)lds, 4, (int)voff, (int)soff, 0, 0);
 }
 
-template <int BM, bool kFP4A, int NS>
+// The K loop as an NS-stage pipeline.  Stage u holds one 128-element chunk:
+// the tile's activation rows in LDS (written by direct-to-LDS buffer loads,
+// no registers) and each wave's four weight strips (16 bytes per lane) in
+// registers.  Iteration c waits for stage c % NS, meets the other waves at
+// the barrier (which also retires every read of the stage about to be
+// refilled), issues chunk c + NS - 1 into that stage and runs the MFMAs of
+// chunk c; NS - 1 chunks stay in flight.  Loads beyond the tile's rows or
+// past the last chunk use an out-of-range offset: they move no data and
+// every wave issues the same number of loads per stage, so the wait counts
+// are constants.  MFMAs run only on the tile's live 16-row sub-tiles.
+template <int BM, bool kFP4A>
 struct TiledGemm {
+  static constexpr int NS = TileCfg<BM, kFP4A>::NS;
+  static constexpr int XB = TileCfg<BM, kFP4A>::XB;
   static constexpr int MT = BM / 16;
   static constexpr int XI = kFP4A ? BM / 64 : BM / 16;   // code / row loads per wave per stage
-  static constexpr int LPS = XI + (kFP4A ? 1 : 0) + 5;     // vmem ops per wave per stage
-  static constexpr int SB = stage_bytes<BM, kFP4A>();
+  static constexpr int LPS = XI + (kFP4A ? 1 : 0) + 4;     // vmem ops per wave per stage
 
   rsrc_t w, ws, a, as;
   uint32_t wo[4];               // lane's weight row offsets (+16 g)
-  uint32_t wso;                 // scale dword of weight row (64 w + l) of the workgroup
   uint32_t xo[XI];              // lane's activation source offsets (or kOOR)
   uint32_t xso;                 // MXFP4 activation scale source offset (or kOOR)
-  int wave, lane, nl, g, nch;
+  uint32_t sro;                 // lane's scale byte offset in LDS for strip 0 (row 64 wave + nl, + g)
+  int wave, lane, nl, g, nch, Q, swz;
+
+  // Weight scales of the workgroup's rows into LDS (all K): wave w fills its
+  // 64 rows, Q size-4 loads per lane; grow(r) = weight row of workgroup row r.
+  template <class RowFn>
+  __device__ __forceinline__ void load_scales(uint8_t* sc, uint32_t row_bytes, RowFn grow) const {
+    const int step_r = 64 / Q, step_s = 64 % Q;
+    int r = 64 * wave + lane / Q, sl = lane % Q;
+    uint8_t* dst = sc + 4 * 64 * wave * Q;
+    for (int i = 0; i < Q; ++i) {
+      const int c = sl ^ scale_swizzle(r, Q);
+      load_to_lds4(ws, grow(r) * row_bytes + 4 * c, 0, dst + 256 * i);
+      r += step_r;
+      sl += step_s;
+      if (sl >= Q) {
+        sl -= Q;
+        ++r;
+      }
+    }
+  }
 
   // Issue chunk c into a stage (weight codes into registers q).
   __device__ __forceinline__ void issue(uint8_t* base, int c, u32x4_t (&q)[4]) const {
@@ -120,19 +168,21 @@ struct TiledGemm {
       for (int i = 0; i < XI; ++i)
         load_to_lds16(a, xo[i] | oor, 256 * cc, base + (wave * XI + i) * 1024);
     }
-    load_to_lds4(ws, wso | oor, 4 * cc, base + x_bytes<BM, kFP4A>() + wave * 256);
 #pragma unroll
     for (int t = 0; t < 4; ++t) q[t] = bload16(w, wo[t] | oor, 64 * cc);
   }
 
-  __device__ __forceinline__ void compute(const uint8_t* x, const u32x4_t (&q)[4],
-                                          floatx4_t (&acc)[MT][4]) const {
+  // MFMAs of one chunk on the first NMT 16-row sub-tiles (the live ones).
+  template <int NMT>
+  __device__ __forceinline__ void compute(const uint8_t* x, const uint8_t* sc, int c,
+                                          const u32x4_t (&q)[4], floatx4_t (&acc)[MT][4]) const {
     uint32_t s[4];
+    const uint32_t so = sro + 4 * (uint32_t)(c ^ swz);
 #pragma unroll
-    for (int t = 0; t < 4; ++t) s[t] = x[x_bytes<BM, kFP4A>() + wave * 256 + (16 * t + nl) * 4 + g];
+    for (int t = 0; t < 4; ++t) s[t] = sc[so + 64 * t * Q];   // strip t: rows + 16 t
     if constexpr (kFP4A) {
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt) {
+      for (int mt = 0; mt < NMT; ++mt) {
         const int r = 16 * mt + nl;
         const u32x4_t av =
             *reinterpret_cast<const u32x4_t*>(x + r * 64 + 16 * (g ^ ((r >> 2) & 3)));
@@ -141,16 +191,16 @@ struct TiledGemm {
         for (int t = 0; t < 4; ++t) acc[mt][t] = mfma_fp4_16x16x128(av, sa, q[t], s[t], acc[mt][t]);
       }
     } else {
-      float sc[4];
+      float scf[4];
 #pragma unroll
-      for (int t = 0; t < 4; ++t) sc[t] = e8m0_to_f32(s[t]);
+      for (int t = 0; t < 4; ++t) scf[t] = e8m0_to_f32(s[t]);
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         bf16x8_t b[4];
 #pragma unroll
-        for (int t = 0; t < 4; ++t) b[t] = dequant8_bf16(q[t][j], sc[t]);
+        for (int t = 0; t < 4; ++t) b[t] = dequant8_bf16(q[t][j], scf[t]);
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt) {
+        for (int mt = 0; mt < NMT; ++mt) {
           const int r = 16 * mt + nl;
           const bf16x8_t av = *reinterpret_cast<const bf16x8_t*>(
               x + r * 256 + 16 * ((4 * g + j) ^ (r & 15)));
@@ -162,10 +212,13 @@ struct TiledGemm {
   }
 
   // stages[u]: one LDS array per stage (separate objects, so the compiler's
-  // wait before reading stage u only covers the loads into stage u).
-  __device__ __forceinline__ void run(uint8_t* const (&stages)[NS],
-                                      floatx4_t (&acc)[MT][4]) const {
+  // wait before reading stage u only covers the loads into stage u).  The
+  // scale loads, issued first, are complete once the first stage is.
+  template <int NMT, class RowFn>
+  __device__ __forceinline__ void run(uint8_t* const (&stages)[NS], uint8_t* sc, uint32_t srow_bytes,
+                                      RowFn grow, floatx4_t (&acc)[MT][4]) const {
     u32x4_t q[NS][4];
+    load_scales(sc, srow_bytes, grow);
 #pragma unroll
     for (int u = 0; u < NS - 1; ++u) issue(stages[u], u, q[u]);
     for (int c0 = 0; c0 < nch; c0 += NS) {
@@ -175,7 +228,7 @@ struct TiledGemm {
         wait_vmcnt<LPS * (NS - 2)>();
         stage_barrier();
         issue(stages[(u + NS - 1) % NS], c + NS - 1, q[(u + NS - 1) % NS]);
-        if (c < nch) compute(stages[u], q[u], acc);
+        if (c < nch) compute<NMT>(stages[u], sc, c, q[u], acc);
       }
     }
     wait_vmcnt<0>();
@@ -183,19 +236,18 @@ struct TiledGemm {
 };
 
 template <int BM>
-__device__ __forceinline__ bool tile_of(const int32_t* tiles, const int32_t* num_tiles,
-                                        const int32_t* offsets, int tile, TileT* ti) {
-  if (tile >= *num_tiles) return false;
-  ti->expert = tiles[2 * tile];
-  ti->row0 = tiles[2 * tile + 1];
-  ti->rows = min(BM, offsets[ti->expert + 1] - ti->row0);
-  return true;
+__device__ __forceinline__ TileT tile_of(const int32_t* tiles, const int32_t* offsets, int tile) {
+  TileT ti;
+  ti.expert = tiles[2 * tile];
+  ti.row0 = tiles[2 * tile + 1];
+  ti.rows = min(BM, offsets[ti.expert + 1] - ti.row0);
+  return ti;
 }
 
 // The lane's activation source offsets for every stage: row r of the tile
 // comes from source row src_row(r) (a token for gate/up, a sorted row for down).
-template <int BM, bool kFP4A, int NS>
-__device__ __forceinline__ void plan_x(TiledGemm<BM, kFP4A, NS>& G, const int32_t* sorted, int Kp,
+template <int BM, bool kFP4A>
+__device__ __forceinline__ void plan_x(TiledGemm<BM, kFP4A>& G, const int32_t* sorted, int Kp,
                                        int T, const TileT& ti, bool gather, uint32_t row_bytes,
                                        uint32_t scale_bytes) {
   auto src_row = [&](int r) -> uint32_t {
@@ -225,61 +277,110 @@ __device__ __forceinline__ void plan_x(TiledGemm<BM, kFP4A, NS>& G, const int32_
   }
 }
 
+// Common set-up of a workgroup's GEMM state (weights of one expert slice;
+// K = reduction length; rs = K/32 scale bytes per weight row).
+template <int BM, bool kFP4A>
+__device__ __forceinline__ void setup(TiledGemm<BM, kFP4A>& G, const TileT& ti, int K,
+                                      const uint8_t* wq, const uint8_t* wsc, int wrows) {
+  G.lane = threadIdx.x & 63;
+  G.wave = threadIdx.x >> 6;
+  G.nl = G.lane & 15;
+  G.g = G.lane >> 4;
+  G.nch = K / 128;
+  G.Q = K / 128;
+  G.swz = scale_swizzle(G.nl, G.Q);
+  G.sro = 4 * (64 * G.wave + G.nl) * G.Q + G.g;
+  const size_t wbytes = (size_t)wrows * (K / 2), sbytes = (size_t)wrows * (K / 32);
+  G.w = make_rsrc(wq + ti.expert * wbytes, (uint32_t)wbytes);
+  G.ws = make_rsrc(wsc + ti.expert * sbytes, (uint32_t)sbytes);
+}
+
+// Static LDS of a kernel: NS stage arrays (separate objects) and the scale
+// array; body(stages, scales) runs with them.
+template <int BM, bool kFP4A, class Body>
+__device__ __forceinline__ void with_lds(Body&& body) {
+  constexpr int XB = TileCfg<BM, kFP4A>::XB, SCB = TileCfg<BM, kFP4A>::SCB;
+  __shared__ __align__(16) uint8_t sc[SCB];
+  __shared__ __align__(16) uint8_t st0[XB];
+  __shared__ __align__(16) uint8_t st1[XB];
+  __shared__ __align__(16) uint8_t st2[XB];
+  if constexpr (TileCfg<BM, kFP4A>::NS == 4) {
+    __shared__ __align__(16) uint8_t st3[XB];
+    uint8_t* const stages[4] = {st0, st1, st2, st3};
+    body(stages, sc);
+  } else {
+    static_assert(TileCfg<BM, kFP4A>::NS == 3, "three or four stages");
+    uint8_t* const stages[3] = {st0, st1, st2};
+    body(stages, sc);
+  }
+}
+
+template <int N>
+struct IntC {
+  static constexpr int value = N;
+};
+
+// Calls f(IntC<NMT>) with the number of 16-row sub-tiles the MFMAs cover:
+// the live ones (ceil(rows / 16)), rounded up to an even count for 128-row
+// tiles (four code variants per kernel instead of eight).
+template <int BM, class F>
+__device__ __forceinline__ void with_nmt(int rows, F&& f) {
+  const int need = (rows + 15) >> 4;
+  if constexpr (BM == 128) {
+    if (need > 6) f(IntC<8>());
+    else if (need > 4) f(IntC<6>());
+    else if (need > 2) f(IntC<4>());
+    else f(IntC<2>());
+  } else {
+    static_assert(BM == 64, "64- or 128-row tiles");
+    if (need > 3) f(IntC<4>());
+    else if (need > 2) f(IntC<3>());
+    else if (need > 1) f(IntC<2>());
+    else f(IntC<1>());
+  }
+}
+
 // gate/up + SwiGLU: weight rows gate [i0, i0 + 128) and up [I + i0, I + i0 + 128),
 // i0 = 128 s; wave w owns i in [i0 + 32 w, i0 + 32 w + 32): strips gate lo/hi, up lo/hi.
-template <int BM, bool kFP4A, int NS>
+template <int BM, bool kFP4A>
 __global__ __launch_bounds__(256) void gate_up_tiled_kernel(
     const void* __restrict__ act, const uint8_t* __restrict__ act_scale,
     const int32_t* __restrict__ sorted, const int32_t* __restrict__ offsets,
     const int32_t* __restrict__ tiles, const int32_t* __restrict__ num_tiles,
     const uint8_t* __restrict__ w13, const uint8_t* __restrict__ w13s, int T, int H, int I, int Kp,
-    int max_tiles, uint16_t* __restrict__ h) {
-  __shared__ __align__(16) uint8_t st0[stage_bytes<BM, kFP4A>()];
-  __shared__ __align__(16) uint8_t st1[stage_bytes<BM, kFP4A>()];
-  __shared__ __align__(16) uint8_t st2[stage_bytes<BM, kFP4A>()];
-  __shared__ __align__(16) uint8_t st3[stage_bytes<BM, kFP4A>()];
-  static_assert(NS == 4, "four LDS stages");
-  uint8_t* const stages[NS] = {st0, st1, st2, st3};
-  const int L = xcd_logical(blockIdx.x, gridDim.x);
-  const int s = L / max_tiles;
-  if (s >= I / 128) return;
-  TileT ti;
-  if (!tile_of<BM>(tiles, num_tiles, offsets, L % max_tiles, &ti)) return;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int nl = lane & 15, g = lane >> 4;
+    uint16_t* __restrict__ h) {
+  int tile, s;
+  if (!tile_slice(blockIdx.x, *num_tiles, I / 128, &tile, &s)) return;
+  const TileT ti = tile_of<BM>(tiles, offsets, tile);
+  TiledGemm<BM, kFP4A> G;
+  setup(G, ti, H, w13, w13s, 2 * I);
+  const int nl = G.nl, g = G.g;
   const uint32_t rb = H / 2, rs = H / 32;
-  const size_t wbytes = (size_t)2 * I * rb, sbytes = (size_t)2 * I * rs;
-  TiledGemm<BM, kFP4A, NS> G;
-  G.wave = wave;
-  G.lane = lane;
-  G.nl = nl;
-  G.g = g;
-  G.w = make_rsrc(w13 + ti.expert * wbytes, (uint32_t)wbytes);
-  G.ws = make_rsrc(w13s + ti.expert * sbytes, (uint32_t)sbytes);
-  const int i0 = s * 128 + wave * 32;
+  const int i0 = s * 128 + G.wave * 32;
   const int rows4[4] = {i0 + nl, i0 + 16 + nl, I + i0 + nl, I + i0 + 16 + nl};
 #pragma unroll
   for (int st = 0; st < 4; ++st) G.wo[st] = rows4[st] * rb + 16 * g;
-  {
-    const int t = lane >> 4, rr = lane & 15;                // scale row (16 t + rr) of the wave
-    const int row = (t < 2 ? i0 : I + i0) + 16 * (t & 1) + rr;
-    G.wso = row * rs;
-  }
   if (kFP4A) {
     G.a = make_rsrc(act, (uint32_t)((size_t)T * rb));
     G.as = make_rsrc(act_scale, (uint32_t)((size_t)T * rs));
   } else {
     G.a = make_rsrc(act, (uint32_t)((size_t)T * H * 2));
   }
-  G.nch = H / 128;
-  plan_x<BM, kFP4A, NS>(G, sorted, Kp, T, ti, true, kFP4A ? rb : (uint32_t)H * 2, rs);
+  plan_x<BM, kFP4A>(G, sorted, Kp, T, ti, true, kFP4A ? rb : (uint32_t)H * 2, rs);
+  // workgroup row r (wave r/64, strip (r/16)%4, lane row r%16) -> weight row
+  auto grow = [&](int r) -> uint32_t {
+    const int t = (r >> 4) & 3;
+    return (uint32_t)((t < 2 ? 0 : I) + s * 128 + 32 * (r >> 6) + 16 * (t & 1) + (r & 15));
+  };
 
   floatx4_t acc[BM / 16][4];
 #pragma unroll
   for (int mt = 0; mt < BM / 16; ++mt)
 #pragma unroll
     for (int st = 0; st < 4; ++st) acc[mt][st] = (floatx4_t){0.f, 0.f, 0.f, 0.f};
-  G.run(stages, acc);
+  with_lds<BM, kFP4A>([&](auto& stages, uint8_t* sc) {
+    with_nmt<BM>(ti.rows, [&](auto n) { G.template run<decltype(n)::value>(stages, sc, rs, grow, acc); });
+  });
 
 #pragma unroll
   for (int mt = 0; mt < BM / 16; ++mt)
@@ -295,53 +396,39 @@ __global__ __launch_bounds__(256) void gate_up_tiled_kernel(
 }
 
 // down: weight rows j in [256 s, 256 s + 256); wave w owns [256 s + 64 w, +64).
-template <int BM, bool kFP4A, int NS>
+template <int BM, bool kFP4A>
 __global__ __launch_bounds__(256) void down_tiled_kernel(
     const void* __restrict__ hin, const uint8_t* __restrict__ hscale,
     const int32_t* __restrict__ offsets, const int32_t* __restrict__ tiles,
     const int32_t* __restrict__ num_tiles, const uint8_t* __restrict__ w2,
-    const uint8_t* __restrict__ w2s, int A, int H, int I, int max_tiles, float* __restrict__ y) {
-  __shared__ __align__(16) uint8_t st0[stage_bytes<BM, kFP4A>()];
-  __shared__ __align__(16) uint8_t st1[stage_bytes<BM, kFP4A>()];
-  __shared__ __align__(16) uint8_t st2[stage_bytes<BM, kFP4A>()];
-  __shared__ __align__(16) uint8_t st3[stage_bytes<BM, kFP4A>()];
-  static_assert(NS == 4, "four LDS stages");
-  uint8_t* const stages[NS] = {st0, st1, st2, st3};
-  const int L = xcd_logical(blockIdx.x, gridDim.x);
-  const int s = L / max_tiles;
-  if (s >= H / 256) return;
-  TileT ti;
-  if (!tile_of<BM>(tiles, num_tiles, offsets, L % max_tiles, &ti)) return;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int nl = lane & 15, g = lane >> 4;
+    const uint8_t* __restrict__ w2s, int A, int H, int I, float* __restrict__ y) {
+  int tile, s;
+  if (!tile_slice(blockIdx.x, *num_tiles, H / 256, &tile, &s)) return;
+  const TileT ti = tile_of<BM>(tiles, offsets, tile);
+  TiledGemm<BM, kFP4A> G;
+  setup(G, ti, I, w2, w2s, H);
+  const int nl = G.nl, g = G.g;
   const uint32_t rb = I / 2, rs = I / 32;
-  const size_t wbytes = (size_t)H * rb, sbytes = (size_t)H * rs;
-  TiledGemm<BM, kFP4A, NS> G;
-  G.wave = wave;
-  G.lane = lane;
-  G.nl = nl;
-  G.g = g;
-  G.w = make_rsrc(w2 + ti.expert * wbytes, (uint32_t)wbytes);
-  G.ws = make_rsrc(w2s + ti.expert * sbytes, (uint32_t)sbytes);
-  const int j0 = s * 256 + wave * 64;
+  const int j0 = s * 256 + G.wave * 64;
 #pragma unroll
   for (int st = 0; st < 4; ++st) G.wo[st] = (j0 + 16 * st + nl) * rb + 16 * g;
-  G.wso = (j0 + lane) * rs;                                   // scale row 16 t + rr = lane
   if (kFP4A) {
     G.a = make_rsrc(hin, (uint32_t)((size_t)A * rb));
     G.as = make_rsrc(hscale, (uint32_t)((size_t)A * rs));
   } else {
     G.a = make_rsrc(hin, (uint32_t)((size_t)A * I * 2));
   }
-  G.nch = I / 128;
-  plan_x<BM, kFP4A, NS>(G, nullptr, 1, A, ti, false, kFP4A ? rb : (uint32_t)I * 2, rs);
+  plan_x<BM, kFP4A>(G, nullptr, 1, A, ti, false, kFP4A ? rb : (uint32_t)I * 2, rs);
+  auto grow = [&](int r) -> uint32_t { return (uint32_t)(s * 256 + r); };
 
   floatx4_t acc[BM / 16][4];
 #pragma unroll
   for (int mt = 0; mt < BM / 16; ++mt)
 #pragma unroll
     for (int st = 0; st < 4; ++st) acc[mt][st] = (floatx4_t){0.f, 0.f, 0.f, 0.f};
-  G.run(stages, acc);
+  with_lds<BM, kFP4A>([&](auto& stages, uint8_t* sc) {
+    with_nmt<BM>(ti.rows, [&](auto n) { G.template run<decltype(n)::value>(stages, sc, rs, grow, acc); });
+  });
 
 #pragma unroll
   for (int mt = 0; mt < BM / 16; ++mt)
@@ -356,12 +443,6 @@ __global__ __launch_bounds__(256) void down_tiled_kernel(
     }
 }
 
-// Pipeline depth: 4 stages (128 KiB of LDS for 128-row bf16 tiles).
-template <int BM, bool kFP4A>
-constexpr int tiled_stages() {
-  return 4;
-}
-
 template <int BM, bool kFP4A>
 hipError_t launch_gate_up_bm(const void* act, const uint8_t* act_scale, const int32_t* sorted,
                              const int32_t* offsets, const int32_t* tiles,
@@ -370,10 +451,8 @@ hipError_t launch_gate_up_bm(const void* act, const uint8_t* act_scale, const in
                              hipStream_t stream) {
   const long n = (long)max_tiles * (I / 128);
   const unsigned grid = (unsigned)((n + 7) / 8 * 8);
-  hipLaunchKernelGGL((gate_up_tiled_kernel<BM, kFP4A, tiled_stages<BM, kFP4A>()>), dim3(grid),
-                     dim3(256), 0, stream, act,
-                     act_scale, sorted, offsets, tiles, num_tiles, w13, w13s, T, H, I, Kp,
-                     max_tiles, h);
+  hipLaunchKernelGGL((gate_up_tiled_kernel<BM, kFP4A>), dim3(grid), dim3(256), 0, stream, act,
+                     act_scale, sorted, offsets, tiles, num_tiles, w13, w13s, T, H, I, Kp, h);
   return hipGetLastError();
 }
 
@@ -384,16 +463,23 @@ hipError_t launch_down_bm(const void* h, const uint8_t* h_scale, const int32_t* 
                           hipStream_t stream) {
   const long n = (long)max_tiles * (H / 256);
   const unsigned grid = (unsigned)((n + 7) / 8 * 8);
-  hipLaunchKernelGGL((down_tiled_kernel<BM, kFP4A, tiled_stages<BM, kFP4A>()>), dim3(grid),
-                     dim3(256), 0, stream, h,
-                     h_scale, offsets, tiles, num_tiles, w2, w2s, A, H, I, max_tiles, y);
+  hipLaunchKernelGGL((down_tiled_kernel<BM, kFP4A>), dim3(grid), dim3(256), 0, stream, h,
+                     h_scale, offsets, tiles, num_tiles, w2, w2s, A, H, I, y);
   return hipGetLastError();
+}
+
+template <int BM, bool kFP4A>
+bool fits(int H, int I) {
+  return H <= TileCfg<BM, kFP4A>::KMAX && I <= TileCfg<BM, kFP4A>::KMAX;
 }
 
 }  // namespace
 
-bool expert_gemm_tiled_supported(int tile_m, int H, int I) {
-  return (tile_m == 64 || tile_m == 128) && H % 256 == 0 && I % 128 == 0;
+bool expert_gemm_tiled_supported(int tile_m, int act_fmt, int H, int I) {
+  if (H % 256 || I % 128 || H <= 0 || I <= 0) return false;
+  if (tile_m == 64) return act_fmt ? fits<64, true>(H, I) : fits<64, false>(H, I);
+  if (tile_m == 128) return act_fmt ? fits<128, true>(H, I) : fits<128, false>(H, I);
+  return false;
 }
 
 hipError_t launch_gate_up_tiled(int tile_m, int act_fmt, const void* act, const uint8_t* act_scale,

@@ -30,7 +30,7 @@ hipError_t launch_down(int act_fmt, const void* h, const uint8_t* h_scale, const
 hipError_t launch_combine(const float* y, const float* w, const int32_t* inv, int T, int H, int Kp,
                           uint16_t* out, hipStream_t stream);
 
-bool expert_gemm_tiled_supported(int tile_m, int H, int I);
+bool expert_gemm_tiled_supported(int tile_m, int act_fmt, int H, int I);
 hipError_t launch_gate_up_tiled(int tile_m, int act_fmt, const void* act, const uint8_t* act_scale,
                                 const int32_t* sorted, const int32_t* offsets,
                                 const int32_t* tiles, const int32_t* num_tiles, int max_tiles,

@@ -24,15 +24,15 @@ inline int64_t max_tiles_for(int64_t A, int64_t Ep, int64_t tile_m = MOE_TILE_M)
 
 // Rows per GEMM tile for a call, from the shapes alone: small groups stream
 // weights through 32-row tiles; larger groups use the LDS-tiled kernels.
-int choose_tile_m(int64_t A, int64_t Ep, int H, int I) {
+int choose_tile_m(int64_t A, int64_t Ep, int H, int I, int act_fmt) {
   const int64_t avg = A / Ep;
   if (avg <= 8) return MOE_TILE_M;
   const int tm = avg <= 48 ? 64 : 128;
-  return expert_gemm_tiled_supported(tm, H, I) ? tm : MOE_TILE_M;
+  return expert_gemm_tiled_supported(tm, act_fmt, H, I) ? tm : MOE_TILE_M;
 }
 
-bool tile_m_ok(int32_t tile_m, int32_t H, int32_t I) {
-  return tile_m == MOE_TILE_M || expert_gemm_tiled_supported(tile_m, H, I);
+bool tile_m_ok(int32_t tile_m, int32_t act_fmt, int32_t H, int32_t I) {
+  return tile_m == MOE_TILE_M || expert_gemm_tiled_supported(tile_m, act_fmt, H, I);
 }
 
 moe_status check_shape_HI(int32_t H, int32_t I) {
@@ -158,7 +158,7 @@ moe_status moe_expert_gate_up(const void* act, const uint8_t* act_scale, int32_t
     return MOE_ERR_INVALID_ARGUMENT;
   moe_status st = check_shape_HI(H, I);
   if (st != MOE_OK) return st;
-  if (Ep > 2048 || !tile_m_ok(tile_m, H, I)) return MOE_ERR_UNSUPPORTED;
+  if (Ep > 2048 || !tile_m_ok(tile_m, act_fmt, H, I)) return MOE_ERR_UNSUPPORTED;
   if (T == 0) return MOE_OK;
   if (!act || !sorted_assign || !expert_offsets || !tile_table || !num_tiles || !w13 ||
       !w13_scale || !h || (act_fmt == MOE_ACT_MXFP4 && !act_scale))
@@ -184,7 +184,7 @@ moe_status moe_expert_down(const void* h, const uint8_t* h_scale, int32_t act_fm
     return MOE_ERR_INVALID_ARGUMENT;
   moe_status st = check_shape_HI(H, I);
   if (st != MOE_OK) return st;
-  if (Ep > 2048 || !tile_m_ok(tile_m, H, I)) return MOE_ERR_UNSUPPORTED;
+  if (Ep > 2048 || !tile_m_ok(tile_m, act_fmt, H, I)) return MOE_ERR_UNSUPPORTED;
   if (T == 0) return MOE_OK;
   if (!h || !expert_offsets || !tile_table || !num_tiles || !w2 || !w2_scale || !y ||
       (act_fmt == MOE_ACT_MXFP4 && !h_scale))
@@ -210,9 +210,10 @@ moe_status moe_combine(const float* y, const float* topk_weights, const int32_t*
   return from_hip(launch_combine(y, topk_weights, inv_assign, T, H, Kp, out, as_stream(stream)));
 }
 
-int32_t moe_gemm_tile_m(int32_t T, int32_t Kp, int32_t Ep, int32_t H, int32_t I) {
+int32_t moe_gemm_tile_m(int32_t T, int32_t Kp, int32_t Ep, int32_t H, int32_t I,
+                        int32_t act_fmt) {
   if (T <= 0 || Kp < 1 || Ep < 1 || H <= 0 || I <= 0) return MOE_TILE_M;
-  return choose_tile_m((int64_t)T * Kp, Ep, H, I);
+  return choose_tile_m((int64_t)T * Kp, Ep, H, I, act_fmt);
 }
 
 size_t moe_mxfp4_workspace_size(int32_t T, int32_t H, int32_t I, int32_t E, int32_t K,
@@ -261,7 +262,7 @@ moe_status moe_mxfp4_forward(const uint16_t* x, const float* router_logits,
   uint8_t* hs = (uint8_t*)(ws + L.hs);
   float* y = (float*)(ws + L.y);
   hipStream_t s = as_stream(stream);
-  const int tm = choose_tile_m(A, Ep, H, I);
+  const int tm = choose_tile_m(A, Ep, H, I, act_fmt);
   const int mt = (int)max_tiles_for(A, Ep, tm);
 
   hipError_t e = launch_route_topk(router_logits, shared_gate_logits, T, E, K, shared, 1, ids, wts, s);

@@ -39,7 +39,7 @@ _SIGS = {
     "moe_expert_down": (_I32, [_P, _P, _I32, _P, _P, _P, _I32, _P, _P, _I32, _I32, _I32, _I32,
                                _I32, _P, _P]),
     "moe_combine": (_I32, [_P, _P, _P, _I32, _I32, _I32, _P, _P]),
-    "moe_gemm_tile_m": (_I32, [_I32, _I32, _I32, _I32, _I32]),
+    "moe_gemm_tile_m": (_I32, [_I32, _I32, _I32, _I32, _I32, _I32]),
     "moe_mxfp4_workspace_size": (_SZ, [_I32, _I32, _I32, _I32, _I32, _I32, _I32]),
     "moe_mxfp4_forward": (_I32, [_P, _P, _P, _P, _P, _P, _P, _I32, _I32, _I32, _I32, _I32, _I32,
                                  _I32, _P, _P, _P, _P, _SZ, _P]),
@@ -170,9 +170,9 @@ def mxfp4_quantize(src, packed=None, scales=None, stream=None):
     return packed, scales
 
 
-def gemm_tile_m(T: int, Kp: int, Ep: int, H: int, I: int) -> int:
+def gemm_tile_m(T: int, Kp: int, Ep: int, H: int, I: int, act_fmt: int = ACT_BF16) -> int:
     """moe_gemm_tile_m: the GEMM tile rows mxfp4_forward uses for these shapes."""
-    return int(lib().moe_gemm_tile_m(T, Kp, Ep, H, I))
+    return int(lib().moe_gemm_tile_m(T, Kp, Ep, H, I, act_fmt))
 
 
 def expert_gate_up(act, act_scale, act_fmt: int, align: dict, w13, w13_scale, T: int, H: int,
@@ -271,7 +271,7 @@ def forward_stages(x, router_logits, shared_gate_logits, w13, w13_scale, w2, w2_
                topk_weights=b["w"], stream=stream)
     rec("route", 1)
     rec("align", 0)
-    align_sort(b["ids"], Ep, tile_m=gemm_tile_m(T, Kp, Ep, H, I), out=b["align"], stream=stream)
+    align_sort(b["ids"], Ep, tile_m=gemm_tile_m(T, Kp, Ep, H, I, act_fmt), out=b["align"], stream=stream)
     rec("align", 1)
     act, act_s = x, None
     if act_fmt == ACT_MXFP4:

@@ -98,6 +98,8 @@ def test_gemm_and_combine_argument_errors():
     assert call(gu, base, a12=96) == UNSUPPORTED           # I % 128
     assert call(gu, base, a7=48) == UNSUPPORTED            # no kernel for 48-row tiles
     assert call(gu, base, a7=128, a11=384) == UNSUPPORTED  # tiled kernels need H % 256
+    assert call(gu, base, a7=128, a11=6144, a10=0) == UNSUPPORTED  # bf16 tiled: H <= 4096
+    assert call(gu, base, a7=128, a11=6144, a2=1, a1=FAKE, a10=0) == OK   # MXFP4: H <= 8192
     assert call(gu, base, a0=MIS) == INVALID
     assert call(gu, base, a10=0) == OK
     dn = ops.lib().moe_expert_down
@@ -118,6 +120,10 @@ def test_gemm_tile_choice():
     assert ops.gemm_tile_m(1536, 11, 513, 4096, 1024) == 64
     assert ops.gemm_tile_m(8192, 11, 513, 4096, 1024) == 128
     assert ops.gemm_tile_m(8192, 11, 513, 384, 1024) == 32      # H % 256 != 0
+    # the tiled kernels keep a workgroup's weight scales for the whole K in LDS
+    assert ops.gemm_tile_m(4096, 9, 257, 6144, 1536, ops.ACT_MXFP4) == 128
+    assert ops.gemm_tile_m(4096, 9, 257, 6144, 1536, ops.ACT_BF16) == 32
+    assert ops.gemm_tile_m(8192, 11, 513, 4096, 4608, ops.ACT_BF16) == 32
 
 
 def test_forward_argument_errors_and_workspace():
