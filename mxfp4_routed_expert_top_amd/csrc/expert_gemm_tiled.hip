@@ -51,22 +51,23 @@ __device__ __forceinline__ bool tile_slice(int b, int num_tiles, int nslices, in
 }
 
 // Per-configuration constants.  NS: pipeline stages.  KMAX: the largest
-// reduction length whose weight scales fit the LDS left over by the stages
-// (256 rows x KMAX/32 bytes).  Totals: bf16 128-row 160 KiB (one workgroup
-// per CU), bf16 64-row 80 KiB (two per CU), MXFP4 128-row 100 KiB, MXFP4
-// 64-row 68 KiB (two per CU).
+// reduction length whose scales fit the LDS left over by the stages (256
+// weight rows x KMAX/32 bytes, plus the tile's activation rows for MXFP4).
+// Totals: bf16 128-row 160 KiB (one workgroup per CU), bf16 64-row 80 KiB
+// (two per CU), MXFP4 128-row 128 KiB, MXFP4 64-row 76 KiB (two per CU).
 template <int BM, bool kFP4A>
 struct TileCfg {
   static constexpr int NS = (BM == 64 && !kFP4A) ? 3 : 4;
   static constexpr int KMAX = kFP4A ? (BM == 128 ? 8192 : 6144) : 4096;
-  static constexpr int SCB = 256 * (KMAX / 32);
+  static constexpr int SCB = 256 * (KMAX / 32);             // weight scales
+  // MXFP4 activation scales of the tile's rows (whole K), BM/4 rows per wave
+  static constexpr int ASB = kFP4A ? 4 * ((BM / 4 * (KMAX / 128) + 63) / 64) * 256 : 0;
   // activation bytes per stage:
   //   bf16:  256 bytes per row, 16-byte slot p of row r holds piece p ^ (r & 15)
-  //   MXFP4: 64 bytes of codes per row, slot p holds piece p ^ ((r >> 2) & 3);
-  //          then 4 scale bytes per row (1 KiB reserved)
+  //   MXFP4: 64 bytes of codes per row, slot p holds piece p ^ ((r >> 2) & 3)
   // (the XOR swizzle spreads the 16 rows an MFMA operand read touches over all
   // LDS banks)
-  static constexpr int XB = kFP4A ? BM * 64 + 1024 : BM * 256;
+  static constexpr int XB = kFP4A ? BM * 64 : BM * 256;
 };
 
 // Weight scales in LDS: the workgroup's 256 weight rows (wave w's strips are
@@ -125,25 +126,29 @@ struct TiledGemm {
   static constexpr int XB = TileCfg<BM, kFP4A>::XB;
   static constexpr int MT = BM / 16;
   static constexpr int XI = kFP4A ? BM / 64 : BM / 16;   // code / row loads per wave per stage
-  static constexpr int LPS = XI + (kFP4A ? 1 : 0) + 4;     // vmem ops per wave per stage
+  static constexpr int LPS = XI + 4;                       // vmem ops per wave per stage
 
   rsrc_t w, ws, a, as;
   uint32_t wo[4];               // lane's weight row offsets (+16 g)
   uint32_t xo[XI];              // lane's activation source offsets (or kOOR)
-  uint32_t xso;                 // MXFP4 activation scale source offset (or kOOR)
   uint32_t sro;                 // lane's scale byte offset in LDS for strip 0 (row 64 wave + nl, + g)
   int wave, lane, nl, g, nch, Q, swz;
 
-  // Weight scales of the workgroup's rows into LDS (all K): wave w fills its
-  // 64 rows, Q size-4 loads per lane; grow(r) = weight row of workgroup row r.
-  template <class RowFn>
-  __device__ __forceinline__ void load_scales(uint8_t* sc, uint32_t row_bytes, RowFn grow) const {
+  // Scale rows (Q dwords each, whole K) into LDS: wave w fills rows
+  // [RW w, RW w + RW), its region padded to whole 64-lane loads (size-4
+  // direct-to-LDS loads); dword c of row r lands at slot c ^ swizzle(r).
+  // src(r) = byte offset of row r in the resource, or kOOR (row of zeros).
+  template <int RW, class SrcFn>
+  __device__ __forceinline__ void stage_rows(uint8_t* lds, rsrc_t rsrc, SrcFn src) const {
+    const int per = (RW * Q + 63) / 64;
     const int step_r = 64 / Q, step_s = 64 % Q;
-    int r = 64 * wave + lane / Q, sl = lane % Q;
-    uint8_t* dst = sc + 4 * 64 * wave * Q;
-    for (int i = 0; i < Q; ++i) {
-      const int c = sl ^ scale_swizzle(r, Q);
-      load_to_lds4(ws, grow(r) * row_bytes + 4 * c, 0, dst + 256 * i);
+    int r = lane / Q, sl = lane % Q;
+    uint8_t* dst = lds + 256 * per * wave;
+    for (int i = 0; i < per; ++i) {
+      const int row = RW * wave + r;
+      // row offset + dword offset (kOOR + a small offset stays out of range)
+      const uint32_t base = r < RW ? src(row) : kOOR;
+      load_to_lds4(rsrc, base + (uint32_t)(4 * (sl ^ scale_swizzle(row, Q))), 0, dst + 256 * i);
       r += step_r;
       sl += step_s;
       if (sl >= Q) {
@@ -151,6 +156,14 @@ struct TiledGemm {
         ++r;
       }
     }
+  }
+
+  // LDS byte of scale row `row` (of an array filled with RW rows per wave),
+  // chunk c, K-group g.
+  template <int RW>
+  __device__ __forceinline__ uint32_t scale_at(int row, int c) const {
+    const int per = (RW * Q + 63) / 64;
+    return 4 * ((row / RW) * per * 64 + (row % RW) * Q + (c ^ scale_swizzle(row, Q))) + g;
   }
 
   // Issue chunk c into a stage (weight codes into registers q).
@@ -162,7 +175,6 @@ struct TiledGemm {
 #pragma unroll
       for (int i = 0; i < XI; ++i)
         load_to_lds16(a, xo[i] | oor, 64 * cc, base + (wave * XI + i) * 1024);
-      load_to_lds4(as, xso | oor, 4 * cc, base + BM * 64 + wave * 256);
     } else {
 #pragma unroll
       for (int i = 0; i < XI; ++i)
@@ -174,51 +186,91 @@ struct TiledGemm {
 
   // MFMAs of one chunk on the first NMT 16-row sub-tiles (the live ones).
   template <int NMT>
-  __device__ __forceinline__ void compute(const uint8_t* x, const uint8_t* sc, int c,
-                                          const u32x4_t (&q)[4], floatx4_t (&acc)[MT][4]) const {
+  __device__ __forceinline__ void compute(const uint8_t* x, const uint8_t* sc, const uint8_t* asc,
+                                          int c, const u32x4_t (&q)[4],
+                                          floatx4_t (&acc)[MT][4]) const {
     uint32_t s[4];
     const uint32_t so = sro + 4 * (uint32_t)(c ^ swz);
 #pragma unroll
     for (int t = 0; t < 4; ++t) s[t] = sc[so + 64 * t * Q];   // strip t: rows + 16 t
     if constexpr (kFP4A) {
+      // all of the chunk's LDS reads first, then the MFMAs
+      u32x4_t av[NMT];
+      uint32_t sa[NMT];
 #pragma unroll
       for (int mt = 0; mt < NMT; ++mt) {
         const int r = 16 * mt + nl;
-        const u32x4_t av =
-            *reinterpret_cast<const u32x4_t*>(x + r * 64 + 16 * (g ^ ((r >> 2) & 3)));
-        const uint32_t sa = x[BM * 64 + r * 4 + g];
-#pragma unroll
-        for (int t = 0; t < 4; ++t) acc[mt][t] = mfma_fp4_16x16x128(av, sa, q[t], s[t], acc[mt][t]);
+        av[mt] = *reinterpret_cast<const u32x4_t*>(x + r * 64 + 16 * (g ^ ((r >> 2) & 3)));
+        sa[mt] = asc[scale_at<BM / 4>(r, c)];
       }
+#pragma unroll
+      for (int mt = 0; mt < NMT; ++mt)
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+          acc[mt][t] = mfma_fp4_16x16x128(av[mt], sa[mt], q[t], s[t], acc[mt][t]);
     } else {
       float scf[4];
 #pragma unroll
       for (int t = 0; t < 4; ++t) scf[t] = e8m0_to_f32(s[t]);
+      // Software pipeline over the chunk's four K-steps: step j + 1's A
+      // fragments (LDS reads) and B fragments (dequantised weights) are
+      // produced while step j's MFMAs run, interleaved MFMA by MFMA.
+      bf16x8_t av[2][NMT], bv[2][4];
+#pragma unroll
+      for (int mt = 0; mt < NMT; ++mt) av[0][mt] = a_frag(x, mt, 0);
+#pragma unroll
+      for (int t = 0; t < 4; ++t) bv[0][t] = dequant8_bf16(q[t][0], scf[t]);
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        bf16x8_t b[4];
+        const int cur = j & 1, nxt = cur ^ 1;
+        if (j < 3) {
 #pragma unroll
-        for (int t = 0; t < 4; ++t) b[t] = dequant8_bf16(q[t][j], scf[t]);
+          for (int mt = 0; mt < NMT; ++mt) av[nxt][mt] = a_frag(x, mt, j + 1);
 #pragma unroll
-        for (int mt = 0; mt < NMT; ++mt) {
-          const int r = 16 * mt + nl;
-          const bf16x8_t av = *reinterpret_cast<const bf16x8_t*>(
-              x + r * 256 + 16 * ((4 * g + j) ^ (r & 15)));
-#pragma unroll
-          for (int t = 0; t < 4; ++t) acc[mt][t] = mfma_bf16_16x16x32(av, b[t], acc[mt][t]);
+          for (int t = 0; t < 4; ++t) bv[nxt][t] = dequant8_bf16(q[t][j + 1], scf[t]);
         }
+#pragma unroll
+        for (int mt = 0; mt < NMT; ++mt)
+#pragma unroll
+          for (int t = 0; t < 4; ++t) acc[mt][t] = mfma_bf16_16x16x32(av[cur][mt], bv[cur][t], acc[mt][t]);
+        if (j < 3) interleave<0, 4 * NMT, 16, NMT>();
+        __builtin_amdgcn_sched_barrier(0);    // one scheduling region per K-step
       }
     }
   }
 
+  // Scheduling groups for one K-step: after each of its NM MFMAs, a share of
+  // the NV conversions and ND LDS reads that prepare the next step.
+  template <int I, int NM, int NV, int ND>
+  __device__ __forceinline__ static void interleave() {
+    if constexpr (I < NM) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                 // MFMA
+      constexpr int v = (I + 1) * NV / NM - I * NV / NM;
+      if constexpr (v > 0) __builtin_amdgcn_sched_group_barrier(0x002, v, 0);   // VALU
+      constexpr int d = (I + 1) * ND / NM - I * ND / NM;
+      if constexpr (d > 0) __builtin_amdgcn_sched_group_barrier(0x100, d, 0);   // DS read
+      interleave<I + 1, NM, NV, ND>();
+    }
+  }
+
+  // bf16 A operand: rows 16 mt + (lane % 16), K-step j of the lane's K-group.
+  __device__ __forceinline__ bf16x8_t a_frag(const uint8_t* x, int mt, int j) const {
+    const int r = 16 * mt + nl;
+    return *reinterpret_cast<const bf16x8_t*>(x + r * 256 + 16 * ((4 * g + j) ^ (r & 15)));
+  }
+
   // stages[u]: one LDS array per stage (separate objects, so the compiler's
   // wait before reading stage u only covers the loads into stage u).  The
-  // scale loads, issued first, are complete once the first stage is.
-  template <int NMT, class RowFn>
-  __device__ __forceinline__ void run(uint8_t* const (&stages)[NS], uint8_t* sc, uint32_t srow_bytes,
-                                      RowFn grow, floatx4_t (&acc)[MT][4]) const {
+  // scale rows, issued first, are complete once the first stage is.
+  // wrow(r): byte offset of weight scale row r; arow(r): of the tile's
+  // activation scale row r (MXFP4) or kOOR.
+  template <int NMT, class WRow, class ARow>
+  __device__ __forceinline__ void run(uint8_t* const (&stages)[NS], uint8_t* sc, uint8_t* asc,
+                                      WRow wrow, ARow arow, floatx4_t (&acc)[MT][4]) const {
     u32x4_t q[NS][4];
-    load_scales(sc, srow_bytes, grow);
+    stage_rows<64>(sc, ws, wrow);
+    if constexpr (kFP4A) stage_rows<BM / 4>(asc, as, arow);
 #pragma unroll
     for (int u = 0; u < NS - 1; ++u) issue(stages[u], u, q[u]);
     for (int c0 = 0; c0 < nch; c0 += NS) {
@@ -228,7 +280,7 @@ struct TiledGemm {
         wait_vmcnt<LPS * (NS - 2)>();
         stage_barrier();
         issue(stages[(u + NS - 1) % NS], c + NS - 1, q[(u + NS - 1) % NS]);
-        if (c < nch) compute<NMT>(stages[u], sc, c, q[u], acc);
+        if (c < nch) compute<NMT>(stages[u], sc, asc, c, q[u], acc);
       }
     }
     wait_vmcnt<0>();
@@ -245,15 +297,10 @@ __device__ __forceinline__ TileT tile_of(const int32_t* tiles, const int32_t* of
 }
 
 // The lane's activation source offsets for every stage: row r of the tile
-// comes from source row src_row(r) (a token for gate/up, a sorted row for down).
-template <int BM, bool kFP4A>
-__device__ __forceinline__ void plan_x(TiledGemm<BM, kFP4A>& G, const int32_t* sorted, int Kp,
-                                       int T, const TileT& ti, bool gather, uint32_t row_bytes,
-                                       uint32_t scale_bytes) {
-  auto src_row = [&](int r) -> uint32_t {
-    return gather ? min((unsigned)(sorted[ti.row0 + r] / Kp), (unsigned)(T - 1))
-                  : (uint32_t)(ti.row0 + r);
-  };
+// comes from source row src(r) (a token for gate/up, a sorted row for down).
+template <int BM, bool kFP4A, class SrcFn>
+__device__ __forceinline__ void plan_x(TiledGemm<BM, kFP4A>& G, const TileT& ti, SrcFn src,
+                                       uint32_t row_bytes) {
 #pragma unroll
   for (int i = 0; i < G.XI; ++i) {
     const int k = G.wave * G.XI + i;
@@ -267,13 +314,7 @@ __device__ __forceinline__ void plan_x(TiledGemm<BM, kFP4A>& G, const int32_t* s
       const int p = G.lane & 15;
       piece = p ^ (r & 15);
     }
-    G.xo[i] = r < ti.rows ? src_row(r) * row_bytes + 16 * piece : kOOR;
-  }
-  if (kFP4A) {
-    const int r = 64 * G.wave + G.lane;
-    G.xso = r < ti.rows ? src_row(r) * scale_bytes : kOOR;
-  } else {
-    G.xso = kOOR;
+    G.xo[i] = r < ti.rows ? src(r) * row_bytes + 16 * piece : kOOR;
   }
 }
 
@@ -293,26 +334,6 @@ __device__ __forceinline__ void setup(TiledGemm<BM, kFP4A>& G, const TileT& ti, 
   const size_t wbytes = (size_t)wrows * (K / 2), sbytes = (size_t)wrows * (K / 32);
   G.w = make_rsrc(wq + ti.expert * wbytes, (uint32_t)wbytes);
   G.ws = make_rsrc(wsc + ti.expert * sbytes, (uint32_t)sbytes);
-}
-
-// Static LDS of a kernel: NS stage arrays (separate objects) and the scale
-// array; body(stages, scales) runs with them.
-template <int BM, bool kFP4A, class Body>
-__device__ __forceinline__ void with_lds(Body&& body) {
-  constexpr int XB = TileCfg<BM, kFP4A>::XB, SCB = TileCfg<BM, kFP4A>::SCB;
-  __shared__ __align__(16) uint8_t sc[SCB];
-  __shared__ __align__(16) uint8_t st0[XB];
-  __shared__ __align__(16) uint8_t st1[XB];
-  __shared__ __align__(16) uint8_t st2[XB];
-  if constexpr (TileCfg<BM, kFP4A>::NS == 4) {
-    __shared__ __align__(16) uint8_t st3[XB];
-    uint8_t* const stages[4] = {st0, st1, st2, st3};
-    body(stages, sc);
-  } else {
-    static_assert(TileCfg<BM, kFP4A>::NS == 3, "three or four stages");
-    uint8_t* const stages[3] = {st0, st1, st2};
-    body(stages, sc);
-  }
 }
 
 template <int N>
@@ -338,6 +359,64 @@ __device__ __forceinline__ void with_nmt(int rows, F&& f) {
     else if (need > 1) f(IntC<2>());
     else f(IntC<1>());
   }
+}
+
+// Static LDS of a kernel: NS stage arrays (separate objects), the weight
+// scales, and for MXFP4 activations their scales and the tile's source
+// rows; body(stages, scales, act_scales, src_rows) runs with them.
+template <int BM, bool kFP4A, class Body>
+__device__ __forceinline__ void with_lds(Body&& body) {
+  constexpr int XB = TileCfg<BM, kFP4A>::XB, SCB = TileCfg<BM, kFP4A>::SCB;
+  __shared__ __align__(16) uint8_t sc[SCB];
+  __shared__ __align__(16) uint8_t st0[XB];
+  __shared__ __align__(16) uint8_t st1[XB];
+  __shared__ __align__(16) uint8_t st2[XB];
+  if constexpr (kFP4A) {
+    static_assert(TileCfg<BM, kFP4A>::NS == 4, "four stages");
+    __shared__ __align__(16) uint8_t st3[XB];
+    __shared__ __align__(16) uint8_t asc[TileCfg<BM, kFP4A>::ASB];
+    __shared__ int32_t srow[BM];
+    uint8_t* const stages[4] = {st0, st1, st2, st3};
+    body(stages, sc, asc, srow);
+  } else if constexpr (TileCfg<BM, kFP4A>::NS == 4) {
+    __shared__ __align__(16) uint8_t st3[XB];
+    uint8_t* const stages[4] = {st0, st1, st2, st3};
+    body(stages, sc, (uint8_t*)nullptr, (int32_t*)nullptr);
+  } else {
+    static_assert(TileCfg<BM, kFP4A>::NS == 3, "three or four stages");
+    uint8_t* const stages[3] = {st0, st1, st2};
+    body(stages, sc, (uint8_t*)nullptr, (int32_t*)nullptr);
+  }
+}
+
+// The tile's K loop: source rows (MXFP4: tabled in LDS first, shared by the
+// activation-code offsets and the activation-scale rows), then the pipeline.
+// direct(r) = source row of tile row r < rows; wrow(r) = byte offset of
+// weight scale row r; arow_bytes = activation scale bytes per source row.
+template <int BM, bool kFP4A, class Direct, class WRow>
+__device__ __forceinline__ void tile_loop(TiledGemm<BM, kFP4A>& G, const TileT& ti, Direct direct,
+                                          WRow wrow, uint32_t row_bytes, uint32_t arow_bytes,
+                                          floatx4_t (&acc)[BM / 16][4]) {
+  with_lds<BM, kFP4A>([&](auto& stages, uint8_t* sc, uint8_t* asc, int32_t* srow) {
+    if constexpr (kFP4A) {
+      const int t = threadIdx.x;
+      if (t < BM) srow[t] = t < ti.rows ? (int32_t)direct(t) : 0;
+      __syncthreads();
+      plan_x<BM, kFP4A>(G, ti, [&](int r) { return (uint32_t)srow[r]; }, row_bytes);
+      auto arow = [&](int r) -> uint32_t {
+        return r < ti.rows ? (uint32_t)srow[r] * arow_bytes : kOOR;
+      };
+      with_nmt<BM>(ti.rows, [&](auto n) {
+        G.template run<decltype(n)::value>(stages, sc, asc, wrow, arow, acc);
+      });
+    } else {
+      plan_x<BM, kFP4A>(G, ti, direct, row_bytes);
+      auto arow = [](int) -> uint32_t { return kOOR; };
+      with_nmt<BM>(ti.rows, [&](auto n) {
+        G.template run<decltype(n)::value>(stages, sc, asc, wrow, arow, acc);
+      });
+    }
+  });
 }
 
 // gate/up + SwiGLU: weight rows gate [i0, i0 + 128) and up [I + i0, I + i0 + 128),
@@ -366,11 +445,13 @@ __global__ __launch_bounds__(256) void gate_up_tiled_kernel(
   } else {
     G.a = make_rsrc(act, (uint32_t)((size_t)T * H * 2));
   }
-  plan_x<BM, kFP4A>(G, sorted, Kp, T, ti, true, kFP4A ? rb : (uint32_t)H * 2, rs);
-  // workgroup row r (wave r/64, strip (r/16)%4, lane row r%16) -> weight row
-  auto grow = [&](int r) -> uint32_t {
+  auto token = [&](int r) -> uint32_t {
+    return min((unsigned)(sorted[ti.row0 + r] / Kp), (unsigned)(T - 1));
+  };
+  // workgroup row r (wave r/64, strip (r/16)%4, lane row r%16) -> weight scale row
+  auto wrow = [&](int r) -> uint32_t {
     const int t = (r >> 4) & 3;
-    return (uint32_t)((t < 2 ? 0 : I) + s * 128 + 32 * (r >> 6) + 16 * (t & 1) + (r & 15));
+    return rs * (uint32_t)((t < 2 ? 0 : I) + s * 128 + 32 * (r >> 6) + 16 * (t & 1) + (r & 15));
   };
 
   floatx4_t acc[BM / 16][4];
@@ -378,9 +459,7 @@ __global__ __launch_bounds__(256) void gate_up_tiled_kernel(
   for (int mt = 0; mt < BM / 16; ++mt)
 #pragma unroll
     for (int st = 0; st < 4; ++st) acc[mt][st] = (floatx4_t){0.f, 0.f, 0.f, 0.f};
-  with_lds<BM, kFP4A>([&](auto& stages, uint8_t* sc) {
-    with_nmt<BM>(ti.rows, [&](auto n) { G.template run<decltype(n)::value>(stages, sc, rs, grow, acc); });
-  });
+  tile_loop<BM, kFP4A>(G, ti, token, wrow, kFP4A ? rb : (uint32_t)H * 2, rs, acc);
 
 #pragma unroll
   for (int mt = 0; mt < BM / 16; ++mt)
@@ -418,17 +497,15 @@ __global__ __launch_bounds__(256) void down_tiled_kernel(
   } else {
     G.a = make_rsrc(hin, (uint32_t)((size_t)A * I * 2));
   }
-  plan_x<BM, kFP4A>(G, nullptr, 1, A, ti, false, kFP4A ? rb : (uint32_t)I * 2, rs);
-  auto grow = [&](int r) -> uint32_t { return (uint32_t)(s * 256 + r); };
+  auto srow = [&](int r) -> uint32_t { return (uint32_t)(ti.row0 + r); };
+  auto wrow = [&](int r) -> uint32_t { return rs * (uint32_t)(s * 256 + r); };
 
   floatx4_t acc[BM / 16][4];
 #pragma unroll
   for (int mt = 0; mt < BM / 16; ++mt)
 #pragma unroll
     for (int st = 0; st < 4; ++st) acc[mt][st] = (floatx4_t){0.f, 0.f, 0.f, 0.f};
-  with_lds<BM, kFP4A>([&](auto& stages, uint8_t* sc) {
-    with_nmt<BM>(ti.rows, [&](auto n) { G.template run<decltype(n)::value>(stages, sc, rs, grow, acc); });
-  });
+  tile_loop<BM, kFP4A>(G, ti, srow, wrow, kFP4A ? rb : (uint32_t)I * 2, rs, acc);
 
 #pragma unroll
   for (int mt = 0; mt < BM / 16; ++mt)
