@@ -83,7 +83,13 @@ def traffic_record(fetch_dir: str, write_dir: str, workload: str) -> dict:
         kernels[k] = {"dispatches": n, "fetch_kib": round(fk, 1), "write_kib": round(wk, 1),
                       "fetch_bytes": round(fk * 1024 * ff), "write_bytes": round(wk * 1024 * wf),
                       "bytes": round(fk * 1024 * ff + wk * 1024 * wf)}
+    cmd = (f"rocprofv3 --pmc {{counter}} -f csv -d <dir> -o p -- python -u <repo>/bench.py "
+           f"--workload {workload} --no-cpu --steps 5 --warmup 2 --pmc-calibrate")
     return {"workload": workload, "fetch_factor": round(ff, 5), "write_factor": round(wf, 5),
+            "commands": ["cd /tmp && export TMPDIR=/tmp", cmd.format(counter="FETCH_SIZE"),
+                         cmd.format(counter="WRITE_SIZE"),
+                         "python -m mxfp4_routed_expert_top_amd.profiling traffic --fetch <FETCH_SIZE dir> "
+                         f"--write <WRITE_SIZE dir> --workload {workload} --out <record>"],
             "calibration": f"torch.bitwise_not over {CALIBRATION_BYTES} B of int32 "
                            f"(reads and writes {CALIBRATION_BYTES} B)",
             "source_sha256": source_digest(), "kernels": kernels}
