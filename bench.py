@@ -35,9 +35,12 @@ def parse():
     p.add_argument("--steps", type=int, default=50)
     p.add_argument("--warmup", type=int, default=10)
     p.add_argument("--workload", default="decode", choices=list(synth.CONFIGS))
-    p.add_argument("--cpu-tokens", type=int, default=32,
+    p.add_argument("--cpu-tokens", type=int, default=40,
                    help="tokens of the batch the CPU oracle is timed on")
     p.add_argument("--no-cpu", action="store_true", help="skip the cpu_baseline leg")
+    p.add_argument("--router", action="store_true",
+                   help="route from x through the router GEMM (bf16 router rows [E + shared, H]) "
+                        "instead of taking precomputed logits")
     p.add_argument("--pmc-calibrate", action="store_true",
                    help="first run a plain 1 GiB kernel (torch.bitwise_not) whose HBM bytes are "
                         "known, for scaling FETCH_SIZE / WRITE_SIZE counter passes")
@@ -106,7 +109,7 @@ def _pack_expert(args):
     return e, (a[0], a[1], b[0], b[1])
 
 
-def cpu_baseline(cfg, n_tokens):
+def cpu_baseline(cfg, n_tokens, router=False):
     """Time the oracle, as it stands, on the first n_tokens tokens of the
     batch (route + align over all tokens, expert MLPs + combine for the
     sample), single-threaded.  Its weights are the same distribution drawn on
@@ -116,21 +119,32 @@ def cpu_baseline(cfg, n_tokens):
     from threadpoolctl import threadpool_limits
     from oracle import moe
     x_bits = synth.activations(cfg).view(torch.int16).numpy().view(np.uint16)
-    logits = synth.router_logits(cfg).numpy()
-    gate = synth.gate_logits(cfg)
-    gate = None if gate is None else gate.numpy()
     tokens = np.arange(min(n_tokens, cfg.T))
+    if router:
+        wr_bits = synth.router_weight(cfg).view(torch.int16).numpy().view(np.uint16)
+        lg = moe.router_logits(x_bits, wr_bits)          # all tokens (routing needs them), untimed
+        logits = lg[:, :cfg.E].astype(np.float32)
+        gate = lg[:, cfg.E].astype(np.float32) if cfg.shared else None
+    else:
+        logits = synth.router_logits(cfg).numpy()
+        gate = synth.gate_logits(cfg)
+        gate = None if gate is None else gate.numpy()
     ids, _ = moe.route(logits, gate, cfg.K, cfg.shared)
     need = sorted(set(ids[tokens].reshape(-1).tolist()))
     procs = max(1, min(16, len(os.sched_getaffinity(0))))
     log(f"cpu_baseline: packing {len(need)} experts with the oracle's quantiser ({procs} procs)")
     with mp.get_context("spawn").Pool(procs) as pool:
         packed = dict(pool.map(_pack_expert, [(cfg, e) for e in need], chunksize=4))
+    t_router = 0.0
     with threadpool_limits(1):
+        if router:                 # the router GEMM over the sampled tokens, single-threaded too
+            t0 = time.perf_counter()
+            moe.router_logits(x_bits[tokens], wr_bits)
+            t_router = time.perf_counter() - t0
         t0 = time.perf_counter()
         moe.forward(x_bits, logits, gate, lambda e: packed[e], cfg.I, cfg.E, cfg.K, cfg.shared,
                     cfg.act_fmt, tokens=tokens)
-        dt = time.perf_counter() - t0
+        dt = time.perf_counter() - t0 + t_router
     return {"value": round(len(tokens) / dt, 3), "unit": "tokens/s", "cores": 1, "kind": "oracle",
             "seconds": round(dt, 2),
             "sample": f"{len(tokens)} of the batch's {cfg.T} tokens ({len(need)} experts decoded); "
@@ -154,6 +168,13 @@ def main():
         del a
         torch.cuda.empty_cache()
     x, logits, gate, w13, w13s, w2, w2s = make_inputs(cfg)
+    wr = synth.router_weight(cfg).to("cuda") if args.router else None
+    if args.router:
+        # the stage-by-stage pass routes on the logits the router GEMM gives
+        lg = torch.empty(cfg.T, cfg.Ep, dtype=torch.float32, device="cuda")
+        ops.route_topk_gemm(x, wr, cfg.K, cfg.shared, logits_out=lg)
+        logits = lg[:, :cfg.E].contiguous()
+        gate = lg[:, cfg.E].contiguous() if cfg.shared else None
     bufs = ops.alloc_stages(cfg.T, cfg.H, cfg.I, cfg.E, cfg.K, cfg.shared, cfg.act_fmt, "cuda")
     ws = torch.empty(ops.workspace_size(cfg.T, cfg.H, cfg.I, cfg.E, cfg.K, cfg.shared, cfg.act_fmt),
                      dtype=torch.uint8, device="cuda")
@@ -161,9 +182,14 @@ def main():
     stream = torch.cuda.current_stream()
 
     def step():
-        # the whole layer, one C call: route, align, [quant x], gate/up+SwiGLU, [quant h], down, combine
-        ops.mxfp4_forward(x, logits, gate, w13, w13s, w2, w2s, cfg.I, cfg.E, cfg.K, cfg.shared,
-                          cfg.act_fmt, out=out, workspace=ws)
+        # the whole layer, one C call: [router GEMM,] route, align, [quant x], gate/up+SwiGLU,
+        # [quant h], down, combine
+        if args.router:
+            ops.mxfp4_forward_router(x, wr, w13, w13s, w2, w2s, cfg.I, cfg.E, cfg.K, cfg.shared,
+                                     cfg.act_fmt, out=out, workspace=ws)
+        else:
+            ops.mxfp4_forward(x, logits, gate, w13, w13s, w2, w2s, cfg.I, cfg.E, cfg.K, cfg.shared,
+                              cfg.act_fmt, out=out, workspace=ws)
 
     def step_stages(events):
         ops.forward_stages(x, logits, gate, w13, w13s, w2, w2s, cfg.I, cfg.E, cfg.K, cfg.shared,
@@ -199,9 +225,35 @@ def main():
         "step ms:", round(ms, 4))
     if not torch.equal(out, bufs["out"]):
         raise RuntimeError("one-call forward and per-stage pass disagree")
+    router = None
+    if args.router:
+        # timed region 3: the router call alone (router GEMM + routing), HIP events
+        rws = torch.empty(ops.route_gemm_workspace_size(cfg.T, cfg.H, cfg.E, cfg.shared),
+                          dtype=torch.uint8, device="cuda")
+        rids = torch.empty(cfg.T, cfg.Kp, dtype=torch.int32, device="cuda")
+        rw_ = torch.empty(cfg.T, cfg.Kp, dtype=torch.float32, device="cuda")
+        rcall = lambda: ops.route_topk_gemm(x, wr, cfg.K, cfg.shared, topk_ids=rids,
+                                            topk_weights=rw_, workspace=rws)
+        for _ in range(3):
+            rcall()
+        re = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(args.steps)]
+        for a, b in re:
+            a.record()
+            rcall()
+            b.record()
+        torch.cuda.synchronize()
+        rms = float(np.mean([a.elapsed_time(b) for a, b in re]))
+        rbytes = cfg.Ep * cfg.H * 2 + cfg.T * cfg.H * 2
+        router = {"call_ms": round(rms, 4), "algorithmic_bytes": rbytes,
+                  "flops": 2 * cfg.T * cfg.Ep * cfg.H, "gbs": round(rbytes / (rms / 1e3) / 1e9, 1)}
+        log("router call ms:", round(rms, 4))
 
     counts = bufs["align"]["counts"].cpu().numpy()
     alg = algorithmic(cfg, counts)
+    if args.router:          # the router rows join the layer's bytes and FLOPs
+        alg["layer_bytes"] += cfg.Ep * cfg.H * 2 - cfg.T * cfg.E * 4 - cfg.T * 4 * cfg.shared
+        alg["flops"] += 2 * cfg.T * cfg.Ep * cfg.H
     from mxfp4_routed_expert_top_amd import profiling
     tile_m = ops.gemm_tile_m(cfg.T, cfg.Kp, cfg.Ep, cfg.H, cfg.I, cfg.act_fmt)
     kname = gate_up_kernel_name(cfg, tile_m)
@@ -234,7 +286,7 @@ def main():
              "down_gbs": round(alg["w2_bytes"] / (stage_ms["down"] / 1e3) / 1e9, 1)}
     cpu = None
     if not args.no_cpu:
-        cpu = cpu_baseline(cfg, args.cpu_tokens)
+        cpu = cpu_baseline(cfg, args.cpu_tokens, router=args.router)
     res = {"metric": METRIC, "value": round(cfg.T / layer_s, 1), "unit": "tokens/s",
            "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
            "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
@@ -242,10 +294,13 @@ def main():
            "data": "synthetic",
            "config": {"workload": f"{cfg.name}: T={cfg.T} H={cfg.H} I={cfg.I} E={cfg.E} "
                                   f"K={cfg.K}+{cfg.shared} shared, "
-                                  f"{'W4A16' if cfg.act_fmt == 0 else 'W4A4'} MXFP4 weights",
+                                  f"{'W4A16' if cfg.act_fmt == 0 else 'W4A4'} MXFP4 weights"
+                                  + (", routed from x by the router GEMM" if args.router else ""),
                       "T": cfg.T, "H": cfg.H, "I": cfg.I, "E": cfg.E, "K": cfg.K,
                       "shared": cfg.shared, "parallelism": "none (1 GPU)"},
            "roofline": roofline, "layer": layer, "cpu_baseline": cpu}
+    if router is not None:
+        res["router"] = router
     print(json.dumps(res), flush=True)
 
 

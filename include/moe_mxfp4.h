@@ -7,6 +7,7 @@
  * "Goal" and "Baseline"; MiniMax M3 on MI355X post, sections "Local shape
  * and tiling" and "Shared expert fusion"):
  *
+ *   0. (optional) the router GEMM producing the logits   moe_route_topk_gemm
  *   1. softmax top-K routing over E experts, the shared expert folded in as
  *      expert E in slot K                              moe_route_topk
  *   2. permute: group the (token, slot) assignments by expert   moe_align_sort
@@ -15,6 +16,7 @@
  *   5. grouped down GEMM                               moe_expert_down
  *   6. weighted combine back into token order          moe_combine
  *   all six in one call                                moe_mxfp4_forward
+ *   0-6 in one call                                    moe_mxfp4_forward_router
  *
  * Conventions for every entry point:
  *   - Data pointers are DEVICE pointers (HBM of the current HIP device),
@@ -99,6 +101,32 @@ MOE_API const char *moe_status_string(moe_status s);
 MOE_API moe_status moe_route_topk(const float *logits, const float *gate_logits, int32_t T, int32_t E,
                           int32_t K, int32_t shared, int32_t renormalize, int32_t *topk_ids,
                           float *topk_weights, void *stream);
+
+/*
+ * Router GEMM and routing in one call: the step just before the layer (the
+ * router producing the gating output that the InferenceX post's fused_topk
+ * consumes) joined to moe_route_topk.
+ *   x             bf16 [T, H] activations (16-byte aligned)
+ *   router_w      bf16 [E + shared, H] (16-byte aligned): rows [0, E) the
+ *                 router; with shared = 1, row E is the shared expert's gate
+ *                 vector, so its gate logit is g_t = x_t . router_w[E]
+ *   logits_out    out fp32 [T, E + shared] or NULL: the logits routed on
+ *   workspace     >= moe_route_gemm_workspace_size(T, H, E, shared) bytes
+ * logits = x . router_w^T with fp32 accumulation of the exact bf16 products
+ * (the reduction is split over H and the fp32 partial sums are added in a
+ * fixed order, so equal inputs give equal logits and selections); then
+ * exactly moe_route_topk on them (renormalize as there).
+ * Errors: INVALID_ARGUMENT (null or misaligned pointers, T < 0, K < 1,
+ * K > E, flags not 0/1), UNSUPPORTED (H not a multiple of 128, E > 1024,
+ * K' > 32, T*H or (E + shared)*H bf16 bytes beyond 2^31),
+ * WORKSPACE_TOO_SMALL.
+ */
+MOE_API size_t moe_route_gemm_workspace_size(int32_t T, int32_t H, int32_t E, int32_t shared);
+MOE_API moe_status moe_route_topk_gemm(const uint16_t *x, const uint16_t *router_w, int32_t T,
+                                       int32_t H, int32_t E, int32_t K, int32_t shared,
+                                       int32_t renormalize, int32_t *topk_ids,
+                                       float *topk_weights, float *logits_out, void *workspace,
+                                       size_t workspace_bytes, void *stream);
 
 /* Scratch bytes moe_align_sort needs for A = T * Kp assignments over Ep experts. */
 MOE_API size_t moe_align_workspace_size(int32_t T, int32_t Kp, int32_t Ep);
@@ -230,6 +258,26 @@ MOE_API moe_status moe_mxfp4_forward(const uint16_t *x, const float *router_logi
                              int32_t act_fmt, uint16_t *out, int32_t *topk_ids_out,
                              float *topk_weights_out, void *workspace, size_t workspace_bytes,
                              void *stream);
+
+/*
+ * The whole layer routed from x: moe_route_topk_gemm's router GEMM and
+ * routing, then everything moe_mxfp4_forward does after its routing.
+ *   router_w     bf16 [E + shared, H] (16-byte aligned); row E = the shared
+ *                expert's gate vector (see moe_route_topk_gemm)
+ *   logits_out   out fp32 [T, E + shared] or NULL
+ *   workspace    >= moe_mxfp4_workspace_size(...) bytes (the same size as
+ *                for moe_mxfp4_forward)
+ * Other arguments, outputs and errors as moe_mxfp4_forward (router_w
+ * replaces router_logits and shared_gate_logits).
+ */
+MOE_API moe_status moe_mxfp4_forward_router(const uint16_t *x, const uint16_t *router_w,
+                                            const uint8_t *w13, const uint8_t *w13_scale,
+                                            const uint8_t *w2, const uint8_t *w2_scale, int32_t T,
+                                            int32_t H, int32_t I, int32_t E, int32_t K,
+                                            int32_t shared, int32_t act_fmt, uint16_t *out,
+                                            int32_t *topk_ids_out, float *topk_weights_out,
+                                            float *logits_out, void *workspace,
+                                            size_t workspace_bytes, void *stream);
 
 #ifdef __cplusplus
 }

@@ -6,5 +6,6 @@ Build the library with ``python -m mxfp4_routed_expert_top_amd.build``.
 """
 from . import ops  # noqa: F401
 from .ops import (ACT_BF16, ACT_MXFP4, MoeError, align_sort, combine, expert_down,  # noqa: F401
-                  expert_gate_up, forward_stages, alloc_stages, mxfp4_forward, mxfp4_quantize, route_topk,
+                  expert_gate_up, forward_stages, alloc_stages, mxfp4_forward, mxfp4_forward_router,
+                  mxfp4_quantize, route_topk, route_topk_gemm,
                   workspace_size)

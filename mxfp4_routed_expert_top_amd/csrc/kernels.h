@@ -8,6 +8,18 @@ hipError_t launch_route_topk(const float* logits, const float* gate, int T, int 
                              int shared, int renormalize, int32_t* ids, float* weights,
                              hipStream_t stream);
 
+// Adds the router GEMM's S partial sums into logits [T, E + shared] (in
+// split order), then routes on them (the gate logit is column E).
+int route_max_splits();
+hipError_t launch_route_topk_split(const float* partial, int S, int T, int E, int K, int shared,
+                                   int renormalize, int32_t* ids, float* weights, float* logits,
+                                   hipStream_t stream);
+
+int router_splits(int T, int H, int Ep);
+size_t router_workspace_bytes(int T, int H, int Ep);   // partial sums + summed logits
+hipError_t launch_router_gemm(const uint16_t* x, const uint16_t* w, int T, int H, int Ep,
+                              float* partial, hipStream_t stream);
+
 size_t align_scratch_bytes(int A, int Ep);
 hipError_t launch_align_sort(const int32_t* ids, int A, int Ep, int tile_m, int32_t* counts,
                              int32_t* offsets, int32_t* sorted, int32_t* inv, int32_t* tiles,

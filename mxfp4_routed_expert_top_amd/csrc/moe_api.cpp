@@ -71,18 +71,28 @@ FwdLayout forward_layout(int64_t T, int64_t H, int64_t I, int64_t E, int64_t K, 
   L.h = take(A * I * 2);
   L.hq = take(q ? A * I / 2 : 0);
   L.hs = take(q ? A * I / 32 : 0);
-  L.y = take(A * H * 4);
+  // y; the router GEMM's partial sums (when the call routes from x) live in
+  // the same bytes: routing consumes them before the down GEMM writes y
+  L.y = take(std::max((size_t)(A * H * 4), router_workspace_bytes((int)T, (int)H, (int)Ep)));
   L.total = p;
   return L;
 }
 
-moe_status check_route(const float* logits, const float* gate, int32_t T, int32_t E, int32_t K,
-                       int32_t shared, int32_t renormalize) {
+// Routing shapes and flags.
+moe_status check_route_shape(int32_t T, int32_t E, int32_t K, int32_t shared,
+                             int32_t renormalize) {
   if (T < 0 || E < 1 || K < 1 || K > E || (shared != 0 && shared != 1) ||
       (renormalize != 0 && renormalize != 1))
     return MOE_ERR_INVALID_ARGUMENT;
-  if (T > 0 && (!logits || (shared && !gate))) return MOE_ERR_INVALID_ARGUMENT;
   if (E > kMaxE || K + shared > kMaxKp) return MOE_ERR_UNSUPPORTED;
+  return MOE_OK;
+}
+
+moe_status check_route(const float* logits, const float* gate, int32_t T, int32_t E, int32_t K,
+                       int32_t shared, int32_t renormalize) {
+  moe_status st = check_route_shape(T, E, K, shared, renormalize);
+  if (st != MOE_OK) return st;
+  if (T > 0 && (!logits || (shared && !gate))) return MOE_ERR_INVALID_ARGUMENT;
   return MOE_OK;
 }
 
@@ -110,6 +120,36 @@ moe_status moe_route_topk(const float* logits, const float* gate_logits, int32_t
   if (T == 0) return MOE_OK;
   return from_hip(launch_route_topk(logits, gate_logits, T, E, K, shared, renormalize, topk_ids,
                                     topk_weights, as_stream(stream)));
+}
+
+size_t moe_route_gemm_workspace_size(int32_t T, int32_t H, int32_t E, int32_t shared) {
+  if (T <= 0 || H <= 0 || H % 128 || E < 1 || (shared != 0 && shared != 1)) return 0;
+  return round_up(router_workspace_bytes(T, H, E + shared));
+}
+
+moe_status moe_route_topk_gemm(const uint16_t* x, const uint16_t* router_w, int32_t T, int32_t H,
+                               int32_t E, int32_t K, int32_t shared, int32_t renormalize,
+                               int32_t* topk_ids, float* topk_weights, float* logits_out,
+                               void* workspace, size_t workspace_bytes, void* stream) {
+  moe_status st = check_route_shape(T, E, K, shared, renormalize);
+  if (st != MOE_OK) return st;
+  if (H <= 0) return MOE_ERR_INVALID_ARGUMENT;
+  if (H % 128) return MOE_ERR_UNSUPPORTED;
+  const int Ep = E + shared;
+  if ((int64_t)T * H * 2 >= INT32_MAX || (int64_t)Ep * H * 2 >= INT32_MAX)
+    return MOE_ERR_UNSUPPORTED;                          // 32-bit buffer ranges
+  if (T == 0) return MOE_OK;
+  if (!x || !router_w || !topk_ids || !topk_weights || !workspace) return MOE_ERR_INVALID_ARGUMENT;
+  if (!aligned16(x) || !aligned16(router_w)) return MOE_ERR_INVALID_ARGUMENT;
+  if (workspace_bytes < router_workspace_bytes(T, H, Ep)) return MOE_ERR_WORKSPACE_TOO_SMALL;
+  hipStream_t s = as_stream(stream);
+  float* partial = (float*)workspace;
+  const int S = router_splits(T, H, Ep);
+  float* logits = logits_out ? logits_out : partial + (size_t)S * T * Ep;
+  hipError_t e = launch_router_gemm(x, router_w, T, H, Ep, partial, s);
+  if (e != hipSuccess) return MOE_ERR_DEVICE;
+  return from_hip(launch_route_topk_split(partial, S, T, E, K, shared, renormalize, topk_ids,
+                                          topk_weights, logits, s));
 }
 
 size_t moe_align_workspace_size(int32_t T, int32_t Kp, int32_t Ep) {
@@ -222,15 +262,26 @@ size_t moe_mxfp4_workspace_size(int32_t T, int32_t H, int32_t I, int32_t E, int3
   return forward_layout(T, H, I, E, K, shared, act_fmt).total;
 }
 
-moe_status moe_mxfp4_forward(const uint16_t* x, const float* router_logits,
-                             const float* shared_gate_logits, const uint8_t* w13,
-                             const uint8_t* w13_scale, const uint8_t* w2, const uint8_t* w2_scale,
-                             int32_t T, int32_t H, int32_t I, int32_t E, int32_t K, int32_t shared,
-                             int32_t act_fmt, uint16_t* out, int32_t* topk_ids_out,
-                             float* topk_weights_out, void* workspace, size_t workspace_bytes,
-                             void* stream) {
-  moe_status st = check_route(router_logits, shared_gate_logits, T, E, K, shared, 1);
+}  // extern "C"
+
+namespace {
+
+// The whole layer.  Routing either from the caller's logits (router_w null)
+// or through the router GEMM on x (router_w [E + shared, H] bf16; its
+// logits optionally copied to logits_out).
+moe_status forward_impl(const uint16_t* x, const float* router_logits,
+                        const float* shared_gate_logits, const uint16_t* router_w,
+                        float* logits_out, const uint8_t* w13, const uint8_t* w13_scale,
+                        const uint8_t* w2, const uint8_t* w2_scale, int32_t T, int32_t H,
+                        int32_t I, int32_t E, int32_t K, int32_t shared, int32_t act_fmt,
+                        uint16_t* out, int32_t* topk_ids_out, float* topk_weights_out,
+                        void* workspace, size_t workspace_bytes, void* stream) {
+  moe_status st = router_w ? check_route_shape(T, E, K, shared, 1)
+                           : check_route(router_logits, shared_gate_logits, T, E, K, shared, 1);
   if (st != MOE_OK) return st;
+  if (router_w && ((int64_t)T * H * 2 >= INT32_MAX || (int64_t)(E + shared) * H * 2 >= INT32_MAX))
+    return MOE_ERR_UNSUPPORTED;                          // 32-bit buffer ranges
+  if (router_w && !aligned16(router_w)) return MOE_ERR_INVALID_ARGUMENT;
   if (act_fmt != MOE_ACT_BF16 && act_fmt != MOE_ACT_MXFP4) return MOE_ERR_INVALID_ARGUMENT;
   st = check_shape_HI(H, I);
   if (st != MOE_OK) return st;
@@ -265,7 +316,16 @@ moe_status moe_mxfp4_forward(const uint16_t* x, const float* router_logits,
   const int tm = choose_tile_m(A, Ep, H, I, act_fmt);
   const int mt = (int)max_tiles_for(A, Ep, tm);
 
-  hipError_t e = launch_route_topk(router_logits, shared_gate_logits, T, E, K, shared, 1, ids, wts, s);
+  hipError_t e;
+  if (router_w) {
+    const int S = router_splits(T, H, Ep);
+    e = launch_router_gemm(x, router_w, T, H, Ep, y, s);
+    if (e != hipSuccess) return MOE_ERR_DEVICE;
+    e = launch_route_topk_split(y, S, T, E, K, shared, 1, ids, wts,
+                                logits_out ? logits_out : y + (size_t)S * T * Ep, s);
+  } else {
+    e = launch_route_topk(router_logits, shared_gate_logits, T, E, K, shared, 1, ids, wts, s);
+  }
   if (e != hipSuccess) return MOE_ERR_DEVICE;
   e = launch_align_sort(ids, (int)A, Ep, tm, counts, offsets, sorted, inv, tiles, ntiles, scratch, s);
   if (e != hipSuccess) return MOE_ERR_DEVICE;
@@ -295,6 +355,35 @@ moe_status moe_mxfp4_forward(const uint16_t* x, const float* router_logits,
                         s);
   if (e != hipSuccess) return MOE_ERR_DEVICE;
   return from_hip(launch_combine(y, wts, inv, T, H, Kp, out, s));
+}
+
+}  // namespace
+
+extern "C" {
+
+moe_status moe_mxfp4_forward(const uint16_t* x, const float* router_logits,
+                             const float* shared_gate_logits, const uint8_t* w13,
+                             const uint8_t* w13_scale, const uint8_t* w2, const uint8_t* w2_scale,
+                             int32_t T, int32_t H, int32_t I, int32_t E, int32_t K, int32_t shared,
+                             int32_t act_fmt, uint16_t* out, int32_t* topk_ids_out,
+                             float* topk_weights_out, void* workspace, size_t workspace_bytes,
+                             void* stream) {
+  return forward_impl(x, router_logits, shared_gate_logits, nullptr, nullptr, w13, w13_scale, w2,
+                      w2_scale, T, H, I, E, K, shared, act_fmt, out, topk_ids_out,
+                      topk_weights_out, workspace, workspace_bytes, stream);
+}
+
+moe_status moe_mxfp4_forward_router(const uint16_t* x, const uint16_t* router_w,
+                                    const uint8_t* w13, const uint8_t* w13_scale,
+                                    const uint8_t* w2, const uint8_t* w2_scale, int32_t T,
+                                    int32_t H, int32_t I, int32_t E, int32_t K, int32_t shared,
+                                    int32_t act_fmt, uint16_t* out, int32_t* topk_ids_out,
+                                    float* topk_weights_out, float* logits_out, void* workspace,
+                                    size_t workspace_bytes, void* stream) {
+  if (T > 0 && !router_w) return MOE_ERR_INVALID_ARGUMENT;
+  return forward_impl(x, nullptr, nullptr, T > 0 ? router_w : nullptr, logits_out, w13, w13_scale,
+                      w2, w2_scale, T, H, I, E, K, shared, act_fmt, out, topk_ids_out,
+                      topk_weights_out, workspace, workspace_bytes, stream);
 }
 
 }  // extern "C"

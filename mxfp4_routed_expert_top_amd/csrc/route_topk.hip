@@ -8,7 +8,9 @@
 // selected experts (renormalised) or over all E (not renormalised).  With a
 // folded-in shared expert, slot K holds expert E with weight sigmoid(g)
 // (same post, shared-expert fusion bullet: the shared expert becomes expert
-// top-K+1 of the one MoE dispatch).
+// top-K+1 of the one MoE dispatch).  The logits come either from the caller
+// or from the router GEMM (router_gemm.hip), whose split partial sums are
+// first added in a fixed order.
 #include "common.h"
 #include "kernels.h"
 
@@ -61,20 +63,26 @@ __device__ __forceinline__ float wave_sum_f32(float v) {
   return v;
 }
 
-__global__ __launch_bounds__(256) void route_topk_kernel(
-    const float* __restrict__ logits, const float* __restrict__ gate, int T, int E, int K,
-    int shared, int renormalize, int32_t* __restrict__ ids, float* __restrict__ weights) {
+// Logits straight from an fp32 [T, ld] array.
+struct RowLogits {
+  const float* l;
+  int ld;
+  __device__ __forceinline__ float operator()(int t, int e) const { return l[(size_t)t * ld + e]; }
+};
+
+// One wave routes token t.  g = the shared expert's gate logit (used when
+// shared = 1).
+__device__ __forceinline__ void route_token(const RowLogits& src, int t, int E, int K, int shared,
+                                            int renormalize, float g, int32_t* __restrict__ ids,
+                                            float* __restrict__ weights) {
   const int lane = threadIdx.x & 63;
-  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (t >= T) return;
-  const float* row = logits + (size_t)t * E;
   const int Kp = K + shared;
 
   uint64_t key[kMaxPerLane];
 #pragma unroll
   for (int j = 0; j < kMaxPerLane; ++j) {
     int e = lane + 64 * j;
-    key[j] = (e < E) ? route_key(row[e], e) : 0ull;    // 0 = never selected
+    key[j] = (e < E) ? route_key(src(t, e), e) : 0ull;    // 0 = never selected
   }
 
   // K rounds: the wave-wide best key is the next slot; its owner retires it.
@@ -105,7 +113,7 @@ __global__ __launch_bounds__(256) void route_topk_kernel(
 
   if (!renormalize) {
     float s = 0.f;
-    for (int e = lane; e < E; e += 64) s += expf(row[e] - lmax);
+    for (int e = lane; e < E; e += 64) s += expf(src(t, e) - lmax);
     den = wave_sum_f32(s);
   }
   if (lane < K) {
@@ -114,8 +122,39 @@ __global__ __launch_bounds__(256) void route_topk_kernel(
   }
   if (shared && lane == 0) {
     ids[(size_t)t * Kp + K] = E;
-    weights[(size_t)t * Kp + K] = 1.0f / (1.0f + expf(-gate[t]));
+    weights[(size_t)t * Kp + K] = 1.0f / (1.0f + expf(-g));
   }
+}
+
+// logits fp32 rows of stride ld; the shared gate logit of token t at
+// gate[t * gate_stride].
+__global__ __launch_bounds__(256) void route_topk_kernel(
+    const float* __restrict__ logits, int ld, const float* __restrict__ gate, int gate_stride,
+    int T, int E, int K, int shared, int renormalize, int32_t* __restrict__ ids,
+    float* __restrict__ weights) {
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= T) return;
+  route_token(RowLogits{logits, ld}, t, E, K, shared, renormalize,
+              shared ? gate[(size_t)t * gate_stride] : 0.f, ids, weights);
+}
+
+// The router GEMM's S partial sums P[s] (fp32 [S, n]) added in split order
+// (a fixed order: equal inputs give equal logits): out[i] = sum_s P[s][i].
+// All S loads of an element are issued before the adds.
+constexpr int kMaxSplits = 32;
+
+__global__ __launch_bounds__(256) void sum_splits_kernel(const float* __restrict__ partial, int S,
+                                                         int64_t n, float* __restrict__ out) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= n) return;
+  float v[kMaxSplits];
+#pragma unroll
+  for (int s = 0; s < kMaxSplits; ++s) v[s] = s < S ? partial[s * n + i] : 0.f;
+  float acc = v[0];
+#pragma unroll
+  for (int s = 1; s < kMaxSplits; ++s)
+    if (s < S) acc += v[s];
+  out[i] = acc;
 }
 
 }  // namespace
@@ -124,7 +163,24 @@ hipError_t launch_route_topk(const float* logits, const float* gate, int T, int 
                              int shared, int renormalize, int32_t* ids, float* weights,
                              hipStream_t stream) {
   dim3 grid((T + 3) / 4), block(256);
-  hipLaunchKernelGGL(route_topk_kernel, grid, block, 0, stream, logits, gate, T, E, K, shared,
+  hipLaunchKernelGGL(route_topk_kernel, grid, block, 0, stream, logits, E, gate, 1, T, E, K, shared,
                      renormalize, ids, weights);
+  return hipGetLastError();
+}
+
+int route_max_splits() { return kMaxSplits; }
+
+hipError_t launch_route_topk_split(const float* partial, int S, int T, int E, int K, int shared,
+                                   int renormalize, int32_t* ids, float* weights, float* logits,
+                                   hipStream_t stream) {
+  const int Ep = E + shared;
+  const int64_t n = (int64_t)T * Ep;
+  hipLaunchKernelGGL(sum_splits_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream,
+                     partial, S, n, logits);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  dim3 grid((T + 3) / 4), block(256);
+  hipLaunchKernelGGL(route_topk_kernel, grid, block, 0, stream, logits, Ep, logits + E, Ep, T, E,
+                     K, shared, renormalize, ids, weights);
   return hipGetLastError();
 }

@@ -31,6 +31,11 @@ _SZ = ctypes.c_size_t
 _SIGS = {
     "moe_status_string": (ctypes.c_char_p, [_I32]),
     "moe_route_topk": (_I32, [_P, _P, _I32, _I32, _I32, _I32, _I32, _P, _P, _P]),
+    "moe_mxfp4_forward_router": (_I32, [_P, _P, _P, _P, _P, _P, _I32, _I32, _I32, _I32, _I32,
+                                        _I32, _I32, _P, _P, _P, _P, _P, _SZ, _P]),
+    "moe_route_gemm_workspace_size": (_SZ, [_I32, _I32, _I32, _I32]),
+    "moe_route_topk_gemm": (_I32, [_P, _P, _I32, _I32, _I32, _I32, _I32, _I32, _P, _P, _P, _P, _SZ,
+                                   _P]),
     "moe_align_workspace_size": (_SZ, [_I32, _I32, _I32]),
     "moe_align_sort": (_I32, [_P, _I32, _I32, _I32, _I32, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
     "moe_mxfp4_quantize": (_I32, [_P, _I32, _I64, _I64, _P, _P, _P]),
@@ -114,6 +119,32 @@ def route_topk(logits, gate_logits, K: int, shared: int, renormalize: int = 1,
         _ptr(logits), _ptr(gate_logits), T, E, K, shared, renormalize, _ptr(topk_ids),
         _ptr(topk_weights), _stream(stream)))
     return topk_ids, topk_weights
+
+
+def route_gemm_workspace_size(T: int, H: int, E: int, shared: int) -> int:
+    return int(lib().moe_route_gemm_workspace_size(T, H, E, shared))
+
+
+def route_topk_gemm(x, router_w, K: int, shared: int, renormalize: int = 1, topk_ids=None,
+                    topk_weights=None, logits_out=None, workspace=None, stream=None):
+    """moe_route_topk_gemm: x bf16 [T, H], router_w bf16 [E + shared, H] (row E = the
+    shared expert's gate vector) -> (ids int32 [T, K'], w fp32 [T, K'], logits or None)."""
+    _dt(x, torch.bfloat16, "x")
+    _dt(router_w, torch.bfloat16, "router_w")
+    T, H = x.shape
+    E = router_w.shape[0] - shared
+    Kp = K + shared
+    if topk_ids is None:
+        topk_ids = torch.empty(T, Kp, dtype=torch.int32, device=x.device)
+    if topk_weights is None:
+        topk_weights = torch.empty(T, Kp, dtype=torch.float32, device=x.device)
+    if workspace is None:
+        workspace = torch.empty(max(1, route_gemm_workspace_size(T, H, E, shared)),
+                                dtype=torch.uint8, device=x.device)
+    _check("moe_route_topk_gemm", lib().moe_route_topk_gemm(
+        _ptr(x), _ptr(router_w), T, H, E, K, shared, renormalize, _ptr(topk_ids),
+        _ptr(topk_weights), _ptr(logits_out), _ptr(workspace), workspace.numel(), _stream(stream)))
+    return topk_ids, topk_weights, logits_out
 
 
 def align_workspace_size(T: int, Kp: int, Ep: int) -> int:
@@ -230,6 +261,26 @@ def mxfp4_forward(x, router_logits, shared_gate_logits, w13, w13_scale, w2, w2_s
         _ptr(x), _ptr(router_logits), _ptr(shared_gate_logits), _ptr(w13), _ptr(w13_scale),
         _ptr(w2), _ptr(w2_scale), T, H, I, E, K, shared, act_fmt, _ptr(out), _ptr(topk_ids),
         _ptr(topk_weights), _ptr(workspace), workspace.numel(), _stream(stream)))
+    return out
+
+
+def mxfp4_forward_router(x, router_w, w13, w13_scale, w2, w2_scale, I: int, E: int, K: int,
+                         shared: int, act_fmt: int = ACT_BF16, out=None, topk_ids=None,
+                         topk_weights=None, logits_out=None, workspace=None, stream=None):
+    """moe_mxfp4_forward_router: the whole layer routed from x through the router
+    GEMM (router_w bf16 [E + shared, H]).  x bf16 [T, H] -> out bf16 [T, H]."""
+    _dt(x, torch.bfloat16, "x")
+    _dt(router_w, torch.bfloat16, "router_w")
+    T, H = x.shape
+    if out is None:
+        out = torch.empty(T, H, dtype=torch.bfloat16, device=x.device)
+    need = workspace_size(T, H, I, E, K, shared, act_fmt)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=x.device)
+    _check("moe_mxfp4_forward_router", lib().moe_mxfp4_forward_router(
+        _ptr(x), _ptr(router_w), _ptr(w13), _ptr(w13_scale), _ptr(w2), _ptr(w2_scale), T, H, I,
+        E, K, shared, act_fmt, _ptr(out), _ptr(topk_ids), _ptr(topk_weights), _ptr(logits_out),
+        _ptr(workspace), workspace.numel(), _stream(stream)))
     return out
 
 

@@ -32,6 +32,12 @@ assignment ids t*K'+k by expert id; the tile list is the 32-row tiles of
 each expert's group (VibeSys post, section "Prefill, cache and
 speculation": 32-row tiles in the MoE kernel).
 
+The router GEMM that produces the logits (the step before routing; the
+InferenceX post's fused_topk consumes a separately computed gating output)
+is logits = x . Wr^T over bf16 x and bf16 router rows, and with a shared
+expert the gate logit g = x . Wr[E] of one more row: router_logits computes
+it exactly (fp64 sums of exact products).
+
 Pins: tests/test_oracle_moe.py, tests/golden/route_align.json.
 """
 from __future__ import annotations
@@ -73,6 +79,16 @@ def route(logits: np.ndarray, gate, K: int, shared: int, renormalize: bool = Tru
         ids[:, K] = E
         w[:, K] = (1.0 / (1.0 + np.exp(-g))).astype(np.float32)
     return ids, w
+
+
+def router_logits(x_bits: np.ndarray, w_bits: np.ndarray) -> np.ndarray:
+    """Router GEMM: x bf16 bits [T, H], router rows bf16 bits [R, H] ->
+    fp64 [T, R] = x . W^T.  The inputs are decoded exactly and each product
+    of two bf16 values is exact in fp64; the sums are fp64 (exact unless a
+    row's products span more than fp64's 53 bits of magnitude)."""
+    x = mxfp4.bf16_to_f64(x_bits)
+    w = mxfp4.bf16_to_f64(w_bits)
+    return x @ w.T
 
 
 def align(ids: np.ndarray, Ep: int, tile_m: int = 32):

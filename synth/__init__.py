@@ -41,6 +41,7 @@ STREAM_W13 = 4
 STREAM_W2 = 5
 STREAM_OUTLIER = 6
 STREAM_SKEW = 7
+STREAM_ROUTER = 8
 
 ACT_BF16 = 0    # W4A16: bf16 activations
 ACT_MXFP4 = 1   # W4A4: activations quantised to MXFP4 on the fly
@@ -174,6 +175,15 @@ def expert_w2(cfg: MoEConfig, e: int, device="cpu") -> torch.Tensor:
     """Down weights of expert e: fp32 [H, I] ~ N(0, w_std)."""
     g = _gen(cfg.seed_w, STREAM_W2, e, device)
     return torch.randn(cfg.H, cfg.I, generator=g, device=device, dtype=torch.float32).mul_(cfg.w_std)
+
+
+def router_weight(cfg: MoEConfig, device="cpu") -> torch.Tensor:
+    """Router rows for the router GEMM: bf16 [E + shared, H] ~ N(0, 1/H), so
+    that x . Wr^T has roughly unit variance like the drawn logits; row E
+    (with a shared expert) is the shared expert's gate vector."""
+    g = _gen(cfg.seed_act, STREAM_ROUTER, 0, device)
+    w = torch.randn(cfg.E + cfg.shared, cfg.H, generator=g, device=device, dtype=torch.float32)
+    return w.mul_(cfg.H ** -0.5).to(torch.bfloat16)
 
 
 def ties_logits(T: int, E: int, seed: int) -> torch.Tensor:

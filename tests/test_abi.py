@@ -26,7 +26,7 @@ def declared_functions():
 def test_library_loads_and_exports_every_declared_symbol():
     lib = ops.lib()
     names = declared_functions()
-    assert len(names) == 11
+    assert len(names) == 14
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(ops.EXPORTS)
@@ -51,6 +51,35 @@ def test_route_topk_argument_errors():
     assert f(FAKE, None, 4, 2048, 2, 0, 1, FAKE, FAKE, None) == UNSUPPORTED  # E > 1024
     assert f(FAKE, FAKE, 4, 64, 32, 1, 1, FAKE, FAKE, None) == UNSUPPORTED   # K' > 32
     assert f(None, None, 0, 8, 2, 0, 1, None, None, None) == OK             # T = 0: nothing to do
+
+
+def test_route_topk_gemm_argument_errors():
+    f = ops.lib().moe_route_topk_gemm
+    ws = ops.route_gemm_workspace_size(64, 4096, 512, 1)
+    assert ws >= 64 * 513 * 4 and ops.route_gemm_workspace_size(0, 4096, 512, 1) == 0
+    assert ops.route_gemm_workspace_size(64, 4000, 512, 1) == 0
+    def call(**kw):
+        a = dict(x=FAKE, w=FAKE, T=64, H=4096, E=512, K=10, s=1, r=1, ids=FAKE, wt=FAKE, lo=None,
+                 ws=FAKE, wsb=ws)
+        a.update(kw)
+        return f(a["x"], a["w"], a["T"], a["H"], a["E"], a["K"], a["s"], a["r"], a["ids"], a["wt"],
+                 a["lo"], a["ws"], a["wsb"], None)
+    assert call(x=None) == INVALID
+    assert call(w=None) == INVALID
+    assert call(ids=None) == INVALID
+    assert call(ws=None) == INVALID
+    assert call(x=MIS) == INVALID
+    assert call(K=0) == INVALID
+    assert call(K=513) == INVALID
+    assert call(s=2) == INVALID
+    assert call(r=2) == INVALID
+    assert call(T=-1) == INVALID
+    assert call(H=4000) == UNSUPPORTED
+    assert call(E=2048, K=4) == UNSUPPORTED
+    assert call(K=32) == UNSUPPORTED                     # K' = 33
+    assert call(T=1 << 20) == UNSUPPORTED                # x beyond 2^31 bytes
+    assert call(wsb=ws - 1) == WS_SMALL
+    assert call(T=0, x=None, w=None, ids=None, wt=None, ws=None) == OK
 
 
 def test_align_sort_argument_errors():
@@ -149,3 +178,18 @@ def test_forward_argument_errors_and_workspace():
     assert call(a10=2048) == UNSUPPORTED
     assert call(a3=MIS) == INVALID
     assert call(a7=0, a0=None, a17=None, a18=0) == OK      # T = 0
+    fr = ops.lib().moe_mxfp4_forward_router
+    based = [FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 8, 256, 128, 16, 2, 1, 0, FAKE, None, None, None,
+             FAKE, ops.workspace_size(8, 256, 128, 16, 2, 1, 0), None]
+    def callr(**over):
+        a = list(based)
+        for i, v in over.items():
+            a[int(i[1:])] = v
+        return fr(*a)
+    assert callr(a1=None) == INVALID                        # no router rows
+    assert callr(a1=MIS) == INVALID
+    assert callr(a0=None) == INVALID
+    assert callr(a10=17) == INVALID                         # K > E
+    assert callr(a7=200) == UNSUPPORTED                     # H % 128
+    assert callr(a18=1) == WS_SMALL
+    assert callr(a6=0, a0=None, a1=None, a17=None, a18=0) == OK

@@ -10,6 +10,7 @@ import math
 import os
 
 import numpy as np
+import torch
 import pytest
 import scipy.special
 
@@ -191,3 +192,42 @@ def test_w4a4_close_to_w4a16():
     a4 = moe.forward(x, l, g, W, cfg.I, cfg.E, cfg.K, 1, act_fmt=moe.ACT_MXFP4)
     rel = np.linalg.norm(a4["out_f64"] - a16["out_f64"]) / np.linalg.norm(a16["out_f64"])
     assert 0.01 < rel < 0.25          # MXFP4 activations cost a few percent, not more
+
+
+# ---------------------------------------------------------------- router GEMM
+
+def _bits(a):
+    return torch.tensor(a, dtype=torch.float32).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+
+
+def test_router_logits_worked():
+    # hand-worked: x = [[1, 2], [0.5, -1]], W rows [1, 0], [3, 0.25], [-2, 4]
+    got = moe.router_logits(_bits([[1.0, 2.0], [0.5, -1.0]]), _bits([[1.0, 0.0], [3.0, 0.25], [-2.0, 4.0]]))
+    assert np.array_equal(got, np.array([[1.0, 3.5, 6.0], [0.5, 1.25, -5.0]]))
+
+
+def test_router_logits_unit_rows_pick_columns():
+    rng = np.random.default_rng(3)
+    w = rng.standard_normal((7, 32)).astype(np.float32)
+    wb = _bits(w)
+    for i in (0, 5, 31):
+        e = np.zeros((1, 32), dtype=np.float32)
+        e[0, i] = 1.0
+        got = moe.router_logits(_bits(e), wb)[0]
+        want = torch.tensor(w[:, i]).to(torch.bfloat16).float().numpy().astype(np.float64)
+        assert np.array_equal(got, want)
+
+
+def test_router_logits_triple_loop():
+    # plain loops over bf16 values; small integers times powers of two keep
+    # every partial sum exact, so the two must agree bit for bit
+    rng = np.random.default_rng(4)
+    x = rng.integers(-8, 9, size=(3, 40)) * 0.25
+    w = rng.integers(-8, 9, size=(5, 40)) * 0.125
+    got = moe.router_logits(_bits(x), _bits(w))
+    for t in range(3):
+        for e in range(5):
+            acc = 0.0
+            for h in range(40):
+                acc += float(x[t, h]) * float(w[e, h])
+            assert got[t, e] == acc
