@@ -29,6 +29,8 @@ CASES = {
     "prefill": (1536, 4096, 512, 10, 1),
     "w4a4_shape": (300, 6144, 256, 8, 1),
     "max_experts": (70, 512, 1024, 31, 1),
+    # enough token tiles for the wide (unsplit) router kernel; ragged last tile
+    "wide": (4200, 256, 300, 5, 1),
 }
 
 
