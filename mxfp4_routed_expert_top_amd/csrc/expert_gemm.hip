@@ -43,9 +43,15 @@ struct TileInfo {
   int expert, row0, rows;
 };
 
+// Workgroups take the tile table from its end: block b works on tile
+// num_tiles - 1 - b / nsl (blocks past the live tiles exit at once).  The
+// shared expert's tiles are last in the table and are the longest-running
+// ones (T rows, several 16-row subtiles, where a routed expert of a decode
+// batch has 1-3 rows); started first they no longer form the kernel's tail.
 __device__ __forceinline__ bool load_tile(const int32_t* tiles, const int32_t* num_tiles,
-                                          const int32_t* offsets, int tile, TileInfo* ti) {
-  if (tile >= *num_tiles) return false;
+                                          const int32_t* offsets, int block, TileInfo* ti) {
+  const int tile = *num_tiles - 1 - block;
+  if (tile < 0) return false;
   ti->expert = tiles[2 * tile];
   ti->row0 = tiles[2 * tile + 1];
   ti->rows = min(kTileM, offsets[ti->expert + 1] - ti->row0);
@@ -187,7 +193,7 @@ __attribute__((amdgpu_waves_per_eu(MOE_GEMM_WAVES_PER_EU))) void gate_up_kernel(
     const uint8_t* __restrict__ w13, const uint8_t* __restrict__ w13s, int T, int H, int I, int Kp,
     int nsl, uint16_t* __restrict__ h) {
   TileInfo ti;
-  if (!load_tile(tiles, num_tiles, offsets, blockIdx.x / nsl, &ti)) return;
+  if (!load_tile(tiles, num_tiles, offsets, (int)(blockIdx.x / nsl), &ti)) return;
   const int s = blockIdx.x % nsl;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int nl = lane & 15, g = lane >> 4;
@@ -259,7 +265,7 @@ __attribute__((amdgpu_waves_per_eu(MOE_GEMM_WAVES_PER_EU))) void down_kernel(
     const int32_t* __restrict__ num_tiles, const uint8_t* __restrict__ w2,
     const uint8_t* __restrict__ w2s, int A, int H, int I, int nsl, float* __restrict__ y) {
   TileInfo ti;
-  if (!load_tile(tiles, num_tiles, offsets, blockIdx.x / nsl, &ti)) return;
+  if (!load_tile(tiles, num_tiles, offsets, (int)(blockIdx.x / nsl), &ti)) return;
   const int s = blockIdx.x % nsl;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int nl = lane & 15, g = lane >> 4;
