@@ -198,11 +198,12 @@ MOE_API moe_status moe_expert_gate_up(const void *act, const uint8_t *act_scale,
                               int32_t I, int32_t Ep, int32_t Kp, uint16_t *h, void *stream);
 
 /*
- * Grouped down GEMM: y[r, j] = sum_i h[r, i] * W2[e, j, i] (fp32 accumulation).
+ * Grouped down GEMM: y[r, j] = bf16( sum_i h[r, i] * W2[e, j, i] ) (fp32
+ * accumulation, one round-to-nearest-even to bf16 when stored).
  *   act_fmt = MOE_ACT_BF16:  h bf16 [A, I], h_scale = NULL
  *   act_fmt = MOE_ACT_MXFP4: h packed uint8 [A, I/2], h_scale uint8 [A, I/32]
  *   tile_m     as for moe_expert_gate_up
- *   y          out fp32 [A, H], sorted row order (A = T*Kp)
+ *   y          out bf16 [A, H], sorted row order (A = T*Kp)
  * Errors: INVALID_ARGUMENT, UNSUPPORTED (H or I not a multiple of 128, or a
  * tile_m / shape the kernels do not cover).
  */
@@ -210,18 +211,18 @@ MOE_API moe_status moe_expert_down(const void *h, const uint8_t *h_scale, int32_
                            const int32_t *expert_offsets, const int32_t *tile_table,
                            const int32_t *num_tiles, int32_t tile_m, const uint8_t *w2,
                            const uint8_t *w2_scale, int32_t T, int32_t H, int32_t I, int32_t Ep,
-                           int32_t Kp, float *y, void *stream);
+                           int32_t Kp, uint16_t *y, void *stream);
 
 /*
  * Weighted combine back into token order (the shared expert is slot K, so
  * no separate dense MLP is added: MiniMax M3 post, section "Shared expert
  * fusion"):  out[t, j] = bf16( sum_{k < Kp} w[t, k] * y[inv[t*Kp + k], j] ),
  * slots summed in order in fp32.
- *   y fp32 [T*Kp, H]; topk_weights fp32 [T, Kp]; inv_assign int32 [T*Kp];
+ *   y bf16 [T*Kp, H]; topk_weights fp32 [T, Kp]; inv_assign int32 [T*Kp];
  *   out bf16 [T, H]
  * Errors: INVALID_ARGUMENT, UNSUPPORTED (H not a multiple of 128).
  */
-MOE_API moe_status moe_combine(const float *y, const float *topk_weights, const int32_t *inv_assign,
+MOE_API moe_status moe_combine(const uint16_t *y, const float *topk_weights, const int32_t *inv_assign,
                        int32_t T, int32_t H, int32_t Kp, uint16_t *out, void *stream);
 
 /* The tile_m moe_mxfp4_forward uses for these shapes and activation format

@@ -263,7 +263,7 @@ __attribute__((amdgpu_waves_per_eu(MOE_GEMM_WAVES_PER_EU))) void down_kernel(
     const void* __restrict__ hin, const uint8_t* __restrict__ hscale,
     const int32_t* __restrict__ offsets, const int32_t* __restrict__ tiles,
     const int32_t* __restrict__ num_tiles, const uint8_t* __restrict__ w2,
-    const uint8_t* __restrict__ w2s, int A, int H, int I, int nsl, float* __restrict__ y) {
+    const uint8_t* __restrict__ w2s, int A, int H, int I, int nsl, uint16_t* __restrict__ y) {
   TileInfo ti;
   if (!load_tile(tiles, num_tiles, offsets, (int)(blockIdx.x / nsl), &ti)) return;
   const int s = blockIdx.x % nsl;
@@ -314,9 +314,9 @@ __attribute__((amdgpu_waves_per_eu(MOE_GEMM_WAVES_PER_EU))) void down_kernel(
     for (int r = 0; r < 4; ++r) {
       const int mm = 16 * mt + 4 * g + r;
       if (mm < ti.rows) {
-        float* yr = y + (size_t)(ti.row0 + mm) * H;
-        yr[j0] = acc[0][r];
-        yr[j0 + 16] = acc[1][r];
+        uint16_t* yr = y + (size_t)(ti.row0 + mm) * H;
+        yr[j0] = f32_to_bf16_rne(acc[0][r]);
+        yr[j0 + 16] = f32_to_bf16_rne(acc[1][r]);
       }
     }
   }
@@ -324,27 +324,30 @@ __attribute__((amdgpu_waves_per_eu(MOE_GEMM_WAVES_PER_EU))) void down_kernel(
 
 // -------------------------------------------------------------- combine ----
 
-// out[t, j] = bf16( sum_k w[t, k] * y[inv[t*K' + k], j] ), slots in order.
-__global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ y,
+// out[t, j] = bf16( sum_k w[t, k] * y[inv[t*K' + k], j] ), slots in order,
+// fp32 sums; 8 outputs per thread (16-byte loads of y, a 16-byte store).
+__global__ __launch_bounds__(256) void combine_kernel(const uint16_t* __restrict__ y,
                                                       const float* __restrict__ w,
                                                       const int32_t* __restrict__ inv, int H,
                                                       int Kp, int nbx, uint16_t* __restrict__ out) {
   const int t = blockIdx.x / nbx;
-  const int j = ((blockIdx.x % nbx) * 256 + threadIdx.x) * 4;
+  const int j = ((blockIdx.x % nbx) * 256 + threadIdx.x) * 8;
   if (j >= H) return;
-  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   for (int k = 0; k < Kp; ++k) {
     const float wk = w[(size_t)t * Kp + k];
-    const float4 v = *reinterpret_cast<const float4*>(y + (size_t)inv[(size_t)t * Kp + k] * H + j);
-    acc.x += wk * v.x;
-    acc.y += wk * v.y;
-    acc.z += wk * v.z;
-    acc.w += wk * v.w;
+    const u32x4_t v = load16(y + (size_t)inv[(size_t)t * Kp + k] * H + j);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      acc[2 * q] += wk * __uint_as_float(v[q] << 16);
+      acc[2 * q + 1] += wk * __uint_as_float(v[q] & 0xFFFF0000u);
+    }
   }
-  uint2 o;
-  o.x = (uint32_t)f32_to_bf16_rne(acc.x) | ((uint32_t)f32_to_bf16_rne(acc.y) << 16);
-  o.y = (uint32_t)f32_to_bf16_rne(acc.z) | ((uint32_t)f32_to_bf16_rne(acc.w) << 16);
-  *reinterpret_cast<uint2*>(out + (size_t)t * H + j) = o;
+  u32x4_t o;
+#pragma unroll
+  for (int q = 0; q < 4; ++q)
+    o[q] = (uint32_t)f32_to_bf16_rne(acc[2 * q]) | ((uint32_t)f32_to_bf16_rne(acc[2 * q + 1]) << 16);
+  *reinterpret_cast<u32x4_t*>(out + (size_t)t * H + j) = o;
 }
 
 }  // namespace
@@ -375,7 +378,7 @@ struct DownLaunch {
   static hipError_t run(dim3 grid, hipStream_t stream, const void* hin, const uint8_t* hscale,
                         const int32_t* offsets, const int32_t* tiles, const int32_t* num_tiles,
                         const uint8_t* w2, const uint8_t* w2s, int A, int H, int I, int nsl,
-                        float* y) {
+                        uint16_t* y) {
     const size_t lds = (size_t)128 * (I / 32) + (kFP4A ? 0 : (size_t)kXR * I * 2);
     hipLaunchKernelGGL((down_kernel<PH, kFP4A>), grid, dim3(256), lds, stream,
                        hin, hscale, offsets,
@@ -407,7 +410,7 @@ hipError_t launch_gate_up(int act_fmt, const void* act, const uint8_t* act_scale
 
 hipError_t launch_down(int act_fmt, const void* h, const uint8_t* h_scale, const int32_t* offsets,
                        const int32_t* tiles, const int32_t* num_tiles, int max_tiles,
-                       const uint8_t* w2, const uint8_t* w2s, int A, int H, int I, float* y,
+                       const uint8_t* w2, const uint8_t* w2s, int A, int H, int I, uint16_t* y,
                        hipStream_t stream) {
   const int nsl = H / 128;
   const int ph = expert_gemm_phase(I / 128);
@@ -419,9 +422,9 @@ hipError_t launch_down(int act_fmt, const void* h, const uint8_t* h_scale, const
                                        w2s, A, H, I, nsl, y);
 }
 
-hipError_t launch_combine(const float* y, const float* w, const int32_t* inv, int T, int H, int Kp,
+hipError_t launch_combine(const uint16_t* y, const float* w, const int32_t* inv, int T, int H, int Kp,
                           uint16_t* out, hipStream_t stream) {
-  const int nbx = (H / 4 + 255) / 256;
+  const int nbx = (H / 8 + 255) / 256;
   dim3 grid((unsigned)(nbx * T)), block(256);
   hipLaunchKernelGGL(combine_kernel, grid, block, 0, stream, y, w, inv, H, Kp, nbx, out);
   return hipGetLastError();

@@ -508,7 +508,7 @@ __global__ __launch_bounds__(256) void down_tiled_kernel(
     const void* __restrict__ hin, const uint8_t* __restrict__ hscale,
     const int32_t* __restrict__ offsets, const int32_t* __restrict__ tiles,
     const int32_t* __restrict__ num_tiles, const uint8_t* __restrict__ w2,
-    const uint8_t* __restrict__ w2s, int A, int H, int I, float* __restrict__ y) {
+    const uint8_t* __restrict__ w2s, int A, int H, int I, uint16_t* __restrict__ y) {
   int tile, s;
   if (!tile_slice<kFP4A>(blockIdx.x, *num_tiles, H / 256, &tile, &s)) return;
   const TileT ti = tile_of<BM>(tiles, offsets, tile);
@@ -541,9 +541,9 @@ __global__ __launch_bounds__(256) void down_tiled_kernel(
     for (int r = 0; r < 4; ++r) {
       const int m = 16 * mt + 4 * g + r;
       if (m < ti.rows) {
-        float* yr = y + (size_t)(ti.row0 + m) * H;
+        uint16_t* yr = y + (size_t)(ti.row0 + m) * H;
 #pragma unroll
-        for (int st = 0; st < 4; ++st) yr[j0 + 16 * st + nl] = acc[mt][st][r];
+        for (int st = 0; st < 4; ++st) yr[j0 + 16 * st + nl] = f32_to_bf16_rne(acc[mt][st][r]);
       }
     }
 }
@@ -563,7 +563,7 @@ hipError_t launch_gate_up_bm(const void* act, const uint8_t* act_scale, const in
 template <int BM, bool kFP4A>
 hipError_t launch_down_bm(const void* h, const uint8_t* h_scale, const int32_t* offsets,
                           const int32_t* tiles, const int32_t* num_tiles, int max_tiles,
-                          const uint8_t* w2, const uint8_t* w2s, int A, int H, int I, float* y,
+                          const uint8_t* w2, const uint8_t* w2s, int A, int H, int I, uint16_t* y,
                           hipStream_t stream) {
   const unsigned grid = tile_slice_grid<kFP4A>(max_tiles, H / 256);
   hipLaunchKernelGGL((down_tiled_kernel<BM, kFP4A>), dim3(grid), dim3(256), 0, stream, h,
@@ -606,7 +606,7 @@ hipError_t launch_gate_up_tiled(int tile_m, int act_fmt, const void* act, const 
 hipError_t launch_down_tiled(int tile_m, int act_fmt, const void* h, const uint8_t* h_scale,
                              const int32_t* offsets, const int32_t* tiles,
                              const int32_t* num_tiles, int max_tiles, const uint8_t* w2,
-                             const uint8_t* w2s, int A, int H, int I, float* y,
+                             const uint8_t* w2s, int A, int H, int I, uint16_t* y,
                              hipStream_t stream) {
   if (tile_m == 128)
     return act_fmt ? launch_down_bm<128, true>(h, h_scale, offsets, tiles, num_tiles, max_tiles,

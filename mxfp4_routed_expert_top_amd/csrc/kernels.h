@@ -37,9 +37,9 @@ hipError_t launch_gate_up(int act_fmt, const void* act, const uint8_t* act_scale
                           hipStream_t stream);
 hipError_t launch_down(int act_fmt, const void* h, const uint8_t* h_scale, const int32_t* offsets,
                        const int32_t* tiles, const int32_t* num_tiles, int max_tiles,
-                       const uint8_t* w2, const uint8_t* w2s, int A, int H, int I, float* y,
+                       const uint8_t* w2, const uint8_t* w2s, int A, int H, int I, uint16_t* y,
                        hipStream_t stream);
-hipError_t launch_combine(const float* y, const float* w, const int32_t* inv, int T, int H, int Kp,
+hipError_t launch_combine(const uint16_t* y, const float* w, const int32_t* inv, int T, int H, int Kp,
                           uint16_t* out, hipStream_t stream);
 
 bool expert_gemm_tiled_supported(int tile_m, int act_fmt, int H, int I);
@@ -51,5 +51,5 @@ hipError_t launch_gate_up_tiled(int tile_m, int act_fmt, const void* act, const 
 hipError_t launch_down_tiled(int tile_m, int act_fmt, const void* h, const uint8_t* h_scale,
                              const int32_t* offsets, const int32_t* tiles,
                              const int32_t* num_tiles, int max_tiles, const uint8_t* w2,
-                             const uint8_t* w2s, int A, int H, int I, float* y,
+                             const uint8_t* w2s, int A, int H, int I, uint16_t* y,
                              hipStream_t stream);

@@ -73,7 +73,7 @@ FwdLayout forward_layout(int64_t T, int64_t H, int64_t I, int64_t E, int64_t K, 
   L.hs = take(q ? A * I / 32 : 0);
   // y; the router GEMM's partial sums (when the call routes from x) live in
   // the same bytes: routing consumes them before the down GEMM writes y
-  L.y = take(std::max((size_t)(A * H * 4), router_workspace_bytes((int)T, (int)H, (int)Ep)));
+  L.y = take(std::max((size_t)(A * H * 2), router_workspace_bytes((int)T, (int)H, (int)Ep)));
   L.total = p;
   return L;
 }
@@ -219,7 +219,7 @@ moe_status moe_expert_down(const void* h, const uint8_t* h_scale, int32_t act_fm
                            const int32_t* expert_offsets, const int32_t* tile_table,
                            const int32_t* num_tiles, int32_t tile_m, const uint8_t* w2,
                            const uint8_t* w2_scale, int32_t T, int32_t H, int32_t I, int32_t Ep,
-                           int32_t Kp, float* y, void* stream) {
+                           int32_t Kp, uint16_t* y, void* stream) {
   if (T < 0 || Ep < 1 || Kp < 1 || (act_fmt != MOE_ACT_BF16 && act_fmt != MOE_ACT_MXFP4))
     return MOE_ERR_INVALID_ARGUMENT;
   moe_status st = check_shape_HI(H, I);
@@ -240,7 +240,7 @@ moe_status moe_expert_down(const void* h, const uint8_t* h_scale, int32_t act_fm
                               w2, w2_scale, T * Kp, H, I, y, s));
 }
 
-moe_status moe_combine(const float* y, const float* topk_weights, const int32_t* inv_assign,
+moe_status moe_combine(const uint16_t* y, const float* topk_weights, const int32_t* inv_assign,
                        int32_t T, int32_t H, int32_t Kp, uint16_t* out, void* stream) {
   if (T < 0 || H <= 0 || Kp < 1) return MOE_ERR_INVALID_ARGUMENT;
   if (H % 128) return MOE_ERR_UNSUPPORTED;
@@ -311,7 +311,8 @@ moe_status forward_impl(const uint16_t* x, const float* router_logits,
   uint16_t* h = (uint16_t*)(ws + L.h);
   uint8_t* hq = (uint8_t*)(ws + L.hq);
   uint8_t* hs = (uint8_t*)(ws + L.hs);
-  float* y = (float*)(ws + L.y);
+  uint16_t* y = (uint16_t*)(ws + L.y);
+  float* rpart = (float*)(ws + L.y);                       // router partial sums (same bytes)
   hipStream_t s = as_stream(stream);
   const int tm = choose_tile_m(A, Ep, H, I, act_fmt);
   const int mt = (int)max_tiles_for(A, Ep, tm);
@@ -319,10 +320,10 @@ moe_status forward_impl(const uint16_t* x, const float* router_logits,
   hipError_t e;
   if (router_w) {
     const int S = router_splits(T, H, Ep);
-    e = launch_router_gemm(x, router_w, T, H, Ep, y, s);
+    e = launch_router_gemm(x, router_w, T, H, Ep, rpart, s);
     if (e != hipSuccess) return MOE_ERR_DEVICE;
-    e = launch_route_topk_split(y, S, T, E, K, shared, 1, ids, wts,
-                                logits_out ? logits_out : y + (size_t)S * T * Ep, s);
+    e = launch_route_topk_split(rpart, S, T, E, K, shared, 1, ids, wts,
+                                logits_out ? logits_out : rpart + (size_t)S * T * Ep, s);
   } else {
     e = launch_route_topk(router_logits, shared_gate_logits, T, E, K, shared, 1, ids, wts, s);
   }

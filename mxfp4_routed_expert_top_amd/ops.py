@@ -220,9 +220,10 @@ def expert_gate_up(act, act_scale, act_fmt: int, align: dict, w13, w13_scale, T:
 
 def expert_down(h, h_scale, act_fmt: int, align: dict, w2, w2_scale, T: int, H: int, I: int,
                 Ep: int, Kp: int, y=None, stream=None):
-    """moe_expert_down -> y fp32 [T*Kp, H] in sorted row order."""
+    """moe_expert_down -> y bf16 [T*Kp, H] in sorted row order."""
     if y is None:
-        y = torch.empty(T * Kp, H, dtype=torch.float32, device=w2.device)
+        y = torch.empty(T * Kp, H, dtype=torch.bfloat16, device=w2.device)
+    _dt(y, torch.bfloat16, "y")
     _check("moe_expert_down", lib().moe_expert_down(
         _ptr(h), _ptr(h_scale), act_fmt, _ptr(align["offsets"]), _ptr(align["tiles"]),
         _ptr(align["num_tiles"]), align["tile_m"], _ptr(w2), _ptr(w2_scale), T, H, I, Ep, Kp,
@@ -231,7 +232,8 @@ def expert_down(h, h_scale, act_fmt: int, align: dict, w2, w2_scale, T: int, H: 
 
 
 def combine(y, topk_weights, inv, T: int, H: int, Kp: int, out=None, stream=None):
-    """moe_combine -> out bf16 [T, H]."""
+    """moe_combine: y bf16 [T*Kp, H] -> out bf16 [T, H]."""
+    _dt(y, torch.bfloat16, "y")
     if out is None:
         out = torch.empty(T, H, dtype=torch.bfloat16, device=y.device)
     _check("moe_combine", lib().moe_combine(
@@ -292,7 +294,7 @@ def alloc_stages(T: int, H: int, I: int, E: int, K: int, shared: int, act_fmt: i
              w=torch.empty(T, Kp, dtype=torch.float32, device=device),
              align=alloc_align(T, Kp, Ep, device),
              h=torch.empty(A, I, dtype=torch.bfloat16, device=device),
-             y=torch.empty(A, H, dtype=torch.float32, device=device),
+             y=torch.empty(A, H, dtype=torch.bfloat16, device=device),
              out=torch.empty(T, H, dtype=torch.bfloat16, device=device))
     if act_fmt == ACT_MXFP4:
         u8 = dict(dtype=torch.uint8, device=device)

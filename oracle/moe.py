@@ -18,11 +18,13 @@ x_t and (when the shared expert is folded in) gate logit g_t:
           expert becomes expert top-K+1 of one MoE dispatch; MiniMax M3 on
           MI355X post, section "Shared expert fusion")
   MLP_e(a) = W2_e . bf16( silu(W13_e[gate] . a) * (W13_e[up] . a) )
-  out_t = bf16( sum_k w_t,k * MLP_{e_k}(x_t) ), summed in slot order.
+  out_t = bf16( sum_k w_t,k * bf16(MLP_{e_k}(x_t)) ), summed in slot order.
 
 MXFP4 weights are decoded exactly; each dot product is an fp64 matmul over
-exact products; bf16 rounding happens where the GPU path stores bf16 (h and
-out).  For W4A4 the activations and h are MXFP4-quantised then decoded
+exact products; bf16 rounding happens where the GPU path stores bf16: h,
+each slot's expert output y (staged between the down GEMM and the combine;
+the pages fix no precision for it, and bf16 is the activations' type on the
+path) and out.  For W4A4 the activations and h are MXFP4-quantised then decoded
 before their GEMM (OpenRelay "Gemma 4 31B on MI355X" post, sections
 "Optimisation 3" and "Optimisation 4": activation + MXFP4 quantisation
 fused into one kernel).
@@ -150,9 +152,10 @@ def forward(x_bits, logits, gate, weights, I: int, E: int, K: int, shared: int,
     tokens: optional list of token indices; when given, only those tokens'
     outputs are computed (routing and grouping still cover all T tokens).
 
-    Returns a dict: ids, w, counts, offsets, sorted, inv, tiles, n_tiles,
-    out (uint16 bf16 bits [len(tokens) or T, H]), out_f64 (before the last
-    rounding), tokens."""
+    Each slot's expert output y is rounded to bf16 before the combine (where
+    the GPU path stores it).  Returns a dict: ids, w, counts, offsets,
+    sorted, inv, tiles, n_tiles, out (uint16 bf16 bits [len(tokens) or T,
+    H]), out_f64 (before the last rounding), tokens."""
     x_bits = np.asarray(x_bits, dtype=np.uint16)
     T, H = x_bits.shape
     Kp, Ep = K + shared, E + shared
@@ -171,7 +174,7 @@ def forward(x_bits, logits, gate, weights, I: int, E: int, K: int, shared: int,
     sel_ids = ids[tokens]                          # [n, Kp]
     for e in np.unique(sel_ids):
         rows, slots = np.nonzero(sel_ids == e)
-        y[rows, slots] = expert_mlp(a_all[rows], *weights(int(e)), I, act_fmt)
+        y[rows, slots] = mxfp4.round_bf16(expert_mlp(a_all[rows], *weights(int(e)), I, act_fmt))
 
     acc = np.zeros((len(tokens), H), dtype=np.float64)
     wt = w[tokens].astype(np.float64)

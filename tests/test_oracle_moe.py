@@ -131,7 +131,7 @@ def test_one_expert_reduces_to_dense_swiglu_mlp():
             u = sum(A[cfg.I + i][k] * xv[t, k] for k in range(cfg.H))
             h.append(float(mxfp4.round_bf16(g / (1 + math.exp(-g)) * u)))
         for j in range(cfg.H):
-            y = sum(B[j][i] * h[i] for i in range(cfg.I))
+            y = float(mxfp4.round_bf16(sum(B[j][i] * h[i] for i in range(cfg.I))))
             assert abs(res["out_f64"][t, j] - y) <= 1e-12 * max(1.0, abs(y))
     assert np.all(res["w"] == 1.0)
 
@@ -142,7 +142,7 @@ def test_shared_expert_fusion_equals_separate_dense_mlp():
     x, l, g = _inputs(cfg)
     fused = moe.forward(x, l, g, W, cfg.I, cfg.E, cfg.K, 1)
     routed = moe.forward(x, l, None, W, cfg.I, cfg.E, cfg.K, 0)
-    dense = moe.expert_mlp(mxfp4.bf16_to_f64(x), *W(cfg.E), cfg.I, moe.ACT_BF16)
+    dense = mxfp4.round_bf16(moe.expert_mlp(mxfp4.bf16_to_f64(x), *W(cfg.E), cfg.I, moe.ACT_BF16))
     sig = (1 / (1 + np.exp(-g.astype(np.float64)))).astype(np.float32).astype(np.float64)
     want = routed["out_f64"] + sig[:, None] * dense
     assert np.allclose(fused["out_f64"], want, rtol=1e-12, atol=1e-15)
