@@ -40,16 +40,28 @@ is logits = x . Wr^T over bf16 x and bf16 router rows, and with a shared
 expert the gate logit g = x . Wr[E] of one more row: router_logits computes
 it exactly (fp64 sums of exact products).
 
+Expert weights may also be MXFP8 (oracle/mxfp8.py), with bf16 activations;
+everything else is unchanged.
+
 Pins: tests/test_oracle_moe.py, tests/golden/route_align.json.
 """
 from __future__ import annotations
 
 import numpy as np
 
-from . import mxfp4
+from . import mxfp4, mxfp8
 
 ACT_BF16 = 0
 ACT_MXFP4 = 1
+# expert weight formats: MXFP4 (two E2M1 codes per byte) or MXFP8 (one E4M3
+# code per byte), both with one E8M0 scale per 32 elements along K
+W_MXFP4 = 0
+W_MXFP8 = 1
+
+
+def decode_weights(codes, scales, wfmt: int) -> np.ndarray:
+    """Expert weight rows -> fp64, exact, in either format."""
+    return mxfp8.decode(codes, scales) if wfmt == W_MXFP8 else mxfp4.decode(codes, scales)
 
 
 def route(logits: np.ndarray, gate, K: int, shared: int, renormalize: bool = True):
@@ -121,17 +133,18 @@ def silu(z):
 
 
 def expert_mlp(a: np.ndarray, w13_e, w13s_e, w2_e, w2s_e, I: int, act_fmt: int,
-               return_h: bool = False):
+               return_h: bool = False, wfmt: int = W_MXFP4):
     """One expert on rows a (fp64 [n, H], already bf16 / MXFP4-exact values).
 
     acc = a . dq(W13)^T (fp64); h = bf16(silu(acc[:, :I]) * acc[:, I:]);
     for W4A4 h is MXFP4-quantised along I and decoded; y = h . dq(W2)^T.
-    With return_h, also returns the bf16 h (before any MXFP4 step)."""
-    W13 = mxfp4.decode(w13_e, w13s_e)              # [2I, H]
+    dq decodes MXFP4 or (wfmt = W_MXFP8) MXFP8 weights.  With return_h, also
+    returns the bf16 h (before any MXFP4 step)."""
+    W13 = decode_weights(w13_e, w13s_e, wfmt)      # [2I, H]
     acc = a @ W13.T                                # [n, 2I]
     h = mxfp4.round_bf16(silu(acc[:, :I]) * acc[:, I:])
     hin = mxfp4.decode(*mxfp4.quantize(h)) if act_fmt == ACT_MXFP4 else h
-    W2 = mxfp4.decode(w2_e, w2s_e)                 # [H, I]
+    W2 = decode_weights(w2_e, w2s_e, wfmt)         # [H, I]
     y = hin @ W2.T                                 # [n, H]
     return (y, h) if return_h else y
 
@@ -143,12 +156,14 @@ def quantize_activations(x_bits: np.ndarray):
 
 def forward(x_bits, logits, gate, weights, I: int, E: int, K: int, shared: int,
             act_fmt: int = ACT_BF16, tokens=None, renormalize: bool = True,
-            tile_m: int = 32):
+            tile_m: int = 32, wfmt: int = W_MXFP4):
     """The whole layer.
 
     x_bits uint16 [T, H] (bf16 bit patterns); logits fp32 [T, E]; gate fp32
     [T] or None; weights(e) -> (w13 uint8 [2I, H/2], w13s uint8 [2I, H/32],
-    w2 uint8 [H, I/2], w2s uint8 [H, I/32]) for e in [0, E+shared).
+    w2 uint8 [H, I/2], w2s uint8 [H, I/32]) for e in [0, E+shared), MXFP4;
+    with wfmt = W_MXFP8 the code arrays hold one byte per element (w13
+    [2I, H], w2 [H, I]).  MXFP8 weights come with bf16 activations.
     tokens: optional list of token indices; when given, only those tokens'
     outputs are computed (routing and grouping still cover all T tokens).
 
@@ -156,6 +171,7 @@ def forward(x_bits, logits, gate, weights, I: int, E: int, K: int, shared: int,
     the GPU path stores it).  Returns a dict: ids, w, counts, offsets,
     sorted, inv, tiles, n_tiles, out (uint16 bf16 bits [len(tokens) or T,
     H]), out_f64 (before the last rounding), tokens."""
+    assert wfmt == W_MXFP4 or act_fmt == ACT_BF16
     x_bits = np.asarray(x_bits, dtype=np.uint16)
     T, H = x_bits.shape
     Kp, Ep = K + shared, E + shared
@@ -174,7 +190,8 @@ def forward(x_bits, logits, gate, weights, I: int, E: int, K: int, shared: int,
     sel_ids = ids[tokens]                          # [n, Kp]
     for e in np.unique(sel_ids):
         rows, slots = np.nonzero(sel_ids == e)
-        y[rows, slots] = mxfp4.round_bf16(expert_mlp(a_all[rows], *weights(int(e)), I, act_fmt))
+        y[rows, slots] = mxfp4.round_bf16(expert_mlp(a_all[rows], *weights(int(e)), I, act_fmt,
+                                                     wfmt=wfmt))
 
     acc = np.zeros((len(tokens), H), dtype=np.float64)
     wt = w[tokens].astype(np.float64)

@@ -15,7 +15,7 @@ import pytest
 import scipy.special
 
 import synth
-from oracle import moe, mxfp4
+from oracle import moe, mxfp4, mxfp8
 
 GOLD = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "route_align.json")))
 E2M1_TABLE = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "mxfp4_blocks.json")))["e2m1_values"]
@@ -134,6 +134,62 @@ def test_one_expert_reduces_to_dense_swiglu_mlp():
             y = float(mxfp4.round_bf16(sum(B[j][i] * h[i] for i in range(cfg.I))))
             assert abs(res["out_f64"][t, j] - y) <= 1e-12 * max(1.0, abs(y))
     assert np.all(res["w"] == 1.0)
+
+
+def _make_weights_mxfp8(cfg):
+    """Random MXFP8 weights for a small config, packed by the oracle."""
+    w13 = [mxfp8.quantize(synth.expert_w13(cfg, e).double().numpy()) for e in range(cfg.Ep)]
+    w2 = [mxfp8.quantize(synth.expert_w2(cfg, e).double().numpy()) for e in range(cfg.Ep)]
+    return lambda e: (w13[e][0], w13[e][1], w2[e][0], w2[e][1])
+
+
+def _decode_e4m3_by_torch(codes, scales):
+    """Independent MXFP8 decode: torch's float8_e4m3fn values times 2^(b-127)."""
+    v = torch.tensor(np.ascontiguousarray(codes)).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    return (v * np.repeat(2.0 ** (scales.astype(np.float64) - 127), 32, axis=-1)).tolist()
+
+
+def test_one_expert_mxfp8_reduces_to_dense_swiglu_mlp():
+    cfg = synth.custom_config(T=3, H=64, I=32, E=1, K=1, shared=0)
+    W = _make_weights_mxfp8(cfg)
+    x, l, _ = _inputs(cfg)
+    res = moe.forward(x, l, None, W, cfg.I, cfg.E, cfg.K, 0, wfmt=moe.W_MXFP8)
+    w13, w13s, w2, w2s = W(0)
+    assert w13.shape == (2 * cfg.I, cfg.H) and w2.shape == (cfg.H, cfg.I)
+    A = _decode_e4m3_by_torch(w13, w13s)   # [2I][H]
+    B = _decode_e4m3_by_torch(w2, w2s)     # [H][I]
+    xv = mxfp4.bf16_to_f64(x)
+    for t in range(cfg.T):
+        h = []
+        for i in range(cfg.I):
+            g = sum(A[i][k] * xv[t, k] for k in range(cfg.H))
+            u = sum(A[cfg.I + i][k] * xv[t, k] for k in range(cfg.H))
+            h.append(float(mxfp4.round_bf16(g / (1 + math.exp(-g)) * u)))
+        for j in range(cfg.H):
+            y = float(mxfp4.round_bf16(sum(B[j][i] * h[i] for i in range(cfg.I))))
+            assert abs(res["out_f64"][t, j] - y) <= 1e-12 * max(1.0, abs(y))
+
+
+def test_mxfp8_layer_closer_to_unquantised_weights_than_mxfp4():
+    """Both formats quantise the same fp32 draw; E4M3's 3 mantissa bits must
+    land much nearer the unquantised-weight layer than E2M1's 1 bit."""
+    cfg = synth.custom_config(T=12, H=128, I=64, E=6, K=2, shared=1)
+    x, l, g = _inputs(cfg)
+    raw = lambda e: (synth.expert_w13(cfg, e).double().numpy(), synth.expert_w2(cfg, e).double().numpy())
+    ids, w = moe.route(l, g, cfg.K, 1)
+    xv = mxfp4.bf16_to_f64(x)
+    ref = np.zeros((cfg.T, cfg.H))
+    for t in range(cfg.T):
+        for k in range(cfg.K + 1):
+            w13, w2 = raw(int(ids[t, k]))
+            acc = w13 @ xv[t]
+            hh = acc[:cfg.I] / (1 + np.exp(-acc[:cfg.I])) * acc[cfg.I:]
+            ref[t] += float(w[t, k]) * (w2 @ hh)
+    o4 = moe.forward(x, l, g, _make_weights(cfg), cfg.I, cfg.E, cfg.K, 1)["out_f64"]
+    o8 = moe.forward(x, l, g, _make_weights_mxfp8(cfg), cfg.I, cfg.E, cfg.K, 1, wfmt=moe.W_MXFP8)["out_f64"]
+    e4 = np.linalg.norm(o4 - ref) / np.linalg.norm(ref)
+    e8 = np.linalg.norm(o8 - ref) / np.linalg.norm(ref)
+    assert e8 < 0.08 and e4 > 2.5 * e8, (e4, e8)
 
 
 def test_shared_expert_fusion_equals_separate_dense_mlp():
