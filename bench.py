@@ -59,13 +59,15 @@ def make_inputs(cfg):
     gate = synth.gate_logits(cfg)
     gate = None if gate is None else gate.to(dev)
     u8 = dict(dtype=torch.uint8, device=dev)
-    w13 = torch.empty(cfg.Ep, 2 * cfg.I, cfg.H // 2, **u8)
+    per = 1 if cfg.wfmt == synth.W_MXFP8 else 2      # elements per code byte
+    quant = ops.mxfp8_quantize if cfg.wfmt == synth.W_MXFP8 else ops.mxfp4_quantize
+    w13 = torch.empty(cfg.Ep, 2 * cfg.I, cfg.H // per, **u8)
     w13s = torch.empty(cfg.Ep, 2 * cfg.I, cfg.H // 32, **u8)
-    w2 = torch.empty(cfg.Ep, cfg.H, cfg.I // 2, **u8)
+    w2 = torch.empty(cfg.Ep, cfg.H, cfg.I // per, **u8)
     w2s = torch.empty(cfg.Ep, cfg.H, cfg.I // 32, **u8)
     for e in range(cfg.Ep):             # float draws packed by the library's own quantiser
-        ops.mxfp4_quantize(synth.expert_w13(cfg, e, dev), w13[e], w13s[e])
-        ops.mxfp4_quantize(synth.expert_w2(cfg, e, dev), w2[e], w2s[e])
+        quant(synth.expert_w13(cfg, e, dev), w13[e], w13s[e])
+        quant(synth.expert_w2(cfg, e, dev), w2[e], w2s[e])
     torch.cuda.synchronize()
     return x, logits, gate, w13, w13s, w2, w2s
 
@@ -77,8 +79,9 @@ def algorithmic(cfg, counts):
     gate_up's own figure: the touched experts' W13 codes + scales and the
     activations it reads (bf16 x, or its MXFP4 codes + scales for W4A4)."""
     touched = int((counts > 0).sum())
-    w13_e = 2 * cfg.I * cfg.H // 2 + 2 * cfg.I * cfg.H // 32
-    w2_e = cfg.H * cfg.I // 2 + cfg.H * cfg.I // 32
+    per = 1 if cfg.wfmt == synth.W_MXFP8 else 2      # elements per code byte
+    w13_e = 2 * cfg.I * cfg.H // per + 2 * cfg.I * cfg.H // 32
+    w2_e = cfg.H * cfg.I // per + cfg.H * cfg.I // 32
     io = cfg.T * cfg.H * 2 + cfg.T * cfg.E * 4 + cfg.T * 4 * cfg.shared + cfg.T * cfg.H * 2
     x_gu = cfg.T * cfg.H * 2 if cfg.act_fmt == 0 else cfg.T * (cfg.H // 2 + cfg.H // 32)
     return dict(touched=touched, w13_bytes=touched * w13_e, w2_bytes=touched * w2_e,
@@ -90,7 +93,12 @@ def algorithmic(cfg, counts):
 def gate_up_kernel_name(cfg, tile_m):
     """The gate/up kernel's name as rocprofv3 reports it for this shape."""
     a = "true" if cfg.act_fmt else "false"
-    return f"gate_up_kernel<2, {a}>" if tile_m == 32 else f"gate_up_tiled_kernel<{tile_m}, {a}>"
+    if tile_m != 32:
+        return f"gate_up_tiled_kernel<{tile_m}, {a}>"
+    if cfg.wfmt == synth.W_MXFP8:
+        return "gate_up_kernel<1, false, true>"
+    ph = 2 if (cfg.H // 128) % 2 == 0 else 1          # phase width of the 32-row kernel
+    return f"gate_up_kernel<{ph}, {a}, false>"
 
 
 def traffic_path(cfg):
@@ -101,11 +109,12 @@ def traffic_path(cfg):
 def _pack_expert(args):
     """Draw one expert's float weights on the CPU and pack them with the
     oracle's quantiser (input preparation for the cpu_baseline leg)."""
-    from oracle import mxfp4
+    from oracle import mxfp4, mxfp8
     cfg, e = args
     torch.set_num_threads(1)
-    a = mxfp4.quantize(synth.expert_w13(cfg, e).double().numpy())
-    b = mxfp4.quantize(synth.expert_w2(cfg, e).double().numpy())
+    q = mxfp8.quantize if cfg.wfmt == synth.W_MXFP8 else mxfp4.quantize
+    a = q(synth.expert_w13(cfg, e).double().numpy())
+    b = q(synth.expert_w2(cfg, e).double().numpy())
     return e, (a[0], a[1], b[0], b[1])
 
 
@@ -143,7 +152,7 @@ def cpu_baseline(cfg, n_tokens, router=False):
             t_router = time.perf_counter() - t0
         t0 = time.perf_counter()
         moe.forward(x_bits, logits, gate, lambda e: packed[e], cfg.I, cfg.E, cfg.K, cfg.shared,
-                    cfg.act_fmt, tokens=tokens)
+                    cfg.act_fmt, tokens=tokens, wfmt=cfg.wfmt)
         dt = time.perf_counter() - t0 + t_router
     return {"value": round(len(tokens) / dt, 3), "unit": "tokens/s", "cores": 1, "kind": "oracle",
             "seconds": round(dt, 2),
@@ -159,8 +168,13 @@ def main():
         sys.exit(2)
     from mxfp4_routed_expert_top_amd import ops
     cfg = synth.CONFIGS[args.workload]
+    w8 = cfg.wfmt == synth.W_MXFP8
+    if args.router and w8:
+        print("--router is for MXFP4 weights", file=sys.stderr)
+        sys.exit(2)
     log(f"workload {cfg.name}: T={cfg.T} H={cfg.H} I={cfg.I} E={cfg.E} K={cfg.K} "
-        f"shared={cfg.shared} act={'mxfp4' if cfg.act_fmt else 'bf16'}")
+        f"shared={cfg.shared} act={'mxfp4' if cfg.act_fmt else 'bf16'} "
+        f"weights={'mxfp8' if w8 else 'mxfp4'}")
     if args.pmc_calibrate:
         a = torch.zeros(1 << 28, dtype=torch.int32, device="cuda")      # 1 GiB
         torch.bitwise_not(a, out=torch.empty_like(a))
@@ -178,6 +192,8 @@ def main():
     bufs = ops.alloc_stages(cfg.T, cfg.H, cfg.I, cfg.E, cfg.K, cfg.shared, cfg.act_fmt, "cuda")
     ws = torch.empty(ops.workspace_size(cfg.T, cfg.H, cfg.I, cfg.E, cfg.K, cfg.shared, cfg.act_fmt),
                      dtype=torch.uint8, device="cuda")
+    assert not w8 or ws.numel() >= ops.mxfp8_workspace_size(cfg.T, cfg.H, cfg.I, cfg.E, cfg.K,
+                                                             cfg.shared)
     out = torch.empty(cfg.T, cfg.H, dtype=torch.bfloat16, device="cuda")
     stream = torch.cuda.current_stream()
 
@@ -187,13 +203,16 @@ def main():
         if args.router:
             ops.mxfp4_forward_router(x, wr, w13, w13s, w2, w2s, cfg.I, cfg.E, cfg.K, cfg.shared,
                                      cfg.act_fmt, out=out, workspace=ws)
+        elif w8:
+            ops.mxfp8_forward(x, logits, gate, w13, w13s, w2, w2s, cfg.I, cfg.E, cfg.K,
+                              cfg.shared, out=out, workspace=ws)
         else:
             ops.mxfp4_forward(x, logits, gate, w13, w13s, w2, w2s, cfg.I, cfg.E, cfg.K, cfg.shared,
                               cfg.act_fmt, out=out, workspace=ws)
 
     def step_stages(events):
         ops.forward_stages(x, logits, gate, w13, w13s, w2, w2s, cfg.I, cfg.E, cfg.K, cfg.shared,
-                           cfg.act_fmt, bufs=bufs, events=events)
+                           cfg.act_fmt, bufs=bufs, events=events, wfmt=cfg.wfmt)
 
     for _ in range(args.warmup):
         step()
@@ -255,7 +274,7 @@ def main():
         alg["layer_bytes"] += cfg.Ep * cfg.H * 2 - cfg.T * cfg.E * 4 - cfg.T * 4 * cfg.shared
         alg["flops"] += 2 * cfg.T * cfg.Ep * cfg.H
     from mxfp4_routed_expert_top_amd import profiling
-    tile_m = ops.gemm_tile_m(cfg.T, cfg.Kp, cfg.Ep, cfg.H, cfg.I, cfg.act_fmt)
+    tile_m = 32 if w8 else ops.gemm_tile_m(cfg.T, cfg.Kp, cfg.Ep, cfg.H, cfg.I, cfg.act_fmt)
     kname = gate_up_kernel_name(cfg, tile_m)
     gu_s = stage_ms["gate_up"] / 1e3
     mfma_peak = BF16_PEAK_TFLOPS if cfg.act_fmt == 0 else MXFP4_PEAK_TFLOPS
@@ -294,7 +313,8 @@ def main():
            "data": "synthetic",
            "config": {"workload": f"{cfg.name}: T={cfg.T} H={cfg.H} I={cfg.I} E={cfg.E} "
                                   f"K={cfg.K}+{cfg.shared} shared, "
-                                  f"{'W4A16' if cfg.act_fmt == 0 else 'W4A4'} MXFP4 weights"
+                                  + ("W8A16 MXFP8 weights" if w8 else
+                                     f"{'W4A16' if cfg.act_fmt == 0 else 'W4A4'} MXFP4 weights")
                                   + (", routed from x by the router GEMM" if args.router else ""),
                       "T": cfg.T, "H": cfg.H, "I": cfg.I, "E": cfg.E, "K": cfg.K,
                       "shared": cfg.shared, "parallelism": "none (1 GPU)"},

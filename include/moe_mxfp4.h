@@ -18,6 +18,12 @@
  *   all six in one call                                moe_mxfp4_forward
  *   0-6 in one call                                    moe_mxfp4_forward_router
  *
+ * The same layer over MXFP8 expert weights (bf16 activations; the pages
+ * serve MoE models in MXFP8 next to MXFP4: MiniMax M3 on MI355X post,
+ * section on its MI355X performance benchmarks): moe_mxfp8_quantize,
+ * moe_mxfp8_expert_gate_up, moe_mxfp8_expert_down, moe_mxfp8_forward, with
+ * steps 1, 2 and 6 shared.
+ *
  * Conventions for every entry point:
  *   - Data pointers are DEVICE pointers (HBM of the current HIP device),
  *     owned by the caller; the library reads/writes them only during the
@@ -46,6 +52,12 @@
  *   w13_scale uint8 [E', 2I, H/32]
  *   w2        uint8 [E', H, I/2]
  *   w2_scale  uint8 [E', H, I/32]
+ *
+ * MXFP8 (OCP Microscaling v1.0): per 32 consecutive elements along the
+ * reduction axis one E8M0 scale byte and 32 FP8 E4M3 codes, one per byte
+ * (s|eeee|mmm, bias 7, subnormals m/8 * 2^-6, largest 448, S.1111.111 =
+ * NaN outside the contract).  Layout as above with one byte per element:
+ *   w13 uint8 [E', 2I, H], w2 uint8 [E', H, I]; the scales as for MXFP4.
  */
 #ifndef MOE_MXFP4_H
 #define MOE_MXFP4_H
@@ -225,6 +237,49 @@ MOE_API moe_status moe_expert_down(const void *h, const uint8_t *h_scale, int32_
 MOE_API moe_status moe_combine(const uint16_t *y, const float *topk_weights, const int32_t *inv_assign,
                        int32_t T, int32_t H, int32_t Kp, uint16_t *out, void *stream);
 
+/*
+ * MXFP8-quantise rows x cols values (packing float expert weights).  Per
+ * 32-block: X = floor(log2 amax) - 8, clamped to [-127, 127] (-127 for an
+ * all-zero block); scale byte X + 127; each v / 2^X rounded to the nearest
+ * E4M3 value, ties to the even code, saturating at 448, sign kept.
+ *   src        fp32 or bf16 [rows, cols] (src_dtype), 16-byte aligned
+ *   codes      out uint8 [rows, cols], 16-byte aligned
+ *   scales     out uint8 [rows, cols/32]
+ * Errors: as moe_mxfp4_quantize.
+ */
+MOE_API moe_status moe_mxfp8_quantize(const void *src, int32_t src_dtype, int64_t rows, int64_t cols,
+                              uint8_t *codes, uint8_t *scales, void *stream);
+
+/*
+ * Grouped gate/up GEMM + SwiGLU over MXFP8 weights, bf16 activations
+ * (W8A16): as moe_expert_gate_up with act_fmt = MOE_ACT_BF16, the weights
+ * dequantised to bf16 in registers by the scaled FP8 converter.  Runs on
+ * 32-row tiles only: tile_m must be 32 (the tile table from moe_align_sort
+ * with tile_m = 32).
+ *   x          bf16 [T, H];  w13 uint8 [E', 2I, H], w13_scale uint8 [E', 2I, H/32]
+ *   h          out bf16 [T*Kp, I] in sorted row order
+ * Errors: INVALID_ARGUMENT, UNSUPPORTED (H or I not a multiple of 128,
+ * tile_m != 32, an expert's 2I x H code bytes above 2^32).
+ */
+MOE_API moe_status moe_mxfp8_expert_gate_up(const uint16_t *x, const int32_t *sorted_assign,
+                                    const int32_t *expert_offsets, const int32_t *tile_table,
+                                    const int32_t *num_tiles, int32_t tile_m, const uint8_t *w13,
+                                    const uint8_t *w13_scale, int32_t T, int32_t H, int32_t I,
+                                    int32_t Ep, int32_t Kp, uint16_t *h, void *stream);
+
+/*
+ * Grouped down GEMM over MXFP8 weights (W8A16): as moe_expert_down with
+ * act_fmt = MOE_ACT_BF16; tile_m must be 32.
+ *   h          bf16 [T*Kp, I];  w2 uint8 [E', H, I], w2_scale uint8 [E', H, I/32]
+ *   y          out bf16 [T*Kp, H], sorted row order
+ * Errors: as moe_mxfp8_expert_gate_up.
+ */
+MOE_API moe_status moe_mxfp8_expert_down(const uint16_t *h, const int32_t *expert_offsets,
+                                 const int32_t *tile_table, const int32_t *num_tiles,
+                                 int32_t tile_m, const uint8_t *w2, const uint8_t *w2_scale,
+                                 int32_t T, int32_t H, int32_t I, int32_t Ep, int32_t Kp,
+                                 uint16_t *y, void *stream);
+
 /* The tile_m moe_mxfp4_forward uses for these shapes and activation format
  * (A = T*Kp assignments over Ep experts): 32, 64 or 128 (see
  * moe_expert_gate_up). */
@@ -279,6 +334,25 @@ MOE_API moe_status moe_mxfp4_forward_router(const uint16_t *x, const uint16_t *r
                                             int32_t *topk_ids_out, float *topk_weights_out,
                                             float *logits_out, void *workspace,
                                             size_t workspace_bytes, void *stream);
+
+/* Workspace bytes moe_mxfp8_forward needs (0 for T = 0). */
+MOE_API size_t moe_mxfp8_workspace_size(int32_t T, int32_t H, int32_t I, int32_t E, int32_t K,
+                                int32_t shared);
+
+/*
+ * The whole layer over MXFP8 expert weights with bf16 activations (W8A16):
+ * route, align (32-row tiles), gate/up + SwiGLU, down, combine, enqueued on
+ * `stream`.  Arguments, outputs and errors as moe_mxfp4_forward with
+ * act_fmt = MOE_ACT_BF16, except the weights (MXFP8 layout above) and the
+ * workspace (moe_mxfp8_workspace_size bytes); UNSUPPORTED also when an
+ * expert's 2I x H code bytes exceed 2^32.
+ */
+MOE_API moe_status moe_mxfp8_forward(const uint16_t *x, const float *router_logits,
+                             const float *shared_gate_logits, const uint8_t *w13,
+                             const uint8_t *w13_scale, const uint8_t *w2, const uint8_t *w2_scale,
+                             int32_t T, int32_t H, int32_t I, int32_t E, int32_t K, int32_t shared,
+                             uint16_t *out, int32_t *topk_ids_out, float *topk_weights_out,
+                             void *workspace, size_t workspace_bytes, void *stream);
 
 #ifdef __cplusplus
 }

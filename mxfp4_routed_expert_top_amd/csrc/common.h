@@ -45,6 +45,19 @@ __device__ __forceinline__ bf16x8_t dequant8_bf16(uint32_t q, float scale) {
   return r;
 }
 
+// Eight E4M3 codes (two dwords, element i in byte i % 4 of dword i / 4)
+// times a power-of-two scale -> eight bf16 values, exact (E4M3 keeps 4
+// significant bits, bf16 8, with fp32's exponent range).  Uses the gfx950
+// scaled FP8 -> BF16 converter; its word select picks bytes 0-1 or 2-3.
+__device__ __forceinline__ bf16x8_t dequant8_bf16_fp8(uint32_t lo, uint32_t hi, float scale) {
+  bf16x2_t p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, scale, false);
+  bf16x2_t p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, scale, true);
+  bf16x2_t p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, scale, false);
+  bf16x2_t p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, scale, true);
+  bf16x8_t r = {p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
+  return r;
+}
+
 __device__ __forceinline__ floatx4_t mfma_bf16_16x16x32(bf16x8_t a, bf16x8_t b, floatx4_t c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }

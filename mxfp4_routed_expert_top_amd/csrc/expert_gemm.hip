@@ -86,9 +86,11 @@ struct Operands {
   bool xvalid;             // the lane's activation row exists (padded rows read zeros)
 };
 
-template <int PH, bool kFP4A, bool XL>
+template <int PH, bool kFP4A, bool XL, bool kW8>
 struct Phase {
-  u32x4_t q[2][PH];
+  // weight bytes per lane per chunk: 16 (32 E2M1 codes) or 32 (32 E4M3 codes)
+  static constexpr int NQ = kW8 ? 2 : 1;
+  u32x4_t q[2][PH * NQ];
   u32x4_t a[PH][(kFP4A || XL) ? 1 : 4];
   uint32_t as[PH];
 
@@ -96,7 +98,10 @@ struct Phase {
 #pragma unroll
     for (int j = 0; j < PH; ++j)
 #pragma unroll
-      for (int si = 0; si < 2; ++si) q[si][j] = bload16(o.w, o.wo[si], 64 * (c0 + j));
+      for (int si = 0; si < 2; ++si)
+#pragma unroll
+        for (int hq = 0; hq < NQ; ++hq)
+          q[si][NQ * j + hq] = bload16(o.w, o.wo[si], 64 * NQ * (c0 + j) + 16 * hq);
 #pragma unroll
     for (int j = 0; j < PH; ++j) {
       if constexpr (kFP4A) {
@@ -134,18 +139,25 @@ struct Phase {
         for (int si = 0; si < 2; ++si) {
           const float sc = e8m0_to_f32(sw[si]);
 #pragma unroll
-          for (int qq = 0; qq < 4; ++qq)
-            acc[si] = mfma_bf16_16x16x32(__builtin_bit_cast(bf16x8_t, x[qq]),
-                                         dequant8_bf16(q[si][j][qq], sc), acc[si]);
+          for (int qq = 0; qq < 4; ++qq) {
+            bf16x8_t wv;
+            if constexpr (kW8) {
+              const u32x4_t& d = q[si][2 * j + (qq >> 1)];
+              wv = dequant8_bf16_fp8(d[2 * (qq & 1)], d[2 * (qq & 1) + 1], sc);
+            } else {
+              wv = dequant8_bf16(q[si][j][qq], sc);
+            }
+            acc[si] = mfma_bf16_16x16x32(__builtin_bit_cast(bf16x8_t, x[qq]), wv, acc[si]);
+          }
         }
       }
     }
   }
 };
 
-template <int PH, bool kFP4A, bool XL>
+template <int PH, bool kFP4A, bool XL, bool kW8>
 __device__ __forceinline__ void wave_gemm(const Operands& o, int nph, floatx4_t (&acc)[2]) {
-  Phase<PH, kFP4A, XL> A, B;
+  Phase<PH, kFP4A, XL, kW8> A, B;
   int p = 0;
   if (nph & 1) {                 // an odd phase first, unpipelined
     A.load(o, 0);
@@ -184,7 +196,7 @@ __device__ __forceinline__ void scales_to_lds(rsrc_t r, uint32_t off, uint32_t b
 // the other (the second re-reads the weights, from L2): decode tiles mostly
 // have 1-3 rows and this keeps a single subtile's registers live.  SwiGLU in
 // registers, bf16 h stored in sorted row order.
-template <int PH, bool kFP4A>
+template <int PH, bool kFP4A, bool kW8>
 __global__ __launch_bounds__(256)
 __attribute__((amdgpu_waves_per_eu(MOE_GEMM_WAVES_PER_EU))) void gate_up_kernel(
     const void* __restrict__ act, const uint8_t* __restrict__ act_scale,
@@ -199,13 +211,14 @@ __attribute__((amdgpu_waves_per_eu(MOE_GEMM_WAVES_PER_EU))) void gate_up_kernel(
   const int nl = lane & 15, g = lane >> 4;
   const int i = s * 64 + wave * 16 + nl;
   const uint32_t rb = H / 2, rs = H / 32;
-  const size_t wbytes = (size_t)2 * I * rb, sbytes = (size_t)2 * I * rs;
+  const uint32_t wrb = kW8 ? H : H / 2;                    // weight code bytes per row
+  const size_t wbytes = (size_t)2 * I * wrb, sbytes = (size_t)2 * I * rs;
   extern __shared__ uint8_t lds_scales[];                  // [2][64 rows][rs]: gate, up
   Operands o;
   o.lds = lds_scales;
   o.w = make_rsrc(w13 + ti.expert * wbytes, (uint32_t)wbytes);
-  o.wo[0] = i * rb + 16 * g;
-  o.wo[1] = (I + i) * rb + 16 * g;
+  o.wo[0] = i * wrb + 16 * Phase<PH, kFP4A, false, kW8>::NQ * g;
+  o.wo[1] = (I + i) * wrb + 16 * Phase<PH, kFP4A, false, kW8>::NQ * g;
   o.lso[0] = (wave * 16 + nl) * rs + g;
   o.lso[1] = (64 + wave * 16 + nl) * rs + g;
   if (kFP4A) {
@@ -237,13 +250,13 @@ __attribute__((amdgpu_waves_per_eu(MOE_GEMM_WAVES_PER_EU))) void gate_up_kernel(
     if (xl) {
       o.ldx = lds_x + min(m, kXR - 1) * H * 2 + 64 * g;
       o.xvalid = m < ti.rows;
-      wave_gemm<PH, kFP4A, true>(o, H / 128 / PH, acc);
+      wave_gemm<PH, kFP4A, true, kW8>(o, H / 128 / PH, acc);
     } else {
       const uint32_t tok = min((unsigned)(sorted[ti.row0 + min(m, ti.rows - 1)] / Kp),
                                (unsigned)(T - 1));
       o.ao = m >= ti.rows ? kOutOfRange : (kFP4A ? tok * rb + 16 * g : tok * H * 2 + 64 * g);
       o.aso = m >= ti.rows ? kOutOfRange : tok * rs + g;
-      wave_gemm<PH, kFP4A, false>(o, H / 128 / PH, acc);
+      wave_gemm<PH, kFP4A, false, kW8>(o, H / 128 / PH, acc);
     }
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
@@ -257,7 +270,7 @@ __attribute__((amdgpu_waves_per_eu(MOE_GEMM_WAVES_PER_EU))) void gate_up_kernel(
 // down: a workgroup (4 waves) owns one tile and 128 output columns j; wave w
 // owns [32 w, 32 w + 32) of them (two 16-row strips of W2) over K = I.  y is
 // stored as fp32 in sorted row order.
-template <int PH, bool kFP4A>
+template <int PH, bool kFP4A, bool kW8>
 __global__ __launch_bounds__(256)
 __attribute__((amdgpu_waves_per_eu(MOE_GEMM_WAVES_PER_EU))) void down_kernel(
     const void* __restrict__ hin, const uint8_t* __restrict__ hscale,
@@ -271,13 +284,14 @@ __attribute__((amdgpu_waves_per_eu(MOE_GEMM_WAVES_PER_EU))) void down_kernel(
   const int nl = lane & 15, g = lane >> 4;
   const int j0 = s * 128 + wave * 32 + nl;                 // strip 0; strip 1 is j0 + 16
   const uint32_t rb = I / 2, rs = I / 32;
-  const size_t wbytes = (size_t)H * rb, sbytes = (size_t)H * rs;
+  const uint32_t wrb = kW8 ? I : I / 2;                    // weight code bytes per row
+  const size_t wbytes = (size_t)H * wrb, sbytes = (size_t)H * rs;
   extern __shared__ uint8_t lds_scales[];                  // [128 rows][rs]
   Operands o;
   o.lds = lds_scales;
   o.w = make_rsrc(w2 + ti.expert * wbytes, (uint32_t)wbytes);
-  o.wo[0] = j0 * rb + 16 * g;
-  o.wo[1] = (j0 + 16) * rb + 16 * g;
+  o.wo[0] = j0 * wrb + 16 * Phase<PH, kFP4A, false, kW8>::NQ * g;
+  o.wo[1] = (j0 + 16) * wrb + 16 * Phase<PH, kFP4A, false, kW8>::NQ * g;
   o.lso[0] = (wave * 32 + nl) * rs + g;
   o.lso[1] = (wave * 32 + 16 + nl) * rs + g;
   if (kFP4A) {
@@ -303,12 +317,12 @@ __attribute__((amdgpu_waves_per_eu(MOE_GEMM_WAVES_PER_EU))) void down_kernel(
     if (xl) {
       o.ldx = lds_x + min(m, kXR - 1) * I * 2 + 64 * g;
       o.xvalid = m < ti.rows;
-      wave_gemm<PH, kFP4A, true>(o, I / 128 / PH, acc);
+      wave_gemm<PH, kFP4A, true, kW8>(o, I / 128 / PH, acc);
     } else {
       const uint32_t row = ti.row0 + m;
       o.ao = m >= ti.rows ? kOutOfRange : (kFP4A ? row * rb + 16 * g : row * I * 2 + 64 * g);
       o.aso = m >= ti.rows ? kOutOfRange : row * rs + g;
-      wave_gemm<PH, kFP4A, false>(o, I / 128 / PH, acc);
+      wave_gemm<PH, kFP4A, false, kW8>(o, I / 128 / PH, acc);
     }
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
@@ -355,71 +369,70 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint16_t* __restrict
 int expert_gemm_tile_m() { return kTileM; }
 
 // Phase width (chunks of 128 K-elements per pipeline stage): 2 when the chunk
-// count is even, else 1.
+// count is even, else 1.  MXFP8 weights (32 bytes per lane per chunk) use 1,
+// which keeps the same bytes in flight per phase as MXFP4 with 2.
 int expert_gemm_phase(int nch) { return (MOE_GEMM_PH_MAX >= 2 && nch % 2 == 0) ? 2 : 1; }
 
 namespace {
-template <int PH, bool kFP4A>
+template <int PH, bool kFP4A, bool kW8>
 struct GateUpLaunch {
   static hipError_t run(dim3 grid, hipStream_t stream, const void* act, const uint8_t* act_scale,
                         const int32_t* sorted, const int32_t* offsets, const int32_t* tiles,
                         const int32_t* num_tiles, const uint8_t* w13, const uint8_t* w13s, int T,
                         int H, int I, int Kp, int nsl, uint16_t* h) {
     const size_t lds = (size_t)128 * (H / 32) + (kFP4A ? 0 : (size_t)kXR * H * 2);
-    hipLaunchKernelGGL((gate_up_kernel<PH, kFP4A>), grid, dim3(256), lds, stream,
+    hipLaunchKernelGGL((gate_up_kernel<PH, kFP4A, kW8>), grid, dim3(256), lds, stream,
                        act, act_scale,
                        sorted, offsets, tiles, num_tiles, w13, w13s, T, H, I, Kp, nsl, h);
     return hipGetLastError();
   }
 };
 
-template <int PH, bool kFP4A>
+template <int PH, bool kFP4A, bool kW8>
 struct DownLaunch {
   static hipError_t run(dim3 grid, hipStream_t stream, const void* hin, const uint8_t* hscale,
                         const int32_t* offsets, const int32_t* tiles, const int32_t* num_tiles,
                         const uint8_t* w2, const uint8_t* w2s, int A, int H, int I, int nsl,
                         uint16_t* y) {
     const size_t lds = (size_t)128 * (I / 32) + (kFP4A ? 0 : (size_t)kXR * I * 2);
-    hipLaunchKernelGGL((down_kernel<PH, kFP4A>), grid, dim3(256), lds, stream,
+    hipLaunchKernelGGL((down_kernel<PH, kFP4A, kW8>), grid, dim3(256), lds, stream,
                        hin, hscale, offsets,
                        tiles, num_tiles, w2, w2s, A, H, I, nsl, y);
     return hipGetLastError();
   }
 };
 
-template <template <int, bool> class Launch, bool kFP4A, typename... Args>
-hipError_t dispatch_ph(int ph, Args... args) {
-  return ph == 2 ? Launch<2, kFP4A>::run(args...) : Launch<1, kFP4A>::run(args...);
+// (activation format, weight format, phase width) -> kernel instance.  MXFP8
+// weights come with bf16 activations only (checked by the caller).
+template <template <int, bool, bool> class Launch, typename... Args>
+hipError_t dispatch(int act_fmt, int wfmt, int nch, Args... args) {
+  if (wfmt == 1) return Launch<1, false, true>::run(args...);
+  const int ph = expert_gemm_phase(nch);
+  if (act_fmt == 0)
+    return ph == 2 ? Launch<2, false, false>::run(args...) : Launch<1, false, false>::run(args...);
+  return ph == 2 ? Launch<2, true, false>::run(args...) : Launch<1, true, false>::run(args...);
 }
 }  // namespace
 
-hipError_t launch_gate_up(int act_fmt, const void* act, const uint8_t* act_scale,
+hipError_t launch_gate_up(int act_fmt, int wfmt, const void* act, const uint8_t* act_scale,
                           const int32_t* sorted, const int32_t* offsets, const int32_t* tiles,
                           const int32_t* num_tiles, int max_tiles, const uint8_t* w13,
                           const uint8_t* w13s, int T, int H, int I, int Kp, uint16_t* h,
                           hipStream_t stream) {
   const int nsl = I / 64;
-  const int ph = expert_gemm_phase(H / 128);
   dim3 grid((unsigned)(max_tiles * nsl));
-  if (act_fmt == 0)
-    return dispatch_ph<GateUpLaunch, false>(ph, grid, stream, act, act_scale, sorted, offsets,
-                                            tiles, num_tiles, w13, w13s, T, H, I, Kp, nsl, h);
-  return dispatch_ph<GateUpLaunch, true>(ph, grid, stream, act, act_scale, sorted, offsets, tiles,
-                                         num_tiles, w13, w13s, T, H, I, Kp, nsl, h);
+  return dispatch<GateUpLaunch>(act_fmt, wfmt, H / 128, grid, stream, act, act_scale, sorted,
+                                offsets, tiles, num_tiles, w13, w13s, T, H, I, Kp, nsl, h);
 }
 
-hipError_t launch_down(int act_fmt, const void* h, const uint8_t* h_scale, const int32_t* offsets,
-                       const int32_t* tiles, const int32_t* num_tiles, int max_tiles,
-                       const uint8_t* w2, const uint8_t* w2s, int A, int H, int I, uint16_t* y,
-                       hipStream_t stream) {
+hipError_t launch_down(int act_fmt, int wfmt, const void* h, const uint8_t* h_scale,
+                       const int32_t* offsets, const int32_t* tiles, const int32_t* num_tiles,
+                       int max_tiles, const uint8_t* w2, const uint8_t* w2s, int A, int H, int I,
+                       uint16_t* y, hipStream_t stream) {
   const int nsl = H / 128;
-  const int ph = expert_gemm_phase(I / 128);
   dim3 grid((unsigned)(max_tiles * nsl));
-  if (act_fmt == 0)
-    return dispatch_ph<DownLaunch, false>(ph, grid, stream, h, h_scale, offsets, tiles, num_tiles,
-                                          w2, w2s, A, H, I, nsl, y);
-  return dispatch_ph<DownLaunch, true>(ph, grid, stream, h, h_scale, offsets, tiles, num_tiles, w2,
-                                       w2s, A, H, I, nsl, y);
+  return dispatch<DownLaunch>(act_fmt, wfmt, I / 128, grid, stream, h, h_scale, offsets, tiles,
+                              num_tiles, w2, w2s, A, H, I, nsl, y);
 }
 
 hipError_t launch_combine(const uint16_t* y, const float* w, const int32_t* inv, int T, int H, int Kp,

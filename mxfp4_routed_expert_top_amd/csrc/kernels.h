@@ -27,18 +27,21 @@ hipError_t launch_align_sort(const int32_t* ids, int A, int Ep, int tile_m, int3
 
 hipError_t launch_mxfp4_quant(const void* src, int src_is_bf16, int64_t rows, int64_t cols,
                               uint8_t* packed, uint8_t* scales, hipStream_t stream);
+hipError_t launch_mxfp8_quant(const void* src, int src_is_bf16, int64_t rows, int64_t cols,
+                              uint8_t* codes, uint8_t* scales, hipStream_t stream);
 
 int expert_gemm_tile_m();
 int expert_gemm_phase(int nch);
-hipError_t launch_gate_up(int act_fmt, const void* act, const uint8_t* act_scale,
+// wfmt: 0 = MXFP4 weights, 1 = MXFP8 weights (bf16 activations only)
+hipError_t launch_gate_up(int act_fmt, int wfmt, const void* act, const uint8_t* act_scale,
                           const int32_t* sorted, const int32_t* offsets, const int32_t* tiles,
                           const int32_t* num_tiles, int max_tiles, const uint8_t* w13,
                           const uint8_t* w13s, int T, int H, int I, int Kp, uint16_t* h,
                           hipStream_t stream);
-hipError_t launch_down(int act_fmt, const void* h, const uint8_t* h_scale, const int32_t* offsets,
-                       const int32_t* tiles, const int32_t* num_tiles, int max_tiles,
-                       const uint8_t* w2, const uint8_t* w2s, int A, int H, int I, uint16_t* y,
-                       hipStream_t stream);
+hipError_t launch_down(int act_fmt, int wfmt, const void* h, const uint8_t* h_scale,
+                       const int32_t* offsets, const int32_t* tiles, const int32_t* num_tiles,
+                       int max_tiles, const uint8_t* w2, const uint8_t* w2s, int A, int H, int I,
+                       uint16_t* y, hipStream_t stream);
 hipError_t launch_combine(const uint16_t* y, const float* w, const int32_t* inv, int T, int H, int Kp,
                           uint16_t* out, hipStream_t stream);
 

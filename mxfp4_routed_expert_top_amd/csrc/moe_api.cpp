@@ -24,7 +24,9 @@ inline int64_t max_tiles_for(int64_t A, int64_t Ep, int64_t tile_m = MOE_TILE_M)
 
 // Rows per GEMM tile for a call, from the shapes alone: small groups stream
 // weights through 32-row tiles; larger groups use the LDS-tiled kernels.
-int choose_tile_m(int64_t A, int64_t Ep, int H, int I, int act_fmt) {
+// MXFP8 weights (wfmt 1) run on the 32-row kernels at every batch size.
+int choose_tile_m(int64_t A, int64_t Ep, int H, int I, int act_fmt, int wfmt = 0) {
+  if (wfmt == 1) return MOE_TILE_M;
   const int64_t avg = A / Ep;
   if (avg <= 8) return MOE_TILE_M;
   const int tm = avg <= 48 ? 64 : 128;
@@ -189,16 +191,41 @@ moe_status moe_mxfp4_quantize(const void* src, int32_t src_dtype, int64_t rows, 
                                      as_stream(stream)));
 }
 
-moe_status moe_expert_gate_up(const void* act, const uint8_t* act_scale, int32_t act_fmt,
-                              const int32_t* sorted_assign, const int32_t* expert_offsets,
-                              const int32_t* tile_table, const int32_t* num_tiles, int32_t tile_m,
-                              const uint8_t* w13, const uint8_t* w13_scale, int32_t T, int32_t H,
-                              int32_t I, int32_t Ep, int32_t Kp, uint16_t* h, void* stream) {
+moe_status moe_mxfp8_quantize(const void* src, int32_t src_dtype, int64_t rows, int64_t cols,
+                              uint8_t* codes, uint8_t* scales, void* stream) {
+  if (rows < 0 || cols < 0 || (src_dtype != MOE_SRC_F32 && src_dtype != MOE_SRC_BF16))
+    return MOE_ERR_INVALID_ARGUMENT;
+  if (cols % 32) return MOE_ERR_UNSUPPORTED;
+  if (rows == 0 || cols == 0) return MOE_OK;
+  if (!src || !codes || !scales || !aligned16(src) || !aligned16(codes))
+    return MOE_ERR_INVALID_ARGUMENT;
+  if (rows * (cols / 32) / 256 >= (int64_t)UINT32_MAX) return MOE_ERR_UNSUPPORTED;
+  return from_hip(launch_mxfp8_quant(src, src_dtype == MOE_SRC_BF16, rows, cols, codes, scales,
+                                     as_stream(stream)));
+}
+
+}  // extern "C"
+
+namespace {
+
+// Weight code bytes of one expert's W13 (2I rows) or W2 (H rows) must stay
+// within a 32-bit buffer range.
+bool weights_fit(int wfmt, int64_t rows, int64_t k) {
+  return rows * (wfmt == 1 ? k : k / 2) < (int64_t)UINT32_MAX;
+}
+
+moe_status gate_up_impl(const void* act, const uint8_t* act_scale, int32_t act_fmt, int wfmt,
+                        const int32_t* sorted_assign, const int32_t* expert_offsets,
+                        const int32_t* tile_table, const int32_t* num_tiles, int32_t tile_m,
+                        const uint8_t* w13, const uint8_t* w13_scale, int32_t T, int32_t H,
+                        int32_t I, int32_t Ep, int32_t Kp, uint16_t* h, void* stream) {
   if (T < 0 || Ep < 1 || Kp < 1 || (act_fmt != MOE_ACT_BF16 && act_fmt != MOE_ACT_MXFP4))
     return MOE_ERR_INVALID_ARGUMENT;
   moe_status st = check_shape_HI(H, I);
   if (st != MOE_OK) return st;
-  if (Ep > 2048 || !tile_m_ok(tile_m, act_fmt, H, I)) return MOE_ERR_UNSUPPORTED;
+  if (Ep > 2048 || !weights_fit(wfmt, 2 * (int64_t)I, H)) return MOE_ERR_UNSUPPORTED;
+  if (wfmt == 1 ? tile_m != MOE_TILE_M : !tile_m_ok(tile_m, act_fmt, H, I))
+    return MOE_ERR_UNSUPPORTED;
   if (T == 0) return MOE_OK;
   if (!act || !sorted_assign || !expert_offsets || !tile_table || !num_tiles || !w13 ||
       !w13_scale || !h || (act_fmt == MOE_ACT_MXFP4 && !act_scale))
@@ -211,20 +238,23 @@ moe_status moe_expert_gate_up(const void* act, const uint8_t* act_scale, int32_t
     return from_hip(launch_gate_up_tiled(tile_m, act_fmt, act, act_scale, sorted_assign,
                                          expert_offsets, tile_table, num_tiles, (int)mt, w13,
                                          w13_scale, T, H, I, Kp, h, s));
-  return from_hip(launch_gate_up(act_fmt, act, act_scale, sorted_assign, expert_offsets, tile_table,
-                                 num_tiles, (int)mt, w13, w13_scale, T, H, I, Kp, h, s));
+  return from_hip(launch_gate_up(act_fmt, wfmt, act, act_scale, sorted_assign, expert_offsets,
+                                 tile_table, num_tiles, (int)mt, w13, w13_scale, T, H, I, Kp, h,
+                                 s));
 }
 
-moe_status moe_expert_down(const void* h, const uint8_t* h_scale, int32_t act_fmt,
-                           const int32_t* expert_offsets, const int32_t* tile_table,
-                           const int32_t* num_tiles, int32_t tile_m, const uint8_t* w2,
-                           const uint8_t* w2_scale, int32_t T, int32_t H, int32_t I, int32_t Ep,
-                           int32_t Kp, uint16_t* y, void* stream) {
+moe_status down_impl(const void* h, const uint8_t* h_scale, int32_t act_fmt, int wfmt,
+                     const int32_t* expert_offsets, const int32_t* tile_table,
+                     const int32_t* num_tiles, int32_t tile_m, const uint8_t* w2,
+                     const uint8_t* w2_scale, int32_t T, int32_t H, int32_t I, int32_t Ep,
+                     int32_t Kp, uint16_t* y, void* stream) {
   if (T < 0 || Ep < 1 || Kp < 1 || (act_fmt != MOE_ACT_BF16 && act_fmt != MOE_ACT_MXFP4))
     return MOE_ERR_INVALID_ARGUMENT;
   moe_status st = check_shape_HI(H, I);
   if (st != MOE_OK) return st;
-  if (Ep > 2048 || !tile_m_ok(tile_m, act_fmt, H, I)) return MOE_ERR_UNSUPPORTED;
+  if (Ep > 2048 || !weights_fit(wfmt, H, I)) return MOE_ERR_UNSUPPORTED;
+  if (wfmt == 1 ? tile_m != MOE_TILE_M : !tile_m_ok(tile_m, act_fmt, H, I))
+    return MOE_ERR_UNSUPPORTED;
   if (T == 0) return MOE_OK;
   if (!h || !expert_offsets || !tile_table || !num_tiles || !w2 || !w2_scale || !y ||
       (act_fmt == MOE_ACT_MXFP4 && !h_scale))
@@ -236,8 +266,48 @@ moe_status moe_expert_down(const void* h, const uint8_t* h_scale, int32_t act_fm
   if (tile_m != MOE_TILE_M)
     return from_hip(launch_down_tiled(tile_m, act_fmt, h, h_scale, expert_offsets, tile_table,
                                       num_tiles, (int)mt, w2, w2_scale, T * Kp, H, I, y, s));
-  return from_hip(launch_down(act_fmt, h, h_scale, expert_offsets, tile_table, num_tiles, (int)mt,
-                              w2, w2_scale, T * Kp, H, I, y, s));
+  return from_hip(launch_down(act_fmt, wfmt, h, h_scale, expert_offsets, tile_table, num_tiles,
+                              (int)mt, w2, w2_scale, T * Kp, H, I, y, s));
+}
+
+}  // namespace
+
+extern "C" {
+
+moe_status moe_expert_gate_up(const void* act, const uint8_t* act_scale, int32_t act_fmt,
+                              const int32_t* sorted_assign, const int32_t* expert_offsets,
+                              const int32_t* tile_table, const int32_t* num_tiles, int32_t tile_m,
+                              const uint8_t* w13, const uint8_t* w13_scale, int32_t T, int32_t H,
+                              int32_t I, int32_t Ep, int32_t Kp, uint16_t* h, void* stream) {
+  return gate_up_impl(act, act_scale, act_fmt, 0, sorted_assign, expert_offsets, tile_table,
+                      num_tiles, tile_m, w13, w13_scale, T, H, I, Ep, Kp, h, stream);
+}
+
+moe_status moe_mxfp8_expert_gate_up(const uint16_t* x, const int32_t* sorted_assign,
+                                    const int32_t* expert_offsets, const int32_t* tile_table,
+                                    const int32_t* num_tiles, int32_t tile_m, const uint8_t* w13,
+                                    const uint8_t* w13_scale, int32_t T, int32_t H, int32_t I,
+                                    int32_t Ep, int32_t Kp, uint16_t* h, void* stream) {
+  return gate_up_impl(x, nullptr, MOE_ACT_BF16, 1, sorted_assign, expert_offsets, tile_table,
+                      num_tiles, tile_m, w13, w13_scale, T, H, I, Ep, Kp, h, stream);
+}
+
+moe_status moe_expert_down(const void* h, const uint8_t* h_scale, int32_t act_fmt,
+                           const int32_t* expert_offsets, const int32_t* tile_table,
+                           const int32_t* num_tiles, int32_t tile_m, const uint8_t* w2,
+                           const uint8_t* w2_scale, int32_t T, int32_t H, int32_t I, int32_t Ep,
+                           int32_t Kp, uint16_t* y, void* stream) {
+  return down_impl(h, h_scale, act_fmt, 0, expert_offsets, tile_table, num_tiles, tile_m, w2,
+                   w2_scale, T, H, I, Ep, Kp, y, stream);
+}
+
+moe_status moe_mxfp8_expert_down(const uint16_t* h, const int32_t* expert_offsets,
+                                 const int32_t* tile_table, const int32_t* num_tiles,
+                                 int32_t tile_m, const uint8_t* w2, const uint8_t* w2_scale,
+                                 int32_t T, int32_t H, int32_t I, int32_t Ep, int32_t Kp,
+                                 uint16_t* y, void* stream) {
+  return down_impl(h, nullptr, MOE_ACT_BF16, 1, expert_offsets, tile_table, num_tiles, tile_m, w2,
+                   w2_scale, T, H, I, Ep, Kp, y, stream);
 }
 
 moe_status moe_combine(const uint16_t* y, const float* topk_weights, const int32_t* inv_assign,
@@ -274,7 +344,7 @@ moe_status forward_impl(const uint16_t* x, const float* router_logits,
                         float* logits_out, const uint8_t* w13, const uint8_t* w13_scale,
                         const uint8_t* w2, const uint8_t* w2_scale, int32_t T, int32_t H,
                         int32_t I, int32_t E, int32_t K, int32_t shared, int32_t act_fmt,
-                        uint16_t* out, int32_t* topk_ids_out, float* topk_weights_out,
+                        int wfmt, uint16_t* out, int32_t* topk_ids_out, float* topk_weights_out,
                         void* workspace, size_t workspace_bytes, void* stream) {
   moe_status st = router_w ? check_route_shape(T, E, K, shared, 1)
                            : check_route(router_logits, shared_gate_logits, T, E, K, shared, 1);
@@ -283,8 +353,10 @@ moe_status forward_impl(const uint16_t* x, const float* router_logits,
     return MOE_ERR_UNSUPPORTED;                          // 32-bit buffer ranges
   if (router_w && !aligned16(router_w)) return MOE_ERR_INVALID_ARGUMENT;
   if (act_fmt != MOE_ACT_BF16 && act_fmt != MOE_ACT_MXFP4) return MOE_ERR_INVALID_ARGUMENT;
+  if (wfmt == 1 && act_fmt != MOE_ACT_BF16) return MOE_ERR_INVALID_ARGUMENT;
   st = check_shape_HI(H, I);
   if (st != MOE_OK) return st;
+  if (!weights_fit(wfmt, 2 * (int64_t)I, H) || !weights_fit(wfmt, H, I)) return MOE_ERR_UNSUPPORTED;
   if (T == 0) return MOE_OK;
   if (!x || !w13 || !w13_scale || !w2 || !w2_scale || !out) return MOE_ERR_INVALID_ARGUMENT;
   if (!aligned16(x) || !aligned16(w13) || !aligned16(w2) || !aligned16(out))
@@ -314,7 +386,7 @@ moe_status forward_impl(const uint16_t* x, const float* router_logits,
   uint16_t* y = (uint16_t*)(ws + L.y);
   float* rpart = (float*)(ws + L.y);                       // router partial sums (same bytes)
   hipStream_t s = as_stream(stream);
-  const int tm = choose_tile_m(A, Ep, H, I, act_fmt);
+  const int tm = choose_tile_m(A, Ep, H, I, act_fmt, wfmt);
   const int mt = (int)max_tiles_for(A, Ep, tm);
 
   hipError_t e;
@@ -340,8 +412,8 @@ moe_status forward_impl(const uint16_t* x, const float* router_logits,
   e = tm != MOE_TILE_M
           ? launch_gate_up_tiled(tm, act_fmt, a1, a1s, sorted, offsets, tiles, ntiles, mt, w13,
                                  w13_scale, T, H, I, Kp, h, s)
-          : launch_gate_up(act_fmt, a1, a1s, sorted, offsets, tiles, ntiles, mt, w13, w13_scale, T,
-                           H, I, Kp, h, s);
+          : launch_gate_up(act_fmt, wfmt, a1, a1s, sorted, offsets, tiles, ntiles, mt, w13,
+                           w13_scale, T, H, I, Kp, h, s);
   if (e != hipSuccess) return MOE_ERR_DEVICE;
   if (q) {
     e = launch_mxfp4_quant(h, 1, A, I, hq, hs, s);
@@ -352,8 +424,8 @@ moe_status forward_impl(const uint16_t* x, const float* router_logits,
   e = tm != MOE_TILE_M
           ? launch_down_tiled(tm, act_fmt, a2, a2s, offsets, tiles, ntiles, mt, w2, w2_scale,
                               (int)A, H, I, y, s)
-          : launch_down(act_fmt, a2, a2s, offsets, tiles, ntiles, mt, w2, w2_scale, (int)A, H, I, y,
-                        s);
+          : launch_down(act_fmt, wfmt, a2, a2s, offsets, tiles, ntiles, mt, w2, w2_scale, (int)A, H,
+                        I, y, s);
   if (e != hipSuccess) return MOE_ERR_DEVICE;
   return from_hip(launch_combine(y, wts, inv, T, H, Kp, out, s));
 }
@@ -370,7 +442,23 @@ moe_status moe_mxfp4_forward(const uint16_t* x, const float* router_logits,
                              float* topk_weights_out, void* workspace, size_t workspace_bytes,
                              void* stream) {
   return forward_impl(x, router_logits, shared_gate_logits, nullptr, nullptr, w13, w13_scale, w2,
-                      w2_scale, T, H, I, E, K, shared, act_fmt, out, topk_ids_out,
+                      w2_scale, T, H, I, E, K, shared, act_fmt, 0, out, topk_ids_out,
+                      topk_weights_out, workspace, workspace_bytes, stream);
+}
+
+size_t moe_mxfp8_workspace_size(int32_t T, int32_t H, int32_t I, int32_t E, int32_t K,
+                                int32_t shared) {
+  return moe_mxfp4_workspace_size(T, H, I, E, K, shared, MOE_ACT_BF16);
+}
+
+moe_status moe_mxfp8_forward(const uint16_t* x, const float* router_logits,
+                             const float* shared_gate_logits, const uint8_t* w13,
+                             const uint8_t* w13_scale, const uint8_t* w2, const uint8_t* w2_scale,
+                             int32_t T, int32_t H, int32_t I, int32_t E, int32_t K, int32_t shared,
+                             uint16_t* out, int32_t* topk_ids_out, float* topk_weights_out,
+                             void* workspace, size_t workspace_bytes, void* stream) {
+  return forward_impl(x, router_logits, shared_gate_logits, nullptr, nullptr, w13, w13_scale, w2,
+                      w2_scale, T, H, I, E, K, shared, MOE_ACT_BF16, 1, out, topk_ids_out,
                       topk_weights_out, workspace, workspace_bytes, stream);
 }
 
@@ -383,7 +471,7 @@ moe_status moe_mxfp4_forward_router(const uint16_t* x, const uint16_t* router_w,
                                     size_t workspace_bytes, void* stream) {
   if (T > 0 && !router_w) return MOE_ERR_INVALID_ARGUMENT;
   return forward_impl(x, nullptr, nullptr, T > 0 ? router_w : nullptr, logits_out, w13, w13_scale,
-                      w2, w2_scale, T, H, I, E, K, shared, act_fmt, out, topk_ids_out,
+                      w2, w2_scale, T, H, I, E, K, shared, act_fmt, 0, out, topk_ids_out,
                       topk_weights_out, workspace, workspace_bytes, stream);
 }
 

@@ -18,6 +18,7 @@ LIB_PATH = os.path.join(PKG, "libmoe_mxfp4.so")
 
 MOE_OK, MOE_ERR_INVALID_ARGUMENT, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE_TOO_SMALL, MOE_ERR_DEVICE = range(5)
 ACT_BF16, ACT_MXFP4 = 0, 1
+W_MXFP4, W_MXFP8 = 0, 1            # expert weight formats
 SRC_F32, SRC_BF16 = 0, 1
 TILE_M = 32
 
@@ -48,6 +49,14 @@ _SIGS = {
     "moe_mxfp4_workspace_size": (_SZ, [_I32, _I32, _I32, _I32, _I32, _I32, _I32]),
     "moe_mxfp4_forward": (_I32, [_P, _P, _P, _P, _P, _P, _P, _I32, _I32, _I32, _I32, _I32, _I32,
                                  _I32, _P, _P, _P, _P, _SZ, _P]),
+    "moe_mxfp8_quantize": (_I32, [_P, _I32, _I64, _I64, _P, _P, _P]),
+    "moe_mxfp8_expert_gate_up": (_I32, [_P, _P, _P, _P, _P, _I32, _P, _P, _I32, _I32, _I32, _I32,
+                                        _I32, _P, _P]),
+    "moe_mxfp8_expert_down": (_I32, [_P, _P, _P, _P, _I32, _P, _P, _I32, _I32, _I32, _I32, _I32,
+                                     _P, _P]),
+    "moe_mxfp8_workspace_size": (_SZ, [_I32, _I32, _I32, _I32, _I32, _I32]),
+    "moe_mxfp8_forward": (_I32, [_P, _P, _P, _P, _P, _P, _P, _I32, _I32, _I32, _I32, _I32, _I32,
+                                 _P, _P, _P, _P, _SZ, _P]),
 }
 EXPORTS = tuple(_SIGS)
 
@@ -201,6 +210,26 @@ def mxfp4_quantize(src, packed=None, scales=None, stream=None):
     return packed, scales
 
 
+def mxfp8_quantize(src, codes=None, scales=None, stream=None):
+    """moe_mxfp8_quantize: fp32 or bf16 [..., cols] -> (codes uint8 [..., cols], scales uint8 [..., cols/32])."""
+    if src.dtype == torch.float32:
+        dt = SRC_F32
+    elif src.dtype == torch.bfloat16:
+        dt = SRC_BF16
+    else:
+        raise TypeError("src must be float32 or bfloat16")
+    cols = src.shape[-1]
+    rows = src.numel() // cols if cols else 0
+    lead = src.shape[:-1]
+    if codes is None:
+        codes = torch.empty(*lead, cols, dtype=torch.uint8, device=src.device)
+    if scales is None:
+        scales = torch.empty(*lead, cols // 32, dtype=torch.uint8, device=src.device)
+    _check("moe_mxfp8_quantize", lib().moe_mxfp8_quantize(
+        _ptr(src), dt, rows, cols, _ptr(codes), _ptr(scales), _stream(stream)))
+    return codes, scales
+
+
 def gemm_tile_m(T: int, Kp: int, Ep: int, H: int, I: int, act_fmt: int = ACT_BF16) -> int:
     """moe_gemm_tile_m: the GEMM tile rows mxfp4_forward uses for these shapes."""
     return int(lib().moe_gemm_tile_m(T, Kp, Ep, H, I, act_fmt))
@@ -228,6 +257,32 @@ def expert_down(h, h_scale, act_fmt: int, align: dict, w2, w2_scale, T: int, H: 
         _ptr(h), _ptr(h_scale), act_fmt, _ptr(align["offsets"]), _ptr(align["tiles"]),
         _ptr(align["num_tiles"]), align["tile_m"], _ptr(w2), _ptr(w2_scale), T, H, I, Ep, Kp,
         _ptr(y), _stream(stream)))
+    return y
+
+
+def mxfp8_expert_gate_up(x, align: dict, w13, w13_scale, T: int, H: int, I: int, Ep: int,
+                         Kp: int, h=None, stream=None):
+    """moe_mxfp8_expert_gate_up (MXFP8 weights, bf16 x) -> h bf16 [T*Kp, I], sorted rows."""
+    _dt(x, torch.bfloat16, "x")
+    if h is None:
+        h = torch.empty(T * Kp, I, dtype=torch.bfloat16, device=w13.device)
+    _check("moe_mxfp8_expert_gate_up", lib().moe_mxfp8_expert_gate_up(
+        _ptr(x), _ptr(align["sorted"]), _ptr(align["offsets"]), _ptr(align["tiles"]),
+        _ptr(align["num_tiles"]), align["tile_m"], _ptr(w13), _ptr(w13_scale), T, H, I, Ep, Kp,
+        _ptr(h), _stream(stream)))
+    return h
+
+
+def mxfp8_expert_down(h, align: dict, w2, w2_scale, T: int, H: int, I: int, Ep: int, Kp: int,
+                      y=None, stream=None):
+    """moe_mxfp8_expert_down (MXFP8 weights, bf16 h) -> y bf16 [T*Kp, H], sorted rows."""
+    _dt(h, torch.bfloat16, "h")
+    if y is None:
+        y = torch.empty(T * Kp, H, dtype=torch.bfloat16, device=w2.device)
+    _dt(y, torch.bfloat16, "y")
+    _check("moe_mxfp8_expert_down", lib().moe_mxfp8_expert_down(
+        _ptr(h), _ptr(align["offsets"]), _ptr(align["tiles"]), _ptr(align["num_tiles"]),
+        align["tile_m"], _ptr(w2), _ptr(w2_scale), T, H, I, Ep, Kp, _ptr(y), _stream(stream)))
     return y
 
 
@@ -286,6 +341,29 @@ def mxfp4_forward_router(x, router_w, w13, w13_scale, w2, w2_scale, I: int, E: i
     return out
 
 
+def mxfp8_workspace_size(T, H, I, E, K, shared) -> int:
+    return int(lib().moe_mxfp8_workspace_size(T, H, I, E, K, shared))
+
+
+def mxfp8_forward(x, router_logits, shared_gate_logits, w13, w13_scale, w2, w2_scale, I: int,
+                  E: int, K: int, shared: int, out=None, topk_ids=None, topk_weights=None,
+                  workspace=None, stream=None):
+    """moe_mxfp8_forward: the whole layer over MXFP8 weights, bf16 activations."""
+    _dt(x, torch.bfloat16, "x")
+    _dt(router_logits, torch.float32, "router_logits")
+    T, H = x.shape
+    if out is None:
+        out = torch.empty(T, H, dtype=torch.bfloat16, device=x.device)
+    need = mxfp8_workspace_size(T, H, I, E, K, shared)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=x.device)
+    _check("moe_mxfp8_forward", lib().moe_mxfp8_forward(
+        _ptr(x), _ptr(router_logits), _ptr(shared_gate_logits), _ptr(w13), _ptr(w13_scale),
+        _ptr(w2), _ptr(w2_scale), T, H, I, E, K, shared, _ptr(out), _ptr(topk_ids),
+        _ptr(topk_weights), _ptr(workspace), workspace.numel(), _stream(stream)))
+    return out
+
+
 def alloc_stages(T: int, H: int, I: int, E: int, K: int, shared: int, act_fmt: int,
                  device) -> dict:
     """Preallocated outputs of every stage of one pass (for forward_stages)."""
@@ -305,11 +383,14 @@ def alloc_stages(T: int, H: int, I: int, E: int, K: int, shared: int, act_fmt: i
 
 def forward_stages(x, router_logits, shared_gate_logits, w13, w13_scale, w2, w2_scale, I: int,
                    E: int, K: int, shared: int, act_fmt: int = ACT_BF16, bufs=None, stream=None,
-                   events=None):
-    """The same pass as mxfp4_forward, one C entry point per stage, keeping
-    every intermediate (in `bufs` if given, see alloc_stages).  `events`, if
-    given, maps a stage name (route, align, quant_x, gate_up, quant_h, down,
-    combine) to a (start, end) pair of torch.cuda.Event recorded around it."""
+                   events=None, wfmt: int = W_MXFP4):
+    """The same pass as mxfp4_forward (mxfp8_forward for wfmt = W_MXFP8), one
+    C entry point per stage, keeping every intermediate (in `bufs` if given,
+    see alloc_stages).  `events`, if given, maps a stage name (route, align,
+    quant_x, gate_up, quant_h, down, combine) to a (start, end) pair of
+    torch.cuda.Event recorded around it."""
+    if wfmt == W_MXFP8 and act_fmt != ACT_BF16:
+        raise ValueError("MXFP8 weights take bf16 activations")
     T, H = x.shape
     Kp, Ep = K + shared, E + shared
     b = alloc_stages(T, H, I, E, K, shared, act_fmt, x.device) if bufs is None else bufs
@@ -324,7 +405,8 @@ def forward_stages(x, router_logits, shared_gate_logits, w13, w13_scale, w2, w2_
                topk_weights=b["w"], stream=stream)
     rec("route", 1)
     rec("align", 0)
-    align_sort(b["ids"], Ep, tile_m=gemm_tile_m(T, Kp, Ep, H, I, act_fmt), out=b["align"], stream=stream)
+    tm = TILE_M if wfmt == W_MXFP8 else gemm_tile_m(T, Kp, Ep, H, I, act_fmt)
+    align_sort(b["ids"], Ep, tile_m=tm, out=b["align"], stream=stream)
     rec("align", 1)
     act, act_s = x, None
     if act_fmt == ACT_MXFP4:
@@ -333,8 +415,11 @@ def forward_stages(x, router_logits, shared_gate_logits, w13, w13_scale, w2, w2_
         rec("quant_x", 1)
         act, act_s = b["xq"], b["xs"]
     rec("gate_up", 0)
-    expert_gate_up(act, act_s, act_fmt, b["align"], w13, w13_scale, T, H, I, Ep, Kp, h=b["h"],
-                   stream=stream)
+    if wfmt == W_MXFP8:
+        mxfp8_expert_gate_up(x, b["align"], w13, w13_scale, T, H, I, Ep, Kp, h=b["h"], stream=stream)
+    else:
+        expert_gate_up(act, act_s, act_fmt, b["align"], w13, w13_scale, T, H, I, Ep, Kp, h=b["h"],
+                       stream=stream)
     rec("gate_up", 1)
     hin, hin_s = b["h"], None
     if act_fmt == ACT_MXFP4:
@@ -343,8 +428,11 @@ def forward_stages(x, router_logits, shared_gate_logits, w13, w13_scale, w2, w2_
         rec("quant_h", 1)
         hin, hin_s = b["hq"], b["hs"]
     rec("down", 0)
-    expert_down(hin, hin_s, act_fmt, b["align"], w2, w2_scale, T, H, I, Ep, Kp, y=b["y"],
-                stream=stream)
+    if wfmt == W_MXFP8:
+        mxfp8_expert_down(hin, b["align"], w2, w2_scale, T, H, I, Ep, Kp, y=b["y"], stream=stream)
+    else:
+        expert_down(hin, hin_s, act_fmt, b["align"], w2, w2_scale, T, H, I, Ep, Kp, y=b["y"],
+                    stream=stream)
     rec("down", 1)
     rec("combine", 0)
     combine(b["y"], b["w"], b["align"]["inv"], T, H, Kp, out=b["out"], stream=stream)

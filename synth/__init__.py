@@ -70,6 +70,7 @@ class MoEConfig:
     skew: bool = False     # Zipf-biased router logits with 3 dead experts
     outlier_p: float = 0.0 # fraction of activations multiplied by outlier_mult
     outlier_mult: float = 50.0
+    wfmt: int = 0          # expert weights packed as W_MXFP4 or W_MXFP8
 
     @property
     def Kp(self) -> int:
@@ -84,7 +85,10 @@ class MoEConfig:
         return self.T * self.Kp
 
 
-# The five workloads.  "decode" is the one the throughput line is quoted on.
+W_MXFP4, W_MXFP8 = 0, 1
+
+# The workloads.  "decode" is the one the throughput line is quoted on;
+# "decode_mxfp8" is the same batch and the same weight draws packed as MXFP8.
 CONFIGS = {
     "tiny": MoEConfig("tiny", T=8, H=256, I=128, E=16, K=2, shared=0,
                       act_fmt=ACT_BF16, seed_act=1000, seed_w=70),
@@ -97,6 +101,8 @@ CONFIGS = {
                                 skew=True),
     "w4a4": MoEConfig("w4a4", T=4096, H=6144, I=1536, E=256, K=8, shared=1,
                       act_fmt=ACT_MXFP4, seed_act=1004, seed_w=74, outlier_p=0.001),
+    "decode_mxfp8": MoEConfig("decode_mxfp8", T=64, H=4096, I=1024, E=512, K=10, shared=1,
+                              act_fmt=ACT_BF16, seed_act=1001, seed_w=77, wfmt=W_MXFP8),
 }
 
 

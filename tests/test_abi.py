@@ -26,7 +26,7 @@ def declared_functions():
 def test_library_loads_and_exports_every_declared_symbol():
     lib = ops.lib()
     names = declared_functions()
-    assert len(names) == 14
+    assert len(names) == 19
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(ops.EXPORTS)
@@ -193,3 +193,44 @@ def test_forward_argument_errors_and_workspace():
     assert callr(a7=200) == UNSUPPORTED                     # H % 128
     assert callr(a18=1) == WS_SMALL
     assert callr(a6=0, a0=None, a1=None, a17=None, a18=0) == OK
+
+
+def test_mxfp8_argument_errors():
+    L = ops.lib()
+    q = L.moe_mxfp8_quantize
+    assert q(FAKE, 2, 4, 64, FAKE, FAKE, None) == INVALID       # bad dtype
+    assert q(FAKE, 0, 4, 48, FAKE, FAKE, None) == UNSUPPORTED   # cols not a multiple of 32
+    assert q(MIS, 0, 4, 64, FAKE, FAKE, None) == INVALID        # misaligned source
+    assert q(None, 0, 0, 64, None, None, None) == OK            # nothing to do
+    gu = L.moe_mxfp8_expert_gate_up
+    # x, sorted, offsets, tiles, num_tiles, tile_m, w13, w13s, T, H, I, Ep, Kp, h, stream
+    base = [FAKE, FAKE, FAKE, FAKE, FAKE, 32, FAKE, FAKE, 4, 256, 128, 9, 3, FAKE, None]
+    def call(f, args, **kw):
+        a = list(args)
+        for k, v in kw.items():
+            a[int(k[1:])] = v
+        return f(*a)
+    assert call(gu, base, a5=64) == UNSUPPORTED                 # MXFP8 runs on 32-row tiles only
+    assert call(gu, base, a9=200) == UNSUPPORTED                # H not a multiple of 128
+    assert call(gu, base, a0=None) == INVALID
+    assert call(gu, base, a0=MIS) == INVALID
+    assert call(gu, base, a8=0, a0=None) == OK                  # T = 0
+    dn = L.moe_mxfp8_expert_down
+    # h, offsets, tiles, num_tiles, tile_m, w2, w2s, T, H, I, Ep, Kp, y, stream
+    based = [FAKE, FAKE, FAKE, FAKE, 32, FAKE, FAKE, 4, 256, 128, 9, 3, FAKE, None]
+    assert call(dn, based, a4=128) == UNSUPPORTED
+    assert call(dn, based, a12=None) == INVALID
+    assert call(dn, based, a5=MIS) == INVALID
+    # an expert's 2I x H code bytes must fit a 32-bit buffer range
+    assert call(gu, base, a9=65536, a10=65536) == UNSUPPORTED
+    ws = ops.mxfp8_workspace_size(64, 4096, 1024, 512, 10, 1)
+    assert ws == ops.workspace_size(64, 4096, 1024, 512, 10, 1, ops.ACT_BF16) and ws > 0
+    assert ops.mxfp8_workspace_size(0, 4096, 1024, 512, 10, 1) == 0
+    fw = L.moe_mxfp8_forward
+    # x, logits, gate, w13, w13s, w2, w2s, T, H, I, E, K, shared, out, ids, w, ws, bytes, stream
+    fb = [FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 4, 256, 128, 8, 2, 1, FAKE, None, None, FAKE,
+          1 << 30, None]
+    assert call(fw, fb, a17=16) == WS_SMALL
+    assert call(fw, fb, a2=None) == INVALID                     # shared without gate logits
+    assert call(fw, fb, a8=300) == UNSUPPORTED
+    assert call(fw, fb, a7=0) == OK
