@@ -41,6 +41,12 @@ def parse():
     p.add_argument("--router", action="store_true",
                    help="route from x through the router GEMM (bf16 router rows [E + shared, H]) "
                         "instead of taking precomputed logits")
+    p.add_argument("--layers", type=int, default=0,
+                   help="time L layers of the workload (each its own weights and router rows) "
+                        "in one moe_mxfp4_forward_layers call, eager and replayed from a HIP graph")
+    p.add_argument("--prefetch", action="store_true",
+                   help="with --layers: each layer's combine prefetches the next layer's router "
+                        "rows and shared expert into the caches")
     p.add_argument("--pmc-calibrate", action="store_true",
                    help="first run a plain 1 GiB kernel (torch.bitwise_not) whose HBM bytes are "
                         "known, for scaling FETCH_SIZE / WRITE_SIZE counter passes")
@@ -160,6 +166,69 @@ def cpu_baseline(cfg, n_tokens, router=False):
                       "numpy fp64 oracle on one host core"}
 
 
+def bench_layers(cfg, args):
+    """--layers L: the MoE part of a decode step through L layers in one C call
+    (router GEMM + the layer, per layer), eager and as one HIP graph."""
+    from mxfp4_routed_expert_top_amd import ops
+    L, dev = args.layers, "cuda"
+    x = synth.activations(cfg).to(dev)
+    layers = []
+    for l in range(L):
+        lc = synth.layer_config(cfg, l)
+        _, _, _, w13, w13s, w2, w2s = make_inputs(lc)
+        layers.append((synth.router_weight(lc).to(dev), w13, w13s, w2, w2s))
+        log(f"layer {l} weights ready")
+    ws = torch.empty(ops.workspace_size(cfg.T, cfg.H, cfg.I, cfg.E, cfg.K, cfg.shared, cfg.act_fmt),
+                     dtype=torch.uint8, device=dev)
+    out = torch.empty(cfg.T, cfg.H, dtype=torch.bfloat16, device=dev)
+    pf = 1 if args.prefetch else 0
+    s = torch.cuda.Stream()
+    call = lambda: ops.mxfp4_forward_layers(x, layers, cfg.I, cfg.E, cfg.K, cfg.shared,
+                                            cfg.act_fmt, prefetch=pf, out=out, workspace=ws)
+    with torch.cuda.stream(s):
+        for _ in range(args.warmup):
+            call()
+        torch.cuda.synchronize()
+        eager_out = out.clone()
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            call()
+        torch.cuda.synchronize()
+        eager_ms = (time.perf_counter() - t0) * 1e3 / args.steps
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=s):
+            call()
+    torch.cuda.synchronize()
+    for _ in range(3):
+        g.replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        g.replay()
+    torch.cuda.synchronize()
+    graph_ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    if not torch.equal(out, eager_out):
+        raise RuntimeError("graph replay and eager call disagree")
+    log(f"{L} layers: eager {eager_ms:.4f} ms, graph {graph_ms:.4f} ms")
+    res = {"metric": METRIC, "value": round(cfg.T / (graph_ms / L / 1e3), 1), "unit": "tokens/s",
+           "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+           "ms_per_step": round(graph_ms, 4), "higher_is_better": True, "scaling": "weak",
+           "vs_baseline": None, "dtype": "bf16" if cfg.act_fmt == 0 else "mxfp4",
+           "data": "synthetic",
+           "config": {"workload": f"{cfg.name}: {L} MoE layers in one call (T={cfg.T} H={cfg.H} "
+                                  f"I={cfg.I} E={cfg.E} K={cfg.K}+{cfg.shared} shared, each routed "
+                                  "from its input by its router GEMM), one HIP graph",
+                      "T": cfg.T, "H": cfg.H, "I": cfg.I, "E": cfg.E, "K": cfg.K,
+                      "shared": cfg.shared, "layers": L, "prefetch": bool(pf),
+                      "parallelism": "none (1 GPU)"},
+           "layers": {"L": L, "prefetch": bool(pf), "eager_ms": round(eager_ms, 4),
+                      "graph_ms": round(graph_ms, 4),
+                      "eager_ms_per_layer": round(eager_ms / L, 4),
+                      "graph_ms_per_layer": round(graph_ms / L, 4)},
+           "roofline": None, "cpu_baseline": None}
+    print(json.dumps(res), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -168,6 +237,11 @@ def main():
         sys.exit(2)
     from mxfp4_routed_expert_top_amd import ops
     cfg = synth.CONFIGS[args.workload]
+    if args.layers:
+        if cfg.wfmt == synth.W_MXFP8:
+            print("--layers is for MXFP4 weights", file=sys.stderr)
+            sys.exit(2)
+        return bench_layers(cfg, args)
     w8 = cfg.wfmt == synth.W_MXFP8
     if args.router and w8:
         print("--router is for MXFP4 weights", file=sys.stderr)

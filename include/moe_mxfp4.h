@@ -17,6 +17,8 @@
  *   6. weighted combine back into token order          moe_combine
  *   all six in one call                                moe_mxfp4_forward
  *   0-6 in one call                                    moe_mxfp4_forward_router
+ *   L layers of 0-6 in one call (a decode step's MoE layers)
+ *                                                      moe_mxfp4_forward_layers
  *
  * The same layer over MXFP8 expert weights (bf16 activations; the pages
  * serve MoE models in MXFP8 next to MXFP4: MiniMax M3 on MI355X post,
@@ -334,6 +336,41 @@ MOE_API moe_status moe_mxfp4_forward_router(const uint16_t *x, const uint16_t *r
                                             int32_t *topk_ids_out, float *topk_weights_out,
                                             float *logits_out, void *workspace,
                                             size_t workspace_bytes, void *stream);
+
+/* One layer of a multi-layer pass: its router rows and MXFP4 expert weights
+ * (device pointers, layouts as for moe_mxfp4_forward_router). */
+typedef struct {
+  const uint16_t *router_w;      /* bf16 [E + shared, H], 16-byte aligned */
+  const uint8_t *w13;            /* [E', 2I, H/2] */
+  const uint8_t *w13_scale;      /* [E', 2I, H/32] */
+  const uint8_t *w2;             /* [E', H, I/2] */
+  const uint8_t *w2_scale;       /* [E', H, I/32] */
+} moe_mxfp4_layer;
+
+/*
+ * L MoE layers back to back, as the MoE part of a decode step (the pages
+ * capture whole decode steps in HIP graphs, one launch per step: VibeSys
+ * post, section "Kernels and graph capture"; OpenRelay "Gemma 4 31B on
+ * MI355X" post, "Optimisation 2", the GPU waiting on the CPU): layer l computes
+ * moe_mxfp4_forward_router on its input with layers[l]'s weights; layer 0
+ * reads x, layer l > 0 reads layer l-1's output.  All layers write `out` in
+ * place (a layer's combine, its only write, runs after all its reads), so
+ * out holds the last layer's output.  With prefetch = 1 the combine of
+ * layer l also reads layer l+1's router rows and shared expert's weights
+ * (the only weights of the next layer known before its routing) into the
+ * caches while it runs; results are identical either way.  The call only
+ * enqueues work, so the whole pass can be captured in one HIP graph.
+ *   layers     host array of L layer descriptors (read during the call only)
+ *   workspace  >= moe_mxfp4_workspace_size(T, H, I, E, K, shared, act_fmt)
+ * Errors: INVALID_ARGUMENT (L < 1, null or misaligned layer pointers, bad
+ * prefetch flag), and those of moe_mxfp4_forward_router; every check runs
+ * before the first enqueue.
+ */
+MOE_API moe_status moe_mxfp4_forward_layers(const uint16_t *x, int32_t L,
+                                            const moe_mxfp4_layer *layers, int32_t T, int32_t H,
+                                            int32_t I, int32_t E, int32_t K, int32_t shared,
+                                            int32_t act_fmt, int32_t prefetch, uint16_t *out,
+                                            void *workspace, size_t workspace_bytes, void *stream);
 
 /* Workspace bytes moe_mxfp8_forward needs (0 for T = 0). */
 MOE_API size_t moe_mxfp8_workspace_size(int32_t T, int32_t H, int32_t I, int32_t E, int32_t K,

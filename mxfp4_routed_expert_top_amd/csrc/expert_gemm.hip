@@ -338,12 +338,36 @@ __attribute__((amdgpu_waves_per_eu(MOE_GEMM_WAVES_PER_EU))) void down_kernel(
 
 // -------------------------------------------------------------- combine ----
 
+constexpr int kPrefetchBlocks = 256;
+
+// Workgroups past the combine's own read pf's byte ranges in 4 KiB pages
+// (page j of a range goes to prefetch block j % kPrefetchBlocks) and discard
+// the data: the reads leave the lines in L2 and the memory-side cache for the
+// next kernels.  Buffer loads, so nothing outside a range is touched.
+__device__ __forceinline__ void prefetch_ranges(const Prefetch& pf, int b) {
+  uint32_t acc = 0;
+  for (int r = 0; r < pf.n; ++r) {
+    const rsrc_t rs = make_rsrc(pf.p[r], pf.bytes[r]);
+    const uint32_t pages = (pf.bytes[r] + 4095) / 4096;
+    for (uint32_t j = b; j < pages; j += kPrefetchBlocks) {
+      const u32x4_t v = bload16(rs, j * 4096 + threadIdx.x * 16, 0);
+      acc ^= v[0] ^ v[1] ^ v[2] ^ v[3];
+    }
+  }
+  asm volatile("" ::"v"(acc));                 // keeps the loads; no memory effect
+}
+
 // out[t, j] = bf16( sum_k w[t, k] * y[inv[t*K' + k], j] ), slots in order,
 // fp32 sums; 8 outputs per thread (16-byte loads of y, a 16-byte store).
 __global__ __launch_bounds__(256) void combine_kernel(const uint16_t* __restrict__ y,
                                                       const float* __restrict__ w,
                                                       const int32_t* __restrict__ inv, int H,
-                                                      int Kp, int nbx, uint16_t* __restrict__ out) {
+                                                      int Kp, int nbx, uint16_t* __restrict__ out,
+                                                      int T, Prefetch pf) {
+  if ((int)blockIdx.x >= nbx * T) {
+    prefetch_ranges(pf, (int)blockIdx.x - nbx * T);
+    return;
+  }
   const int t = blockIdx.x / nbx;
   const int j = ((blockIdx.x % nbx) * 256 + threadIdx.x) * 8;
   if (j >= H) return;
@@ -436,9 +460,11 @@ hipError_t launch_down(int act_fmt, int wfmt, const void* h, const uint8_t* h_sc
 }
 
 hipError_t launch_combine(const uint16_t* y, const float* w, const int32_t* inv, int T, int H, int Kp,
-                          uint16_t* out, hipStream_t stream) {
+                          uint16_t* out, hipStream_t stream, const Prefetch* pf) {
   const int nbx = (H / 8 + 255) / 256;
-  dim3 grid((unsigned)(nbx * T)), block(256);
-  hipLaunchKernelGGL(combine_kernel, grid, block, 0, stream, y, w, inv, H, Kp, nbx, out);
+  Prefetch none{};
+  const Prefetch& p = pf ? *pf : none;
+  dim3 grid((unsigned)(nbx * T + (p.n > 0 ? kPrefetchBlocks : 0))), block(256);
+  hipLaunchKernelGGL(combine_kernel, grid, block, 0, stream, y, w, inv, H, Kp, nbx, out, T, p);
   return hipGetLastError();
 }

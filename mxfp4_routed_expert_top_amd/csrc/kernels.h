@@ -42,8 +42,16 @@ hipError_t launch_down(int act_fmt, int wfmt, const void* h, const uint8_t* h_sc
                        const int32_t* offsets, const int32_t* tiles, const int32_t* num_tiles,
                        int max_tiles, const uint8_t* w2, const uint8_t* w2s, int A, int H, int I,
                        uint16_t* y, hipStream_t stream);
+// Byte ranges the combine's extra workgroups read into the caches (the next
+// layer's weights that are known before its routing); n = 0 for none.
+struct Prefetch {
+  static constexpr int kMax = 5;
+  const void* p[kMax];
+  uint32_t bytes[kMax];
+  int n;
+};
 hipError_t launch_combine(const uint16_t* y, const float* w, const int32_t* inv, int T, int H, int Kp,
-                          uint16_t* out, hipStream_t stream);
+                          uint16_t* out, hipStream_t stream, const Prefetch* pf = nullptr);
 
 bool expert_gemm_tiled_supported(int tile_m, int act_fmt, int H, int I);
 hipError_t launch_gate_up_tiled(int tile_m, int act_fmt, const void* act, const uint8_t* act_scale,

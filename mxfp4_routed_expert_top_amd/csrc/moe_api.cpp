@@ -345,7 +345,8 @@ moe_status forward_impl(const uint16_t* x, const float* router_logits,
                         const uint8_t* w2, const uint8_t* w2_scale, int32_t T, int32_t H,
                         int32_t I, int32_t E, int32_t K, int32_t shared, int32_t act_fmt,
                         int wfmt, uint16_t* out, int32_t* topk_ids_out, float* topk_weights_out,
-                        void* workspace, size_t workspace_bytes, void* stream) {
+                        void* workspace, size_t workspace_bytes, void* stream,
+                        const Prefetch* pf = nullptr) {
   moe_status st = router_w ? check_route_shape(T, E, K, shared, 1)
                            : check_route(router_logits, shared_gate_logits, T, E, K, shared, 1);
   if (st != MOE_OK) return st;
@@ -427,7 +428,7 @@ moe_status forward_impl(const uint16_t* x, const float* router_logits,
           : launch_down(act_fmt, wfmt, a2, a2s, offsets, tiles, ntiles, mt, w2, w2_scale, (int)A, H,
                         I, y, s);
   if (e != hipSuccess) return MOE_ERR_DEVICE;
-  return from_hip(launch_combine(y, wts, inv, T, H, Kp, out, s));
+  return from_hip(launch_combine(y, wts, inv, T, H, Kp, out, s, pf));
 }
 
 }  // namespace
@@ -473,6 +474,59 @@ moe_status moe_mxfp4_forward_router(const uint16_t* x, const uint16_t* router_w,
   return forward_impl(x, nullptr, nullptr, T > 0 ? router_w : nullptr, logits_out, w13, w13_scale,
                       w2, w2_scale, T, H, I, E, K, shared, act_fmt, 0, out, topk_ids_out,
                       topk_weights_out, workspace, workspace_bytes, stream);
+}
+
+
+moe_status moe_mxfp4_forward_layers(const uint16_t* x, int32_t L, const moe_mxfp4_layer* layers,
+                                    int32_t T, int32_t H, int32_t I, int32_t E, int32_t K,
+                                    int32_t shared, int32_t act_fmt, int32_t prefetch,
+                                    uint16_t* out, void* workspace, size_t workspace_bytes,
+                                    void* stream) {
+  if (L < 1 || !layers || (prefetch != 0 && prefetch != 1)) return MOE_ERR_INVALID_ARGUMENT;
+  // Every layer's pointers are checked before anything is enqueued; the shapes
+  // (shared by all layers) are checked by the first layer's call, before its
+  // first enqueue.
+  for (int l = 0; l < L; ++l) {
+    const moe_mxfp4_layer& w = layers[l];
+    if (T > 0 && (!w.router_w || !w.w13 || !w.w13_scale || !w.w2 || !w.w2_scale))
+      return MOE_ERR_INVALID_ARGUMENT;
+    if (!aligned16(w.router_w) || !aligned16(w.w13) || !aligned16(w.w2))
+      return MOE_ERR_INVALID_ARGUMENT;
+  }
+  const int64_t Ep = (int64_t)E + shared;
+  for (int l = 0; l < L; ++l) {
+    // The next layer's weights known before its routing: its router rows and
+    // its shared expert (every token's slot K).
+    Prefetch pf{};
+    if (prefetch && l + 1 < L && T > 0 && E > 0 && H > 0 && I > 0) {
+      const moe_mxfp4_layer& n = layers[l + 1];
+      const int64_t w13b = 2 * (int64_t)I * H / 2, w13sb = 2 * (int64_t)I * H / 32;
+      const int64_t w2b = (int64_t)H * I / 2, w2sb = (int64_t)H * I / 32;
+      auto add = [&](const void* p, int64_t bytes) {
+        if (bytes > 0 && bytes < (int64_t)UINT32_MAX) {
+          pf.p[pf.n] = p;
+          pf.bytes[pf.n++] = (uint32_t)bytes;
+        }
+      };
+      add(n.router_w, Ep * H * 2);
+      if (shared) {
+        add(n.w13 + (int64_t)E * w13b, w13b);
+        add(n.w13_scale + (int64_t)E * w13sb, w13sb);
+        add(n.w2 + (int64_t)E * w2b, w2b);
+        add(n.w2_scale + (int64_t)E * w2sb, w2sb);
+      }
+    }
+    // Layer 0 reads x; later layers read and rewrite out in place (each
+    // layer's combine, its only writer of out, runs after all its reads).
+    const moe_mxfp4_layer& w = layers[l];
+    moe_status st = forward_impl(l == 0 ? x : out, nullptr, nullptr, T > 0 ? w.router_w : nullptr,
+                                 nullptr, w.w13, w.w13_scale, w.w2, w.w2_scale, T, H, I, E, K,
+                                 shared, act_fmt, 0, out, nullptr, nullptr, workspace,
+                                 workspace_bytes, stream, pf.n ? &pf : nullptr);
+    if (st != MOE_OK) return st;
+    if (T == 0) return MOE_OK;
+  }
+  return MOE_OK;
 }
 
 }  // extern "C"

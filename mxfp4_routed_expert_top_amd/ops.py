@@ -49,6 +49,8 @@ _SIGS = {
     "moe_mxfp4_workspace_size": (_SZ, [_I32, _I32, _I32, _I32, _I32, _I32, _I32]),
     "moe_mxfp4_forward": (_I32, [_P, _P, _P, _P, _P, _P, _P, _I32, _I32, _I32, _I32, _I32, _I32,
                                  _I32, _P, _P, _P, _P, _SZ, _P]),
+    "moe_mxfp4_forward_layers": (_I32, [_P, _I32, _P, _I32, _I32, _I32, _I32, _I32, _I32, _I32,
+                                        _I32, _P, _P, _SZ, _P]),
     "moe_mxfp8_quantize": (_I32, [_P, _I32, _I64, _I64, _P, _P, _P]),
     "moe_mxfp8_expert_gate_up": (_I32, [_P, _P, _P, _P, _P, _I32, _P, _P, _I32, _I32, _I32, _I32,
                                         _I32, _P, _P]),
@@ -361,6 +363,34 @@ def mxfp8_forward(x, router_logits, shared_gate_logits, w13, w13_scale, w2, w2_s
         _ptr(x), _ptr(router_logits), _ptr(shared_gate_logits), _ptr(w13), _ptr(w13_scale),
         _ptr(w2), _ptr(w2_scale), T, H, I, E, K, shared, _ptr(out), _ptr(topk_ids),
         _ptr(topk_weights), _ptr(workspace), workspace.numel(), _stream(stream)))
+    return out
+
+
+class _Layer(ctypes.Structure):
+    """moe_mxfp4_layer: one layer's router rows and MXFP4 expert weights."""
+    _fields_ = [("router_w", _P), ("w13", _P), ("w13_scale", _P), ("w2", _P), ("w2_scale", _P)]
+
+
+def mxfp4_forward_layers(x, layers, I: int, E: int, K: int, shared: int,
+                         act_fmt: int = ACT_BF16, prefetch: int = 0, out=None, workspace=None,
+                         stream=None):
+    """moe_mxfp4_forward_layers: len(layers) layers back to back, each a
+    (router_w, w13, w13_scale, w2, w2_scale) tuple of device tensors; layer 0
+    reads x, each later layer the previous layer's output.  -> out bf16 [T, H]."""
+    _dt(x, torch.bfloat16, "x")
+    T, H = x.shape
+    if out is None:
+        out = torch.empty(T, H, dtype=torch.bfloat16, device=x.device)
+    need = workspace_size(T, H, I, E, K, shared, act_fmt)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=x.device)
+    arr = (_Layer * max(len(layers), 1))()
+    for i, (wr, w13, w13s, w2, w2s) in enumerate(layers):
+        _dt(wr, torch.bfloat16, "router_w")
+        arr[i] = _Layer(_ptr(wr), _ptr(w13), _ptr(w13s), _ptr(w2), _ptr(w2s))
+    _check("moe_mxfp4_forward_layers", lib().moe_mxfp4_forward_layers(
+        _ptr(x), len(layers), ctypes.cast(arr, _P), T, H, I, E, K, shared, act_fmt, prefetch,
+        _ptr(out), _ptr(workspace), workspace.numel(), _stream(stream)))
     return out
 
 

@@ -29,6 +29,7 @@ tensor is copied to the host for the oracle.
 from __future__ import annotations
 
 import math
+import dataclasses
 from dataclasses import dataclass, field
 
 import torch
@@ -104,6 +105,15 @@ CONFIGS = {
     "decode_mxfp8": MoEConfig("decode_mxfp8", T=64, H=4096, I=1024, E=512, K=10, shared=1,
                               act_fmt=ACT_BF16, seed_act=1001, seed_w=77, wfmt=W_MXFP8),
 }
+
+
+def layer_config(cfg: MoEConfig, layer: int) -> MoEConfig:
+    """The config of layer `layer` of a multi-layer pass: the same shapes with
+    its own weight and router-row draws (layer 0 is cfg itself)."""
+    if layer == 0:
+        return cfg
+    return dataclasses.replace(cfg, name=f"{cfg.name}_layer{layer}",
+                               seed_w=cfg.seed_w + 1000 * layer, seed_act=cfg.seed_act + 1000 * layer)
 
 
 def custom_config(name="custom", **kw) -> MoEConfig:

@@ -26,7 +26,7 @@ def declared_functions():
 def test_library_loads_and_exports_every_declared_symbol():
     lib = ops.lib()
     names = declared_functions()
-    assert len(names) == 19
+    assert len(names) == 20
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(ops.EXPORTS)
@@ -234,3 +234,27 @@ def test_mxfp8_argument_errors():
     assert call(fw, fb, a2=None) == INVALID                     # shared without gate logits
     assert call(fw, fb, a8=300) == UNSUPPORTED
     assert call(fw, fb, a7=0) == OK
+
+
+def test_forward_layers_argument_errors():
+    f = ops.lib().moe_mxfp4_forward_layers
+    arr = (ops._Layer * 2)(ops._Layer(FAKE, FAKE, FAKE, FAKE, FAKE),
+                           ops._Layer(FAKE, FAKE, FAKE, FAKE, FAKE))
+    p = ctypes.cast(arr, ctypes.c_void_p)
+    # x, L, layers, T, H, I, E, K, shared, act, prefetch, out, ws, bytes, stream
+    base = [FAKE, 2, p, 4, 256, 128, 8, 2, 1, 0, 1, FAKE, FAKE, 1 << 30, None]
+    def call(**kw):
+        a = list(base)
+        for k, v in kw.items():
+            a[int(k[1:])] = v
+        return f(*a)
+    assert call(a1=0) == INVALID                       # L < 1
+    assert call(a2=None) == INVALID                    # no layer array
+    assert call(a10=2) == INVALID                      # prefetch flag
+    assert call(a13=16) == WS_SMALL
+    assert call(a4=200) == UNSUPPORTED                 # H not a multiple of 128
+    assert call(a3=0) == OK                            # T = 0: nothing to do
+    arr[1] = ops._Layer(FAKE, None, FAKE, FAKE, FAKE)  # a later layer's null pointer
+    assert call() == INVALID
+    arr[1] = ops._Layer(FAKE, FAKE, FAKE, MIS, FAKE)   # a later layer's misaligned W2
+    assert call() == INVALID

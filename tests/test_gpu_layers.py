@@ -1,0 +1,182 @@
+"""Several MoE layers in one call (moe_mxfp4_forward_layers) against the same
+layers called one at a time, against the oracle, and under HIP graph capture.
+
+Each layer routes from its input through its own router rows, so a layer's
+top-K is an integer decision taken on floating-point logits.  As in the
+router tests, the oracle takes that decision on the GPU's own fp32 logits
+of the layer (and the GPU's output of the previous layer as the layer's
+input); the multi-layer call must equal the chain of single-layer router
+calls bit for bit, with and without the cache prefetch, and every graph
+replay must equal the eager result.
+
+Tolerance of a layer against the oracle: relative L2 as for one layer; the
+max-abs bound is taken per element against max(|want|, RMS(want)).  Both
+sides round y and out to bf16 at the same points, so they differ by rare
+one-ulp rounding flips, and a flip is proportional to the element it hits.
+A layer fed by another layer (no residual or norm in between) gives
+heavy-tailed outputs (max/RMS 6-9 by the third layer, against ~4 for
+N(0,1) inputs), where one flip at the largest element alone is 2.5-3.5% of
+the RMS."""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import synth
+from oracle import moe, mxfp4
+from tests.helpers import DEV, MAX_ABS_RMS, REL_L2, W_ATOL, bits, rel_l2
+
+pytestmark = pytest.mark.gpu
+
+
+def _say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def ops():
+    from mxfp4_routed_expert_top_amd import ops as o
+    return o
+
+
+def max_abs_elementwise(got_bits, want_bits) -> float:
+    """max_j |got_j - want_j| / max(|want_j|, RMS(want))."""
+    g = mxfp4.bf16_to_f64(got_bits)
+    w = mxfp4.bf16_to_f64(want_bits)
+    rms = float(np.sqrt(np.mean(w * w)))
+    return float(np.max(np.abs(g - w) / np.maximum(np.abs(w), max(rms, 1e-300))))
+
+
+class Layers:
+    """L layers of one workload's shapes, each with its own weights and
+    router rows (synth.layer_config), packed on the GPU, plus the oracle's
+    own packing of the same draws."""
+
+    def __init__(self, cfg, L):
+        self.cfg, self.L = cfg, L
+        c = cfg
+        self.x_cpu = synth.activations(c)
+        self.x = self.x_cpu.to(DEV)
+        self.w = []
+        u8 = dict(dtype=torch.uint8, device=DEV)
+        for l in range(L):
+            lc = synth.layer_config(c, l)
+            w13 = torch.empty(c.Ep, 2 * c.I, c.H // 2, **u8)
+            w13s = torch.empty(c.Ep, 2 * c.I, c.H // 32, **u8)
+            w2 = torch.empty(c.Ep, c.H, c.I // 2, **u8)
+            w2s = torch.empty(c.Ep, c.H, c.I // 32, **u8)
+            for e in range(c.Ep):
+                ops().mxfp4_quantize(synth.expert_w13(lc, e, DEV), w13[e], w13s[e])
+                ops().mxfp4_quantize(synth.expert_w2(lc, e, DEV), w2[e], w2s[e])
+            self.w.append((synth.router_weight(lc).to(DEV), w13, w13s, w2, w2s))
+        torch.cuda.synchronize()
+        self._ow = {}
+
+    def oracle_weights(self, l, e):
+        if (l, e) not in self._ow:
+            lc = synth.layer_config(self.cfg, l)
+            a = mxfp4.quantize(synth.expert_w13(lc, e, DEV).cpu().double().numpy())
+            b = mxfp4.quantize(synth.expert_w2(lc, e, DEV).cpu().double().numpy())
+            self._ow[(l, e)] = (a[0], a[1], b[0], b[1])
+        return self._ow[(l, e)]
+
+    def multi(self, prefetch, **kw):
+        c = self.cfg
+        return ops().mxfp4_forward_layers(self.x, self.w, c.I, c.E, c.K, c.shared, c.act_fmt,
+                                          prefetch=prefetch, **kw)
+
+    def chain(self):
+        """The layers one call at a time: (input, logits, output) per layer."""
+        c = self.cfg
+        cur, steps = self.x, []
+        for l in range(self.L):
+            lg = torch.empty(c.T, c.Ep, dtype=torch.float32, device=DEV)
+            out = ops().mxfp4_forward_router(cur, self.w[l][0], *self.w[l][1:], c.I, c.E, c.K,
+                                             c.shared, c.act_fmt, logits_out=lg)
+            steps.append((cur, lg, out))
+            cur = out
+        torch.cuda.synchronize()
+        return steps
+
+    def oracle_layer(self, l, x_in, logits, tokens=None):
+        """Layer l by the oracle on the GPU's input and fp32 logits of that layer."""
+        c = self.cfg
+        lg = logits.cpu().numpy()
+        return moe.forward(bits(x_in), lg[:, :c.E], lg[:, c.E] if c.shared else None,
+                           lambda e: self.oracle_weights(l, e), c.I, c.E, c.K, c.shared,
+                           c.act_fmt, tokens=tokens)
+
+
+SMALL = {
+    "ragged": synth.custom_config("layers_ragged", T=50, H=512, I=256, E=32, K=4, shared=1),
+    "no_shared": synth.custom_config("layers_no_shared", T=33, H=256, I=128, E=8, K=2, shared=0),
+    "w4a4": synth.custom_config("layers_w4a4", T=40, H=256, I=128, E=16, K=3, shared=1,
+                                act_fmt=synth.ACT_MXFP4, outlier_p=0.01),
+    "tiled": synth.custom_config("layers_tiled", T=300, H=512, I=256, E=16, K=3, shared=1),
+}
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+def test_layers_match_chain_and_oracle(name):
+    _say("layers", name)
+    P = Layers(SMALL[name], 3)
+    c = P.cfg
+    steps = P.chain()
+    for prefetch in (0, 1):
+        out = P.multi(prefetch)
+        torch.cuda.synchronize()
+        assert np.array_equal(bits(out), bits(steps[-1][2])), prefetch
+    for l, (x_in, lg, out) in enumerate(steps):
+        want = P.oracle_layer(l, x_in, lg)
+        e_rel = rel_l2(bits(out), want["out"])
+        e_max = max_abs_elementwise(bits(out), want["out"])
+        _say(f"  layer {l}: rel_l2 {e_rel:.2e}  max_abs (per element) {e_max:.2e}")
+        assert e_rel <= REL_L2[c.act_fmt] and e_max <= MAX_ABS_RMS
+    assert not np.array_equal(bits(steps[0][2]), bits(steps[1][2]))   # the layers differ
+
+
+def test_layers_graph_replays_equal_eager():
+    P = Layers(SMALL["ragged"], 2)
+    c = P.cfg
+    ws = torch.empty(ops().workspace_size(c.T, c.H, c.I, c.E, c.K, c.shared, c.act_fmt),
+                     dtype=torch.uint8, device=DEV)
+    out = torch.empty(c.T, c.H, dtype=torch.bfloat16, device=DEV)
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        P.multi(1, out=out, workspace=ws)
+        torch.cuda.synchronize()
+        eager = out.clone()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=s):
+            P.multi(1, out=out, workspace=ws)
+    torch.cuda.synchronize()
+    for i in range(4):
+        out.fill_(0)
+        ws.fill_(0xFF)                     # eager work between replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, eager), i
+
+
+def test_layers_full_decode_sampled():
+    """Two layers of the decode workload's shapes in the configuration the
+    bench times: equal to the chained calls bit for bit (with the prefetch),
+    and the last layer's sampled tokens against the oracle."""
+    cfg = synth.CONFIGS["decode"]
+    _say("layers full decode", cfg.T, cfg.H, cfg.I, cfg.E, cfg.K)
+    P = Layers(cfg, 2)
+    steps = P.chain()
+    out = P.multi(1)
+    torch.cuda.synchronize()
+    assert np.array_equal(bits(out), bits(steps[-1][2]))
+    _say("  chain == multi-layer call")
+    x_in, lg, last = steps[-1]
+    tokens = np.sort(np.random.default_rng(cfg.seed_act).choice(cfg.T, size=2, replace=False))
+    want = P.oracle_layer(1, x_in, lg, tokens=tokens)
+    got = bits(last)[tokens]
+    e_rel = rel_l2(got, want["out"])
+    e_max = max_abs_elementwise(got, want["out"])
+    _say(f"  last layer: rel_l2 {e_rel:.2e}  max_abs (per element) {e_max:.2e}")
+    assert e_rel <= REL_L2[cfg.act_fmt] and e_max <= MAX_ABS_RMS
