@@ -71,36 +71,44 @@ struct RowLogits {
 };
 
 // One wave routes token t.  g = the shared expert's gate logit (used when
-// shared = 1).
+// shared = 1).  Lane l holds the keys of experts l, l + 64, ..., NPL of
+// them (E <= 64 NPL), sorted descending once; each of the K rounds then
+// takes the wave-wide maximum of the lanes' first keys (the next slot), and
+// the lane that held it shifts its list by one.
+template <int NPL>
 __device__ __forceinline__ void route_token(const RowLogits& src, int t, int E, int K, int shared,
                                             int renormalize, float g, int32_t* __restrict__ ids,
                                             float* __restrict__ weights) {
   const int lane = threadIdx.x & 63;
   const int Kp = K + shared;
 
-  uint64_t key[kMaxPerLane];
+  uint64_t key[NPL];
 #pragma unroll
-  for (int j = 0; j < kMaxPerLane; ++j) {
+  for (int j = 0; j < NPL; ++j) {
     int e = lane + 64 * j;
     key[j] = (e < E) ? route_key(src(t, e), e) : 0ull;    // 0 = never selected
   }
+#pragma unroll
+  for (int i = 1; i < NPL; ++i)                           // insertion network, descending
+#pragma unroll
+    for (int j = i; j > 0; --j) {
+      const uint64_t a = key[j - 1], b = key[j];
+      key[j - 1] = a > b ? a : b;
+      key[j] = a > b ? b : a;
+    }
 
-  // K rounds: the wave-wide best key is the next slot; its owner retires it.
   // Selected values are wave-uniform, so every lane accumulates the
   // renormalised denominator itself, in slot order.
   float lmax = 0.f, den = 0.f, num = 0.f;
   int sel_e = 0;
   for (int k = 0; k < K; ++k) {
-    uint64_t best = 0ull;
-#pragma unroll
-    for (int j = 0; j < kMaxPerLane; ++j) best = key[j] > best ? key[j] : best;
-    best = wave_max_u64(best);
+    const uint64_t best = wave_max_u64(key[0]);
     const int e = (int)(0xFFFFFFFFu - (uint32_t)(best & 0xFFFFFFFFu));
     const float v = key_value(best);
     if ((e & 63) == lane) {
 #pragma unroll
-      for (int j = 0; j < kMaxPerLane; ++j)
-        if (j == (e >> 6)) key[j] = 0ull;
+      for (int j = 0; j + 1 < NPL; ++j) key[j] = key[j + 1];
+      key[NPL - 1] = 0ull;
     }
     if (k == 0) lmax = v;
     const float ek = expf(v - lmax);
@@ -128,14 +136,32 @@ __device__ __forceinline__ void route_token(const RowLogits& src, int t, int E, 
 
 // logits fp32 rows of stride ld; the shared gate logit of token t at
 // gate[t * gate_stride].
+template <int NPL>
 __global__ __launch_bounds__(256) void route_topk_kernel(
     const float* __restrict__ logits, int ld, const float* __restrict__ gate, int gate_stride,
     int T, int E, int K, int shared, int renormalize, int32_t* __restrict__ ids,
     float* __restrict__ weights) {
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= T) return;
-  route_token(RowLogits{logits, ld}, t, E, K, shared, renormalize,
-              shared ? gate[(size_t)t * gate_stride] : 0.f, ids, weights);
+  route_token<NPL>(RowLogits{logits, ld}, t, E, K, shared, renormalize,
+                   shared ? gate[(size_t)t * gate_stride] : 0.f, ids, weights);
+}
+
+// Keys per lane for E experts: 4, 8 or 16.
+hipError_t launch_route_kernel(const float* logits, int ld, const float* gate, int gate_stride,
+                               int T, int E, int K, int shared, int renormalize, int32_t* ids,
+                               float* weights, hipStream_t stream) {
+  dim3 grid((T + 3) / 4), block(256);
+  if (E <= 256)
+    hipLaunchKernelGGL(route_topk_kernel<4>, grid, block, 0, stream, logits, ld, gate,
+                       gate_stride, T, E, K, shared, renormalize, ids, weights);
+  else if (E <= 512)
+    hipLaunchKernelGGL(route_topk_kernel<8>, grid, block, 0, stream, logits, ld, gate,
+                       gate_stride, T, E, K, shared, renormalize, ids, weights);
+  else
+    hipLaunchKernelGGL(route_topk_kernel<kMaxPerLane>, grid, block, 0, stream, logits, ld, gate,
+                       gate_stride, T, E, K, shared, renormalize, ids, weights);
+  return hipGetLastError();
 }
 
 // The router GEMM's S partial sums P[s] (fp32 [S, n]) added in split order
@@ -162,10 +188,8 @@ __global__ __launch_bounds__(256) void sum_splits_kernel(const float* __restrict
 hipError_t launch_route_topk(const float* logits, const float* gate, int T, int E, int K,
                              int shared, int renormalize, int32_t* ids, float* weights,
                              hipStream_t stream) {
-  dim3 grid((T + 3) / 4), block(256);
-  hipLaunchKernelGGL(route_topk_kernel, grid, block, 0, stream, logits, E, gate, 1, T, E, K, shared,
-                     renormalize, ids, weights);
-  return hipGetLastError();
+  return launch_route_kernel(logits, E, gate, 1, T, E, K, shared, renormalize, ids, weights,
+                             stream);
 }
 
 int route_max_splits() { return kMaxSplits; }
@@ -179,8 +203,6 @@ hipError_t launch_route_topk_split(const float* partial, int S, int T, int E, in
                      partial, S, n, logits);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  dim3 grid((T + 3) / 4), block(256);
-  hipLaunchKernelGGL(route_topk_kernel, grid, block, 0, stream, logits, Ep, logits + E, Ep, T, E,
-                     K, shared, renormalize, ids, weights);
-  return hipGetLastError();
+  return launch_route_kernel(logits, Ep, logits + E, Ep, T, E, K, shared, renormalize, ids,
+                             weights, stream);
 }
