@@ -82,10 +82,14 @@ unsigned tile_slice_grid(int max_tiles, int nslices) {
 // reduction length whose scales fit the LDS left over by the stages (256
 // weight rows x KMAX/32 bytes, plus the tile's activation rows for MXFP4).
 // Totals: bf16 128-row 160 KiB (one workgroup per CU), bf16 64-row 80 KiB
-// (two per CU), MXFP4 128-row 128 KiB, MXFP4 64-row 76 KiB (two per CU).
+// (two per CU), MXFP4 256-row 145 KiB (three stages), MXFP4 128-row
+// 128 KiB, MXFP4 64-row 76 KiB (two per CU).  256-row tiles exist for MXFP4
+// activations only: an expert of the W4A4 batch (~143 rows) then streams its
+// weights once instead of once per 128-row tile.
 template <int BM, bool kFP4A>
 struct TileCfg {
-  static constexpr int NS = (BM == 64 && !kFP4A) ? 3 : 4;
+  static_assert(BM == 64 || BM == 128 || (BM == 256 && kFP4A), "tile sizes");
+  static constexpr int NS = ((BM == 64 && !kFP4A) || BM == 256) ? 3 : 4;
   static constexpr int KMAX = kFP4A ? (BM == 128 ? 8192 : 6144) : 4096;
   static constexpr int SCB = 256 * (KMAX / 32);             // weight scales
   // MXFP4 activation scales of the tile's rows (whole K), BM/4 rows per wave
@@ -371,11 +375,17 @@ struct IntC {
 
 // Calls f(IntC<NMT>) with the number of 16-row sub-tiles the MFMAs cover:
 // the live ones (ceil(rows / 16)), rounded up to an even count for 128-row
-// tiles (four code variants per kernel instead of eight).
+// tiles and to a multiple of four for 256-row tiles (four code variants per
+// kernel).
 template <int BM, class F>
 __device__ __forceinline__ void with_nmt(int rows, F&& f) {
   const int need = (rows + 15) >> 4;
-  if constexpr (BM == 128) {
+  if constexpr (BM == 256) {
+    if (need > 12) f(IntC<16>());
+    else if (need > 8) f(IntC<12>());
+    else if (need > 4) f(IntC<8>());
+    else f(IntC<4>());
+  } else if constexpr (BM == 128) {
     if (need > 6) f(IntC<8>());
     else if (need > 4) f(IntC<6>());
     else if (need > 2) f(IntC<4>());
@@ -399,12 +409,17 @@ __device__ __forceinline__ void with_lds(Body&& body) {
   __shared__ __align__(16) uint8_t st0[XB];
   __shared__ __align__(16) uint8_t st1[XB];
   __shared__ __align__(16) uint8_t st2[XB];
-  if constexpr (kFP4A) {
-    static_assert(TileCfg<BM, kFP4A>::NS == 4, "four stages");
+  if constexpr (kFP4A && TileCfg<BM, kFP4A>::NS == 4) {
     __shared__ __align__(16) uint8_t st3[XB];
     __shared__ __align__(16) uint8_t asc[TileCfg<BM, kFP4A>::ASB];
     __shared__ int32_t srow[BM];
     uint8_t* const stages[4] = {st0, st1, st2, st3};
+    body(stages, sc, asc, srow);
+  } else if constexpr (kFP4A) {
+    static_assert(TileCfg<BM, kFP4A>::NS == 3, "three or four stages");
+    __shared__ __align__(16) uint8_t asc[TileCfg<BM, kFP4A>::ASB];
+    __shared__ int32_t srow[BM];
+    uint8_t* const stages[3] = {st0, st1, st2};
     body(stages, sc, asc, srow);
   } else if constexpr (TileCfg<BM, kFP4A>::NS == 4) {
     __shared__ __align__(16) uint8_t st3[XB];
@@ -582,6 +597,7 @@ bool expert_gemm_tiled_supported(int tile_m, int act_fmt, int H, int I) {
   if (H % 256 || I % 128 || H <= 0 || I <= 0) return false;
   if (tile_m == 64) return act_fmt ? fits<64, true>(H, I) : fits<64, false>(H, I);
   if (tile_m == 128) return act_fmt ? fits<128, true>(H, I) : fits<128, false>(H, I);
+  if (tile_m == 256) return act_fmt && fits<256, true>(H, I);
   return false;
 }
 
@@ -590,6 +606,9 @@ hipError_t launch_gate_up_tiled(int tile_m, int act_fmt, const void* act, const 
                                 const int32_t* tiles, const int32_t* num_tiles, int max_tiles,
                                 const uint8_t* w13, const uint8_t* w13s, int T, int H, int I,
                                 int Kp, uint16_t* h, hipStream_t stream) {
+  if (tile_m == 256 && act_fmt)
+    return launch_gate_up_bm<256, true>(act, act_scale, sorted, offsets, tiles, num_tiles,
+                                        max_tiles, w13, w13s, T, H, I, Kp, h, stream);
   if (tile_m == 128)
     return act_fmt ? launch_gate_up_bm<128, true>(act, act_scale, sorted, offsets, tiles,
                                                    num_tiles, max_tiles, w13, w13s, T, H, I, Kp,
@@ -608,6 +627,9 @@ hipError_t launch_down_tiled(int tile_m, int act_fmt, const void* h, const uint8
                              const int32_t* num_tiles, int max_tiles, const uint8_t* w2,
                              const uint8_t* w2s, int A, int H, int I, uint16_t* y,
                              hipStream_t stream) {
+  if (tile_m == 256 && act_fmt)
+    return launch_down_bm<256, true>(h, h_scale, offsets, tiles, num_tiles, max_tiles, w2, w2s, A,
+                                     H, I, y, stream);
   if (tile_m == 128)
     return act_fmt ? launch_down_bm<128, true>(h, h_scale, offsets, tiles, num_tiles, max_tiles,
                                                 w2, w2s, A, H, I, y, stream)

@@ -29,6 +29,10 @@ int choose_tile_m(int64_t A, int64_t Ep, int H, int I, int act_fmt, int wfmt = 0
   if (wfmt == 1) return MOE_TILE_M;
   const int64_t avg = A / Ep;
   if (avg <= 8) return MOE_TILE_M;
+  // MXFP4 activations: groups above 128 rows take 256-row tiles (one weight
+  // pass per expert instead of two)
+  if (act_fmt == MOE_ACT_MXFP4 && avg > 128 && expert_gemm_tiled_supported(256, act_fmt, H, I))
+    return 256;
   const int tm = avg <= 48 ? 64 : 128;
   return expert_gemm_tiled_supported(tm, act_fmt, H, I) ? tm : MOE_TILE_M;
 }

@@ -321,11 +321,14 @@ def test_forward_capturable_in_hip_graph():
         torch.cuda.synchronize()
 
 
-@pytest.mark.parametrize("tile_m", [32, 64, 128])
-@pytest.mark.parametrize("act", [synth.ACT_BF16, synth.ACT_MXFP4])
+@pytest.mark.parametrize("tile_m,act", [(32, synth.ACT_BF16), (64, synth.ACT_BF16),
+                                         (128, synth.ACT_BF16), (32, synth.ACT_MXFP4),
+                                         (64, synth.ACT_MXFP4), (128, synth.ACT_MXFP4),
+                                         (256, synth.ACT_MXFP4)])
 def test_gemm_kernels_for_every_tile_size(tile_m, act):
     """The staged entry points with each tile size (weight-streaming 32-row
-    tiles, LDS-tiled 64- and 128-row tiles) against the oracle."""
+    tiles, LDS-tiled 64-, 128- and, for MXFP4 activations, 256-row tiles)
+    against the oracle."""
     cfg = synth.custom_config("tiles", T=150, H=512, I=256, E=8, K=3, shared=1, act_fmt=act,
                               outlier_p=0.002 if act else 0.0)
     _say("tile_m", tile_m, "act", act)
