@@ -99,8 +99,9 @@ def algorithmic(cfg, counts):
 def gate_up_kernel_name(cfg, tile_m):
     """The gate/up kernel's name as rocprofv3 reports it for this shape."""
     a = "true" if cfg.act_fmt else "false"
+    w8 = "true" if cfg.wfmt == synth.W_MXFP8 else "false"
     if tile_m != 32:
-        return f"gate_up_tiled_kernel<{tile_m}, {a}>"
+        return f"gate_up_tiled_kernel<{tile_m}, {a}, {w8}>"
     if cfg.wfmt == synth.W_MXFP8:
         return "gate_up_kernel<1, false, true>"
     ph = 2 if (cfg.H // 128) % 2 == 0 else 1          # phase width of the 32-row kernel
@@ -348,7 +349,8 @@ def main():
         alg["layer_bytes"] += cfg.Ep * cfg.H * 2 - cfg.T * cfg.E * 4 - cfg.T * 4 * cfg.shared
         alg["flops"] += 2 * cfg.T * cfg.Ep * cfg.H
     from mxfp4_routed_expert_top_amd import profiling
-    tile_m = 32 if w8 else ops.gemm_tile_m(cfg.T, cfg.Kp, cfg.Ep, cfg.H, cfg.I, cfg.act_fmt)
+    tile_m = (ops.mxfp8_gemm_tile_m(cfg.T, cfg.Kp, cfg.Ep, cfg.H, cfg.I) if w8 else
+              ops.gemm_tile_m(cfg.T, cfg.Kp, cfg.Ep, cfg.H, cfg.I, cfg.act_fmt))
     kname = gate_up_kernel_name(cfg, tile_m)
     gu_s = stage_ms["gate_up"] / 1e3
     mfma_peak = BF16_PEAK_TFLOPS if cfg.act_fmt == 0 else MXFP4_PEAK_TFLOPS

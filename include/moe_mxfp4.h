@@ -256,13 +256,15 @@ MOE_API moe_status moe_mxfp8_quantize(const void *src, int32_t src_dtype, int64_
 /*
  * Grouped gate/up GEMM + SwiGLU over MXFP8 weights, bf16 activations
  * (W8A16): as moe_expert_gate_up with act_fmt = MOE_ACT_BF16, the weights
- * dequantised to bf16 in registers by the scaled FP8 converter.  Runs on
- * 32-row tiles only: tile_m must be 32 (the tile table from moe_align_sort
- * with tile_m = 32).
+ * dequantised to bf16 in registers by the scaled FP8 converter.  tile_m 32
+ * (weight-streaming kernel) or 64 / 128 (LDS-tiled kernel; H a multiple of
+ * 256, H and I at most 4096); the tile table from moe_align_sort with the
+ * same tile_m.
  *   x          bf16 [T, H];  w13 uint8 [E', 2I, H], w13_scale uint8 [E', 2I, H/32]
  *   h          out bf16 [T*Kp, I] in sorted row order
- * Errors: INVALID_ARGUMENT, UNSUPPORTED (H or I not a multiple of 128,
- * tile_m != 32, an expert's 2I x H code bytes above 2^32).
+ * Errors: INVALID_ARGUMENT, UNSUPPORTED (H or I not a multiple of 128, a
+ * tile_m / shape the kernels do not cover, an expert's 2I x H code bytes
+ * above 2^32).
  */
 MOE_API moe_status moe_mxfp8_expert_gate_up(const uint16_t *x, const int32_t *sorted_assign,
                                     const int32_t *expert_offsets, const int32_t *tile_table,
@@ -272,7 +274,7 @@ MOE_API moe_status moe_mxfp8_expert_gate_up(const uint16_t *x, const int32_t *so
 
 /*
  * Grouped down GEMM over MXFP8 weights (W8A16): as moe_expert_down with
- * act_fmt = MOE_ACT_BF16; tile_m must be 32.
+ * act_fmt = MOE_ACT_BF16; tile_m as for moe_mxfp8_expert_gate_up.
  *   h          bf16 [T*Kp, I];  w2 uint8 [E', H, I], w2_scale uint8 [E', H, I/32]
  *   y          out bf16 [T*Kp, H], sorted row order
  * Errors: as moe_mxfp8_expert_gate_up.
@@ -374,13 +376,17 @@ MOE_API moe_status moe_mxfp4_forward_layers(const uint16_t *x, int32_t L,
                                             int32_t act_fmt, int32_t prefetch, uint16_t *out,
                                             void *workspace, size_t workspace_bytes, void *stream);
 
+/* The tile_m moe_mxfp8_forward uses for these shapes: 32, 64 or 128, by the
+ * rule of moe_mxfp4_forward with bf16 activations. */
+MOE_API int32_t moe_mxfp8_gemm_tile_m(int32_t T, int32_t Kp, int32_t Ep, int32_t H, int32_t I);
+
 /* Workspace bytes moe_mxfp8_forward needs (0 for T = 0). */
 MOE_API size_t moe_mxfp8_workspace_size(int32_t T, int32_t H, int32_t I, int32_t E, int32_t K,
                                 int32_t shared);
 
 /*
  * The whole layer over MXFP8 expert weights with bf16 activations (W8A16):
- * route, align (32-row tiles), gate/up + SwiGLU, down, combine, enqueued on
+ * route, align (moe_mxfp8_gemm_tile_m), gate/up + SwiGLU, down, combine, enqueued on
  * `stream`.  Arguments, outputs and errors as moe_mxfp4_forward with
  * act_fmt = MOE_ACT_BF16, except the weights (MXFP8 layout above) and the
  * workspace (moe_mxfp8_workspace_size bytes); UNSUPPORTED also when an

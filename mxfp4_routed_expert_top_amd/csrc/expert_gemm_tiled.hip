@@ -86,10 +86,13 @@ unsigned tile_slice_grid(int max_tiles, int nslices) {
 // 128 KiB, MXFP4 64-row 76 KiB (two per CU).  256-row tiles exist for MXFP4
 // activations only: an expert of the W4A4 batch (~143 rows) then streams its
 // weights once instead of once per 128-row tile.
-template <int BM, bool kFP4A>
+template <int BM, bool kFP4A, bool kW8 = false>
 struct TileCfg {
   static_assert(BM == 64 || BM == 128 || (BM == 256 && kFP4A), "tile sizes");
-  static constexpr int NS = ((BM == 64 && !kFP4A) || BM == 256) ? 3 : 4;
+  static_assert(!(kW8 && kFP4A), "MXFP8 weights take bf16 activations");
+  // (MXFP8 weights: twice the weight registers per stage, so 128-row tiles
+  // keep three stages in flight instead of four)
+  static constexpr int NS = ((BM == 64 && !kFP4A) || BM == 256 || (kW8 && BM == 128)) ? 3 : 4;
   static constexpr int KMAX = kFP4A ? (BM == 128 ? 8192 : 6144) : 4096;
   static constexpr int SCB = 256 * (KMAX / 32);             // weight scales
   // MXFP4 activation scales of the tile's rows (whole K), BM/4 rows per wave
@@ -152,13 +155,15 @@ __device__ __forceinline__ void load_to_lds4(rsrc_t r, uint32_t voff, uint32_t s
 // past the last chunk use an out-of-range offset: they move no data and
 // every wave issues the same number of loads per stage, so the wait counts
 // are constants.  MFMAs run only on the tile's live 16-row sub-tiles.
-template <int BM, bool kFP4A>
+template <int BM, bool kFP4A, bool kW8 = false>
 struct TiledGemm {
-  static constexpr int NS = TileCfg<BM, kFP4A>::NS;
-  static constexpr int XB = TileCfg<BM, kFP4A>::XB;
+  static constexpr int NS = TileCfg<BM, kFP4A, kW8>::NS;
+  static constexpr int XB = TileCfg<BM, kFP4A, kW8>::XB;
   static constexpr int MT = BM / 16;
   static constexpr int XI = kFP4A ? BM / 64 : BM / 16;   // code / row loads per wave per stage
-  static constexpr int LPS = XI + 4;                       // vmem ops per wave per stage
+  // weight registers per strip and stage: 16 bytes (32 E2M1 codes) or 32 (32 E4M3 codes)
+  static constexpr int NQ = kW8 ? 2 : 1;
+  static constexpr int LPS = XI + 4 * NQ;                  // vmem ops per wave per stage
 
   rsrc_t w, ws, a, as;
   uint32_t wo[4];               // lane's weight row offsets (+16 g)
@@ -198,8 +203,9 @@ struct TiledGemm {
     return 4 * ((row / RW) * per * 64 + (row % RW) * Q + (c ^ scale_swizzle(row, Q))) + g;
   }
 
-  // Issue chunk c into a stage (weight codes into registers q).
-  __device__ __forceinline__ void issue(uint8_t* base, int c, u32x4_t (&q)[4]) const {
+  // Issue chunk c into a stage (weight codes into registers q: strip t's
+  // 16-byte pieces at q[NQ t .. NQ t + NQ)).
+  __device__ __forceinline__ void issue(uint8_t* base, int c, u32x4_t (&q)[4 * NQ]) const {
     const bool ok = c < nch;
     const uint32_t oor = ok ? 0u : kOOR;
     const uint32_t cc = ok ? (uint32_t)c : 0u;
@@ -213,13 +219,15 @@ struct TiledGemm {
         load_to_lds16(a, xo[i] | oor, 256 * cc, base + (wave * XI + i) * 1024);
     }
 #pragma unroll
-    for (int t = 0; t < 4; ++t) q[t] = bload16(w, wo[t] | oor, 64 * cc);
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+      for (int hq = 0; hq < NQ; ++hq) q[NQ * t + hq] = bload16(w, wo[t] | oor, 64 * NQ * cc + 16 * hq);
   }
 
   // MFMAs of one chunk on the first NMT 16-row sub-tiles (the live ones).
   template <int NMT>
   __device__ __forceinline__ void compute(const uint8_t* x, const uint8_t* sc, const uint8_t* asc,
-                                          int c, const u32x4_t (&q)[4],
+                                          int c, const u32x4_t (&q)[4 * NQ],
                                           floatx4_t (&acc)[MT][4]) const {
     uint32_t s[4];
     const uint32_t so = sro + 4 * (uint32_t)(c ^ swz);
@@ -251,7 +259,7 @@ struct TiledGemm {
 #pragma unroll
       for (int mt = 0; mt < NMT; ++mt) av[0][mt] = a_frag(x, mt, 0);
 #pragma unroll
-      for (int t = 0; t < 4; ++t) bv[0][t] = dequant8_bf16(q[t][0], scf[t]);
+      for (int t = 0; t < 4; ++t) bv[0][t] = wfrag(q, t, 0, scf[t]);
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
@@ -260,7 +268,7 @@ struct TiledGemm {
 #pragma unroll
           for (int mt = 0; mt < NMT; ++mt) av[nxt][mt] = a_frag(x, mt, j + 1);
 #pragma unroll
-          for (int t = 0; t < 4; ++t) bv[nxt][t] = dequant8_bf16(q[t][j + 1], scf[t]);
+          for (int t = 0; t < 4; ++t) bv[nxt][t] = wfrag(q, t, j + 1, scf[t]);
         }
 #pragma unroll
         for (int mt = 0; mt < NMT; ++mt)
@@ -286,6 +294,18 @@ struct TiledGemm {
     }
   }
 
+  // bf16 B operand of strip t, K-step j: the lane's 8 weights of the step
+  // (MXFP4: dword j of its 16 bytes; MXFP8: bytes 8 j .. 8 j + 7 of its 32).
+  __device__ __forceinline__ static bf16x8_t wfrag(const u32x4_t (&q)[4 * NQ], int t, int j,
+                                                   float sc) {
+    if constexpr (kW8) {
+      const u32x4_t& d = q[2 * t + (j >> 1)];
+      return dequant8_bf16_fp8(d[2 * (j & 1)], d[2 * (j & 1) + 1], sc);
+    } else {
+      return dequant8_bf16(q[t][j], sc);
+    }
+  }
+
   // bf16 A operand: rows 16 mt + (lane % 16), K-step j of the lane's K-group.
   __device__ __forceinline__ bf16x8_t a_frag(const uint8_t* x, int mt, int j) const {
     const int r = 16 * mt + nl;
@@ -300,7 +320,7 @@ struct TiledGemm {
   template <int NMT, class WRow, class ARow>
   __device__ __forceinline__ void run(uint8_t* const (&stages)[NS], uint8_t* sc, uint8_t* asc,
                                       WRow wrow, ARow arow, floatx4_t (&acc)[MT][4]) const {
-    u32x4_t q[NS][4];
+    u32x4_t q[NS][4 * NQ];
     stage_rows<64>(sc, ws, wrow);
     if constexpr (kFP4A) stage_rows<BM / 4>(asc, as, arow);
 #pragma unroll
@@ -330,8 +350,8 @@ __device__ __forceinline__ TileT tile_of(const int32_t* tiles, const int32_t* of
 
 // The lane's activation source offsets for every stage: row r of the tile
 // comes from source row src(r) (a token for gate/up, a sorted row for down).
-template <int BM, bool kFP4A, class SrcFn>
-__device__ __forceinline__ void plan_x(TiledGemm<BM, kFP4A>& G, const TileT& ti, SrcFn src,
+template <int BM, bool kFP4A, bool kW8, class SrcFn>
+__device__ __forceinline__ void plan_x(TiledGemm<BM, kFP4A, kW8>& G, const TileT& ti, SrcFn src,
                                        uint32_t row_bytes) {
 #pragma unroll
   for (int i = 0; i < G.XI; ++i) {
@@ -352,8 +372,8 @@ __device__ __forceinline__ void plan_x(TiledGemm<BM, kFP4A>& G, const TileT& ti,
 
 // Common set-up of a workgroup's GEMM state (weights of one expert slice;
 // K = reduction length; rs = K/32 scale bytes per weight row).
-template <int BM, bool kFP4A>
-__device__ __forceinline__ void setup(TiledGemm<BM, kFP4A>& G, const TileT& ti, int K,
+template <int BM, bool kFP4A, bool kW8>
+__device__ __forceinline__ void setup(TiledGemm<BM, kFP4A, kW8>& G, const TileT& ti, int K,
                                       const uint8_t* wq, const uint8_t* wsc, int wrows) {
   G.lane = threadIdx.x & 63;
   G.wave = threadIdx.x >> 6;
@@ -363,7 +383,7 @@ __device__ __forceinline__ void setup(TiledGemm<BM, kFP4A>& G, const TileT& ti, 
   G.Q = K / 128;
   G.swz = scale_swizzle(G.nl, G.Q);
   G.sro = 4 * (64 * G.wave + G.nl) * G.Q + G.g;
-  const size_t wbytes = (size_t)wrows * (K / 2), sbytes = (size_t)wrows * (K / 32);
+  const size_t wbytes = (size_t)wrows * (kW8 ? K : K / 2), sbytes = (size_t)wrows * (K / 32);
   G.w = make_rsrc(wq + ti.expert * wbytes, (uint32_t)wbytes);
   G.ws = make_rsrc(wsc + ti.expert * sbytes, (uint32_t)sbytes);
 }
@@ -402,31 +422,31 @@ __device__ __forceinline__ void with_nmt(int rows, F&& f) {
 // Static LDS of a kernel: NS stage arrays (separate objects), the weight
 // scales, and for MXFP4 activations their scales and the tile's source
 // rows; body(stages, scales, act_scales, src_rows) runs with them.
-template <int BM, bool kFP4A, class Body>
+template <int BM, bool kFP4A, bool kW8, class Body>
 __device__ __forceinline__ void with_lds(Body&& body) {
-  constexpr int XB = TileCfg<BM, kFP4A>::XB, SCB = TileCfg<BM, kFP4A>::SCB;
+  constexpr int XB = TileCfg<BM, kFP4A, kW8>::XB, SCB = TileCfg<BM, kFP4A, kW8>::SCB;
   __shared__ __align__(16) uint8_t sc[SCB];
   __shared__ __align__(16) uint8_t st0[XB];
   __shared__ __align__(16) uint8_t st1[XB];
   __shared__ __align__(16) uint8_t st2[XB];
-  if constexpr (kFP4A && TileCfg<BM, kFP4A>::NS == 4) {
+  if constexpr (kFP4A && TileCfg<BM, kFP4A, kW8>::NS == 4) {
     __shared__ __align__(16) uint8_t st3[XB];
-    __shared__ __align__(16) uint8_t asc[TileCfg<BM, kFP4A>::ASB];
+    __shared__ __align__(16) uint8_t asc[TileCfg<BM, kFP4A, kW8>::ASB];
     __shared__ int32_t srow[BM];
     uint8_t* const stages[4] = {st0, st1, st2, st3};
     body(stages, sc, asc, srow);
   } else if constexpr (kFP4A) {
-    static_assert(TileCfg<BM, kFP4A>::NS == 3, "three or four stages");
-    __shared__ __align__(16) uint8_t asc[TileCfg<BM, kFP4A>::ASB];
+    static_assert(TileCfg<BM, kFP4A, kW8>::NS == 3, "three or four stages");
+    __shared__ __align__(16) uint8_t asc[TileCfg<BM, kFP4A, kW8>::ASB];
     __shared__ int32_t srow[BM];
     uint8_t* const stages[3] = {st0, st1, st2};
     body(stages, sc, asc, srow);
-  } else if constexpr (TileCfg<BM, kFP4A>::NS == 4) {
+  } else if constexpr (TileCfg<BM, kFP4A, kW8>::NS == 4) {
     __shared__ __align__(16) uint8_t st3[XB];
     uint8_t* const stages[4] = {st0, st1, st2, st3};
     body(stages, sc, (uint8_t*)nullptr, (int32_t*)nullptr);
   } else {
-    static_assert(TileCfg<BM, kFP4A>::NS == 3, "three or four stages");
+    static_assert(TileCfg<BM, kFP4A, kW8>::NS == 3, "three or four stages");
     uint8_t* const stages[3] = {st0, st1, st2};
     body(stages, sc, (uint8_t*)nullptr, (int32_t*)nullptr);
   }
@@ -436,16 +456,16 @@ __device__ __forceinline__ void with_lds(Body&& body) {
 // activation-code offsets and the activation-scale rows), then the pipeline.
 // direct(r) = source row of tile row r < rows; wrow(r) = byte offset of
 // weight scale row r; arow_bytes = activation scale bytes per source row.
-template <int BM, bool kFP4A, class Direct, class WRow>
-__device__ __forceinline__ void tile_loop(TiledGemm<BM, kFP4A>& G, const TileT& ti, Direct direct,
+template <int BM, bool kFP4A, bool kW8, class Direct, class WRow>
+__device__ __forceinline__ void tile_loop(TiledGemm<BM, kFP4A, kW8>& G, const TileT& ti, Direct direct,
                                           WRow wrow, uint32_t row_bytes, uint32_t arow_bytes,
                                           floatx4_t (&acc)[BM / 16][4]) {
-  with_lds<BM, kFP4A>([&](auto& stages, uint8_t* sc, uint8_t* asc, int32_t* srow) {
+  with_lds<BM, kFP4A, kW8>([&](auto& stages, uint8_t* sc, uint8_t* asc, int32_t* srow) {
     if constexpr (kFP4A) {
       const int t = threadIdx.x;
       if (t < BM) srow[t] = t < ti.rows ? (int32_t)direct(t) : 0;
       __syncthreads();
-      plan_x<BM, kFP4A>(G, ti, [&](int r) { return (uint32_t)srow[r]; }, row_bytes);
+      plan_x<BM, kFP4A, kW8>(G, ti, [&](int r) { return (uint32_t)srow[r]; }, row_bytes);
       auto arow = [&](int r) -> uint32_t {
         return r < ti.rows ? (uint32_t)srow[r] * arow_bytes : kOOR;
       };
@@ -453,7 +473,7 @@ __device__ __forceinline__ void tile_loop(TiledGemm<BM, kFP4A>& G, const TileT& 
         G.template run<decltype(n)::value>(stages, sc, asc, wrow, arow, acc);
       });
     } else {
-      plan_x<BM, kFP4A>(G, ti, direct, row_bytes);
+      plan_x<BM, kFP4A, kW8>(G, ti, direct, row_bytes);
       auto arow = [](int) -> uint32_t { return kOOR; };
       with_nmt<BM>(ti.rows, [&](auto n) {
         G.template run<decltype(n)::value>(stages, sc, asc, wrow, arow, acc);
@@ -464,7 +484,7 @@ __device__ __forceinline__ void tile_loop(TiledGemm<BM, kFP4A>& G, const TileT& 
 
 // gate/up + SwiGLU: weight rows gate [i0, i0 + 128) and up [I + i0, I + i0 + 128),
 // i0 = 128 s; wave w owns i in [i0 + 32 w, i0 + 32 w + 32): strips gate lo/hi, up lo/hi.
-template <int BM, bool kFP4A>
+template <int BM, bool kFP4A, bool kW8>
 __global__ __launch_bounds__(256) void gate_up_tiled_kernel(
     const void* __restrict__ act, const uint8_t* __restrict__ act_scale,
     const int32_t* __restrict__ sorted, const int32_t* __restrict__ offsets,
@@ -474,14 +494,15 @@ __global__ __launch_bounds__(256) void gate_up_tiled_kernel(
   int tile, s;
   if (!tile_slice<kFP4A>(blockIdx.x, *num_tiles, I / 128, &tile, &s)) return;
   const TileT ti = tile_of<BM>(tiles, offsets, tile);
-  TiledGemm<BM, kFP4A> G;
+  TiledGemm<BM, kFP4A, kW8> G;
   setup(G, ti, H, w13, w13s, 2 * I);
   const int nl = G.nl, g = G.g;
   const uint32_t rb = H / 2, rs = H / 32;
+  const uint32_t wrb = kW8 ? H : H / 2;                    // weight code bytes per row
   const int i0 = s * 128 + G.wave * 32;
   const int rows4[4] = {i0 + nl, i0 + 16 + nl, I + i0 + nl, I + i0 + 16 + nl};
 #pragma unroll
-  for (int st = 0; st < 4; ++st) G.wo[st] = rows4[st] * rb + 16 * g;
+  for (int st = 0; st < 4; ++st) G.wo[st] = rows4[st] * wrb + 16 * G.NQ * g;
   if (kFP4A) {
     G.a = make_rsrc(act, (uint32_t)((size_t)T * rb));
     G.as = make_rsrc(act_scale, (uint32_t)((size_t)T * rs));
@@ -502,7 +523,7 @@ __global__ __launch_bounds__(256) void gate_up_tiled_kernel(
   for (int mt = 0; mt < BM / 16; ++mt)
 #pragma unroll
     for (int st = 0; st < 4; ++st) acc[mt][st] = (floatx4_t){0.f, 0.f, 0.f, 0.f};
-  tile_loop<BM, kFP4A>(G, ti, token, wrow, kFP4A ? rb : (uint32_t)H * 2, rs, acc);
+  tile_loop<BM, kFP4A, kW8>(G, ti, token, wrow, kFP4A ? rb : (uint32_t)H * 2, rs, acc);
 
 #pragma unroll
   for (int mt = 0; mt < BM / 16; ++mt)
@@ -518,7 +539,7 @@ __global__ __launch_bounds__(256) void gate_up_tiled_kernel(
 }
 
 // down: weight rows j in [256 s, 256 s + 256); wave w owns [256 s + 64 w, +64).
-template <int BM, bool kFP4A>
+template <int BM, bool kFP4A, bool kW8>
 __global__ __launch_bounds__(256) void down_tiled_kernel(
     const void* __restrict__ hin, const uint8_t* __restrict__ hscale,
     const int32_t* __restrict__ offsets, const int32_t* __restrict__ tiles,
@@ -527,13 +548,14 @@ __global__ __launch_bounds__(256) void down_tiled_kernel(
   int tile, s;
   if (!tile_slice<kFP4A>(blockIdx.x, *num_tiles, H / 256, &tile, &s)) return;
   const TileT ti = tile_of<BM>(tiles, offsets, tile);
-  TiledGemm<BM, kFP4A> G;
+  TiledGemm<BM, kFP4A, kW8> G;
   setup(G, ti, I, w2, w2s, H);
   const int nl = G.nl, g = G.g;
   const uint32_t rb = I / 2, rs = I / 32;
+  const uint32_t wrb = kW8 ? I : I / 2;                    // weight code bytes per row
   const int j0 = s * 256 + G.wave * 64;
 #pragma unroll
-  for (int st = 0; st < 4; ++st) G.wo[st] = (j0 + 16 * st + nl) * rb + 16 * g;
+  for (int st = 0; st < 4; ++st) G.wo[st] = (j0 + 16 * st + nl) * wrb + 16 * G.NQ * g;
   if (kFP4A) {
     G.a = make_rsrc(hin, (uint32_t)((size_t)A * rb));
     G.as = make_rsrc(hscale, (uint32_t)((size_t)A * rs));
@@ -548,7 +570,7 @@ __global__ __launch_bounds__(256) void down_tiled_kernel(
   for (int mt = 0; mt < BM / 16; ++mt)
 #pragma unroll
     for (int st = 0; st < 4; ++st) acc[mt][st] = (floatx4_t){0.f, 0.f, 0.f, 0.f};
-  tile_loop<BM, kFP4A>(G, ti, srow, wrow, kFP4A ? rb : (uint32_t)I * 2, rs, acc);
+  tile_loop<BM, kFP4A, kW8>(G, ti, srow, wrow, kFP4A ? rb : (uint32_t)I * 2, rs, acc);
 
 #pragma unroll
   for (int mt = 0; mt < BM / 16; ++mt)
@@ -563,49 +585,61 @@ __global__ __launch_bounds__(256) void down_tiled_kernel(
     }
 }
 
-template <int BM, bool kFP4A>
+template <int BM, bool kFP4A, bool kW8 = false>
 hipError_t launch_gate_up_bm(const void* act, const uint8_t* act_scale, const int32_t* sorted,
                              const int32_t* offsets, const int32_t* tiles,
                              const int32_t* num_tiles, int max_tiles, const uint8_t* w13,
                              const uint8_t* w13s, int T, int H, int I, int Kp, uint16_t* h,
                              hipStream_t stream) {
   const unsigned grid = tile_slice_grid<kFP4A>(max_tiles, I / 128);
-  hipLaunchKernelGGL((gate_up_tiled_kernel<BM, kFP4A>), dim3(grid), dim3(256), 0, stream, act,
+  hipLaunchKernelGGL((gate_up_tiled_kernel<BM, kFP4A, kW8>), dim3(grid), dim3(256), 0, stream, act,
                      act_scale, sorted, offsets, tiles, num_tiles, w13, w13s, T, H, I, Kp, h);
   return hipGetLastError();
 }
 
-template <int BM, bool kFP4A>
+template <int BM, bool kFP4A, bool kW8 = false>
 hipError_t launch_down_bm(const void* h, const uint8_t* h_scale, const int32_t* offsets,
                           const int32_t* tiles, const int32_t* num_tiles, int max_tiles,
                           const uint8_t* w2, const uint8_t* w2s, int A, int H, int I, uint16_t* y,
                           hipStream_t stream) {
   const unsigned grid = tile_slice_grid<kFP4A>(max_tiles, H / 256);
-  hipLaunchKernelGGL((down_tiled_kernel<BM, kFP4A>), dim3(grid), dim3(256), 0, stream, h,
+  hipLaunchKernelGGL((down_tiled_kernel<BM, kFP4A, kW8>), dim3(grid), dim3(256), 0, stream, h,
                      h_scale, offsets, tiles, num_tiles, w2, w2s, A, H, I, y);
   return hipGetLastError();
 }
 
-template <int BM, bool kFP4A>
+template <int BM, bool kFP4A, bool kW8 = false>
 bool fits(int H, int I) {
-  return H <= TileCfg<BM, kFP4A>::KMAX && I <= TileCfg<BM, kFP4A>::KMAX;
+  return H <= TileCfg<BM, kFP4A, kW8>::KMAX && I <= TileCfg<BM, kFP4A, kW8>::KMAX;
 }
 
 }  // namespace
 
-bool expert_gemm_tiled_supported(int tile_m, int act_fmt, int H, int I) {
+bool expert_gemm_tiled_supported(int tile_m, int act_fmt, int H, int I, int wfmt) {
   if (H % 256 || I % 128 || H <= 0 || I <= 0) return false;
+  if (wfmt == 1) {                 // MXFP8 weights, bf16 activations: 64- and 128-row tiles
+    if (act_fmt) return false;
+    return tile_m == 64 ? fits<64, false, true>(H, I) : tile_m == 128 && fits<128, false, true>(H, I);
+  }
   if (tile_m == 64) return act_fmt ? fits<64, true>(H, I) : fits<64, false>(H, I);
   if (tile_m == 128) return act_fmt ? fits<128, true>(H, I) : fits<128, false>(H, I);
   if (tile_m == 256) return act_fmt && fits<256, true>(H, I);
   return false;
 }
 
-hipError_t launch_gate_up_tiled(int tile_m, int act_fmt, const void* act, const uint8_t* act_scale,
+hipError_t launch_gate_up_tiled(int tile_m, int act_fmt, int wfmt, const void* act,
+                                const uint8_t* act_scale,
                                 const int32_t* sorted, const int32_t* offsets,
                                 const int32_t* tiles, const int32_t* num_tiles, int max_tiles,
                                 const uint8_t* w13, const uint8_t* w13s, int T, int H, int I,
                                 int Kp, uint16_t* h, hipStream_t stream) {
+  if (wfmt == 1)
+    return tile_m == 128 ? launch_gate_up_bm<128, false, true>(act, act_scale, sorted, offsets, tiles,
+                                                               num_tiles, max_tiles, w13, w13s, T,
+                                                               H, I, Kp, h, stream)
+                         : launch_gate_up_bm<64, false, true>(act, act_scale, sorted, offsets, tiles,
+                                                              num_tiles, max_tiles, w13, w13s, T, H,
+                                                              I, Kp, h, stream);
   if (tile_m == 256 && act_fmt)
     return launch_gate_up_bm<256, true>(act, act_scale, sorted, offsets, tiles, num_tiles,
                                         max_tiles, w13, w13s, T, H, I, Kp, h, stream);
@@ -622,11 +656,17 @@ hipError_t launch_gate_up_tiled(int tile_m, int act_fmt, const void* act, const 
                                                  max_tiles, w13, w13s, T, H, I, Kp, h, stream);
 }
 
-hipError_t launch_down_tiled(int tile_m, int act_fmt, const void* h, const uint8_t* h_scale,
+hipError_t launch_down_tiled(int tile_m, int act_fmt, int wfmt, const void* h,
+                             const uint8_t* h_scale,
                              const int32_t* offsets, const int32_t* tiles,
                              const int32_t* num_tiles, int max_tiles, const uint8_t* w2,
                              const uint8_t* w2s, int A, int H, int I, uint16_t* y,
                              hipStream_t stream) {
+  if (wfmt == 1)
+    return tile_m == 128 ? launch_down_bm<128, false, true>(h, h_scale, offsets, tiles, num_tiles,
+                                                            max_tiles, w2, w2s, A, H, I, y, stream)
+                         : launch_down_bm<64, false, true>(h, h_scale, offsets, tiles, num_tiles,
+                                                           max_tiles, w2, w2s, A, H, I, y, stream);
   if (tile_m == 256 && act_fmt)
     return launch_down_bm<256, true>(h, h_scale, offsets, tiles, num_tiles, max_tiles, w2, w2s, A,
                                      H, I, y, stream);

@@ -53,13 +53,15 @@ struct Prefetch {
 hipError_t launch_combine(const uint16_t* y, const float* w, const int32_t* inv, int T, int H, int Kp,
                           uint16_t* out, hipStream_t stream, const Prefetch* pf = nullptr);
 
-bool expert_gemm_tiled_supported(int tile_m, int act_fmt, int H, int I);
-hipError_t launch_gate_up_tiled(int tile_m, int act_fmt, const void* act, const uint8_t* act_scale,
+bool expert_gemm_tiled_supported(int tile_m, int act_fmt, int H, int I, int wfmt = 0);
+hipError_t launch_gate_up_tiled(int tile_m, int act_fmt, int wfmt, const void* act,
+                                const uint8_t* act_scale,
                                 const int32_t* sorted, const int32_t* offsets,
                                 const int32_t* tiles, const int32_t* num_tiles, int max_tiles,
                                 const uint8_t* w13, const uint8_t* w13s, int T, int H, int I,
                                 int Kp, uint16_t* h, hipStream_t stream);
-hipError_t launch_down_tiled(int tile_m, int act_fmt, const void* h, const uint8_t* h_scale,
+hipError_t launch_down_tiled(int tile_m, int act_fmt, int wfmt, const void* h,
+                             const uint8_t* h_scale,
                              const int32_t* offsets, const int32_t* tiles,
                              const int32_t* num_tiles, int max_tiles, const uint8_t* w2,
                              const uint8_t* w2s, int A, int H, int I, uint16_t* y,

@@ -24,9 +24,9 @@ inline int64_t max_tiles_for(int64_t A, int64_t Ep, int64_t tile_m = MOE_TILE_M)
 
 // Rows per GEMM tile for a call, from the shapes alone: small groups stream
 // weights through 32-row tiles; larger groups use the LDS-tiled kernels.
-// MXFP8 weights (wfmt 1) run on the 32-row kernels at every batch size.
+// MXFP8 weights (wfmt 1, bf16 activations) take 32-, 64- or 128-row tiles
+// by the same rule as bf16 activations over MXFP4 weights.
 int choose_tile_m(int64_t A, int64_t Ep, int H, int I, int act_fmt, int wfmt = 0) {
-  if (wfmt == 1) return MOE_TILE_M;
   const int64_t avg = A / Ep;
   if (avg <= 8) return MOE_TILE_M;
   // MXFP4 activations: groups above 128 rows take 256-row tiles (one weight
@@ -34,11 +34,11 @@ int choose_tile_m(int64_t A, int64_t Ep, int H, int I, int act_fmt, int wfmt = 0
   if (act_fmt == MOE_ACT_MXFP4 && avg > 128 && expert_gemm_tiled_supported(256, act_fmt, H, I))
     return 256;
   const int tm = avg <= 48 ? 64 : 128;
-  return expert_gemm_tiled_supported(tm, act_fmt, H, I) ? tm : MOE_TILE_M;
+  return expert_gemm_tiled_supported(tm, act_fmt, H, I, wfmt) ? tm : MOE_TILE_M;
 }
 
-bool tile_m_ok(int32_t tile_m, int32_t act_fmt, int32_t H, int32_t I) {
-  return tile_m == MOE_TILE_M || expert_gemm_tiled_supported(tile_m, act_fmt, H, I);
+bool tile_m_ok(int32_t tile_m, int32_t act_fmt, int32_t H, int32_t I, int wfmt = 0) {
+  return tile_m == MOE_TILE_M || expert_gemm_tiled_supported(tile_m, act_fmt, H, I, wfmt);
 }
 
 moe_status check_shape_HI(int32_t H, int32_t I) {
@@ -228,7 +228,7 @@ moe_status gate_up_impl(const void* act, const uint8_t* act_scale, int32_t act_f
   moe_status st = check_shape_HI(H, I);
   if (st != MOE_OK) return st;
   if (Ep > 2048 || !weights_fit(wfmt, 2 * (int64_t)I, H)) return MOE_ERR_UNSUPPORTED;
-  if (wfmt == 1 ? tile_m != MOE_TILE_M : !tile_m_ok(tile_m, act_fmt, H, I))
+  if (!tile_m_ok(tile_m, act_fmt, H, I, wfmt))
     return MOE_ERR_UNSUPPORTED;
   if (T == 0) return MOE_OK;
   if (!act || !sorted_assign || !expert_offsets || !tile_table || !num_tiles || !w13 ||
@@ -239,7 +239,7 @@ moe_status gate_up_impl(const void* act, const uint8_t* act_scale, int32_t act_f
   if (mt * (I / 16) >= INT32_MAX) return MOE_ERR_UNSUPPORTED;
   hipStream_t s = as_stream(stream);
   if (tile_m != MOE_TILE_M)
-    return from_hip(launch_gate_up_tiled(tile_m, act_fmt, act, act_scale, sorted_assign,
+    return from_hip(launch_gate_up_tiled(tile_m, act_fmt, wfmt, act, act_scale, sorted_assign,
                                          expert_offsets, tile_table, num_tiles, (int)mt, w13,
                                          w13_scale, T, H, I, Kp, h, s));
   return from_hip(launch_gate_up(act_fmt, wfmt, act, act_scale, sorted_assign, expert_offsets,
@@ -257,7 +257,7 @@ moe_status down_impl(const void* h, const uint8_t* h_scale, int32_t act_fmt, int
   moe_status st = check_shape_HI(H, I);
   if (st != MOE_OK) return st;
   if (Ep > 2048 || !weights_fit(wfmt, H, I)) return MOE_ERR_UNSUPPORTED;
-  if (wfmt == 1 ? tile_m != MOE_TILE_M : !tile_m_ok(tile_m, act_fmt, H, I))
+  if (!tile_m_ok(tile_m, act_fmt, H, I, wfmt))
     return MOE_ERR_UNSUPPORTED;
   if (T == 0) return MOE_OK;
   if (!h || !expert_offsets || !tile_table || !num_tiles || !w2 || !w2_scale || !y ||
@@ -268,7 +268,7 @@ moe_status down_impl(const void* h, const uint8_t* h_scale, int32_t act_fmt, int
   if (mt * (H / 128) >= INT32_MAX) return MOE_ERR_UNSUPPORTED;
   hipStream_t s = as_stream(stream);
   if (tile_m != MOE_TILE_M)
-    return from_hip(launch_down_tiled(tile_m, act_fmt, h, h_scale, expert_offsets, tile_table,
+    return from_hip(launch_down_tiled(tile_m, act_fmt, wfmt, h, h_scale, expert_offsets, tile_table,
                                       num_tiles, (int)mt, w2, w2_scale, T * Kp, H, I, y, s));
   return from_hip(launch_down(act_fmt, wfmt, h, h_scale, expert_offsets, tile_table, num_tiles,
                               (int)mt, w2, w2_scale, T * Kp, H, I, y, s));
@@ -328,6 +328,11 @@ int32_t moe_gemm_tile_m(int32_t T, int32_t Kp, int32_t Ep, int32_t H, int32_t I,
                         int32_t act_fmt) {
   if (T <= 0 || Kp < 1 || Ep < 1 || H <= 0 || I <= 0) return MOE_TILE_M;
   return choose_tile_m((int64_t)T * Kp, Ep, H, I, act_fmt);
+}
+
+int32_t moe_mxfp8_gemm_tile_m(int32_t T, int32_t Kp, int32_t Ep, int32_t H, int32_t I) {
+  if (T <= 0 || Kp < 1 || Ep < 1 || H <= 0 || I <= 0) return MOE_TILE_M;
+  return choose_tile_m((int64_t)T * Kp, Ep, H, I, MOE_ACT_BF16, 1);
 }
 
 size_t moe_mxfp4_workspace_size(int32_t T, int32_t H, int32_t I, int32_t E, int32_t K,
@@ -415,7 +420,7 @@ moe_status forward_impl(const uint16_t* x, const float* router_logits,
   const void* a1 = q ? (const void*)xq : (const void*)x;
   const uint8_t* a1s = q ? xs : nullptr;
   e = tm != MOE_TILE_M
-          ? launch_gate_up_tiled(tm, act_fmt, a1, a1s, sorted, offsets, tiles, ntiles, mt, w13,
+          ? launch_gate_up_tiled(tm, act_fmt, wfmt, a1, a1s, sorted, offsets, tiles, ntiles, mt, w13,
                                  w13_scale, T, H, I, Kp, h, s)
           : launch_gate_up(act_fmt, wfmt, a1, a1s, sorted, offsets, tiles, ntiles, mt, w13,
                            w13_scale, T, H, I, Kp, h, s);
@@ -427,7 +432,7 @@ moe_status forward_impl(const uint16_t* x, const float* router_logits,
   const void* a2 = q ? (const void*)hq : (const void*)h;
   const uint8_t* a2s = q ? hs : nullptr;
   e = tm != MOE_TILE_M
-          ? launch_down_tiled(tm, act_fmt, a2, a2s, offsets, tiles, ntiles, mt, w2, w2_scale,
+          ? launch_down_tiled(tm, act_fmt, wfmt, a2, a2s, offsets, tiles, ntiles, mt, w2, w2_scale,
                               (int)A, H, I, y, s)
           : launch_down(act_fmt, wfmt, a2, a2s, offsets, tiles, ntiles, mt, w2, w2_scale, (int)A, H,
                         I, y, s);

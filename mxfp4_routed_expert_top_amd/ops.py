@@ -57,6 +57,7 @@ _SIGS = {
     "moe_mxfp8_expert_down": (_I32, [_P, _P, _P, _P, _I32, _P, _P, _I32, _I32, _I32, _I32, _I32,
                                      _P, _P]),
     "moe_mxfp8_workspace_size": (_SZ, [_I32, _I32, _I32, _I32, _I32, _I32]),
+    "moe_mxfp8_gemm_tile_m": (_I32, [_I32, _I32, _I32, _I32, _I32]),
     "moe_mxfp8_forward": (_I32, [_P, _P, _P, _P, _P, _P, _P, _I32, _I32, _I32, _I32, _I32, _I32,
                                  _P, _P, _P, _P, _SZ, _P]),
 }
@@ -262,6 +263,11 @@ def expert_down(h, h_scale, act_fmt: int, align: dict, w2, w2_scale, T: int, H: 
     return y
 
 
+def mxfp8_gemm_tile_m(T: int, Kp: int, Ep: int, H: int, I: int) -> int:
+    """moe_mxfp8_gemm_tile_m: the GEMM tile rows mxfp8_forward uses for these shapes."""
+    return int(lib().moe_mxfp8_gemm_tile_m(T, Kp, Ep, H, I))
+
+
 def mxfp8_expert_gate_up(x, align: dict, w13, w13_scale, T: int, H: int, I: int, Ep: int,
                          Kp: int, h=None, stream=None):
     """moe_mxfp8_expert_gate_up (MXFP8 weights, bf16 x) -> h bf16 [T*Kp, I], sorted rows."""
@@ -435,7 +441,8 @@ def forward_stages(x, router_logits, shared_gate_logits, w13, w13_scale, w2, w2_
                topk_weights=b["w"], stream=stream)
     rec("route", 1)
     rec("align", 0)
-    tm = TILE_M if wfmt == W_MXFP8 else gemm_tile_m(T, Kp, Ep, H, I, act_fmt)
+    tm = (mxfp8_gemm_tile_m(T, Kp, Ep, H, I) if wfmt == W_MXFP8 else
+          gemm_tile_m(T, Kp, Ep, H, I, act_fmt))
     align_sort(b["ids"], Ep, tile_m=tm, out=b["align"], stream=stream)
     rec("align", 1)
     act, act_s = x, None

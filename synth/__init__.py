@@ -104,6 +104,8 @@ CONFIGS = {
                       act_fmt=ACT_MXFP4, seed_act=1004, seed_w=74, outlier_p=0.001),
     "decode_mxfp8": MoEConfig("decode_mxfp8", T=64, H=4096, I=1024, E=512, K=10, shared=1,
                               act_fmt=ACT_BF16, seed_act=1001, seed_w=77, wfmt=W_MXFP8),
+    "prefill_mxfp8": MoEConfig("prefill_mxfp8", T=1536, H=4096, I=1024, E=512, K=10, shared=1,
+                               act_fmt=ACT_BF16, seed_act=1002, seed_w=77, wfmt=W_MXFP8),
     # one GPU's share of the decode layer split 8 ways by tensor parallelism:
     # every expert's I/8 slice of gate/up rows and down columns
     "decode_tp8": MoEConfig("decode_tp8", T=64, H=4096, I=128, E=512, K=10, shared=1,

@@ -26,7 +26,7 @@ def declared_functions():
 def test_library_loads_and_exports_every_declared_symbol():
     lib = ops.lib()
     names = declared_functions()
-    assert len(names) == 20
+    assert len(names) == 21
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(ops.EXPORTS)
@@ -213,7 +213,8 @@ def test_mxfp8_argument_errors():
         for k, v in kw.items():
             a[int(k[1:])] = v
         return f(*a)
-    assert call(gu, base, a5=64) == UNSUPPORTED                 # MXFP8 runs on 32-row tiles only
+    assert call(gu, base, a5=256) == UNSUPPORTED                # no 256-row MXFP8 tiles
+    assert call(gu, base, a5=64, a9=384) == UNSUPPORTED         # tiled: H a multiple of 256
     assert call(gu, base, a9=200) == UNSUPPORTED                # H not a multiple of 128
     assert call(gu, base, a0=None) == INVALID
     assert call(gu, base, a0=MIS) == INVALID
@@ -221,7 +222,11 @@ def test_mxfp8_argument_errors():
     dn = L.moe_mxfp8_expert_down
     # h, offsets, tiles, num_tiles, tile_m, w2, w2s, T, H, I, Ep, Kp, y, stream
     based = [FAKE, FAKE, FAKE, FAKE, 32, FAKE, FAKE, 4, 256, 128, 9, 3, FAKE, None]
-    assert call(dn, based, a4=128) == UNSUPPORTED
+    assert call(dn, based, a4=256) == UNSUPPORTED
+    assert ops.mxfp8_gemm_tile_m(64, 11, 513, 4096, 1024) == 32
+    assert ops.mxfp8_gemm_tile_m(1536, 11, 513, 4096, 1024) == 64
+    assert ops.mxfp8_gemm_tile_m(8192, 11, 513, 4096, 1024) == 128
+    assert ops.mxfp8_gemm_tile_m(8192, 11, 513, 4096, 4608) == 32   # I above the tiled limit
     assert call(dn, based, a12=None) == INVALID
     assert call(dn, based, a5=MIS) == INVALID
     # an expert's 2I x H code bytes must fit a 32-bit buffer range

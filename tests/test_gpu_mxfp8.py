@@ -136,6 +136,9 @@ SMALL = {
     "sparse": synth.custom_config("sparse8", T=3, H=256, I=128, E=300, K=2, shared=1),
     # many 32-row tiles per expert, several 16-row subtiles per tile, odd K chunk count
     "big_groups": synth.custom_config("big_groups8", T=300, H=384, I=384, E=16, K=3, shared=1),
+    # groups large enough for the LDS-tiled kernels (64- and 128-row tiles)
+    "tiled64": synth.custom_config("tiled64_8", T=200, H=256, I=128, E=24, K=4, shared=1),
+    "tiled128": synth.custom_config("tiled128_8", T=300, H=512, I=256, E=16, K=3, shared=1),
 }
 
 
@@ -199,3 +202,23 @@ def test_mxfp8_layer_full_size_decode_sampled():
     _say(f"  decode mxfp8: rel_l2 {e_rel:.2e}  max_abs/rms {e_max:.2e}")
     assert e_rel <= TOL and e_max <= MAX_ABS_RMS
     assert torch.isfinite(out.float()).all()
+
+
+@pytest.mark.parametrize("tile_m", [32, 64, 128])
+def test_mxfp8_gemm_kernels_for_every_tile_size(tile_m):
+    """The MXFP8 per-step entry points with each tile size against the oracle."""
+    cfg = synth.custom_config("tiles8", T=150, H=512, I=256, E=8, K=3, shared=1)
+    _say("mxfp8 tile_m", tile_m)
+    prob = Problem8(cfg)
+    c, o = prob.cfg, ops()
+    ids, w = o.route_topk(prob.logits, prob.gate, c.K, c.shared)
+    al = o.align_sort(ids, c.Ep, tile_m=tile_m)
+    h = o.mxfp8_expert_gate_up(prob.x, al, prob.w13, prob.w13s, c.T, c.H, c.I, c.Ep, c.Kp)
+    y = o.mxfp8_expert_down(h, al, prob.w2, prob.w2s, c.T, c.H, c.I, c.Ep, c.Kp)
+    out = o.combine(y, w, al["inv"], c.T, c.H, c.Kp)
+    torch.cuda.synchronize()
+    want = prob.oracle()
+    e_rel = rel_l2(bits(out), want["out"])
+    e_max = max_abs_over_rms(bits(out), want["out"])
+    _say(f"  tile_m {tile_m}: rel_l2 {e_rel:.2e}  max_abs/rms {e_max:.2e}")
+    assert e_rel <= TOL and e_max <= MAX_ABS_RMS

@@ -53,12 +53,13 @@ def test_committed_records_match_kernel_names():
     import bench
     import synth
     from mxfp4_routed_expert_top_amd import ops
-    for name in ("decode", "prefill", "prefill_skewed", "w4a4", "decode_mxfp8"):
+    for name in ("decode", "prefill", "prefill_skewed", "w4a4", "decode_mxfp8", "prefill_mxfp8"):
         cfg = synth.CONFIGS[name]
         path = bench.traffic_path(cfg)
         if not os.path.exists(path):
             continue
         rec = json.load(open(path))
-        tile_m = (32 if cfg.wfmt == synth.W_MXFP8 else
+        tile_m = (ops.mxfp8_gemm_tile_m(cfg.T, cfg.Kp, cfg.Ep, cfg.H, cfg.I)
+                  if cfg.wfmt == synth.W_MXFP8 else
                   ops.gemm_tile_m(cfg.T, cfg.Kp, cfg.Ep, cfg.H, cfg.I, cfg.act_fmt))
         assert bench.gate_up_kernel_name(cfg, tile_m) in rec["kernels"], name
