@@ -17,8 +17,10 @@ hipError_t launch_route_topk_split(const float* partial, int S, int T, int E, in
 
 int router_splits(int T, int H, int Ep);
 size_t router_workspace_bytes(int T, int H, int Ep);   // partial sums + summed logits
+// S = router_splits(...) > 1: partial sums into partial [S, T, Ep] (added by
+// launch_route_topk_split); S = 1: the logits straight into logits [T, Ep].
 hipError_t launch_router_gemm(const uint16_t* x, const uint16_t* w, int T, int H, int Ep,
-                              float* partial, hipStream_t stream);
+                              float* partial, float* logits, hipStream_t stream);
 
 size_t align_scratch_bytes(int A, int Ep);
 hipError_t launch_align_sort(const int32_t* ids, int A, int Ep, int tile_m, int32_t* counts,

@@ -152,7 +152,7 @@ moe_status moe_route_topk_gemm(const uint16_t* x, const uint16_t* router_w, int3
   float* partial = (float*)workspace;
   const int S = router_splits(T, H, Ep);
   float* logits = logits_out ? logits_out : partial + (size_t)S * T * Ep;
-  hipError_t e = launch_router_gemm(x, router_w, T, H, Ep, partial, s);
+  hipError_t e = launch_router_gemm(x, router_w, T, H, Ep, partial, logits, s);
   if (e != hipSuccess) return MOE_ERR_DEVICE;
   return from_hip(launch_route_topk_split(partial, S, T, E, K, shared, renormalize, topk_ids,
                                           topk_weights, logits, s));
@@ -402,10 +402,10 @@ moe_status forward_impl(const uint16_t* x, const float* router_logits,
   hipError_t e;
   if (router_w) {
     const int S = router_splits(T, H, Ep);
-    e = launch_router_gemm(x, router_w, T, H, Ep, rpart, s);
+    float* lg = logits_out ? logits_out : rpart + (size_t)S * T * Ep;
+    e = launch_router_gemm(x, router_w, T, H, Ep, rpart, lg, s);
     if (e != hipSuccess) return MOE_ERR_DEVICE;
-    e = launch_route_topk_split(rpart, S, T, E, K, shared, 1, ids, wts,
-                                logits_out ? logits_out : rpart + (size_t)S * T * Ep, s);
+    e = launch_route_topk_split(rpart, S, T, E, K, shared, 1, ids, wts, lg, s);
   } else {
     e = launch_route_topk(router_logits, shared_gate_logits, T, E, K, shared, 1, ids, wts, s);
   }

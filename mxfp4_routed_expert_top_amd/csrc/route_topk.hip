@@ -199,10 +199,12 @@ hipError_t launch_route_topk_split(const float* partial, int S, int T, int E, in
                                    hipStream_t stream) {
   const int Ep = E + shared;
   const int64_t n = (int64_t)T * Ep;
-  hipLaunchKernelGGL(sum_splits_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream,
-                     partial, S, n, logits);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  if (S > 1) {                       // one split: the router GEMM wrote the logits itself
+    hipLaunchKernelGGL(sum_splits_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream,
+                       partial, S, n, logits);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
   return launch_route_kernel(logits, Ep, logits + E, Ep, T, E, K, shared, renormalize, ids,
                              weights, stream);
 }
