@@ -66,14 +66,13 @@ def make_inputs(cfg):
     gate = None if gate is None else gate.to(dev)
     u8 = dict(dtype=torch.uint8, device=dev)
     per = 1 if cfg.wfmt == synth.W_MXFP8 else 2      # elements per code byte
-    quant = ops.mxfp8_quantize if cfg.wfmt == synth.W_MXFP8 else ops.mxfp4_quantize
     w13 = torch.empty(cfg.Ep, 2 * cfg.I, cfg.H // per, **u8)
     w13s = torch.empty(cfg.Ep, 2 * cfg.I, cfg.H // 32, **u8)
     w2 = torch.empty(cfg.Ep, cfg.H, cfg.I // per, **u8)
     w2s = torch.empty(cfg.Ep, cfg.H, cfg.I // 32, **u8)
     for e in range(cfg.Ep):             # float draws packed by the library's own quantiser
-        quant(synth.expert_w13(cfg, e, dev), w13[e], w13s[e])
-        quant(synth.expert_w2(cfg, e, dev), w2[e], w2s[e])
+        ops.quantize_weights(synth.expert_w13(cfg, e, dev), w13[e], w13s[e], cfg.wfmt)
+        ops.quantize_weights(synth.expert_w2(cfg, e, dev), w2[e], w2s[e], cfg.wfmt)
     torch.cuda.synchronize()
     return x, logits, gate, w13, w13s, w2, w2s
 

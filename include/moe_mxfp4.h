@@ -48,8 +48,8 @@
  * element 2j in the low nibble.  Scale bytes 1..254 are supported; 0 only
  * for all-zero blocks; 255 (NaN) is outside the contract.
  *
- * Weight layout (expert e in [0, E'), E' = E + shared; the shared expert is
- * expert E):
+ * Weight matrices (expert e in [0, E'), E' = E + shared; the shared expert
+ * is expert E), row-major as moe_mxfp4_quantize writes them:
  *   w13       uint8 [E', 2I, H/2]  rows [0, I) gate, rows [I, 2I) up
  *   w13_scale uint8 [E', 2I, H/32]
  *   w2        uint8 [E', H, I/2]
@@ -58,8 +58,21 @@
  * MXFP8 (OCP Microscaling v1.0): per 32 consecutive elements along the
  * reduction axis one E8M0 scale byte and 32 FP8 E4M3 codes, one per byte
  * (s|eeee|mmm, bias 7, subnormals m/8 * 2^-6, largest 448, S.1111.111 =
- * NaN outside the contract).  Layout as above with one byte per element:
+ * NaN outside the contract).  Matrices as above with one byte per element:
  *   w13 uint8 [E', 2I, H], w2 uint8 [E', H, I]; the scales as for MXFP4.
+ *
+ * Native code order.  The GEMM entry points (moe_expert_gate_up,
+ * moe_expert_down, the mxfp8 ones and every forward) take the weight CODES
+ * (w13, w2) in the kernels' native order, which moe_weights_to_native makes
+ * from the row-major matrices once, when the weights are loaded; the scales
+ * stay row-major.  Per expert, with K the reduction length (H for w13, I for
+ * w2), NQ = 1 (MXFP4) or 2 (MXFP8) and C = K/128 chunks, the codes are
+ * 1 KiB blocks: block ((s*C + c)*NQ + q) holds at byte 16*l (l < 64,
+ * l = 16*g + n) the 16 row-major bytes of row 16*s + n starting at byte
+ * NQ*(64*c + 16*g) + 16*q.  An expert keeps its size and place (expert e
+ * starts at e * rows * K * NQ / 2 bytes), so each expert's codes stay one
+ * contiguous range.  (One MFMA operand load of 16 rows x 128 elements is
+ * then one contiguous KiB instead of 16 half cache lines.)
  */
 #ifndef MOE_MXFP4_H
 #define MOE_MXFP4_H
@@ -186,6 +199,23 @@ MOE_API moe_status moe_mxfp4_quantize(const void *src, int32_t src_dtype, int64_
                               uint8_t *packed, uint8_t *scales, void *stream);
 
 /*
+ * Row-major weight codes -> the native code order the GEMM kernels read
+ * (defined above), for rows x cols elements of one or more experts stacked
+ * by rows (e.g. all of w13 as [E' * 2I, H]): a pure permutation of 16-byte
+ * pieces, done once when weights are loaded.  (A layout for the memory
+ * system, not a step of the method: the MoE computes the same either way.)
+ *   src        uint8 row-major codes [rows, cols/2] (wfmt 0, MXFP4) or
+ *              [rows, cols] (wfmt 1, MXFP8), 16-byte aligned
+ *   wfmt       0 = MXFP4, 1 = MXFP8
+ *   dst        out, same size, 16-byte aligned, not overlapping src
+ * Errors: INVALID_ARGUMENT (null or misaligned pointers, rows < 0, cols < 0,
+ * bad wfmt, overlapping buffers), UNSUPPORTED (rows not a multiple of 16,
+ * cols not a multiple of 128).
+ */
+MOE_API moe_status moe_weights_to_native(const uint8_t *src, int32_t wfmt, int64_t rows,
+                                         int64_t cols, uint8_t *dst, void *stream);
+
+/*
  * Grouped gate/up GEMM with SwiGLU (VibeSys post, section "Baseline": the
  * fused HIP MoE kernel dequantises MXFP4 weights in registers).
  * For every sorted row r of expert e (token t = sorted_assign[r] / Kp):
@@ -202,6 +232,7 @@ MOE_API moe_status moe_mxfp4_quantize(const void *src, int32_t src_dtype, int64_
  *              for MXFP4 ones: the weight scales of a workgroup's rows sit
  *              in LDS for the whole reduction); 256 the LDS-tiled kernel
  *              for MXFP4 activations only (H, I at most 6144)
+ *   w13        codes [E', 2I, H/2] in the native order; w13_scale [E', 2I, H/32]
  *   h          out bf16 [T*Kp, I], sorted row order
  * Errors: INVALID_ARGUMENT, UNSUPPORTED (H or I not a multiple of 128, or a
  * tile_m / shape the kernels do not cover).
@@ -218,6 +249,7 @@ MOE_API moe_status moe_expert_gate_up(const void *act, const uint8_t *act_scale,
  *   act_fmt = MOE_ACT_BF16:  h bf16 [A, I], h_scale = NULL
  *   act_fmt = MOE_ACT_MXFP4: h packed uint8 [A, I/2], h_scale uint8 [A, I/32]
  *   tile_m     as for moe_expert_gate_up
+ *   w2         codes [E', H, I/2] in the native order; w2_scale [E', H, I/32]
  *   y          out bf16 [A, H], sorted row order (A = T*Kp)
  * Errors: INVALID_ARGUMENT, UNSUPPORTED (H or I not a multiple of 128, or a
  * tile_m / shape the kernels do not cover).
@@ -260,7 +292,8 @@ MOE_API moe_status moe_mxfp8_quantize(const void *src, int32_t src_dtype, int64_
  * (weight-streaming kernel) or 64 / 128 (LDS-tiled kernel; H a multiple of
  * 256, H and I at most 4096); the tile table from moe_align_sort with the
  * same tile_m.
- *   x          bf16 [T, H];  w13 uint8 [E', 2I, H], w13_scale uint8 [E', 2I, H/32]
+ *   x          bf16 [T, H];  w13 uint8 [E', 2I, H] (native code order),
+ *              w13_scale uint8 [E', 2I, H/32]
  *   h          out bf16 [T*Kp, I] in sorted row order
  * Errors: INVALID_ARGUMENT, UNSUPPORTED (H or I not a multiple of 128, a
  * tile_m / shape the kernels do not cover, an expert's 2I x H code bytes
@@ -275,7 +308,8 @@ MOE_API moe_status moe_mxfp8_expert_gate_up(const uint16_t *x, const int32_t *so
 /*
  * Grouped down GEMM over MXFP8 weights (W8A16): as moe_expert_down with
  * act_fmt = MOE_ACT_BF16; tile_m as for moe_mxfp8_expert_gate_up.
- *   h          bf16 [T*Kp, I];  w2 uint8 [E', H, I], w2_scale uint8 [E', H, I/32]
+ *   h          bf16 [T*Kp, I];  w2 uint8 [E', H, I] (native code order),
+ *              w2_scale uint8 [E', H, I/32]
  *   y          out bf16 [T*Kp, H], sorted row order
  * Errors: as moe_mxfp8_expert_gate_up.
  */
@@ -306,6 +340,7 @@ MOE_API size_t moe_mxfp4_workspace_size(int32_t T, int32_t H, int32_t I, int32_t
  *   x              bf16 [T, H]
  *   router_logits  fp32 [T, E];  shared_gate_logits fp32 [T] (shared = 1) or NULL
  *   w13, w13_scale, w2, w2_scale: the MXFP4 weights of E + shared experts
+ *                  (codes in the native order, scales row-major)
  *   act_fmt        MOE_ACT_BF16 (W4A16) or MOE_ACT_MXFP4 (W4A4: x and h are
  *                  MXFP4-quantised before their GEMM)
  *   out            out bf16 [T, H]
@@ -345,9 +380,9 @@ MOE_API moe_status moe_mxfp4_forward_router(const uint16_t *x, const uint16_t *r
  * (device pointers, layouts as for moe_mxfp4_forward_router). */
 typedef struct {
   const uint16_t *router_w;      /* bf16 [E + shared, H], 16-byte aligned */
-  const uint8_t *w13;            /* [E', 2I, H/2] */
+  const uint8_t *w13;            /* [E', 2I, H/2], native code order */
   const uint8_t *w13_scale;      /* [E', 2I, H/32] */
-  const uint8_t *w2;             /* [E', H, I/2] */
+  const uint8_t *w2;             /* [E', H, I/2], native code order */
   const uint8_t *w2_scale;       /* [E', H, I/32] */
 } moe_mxfp4_layer;
 

@@ -10,4 +10,5 @@ from .ops import (ACT_BF16, ACT_MXFP4, W_MXFP4, W_MXFP8, MoeError, align_sort,  
                   mxfp4_forward, mxfp4_forward_layers, mxfp4_forward_router, mxfp4_quantize,
                   mxfp8_expert_down,
                   mxfp8_expert_gate_up, mxfp8_forward, mxfp8_quantize, mxfp8_workspace_size,
-                  route_topk, route_topk_gemm, workspace_size)
+                  quantize_weights, route_topk, route_topk_gemm, weights_to_native,
+                  workspace_size)

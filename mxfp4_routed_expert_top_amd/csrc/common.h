@@ -86,6 +86,22 @@ __device__ __forceinline__ u32x4_t bload16(rsrc_t r, uint32_t voff, uint32_t sof
   return __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, (int)soff, 0));
 }
 
+// Expert weight codes in the GEMM kernels' native order.  An expert's code
+// matrix (rows a multiple of 16, reduction length K a multiple of 128; NQ =
+// 1 byte per two MXFP4 codes -> 16 code bytes per lane and chunk, NQ = 2 for
+// MXFP8's byte per code -> 32) is a sequence of 1 KiB blocks: block
+// (s * (K / 128) + c) * NQ + hq holds, at byte 16 l, the 16 bytes lane
+// l = 16 g + n loads for row 16 s + n, chunk c (elements [128 c, 128 c + 128)),
+// K-group g, part hq: row-major code bytes [NQ (64 c + 16 g) + 16 hq, +16).
+// A wave's load of one strip chunk is then one contiguous KiB, where the
+// row-major layout touches 16 rows at half a 128-byte line each.
+__device__ __forceinline__ uint32_t wnat_lane(int strip, int K, int NQ, int lane) {
+  return (uint32_t)strip * (uint32_t)(K / 128 * NQ) * 1024u + 16u * (uint32_t)lane;
+}
+__device__ __forceinline__ uint32_t wnat_chunk(int c, int NQ, int hq) {
+  return (uint32_t)(NQ * c + hq) * 1024u;
+}
+
 __device__ __forceinline__ uint32_t bload1(rsrc_t r, uint32_t voff, uint32_t soff) {
   return (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(r, (int)voff, (int)soff, 0);
 }

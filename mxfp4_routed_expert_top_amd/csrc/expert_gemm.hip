@@ -5,7 +5,8 @@
 //
 // W4A16 (bf16 activations): the fused HIP MoE kernel dequantises MXFP4 in
 // registers (same post, section "Baseline"); here each lane loads 16 bytes
-// (32 codes, one scale block) of a weight row, expands them to bf16 with the
+// (32 codes, one scale block) of a weight row (from the native code order of
+// common.h: a strip's chunk is one contiguous KiB), expands them to bf16 with the
 // gfx950 scaled converter (exact: an E2M1 value times a power of two) and
 // feeds v_mfma_f32_16x16x32_bf16.  W4A4 (MXFP4 activations): both operands
 // go straight into the scaled MFMA v_mfma_scale_f32_16x16x128_f8f6f4 with
@@ -22,7 +23,7 @@
 // projection; a wave owns 16 intermediate columns i and both projections, so
 // SwiGLU h = silu(gate) * up runs in registers and h is stored as bf16 in
 // the sorted row order.  down: a wave owns 32 output columns j; y is stored
-// as fp32 in the sorted row order.
+// as bf16 in the sorted row order.
 #include "common.h"
 #include "kernels.h"
 
@@ -78,7 +79,7 @@ constexpr uint32_t kOutOfRange = 0x80000000u;
 
 struct Operands {
   rsrc_t w, a, as;         // weights, activations, activation scales (MXFP4)
-  uint32_t wo[2];          // lane offsets of its two weight rows (+16 g)
+  uint32_t wo[2];          // lane offsets in its two weight strips (native code order)
   uint32_t lso[2];         // LDS offsets of its two weight rows' scales (+g)
   uint32_t ao, aso;        // lane offset of its activation row (+32 g elements or +16 g bytes)
   const uint8_t* lds;      // the workgroup's weight scales
@@ -101,7 +102,7 @@ struct Phase {
       for (int si = 0; si < 2; ++si)
 #pragma unroll
         for (int hq = 0; hq < NQ; ++hq)
-          q[si][NQ * j + hq] = bload16(o.w, o.wo[si], 64 * NQ * (c0 + j) + 16 * hq);
+          q[si][NQ * j + hq] = bload16(o.w, o.wo[si], wnat_chunk(c0 + j, NQ, hq));
 #pragma unroll
     for (int j = 0; j < PH; ++j) {
       if constexpr (kFP4A) {
@@ -217,8 +218,9 @@ __attribute__((amdgpu_waves_per_eu(MOE_GEMM_WAVES_PER_EU))) void gate_up_kernel(
   Operands o;
   o.lds = lds_scales;
   o.w = make_rsrc(w13 + ti.expert * wbytes, (uint32_t)wbytes);
-  o.wo[0] = i * wrb + 16 * Phase<PH, kFP4A, false, kW8>::NQ * g;
-  o.wo[1] = (I + i) * wrb + 16 * Phase<PH, kFP4A, false, kW8>::NQ * g;
+  constexpr int NQ = Phase<PH, kFP4A, false, kW8>::NQ;
+  o.wo[0] = wnat_lane(i >> 4, H, NQ, lane);
+  o.wo[1] = wnat_lane((I + i) >> 4, H, NQ, lane);
   o.lso[0] = (wave * 16 + nl) * rs + g;
   o.lso[1] = (64 + wave * 16 + nl) * rs + g;
   if (kFP4A) {
@@ -290,8 +292,9 @@ __attribute__((amdgpu_waves_per_eu(MOE_GEMM_WAVES_PER_EU))) void down_kernel(
   Operands o;
   o.lds = lds_scales;
   o.w = make_rsrc(w2 + ti.expert * wbytes, (uint32_t)wbytes);
-  o.wo[0] = j0 * wrb + 16 * Phase<PH, kFP4A, false, kW8>::NQ * g;
-  o.wo[1] = (j0 + 16) * wrb + 16 * Phase<PH, kFP4A, false, kW8>::NQ * g;
+  constexpr int NQ = Phase<PH, kFP4A, false, kW8>::NQ;
+  o.wo[0] = wnat_lane(j0 >> 4, I, NQ, lane);
+  o.wo[1] = wnat_lane((j0 >> 4) + 1, I, NQ, lane);
   o.lso[0] = (wave * 32 + nl) * rs + g;
   o.lso[1] = (wave * 32 + 16 + nl) * rs + g;
   if (kFP4A) {

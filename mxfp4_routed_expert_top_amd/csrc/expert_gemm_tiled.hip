@@ -10,7 +10,8 @@
 //
 // The weight scales of the workgroup's rows (whole K) go to LDS once, up
 // front.  Per 128-element K chunk: every wave loads its four strips' codes
-// (16 bytes per lane = one scale block) from HBM into registers and the
+// (16 bytes per lane = one scale block; one contiguous KiB per strip in the
+// native code order of common.h) from HBM into registers and the
 // workgroup gathers the tile's activation chunk into LDS (a 3- or 4-stage
 // pipeline, one barrier per chunk, later chunks' loads in flight during the
 // MFMAs).
@@ -166,7 +167,7 @@ struct TiledGemm {
   static constexpr int LPS = XI + 4 * NQ;                  // vmem ops per wave per stage
 
   rsrc_t w, ws, a, as;
-  uint32_t wo[4];               // lane's weight row offsets (+16 g)
+  uint32_t wo[4];               // lane's offsets in its four weight strips (native code order)
   uint32_t xo[XI];              // lane's activation source offsets (or kOOR)
   uint32_t sro;                 // lane's scale byte offset in LDS for strip 0 (row 64 wave + nl, + g)
   int wave, lane, nl, g, nch, Q, swz;
@@ -221,7 +222,7 @@ struct TiledGemm {
 #pragma unroll
     for (int t = 0; t < 4; ++t)
 #pragma unroll
-      for (int hq = 0; hq < NQ; ++hq) q[NQ * t + hq] = bload16(w, wo[t] | oor, 64 * NQ * cc + 16 * hq);
+      for (int hq = 0; hq < NQ; ++hq) q[NQ * t + hq] = bload16(w, wo[t] | oor, wnat_chunk(cc, NQ, hq));
   }
 
   // MFMAs of one chunk on the first NMT 16-row sub-tiles (the live ones).
@@ -498,11 +499,10 @@ __global__ __launch_bounds__(256) void gate_up_tiled_kernel(
   setup(G, ti, H, w13, w13s, 2 * I);
   const int nl = G.nl, g = G.g;
   const uint32_t rb = H / 2, rs = H / 32;
-  const uint32_t wrb = kW8 ? H : H / 2;                    // weight code bytes per row
   const int i0 = s * 128 + G.wave * 32;
   const int rows4[4] = {i0 + nl, i0 + 16 + nl, I + i0 + nl, I + i0 + 16 + nl};
 #pragma unroll
-  for (int st = 0; st < 4; ++st) G.wo[st] = rows4[st] * wrb + 16 * G.NQ * g;
+  for (int st = 0; st < 4; ++st) G.wo[st] = wnat_lane(rows4[st] >> 4, H, G.NQ, G.lane);
   if (kFP4A) {
     G.a = make_rsrc(act, (uint32_t)((size_t)T * rb));
     G.as = make_rsrc(act_scale, (uint32_t)((size_t)T * rs));
@@ -552,10 +552,9 @@ __global__ __launch_bounds__(256) void down_tiled_kernel(
   setup(G, ti, I, w2, w2s, H);
   const int nl = G.nl, g = G.g;
   const uint32_t rb = I / 2, rs = I / 32;
-  const uint32_t wrb = kW8 ? I : I / 2;                    // weight code bytes per row
   const int j0 = s * 256 + G.wave * 64;
 #pragma unroll
-  for (int st = 0; st < 4; ++st) G.wo[st] = (j0 + 16 * st + nl) * wrb + 16 * G.NQ * g;
+  for (int st = 0; st < 4; ++st) G.wo[st] = wnat_lane((j0 >> 4) + st, I, G.NQ, G.lane);
   if (kFP4A) {
     G.a = make_rsrc(hin, (uint32_t)((size_t)A * rb));
     G.as = make_rsrc(hscale, (uint32_t)((size_t)A * rs));

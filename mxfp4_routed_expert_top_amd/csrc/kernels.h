@@ -31,6 +31,9 @@ hipError_t launch_mxfp4_quant(const void* src, int src_is_bf16, int64_t rows, in
                               uint8_t* packed, uint8_t* scales, hipStream_t stream);
 hipError_t launch_mxfp8_quant(const void* src, int src_is_bf16, int64_t rows, int64_t cols,
                               uint8_t* codes, uint8_t* scales, hipStream_t stream);
+// row-major weight codes -> native code order (nq = 1 MXFP4, 2 MXFP8)
+hipError_t launch_weights_native(const uint8_t* src, int nq, int64_t rows, int64_t cols,
+                                 uint8_t* dst, hipStream_t stream);
 
 int expert_gemm_tile_m();
 int expert_gemm_phase(int nch);

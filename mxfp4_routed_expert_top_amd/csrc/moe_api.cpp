@@ -208,6 +208,19 @@ moe_status moe_mxfp8_quantize(const void* src, int32_t src_dtype, int64_t rows, 
                                      as_stream(stream)));
 }
 
+moe_status moe_weights_to_native(const uint8_t* src, int32_t wfmt, int64_t rows, int64_t cols,
+                                 uint8_t* dst, void* stream) {
+  if (rows < 0 || cols < 0 || (wfmt != 0 && wfmt != 1)) return MOE_ERR_INVALID_ARGUMENT;
+  if (rows % 16 || cols % 128) return MOE_ERR_UNSUPPORTED;
+  if (rows == 0 || cols == 0) return MOE_OK;
+  if (!src || !dst || !aligned16(src) || !aligned16(dst)) return MOE_ERR_INVALID_ARGUMENT;
+  const int64_t bytes = rows * (wfmt == 1 ? cols : cols / 2);
+  const uintptr_t s0 = (uintptr_t)src, d0 = (uintptr_t)dst;
+  if (s0 < d0 + (uintptr_t)bytes && d0 < s0 + (uintptr_t)bytes) return MOE_ERR_INVALID_ARGUMENT;
+  return from_hip(launch_weights_native(src, wfmt == 1 ? 2 : 1, rows, cols, dst,
+                                        as_stream(stream)));
+}
+
 }  // extern "C"
 
 namespace {

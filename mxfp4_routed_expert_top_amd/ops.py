@@ -52,6 +52,7 @@ _SIGS = {
     "moe_mxfp4_forward_layers": (_I32, [_P, _I32, _P, _I32, _I32, _I32, _I32, _I32, _I32, _I32,
                                         _I32, _P, _P, _SZ, _P]),
     "moe_mxfp8_quantize": (_I32, [_P, _I32, _I64, _I64, _P, _P, _P]),
+    "moe_weights_to_native": (_I32, [_P, _I32, _I64, _I64, _P, _P]),
     "moe_mxfp8_expert_gate_up": (_I32, [_P, _P, _P, _P, _P, _I32, _P, _P, _I32, _I32, _I32, _I32,
                                         _I32, _P, _P]),
     "moe_mxfp8_expert_down": (_I32, [_P, _P, _P, _P, _I32, _P, _P, _I32, _I32, _I32, _I32, _I32,
@@ -230,6 +231,33 @@ def mxfp8_quantize(src, codes=None, scales=None, stream=None):
         scales = torch.empty(*lead, cols // 32, dtype=torch.uint8, device=src.device)
     _check("moe_mxfp8_quantize", lib().moe_mxfp8_quantize(
         _ptr(src), dt, rows, cols, _ptr(codes), _ptr(scales), _stream(stream)))
+    return codes, scales
+
+
+def weights_to_native(codes, wfmt: int = W_MXFP4, out=None, stream=None):
+    """moe_weights_to_native: row-major weight codes uint8 [..., rows, row_bytes]
+    (one matrix or experts stacked along the leading dims) -> the GEMM kernels'
+    native code order, same shape and size."""
+    _dt(codes, torch.uint8, "codes")
+    if codes.dim() < 2:
+        raise ValueError("codes must be [..., rows, row_bytes]")
+    row_bytes = codes.shape[-1]
+    cols = row_bytes if wfmt == W_MXFP8 else 2 * row_bytes
+    rows = codes.numel() // row_bytes if row_bytes else 0
+    if out is None:
+        out = torch.empty_like(codes)
+    _check("moe_weights_to_native", lib().moe_weights_to_native(
+        _ptr(codes), wfmt, rows, cols, _ptr(out), _stream(stream)))
+    return out
+
+
+def quantize_weights(w, codes, scales, wfmt: int = W_MXFP4, stream=None):
+    """Pack float expert weights [rows, K] for the GEMMs: quantise (MXFP4 or
+    MXFP8, row-major), then put the codes into the native order (codes
+    [rows, K/2] or [rows, K]; scales [rows, K/32] stay row-major)."""
+    quant = mxfp8_quantize if wfmt == W_MXFP8 else mxfp4_quantize
+    rm, _ = quant(w, scales=scales, stream=stream)
+    weights_to_native(rm, wfmt, out=codes, stream=stream)
     return codes, scales
 
 

@@ -20,6 +20,17 @@ MAX_ABS_RMS = 2e-2
 W_ATOL = 1e-6          # routing weights, absolute
 
 
+def native_order(codes: np.ndarray, nq: int) -> np.ndarray:
+    """Row-major weight codes [rows, row_bytes] -> the GEMM kernels' native
+    code order (the permutation include/moe_mxfp4.h defines), by reshapes:
+    row 16 s + n, byte nq (64 c + 16 g) + 16 q + b  ->  block (s, c, q),
+    lane 16 g + n, byte b.  nq = 1 (MXFP4) or 2 (MXFP8)."""
+    rows, rb = codes.shape
+    C = rb // (64 * nq)
+    a = codes.reshape(rows // 16, 16, C, 4, nq, 16)      # s, n, c, g, q, b
+    return np.ascontiguousarray(a.transpose(0, 2, 4, 3, 1, 5)).reshape(rows, rb)
+
+
 def bits(t: torch.Tensor) -> np.ndarray:
     """bf16 tensor -> uint16 numpy bit patterns."""
     return t.detach().contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
@@ -57,8 +68,8 @@ class Problem:
         self.w2 = torch.empty(c.Ep, c.H, c.I // 2, **u8)
         self.w2s = torch.empty(c.Ep, c.H, c.I // 32, **u8)
         for e in range(c.Ep):
-            ops.mxfp4_quantize(synth.expert_w13(c, e, DEV), self.w13[e], self.w13s[e])
-            ops.mxfp4_quantize(synth.expert_w2(c, e, DEV), self.w2[e], self.w2s[e])
+            ops.quantize_weights(synth.expert_w13(c, e, DEV), self.w13[e], self.w13s[e])
+            ops.quantize_weights(synth.expert_w2(c, e, DEV), self.w2[e], self.w2s[e])
         torch.cuda.synchronize()
 
     @functools.lru_cache(maxsize=None)

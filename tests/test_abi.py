@@ -26,7 +26,7 @@ def declared_functions():
 def test_library_loads_and_exports_every_declared_symbol():
     lib = ops.lib()
     names = declared_functions()
-    assert len(names) == 21
+    assert len(names) == 22
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(ops.EXPORTS)
@@ -110,6 +110,21 @@ def test_quantize_argument_errors():
     assert f(None, 0, 4, 64, FAKE, FAKE, None) == INVALID
     assert f(MIS, 0, 4, 64, FAKE, FAKE, None) == INVALID           # misaligned source
     assert f(FAKE, 0, 0, 64, FAKE, FAKE, None) == OK               # empty
+
+
+def test_weights_to_native_argument_errors():
+    f = ops.lib().moe_weights_to_native
+    B = ctypes.c_void_p(0x200000)                                  # FAKE + 1 MiB
+    assert f(FAKE, 0, 24, 256, B, None) == UNSUPPORTED             # rows % 16
+    assert f(FAKE, 0, 32, 192, B, None) == UNSUPPORTED             # cols % 128
+    assert f(FAKE, 2, 32, 256, B, None) == INVALID                 # weight format
+    assert f(FAKE, 0, -16, 256, B, None) == INVALID
+    assert f(None, 0, 32, 256, B, None) == INVALID
+    assert f(FAKE, 1, 32, 256, None, None) == INVALID
+    assert f(MIS, 0, 32, 256, B, None) == INVALID                  # misaligned source
+    assert f(FAKE, 0, 32, 256, ctypes.c_void_p(0x100800), None) == INVALID   # overlap (4 KiB)
+    assert f(FAKE, 1, 32, 256, ctypes.c_void_p(0x101000), None) == INVALID   # overlap (8 KiB)
+    assert f(FAKE, 0, 0, 256, B, None) == OK                       # empty
 
 
 def test_gemm_and_combine_argument_errors():

@@ -67,8 +67,8 @@ class Layers:
             w2 = torch.empty(c.Ep, c.H, c.I // 2, **u8)
             w2s = torch.empty(c.Ep, c.H, c.I // 32, **u8)
             for e in range(c.Ep):
-                ops().mxfp4_quantize(synth.expert_w13(lc, e, DEV), w13[e], w13s[e])
-                ops().mxfp4_quantize(synth.expert_w2(lc, e, DEV), w2[e], w2s[e])
+                ops().quantize_weights(synth.expert_w13(lc, e, DEV), w13[e], w13s[e])
+                ops().quantize_weights(synth.expert_w2(lc, e, DEV), w2[e], w2s[e])
             self.w.append((synth.router_weight(lc).to(DEV), w13, w13s, w2, w2s))
         torch.cuda.synchronize()
         self._ow = {}

@@ -14,7 +14,8 @@ import torch
 
 import synth
 from oracle import moe, mxfp4, mxfp8
-from tests.helpers import DEV, MAX_ABS_RMS, REL_L2, W_ATOL, bits, max_abs_over_rms, rel_l2
+from tests.helpers import (DEV, MAX_ABS_RMS, REL_L2, W_ATOL, bits, max_abs_over_rms, native_order,
+                           rel_l2)
 
 pytestmark = pytest.mark.gpu
 
@@ -49,8 +50,10 @@ class Problem8:
         self.w2 = torch.empty(c.Ep, c.H, c.I, **u8)
         self.w2s = torch.empty(c.Ep, c.H, c.I // 32, **u8)
         for e in range(c.Ep):
-            ops().mxfp8_quantize(synth.expert_w13(c, e, DEV), self.w13[e], self.w13s[e])
-            ops().mxfp8_quantize(synth.expert_w2(c, e, DEV), self.w2[e], self.w2s[e])
+            ops().quantize_weights(synth.expert_w13(c, e, DEV), self.w13[e], self.w13s[e],
+                                   ops().W_MXFP8)
+            ops().quantize_weights(synth.expert_w2(c, e, DEV), self.w2[e], self.w2s[e],
+                                   ops().W_MXFP8)
         torch.cuda.synchronize()
 
     @functools.lru_cache(maxsize=None)
@@ -149,9 +152,9 @@ def test_mxfp8_layer_small(name):
     c = prob.cfg
     for e in {0, c.Ep - 1}:                    # the two packings agree bit for bit
         w = prob.oracle_weights(e)
-        assert np.array_equal(prob.w13[e].cpu().numpy(), w[0])
+        assert np.array_equal(prob.w13[e].cpu().numpy(), native_order(w[0], 2))
         assert np.array_equal(prob.w13s[e].cpu().numpy(), w[1])
-        assert np.array_equal(prob.w2[e].cpu().numpy(), w[2])
+        assert np.array_equal(prob.w2[e].cpu().numpy(), native_order(w[2], 2))
         assert np.array_equal(prob.w2s[e].cpu().numpy(), w[3])
     r = prob.stages()
     out = prob.forward()

@@ -34,14 +34,25 @@ def _say(*a):
 
 
 def _shard(prob, g, G):
-    """Expert weights of shard g of G: I/G gate rows, I/G up rows, I/G down columns."""
+    """Expert weights of shard g of G: I/G gate rows, I/G up rows, I/G down
+    columns, sliced from the row-major packing of the same draws (the
+    library's quantiser), then put into the native code order."""
+    from mxfp4_routed_expert_top_amd import ops
     c = prob.cfg
     Ig = c.I // G
     rows = torch.cat([torch.arange(g * Ig, (g + 1) * Ig), torch.arange(c.I + g * Ig, c.I + (g + 1) * Ig)]).to(DEV)
-    w13 = prob.w13.index_select(1, rows).contiguous()
-    w13s = prob.w13s.index_select(1, rows).contiguous()
-    w2 = prob.w2[:, :, g * Ig // 2:(g + 1) * Ig // 2].contiguous()
-    w2s = prob.w2s[:, :, g * Ig // 32:(g + 1) * Ig // 32].contiguous()
+    u8 = dict(dtype=torch.uint8, device=DEV)
+    w13 = torch.empty(c.Ep, 2 * Ig, c.H // 2, **u8)
+    w13s = torch.empty(c.Ep, 2 * Ig, c.H // 32, **u8)
+    w2 = torch.empty(c.Ep, c.H, Ig // 2, **u8)
+    w2s = torch.empty(c.Ep, c.H, Ig // 32, **u8)
+    for e in range(c.Ep):
+        q, s = ops.mxfp4_quantize(synth.expert_w13(c, e, DEV))
+        ops.weights_to_native(q.index_select(0, rows).contiguous(), out=w13[e])
+        w13s[e] = s.index_select(0, rows)
+        q, s = ops.mxfp4_quantize(synth.expert_w2(c, e, DEV))
+        ops.weights_to_native(q[:, g * Ig // 2:(g + 1) * Ig // 2].contiguous(), out=w2[e])
+        w2s[e] = s[:, g * Ig // 32:(g + 1) * Ig // 32]
     return w13, w13s, w2, w2s, Ig
 
 

@@ -1,0 +1,60 @@
+"""The native weight-code order (include/moe_mxfp4.h, "Native code order"),
+as the tests' numpy definition (tests/helpers.native_order) writes it,
+against entries worked out by hand from the header's rule: block
+((s*C + c)*NQ + q) holds at byte 16*l (l = 16*g + n) the row-major bytes of
+row 16*s + n starting at NQ*(64*c + 16*g) + 16*q."""
+import numpy as np
+
+from tests.helpers import native_order
+
+
+def _labelled(rows, row_bytes):
+    """Each byte's value encodes where it sat: (row, byte) -> distinct ids."""
+    r, b = np.meshgrid(np.arange(rows), np.arange(row_bytes), indexing="ij")
+    return r * row_bytes + b
+
+
+def _piece(nat, rb, k):
+    """The k-th 16-byte piece of the native array, as (row, first byte) of its source."""
+    flat = nat.reshape(-1)[16 * k:16 * k + 16]
+    assert np.array_equal(np.diff(flat), np.ones(15))     # one contiguous run of a row
+    return divmod(int(flat[0]), rb)
+
+
+def test_mxfp4_one_strip_one_chunk():
+    rb = 64                                    # 128 MXFP4 codes per row: C = 1
+    nat = native_order(_labelled(16, rb), 1)
+    assert _piece(nat, rb, 0) == (0, 0)        # lane 0: n 0, g 0
+    assert _piece(nat, rb, 1) == (1, 0)        # lane 1: n 1, g 0
+    assert _piece(nat, rb, 15) == (15, 0)
+    assert _piece(nat, rb, 16) == (0, 16)      # lane 16: n 0, g 1
+    assert _piece(nat, rb, 63) == (15, 48)     # lane 63: n 15, g 3
+
+
+def test_mxfp4_two_strips_two_chunks():
+    rb = 128                                   # 256 codes per row: C = 2
+    nat = native_order(_labelled(32, rb), 1)
+    assert _piece(nat, rb, 64) == (0, 64)      # block 1 = (s 0, c 1), lane 0
+    assert _piece(nat, rb, 64 + 17) == (1, 80)  # block 1, lane 17: n 1, g 1
+    assert _piece(nat, rb, 128) == (16, 0)     # block 2 = (s 1, c 0), lane 0
+    assert _piece(nat, rb, 3 * 64 + 63) == (31, 112)   # block 3 = (s 1, c 1), lane 63
+
+
+def test_mxfp8_parts():
+    rb = 256                                   # 256 E4M3 codes per row: C = 2, NQ = 2
+    nat = native_order(_labelled(16, rb), 2)
+    assert _piece(nat, rb, 0) == (0, 0)        # block 0 = (c 0, q 0), lane 0
+    assert _piece(nat, rb, 64) == (0, 16)      # block 1 = (c 0, q 1), lane 0
+    assert _piece(nat, rb, 16) == (0, 32)      # block 0, lane 16: g 1 -> byte 2*16
+    assert _piece(nat, rb, 2 * 64 + 5) == (5, 128)     # block 2 = (c 1, q 0), lane 5
+    assert _piece(nat, rb, 3 * 64 + 50) == (2, 128 + 96 + 16)   # block 3 (c 1, q 1), lane 50: n 2, g 3
+
+
+def test_is_a_permutation_of_pieces_and_keeps_experts_in_place():
+    rng = np.random.default_rng(3)
+    codes = rng.integers(0, 256, size=(3 * 32, 192), dtype=np.uint8)   # 3 experts x 32 rows
+    nat = native_order(codes, 1)
+    assert nat.shape == codes.shape
+    assert sorted(map(bytes, codes.reshape(-1, 16))) == sorted(map(bytes, nat.reshape(-1, 16)))
+    for e in range(3):          # converting the stack = converting each expert on its own
+        assert np.array_equal(nat[32 * e:32 * e + 32], native_order(codes[32 * e:32 * e + 32], 1))
