@@ -320,8 +320,9 @@ MOE_API moe_status moe_mxfp8_expert_down(const uint16_t *h, const int32_t *exper
                                  uint16_t *y, void *stream);
 
 /* The tile_m moe_mxfp4_forward uses for these shapes and activation format
- * (A = T*Kp assignments over Ep experts): 32, 64, 128 or (MXFP4
- * activations) 256 (see moe_expert_gate_up). */
+ * (A = T*Kp assignments over Ep experts): 32, 64 or 128 (see
+ * moe_expert_gate_up; 256-row tiles are used only when a caller of the
+ * per-step entry points asks for them). */
 MOE_API int32_t moe_gemm_tile_m(int32_t T, int32_t Kp, int32_t Ep, int32_t H, int32_t I,
                                 int32_t act_fmt);
 
@@ -334,9 +335,8 @@ MOE_API size_t moe_mxfp4_workspace_size(int32_t T, int32_t H, int32_t I, int32_t
  * [quantise h], down, combine, all enqueued on `stream`.  The GEMM kernels
  * are chosen on the host from the shapes alone (no device read): average
  * rows per expert T*K'/E' <= 8 -> 32-row weight-streaming tiles, <= 48 ->
- * 64-row LDS-tiled, else 128-row LDS-tiled, and for MXFP4 activations
- * above 128 -> 256-row LDS-tiled (when the shapes fit the tiled kernels,
- * see moe_expert_gate_up; otherwise 32).
+ * 64-row LDS-tiled, else 128-row LDS-tiled (when the shapes fit the tiled
+ * kernels, see moe_expert_gate_up; otherwise 32).
  *   x              bf16 [T, H]
  *   router_logits  fp32 [T, E];  shared_gate_logits fp32 [T] (shared = 1) or NULL
  *   w13, w13_scale, w2, w2_scale: the MXFP4 weights of E + shared experts

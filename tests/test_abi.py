@@ -165,8 +165,8 @@ def test_gemm_tile_choice():
     assert ops.gemm_tile_m(8192, 11, 513, 4096, 1024) == 128
     assert ops.gemm_tile_m(8192, 11, 513, 384, 1024) == 32      # H % 256 != 0
     # the tiled kernels keep a workgroup's weight scales for the whole K in LDS
-    # MXFP4 activations: groups above 128 rows take 256-row tiles where K fits (<= 6144)
-    assert ops.gemm_tile_m(4096, 9, 257, 6144, 1536, ops.ACT_MXFP4) == 256
+    # MXFP4 activations: 128-row tiles above 48 rows (256-row tiles only on request)
+    assert ops.gemm_tile_m(4096, 9, 257, 6144, 1536, ops.ACT_MXFP4) == 128
     assert ops.gemm_tile_m(2048, 9, 257, 6144, 1536, ops.ACT_MXFP4) == 128
     assert ops.gemm_tile_m(4096, 9, 257, 8192, 1536, ops.ACT_MXFP4) == 128
     assert ops.gemm_tile_m(4096, 9, 257, 6144, 1536, ops.ACT_BF16) == 32
