@@ -207,6 +207,32 @@ def test_mxfp8_layer_full_size_decode_sampled():
     assert torch.isfinite(out.float()).all()
 
 
+def test_mxfp8_layer_full_size_prefill_sampled():
+    """The MXFP8 prefill workload (T=1536, 64-row LDS-tiled kernels) in the
+    launch configuration the bench times: routing bit-exact for every token,
+    sampled tokens against the oracle."""
+    cfg = synth.CONFIGS["prefill_mxfp8"]
+    _say("mxfp8 full prefill", cfg.T, "tile_m",
+         ops().mxfp8_gemm_tile_m(cfg.T, cfg.Kp, cfg.Ep, cfg.H, cfg.I))
+    prob = Problem8(cfg)
+    ids = torch.empty(cfg.T, cfg.Kp, dtype=torch.int32, device=DEV)
+    w = torch.empty(cfg.T, cfg.Kp, dtype=torch.float32, device=DEV)
+    out = prob.forward(topk_ids=ids, topk_weights=w)
+    torch.cuda.synchronize()
+    _say("  forward done")
+    tokens = np.sort(np.random.default_rng(cfg.seed_act).choice(cfg.T, size=2, replace=False))
+    want = prob.oracle(tokens=tokens)
+    _say("  oracle done for tokens", tokens.tolist())
+    assert np.array_equal(ids.cpu().numpy(), want["ids"])
+    assert np.max(np.abs(w.cpu().numpy() - want["w"])) <= W_ATOL
+    got = bits(out)[tokens]
+    e_rel = rel_l2(got, want["out"])
+    e_max = max_abs_over_rms(got, want["out"])
+    _say(f"  prefill mxfp8: rel_l2 {e_rel:.2e}  max_abs/rms {e_max:.2e}")
+    assert e_rel <= TOL and e_max <= MAX_ABS_RMS
+    assert torch.isfinite(out.float()).all()
+
+
 @pytest.mark.parametrize("tile_m", [32, 64, 128])
 def test_mxfp8_gemm_kernels_for_every_tile_size(tile_m):
     """The MXFP8 per-step entry points with each tile size against the oracle."""

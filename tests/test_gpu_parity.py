@@ -165,6 +165,22 @@ def test_align_sort(name):
     _check_align(got, moe.align(ids.numpy(), Ep, 32))
 
 
+@pytest.mark.parametrize("name", ["prefill", "prefill_skewed", "w4a4", "prefill_mxfp8"])
+def test_align_sort_with_the_forwards_tile_size(name):
+    """The grouping tables at full size with the tile rows the forward picks
+    for the workload (64 or 128), bit-exact against the oracle's."""
+    cfg = synth.CONFIGS[name]
+    o = ops()
+    tile_m = (o.mxfp8_gemm_tile_m if cfg.wfmt == synth.W_MXFP8 else
+              lambda *a: o.gemm_tile_m(*a, cfg.act_fmt))(cfg.T, cfg.Kp, cfg.Ep, cfg.H, cfg.I)
+    _say("align", name, "tile_m", tile_m)
+    assert tile_m in (64, 128)
+    ids = torch.from_numpy(moe.route(synth.router_logits(cfg).numpy(),
+                                     synth.gate_logits(cfg).numpy(), cfg.K, cfg.shared)[0])
+    got = ops().align_sort(ids.to(DEV), cfg.Ep, tile_m=tile_m)
+    _check_align(got, moe.align(ids.numpy(), cfg.Ep, tile_m))
+
+
 def test_align_empty():
     ids = torch.empty(0, 3, dtype=torch.int32, device=DEV)
     got = ops().align_sort(ids, 5)
