@@ -334,9 +334,10 @@ MOE_API size_t moe_mxfp4_workspace_size(int32_t T, int32_t H, int32_t I, int32_t
  * The whole layer in one call: route, align, [quantise x], gate/up + SwiGLU,
  * [quantise h], down, combine, all enqueued on `stream`.  The GEMM kernels
  * are chosen on the host from the shapes alone (no device read): average
- * rows per expert T*K'/E' <= 8 -> 32-row weight-streaming tiles, <= 48 ->
- * 64-row LDS-tiled, else 128-row LDS-tiled (when the shapes fit the tiled
- * kernels, see moe_expert_gate_up; otherwise 32).
+ * rows per expert T*K'/E' <= 8 -> 32-row weight-streaming tiles, else
+ * 64-row LDS-tiled tiles (bf16 activations; MXFP4 activations: 64 up to 48
+ * rows, 128 above) when the shapes fit the tiled kernels (see
+ * moe_expert_gate_up; otherwise 32).
  *   x              bf16 [T, H]
  *   router_logits  fp32 [T, E];  shared_gate_logits fp32 [T] (shared = 1) or NULL
  *   w13, w13_scale, w2, w2_scale: the MXFP4 weights of E + shared experts
@@ -411,8 +412,9 @@ MOE_API moe_status moe_mxfp4_forward_layers(const uint16_t *x, int32_t L,
                                             int32_t act_fmt, int32_t prefetch, uint16_t *out,
                                             void *workspace, size_t workspace_bytes, void *stream);
 
-/* The tile_m moe_mxfp8_forward uses for these shapes: 32, 64 or 128, by the
- * rule of moe_mxfp4_forward with bf16 activations. */
+/* The tile_m moe_mxfp8_forward uses for these shapes: 32 or 64, by the rule
+ * of moe_mxfp4_forward with bf16 activations (128-row tiles only when a
+ * caller of the per-step entry points asks for them). */
 MOE_API int32_t moe_mxfp8_gemm_tile_m(int32_t T, int32_t Kp, int32_t Ep, int32_t H, int32_t I);
 
 /* Workspace bytes moe_mxfp8_forward needs (0 for T = 0). */

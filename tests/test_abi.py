@@ -162,7 +162,7 @@ def test_gemm_tile_choice():
     # decode-like groups stream weights; larger groups use the LDS-tiled kernels
     assert ops.gemm_tile_m(64, 11, 513, 4096, 1024) == 32
     assert ops.gemm_tile_m(1536, 11, 513, 4096, 1024) == 64
-    assert ops.gemm_tile_m(8192, 11, 513, 4096, 1024) == 128
+    assert ops.gemm_tile_m(8192, 11, 513, 4096, 1024) == 64     # bf16: two workgroups per CU
     assert ops.gemm_tile_m(8192, 11, 513, 384, 1024) == 32      # H % 256 != 0
     # the tiled kernels keep a workgroup's weight scales for the whole K in LDS
     # MXFP4 activations: 128-row tiles above 48 rows (256-row tiles only on request)
@@ -240,7 +240,7 @@ def test_mxfp8_argument_errors():
     assert call(dn, based, a4=256) == UNSUPPORTED
     assert ops.mxfp8_gemm_tile_m(64, 11, 513, 4096, 1024) == 32
     assert ops.mxfp8_gemm_tile_m(1536, 11, 513, 4096, 1024) == 64
-    assert ops.mxfp8_gemm_tile_m(8192, 11, 513, 4096, 1024) == 128
+    assert ops.mxfp8_gemm_tile_m(8192, 11, 513, 4096, 1024) == 64
     assert ops.mxfp8_gemm_tile_m(8192, 11, 513, 4096, 4608) == 32   # I above the tiled limit
     assert call(dn, based, a12=None) == INVALID
     assert call(dn, based, a5=MIS) == INVALID
