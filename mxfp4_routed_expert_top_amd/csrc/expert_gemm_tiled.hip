@@ -84,17 +84,25 @@ unsigned tile_slice_grid(int max_tiles, int nslices) {
 // weight rows x KMAX/32 bytes, plus the tile's activation rows for MXFP4).
 // Totals: bf16 128-row 160 KiB (one workgroup per CU), bf16 64-row 80 KiB
 // (two per CU), MXFP4 256-row 145 KiB (three stages), MXFP4 128-row
-// 128 KiB, MXFP4 64-row 76 KiB (two per CU).  256-row tiles exist for MXFP4
+// 128 KiB (48.5 KiB for reductions up to 2048: two per CU), MXFP4 64-row
+// 76 KiB (two per CU).  256-row tiles exist for MXFP4
 // activations only: an expert of the W4A4 batch (~143 rows) then streams its
 // weights once instead of once per 128-row tile.
-template <int BM, bool kFP4A, bool kW8 = false>
+template <int BM, bool kFP4A, bool kW8 = false, bool kSK = false>
 struct TileCfg {
   static_assert(BM == 64 || BM == 128 || (BM == 256 && kFP4A), "tile sizes");
   static_assert(!(kW8 && kFP4A), "MXFP8 weights take bf16 activations");
   // (MXFP8 weights: twice the weight registers per stage, so 128-row tiles
   // keep three stages in flight instead of four)
-  static constexpr int NS = ((BM == 64 && !kFP4A) || BM == 256 || (kW8 && BM == 128)) ? 3 : 4;
-  static constexpr int KMAX = kFP4A ? (BM == 128 ? 8192 : 6144) : 4096;
+  // kSK (MXFP4 activations, 128-row tiles): a reduction of at most 2048
+  // (e.g. the down GEMM of the W4A4 layer, I = 1536): the scale arrays
+  // shrink and the pipeline keeps three stages, so that the kernel fits two
+  // workgroups per CU (48.5 KiB of LDS, under 256 VGPRs): W4A4 down
+  // 0.476 -> 0.409 ms
+  static_assert(!kSK || (kFP4A && BM == 128), "small-K variant: MXFP4 128-row tiles");
+  static constexpr int NS =
+      ((BM == 64 && !kFP4A) || BM == 256 || (kW8 && BM == 128) || (kSK && BM == 128)) ? 3 : 4;
+  static constexpr int KMAX = kSK ? 2048 : kFP4A ? (BM == 128 ? 8192 : 6144) : 4096;
   static constexpr int SCB = 256 * (KMAX / 32);             // weight scales
   // MXFP4 activation scales of the tile's rows (whole K), BM/4 rows per wave
   static constexpr int ASB = kFP4A ? 4 * ((BM / 4 * (KMAX / 128) + 63) / 64) * 256 : 0;
@@ -156,10 +164,10 @@ __device__ __forceinline__ void load_to_lds4(rsrc_t r, uint32_t voff, uint32_t s
 // past the last chunk use an out-of-range offset: they move no data and
 // every wave issues the same number of loads per stage, so the wait counts
 // are constants.  MFMAs run only on the tile's live 16-row sub-tiles.
-template <int BM, bool kFP4A, bool kW8 = false>
+template <int BM, bool kFP4A, bool kW8 = false, bool kSK = false>
 struct TiledGemm {
-  static constexpr int NS = TileCfg<BM, kFP4A, kW8>::NS;
-  static constexpr int XB = TileCfg<BM, kFP4A, kW8>::XB;
+  static constexpr int NS = TileCfg<BM, kFP4A, kW8, kSK>::NS;
+  static constexpr int XB = TileCfg<BM, kFP4A, kW8, kSK>::XB;
   static constexpr int MT = BM / 16;
   static constexpr int XI = kFP4A ? BM / 64 : BM / 16;   // code / row loads per wave per stage
   // weight registers per strip and stage: 16 bytes (32 E2M1 codes) or 32 (32 E4M3 codes)
@@ -351,8 +359,8 @@ __device__ __forceinline__ TileT tile_of(const int32_t* tiles, const int32_t* of
 
 // The lane's activation source offsets for every stage: row r of the tile
 // comes from source row src(r) (a token for gate/up, a sorted row for down).
-template <int BM, bool kFP4A, bool kW8, class SrcFn>
-__device__ __forceinline__ void plan_x(TiledGemm<BM, kFP4A, kW8>& G, const TileT& ti, SrcFn src,
+template <int BM, bool kFP4A, bool kW8, bool kSK, class SrcFn>
+__device__ __forceinline__ void plan_x(TiledGemm<BM, kFP4A, kW8, kSK>& G, const TileT& ti, SrcFn src,
                                        uint32_t row_bytes) {
 #pragma unroll
   for (int i = 0; i < G.XI; ++i) {
@@ -373,8 +381,8 @@ __device__ __forceinline__ void plan_x(TiledGemm<BM, kFP4A, kW8>& G, const TileT
 
 // Common set-up of a workgroup's GEMM state (weights of one expert slice;
 // K = reduction length; rs = K/32 scale bytes per weight row).
-template <int BM, bool kFP4A, bool kW8>
-__device__ __forceinline__ void setup(TiledGemm<BM, kFP4A, kW8>& G, const TileT& ti, int K,
+template <int BM, bool kFP4A, bool kW8, bool kSK>
+__device__ __forceinline__ void setup(TiledGemm<BM, kFP4A, kW8, kSK>& G, const TileT& ti, int K,
                                       const uint8_t* wq, const uint8_t* wsc, int wrows) {
   G.lane = threadIdx.x & 63;
   G.wave = threadIdx.x >> 6;
@@ -423,31 +431,32 @@ __device__ __forceinline__ void with_nmt(int rows, F&& f) {
 // Static LDS of a kernel: NS stage arrays (separate objects), the weight
 // scales, and for MXFP4 activations their scales and the tile's source
 // rows; body(stages, scales, act_scales, src_rows) runs with them.
-template <int BM, bool kFP4A, bool kW8, class Body>
+template <int BM, bool kFP4A, bool kW8, bool kSK, class Body>
 __device__ __forceinline__ void with_lds(Body&& body) {
-  constexpr int XB = TileCfg<BM, kFP4A, kW8>::XB, SCB = TileCfg<BM, kFP4A, kW8>::SCB;
+  using Cfg = TileCfg<BM, kFP4A, kW8, kSK>;
+  constexpr int XB = Cfg::XB, SCB = Cfg::SCB;
   __shared__ __align__(16) uint8_t sc[SCB];
   __shared__ __align__(16) uint8_t st0[XB];
   __shared__ __align__(16) uint8_t st1[XB];
   __shared__ __align__(16) uint8_t st2[XB];
-  if constexpr (kFP4A && TileCfg<BM, kFP4A, kW8>::NS == 4) {
+  if constexpr (kFP4A && Cfg::NS == 4) {
     __shared__ __align__(16) uint8_t st3[XB];
-    __shared__ __align__(16) uint8_t asc[TileCfg<BM, kFP4A, kW8>::ASB];
+    __shared__ __align__(16) uint8_t asc[Cfg::ASB];
     __shared__ int32_t srow[BM];
     uint8_t* const stages[4] = {st0, st1, st2, st3};
     body(stages, sc, asc, srow);
   } else if constexpr (kFP4A) {
-    static_assert(TileCfg<BM, kFP4A, kW8>::NS == 3, "three or four stages");
-    __shared__ __align__(16) uint8_t asc[TileCfg<BM, kFP4A, kW8>::ASB];
+    static_assert(Cfg::NS == 3, "three or four stages");
+    __shared__ __align__(16) uint8_t asc[Cfg::ASB];
     __shared__ int32_t srow[BM];
     uint8_t* const stages[3] = {st0, st1, st2};
     body(stages, sc, asc, srow);
-  } else if constexpr (TileCfg<BM, kFP4A, kW8>::NS == 4) {
+  } else if constexpr (Cfg::NS == 4) {
     __shared__ __align__(16) uint8_t st3[XB];
     uint8_t* const stages[4] = {st0, st1, st2, st3};
     body(stages, sc, (uint8_t*)nullptr, (int32_t*)nullptr);
   } else {
-    static_assert(TileCfg<BM, kFP4A, kW8>::NS == 3, "three or four stages");
+    static_assert(Cfg::NS == 3, "three or four stages");
     uint8_t* const stages[3] = {st0, st1, st2};
     body(stages, sc, (uint8_t*)nullptr, (int32_t*)nullptr);
   }
@@ -457,16 +466,16 @@ __device__ __forceinline__ void with_lds(Body&& body) {
 // activation-code offsets and the activation-scale rows), then the pipeline.
 // direct(r) = source row of tile row r < rows; wrow(r) = byte offset of
 // weight scale row r; arow_bytes = activation scale bytes per source row.
-template <int BM, bool kFP4A, bool kW8, class Direct, class WRow>
-__device__ __forceinline__ void tile_loop(TiledGemm<BM, kFP4A, kW8>& G, const TileT& ti, Direct direct,
+template <int BM, bool kFP4A, bool kW8, bool kSK, class Direct, class WRow>
+__device__ __forceinline__ void tile_loop(TiledGemm<BM, kFP4A, kW8, kSK>& G, const TileT& ti, Direct direct,
                                           WRow wrow, uint32_t row_bytes, uint32_t arow_bytes,
                                           floatx4_t (&acc)[BM / 16][4]) {
-  with_lds<BM, kFP4A, kW8>([&](auto& stages, uint8_t* sc, uint8_t* asc, int32_t* srow) {
+  with_lds<BM, kFP4A, kW8, kSK>([&](auto& stages, uint8_t* sc, uint8_t* asc, int32_t* srow) {
     if constexpr (kFP4A) {
       const int t = threadIdx.x;
       if (t < BM) srow[t] = t < ti.rows ? (int32_t)direct(t) : 0;
       __syncthreads();
-      plan_x<BM, kFP4A, kW8>(G, ti, [&](int r) { return (uint32_t)srow[r]; }, row_bytes);
+      plan_x<BM, kFP4A, kW8, kSK>(G, ti, [&](int r) { return (uint32_t)srow[r]; }, row_bytes);
       auto arow = [&](int r) -> uint32_t {
         return r < ti.rows ? (uint32_t)srow[r] * arow_bytes : kOOR;
       };
@@ -474,7 +483,7 @@ __device__ __forceinline__ void tile_loop(TiledGemm<BM, kFP4A, kW8>& G, const Ti
         G.template run<decltype(n)::value>(stages, sc, asc, wrow, arow, acc);
       });
     } else {
-      plan_x<BM, kFP4A, kW8>(G, ti, direct, row_bytes);
+      plan_x<BM, kFP4A, kW8, kSK>(G, ti, direct, row_bytes);
       auto arow = [](int) -> uint32_t { return kOOR; };
       with_nmt<BM>(ti.rows, [&](auto n) {
         G.template run<decltype(n)::value>(stages, sc, asc, wrow, arow, acc);
@@ -485,8 +494,8 @@ __device__ __forceinline__ void tile_loop(TiledGemm<BM, kFP4A, kW8>& G, const Ti
 
 // gate/up + SwiGLU: weight rows gate [i0, i0 + 128) and up [I + i0, I + i0 + 128),
 // i0 = 128 s; wave w owns i in [i0 + 32 w, i0 + 32 w + 32): strips gate lo/hi, up lo/hi.
-template <int BM, bool kFP4A, bool kW8>
-__global__ __launch_bounds__(256) void gate_up_tiled_kernel(
+template <int BM, bool kFP4A, bool kW8, bool kSK = false>
+__global__ __launch_bounds__(256, kSK ? 2 : 1) void gate_up_tiled_kernel(
     const void* __restrict__ act, const uint8_t* __restrict__ act_scale,
     const int32_t* __restrict__ sorted, const int32_t* __restrict__ offsets,
     const int32_t* __restrict__ tiles, const int32_t* __restrict__ num_tiles,
@@ -495,7 +504,7 @@ __global__ __launch_bounds__(256) void gate_up_tiled_kernel(
   int tile, s;
   if (!tile_slice<kFP4A>(blockIdx.x, *num_tiles, I / 128, &tile, &s)) return;
   const TileT ti = tile_of<BM>(tiles, offsets, tile);
-  TiledGemm<BM, kFP4A, kW8> G;
+  TiledGemm<BM, kFP4A, kW8, kSK> G;
   setup(G, ti, H, w13, w13s, 2 * I);
   const int nl = G.nl, g = G.g;
   const uint32_t rb = H / 2, rs = H / 32;
@@ -523,7 +532,7 @@ __global__ __launch_bounds__(256) void gate_up_tiled_kernel(
   for (int mt = 0; mt < BM / 16; ++mt)
 #pragma unroll
     for (int st = 0; st < 4; ++st) acc[mt][st] = (floatx4_t){0.f, 0.f, 0.f, 0.f};
-  tile_loop<BM, kFP4A, kW8>(G, ti, token, wrow, kFP4A ? rb : (uint32_t)H * 2, rs, acc);
+  tile_loop<BM, kFP4A, kW8, kSK>(G, ti, token, wrow, kFP4A ? rb : (uint32_t)H * 2, rs, acc);
 
 #pragma unroll
   for (int mt = 0; mt < BM / 16; ++mt)
@@ -539,8 +548,8 @@ __global__ __launch_bounds__(256) void gate_up_tiled_kernel(
 }
 
 // down: weight rows j in [256 s, 256 s + 256); wave w owns [256 s + 64 w, +64).
-template <int BM, bool kFP4A, bool kW8>
-__global__ __launch_bounds__(256) void down_tiled_kernel(
+template <int BM, bool kFP4A, bool kW8, bool kSK = false>
+__global__ __launch_bounds__(256, kSK ? 2 : 1) void down_tiled_kernel(
     const void* __restrict__ hin, const uint8_t* __restrict__ hscale,
     const int32_t* __restrict__ offsets, const int32_t* __restrict__ tiles,
     const int32_t* __restrict__ num_tiles, const uint8_t* __restrict__ w2,
@@ -548,7 +557,7 @@ __global__ __launch_bounds__(256) void down_tiled_kernel(
   int tile, s;
   if (!tile_slice<kFP4A>(blockIdx.x, *num_tiles, H / 256, &tile, &s)) return;
   const TileT ti = tile_of<BM>(tiles, offsets, tile);
-  TiledGemm<BM, kFP4A, kW8> G;
+  TiledGemm<BM, kFP4A, kW8, kSK> G;
   setup(G, ti, I, w2, w2s, H);
   const int nl = G.nl, g = G.g;
   const uint32_t rb = I / 2, rs = I / 32;
@@ -569,7 +578,7 @@ __global__ __launch_bounds__(256) void down_tiled_kernel(
   for (int mt = 0; mt < BM / 16; ++mt)
 #pragma unroll
     for (int st = 0; st < 4; ++st) acc[mt][st] = (floatx4_t){0.f, 0.f, 0.f, 0.f};
-  tile_loop<BM, kFP4A, kW8>(G, ti, srow, wrow, kFP4A ? rb : (uint32_t)I * 2, rs, acc);
+  tile_loop<BM, kFP4A, kW8, kSK>(G, ti, srow, wrow, kFP4A ? rb : (uint32_t)I * 2, rs, acc);
 
 #pragma unroll
   for (int mt = 0; mt < BM / 16; ++mt)
@@ -584,25 +593,25 @@ __global__ __launch_bounds__(256) void down_tiled_kernel(
     }
 }
 
-template <int BM, bool kFP4A, bool kW8 = false>
+template <int BM, bool kFP4A, bool kW8 = false, bool kSK = false>
 hipError_t launch_gate_up_bm(const void* act, const uint8_t* act_scale, const int32_t* sorted,
                              const int32_t* offsets, const int32_t* tiles,
                              const int32_t* num_tiles, int max_tiles, const uint8_t* w13,
                              const uint8_t* w13s, int T, int H, int I, int Kp, uint16_t* h,
                              hipStream_t stream) {
   const unsigned grid = tile_slice_grid<kFP4A>(max_tiles, I / 128);
-  hipLaunchKernelGGL((gate_up_tiled_kernel<BM, kFP4A, kW8>), dim3(grid), dim3(256), 0, stream, act,
+  hipLaunchKernelGGL((gate_up_tiled_kernel<BM, kFP4A, kW8, kSK>), dim3(grid), dim3(256), 0, stream, act,
                      act_scale, sorted, offsets, tiles, num_tiles, w13, w13s, T, H, I, Kp, h);
   return hipGetLastError();
 }
 
-template <int BM, bool kFP4A, bool kW8 = false>
+template <int BM, bool kFP4A, bool kW8 = false, bool kSK = false>
 hipError_t launch_down_bm(const void* h, const uint8_t* h_scale, const int32_t* offsets,
                           const int32_t* tiles, const int32_t* num_tiles, int max_tiles,
                           const uint8_t* w2, const uint8_t* w2s, int A, int H, int I, uint16_t* y,
                           hipStream_t stream) {
   const unsigned grid = tile_slice_grid<kFP4A>(max_tiles, H / 256);
-  hipLaunchKernelGGL((down_tiled_kernel<BM, kFP4A, kW8>), dim3(grid), dim3(256), 0, stream, h,
+  hipLaunchKernelGGL((down_tiled_kernel<BM, kFP4A, kW8, kSK>), dim3(grid), dim3(256), 0, stream, h,
                      h_scale, offsets, tiles, num_tiles, w2, w2s, A, H, I, y);
   return hipGetLastError();
 }
@@ -643,9 +652,12 @@ hipError_t launch_gate_up_tiled(int tile_m, int act_fmt, int wfmt, const void* a
     return launch_gate_up_bm<256, true>(act, act_scale, sorted, offsets, tiles, num_tiles,
                                         max_tiles, w13, w13s, T, H, I, Kp, h, stream);
   if (tile_m == 128)
-    return act_fmt ? launch_gate_up_bm<128, true>(act, act_scale, sorted, offsets, tiles,
-                                                   num_tiles, max_tiles, w13, w13s, T, H, I, Kp,
-                                                   h, stream)
+    return act_fmt ? (H <= 2048 ? launch_gate_up_bm<128, true, false, true>(
+                                      act, act_scale, sorted, offsets, tiles, num_tiles,
+                                      max_tiles, w13, w13s, T, H, I, Kp, h, stream)
+                                : launch_gate_up_bm<128, true>(act, act_scale, sorted, offsets,
+                                                               tiles, num_tiles, max_tiles, w13,
+                                                               w13s, T, H, I, Kp, h, stream))
                    : launch_gate_up_bm<128, false>(act, act_scale, sorted, offsets, tiles,
                                                     num_tiles, max_tiles, w13, w13s, T, H, I, Kp,
                                                     h, stream);
@@ -670,8 +682,11 @@ hipError_t launch_down_tiled(int tile_m, int act_fmt, int wfmt, const void* h,
     return launch_down_bm<256, true>(h, h_scale, offsets, tiles, num_tiles, max_tiles, w2, w2s, A,
                                      H, I, y, stream);
   if (tile_m == 128)
-    return act_fmt ? launch_down_bm<128, true>(h, h_scale, offsets, tiles, num_tiles, max_tiles,
-                                                w2, w2s, A, H, I, y, stream)
+    return act_fmt ? (I <= 2048 ? launch_down_bm<128, true, false, true>(h, h_scale, offsets, tiles,
+                                                                         num_tiles, max_tiles, w2,
+                                                                         w2s, A, H, I, y, stream)
+                                : launch_down_bm<128, true>(h, h_scale, offsets, tiles, num_tiles,
+                                                            max_tiles, w2, w2s, A, H, I, y, stream))
                    : launch_down_bm<128, false>(h, h_scale, offsets, tiles, num_tiles, max_tiles,
                                                  w2, w2s, A, H, I, y, stream);
   return act_fmt ? launch_down_bm<64, true>(h, h_scale, offsets, tiles, num_tiles, max_tiles, w2,
