@@ -100,9 +100,11 @@ def gate_up_kernel_name(cfg, tile_m):
     a = "true" if cfg.act_fmt else "false"
     w8 = "true" if cfg.wfmt == synth.W_MXFP8 else "false"
     if tile_m != 32:
-        # the small-reduction variant of the MXFP4-activation 128-row kernel
-        sk = "true" if (cfg.act_fmt and tile_m == 128 and cfg.H <= 2048) else "false"
-        return f"gate_up_tiled_kernel<{tile_m}, {a}, {w8}, {sk}>"
+        # variants of the MXFP4-activation 128-row kernel by reduction length
+        kv = 0
+        if cfg.act_fmt and tile_m == 128:
+            kv = 1 if cfg.H <= 2048 else 2 if cfg.H <= 6144 else 0
+        return f"gate_up_tiled_kernel<{tile_m}, {a}, {w8}, {kv}>"
     if cfg.wfmt == synth.W_MXFP8:
         return "gate_up_kernel<1, false, true>"
     ph = 2 if (cfg.H // 128) % 2 == 0 else 1          # phase width of the 32-row kernel

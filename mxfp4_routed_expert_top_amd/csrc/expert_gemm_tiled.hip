@@ -88,24 +88,30 @@ unsigned tile_slice_grid(int max_tiles, int nslices) {
 // 76 KiB (two per CU).  256-row tiles exist for MXFP4
 // activations only: an expert of the W4A4 batch (~143 rows) then streams its
 // weights once instead of once per 128-row tile.
-template <int BM, bool kFP4A, bool kW8 = false, bool kSK = false>
+template <int BM, bool kFP4A, bool kW8 = false, int KV = 0>
 struct TileCfg {
   static_assert(BM == 64 || BM == 128 || (BM == 256 && kFP4A), "tile sizes");
   static_assert(!(kW8 && kFP4A), "MXFP8 weights take bf16 activations");
   // (MXFP8 weights: twice the weight registers per stage, so 128-row tiles
   // keep three stages in flight instead of four)
-  // kSK (MXFP4 activations, 128-row tiles): a reduction of at most 2048
-  // (e.g. the down GEMM of the W4A4 layer, I = 1536): the scale arrays
-  // shrink and the pipeline keeps three stages, so that the kernel fits two
-  // workgroups per CU (48.5 KiB of LDS, under 256 VGPRs): W4A4 down
-  // 0.476 -> 0.409 ms
-  static_assert(!kSK || (kFP4A && BM == 128), "small-K variant: MXFP4 128-row tiles");
+  // KV (MXFP4 activations, 128-row tiles only) picks a variant that fits two
+  // workgroups per CU (three stages, under 256 VGPRs):
+  //   1: reductions up to 2048 (the W4A4 layer's down GEMM, I = 1536): the
+  //      scale arrays shrink (48.5 KiB of LDS); W4A4 down 0.476 -> 0.409 ms
+  //   2: reductions up to 6144 (its gate/up, H = 6144): the activation
+  //      scales come with each stage (4 bytes per row) instead of for the
+  //      whole K, leaving the weight scales' 48 KiB (74 KiB of LDS)
+  static_assert(KV == 0 || (kFP4A && BM == 128), "variants: MXFP4 128-row tiles");
   static constexpr int NS =
-      ((BM == 64 && !kFP4A) || BM == 256 || (kW8 && BM == 128) || (kSK && BM == 128)) ? 3 : 4;
-  static constexpr int KMAX = kSK ? 2048 : kFP4A ? (BM == 128 ? 8192 : 6144) : 4096;
+      ((BM == 64 && !kFP4A) || BM == 256 || (kW8 && BM == 128) || (KV && BM == 128)) ? 3 : 4;
+  static constexpr int KMAX =
+      KV == 1 ? 2048 : KV == 2 ? 6144 : kFP4A ? (BM == 128 ? 8192 : 6144) : 4096;
   static constexpr int SCB = 256 * (KMAX / 32);             // weight scales
   // MXFP4 activation scales of the tile's rows (whole K), BM/4 rows per wave
-  static constexpr int ASB = kFP4A ? 4 * ((BM / 4 * (KMAX / 128) + 63) / 64) * 256 : 0;
+  // (KV 2: NS stage slots of BM rows x 4 bytes, plus 256 bytes the waves
+  // that load no scales write their zeros to)
+  static constexpr int ASB = KV == 2 ? NS * BM * 4 + 256
+                             : kFP4A ? 4 * ((BM / 4 * (KMAX / 128) + 63) / 64) * 256 : 0;
   // activation bytes per stage:
   //   bf16:  256 bytes per row, 16-byte slot p of row r holds piece p ^ (r & 15)
   //   MXFP4: 64 bytes of codes per row, slot p holds piece p ^ ((r >> 2) & 3)
@@ -164,20 +170,22 @@ __device__ __forceinline__ void load_to_lds4(rsrc_t r, uint32_t voff, uint32_t s
 // past the last chunk use an out-of-range offset: they move no data and
 // every wave issues the same number of loads per stage, so the wait counts
 // are constants.  MFMAs run only on the tile's live 16-row sub-tiles.
-template <int BM, bool kFP4A, bool kW8 = false, bool kSK = false>
+template <int BM, bool kFP4A, bool kW8 = false, int KV = 0>
 struct TiledGemm {
-  static constexpr int NS = TileCfg<BM, kFP4A, kW8, kSK>::NS;
-  static constexpr int XB = TileCfg<BM, kFP4A, kW8, kSK>::XB;
+  static constexpr int NS = TileCfg<BM, kFP4A, kW8, KV>::NS;
+  static constexpr int XB = TileCfg<BM, kFP4A, kW8, KV>::XB;
   static constexpr int MT = BM / 16;
   static constexpr int XI = kFP4A ? BM / 64 : BM / 16;   // code / row loads per wave per stage
   // weight registers per strip and stage: 16 bytes (32 E2M1 codes) or 32 (32 E4M3 codes)
   static constexpr int NQ = kW8 ? 2 : 1;
-  static constexpr int LPS = XI + 4 * NQ;                  // vmem ops per wave per stage
+  static constexpr bool kAS = KV == 2;                    // activation scales per stage
+  static constexpr int LPS = XI + 4 * NQ + (kAS ? 1 : 0);  // vmem ops per wave per stage
 
   rsrc_t w, ws, a, as;
   uint32_t wo[4];               // lane's offsets in its four weight strips (native code order)
   uint32_t xo[XI];              // lane's activation source offsets (or kOOR)
   uint32_t sro;                 // lane's scale byte offset in LDS for strip 0 (row 64 wave + nl, + g)
+  uint32_t aso;                 // (kAS) lane's activation scale row offset, or kOOR
   int wave, lane, nl, g, nch, Q, swz;
 
   // Scale rows (Q dwords each, whole K) into LDS: wave w fills rows
@@ -214,10 +222,13 @@ struct TiledGemm {
 
   // Issue chunk c into a stage (weight codes into registers q: strip t's
   // 16-byte pieces at q[NQ t .. NQ t + NQ)).
-  __device__ __forceinline__ void issue(uint8_t* base, int c, u32x4_t (&q)[4 * NQ]) const {
+  // (kAS: adst = where this wave's activation-scale load lands)
+  __device__ __forceinline__ void issue(uint8_t* base, int c, u32x4_t (&q)[4 * NQ],
+                                        uint8_t* adst = nullptr) const {
     const bool ok = c < nch;
     const uint32_t oor = ok ? 0u : kOOR;
     const uint32_t cc = ok ? (uint32_t)c : 0u;
+    if constexpr (kAS) load_to_lds4(as, aso | oor, 4 * cc, adst);
     if constexpr (kFP4A) {
 #pragma unroll
       for (int i = 0; i < XI; ++i)
@@ -250,7 +261,7 @@ struct TiledGemm {
       for (int mt = 0; mt < NMT; ++mt) {
         const int r = 16 * mt + nl;
         av[mt] = *reinterpret_cast<const u32x4_t*>(x + r * 64 + 16 * (g ^ ((r >> 2) & 3)));
-        sa[mt] = asc[scale_at<BM / 4>(r, c)];
+        sa[mt] = kAS ? asc[4 * r + g] : asc[scale_at<BM / 4>(r, c)];
       }
 #pragma unroll
       for (int mt = 0; mt < NMT; ++mt)
@@ -328,20 +339,30 @@ struct TiledGemm {
   // activation scale row r (MXFP4) or kOOR.
   template <int NMT, class WRow, class ARow>
   __device__ __forceinline__ void run(uint8_t* const (&stages)[NS], uint8_t* sc, uint8_t* asc,
-                                      WRow wrow, ARow arow, floatx4_t (&acc)[MT][4]) const {
+                                      WRow wrow, ARow arow, floatx4_t (&acc)[MT][4]) {
     u32x4_t q[NS][4 * NQ];
     stage_rows<64>(sc, ws, wrow);
-    if constexpr (kFP4A) stage_rows<BM / 4>(asc, as, arow);
+    // kAS: slot u's activation scales at asc + 4 BM u (waves 0 and 1 load
+    // rows 64 wave + lane; waves 2 and 3 write zeros past the slots)
+    auto aslot = [&](int u) -> uint8_t* { return kAS ? asc + 4 * BM * u : asc; };
+    auto adst = [&](int u) -> uint8_t* {
+      return wave < 2 ? asc + 4 * BM * u + 256 * wave : asc + 4 * BM * NS;
+    };
+    if constexpr (kAS) {
+      aso = wave < 2 ? arow(64 * wave + lane) : kOOR;
+    } else if constexpr (kFP4A) {
+      stage_rows<BM / 4>(asc, as, arow);
+    }
 #pragma unroll
-    for (int u = 0; u < NS - 1; ++u) issue(stages[u], u, q[u]);
+    for (int u = 0; u < NS - 1; ++u) issue(stages[u], u, q[u], adst(u));
     for (int c0 = 0; c0 < nch; c0 += NS) {
 #pragma unroll
       for (int u = 0; u < NS; ++u) {
         const int c = c0 + u;
         wait_vmcnt<LPS * (NS - 2)>();
         stage_barrier();
-        issue(stages[(u + NS - 1) % NS], c + NS - 1, q[(u + NS - 1) % NS]);
-        if (c < nch) compute<NMT>(stages[u], sc, asc, c, q[u], acc);
+        issue(stages[(u + NS - 1) % NS], c + NS - 1, q[(u + NS - 1) % NS], adst((u + NS - 1) % NS));
+        if (c < nch) compute<NMT>(stages[u], sc, aslot(u), c, q[u], acc);
       }
     }
     wait_vmcnt<0>();
@@ -359,8 +380,8 @@ __device__ __forceinline__ TileT tile_of(const int32_t* tiles, const int32_t* of
 
 // The lane's activation source offsets for every stage: row r of the tile
 // comes from source row src(r) (a token for gate/up, a sorted row for down).
-template <int BM, bool kFP4A, bool kW8, bool kSK, class SrcFn>
-__device__ __forceinline__ void plan_x(TiledGemm<BM, kFP4A, kW8, kSK>& G, const TileT& ti, SrcFn src,
+template <int BM, bool kFP4A, bool kW8, int KV, class SrcFn>
+__device__ __forceinline__ void plan_x(TiledGemm<BM, kFP4A, kW8, KV>& G, const TileT& ti, SrcFn src,
                                        uint32_t row_bytes) {
 #pragma unroll
   for (int i = 0; i < G.XI; ++i) {
@@ -381,8 +402,8 @@ __device__ __forceinline__ void plan_x(TiledGemm<BM, kFP4A, kW8, kSK>& G, const 
 
 // Common set-up of a workgroup's GEMM state (weights of one expert slice;
 // K = reduction length; rs = K/32 scale bytes per weight row).
-template <int BM, bool kFP4A, bool kW8, bool kSK>
-__device__ __forceinline__ void setup(TiledGemm<BM, kFP4A, kW8, kSK>& G, const TileT& ti, int K,
+template <int BM, bool kFP4A, bool kW8, int KV>
+__device__ __forceinline__ void setup(TiledGemm<BM, kFP4A, kW8, KV>& G, const TileT& ti, int K,
                                       const uint8_t* wq, const uint8_t* wsc, int wrows) {
   G.lane = threadIdx.x & 63;
   G.wave = threadIdx.x >> 6;
@@ -431,9 +452,9 @@ __device__ __forceinline__ void with_nmt(int rows, F&& f) {
 // Static LDS of a kernel: NS stage arrays (separate objects), the weight
 // scales, and for MXFP4 activations their scales and the tile's source
 // rows; body(stages, scales, act_scales, src_rows) runs with them.
-template <int BM, bool kFP4A, bool kW8, bool kSK, class Body>
+template <int BM, bool kFP4A, bool kW8, int KV, class Body>
 __device__ __forceinline__ void with_lds(Body&& body) {
-  using Cfg = TileCfg<BM, kFP4A, kW8, kSK>;
+  using Cfg = TileCfg<BM, kFP4A, kW8, KV>;
   constexpr int XB = Cfg::XB, SCB = Cfg::SCB;
   __shared__ __align__(16) uint8_t sc[SCB];
   __shared__ __align__(16) uint8_t st0[XB];
@@ -466,16 +487,16 @@ __device__ __forceinline__ void with_lds(Body&& body) {
 // activation-code offsets and the activation-scale rows), then the pipeline.
 // direct(r) = source row of tile row r < rows; wrow(r) = byte offset of
 // weight scale row r; arow_bytes = activation scale bytes per source row.
-template <int BM, bool kFP4A, bool kW8, bool kSK, class Direct, class WRow>
-__device__ __forceinline__ void tile_loop(TiledGemm<BM, kFP4A, kW8, kSK>& G, const TileT& ti, Direct direct,
+template <int BM, bool kFP4A, bool kW8, int KV, class Direct, class WRow>
+__device__ __forceinline__ void tile_loop(TiledGemm<BM, kFP4A, kW8, KV>& G, const TileT& ti, Direct direct,
                                           WRow wrow, uint32_t row_bytes, uint32_t arow_bytes,
                                           floatx4_t (&acc)[BM / 16][4]) {
-  with_lds<BM, kFP4A, kW8, kSK>([&](auto& stages, uint8_t* sc, uint8_t* asc, int32_t* srow) {
+  with_lds<BM, kFP4A, kW8, KV>([&](auto& stages, uint8_t* sc, uint8_t* asc, int32_t* srow) {
     if constexpr (kFP4A) {
       const int t = threadIdx.x;
       if (t < BM) srow[t] = t < ti.rows ? (int32_t)direct(t) : 0;
       __syncthreads();
-      plan_x<BM, kFP4A, kW8, kSK>(G, ti, [&](int r) { return (uint32_t)srow[r]; }, row_bytes);
+      plan_x<BM, kFP4A, kW8, KV>(G, ti, [&](int r) { return (uint32_t)srow[r]; }, row_bytes);
       auto arow = [&](int r) -> uint32_t {
         return r < ti.rows ? (uint32_t)srow[r] * arow_bytes : kOOR;
       };
@@ -483,7 +504,7 @@ __device__ __forceinline__ void tile_loop(TiledGemm<BM, kFP4A, kW8, kSK>& G, con
         G.template run<decltype(n)::value>(stages, sc, asc, wrow, arow, acc);
       });
     } else {
-      plan_x<BM, kFP4A, kW8, kSK>(G, ti, direct, row_bytes);
+      plan_x<BM, kFP4A, kW8, KV>(G, ti, direct, row_bytes);
       auto arow = [](int) -> uint32_t { return kOOR; };
       with_nmt<BM>(ti.rows, [&](auto n) {
         G.template run<decltype(n)::value>(stages, sc, asc, wrow, arow, acc);
@@ -494,8 +515,8 @@ __device__ __forceinline__ void tile_loop(TiledGemm<BM, kFP4A, kW8, kSK>& G, con
 
 // gate/up + SwiGLU: weight rows gate [i0, i0 + 128) and up [I + i0, I + i0 + 128),
 // i0 = 128 s; wave w owns i in [i0 + 32 w, i0 + 32 w + 32): strips gate lo/hi, up lo/hi.
-template <int BM, bool kFP4A, bool kW8, bool kSK = false>
-__global__ __launch_bounds__(256, kSK ? 2 : 1) void gate_up_tiled_kernel(
+template <int BM, bool kFP4A, bool kW8, int KV = 0>
+__global__ __launch_bounds__(256, KV ? 2 : 1) void gate_up_tiled_kernel(
     const void* __restrict__ act, const uint8_t* __restrict__ act_scale,
     const int32_t* __restrict__ sorted, const int32_t* __restrict__ offsets,
     const int32_t* __restrict__ tiles, const int32_t* __restrict__ num_tiles,
@@ -504,7 +525,7 @@ __global__ __launch_bounds__(256, kSK ? 2 : 1) void gate_up_tiled_kernel(
   int tile, s;
   if (!tile_slice<kFP4A>(blockIdx.x, *num_tiles, I / 128, &tile, &s)) return;
   const TileT ti = tile_of<BM>(tiles, offsets, tile);
-  TiledGemm<BM, kFP4A, kW8, kSK> G;
+  TiledGemm<BM, kFP4A, kW8, KV> G;
   setup(G, ti, H, w13, w13s, 2 * I);
   const int nl = G.nl, g = G.g;
   const uint32_t rb = H / 2, rs = H / 32;
@@ -532,7 +553,7 @@ __global__ __launch_bounds__(256, kSK ? 2 : 1) void gate_up_tiled_kernel(
   for (int mt = 0; mt < BM / 16; ++mt)
 #pragma unroll
     for (int st = 0; st < 4; ++st) acc[mt][st] = (floatx4_t){0.f, 0.f, 0.f, 0.f};
-  tile_loop<BM, kFP4A, kW8, kSK>(G, ti, token, wrow, kFP4A ? rb : (uint32_t)H * 2, rs, acc);
+  tile_loop<BM, kFP4A, kW8, KV>(G, ti, token, wrow, kFP4A ? rb : (uint32_t)H * 2, rs, acc);
 
 #pragma unroll
   for (int mt = 0; mt < BM / 16; ++mt)
@@ -548,8 +569,8 @@ __global__ __launch_bounds__(256, kSK ? 2 : 1) void gate_up_tiled_kernel(
 }
 
 // down: weight rows j in [256 s, 256 s + 256); wave w owns [256 s + 64 w, +64).
-template <int BM, bool kFP4A, bool kW8, bool kSK = false>
-__global__ __launch_bounds__(256, kSK ? 2 : 1) void down_tiled_kernel(
+template <int BM, bool kFP4A, bool kW8, int KV = 0>
+__global__ __launch_bounds__(256, KV ? 2 : 1) void down_tiled_kernel(
     const void* __restrict__ hin, const uint8_t* __restrict__ hscale,
     const int32_t* __restrict__ offsets, const int32_t* __restrict__ tiles,
     const int32_t* __restrict__ num_tiles, const uint8_t* __restrict__ w2,
@@ -557,7 +578,7 @@ __global__ __launch_bounds__(256, kSK ? 2 : 1) void down_tiled_kernel(
   int tile, s;
   if (!tile_slice<kFP4A>(blockIdx.x, *num_tiles, H / 256, &tile, &s)) return;
   const TileT ti = tile_of<BM>(tiles, offsets, tile);
-  TiledGemm<BM, kFP4A, kW8, kSK> G;
+  TiledGemm<BM, kFP4A, kW8, KV> G;
   setup(G, ti, I, w2, w2s, H);
   const int nl = G.nl, g = G.g;
   const uint32_t rb = I / 2, rs = I / 32;
@@ -578,7 +599,7 @@ __global__ __launch_bounds__(256, kSK ? 2 : 1) void down_tiled_kernel(
   for (int mt = 0; mt < BM / 16; ++mt)
 #pragma unroll
     for (int st = 0; st < 4; ++st) acc[mt][st] = (floatx4_t){0.f, 0.f, 0.f, 0.f};
-  tile_loop<BM, kFP4A, kW8, kSK>(G, ti, srow, wrow, kFP4A ? rb : (uint32_t)I * 2, rs, acc);
+  tile_loop<BM, kFP4A, kW8, KV>(G, ti, srow, wrow, kFP4A ? rb : (uint32_t)I * 2, rs, acc);
 
 #pragma unroll
   for (int mt = 0; mt < BM / 16; ++mt)
@@ -593,25 +614,25 @@ __global__ __launch_bounds__(256, kSK ? 2 : 1) void down_tiled_kernel(
     }
 }
 
-template <int BM, bool kFP4A, bool kW8 = false, bool kSK = false>
+template <int BM, bool kFP4A, bool kW8 = false, int KV = 0>
 hipError_t launch_gate_up_bm(const void* act, const uint8_t* act_scale, const int32_t* sorted,
                              const int32_t* offsets, const int32_t* tiles,
                              const int32_t* num_tiles, int max_tiles, const uint8_t* w13,
                              const uint8_t* w13s, int T, int H, int I, int Kp, uint16_t* h,
                              hipStream_t stream) {
   const unsigned grid = tile_slice_grid<kFP4A>(max_tiles, I / 128);
-  hipLaunchKernelGGL((gate_up_tiled_kernel<BM, kFP4A, kW8, kSK>), dim3(grid), dim3(256), 0, stream, act,
+  hipLaunchKernelGGL((gate_up_tiled_kernel<BM, kFP4A, kW8, KV>), dim3(grid), dim3(256), 0, stream, act,
                      act_scale, sorted, offsets, tiles, num_tiles, w13, w13s, T, H, I, Kp, h);
   return hipGetLastError();
 }
 
-template <int BM, bool kFP4A, bool kW8 = false, bool kSK = false>
+template <int BM, bool kFP4A, bool kW8 = false, int KV = 0>
 hipError_t launch_down_bm(const void* h, const uint8_t* h_scale, const int32_t* offsets,
                           const int32_t* tiles, const int32_t* num_tiles, int max_tiles,
                           const uint8_t* w2, const uint8_t* w2s, int A, int H, int I, uint16_t* y,
                           hipStream_t stream) {
   const unsigned grid = tile_slice_grid<kFP4A>(max_tiles, H / 256);
-  hipLaunchKernelGGL((down_tiled_kernel<BM, kFP4A, kW8, kSK>), dim3(grid), dim3(256), 0, stream, h,
+  hipLaunchKernelGGL((down_tiled_kernel<BM, kFP4A, kW8, KV>), dim3(grid), dim3(256), 0, stream, h,
                      h_scale, offsets, tiles, num_tiles, w2, w2s, A, H, I, y);
   return hipGetLastError();
 }
@@ -652,12 +673,15 @@ hipError_t launch_gate_up_tiled(int tile_m, int act_fmt, int wfmt, const void* a
     return launch_gate_up_bm<256, true>(act, act_scale, sorted, offsets, tiles, num_tiles,
                                         max_tiles, w13, w13s, T, H, I, Kp, h, stream);
   if (tile_m == 128)
-    return act_fmt ? (H <= 2048 ? launch_gate_up_bm<128, true, false, true>(
-                                      act, act_scale, sorted, offsets, tiles, num_tiles,
-                                      max_tiles, w13, w13s, T, H, I, Kp, h, stream)
-                                : launch_gate_up_bm<128, true>(act, act_scale, sorted, offsets,
-                                                               tiles, num_tiles, max_tiles, w13,
-                                                               w13s, T, H, I, Kp, h, stream))
+    return act_fmt ? (H <= 2048   ? launch_gate_up_bm<128, true, false, 1>(
+                                        act, act_scale, sorted, offsets, tiles, num_tiles,
+                                        max_tiles, w13, w13s, T, H, I, Kp, h, stream)
+                      : H <= 6144 ? launch_gate_up_bm<128, true, false, 2>(
+                                        act, act_scale, sorted, offsets, tiles, num_tiles,
+                                        max_tiles, w13, w13s, T, H, I, Kp, h, stream)
+                                  : launch_gate_up_bm<128, true>(act, act_scale, sorted, offsets,
+                                                                 tiles, num_tiles, max_tiles, w13,
+                                                                 w13s, T, H, I, Kp, h, stream))
                    : launch_gate_up_bm<128, false>(act, act_scale, sorted, offsets, tiles,
                                                     num_tiles, max_tiles, w13, w13s, T, H, I, Kp,
                                                     h, stream);
@@ -682,11 +706,15 @@ hipError_t launch_down_tiled(int tile_m, int act_fmt, int wfmt, const void* h,
     return launch_down_bm<256, true>(h, h_scale, offsets, tiles, num_tiles, max_tiles, w2, w2s, A,
                                      H, I, y, stream);
   if (tile_m == 128)
-    return act_fmt ? (I <= 2048 ? launch_down_bm<128, true, false, true>(h, h_scale, offsets, tiles,
-                                                                         num_tiles, max_tiles, w2,
-                                                                         w2s, A, H, I, y, stream)
-                                : launch_down_bm<128, true>(h, h_scale, offsets, tiles, num_tiles,
-                                                            max_tiles, w2, w2s, A, H, I, y, stream))
+    return act_fmt ? (I <= 2048   ? launch_down_bm<128, true, false, 1>(h, h_scale, offsets, tiles,
+                                                                        num_tiles, max_tiles, w2,
+                                                                        w2s, A, H, I, y, stream)
+                      : I <= 6144 ? launch_down_bm<128, true, false, 2>(h, h_scale, offsets, tiles,
+                                                                        num_tiles, max_tiles, w2,
+                                                                        w2s, A, H, I, y, stream)
+                                  : launch_down_bm<128, true>(h, h_scale, offsets, tiles,
+                                                              num_tiles, max_tiles, w2, w2s, A, H,
+                                                              I, y, stream))
                    : launch_down_bm<128, false>(h, h_scale, offsets, tiles, num_tiles, max_tiles,
                                                  w2, w2s, A, H, I, y, stream);
   return act_fmt ? launch_down_bm<64, true>(h, h_scale, offsets, tiles, num_tiles, max_tiles, w2,
