@@ -52,6 +52,11 @@ SMALL = {
     "tiled128": synth.custom_config("tiled128", T=300, H=512, I=256, E=16, K=3, shared=1),
     "tiled128_w4a4": synth.custom_config("tiled128_w4a4", T=300, H=512, I=256, E=16, K=3,
                                          shared=1, act_fmt=synth.ACT_MXFP4, outlier_p=0.002),
+    # reductions in (2048, 6144]: the MXFP4 128-row kernels that bring the
+    # activation scales with each stage (gate/up and down)
+    "tiled128_w4a4_k2560": synth.custom_config("tiled128_w4a4_k2560", T=200, H=2560, I=2560,
+                                               E=4, K=1, shared=1, act_fmt=synth.ACT_MXFP4,
+                                               outlier_p=0.002),
     # reductions above 6144: the MXFP4 128-row kernels with whole-K scale
     # arrays (smaller K takes their two-workgroups-per-CU variants)
     "tiled128_w4a4_k6400": synth.custom_config("tiled128_w4a4_k6400", T=200, H=6400, I=6400,
