@@ -41,6 +41,10 @@
  *   - Vector-loaded buffers (activations, packed weights, y, quantiser
  *     input and output) must be 16-byte aligned.
  *   - Shapes: H and I multiples of 128; E <= 1024; K + shared <= 32.
+ *     The kernels address the activations, h and each expert's weight
+ *     codes with 32-bit offsets: x (T*H*2 bytes bf16, T*H/2 MXFP4), h
+ *     (T*K'*I*2 or T*K'*I/2) and one expert's codes (2I*H/2, 2I*H for MXFP8;
+ *     the same for W2) each stay below 2 GiB, else UNSUPPORTED.
  *
  * MXFP4 (OCP Microscaling v1.0): per 32 consecutive elements along the
  * reduction axis one E8M0 scale byte b (value 2^(b-127)) and 32 E2M1 codes
@@ -297,7 +301,7 @@ MOE_API moe_status moe_mxfp8_quantize(const void *src, int32_t src_dtype, int64_
  *   h          out bf16 [T*Kp, I] in sorted row order
  * Errors: INVALID_ARGUMENT, UNSUPPORTED (H or I not a multiple of 128, a
  * tile_m / shape the kernels do not cover, an expert's 2I x H code bytes
- * above 2^32).
+ * at or above 2^31).
  */
 MOE_API moe_status moe_mxfp8_expert_gate_up(const uint16_t *x, const int32_t *sorted_assign,
                                     const int32_t *expert_offsets, const int32_t *tile_table,
@@ -427,7 +431,7 @@ MOE_API size_t moe_mxfp8_workspace_size(int32_t T, int32_t H, int32_t I, int32_t
  * `stream`.  Arguments, outputs and errors as moe_mxfp4_forward with
  * act_fmt = MOE_ACT_BF16, except the weights (MXFP8 layout above) and the
  * workspace (moe_mxfp8_workspace_size bytes); UNSUPPORTED also when an
- * expert's 2I x H code bytes exceed 2^32.
+ * expert's 2I x H code bytes reach 2^31.
  */
 MOE_API moe_status moe_mxfp8_forward(const uint16_t *x, const float *router_logits,
                              const float *shared_gate_logits, const uint8_t *w13,

@@ -227,10 +227,19 @@ moe_status moe_weights_to_native(const uint8_t* src, int32_t wfmt, int64_t rows,
 
 namespace {
 
-// Weight code bytes of one expert's W13 (2I rows) or W2 (H rows) must stay
-// within a 32-bit buffer range.
+// The GEMM kernels address each expert's weight codes, the activation rows
+// and h with 32-bit buffer offsets in which bit 31 marks a row that is not
+// there (the load returns zeros): every such buffer stays below 2 GiB.
+constexpr int64_t kMaxBufferBytes = (int64_t)1 << 31;
+
+// Weight code bytes of one expert's W13 (2I rows) or W2 (H rows).
 bool weights_fit(int wfmt, int64_t rows, int64_t k) {
-  return rows * (wfmt == 1 ? k : k / 2) < (int64_t)UINT32_MAX;
+  return rows * (wfmt == 1 ? k : k / 2) < kMaxBufferBytes;
+}
+
+// rows x cols activations (bf16, or MXFP4 codes).
+bool acts_fit(int act_fmt, int64_t rows, int64_t cols) {
+  return rows * (act_fmt == MOE_ACT_MXFP4 ? cols / 2 : cols * 2) < kMaxBufferBytes;
 }
 
 moe_status gate_up_impl(const void* act, const uint8_t* act_scale, int32_t act_fmt, int wfmt,
@@ -242,7 +251,8 @@ moe_status gate_up_impl(const void* act, const uint8_t* act_scale, int32_t act_f
     return MOE_ERR_INVALID_ARGUMENT;
   moe_status st = check_shape_HI(H, I);
   if (st != MOE_OK) return st;
-  if (Ep > 2048 || !weights_fit(wfmt, 2 * (int64_t)I, H)) return MOE_ERR_UNSUPPORTED;
+  if (Ep > 2048 || !weights_fit(wfmt, 2 * (int64_t)I, H) || !acts_fit(act_fmt, T, H))
+    return MOE_ERR_UNSUPPORTED;
   if (!tile_m_ok(tile_m, act_fmt, H, I, wfmt))
     return MOE_ERR_UNSUPPORTED;
   if (T == 0) return MOE_OK;
@@ -271,7 +281,8 @@ moe_status down_impl(const void* h, const uint8_t* h_scale, int32_t act_fmt, int
     return MOE_ERR_INVALID_ARGUMENT;
   moe_status st = check_shape_HI(H, I);
   if (st != MOE_OK) return st;
-  if (Ep > 2048 || !weights_fit(wfmt, H, I)) return MOE_ERR_UNSUPPORTED;
+  if (Ep > 2048 || !weights_fit(wfmt, H, I) || !acts_fit(act_fmt, (int64_t)T * Kp, I))
+    return MOE_ERR_UNSUPPORTED;
   if (!tile_m_ok(tile_m, act_fmt, H, I, wfmt))
     return MOE_ERR_UNSUPPORTED;
   if (T == 0) return MOE_OK;
@@ -382,6 +393,9 @@ moe_status forward_impl(const uint16_t* x, const float* router_logits,
   st = check_shape_HI(H, I);
   if (st != MOE_OK) return st;
   if (!weights_fit(wfmt, 2 * (int64_t)I, H) || !weights_fit(wfmt, H, I)) return MOE_ERR_UNSUPPORTED;
+  // x and the bf16 h (the larger of each pair of formats)
+  if (!acts_fit(MOE_ACT_BF16, T, H) || !acts_fit(MOE_ACT_BF16, (int64_t)T * (K + shared), I))
+    return MOE_ERR_UNSUPPORTED;
   if (T == 0) return MOE_OK;
   if (!x || !w13 || !w13_scale || !w2 || !w2_scale || !out) return MOE_ERR_INVALID_ARGUMENT;
   if (!aligned16(x) || !aligned16(w13) || !aligned16(w2) || !aligned16(out))

@@ -143,6 +143,9 @@ def test_gemm_and_combine_argument_errors():
     assert call(gu, base, a7=48) == UNSUPPORTED            # no kernel for 48-row tiles
     assert call(gu, base, a7=128, a11=384) == UNSUPPORTED  # tiled kernels need H % 256
     assert call(gu, base, a7=128, a11=6144, a10=0) == UNSUPPORTED  # bf16 tiled: H <= 4096
+    # buffers addressed with 32-bit offsets stay below 2 GiB (checked before the pointers)
+    assert call(gu, base, a10=300000, a11=4096) == UNSUPPORTED    # x: T*H*2 bytes
+    assert call(gu, base, a11=65536, a12=32768) == UNSUPPORTED    # one expert's W13 codes
     assert call(gu, base, a7=128, a11=6144, a2=1, a1=FAKE, a10=0) == OK   # MXFP4: H <= 8192
     assert call(gu, base, a0=MIS) == INVALID
     assert call(gu, base, a10=0) == OK
@@ -151,6 +154,7 @@ def test_gemm_and_combine_argument_errors():
     assert call(dn, based, a14=None) == INVALID
     assert call(dn, based, a10=100) == UNSUPPORTED
     assert call(dn, based, a6=64, a10=384) == UNSUPPORTED
+    assert call(dn, based, a9=300000, a11=4096) == UNSUPPORTED   # h: T*K'*I*2 bytes >= 2 GiB
     assert call(dn, based, a9=0) == OK
     cb = ops.lib().moe_combine
     assert cb(None, FAKE, FAKE, 4, 256, 3, FAKE, None) == INVALID
@@ -194,6 +198,7 @@ def test_forward_argument_errors_and_workspace():
     assert call(a11=17) == INVALID                         # K > E
     assert call(a8=96) == UNSUPPORTED
     assert call(a10=2048) == UNSUPPORTED
+    assert call(a7=300000, a8=4096) == UNSUPPORTED          # x: T*H*2 bytes >= 2 GiB
     assert call(a3=MIS) == INVALID
     assert call(a7=0, a0=None, a17=None, a18=0) == OK      # T = 0
     fr = ops.lib().moe_mxfp4_forward_router
