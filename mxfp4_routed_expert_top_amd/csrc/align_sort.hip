@@ -7,12 +7,17 @@
 // the routed experts and the shared one).
 //
 // Up to kSmallA assignments: one workgroup does everything in LDS.  Beyond:
-// three launches over chunks of kChunk assignments:
+// four launches over chunks of kChunk assignments:
 //   1. per-chunk histograms            hist[b][e]
-//   2. one block: column scans over chunks, the exclusive scan over experts
-//      (offsets), per-chunk base positions and the tile table
-//   3. per-chunk stable scatter: inside a chunk, wave by wave in order, each
-//      lane's rank among the earlier lanes with the same expert
+//   2. column scans, one block per 64 experts, each of its 16 waves owning a
+//      slice of the chunks (rows of 64 experts per load, up to twelve in
+//      flight): counts[e] and, in place, hist[b][e] = the count of e in the
+//      chunks before b
+//   3. one block: the exclusive scan over experts (offsets) and the tile
+//      table
+//   4. per-chunk stable scatter from offsets[e] + hist[b][e]: inside a
+//      chunk, wave by wave in order, each lane's rank among the earlier
+//      lanes with the same expert
 // A lane's rank among equal experts in its wave comes from ballots: one
 // round per distinct expert in the wave (at most 64), no data exchange.
 #include "common.h"
@@ -20,9 +25,11 @@
 
 namespace {
 
-constexpr int kChunk = 2048;      // assignments per block in passes 1 and 3
+constexpr int kChunk = 512;       // assignments per block in passes 1 and 4
 constexpr int kScanThreads = 1024;
 constexpr int kSmallA = 8192;     // single-workgroup path up to this many assignments
+constexpr int kSlices = kScanThreads / 64;   // chunk slices of a column scan: one per wave
+constexpr int kBatch = 12;        // histogram loads in flight per lane in a column scan
 
 // Rank of this lane among the lanes of its wave holding the same expert e
 // (lower lanes first) and the number of such lanes; e < 0 takes no part.
@@ -85,38 +92,68 @@ __device__ int block_exclusive_scan(int v, int* tmp /* >= 16 ints */, int* total
   return r;
 }
 
-__global__ __launch_bounds__(kScanThreads) void align_scan_kernel(
-    int32_t* __restrict__ hist, int nb, int A, int Ep, int tile_m, int32_t* __restrict__ counts,
-    int32_t* __restrict__ offsets, int32_t* __restrict__ tiles, int32_t* __restrict__ num_tiles) {
+// Lane's expert e = 64 * block + lane; wave w's slice of the chunks,
+// [b0, b0 + n): f(j, count of e in chunk b0 + j) for j ascending, loads
+// kBatch at a time.
+template <class F>
+__device__ __forceinline__ void for_slice(const int32_t* hist, int Ep, int e, int b0, int n,
+                                          F&& f) {
+  for (int j0 = 0; j0 < n; j0 += kBatch) {
+    int v[kBatch];
+#pragma unroll
+    for (int k = 0; k < kBatch; ++k)
+      v[k] = j0 + k < n && e < Ep ? hist[(size_t)(b0 + j0 + k) * Ep + e] : 0;
+#pragma unroll
+    for (int k = 0; k < kBatch; ++k)
+      if (j0 + k < n && e < Ep) f(j0 + k, v[k]);
+  }
+}
+
+__global__ __launch_bounds__(kScanThreads) void align_colscan_kernel(
+    int32_t* __restrict__ hist, int nb, int Ep, int32_t* __restrict__ counts) {
+  __shared__ int part[kSlices][64];
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int e = 64 * blockIdx.x + lane;
+  const int per = (nb + kSlices - 1) / kSlices;
+  const int b0 = min(nb, w * per), n = min(nb, b0 + per) - b0;
+  int sum = 0;
+  for_slice(hist, Ep, e, b0, n, [&](int, int v) { sum += v; });
+  part[w][lane] = sum;
+  __syncthreads();
+  int run = 0, total = 0;
+  for (int s = 0; s < kSlices; ++s) {
+    const int c = part[s][lane];
+    run += s < w ? c : 0;
+    total += c;
+  }
+  if (w == 0 && e < Ep) counts[e] = total;
+  for_slice(hist, Ep, e, b0, n, [&](int j, int v) {
+    hist[(size_t)(b0 + j) * Ep + e] = run;
+    run += v;
+  });
+}
+
+__global__ __launch_bounds__(kScanThreads) void align_offsets_kernel(
+    const int32_t* __restrict__ counts, int A, int Ep, int tile_m, int32_t* __restrict__ offsets,
+    int32_t* __restrict__ tiles, int32_t* __restrict__ num_tiles) {
   __shared__ int tmp[17];
   // Each thread owns experts e = 2*tid and 2*tid + 1 (Ep <= 2048).
   int cnt[2] = {0, 0};
   for (int q = 0; q < 2; ++q) {
-    int e = 2 * threadIdx.x + q;
-    if (e < Ep) {
-      int run = 0;
-      for (int b = 0; b < nb; ++b) {
-        int32_t* p = hist + (size_t)b * Ep + e;
-        int c = *p;
-        *p = run;          // exclusive prefix over chunks
-        run += c;
-      }
-      cnt[q] = run;
-    }
+    const int e = 2 * threadIdx.x + q;
+    if (e < Ep) cnt[q] = counts[e];
   }
   int total;
-  int base = block_exclusive_scan(cnt[0] + cnt[1], tmp, &total);
-  int off[2] = {base, base + cnt[0]};
-  int nt[2] = {(cnt[0] + tile_m - 1) / tile_m, (cnt[1] + tile_m - 1) / tile_m};
+  const int base = block_exclusive_scan(cnt[0] + cnt[1], tmp, &total);
+  const int off[2] = {base, base + cnt[0]};
+  const int nt[2] = {(cnt[0] + tile_m - 1) / tile_m, (cnt[1] + tile_m - 1) / tile_m};
   int ttotal;
-  int tbase = block_exclusive_scan(nt[0] + nt[1], tmp, &ttotal);
-  int toff[2] = {tbase, tbase + nt[0]};
+  const int tbase = block_exclusive_scan(nt[0] + nt[1], tmp, &ttotal);
+  const int toff[2] = {tbase, tbase + nt[0]};
   for (int q = 0; q < 2; ++q) {
-    int e = 2 * threadIdx.x + q;
+    const int e = 2 * threadIdx.x + q;
     if (e < Ep) {
-      counts[e] = cnt[q];
       offsets[e] = off[q];
-      for (int b = 0; b < nb; ++b) hist[(size_t)b * Ep + e] += off[q];
       if (tiles)
         for (int j = 0; j < nt[q]; ++j) {
           tiles[2 * (toff[q] + j)] = e;
@@ -131,10 +168,11 @@ __global__ __launch_bounds__(kScanThreads) void align_scan_kernel(
 }
 
 __global__ __launch_bounds__(256) void align_scatter_kernel(
-    const int32_t* __restrict__ ids, int A, int Ep, const int32_t* __restrict__ base,
-    int32_t* __restrict__ sorted, int32_t* __restrict__ inv) {
+    const int32_t* __restrict__ ids, int A, int Ep, const int32_t* __restrict__ offsets,
+    const int32_t* __restrict__ before, int32_t* __restrict__ sorted, int32_t* __restrict__ inv) {
   extern __shared__ int32_t pos[];
-  for (int e = threadIdx.x; e < Ep; e += blockDim.x) pos[e] = base[(size_t)blockIdx.x * Ep + e];
+  for (int e = threadIdx.x; e < Ep; e += blockDim.x)
+    pos[e] = offsets[e] + before[(size_t)blockIdx.x * Ep + e];
   __syncthreads();
   const int wave = threadIdx.x >> 6;
   const int a0 = blockIdx.x * kChunk;
@@ -227,7 +265,7 @@ __global__ __launch_bounds__(kScanThreads) void align_small_kernel(
 }  // namespace
 
 size_t align_scratch_bytes(int A, int Ep) {
-  int nb = (A + kChunk - 1) / kChunk;
+  const int nb = (A + kChunk - 1) / kChunk;
   return (size_t)(nb > 0 ? nb : 1) * Ep * sizeof(int32_t);
 }
 
@@ -243,9 +281,11 @@ hipError_t launch_align_sort(const int32_t* ids, int A, int Ep, int tile_m, int3
   const int nb = (A + kChunk - 1) / kChunk;
   const size_t lds = (size_t)Ep * sizeof(int32_t);
   hipLaunchKernelGGL(align_hist_kernel, dim3(nb), dim3(256), lds, stream, ids, A, Ep, scratch);
-  hipLaunchKernelGGL(align_scan_kernel, dim3(1), dim3(kScanThreads), 0, stream, scratch, nb, A, Ep,
-                     tile_m, counts, offsets, tiles, num_tiles);
-  hipLaunchKernelGGL(align_scatter_kernel, dim3(nb), dim3(256), lds, stream, ids, A, Ep, scratch,
-                     sorted, inv);
+  hipLaunchKernelGGL(align_colscan_kernel, dim3((Ep + 63) / 64), dim3(kScanThreads), 0, stream,
+                     scratch, nb, Ep, counts);
+  hipLaunchKernelGGL(align_offsets_kernel, dim3(1), dim3(kScanThreads), 0, stream, counts, A, Ep,
+                     tile_m, offsets, tiles, num_tiles);
+  hipLaunchKernelGGL(align_scatter_kernel, dim3(nb), dim3(256), lds, stream, ids, A, Ep, offsets,
+                     scratch, sorted, inv);
   return hipGetLastError();
 }

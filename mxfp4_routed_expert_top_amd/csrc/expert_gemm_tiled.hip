@@ -34,41 +34,63 @@ struct TileT {
 };
 
 // Block -> (tile, weight slice).  The hardware hands workgroup b to XCD
-// b % 8, and an XCD runs all slices of a tile back to back (the tile's
-// activation rows are fetched into its L2 once, not once per slice).
+// b % 8, and an XCD runs the pairs it is given in order.
 //
-// MXFP4 activations (bandwidth-bound): the num_tiles * nslices live pairs,
-// tile-major, are cut into 8 contiguous runs, one per XCD, so consecutive
-// tiles of one expert also run on one XCD and re-read its weight slices from
-// L2.
+// MXFP4 activations (bandwidth-bound): the num_tiles * nslices live pairs
+// are cut into 8 contiguous runs, one per XCD.  Inside a run an expert's
+// tiles are taken G at a time and each group goes slice by slice: its tiles
+// read one weight slice back to back, so all but the first find the slice in
+// L2, and each tile's activation rows are re-read from L2 by the next slice
+// G pairs later.  G = 1 is the plain tile-major order (an XCD runs all
+// slices of a tile back to back).  On the W4A4 batch (experts of ~128 rows,
+// about half of them with a second, nearly empty 128-row tile) the down GEMM
+// takes G = 4: fetched bytes 1.74 -> 1.36 GB per launch, 1-2% faster; its
+// gate/up keeps G = 1, which measured 2.5% faster than 4 at the same fetch.
 //
 // bf16 activations (bound by the MFMA work, which grows with a tile's rows):
 // runs of equal pair counts leave the XCD holding a hot expert's full tiles
 // (or the shared expert's) with more work than the others, so chunks of
-// kDeal consecutive tiles are dealt to the XCDs in turn instead; on the
-// skewed 8,192-token batch this shortens both GEMMs by 5-7%.
+// kDeal consecutive tiles are dealt to the XCDs in turn instead, each chunk
+// tile-major; on the skewed 8,192-token batch this shortens both GEMMs by
+// 5-7%.
 //
 // Blocks past the live pairs exit.
 constexpr int kDeal = 4;
 
-template <bool kFP4A>
-__device__ __forceinline__ bool tile_slice(int b, int num_tiles, int nslices, int* tile,
-                                           int* slice) {
+template <int BM, bool kFP4A, int G = 1>
+__device__ __forceinline__ bool tile_slice(int b, const int32_t* tiles, const int32_t* offsets,
+                                           int num_tiles, int nslices, TileT* ti, int* slice) {
   const int j = b >> 3;
+  int tile;
   if constexpr (kFP4A) {
     const int live = num_tiles * nslices;
     const int per = (live + 7) >> 3;
     const int L = (b & 7) * per + j;
     if (j >= per || L >= live) return false;
-    *tile = L / nslices;
-    *slice = L - *tile * nslices;
+    // The pairs of group [t_g, t_g + n) are [t_g * nslices, (t_g + n) * nslices),
+    // so tile L / nslices lies in L's group.
+    const int t0 = L / nslices;
+    const int e = tiles[2 * t0];
+    const int o0 = offsets[e], o1 = offsets[e + 1];
+    const int k0 = (tiles[2 * t0 + 1] - o0) / BM;         // t0's place among e's tiles
+    const int kg = k0 - k0 % G;                             // its group's first place
+    const int n = min(G, (o1 - o0 + BM - 1) / BM - kg);
+    const int local = L - (t0 - k0 + kg) * nslices;
+    const int k = kg + local % n;
+    *slice = local / n;
+    ti->expert = e;
+    ti->row0 = o0 + k * BM;
+    ti->rows = min(BM, o1 - ti->row0);
+    return true;
   } else {
     const int q = j / (kDeal * nslices), p = j - q * kDeal * nslices;
-    const int t = (q * 8 + (b & 7)) * kDeal + p / nslices;
-    if (t >= num_tiles) return false;
-    *tile = t;
+    tile = (q * 8 + (b & 7)) * kDeal + p / nslices;
+    if (tile >= num_tiles) return false;
     *slice = p % nslices;
   }
+  ti->expert = tiles[2 * tile];
+  ti->row0 = tiles[2 * tile + 1];
+  ti->rows = min(BM, offsets[ti->expert + 1] - ti->row0);
   return true;
 }
 
@@ -369,15 +391,6 @@ struct TiledGemm {
   }
 };
 
-template <int BM>
-__device__ __forceinline__ TileT tile_of(const int32_t* tiles, const int32_t* offsets, int tile) {
-  TileT ti;
-  ti.expert = tiles[2 * tile];
-  ti.row0 = tiles[2 * tile + 1];
-  ti.rows = min(BM, offsets[ti.expert + 1] - ti.row0);
-  return ti;
-}
-
 // The lane's activation source offsets for every stage: row r of the tile
 // comes from source row src(r) (a token for gate/up, a sorted row for down).
 template <int BM, bool kFP4A, bool kW8, int KV, class SrcFn>
@@ -522,9 +535,9 @@ __global__ __launch_bounds__(256, KV ? 2 : 1) void gate_up_tiled_kernel(
     const int32_t* __restrict__ tiles, const int32_t* __restrict__ num_tiles,
     const uint8_t* __restrict__ w13, const uint8_t* __restrict__ w13s, int T, int H, int I, int Kp,
     uint16_t* __restrict__ h) {
-  int tile, s;
-  if (!tile_slice<kFP4A>(blockIdx.x, *num_tiles, I / 128, &tile, &s)) return;
-  const TileT ti = tile_of<BM>(tiles, offsets, tile);
+  TileT ti;
+  int s;
+  if (!tile_slice<BM, kFP4A>(blockIdx.x, tiles, offsets, *num_tiles, I / 128, &ti, &s)) return;
   TiledGemm<BM, kFP4A, kW8, KV> G;
   setup(G, ti, H, w13, w13s, 2 * I);
   const int nl = G.nl, g = G.g;
@@ -575,9 +588,9 @@ __global__ __launch_bounds__(256, KV ? 2 : 1) void down_tiled_kernel(
     const int32_t* __restrict__ offsets, const int32_t* __restrict__ tiles,
     const int32_t* __restrict__ num_tiles, const uint8_t* __restrict__ w2,
     const uint8_t* __restrict__ w2s, int A, int H, int I, uint16_t* __restrict__ y) {
-  int tile, s;
-  if (!tile_slice<kFP4A>(blockIdx.x, *num_tiles, H / 256, &tile, &s)) return;
-  const TileT ti = tile_of<BM>(tiles, offsets, tile);
+  TileT ti;
+  int s;
+  if (!tile_slice<BM, kFP4A, 4>(blockIdx.x, tiles, offsets, *num_tiles, H / 256, &ti, &s)) return;
   TiledGemm<BM, kFP4A, kW8, KV> G;
   setup(G, ti, I, w2, w2s, H);
   const int nl = G.nl, g = G.g;

@@ -155,14 +155,15 @@ def test_align_golden_tile_m_2():
 
 
 @pytest.mark.parametrize("name", ["tiny", "ragged", "sparse", "decode", "prefill",
-                                  "prefill_skewed", "w4a4", "one_hot", "big_a"])
+                                  "prefill_skewed", "w4a4", "one_hot", "big_a", "chunks19"])
 def test_align_sort(name):
     _say("align", name)
     if name == "one_hot":                  # every assignment to one expert: many tiles
         T, Kp, Ep = 3000, 1, 40
         ids = torch.full((T, Kp), 17, dtype=torch.int32)
-    elif name == "big_a":                  # many chunks, random ids, a ragged last chunk
-        T, Kp, Ep = 12345, 9, 1025
+    elif name in ("big_a", "chunks19"):    # many chunks, random ids, a ragged last chunk
+        # (218 and 19 chunks of 512: histogram columns padded by 2 and 1)
+        T, Kp, Ep = (12345, 9, 1025) if name == "big_a" else (1080, 9, 300)
         ids = torch.randint(0, Ep, (T, Kp), generator=torch.Generator().manual_seed(9),
                             dtype=torch.int32)
     else:
