@@ -104,7 +104,9 @@ def gate_up_kernel_name(cfg, tile_m):
         kv = 0
         if cfg.act_fmt and tile_m == 128:
             kv = 1 if cfg.H <= 2048 else 2 if cfg.H <= 6144 else 0
-        return f"gate_up_tiled_kernel<{tile_m}, {a}, {w8}, {kv}>"
+        # the forward feeds MXFP4 activations to the tiled kernels in the blocked row order
+        blk = "true" if cfg.act_fmt else "false"
+        return f"gate_up_tiled_kernel<{tile_m}, {a}, {w8}, {kv}, {blk}>"
     if cfg.wfmt == synth.W_MXFP8:
         return "gate_up_kernel<1, false, true>"
     ph = 2 if (cfg.H // 128) % 2 == 0 else 1          # phase width of the 32-row kernel

@@ -102,7 +102,14 @@ typedef enum {
   MOE_ERR_DEVICE = 4              /* a HIP launch error (hipGetLastError) */
 } moe_status;
 
-typedef enum { MOE_ACT_BF16 = 0 /* W4A16 */, MOE_ACT_MXFP4 = 1 /* W4A4 */ } moe_act_fmt;
+/* Activation formats of the GEMM entry points.  MOE_ACT_MXFP4_BLOCKED is
+ * MXFP4 in the blocked row order below, for the LDS-tiled GEMMs only (the
+ * forward uses it for W4A4 whenever it picks tiled GEMMs). */
+typedef enum {
+  MOE_ACT_BF16 = 0 /* W4A16 */,
+  MOE_ACT_MXFP4 = 1 /* W4A4, row-major codes and scales */,
+  MOE_ACT_MXFP4_BLOCKED = 2 /* W4A4, sorted rows in the blocked order */
+} moe_act_fmt;
 typedef enum { MOE_SRC_F32 = 0, MOE_SRC_BF16 = 1 } moe_src_dtype;
 
 /* Rows per tile of the weight-streaming (decode) GEMMs: the 32-row tiles of
@@ -203,6 +210,36 @@ MOE_API moe_status moe_mxfp4_quantize(const void *src, int32_t src_dtype, int64_
                               uint8_t *packed, uint8_t *scales, void *stream);
 
 /*
+ * The same MXFP4 quantisation, written in the blocked row order that the
+ * LDS-tiled GEMMs read MXFP4 activations in (a layout for the memory system,
+ * not a step of the method: each row gets the codes and scales
+ * moe_mxfp4_quantize gives it).  With C = cols/128 chunks per row, output
+ * row p's chunk c (elements [128c, 128c + 128)) has its 64 code bytes (the
+ * row-major bytes [64c, 64c + 64)) at
+ *   packed + ((p/16)*C + c)*1024 + (p%16)*64
+ * and its 4 scale bytes (row-major [4c, 4c + 4)) at
+ *   scales + ((p/16)*C + c)*64 + (p%16)*4,
+ * so 16 consecutive rows' chunk is one contiguous KiB of codes and 64 bytes
+ * of scales.
+ *   src        fp32 or bf16 [rows, cols] (src_dtype), 16-byte aligned
+ *   row_map    NULL: source row t -> output row t (out_rows >= rows);
+ *              else int32 [rows, Kp]: source row t -> output rows
+ *              row_map[t*Kp + k], k < Kp (e.g. inv_assign: each token into
+ *              its sorted slots); values outside [0, out_rows) write nothing
+ *   packed     out uint8 [ceil(out_rows/16)*16, cols/2], 16-byte aligned
+ *   scales     out uint8 [ceil(out_rows/16)*16, cols/32], 16-byte aligned
+ * Output rows no source row goes to are left as they were.
+ * Errors: INVALID_ARGUMENT (null or misaligned pointers, negative sizes, bad
+ * dtype, Kp < 1 with a map, out_rows < rows without one), UNSUPPORTED (cols
+ * not a multiple of 128 or above 2^30, packed at or above 2^31 bytes, a
+ * grid above 2^32 - 1 workgroups).
+ */
+MOE_API moe_status moe_mxfp4_quantize_blocked(const void *src, int32_t src_dtype, int64_t rows,
+                                              int64_t cols, const int32_t *row_map, int32_t Kp,
+                                              int64_t out_rows, uint8_t *packed, uint8_t *scales,
+                                              void *stream);
+
+/*
  * Row-major weight codes -> the native code order the GEMM kernels read
  * (defined above), for rows x cols elements of one or more experts stacked
  * by rows (e.g. all of w13 as [E' * 2I, H]): a pure permutation of 16-byte
@@ -227,6 +264,11 @@ MOE_API moe_status moe_weights_to_native(const uint8_t *src, int32_t wfmt, int64
  *   h[r, i] = bf16( silu(acc[i]) * acc[I + i] )
  *   act_fmt = MOE_ACT_BF16:  act = x bf16 [T, H], act_scale = NULL
  *   act_fmt = MOE_ACT_MXFP4: act = packed uint8 [T, H/2], act_scale uint8 [T, H/32]
+ *   act_fmt = MOE_ACT_MXFP4_BLOCKED (tile_m 64, 128, 256): act, act_scale =
+ *              the activations of the SORTED rows r < T*Kp (token
+ *              sorted_assign[r] / Kp) in the blocked order, ceil(T*Kp/16)*16
+ *              rows (moe_mxfp4_quantize_blocked with row_map = inv_assign);
+ *              act_scale 16-byte aligned
  *   sorted_assign, expert_offsets, tile_table, num_tiles: moe_align_sort's
  *     outputs built with the same tile_m
  *   tile_m     rows per tile: 32 selects the weight-streaming kernel (small
@@ -252,6 +294,8 @@ MOE_API moe_status moe_expert_gate_up(const void *act, const uint8_t *act_scale,
  * accumulation, one round-to-nearest-even to bf16 when stored).
  *   act_fmt = MOE_ACT_BF16:  h bf16 [A, I], h_scale = NULL
  *   act_fmt = MOE_ACT_MXFP4: h packed uint8 [A, I/2], h_scale uint8 [A, I/32]
+ *   act_fmt = MOE_ACT_MXFP4_BLOCKED (tile_m 64, 128, 256): h, h_scale in the
+ *              blocked order, ceil(A/16)*16 rows; h_scale 16-byte aligned
  *   tile_m     as for moe_expert_gate_up
  *   w2         codes [E', H, I/2] in the native order; w2_scale [E', H, I/32]
  *   y          out bf16 [A, H], sorted row order (A = T*Kp)
@@ -347,7 +391,9 @@ MOE_API size_t moe_mxfp4_workspace_size(int32_t T, int32_t H, int32_t I, int32_t
  *   w13, w13_scale, w2, w2_scale: the MXFP4 weights of E + shared experts
  *                  (codes in the native order, scales row-major)
  *   act_fmt        MOE_ACT_BF16 (W4A16) or MOE_ACT_MXFP4 (W4A4: x and h are
- *                  MXFP4-quantised before their GEMM)
+ *                  MXFP4-quantised before their GEMM; with tiled GEMMs into
+ *                  the blocked sorted-row order, x into each of its token's
+ *                  slots)
  *   out            out bf16 [T, H]
  *   topk_ids_out, topk_weights_out: optional copies of the routing [T, K']
  *   workspace      caller-owned device scratch of moe_mxfp4_workspace_size bytes

@@ -110,7 +110,7 @@ unsigned tile_slice_grid(int max_tiles, int nslices) {
 // 76 KiB (two per CU).  256-row tiles exist for MXFP4
 // activations only: an expert of the W4A4 batch (~143 rows) then streams its
 // weights once instead of once per 128-row tile.
-template <int BM, bool kFP4A, bool kW8 = false, int KV = 0>
+template <int BM, bool kFP4A, bool kW8 = false, int KV = 0, bool kBlk = false>
 struct TileCfg {
   static_assert(BM == 64 || BM == 128 || (BM == 256 && kFP4A), "tile sizes");
   static_assert(!(kW8 && kFP4A), "MXFP8 weights take bf16 activations");
@@ -124,15 +124,19 @@ struct TileCfg {
   //      scales come with each stage (4 bytes per row) instead of for the
   //      whole K, leaving the weight scales' 48 KiB (74 KiB of LDS)
   static_assert(KV == 0 || (kFP4A && BM == 128), "variants: MXFP4 128-row tiles");
+  // kBlk: MXFP4 activations in the blocked row order (sorted rows, 16-row
+  // blocks: per block and chunk 1 KiB of codes and 64 bytes of scales, each
+  // contiguous); their scales then always come with each stage
+  static_assert(!kBlk || kFP4A, "blocked rows: MXFP4 activations");
   static constexpr int NS =
       ((BM == 64 && !kFP4A) || BM == 256 || (kW8 && BM == 128) || (KV && BM == 128)) ? 3 : 4;
   static constexpr int KMAX =
       KV == 1 ? 2048 : KV == 2 ? 6144 : kFP4A ? (BM == 128 ? 8192 : 6144) : 4096;
   static constexpr int SCB = 256 * (KMAX / 32);             // weight scales
   // MXFP4 activation scales of the tile's rows (whole K), BM/4 rows per wave
-  // (KV 2: NS stage slots of BM rows x 4 bytes, plus 256 bytes the waves
-  // that load no scales write their zeros to)
-  static constexpr int ASB = KV == 2 ? NS * BM * 4 + 256
+  // (KV 2 or blocked rows: NS stage slots of BM rows x 4 bytes, plus 256
+  // bytes the waves that load no scales write their zeros to)
+  static constexpr int ASB = (KV == 2 || kBlk) ? NS * BM * 4 + 256
                              : kFP4A ? 4 * ((BM / 4 * (KMAX / 128) + 63) / 64) * 256 : 0;
   // activation bytes per stage:
   //   bf16:  256 bytes per row, 16-byte slot p of row r holds piece p ^ (r & 15)
@@ -192,15 +196,17 @@ __device__ __forceinline__ void load_to_lds4(rsrc_t r, uint32_t voff, uint32_t s
 // past the last chunk use an out-of-range offset: they move no data and
 // every wave issues the same number of loads per stage, so the wait counts
 // are constants.  MFMAs run only on the tile's live 16-row sub-tiles.
-template <int BM, bool kFP4A, bool kW8 = false, int KV = 0>
+template <int BM, bool kFP4A, bool kW8 = false, int KV = 0, bool kBlk = false>
 struct TiledGemm {
-  static constexpr int NS = TileCfg<BM, kFP4A, kW8, KV>::NS;
-  static constexpr int XB = TileCfg<BM, kFP4A, kW8, KV>::XB;
+  static constexpr int NS = TileCfg<BM, kFP4A, kW8, KV, kBlk>::NS;
+  static constexpr int XB = TileCfg<BM, kFP4A, kW8, KV, kBlk>::XB;
   static constexpr int MT = BM / 16;
   static constexpr int XI = kFP4A ? BM / 64 : BM / 16;   // code / row loads per wave per stage
   // weight registers per strip and stage: 16 bytes (32 E2M1 codes) or 32 (32 E4M3 codes)
   static constexpr int NQ = kW8 ? 2 : 1;
-  static constexpr bool kAS = KV == 2;                    // activation scales per stage
+  static constexpr bool kAS = KV == 2 || kBlk;            // activation scales per stage
+  // per-chunk step of the activation code / scale offsets
+  static constexpr uint32_t kXStep = kBlk ? 1024 : kFP4A ? 64 : 256, kSStep = kBlk ? 64 : 4;
   static constexpr int LPS = XI + 4 * NQ + (kAS ? 1 : 0);  // vmem ops per wave per stage
 
   rsrc_t w, ws, a, as;
@@ -250,16 +256,10 @@ struct TiledGemm {
     const bool ok = c < nch;
     const uint32_t oor = ok ? 0u : kOOR;
     const uint32_t cc = ok ? (uint32_t)c : 0u;
-    if constexpr (kAS) load_to_lds4(as, aso | oor, 4 * cc, adst);
-    if constexpr (kFP4A) {
+    if constexpr (kAS) load_to_lds4(as, aso | oor, kSStep * cc, adst);
 #pragma unroll
-      for (int i = 0; i < XI; ++i)
-        load_to_lds16(a, xo[i] | oor, 64 * cc, base + (wave * XI + i) * 1024);
-    } else {
-#pragma unroll
-      for (int i = 0; i < XI; ++i)
-        load_to_lds16(a, xo[i] | oor, 256 * cc, base + (wave * XI + i) * 1024);
-    }
+    for (int i = 0; i < XI; ++i)
+      load_to_lds16(a, xo[i] | oor, kXStep * cc, base + (wave * XI + i) * 1024);
 #pragma unroll
     for (int t = 0; t < 4; ++t)
 #pragma unroll
@@ -364,14 +364,14 @@ struct TiledGemm {
                                       WRow wrow, ARow arow, floatx4_t (&acc)[MT][4]) {
     u32x4_t q[NS][4 * NQ];
     stage_rows<64>(sc, ws, wrow);
-    // kAS: slot u's activation scales at asc + 4 BM u (waves 0 and 1 load
-    // rows 64 wave + lane; waves 2 and 3 write zeros past the slots)
+    // kAS: slot u's activation scales at asc + 4 BM u (waves w < BM / 64
+    // load rows 64 w + lane; the others write zeros past the slots)
     auto aslot = [&](int u) -> uint8_t* { return kAS ? asc + 4 * BM * u : asc; };
     auto adst = [&](int u) -> uint8_t* {
-      return wave < 2 ? asc + 4 * BM * u + 256 * wave : asc + 4 * BM * NS;
+      return wave < BM / 64 ? asc + 4 * BM * u + 256 * wave : asc + 4 * BM * NS;
     };
     if constexpr (kAS) {
-      aso = wave < 2 ? arow(64 * wave + lane) : kOOR;
+      aso = wave < BM / 64 ? arow(64 * wave + lane) : kOOR;
     } else if constexpr (kFP4A) {
       stage_rows<BM / 4>(asc, as, arow);
     }
@@ -393,8 +393,8 @@ struct TiledGemm {
 
 // The lane's activation source offsets for every stage: row r of the tile
 // comes from source row src(r) (a token for gate/up, a sorted row for down).
-template <int BM, bool kFP4A, bool kW8, int KV, class SrcFn>
-__device__ __forceinline__ void plan_x(TiledGemm<BM, kFP4A, kW8, KV>& G, const TileT& ti, SrcFn src,
+template <int BM, bool kFP4A, bool kW8, int KV, bool kBlk, class SrcFn>
+__device__ __forceinline__ void plan_x(TiledGemm<BM, kFP4A, kW8, KV, kBlk>& G, const TileT& ti, SrcFn src,
                                        uint32_t row_bytes) {
 #pragma unroll
   for (int i = 0; i < G.XI; ++i) {
@@ -409,14 +409,20 @@ __device__ __forceinline__ void plan_x(TiledGemm<BM, kFP4A, kW8, KV>& G, const T
       const int p = G.lane & 15;
       piece = p ^ (r & 15);
     }
-    G.xo[i] = r < ti.rows ? src(r) * row_bytes + 16 * piece : kOOR;
+    if constexpr (kBlk) {           // sorted row s = row0 + r, chunk 0 of its block
+      const uint32_t s = (uint32_t)(ti.row0 + r);
+      G.xo[i] = r < ti.rows ? (s >> 4) * (row_bytes / 64) * 1024u + (s & 15) * 64u + 16 * piece
+                            : kOOR;
+    } else {
+      G.xo[i] = r < ti.rows ? src(r) * row_bytes + 16 * piece : kOOR;
+    }
   }
 }
 
 // Common set-up of a workgroup's GEMM state (weights of one expert slice;
 // K = reduction length; rs = K/32 scale bytes per weight row).
-template <int BM, bool kFP4A, bool kW8, int KV>
-__device__ __forceinline__ void setup(TiledGemm<BM, kFP4A, kW8, KV>& G, const TileT& ti, int K,
+template <int BM, bool kFP4A, bool kW8, int KV, bool kBlk>
+__device__ __forceinline__ void setup(TiledGemm<BM, kFP4A, kW8, KV, kBlk>& G, const TileT& ti, int K,
                                       const uint8_t* wq, const uint8_t* wsc, int wrows) {
   G.lane = threadIdx.x & 63;
   G.wave = threadIdx.x >> 6;
@@ -465,9 +471,9 @@ __device__ __forceinline__ void with_nmt(int rows, F&& f) {
 // Static LDS of a kernel: NS stage arrays (separate objects), the weight
 // scales, and for MXFP4 activations their scales and the tile's source
 // rows; body(stages, scales, act_scales, src_rows) runs with them.
-template <int BM, bool kFP4A, bool kW8, int KV, class Body>
+template <int BM, bool kFP4A, bool kW8, int KV, bool kBlk, class Body>
 __device__ __forceinline__ void with_lds(Body&& body) {
-  using Cfg = TileCfg<BM, kFP4A, kW8, KV>;
+  using Cfg = TileCfg<BM, kFP4A, kW8, KV, kBlk>;
   constexpr int XB = Cfg::XB, SCB = Cfg::SCB;
   __shared__ __align__(16) uint8_t sc[SCB];
   __shared__ __align__(16) uint8_t st0[XB];
@@ -500,16 +506,26 @@ __device__ __forceinline__ void with_lds(Body&& body) {
 // activation-code offsets and the activation-scale rows), then the pipeline.
 // direct(r) = source row of tile row r < rows; wrow(r) = byte offset of
 // weight scale row r; arow_bytes = activation scale bytes per source row.
-template <int BM, bool kFP4A, bool kW8, int KV, class Direct, class WRow>
-__device__ __forceinline__ void tile_loop(TiledGemm<BM, kFP4A, kW8, KV>& G, const TileT& ti, Direct direct,
+template <int BM, bool kFP4A, bool kW8, int KV, bool kBlk, class Direct, class WRow>
+__device__ __forceinline__ void tile_loop(TiledGemm<BM, kFP4A, kW8, KV, kBlk>& G, const TileT& ti, Direct direct,
                                           WRow wrow, uint32_t row_bytes, uint32_t arow_bytes,
                                           floatx4_t (&acc)[BM / 16][4]) {
-  with_lds<BM, kFP4A, kW8, KV>([&](auto& stages, uint8_t* sc, uint8_t* asc, int32_t* srow) {
-    if constexpr (kFP4A) {
+  with_lds<BM, kFP4A, kW8, KV, kBlk>([&](auto& stages, uint8_t* sc, uint8_t* asc, int32_t* srow) {
+    if constexpr (kBlk) {
+      plan_x<BM, kFP4A, kW8, KV, kBlk>(G, ti, direct, row_bytes);
+      // scales of sorted row s, chunk 0: ((s / 16) * C) * 64 + (s % 16) * 4
+      auto arow = [&](int r) -> uint32_t {
+        const uint32_t s = (uint32_t)(ti.row0 + r);
+        return r < ti.rows ? (s >> 4) * (arow_bytes / 4) * 64u + (s & 15) * 4u : kOOR;
+      };
+      with_nmt<BM>(ti.rows, [&](auto n) {
+        G.template run<decltype(n)::value>(stages, sc, asc, wrow, arow, acc);
+      });
+    } else if constexpr (kFP4A) {
       const int t = threadIdx.x;
       if (t < BM) srow[t] = t < ti.rows ? (int32_t)direct(t) : 0;
       __syncthreads();
-      plan_x<BM, kFP4A, kW8, KV>(G, ti, [&](int r) { return (uint32_t)srow[r]; }, row_bytes);
+      plan_x<BM, kFP4A, kW8, KV, kBlk>(G, ti, [&](int r) { return (uint32_t)srow[r]; }, row_bytes);
       auto arow = [&](int r) -> uint32_t {
         return r < ti.rows ? (uint32_t)srow[r] * arow_bytes : kOOR;
       };
@@ -517,7 +533,7 @@ __device__ __forceinline__ void tile_loop(TiledGemm<BM, kFP4A, kW8, KV>& G, cons
         G.template run<decltype(n)::value>(stages, sc, asc, wrow, arow, acc);
       });
     } else {
-      plan_x<BM, kFP4A, kW8, KV>(G, ti, direct, row_bytes);
+      plan_x<BM, kFP4A, kW8, KV, kBlk>(G, ti, direct, row_bytes);
       auto arow = [](int) -> uint32_t { return kOOR; };
       with_nmt<BM>(ti.rows, [&](auto n) {
         G.template run<decltype(n)::value>(stages, sc, asc, wrow, arow, acc);
@@ -528,7 +544,7 @@ __device__ __forceinline__ void tile_loop(TiledGemm<BM, kFP4A, kW8, KV>& G, cons
 
 // gate/up + SwiGLU: weight rows gate [i0, i0 + 128) and up [I + i0, I + i0 + 128),
 // i0 = 128 s; wave w owns i in [i0 + 32 w, i0 + 32 w + 32): strips gate lo/hi, up lo/hi.
-template <int BM, bool kFP4A, bool kW8, int KV = 0>
+template <int BM, bool kFP4A, bool kW8, int KV = 0, bool kBlk = false>
 __global__ __launch_bounds__(256, KV ? 2 : 1) void gate_up_tiled_kernel(
     const void* __restrict__ act, const uint8_t* __restrict__ act_scale,
     const int32_t* __restrict__ sorted, const int32_t* __restrict__ offsets,
@@ -538,7 +554,7 @@ __global__ __launch_bounds__(256, KV ? 2 : 1) void gate_up_tiled_kernel(
   TileT ti;
   int s;
   if (!tile_slice<BM, kFP4A>(blockIdx.x, tiles, offsets, *num_tiles, I / 128, &ti, &s)) return;
-  TiledGemm<BM, kFP4A, kW8, KV> G;
+  TiledGemm<BM, kFP4A, kW8, KV, kBlk> G;
   setup(G, ti, H, w13, w13s, 2 * I);
   const int nl = G.nl, g = G.g;
   const uint32_t rb = H / 2, rs = H / 32;
@@ -547,8 +563,10 @@ __global__ __launch_bounds__(256, KV ? 2 : 1) void gate_up_tiled_kernel(
 #pragma unroll
   for (int st = 0; st < 4; ++st) G.wo[st] = wnat_lane(rows4[st] >> 4, H, G.NQ, G.lane);
   if (kFP4A) {
-    G.a = make_rsrc(act, (uint32_t)((size_t)T * rb));
-    G.as = make_rsrc(act_scale, (uint32_t)((size_t)T * rs));
+    // per token, or (blocked) per sorted row in whole 16-row blocks
+    const size_t nr = kBlk ? ((size_t)T * Kp + 15) / 16 * 16 : (size_t)T;
+    G.a = make_rsrc(act, (uint32_t)(nr * rb));
+    G.as = make_rsrc(act_scale, (uint32_t)(nr * rs));
   } else {
     G.a = make_rsrc(act, (uint32_t)((size_t)T * H * 2));
   }
@@ -566,7 +584,7 @@ __global__ __launch_bounds__(256, KV ? 2 : 1) void gate_up_tiled_kernel(
   for (int mt = 0; mt < BM / 16; ++mt)
 #pragma unroll
     for (int st = 0; st < 4; ++st) acc[mt][st] = (floatx4_t){0.f, 0.f, 0.f, 0.f};
-  tile_loop<BM, kFP4A, kW8, KV>(G, ti, token, wrow, kFP4A ? rb : (uint32_t)H * 2, rs, acc);
+  tile_loop<BM, kFP4A, kW8, KV, kBlk>(G, ti, token, wrow, kFP4A ? rb : (uint32_t)H * 2, rs, acc);
 
 #pragma unroll
   for (int mt = 0; mt < BM / 16; ++mt)
@@ -582,7 +600,7 @@ __global__ __launch_bounds__(256, KV ? 2 : 1) void gate_up_tiled_kernel(
 }
 
 // down: weight rows j in [256 s, 256 s + 256); wave w owns [256 s + 64 w, +64).
-template <int BM, bool kFP4A, bool kW8, int KV = 0>
+template <int BM, bool kFP4A, bool kW8, int KV = 0, bool kBlk = false>
 __global__ __launch_bounds__(256, KV ? 2 : 1) void down_tiled_kernel(
     const void* __restrict__ hin, const uint8_t* __restrict__ hscale,
     const int32_t* __restrict__ offsets, const int32_t* __restrict__ tiles,
@@ -591,7 +609,7 @@ __global__ __launch_bounds__(256, KV ? 2 : 1) void down_tiled_kernel(
   TileT ti;
   int s;
   if (!tile_slice<BM, kFP4A, 4>(blockIdx.x, tiles, offsets, *num_tiles, H / 256, &ti, &s)) return;
-  TiledGemm<BM, kFP4A, kW8, KV> G;
+  TiledGemm<BM, kFP4A, kW8, KV, kBlk> G;
   setup(G, ti, I, w2, w2s, H);
   const int nl = G.nl, g = G.g;
   const uint32_t rb = I / 2, rs = I / 32;
@@ -599,8 +617,9 @@ __global__ __launch_bounds__(256, KV ? 2 : 1) void down_tiled_kernel(
 #pragma unroll
   for (int st = 0; st < 4; ++st) G.wo[st] = wnat_lane((j0 >> 4) + st, I, G.NQ, G.lane);
   if (kFP4A) {
-    G.a = make_rsrc(hin, (uint32_t)((size_t)A * rb));
-    G.as = make_rsrc(hscale, (uint32_t)((size_t)A * rs));
+    const size_t nr = kBlk ? ((size_t)A + 15) / 16 * 16 : (size_t)A;
+    G.a = make_rsrc(hin, (uint32_t)(nr * rb));
+    G.as = make_rsrc(hscale, (uint32_t)(nr * rs));
   } else {
     G.a = make_rsrc(hin, (uint32_t)((size_t)A * I * 2));
   }
@@ -612,7 +631,7 @@ __global__ __launch_bounds__(256, KV ? 2 : 1) void down_tiled_kernel(
   for (int mt = 0; mt < BM / 16; ++mt)
 #pragma unroll
     for (int st = 0; st < 4; ++st) acc[mt][st] = (floatx4_t){0.f, 0.f, 0.f, 0.f};
-  tile_loop<BM, kFP4A, kW8, KV>(G, ti, srow, wrow, kFP4A ? rb : (uint32_t)I * 2, rs, acc);
+  tile_loop<BM, kFP4A, kW8, KV, kBlk>(G, ti, srow, wrow, kFP4A ? rb : (uint32_t)I * 2, rs, acc);
 
 #pragma unroll
   for (int mt = 0; mt < BM / 16; ++mt)
@@ -627,25 +646,25 @@ __global__ __launch_bounds__(256, KV ? 2 : 1) void down_tiled_kernel(
     }
 }
 
-template <int BM, bool kFP4A, bool kW8 = false, int KV = 0>
+template <int BM, bool kFP4A, bool kW8 = false, int KV = 0, bool kBlk = false>
 hipError_t launch_gate_up_bm(const void* act, const uint8_t* act_scale, const int32_t* sorted,
                              const int32_t* offsets, const int32_t* tiles,
                              const int32_t* num_tiles, int max_tiles, const uint8_t* w13,
                              const uint8_t* w13s, int T, int H, int I, int Kp, uint16_t* h,
                              hipStream_t stream) {
   const unsigned grid = tile_slice_grid<kFP4A>(max_tiles, I / 128);
-  hipLaunchKernelGGL((gate_up_tiled_kernel<BM, kFP4A, kW8, KV>), dim3(grid), dim3(256), 0, stream, act,
+  hipLaunchKernelGGL((gate_up_tiled_kernel<BM, kFP4A, kW8, KV, kBlk>), dim3(grid), dim3(256), 0, stream, act,
                      act_scale, sorted, offsets, tiles, num_tiles, w13, w13s, T, H, I, Kp, h);
   return hipGetLastError();
 }
 
-template <int BM, bool kFP4A, bool kW8 = false, int KV = 0>
+template <int BM, bool kFP4A, bool kW8 = false, int KV = 0, bool kBlk = false>
 hipError_t launch_down_bm(const void* h, const uint8_t* h_scale, const int32_t* offsets,
                           const int32_t* tiles, const int32_t* num_tiles, int max_tiles,
                           const uint8_t* w2, const uint8_t* w2s, int A, int H, int I, uint16_t* y,
                           hipStream_t stream) {
   const unsigned grid = tile_slice_grid<kFP4A>(max_tiles, H / 256);
-  hipLaunchKernelGGL((down_tiled_kernel<BM, kFP4A, kW8, KV>), dim3(grid), dim3(256), 0, stream, h,
+  hipLaunchKernelGGL((down_tiled_kernel<BM, kFP4A, kW8, KV, kBlk>), dim3(grid), dim3(256), 0, stream, h,
                      h_scale, offsets, tiles, num_tiles, w2, w2s, A, H, I, y);
   return hipGetLastError();
 }
@@ -653,6 +672,39 @@ hipError_t launch_down_bm(const void* h, const uint8_t* h_scale, const int32_t* 
 template <int BM, bool kFP4A, bool kW8 = false>
 bool fits(int H, int I) {
   return H <= TileCfg<BM, kFP4A, kW8>::KMAX && I <= TileCfg<BM, kFP4A, kW8>::KMAX;
+}
+
+// MXFP4 activations, per token (kBlk false) or in the blocked sorted-row
+// order: 256-, 128- (variant by reduction length) or 64-row tiles.
+template <bool kBlk>
+hipError_t gate_up_fp4(int tile_m, const void* act, const uint8_t* act_scale,
+                       const int32_t* sorted, const int32_t* offsets, const int32_t* tiles,
+                       const int32_t* num_tiles, int max_tiles, const uint8_t* w13,
+                       const uint8_t* w13s, int T, int H, int I, int Kp, uint16_t* h,
+                       hipStream_t stream) {
+#define MOE_GU_ARGS act, act_scale, sorted, offsets, tiles, num_tiles, max_tiles, w13, w13s, T, H, I, Kp, h, stream
+  if (tile_m == 256) return launch_gate_up_bm<256, true, false, 0, kBlk>(MOE_GU_ARGS);
+  if (tile_m == 128)
+    return H <= 2048   ? launch_gate_up_bm<128, true, false, 1, kBlk>(MOE_GU_ARGS)
+           : H <= 6144 ? launch_gate_up_bm<128, true, false, 2, kBlk>(MOE_GU_ARGS)
+                       : launch_gate_up_bm<128, true, false, 0, kBlk>(MOE_GU_ARGS);
+  return launch_gate_up_bm<64, true, false, 0, kBlk>(MOE_GU_ARGS);
+#undef MOE_GU_ARGS
+}
+
+template <bool kBlk>
+hipError_t down_fp4(int tile_m, const void* h, const uint8_t* h_scale, const int32_t* offsets,
+                    const int32_t* tiles, const int32_t* num_tiles, int max_tiles,
+                    const uint8_t* w2, const uint8_t* w2s, int A, int H, int I, uint16_t* y,
+                    hipStream_t stream) {
+#define MOE_DN_ARGS h, h_scale, offsets, tiles, num_tiles, max_tiles, w2, w2s, A, H, I, y, stream
+  if (tile_m == 256) return launch_down_bm<256, true, false, 0, kBlk>(MOE_DN_ARGS);
+  if (tile_m == 128)
+    return I <= 2048   ? launch_down_bm<128, true, false, 1, kBlk>(MOE_DN_ARGS)
+           : I <= 6144 ? launch_down_bm<128, true, false, 2, kBlk>(MOE_DN_ARGS)
+                       : launch_down_bm<128, true, false, 0, kBlk>(MOE_DN_ARGS);
+  return launch_down_bm<64, true, false, 0, kBlk>(MOE_DN_ARGS);
+#undef MOE_DN_ARGS
 }
 
 }  // namespace
@@ -669,6 +721,8 @@ bool expert_gemm_tiled_supported(int tile_m, int act_fmt, int H, int I, int wfmt
   return false;
 }
 
+// act_fmt: 0 bf16, 1 MXFP4 per token (gate/up) or per sorted row (down),
+// 2 MXFP4 in the blocked sorted-row order.
 hipError_t launch_gate_up_tiled(int tile_m, int act_fmt, int wfmt, const void* act,
                                 const uint8_t* act_scale,
                                 const int32_t* sorted, const int32_t* offsets,
@@ -682,26 +736,18 @@ hipError_t launch_gate_up_tiled(int tile_m, int act_fmt, int wfmt, const void* a
                          : launch_gate_up_bm<64, false, true>(act, act_scale, sorted, offsets, tiles,
                                                               num_tiles, max_tiles, w13, w13s, T, H,
                                                               I, Kp, h, stream);
-  if (tile_m == 256 && act_fmt)
-    return launch_gate_up_bm<256, true>(act, act_scale, sorted, offsets, tiles, num_tiles,
-                                        max_tiles, w13, w13s, T, H, I, Kp, h, stream);
-  if (tile_m == 128)
-    return act_fmt ? (H <= 2048   ? launch_gate_up_bm<128, true, false, 1>(
-                                        act, act_scale, sorted, offsets, tiles, num_tiles,
-                                        max_tiles, w13, w13s, T, H, I, Kp, h, stream)
-                      : H <= 6144 ? launch_gate_up_bm<128, true, false, 2>(
-                                        act, act_scale, sorted, offsets, tiles, num_tiles,
-                                        max_tiles, w13, w13s, T, H, I, Kp, h, stream)
-                                  : launch_gate_up_bm<128, true>(act, act_scale, sorted, offsets,
-                                                                 tiles, num_tiles, max_tiles, w13,
-                                                                 w13s, T, H, I, Kp, h, stream))
-                   : launch_gate_up_bm<128, false>(act, act_scale, sorted, offsets, tiles,
-                                                    num_tiles, max_tiles, w13, w13s, T, H, I, Kp,
-                                                    h, stream);
-  return act_fmt ? launch_gate_up_bm<64, true>(act, act_scale, sorted, offsets, tiles, num_tiles,
-                                                max_tiles, w13, w13s, T, H, I, Kp, h, stream)
-                 : launch_gate_up_bm<64, false>(act, act_scale, sorted, offsets, tiles, num_tiles,
-                                                 max_tiles, w13, w13s, T, H, I, Kp, h, stream);
+  if (act_fmt == 2)
+    return gate_up_fp4<true>(tile_m, act, act_scale, sorted, offsets, tiles, num_tiles, max_tiles,
+                             w13, w13s, T, H, I, Kp, h, stream);
+  if (act_fmt)
+    return gate_up_fp4<false>(tile_m, act, act_scale, sorted, offsets, tiles, num_tiles, max_tiles,
+                              w13, w13s, T, H, I, Kp, h, stream);
+  return tile_m == 128 ? launch_gate_up_bm<128, false>(act, act_scale, sorted, offsets, tiles,
+                                                       num_tiles, max_tiles, w13, w13s, T, H, I, Kp,
+                                                       h, stream)
+                       : launch_gate_up_bm<64, false>(act, act_scale, sorted, offsets, tiles,
+                                                      num_tiles, max_tiles, w13, w13s, T, H, I, Kp,
+                                                      h, stream);
 }
 
 hipError_t launch_down_tiled(int tile_m, int act_fmt, int wfmt, const void* h,
@@ -715,23 +761,14 @@ hipError_t launch_down_tiled(int tile_m, int act_fmt, int wfmt, const void* h,
                                                             max_tiles, w2, w2s, A, H, I, y, stream)
                          : launch_down_bm<64, false, true>(h, h_scale, offsets, tiles, num_tiles,
                                                            max_tiles, w2, w2s, A, H, I, y, stream);
-  if (tile_m == 256 && act_fmt)
-    return launch_down_bm<256, true>(h, h_scale, offsets, tiles, num_tiles, max_tiles, w2, w2s, A,
-                                     H, I, y, stream);
-  if (tile_m == 128)
-    return act_fmt ? (I <= 2048   ? launch_down_bm<128, true, false, 1>(h, h_scale, offsets, tiles,
-                                                                        num_tiles, max_tiles, w2,
-                                                                        w2s, A, H, I, y, stream)
-                      : I <= 6144 ? launch_down_bm<128, true, false, 2>(h, h_scale, offsets, tiles,
-                                                                        num_tiles, max_tiles, w2,
-                                                                        w2s, A, H, I, y, stream)
-                                  : launch_down_bm<128, true>(h, h_scale, offsets, tiles,
-                                                              num_tiles, max_tiles, w2, w2s, A, H,
-                                                              I, y, stream))
-                   : launch_down_bm<128, false>(h, h_scale, offsets, tiles, num_tiles, max_tiles,
-                                                 w2, w2s, A, H, I, y, stream);
-  return act_fmt ? launch_down_bm<64, true>(h, h_scale, offsets, tiles, num_tiles, max_tiles, w2,
-                                             w2s, A, H, I, y, stream)
-                 : launch_down_bm<64, false>(h, h_scale, offsets, tiles, num_tiles, max_tiles, w2,
-                                              w2s, A, H, I, y, stream);
+  if (act_fmt == 2)
+    return down_fp4<true>(tile_m, h, h_scale, offsets, tiles, num_tiles, max_tiles, w2, w2s, A, H,
+                          I, y, stream);
+  if (act_fmt)
+    return down_fp4<false>(tile_m, h, h_scale, offsets, tiles, num_tiles, max_tiles, w2, w2s, A, H,
+                           I, y, stream);
+  return tile_m == 128 ? launch_down_bm<128, false>(h, h_scale, offsets, tiles, num_tiles, max_tiles,
+                                                    w2, w2s, A, H, I, y, stream)
+                       : launch_down_bm<64, false>(h, h_scale, offsets, tiles, num_tiles, max_tiles,
+                                                   w2, w2s, A, H, I, y, stream);
 }

@@ -29,6 +29,12 @@ hipError_t launch_align_sort(const int32_t* ids, int A, int Ep, int tile_m, int3
 
 hipError_t launch_mxfp4_quant(const void* src, int src_is_bf16, int64_t rows, int64_t cols,
                               uint8_t* packed, uint8_t* scales, hipStream_t stream);
+// MXFP4 quantisation into the blocked row order of the tiled GEMMs' MXFP4
+// activations (cols a multiple of 128): source row t to output rows
+// map[t * Kp + k] < out_rows, k < Kp (or to row t without a map).
+hipError_t launch_mxfp4_quant_blocked(const void* src, int src_is_bf16, int64_t rows, int64_t cols,
+                                      const int32_t* map, int Kp, int64_t out_rows,
+                                      uint8_t* packed, uint8_t* scales, hipStream_t stream);
 hipError_t launch_mxfp8_quant(const void* src, int src_is_bf16, int64_t rows, int64_t cols,
                               uint8_t* codes, uint8_t* scales, hipStream_t stream);
 // row-major weight codes -> native code order (nq = 1 MXFP4, 2 MXFP8)

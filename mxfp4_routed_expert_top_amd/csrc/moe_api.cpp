@@ -15,6 +15,11 @@ constexpr size_t kAlign = 256;
 
 inline size_t round_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 inline bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+// The GEMM kernels address each expert's weight codes, the activation rows
+// and h with 32-bit buffer offsets in which bit 31 marks a row that is not
+// there (the load returns zeros): every such buffer stays below 2 GiB.
+constexpr int64_t kMaxBufferBytes = (int64_t)1 << 31;
 inline hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
 inline moe_status from_hip(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_DEVICE; }
 
@@ -73,12 +78,15 @@ FwdLayout forward_layout(int64_t T, int64_t H, int64_t I, int64_t E, int64_t K, 
   L.tiles = take(max_tiles_for(A, Ep) * 2 * 4);
   L.ntiles = take(4);
   L.scratch = take(align_scratch_bytes((int)A, (int)Ep));
+  // MXFP4 activations: per token (decode kernels) or per sorted row in the
+  // blocked order (tiled kernels), A16 >= T rows either way
   const bool q = act_fmt == MOE_ACT_MXFP4;
-  L.xq = take(q ? T * H / 2 : 0);
-  L.xs = take(q ? T * H / 32 : 0);
+  const int64_t A16 = (A + 15) / 16 * 16;
+  L.xq = take(q ? A16 * H / 2 : 0);
+  L.xs = take(q ? A16 * H / 32 : 0);
   L.h = take(A * I * 2);
-  L.hq = take(q ? A * I / 2 : 0);
-  L.hs = take(q ? A * I / 32 : 0);
+  L.hq = take(q ? A16 * I / 2 : 0);
+  L.hs = take(q ? A16 * I / 32 : 0);
   // y; the router GEMM's partial sums (when the call routes from x) live in
   // the same bytes: routing consumes them before the down GEMM writes y
   L.y = take(std::max((size_t)(A * H * 2), router_workspace_bytes((int)T, (int)H, (int)Ep)));
@@ -197,6 +205,27 @@ moe_status moe_mxfp4_quantize(const void* src, int32_t src_dtype, int64_t rows, 
                                      as_stream(stream)));
 }
 
+moe_status moe_mxfp4_quantize_blocked(const void* src, int32_t src_dtype, int64_t rows,
+                                      int64_t cols, const int32_t* row_map, int32_t Kp,
+                                      int64_t out_rows, uint8_t* packed, uint8_t* scales,
+                                      void* stream) {
+  if (rows < 0 || cols < 0 || out_rows < 0 || (src_dtype != MOE_SRC_F32 && src_dtype != MOE_SRC_BF16))
+    return MOE_ERR_INVALID_ARGUMENT;
+  if (row_map ? Kp < 1 : out_rows < rows) return MOE_ERR_INVALID_ARGUMENT;
+  if (cols % 128) return MOE_ERR_UNSUPPORTED;
+  const int64_t out16 = (out_rows + 15) / 16 * 16;
+  const int64_t grid = row_map ? rows * ((cols / 8 + 255) / 256) : out16 / 16 * ((cols / 128 + 3) / 4);
+  if (out16 * (cols / 2) >= kMaxBufferBytes || (row_map && rows * Kp >= INT32_MAX) ||
+      cols > ((int64_t)1 << 30) || grid >= (int64_t)UINT32_MAX)
+    return MOE_ERR_UNSUPPORTED;                          // 32-bit offsets, columns and grid
+  if (rows == 0 || cols == 0) return MOE_OK;
+  if (!src || !packed || !scales || !aligned16(src) || !aligned16(packed) || !aligned16(scales))
+    return MOE_ERR_INVALID_ARGUMENT;
+  return from_hip(launch_mxfp4_quant_blocked(src, src_dtype == MOE_SRC_BF16, rows, cols, row_map,
+                                             row_map ? Kp : 1, out_rows, packed, scales,
+                                             as_stream(stream)));
+}
+
 moe_status moe_mxfp8_quantize(const void* src, int32_t src_dtype, int64_t rows, int64_t cols,
                               uint8_t* codes, uint8_t* scales, void* stream) {
   if (rows < 0 || cols < 0 || (src_dtype != MOE_SRC_F32 && src_dtype != MOE_SRC_BF16))
@@ -227,19 +256,20 @@ moe_status moe_weights_to_native(const uint8_t* src, int32_t wfmt, int64_t rows,
 
 namespace {
 
-// The GEMM kernels address each expert's weight codes, the activation rows
-// and h with 32-bit buffer offsets in which bit 31 marks a row that is not
-// there (the load returns zeros): every such buffer stays below 2 GiB.
-constexpr int64_t kMaxBufferBytes = (int64_t)1 << 31;
-
 // Weight code bytes of one expert's W13 (2I rows) or W2 (H rows).
 bool weights_fit(int wfmt, int64_t rows, int64_t k) {
   return rows * (wfmt == 1 ? k : k / 2) < kMaxBufferBytes;
 }
 
-// rows x cols activations (bf16, or MXFP4 codes).
+// rows x cols activations (bf16, or MXFP4 codes; blocked rows come in whole
+// 16-row blocks).
 bool acts_fit(int act_fmt, int64_t rows, int64_t cols) {
-  return rows * (act_fmt == MOE_ACT_MXFP4 ? cols / 2 : cols * 2) < kMaxBufferBytes;
+  if (act_fmt == MOE_ACT_MXFP4_BLOCKED) rows = (rows + 15) / 16 * 16;
+  return rows * (act_fmt == MOE_ACT_BF16 ? cols * 2 : cols / 2) < kMaxBufferBytes;
+}
+
+bool act_fmt_ok(int32_t act_fmt) {
+  return act_fmt == MOE_ACT_BF16 || act_fmt == MOE_ACT_MXFP4 || act_fmt == MOE_ACT_MXFP4_BLOCKED;
 }
 
 moe_status gate_up_impl(const void* act, const uint8_t* act_scale, int32_t act_fmt, int wfmt,
@@ -247,19 +277,21 @@ moe_status gate_up_impl(const void* act, const uint8_t* act_scale, int32_t act_f
                         const int32_t* tile_table, const int32_t* num_tiles, int32_t tile_m,
                         const uint8_t* w13, const uint8_t* w13_scale, int32_t T, int32_t H,
                         int32_t I, int32_t Ep, int32_t Kp, uint16_t* h, void* stream) {
-  if (T < 0 || Ep < 1 || Kp < 1 || (act_fmt != MOE_ACT_BF16 && act_fmt != MOE_ACT_MXFP4))
-    return MOE_ERR_INVALID_ARGUMENT;
+  if (T < 0 || Ep < 1 || Kp < 1 || !act_fmt_ok(act_fmt)) return MOE_ERR_INVALID_ARGUMENT;
   moe_status st = check_shape_HI(H, I);
   if (st != MOE_OK) return st;
-  if (Ep > 2048 || !weights_fit(wfmt, 2 * (int64_t)I, H) || !acts_fit(act_fmt, T, H))
+  const bool blk = act_fmt == MOE_ACT_MXFP4_BLOCKED;
+  if (Ep > 2048 || !weights_fit(wfmt, 2 * (int64_t)I, H) ||
+      !acts_fit(act_fmt, blk ? (int64_t)T * Kp : T, H))
     return MOE_ERR_UNSUPPORTED;
-  if (!tile_m_ok(tile_m, act_fmt, H, I, wfmt))
+  if (!tile_m_ok(tile_m, act_fmt, H, I, wfmt) || (blk && tile_m == MOE_TILE_M))
     return MOE_ERR_UNSUPPORTED;
   if (T == 0) return MOE_OK;
   if (!act || !sorted_assign || !expert_offsets || !tile_table || !num_tiles || !w13 ||
-      !w13_scale || !h || (act_fmt == MOE_ACT_MXFP4 && !act_scale))
+      !w13_scale || !h || (act_fmt != MOE_ACT_BF16 && !act_scale))
     return MOE_ERR_INVALID_ARGUMENT;
-  if (!aligned16(act) || !aligned16(w13)) return MOE_ERR_INVALID_ARGUMENT;
+  if (!aligned16(act) || !aligned16(w13) || (blk && !aligned16(act_scale)))
+    return MOE_ERR_INVALID_ARGUMENT;
   const int64_t mt = max_tiles_for((int64_t)T * Kp, Ep, tile_m);
   if (mt * (I / 16) >= INT32_MAX) return MOE_ERR_UNSUPPORTED;
   hipStream_t s = as_stream(stream);
@@ -277,19 +309,20 @@ moe_status down_impl(const void* h, const uint8_t* h_scale, int32_t act_fmt, int
                      const int32_t* num_tiles, int32_t tile_m, const uint8_t* w2,
                      const uint8_t* w2_scale, int32_t T, int32_t H, int32_t I, int32_t Ep,
                      int32_t Kp, uint16_t* y, void* stream) {
-  if (T < 0 || Ep < 1 || Kp < 1 || (act_fmt != MOE_ACT_BF16 && act_fmt != MOE_ACT_MXFP4))
-    return MOE_ERR_INVALID_ARGUMENT;
+  if (T < 0 || Ep < 1 || Kp < 1 || !act_fmt_ok(act_fmt)) return MOE_ERR_INVALID_ARGUMENT;
   moe_status st = check_shape_HI(H, I);
   if (st != MOE_OK) return st;
+  const bool blk = act_fmt == MOE_ACT_MXFP4_BLOCKED;
   if (Ep > 2048 || !weights_fit(wfmt, H, I) || !acts_fit(act_fmt, (int64_t)T * Kp, I))
     return MOE_ERR_UNSUPPORTED;
-  if (!tile_m_ok(tile_m, act_fmt, H, I, wfmt))
+  if (!tile_m_ok(tile_m, act_fmt, H, I, wfmt) || (blk && tile_m == MOE_TILE_M))
     return MOE_ERR_UNSUPPORTED;
   if (T == 0) return MOE_OK;
   if (!h || !expert_offsets || !tile_table || !num_tiles || !w2 || !w2_scale || !y ||
-      (act_fmt == MOE_ACT_MXFP4 && !h_scale))
+      (act_fmt != MOE_ACT_BF16 && !h_scale))
     return MOE_ERR_INVALID_ARGUMENT;
-  if (!aligned16(h) || !aligned16(w2)) return MOE_ERR_INVALID_ARGUMENT;
+  if (!aligned16(h) || !aligned16(w2) || (blk && !aligned16(h_scale)))
+    return MOE_ERR_INVALID_ARGUMENT;
   const int64_t mt = max_tiles_for((int64_t)T * Kp, Ep, tile_m);
   if (mt * (H / 128) >= INT32_MAX) return MOE_ERR_UNSUPPORTED;
   hipStream_t s = as_stream(stream);
@@ -441,27 +474,34 @@ moe_status forward_impl(const uint16_t* x, const float* router_logits,
   if (e != hipSuccess) return MOE_ERR_DEVICE;
   e = launch_align_sort(ids, (int)A, Ep, tm, counts, offsets, sorted, inv, tiles, ntiles, scratch, s);
   if (e != hipSuccess) return MOE_ERR_DEVICE;
+  // W4A4 on the tiled kernels: x quantised once per token and written into
+  // each of its sorted slots, h in its sorted rows, both in the blocked order
+  // (contiguous per 16 rows and chunk instead of gathered rows)
   const bool q = act_fmt == MOE_ACT_MXFP4;
+  const bool blk = q && tm != MOE_TILE_M;
+  const int32_t gemm_act = blk ? MOE_ACT_MXFP4_BLOCKED : act_fmt;
   if (q) {
-    e = launch_mxfp4_quant(x, 1, T, H, xq, xs, s);
+    e = blk ? launch_mxfp4_quant_blocked(x, 1, T, H, inv, Kp, A, xq, xs, s)
+            : launch_mxfp4_quant(x, 1, T, H, xq, xs, s);
     if (e != hipSuccess) return MOE_ERR_DEVICE;
   }
   const void* a1 = q ? (const void*)xq : (const void*)x;
   const uint8_t* a1s = q ? xs : nullptr;
   e = tm != MOE_TILE_M
-          ? launch_gate_up_tiled(tm, act_fmt, wfmt, a1, a1s, sorted, offsets, tiles, ntiles, mt, w13,
+          ? launch_gate_up_tiled(tm, gemm_act, wfmt, a1, a1s, sorted, offsets, tiles, ntiles, mt, w13,
                                  w13_scale, T, H, I, Kp, h, s)
           : launch_gate_up(act_fmt, wfmt, a1, a1s, sorted, offsets, tiles, ntiles, mt, w13,
                            w13_scale, T, H, I, Kp, h, s);
   if (e != hipSuccess) return MOE_ERR_DEVICE;
   if (q) {
-    e = launch_mxfp4_quant(h, 1, A, I, hq, hs, s);
+    e = blk ? launch_mxfp4_quant_blocked(h, 1, A, I, nullptr, 1, A, hq, hs, s)
+            : launch_mxfp4_quant(h, 1, A, I, hq, hs, s);
     if (e != hipSuccess) return MOE_ERR_DEVICE;
   }
   const void* a2 = q ? (const void*)hq : (const void*)h;
   const uint8_t* a2s = q ? hs : nullptr;
   e = tm != MOE_TILE_M
-          ? launch_down_tiled(tm, act_fmt, wfmt, a2, a2s, offsets, tiles, ntiles, mt, w2, w2_scale,
+          ? launch_down_tiled(tm, gemm_act, wfmt, a2, a2s, offsets, tiles, ntiles, mt, w2, w2_scale,
                               (int)A, H, I, y, s)
           : launch_down(act_fmt, wfmt, a2, a2s, offsets, tiles, ntiles, mt, w2, w2_scale, (int)A, H,
                         I, y, s);

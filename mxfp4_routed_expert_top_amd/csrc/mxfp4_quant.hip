@@ -83,7 +83,133 @@ __global__ __launch_bounds__(256) void mxfp4_quant_kernel(const void* __restrict
   scales[b] = sc;
 }
 
+// The same rule, written in the blocked row order the tiled GEMMs read:
+// output row p's chunk c (elements [128 c, 128 c + 128)) has its 64 code
+// bytes at ((p / 16) * C + c) * 1024 + (p % 16) * 64 and its four scale
+// bytes at ((p / 16) * C + c) * 64 + (p % 16) * 4 (C = cols / 128).
+//
+// Row p from source row p: a workgroup owns 16-row output block b and
+// kChunksPerGroup chunks of it.  Lane L = 16 r + k takes elements
+// [8 k, 8 k + 8) of row 16 b + r's chunk (one 16-byte bf16 load: each row's
+// chunk is 256 contiguous bytes); the four lanes of a 32-block share its amax
+// through two lane swaps, and lane L writes the four code bytes of its 8
+// elements at byte 4 L of the block's KiB (the lane with k % 4 = 0 also the
+// scale byte): each block's codes and scales are stored whole by one
+// workgroup.
+constexpr int kChunksPerGroup = 4;
+
+// The 8 values at e quantised with the amax of the lane's aligned group of
+// four lanes (one 32-block): the four code bytes and the scale byte.
+template <bool kBf16>
+__device__ __forceinline__ uint32_t quant8_in_block(const void* src, int64_t e, uint8_t* scale) {
+  float v[8];
+  if (kBf16) {
+    const u32x4_t d = *reinterpret_cast<const u32x4_t*>(reinterpret_cast<const uint16_t*>(src) + e);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      v[2 * j] = __uint_as_float(d[j] << 16);
+      v[2 * j + 1] = __uint_as_float(d[j] & 0xFFFF0000u);
+    }
+  } else {
+    const float4 d0 = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(src) + e);
+    const float4 d1 = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(src) + e + 4);
+    v[0] = d0.x; v[1] = d0.y; v[2] = d0.z; v[3] = d0.w;
+    v[4] = d1.x; v[5] = d1.y; v[6] = d1.z; v[7] = d1.w;
+  }
+  float amax = 0.f;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) amax = fmaxf(amax, fabsf(v[j]));
+  amax = fmaxf(amax, __shfl_xor(amax, 1, MOE_WAVE));
+  amax = fmaxf(amax, __shfl_xor(amax, 2, MOE_WAVE));
+  const int ebits = (int)((__float_as_uint(amax) >> 23) & 0xFF);
+  const int X = max(ebits - 129, -127);                       // floor(log2 amax) - 2
+  const float inv = __uint_as_float((uint32_t)(127 - X) << 23);  // 2^-X, a normal float
+  uint32_t w = 0;
+#pragma unroll
+  for (int j = 0; j < 8; ++j)
+    w |= (e2m1_code(fabsf(v[j]) * inv) | ((__float_as_uint(v[j]) >> 31) << 3)) << (4 * j);
+  *scale = (uint8_t)(X + 127);
+  return w;
+}
+
+template <bool kBf16>
+__global__ __launch_bounds__(256) void mxfp4_quant_blocked_kernel(
+    const void* __restrict__ src, int64_t rows, int cols, int cgroups,
+    uint8_t* __restrict__ packed, uint8_t* __restrict__ scales) {
+  const int64_t b = blockIdx.x / cgroups;
+  const int cg = (int)(blockIdx.x - b * cgroups);
+  const int L = threadIdx.x, r = L >> 4, k = L & 15;
+  const int64_t t = 16 * b + r;
+  const bool live = t < rows;
+  const int C = cols / 128;
+  for (int cc = 0; cc < kChunksPerGroup; ++cc) {
+    const int c = cg * kChunksPerGroup + cc;
+    if (c >= C) break;                                   // uniform in the workgroup
+    uint8_t sc;
+    const uint32_t w = quant8_in_block<kBf16>(src, live ? t * cols + 128 * c + 8 * k : 0, &sc);
+    if (live) {
+      const int64_t blk = b * C + c;
+      *reinterpret_cast<uint32_t*>(packed + blk * 1024 + 4 * L) = w;
+      if ((k & 3) == 0) scales[blk * 64 + 4 * r + (k >> 2)] = sc;
+    }
+  }
+}
+
+// Source row t to output rows map[t * Kp + k], k < Kp (a value outside
+// [0, out_rows) writes nothing): workgroup b covers 2048 elements of source
+// row t = b / bpr, lane j of it elements [8 j', 8 j' + 8), j' = 256 (b % bpr)
+// + j; each lane writes its four code bytes (and, for k % 4 = 0, the scale
+// byte) into every output row of its source row.
+template <bool kBf16>
+__global__ __launch_bounds__(256) void mxfp4_quant_scatter_kernel(
+    const void* __restrict__ src, int bpr, int cols, const int32_t* __restrict__ map, int Kp,
+    int64_t out_rows, uint8_t* __restrict__ packed, uint8_t* __restrict__ scales) {
+  const int64_t t = blockIdx.x / bpr;
+  const int j8 = (int)(blockIdx.x - t * bpr) * 256 + (int)threadIdx.x;
+  const bool live = j8 < cols / 8;        // dead lanes come in aligned groups of four
+  uint8_t sc;
+  const uint32_t w = quant8_in_block<kBf16>(src, t * cols + 8 * (live ? j8 : 0), &sc);
+  if (!live) return;
+  const int col = 8 * j8;
+  const int64_t C = cols / 128;
+  const int64_t c = col >> 7;
+  const int g = (col >> 5) & 3, q = (col >> 3) & 3;
+  for (int k = 0; k < Kp; ++k) {
+    const int64_t p = map[t * Kp + k];
+    if (p < 0 || p >= out_rows) continue;
+    const int64_t blk = (p >> 4) * C + c;
+    *reinterpret_cast<uint32_t*>(packed + blk * 1024 + (p & 15) * 64 + 16 * g + 4 * q) = w;
+    if (q == 0) scales[blk * 64 + (p & 15) * 4 + g] = sc;
+  }
+}
+
 }  // namespace
+
+hipError_t launch_mxfp4_quant_blocked(const void* src, int src_is_bf16, int64_t rows, int64_t cols,
+                                      const int32_t* map, int Kp, int64_t out_rows,
+                                      uint8_t* packed, uint8_t* scales, hipStream_t stream) {
+  if (rows == 0 || cols == 0) return hipSuccess;
+  if (map) {
+    const int bpr = (int)((cols / 8 + 255) / 256);
+    const unsigned grid = (unsigned)(rows * bpr);
+    if (src_is_bf16)
+      hipLaunchKernelGGL(mxfp4_quant_scatter_kernel<true>, dim3(grid), dim3(256), 0, stream, src,
+                         bpr, (int)cols, map, Kp, out_rows, packed, scales);
+    else
+      hipLaunchKernelGGL(mxfp4_quant_scatter_kernel<false>, dim3(grid), dim3(256), 0, stream, src,
+                         bpr, (int)cols, map, Kp, out_rows, packed, scales);
+    return hipGetLastError();
+  }
+  const int cgroups = (int)((cols / 128 + kChunksPerGroup - 1) / kChunksPerGroup);
+  const unsigned grid = (unsigned)((rows + 15) / 16 * cgroups);
+  if (src_is_bf16)
+    hipLaunchKernelGGL(mxfp4_quant_blocked_kernel<true>, dim3(grid), dim3(256), 0, stream, src,
+                       rows, (int)cols, cgroups, packed, scales);
+  else
+    hipLaunchKernelGGL(mxfp4_quant_blocked_kernel<false>, dim3(grid), dim3(256), 0, stream, src,
+                       rows, (int)cols, cgroups, packed, scales);
+  return hipGetLastError();
+}
 
 // rows x cols values (cols a multiple of 32) are one flat run of blocks: the
 // packed output is [rows, cols/2] and the scales [rows, cols/32], row-major.

@@ -17,7 +17,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG, "libmoe_mxfp4.so")
 
 MOE_OK, MOE_ERR_INVALID_ARGUMENT, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE_TOO_SMALL, MOE_ERR_DEVICE = range(5)
-ACT_BF16, ACT_MXFP4 = 0, 1
+ACT_BF16, ACT_MXFP4, ACT_MXFP4_BLOCKED = 0, 1, 2
 W_MXFP4, W_MXFP8 = 0, 1            # expert weight formats
 SRC_F32, SRC_BF16 = 0, 1
 TILE_M = 32
@@ -40,6 +40,7 @@ _SIGS = {
     "moe_align_workspace_size": (_SZ, [_I32, _I32, _I32]),
     "moe_align_sort": (_I32, [_P, _I32, _I32, _I32, _I32, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
     "moe_mxfp4_quantize": (_I32, [_P, _I32, _I64, _I64, _P, _P, _P]),
+    "moe_mxfp4_quantize_blocked": (_I32, [_P, _I32, _I64, _I64, _P, _I32, _I64, _P, _P, _P]),
     "moe_expert_gate_up": (_I32, [_P, _P, _I32, _P, _P, _P, _P, _I32, _P, _P, _I32, _I32, _I32,
                                   _I32, _I32, _P, _P]),
     "moe_expert_down": (_I32, [_P, _P, _I32, _P, _P, _P, _I32, _P, _P, _I32, _I32, _I32, _I32,
@@ -211,6 +212,36 @@ def mxfp4_quantize(src, packed=None, scales=None, stream=None):
         scales = torch.empty(*lead, cols // 32, dtype=torch.uint8, device=src.device)
     _check("moe_mxfp4_quantize", lib().moe_mxfp4_quantize(
         _ptr(src), dt, rows, cols, _ptr(packed), _ptr(scales), _stream(stream)))
+    return packed, scales
+
+
+def mxfp4_quantize_blocked(src, row_map=None, Kp: int = 1, out_rows=None, packed=None,
+                           scales=None, stream=None):
+    """moe_mxfp4_quantize_blocked: fp32 or bf16 [rows, cols] -> (packed uint8
+    [R, cols/2], scales uint8 [R, cols/32]) in the blocked row order, R =
+    out_rows rounded up to 16; row_map (int32 [rows * Kp], e.g. a grouping's
+    inv) sends source row t to output rows row_map[t * Kp + k]."""
+    if src.dtype == torch.float32:
+        dt = SRC_F32
+    elif src.dtype == torch.bfloat16:
+        dt = SRC_BF16
+    else:
+        raise TypeError("src must be float32 or bfloat16")
+    rows, cols = src.shape
+    if out_rows is None:
+        out_rows = rows * Kp if row_map is not None else rows
+    r16 = (out_rows + 15) // 16 * 16
+    if packed is None:
+        packed = torch.empty(r16, cols // 2, dtype=torch.uint8, device=src.device)
+    if scales is None:
+        scales = torch.empty(r16, cols // 32, dtype=torch.uint8, device=src.device)
+    if row_map is not None:
+        _dt(row_map, torch.int32, "row_map")
+        if row_map.numel() < rows * Kp:
+            raise ValueError("row_map needs rows * Kp entries")
+    _check("moe_mxfp4_quantize_blocked", lib().moe_mxfp4_quantize_blocked(
+        _ptr(src), dt, rows, cols, _ptr(row_map), Kp, out_rows, _ptr(packed), _ptr(scales),
+        _stream(stream)))
     return packed, scales
 
 
@@ -439,9 +470,11 @@ def alloc_stages(T: int, H: int, I: int, E: int, K: int, shared: int, act_fmt: i
              y=torch.empty(A, H, dtype=torch.bfloat16, device=device),
              out=torch.empty(T, H, dtype=torch.bfloat16, device=device))
     if act_fmt == ACT_MXFP4:
+        # per token / sorted row, or sorted rows in the blocked order (tiled GEMMs)
         u8 = dict(dtype=torch.uint8, device=device)
-        b.update(xq=torch.empty(T, H // 2, **u8), xs=torch.empty(T, H // 32, **u8),
-                 hq=torch.empty(A, I // 2, **u8), hs=torch.empty(A, I // 32, **u8))
+        A16 = (A + 15) // 16 * 16
+        b.update(xq=torch.empty(A16, H // 2, **u8), xs=torch.empty(A16, H // 32, **u8),
+                 hq=torch.empty(A16, I // 2, **u8), hs=torch.empty(A16, I // 32, **u8))
     return b
 
 
@@ -473,30 +506,39 @@ def forward_stages(x, router_logits, shared_gate_logits, w13, w13_scale, w2, w2_
           gemm_tile_m(T, Kp, Ep, H, I, act_fmt))
     align_sort(b["ids"], Ep, tile_m=tm, out=b["align"], stream=stream)
     rec("align", 1)
-    act, act_s = x, None
+    act, act_s, gemm_act = x, None, act_fmt
+    blk = act_fmt == ACT_MXFP4 and tm != TILE_M      # tiled GEMMs: blocked sorted rows
     if act_fmt == ACT_MXFP4:
         rec("quant_x", 0)
-        mxfp4_quantize(x, b["xq"], b["xs"], stream=stream)
+        if blk:
+            mxfp4_quantize_blocked(x, b["align"]["inv"], Kp, T * Kp, b["xq"], b["xs"],
+                                   stream=stream)
+            gemm_act = ACT_MXFP4_BLOCKED
+        else:
+            mxfp4_quantize(x, b["xq"][:T], b["xs"][:T], stream=stream)
         rec("quant_x", 1)
         act, act_s = b["xq"], b["xs"]
     rec("gate_up", 0)
     if wfmt == W_MXFP8:
         mxfp8_expert_gate_up(x, b["align"], w13, w13_scale, T, H, I, Ep, Kp, h=b["h"], stream=stream)
     else:
-        expert_gate_up(act, act_s, act_fmt, b["align"], w13, w13_scale, T, H, I, Ep, Kp, h=b["h"],
+        expert_gate_up(act, act_s, gemm_act, b["align"], w13, w13_scale, T, H, I, Ep, Kp, h=b["h"],
                        stream=stream)
     rec("gate_up", 1)
     hin, hin_s = b["h"], None
     if act_fmt == ACT_MXFP4:
         rec("quant_h", 0)
-        mxfp4_quantize(b["h"], b["hq"], b["hs"], stream=stream)
+        if blk:
+            mxfp4_quantize_blocked(b["h"], packed=b["hq"], scales=b["hs"], stream=stream)
+        else:
+            mxfp4_quantize(b["h"], b["hq"][:T * Kp], b["hs"][:T * Kp], stream=stream)
         rec("quant_h", 1)
         hin, hin_s = b["hq"], b["hs"]
     rec("down", 0)
     if wfmt == W_MXFP8:
         mxfp8_expert_down(hin, b["align"], w2, w2_scale, T, H, I, Ep, Kp, y=b["y"], stream=stream)
     else:
-        expert_down(hin, hin_s, act_fmt, b["align"], w2, w2_scale, T, H, I, Ep, Kp, y=b["y"],
+        expert_down(hin, hin_s, gemm_act, b["align"], w2, w2_scale, T, H, I, Ep, Kp, y=b["y"],
                     stream=stream)
     rec("down", 1)
     rec("combine", 0)

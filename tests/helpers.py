@@ -31,6 +31,28 @@ def native_order(codes: np.ndarray, nq: int) -> np.ndarray:
     return np.ascontiguousarray(a.transpose(0, 2, 4, 3, 1, 5)).reshape(rows, rb)
 
 
+def blocked_order(codes: np.ndarray, scales: np.ndarray):
+    """Row-major MXFP4 activations (codes [R, cols/2], scales [R, cols/32],
+    R a multiple of 16) -> the blocked row order of include/moe_mxfp4.h
+    (moe_mxfp4_quantize_blocked), by reshapes: row 16 b + n, chunk c ->
+    codes block (b, c) byte 64 n + j, scales block (b, c) byte 4 n + g."""
+    R, cb = codes.shape
+    C = cb // 64
+    pc = codes.reshape(R // 16, 16, C, 64).transpose(0, 2, 1, 3)
+    ps = scales.reshape(R // 16, 16, C, 4).transpose(0, 2, 1, 3)
+    return (np.ascontiguousarray(pc).reshape(R, cb),
+            np.ascontiguousarray(ps).reshape(R, scales.shape[1]))
+
+
+def unblocked_rows(codes: np.ndarray, scales: np.ndarray):
+    """The inverse of blocked_order: blocked MXFP4 activations -> row-major rows."""
+    R, cb = codes.shape
+    C = cb // 64
+    rc = codes.reshape(R // 16, C, 16, 64).transpose(0, 2, 1, 3).reshape(R, cb)
+    rs = scales.reshape(R // 16, C, 16, 4).transpose(0, 2, 1, 3).reshape(R, scales.shape[1])
+    return rc, rs
+
+
 def bits(t: torch.Tensor) -> np.ndarray:
     """bf16 tensor -> uint16 numpy bit patterns."""
     return t.detach().contiguous().view(torch.int16).cpu().numpy().view(np.uint16)

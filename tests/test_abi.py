@@ -26,7 +26,7 @@ def declared_functions():
 def test_library_loads_and_exports_every_declared_symbol():
     lib = ops.lib()
     names = declared_functions()
-    assert len(names) == 22
+    assert len(names) == 23
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(ops.EXPORTS)
@@ -112,6 +112,21 @@ def test_quantize_argument_errors():
     assert f(FAKE, 0, 0, 64, FAKE, FAKE, None) == OK               # empty
 
 
+def test_quantize_blocked_argument_errors():
+    f = ops.lib().moe_mxfp4_quantize_blocked
+    assert f(FAKE, 0, 4, 96, None, 1, 4, FAKE, FAKE, None) == UNSUPPORTED    # cols % 128
+    assert f(FAKE, 2, 4, 128, None, 1, 4, FAKE, FAKE, None) == INVALID       # dtype
+    assert f(FAKE, 0, 4, 128, None, 1, 3, FAKE, FAKE, None) == INVALID       # out_rows < rows
+    assert f(FAKE, 0, 4, 128, FAKE, 0, 12, FAKE, FAKE, None) == INVALID      # map with Kp < 1
+    assert f(FAKE, 0, -1, 128, None, 1, 4, FAKE, FAKE, None) == INVALID
+    assert f(FAKE, 0, 4, 128, None, 1, 4, FAKE, MIS, None) == INVALID        # misaligned scales
+    assert f(None, 0, 4, 128, None, 1, 4, FAKE, FAKE, None) == INVALID
+    assert f(FAKE, 0, 4, 128, None, 1, 1 << 25, FAKE, FAKE, None) == UNSUPPORTED  # >= 2 GiB out
+    assert f(FAKE, 0, 1, 1 << 31, FAKE, 1, 0, FAKE, FAKE, None) == UNSUPPORTED    # cols > 2^30
+    assert f(FAKE, 0, 1 << 33, 128, FAKE, 1, 16, FAKE, FAKE, None) == UNSUPPORTED  # rows * Kp
+    assert f(FAKE, 0, 0, 128, None, 1, 0, FAKE, FAKE, None) == OK            # empty
+
+
 def test_weights_to_native_argument_errors():
     f = ops.lib().moe_weights_to_native
     B = ctypes.c_void_p(0x200000)                                  # FAKE + 1 MiB
@@ -149,6 +164,14 @@ def test_gemm_and_combine_argument_errors():
     assert call(gu, base, a7=128, a11=6144, a2=1, a1=FAKE, a10=0) == OK   # MXFP4: H <= 8192
     assert call(gu, base, a0=MIS) == INVALID
     assert call(gu, base, a10=0) == OK
+    # blocked MXFP4 rows: tiled kernels only, scales needed and 16-byte aligned
+    assert call(gu, base, a2=2, a1=FAKE) == UNSUPPORTED                     # 32-row tiles
+    assert call(gu, base, a2=2, a7=128, a11=512) == INVALID                 # no scales
+    assert call(gu, base, a2=2, a7=128, a11=512, a1=MIS) == INVALID         # misaligned scales
+    assert call(gu, base, a2=3, a1=FAKE) == INVALID                         # no such format
+    # blocked rows of T*K' sorted rows (rounded up to 16), not T tokens
+    assert call(gu, base, a2=2, a7=128, a1=FAKE, a10=120000, a11=512, a14=80) == UNSUPPORTED
+    assert call(gu, base, a2=1, a7=128, a1=FAKE, a10=120000, a11=512, a14=80, a15=None) == INVALID
     dn = ops.lib().moe_expert_down
     based = [FAKE, None, 0, FAKE, FAKE, FAKE, 32, FAKE, FAKE, 8, 256, 128, 16, 2, FAKE, None]
     assert call(dn, based, a14=None) == INVALID
@@ -156,6 +179,8 @@ def test_gemm_and_combine_argument_errors():
     assert call(dn, based, a6=64, a10=384) == UNSUPPORTED
     assert call(dn, based, a9=300000, a11=4096) == UNSUPPORTED   # h: T*K'*I*2 bytes >= 2 GiB
     assert call(dn, based, a9=0) == OK
+    assert call(dn, based, a2=2, a1=FAKE) == UNSUPPORTED                    # 32-row tiles
+    assert call(dn, based, a2=2, a6=128, a1=MIS) == INVALID                 # misaligned scales
     cb = ops.lib().moe_combine
     assert cb(None, FAKE, FAKE, 4, 256, 3, FAKE, None) == INVALID
     assert cb(FAKE, FAKE, FAKE, 4, 200, 3, FAKE, None) == UNSUPPORTED

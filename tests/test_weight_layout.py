@@ -2,10 +2,13 @@
 as the tests' numpy definition (tests/helpers.native_order) writes it,
 against entries worked out by hand from the header's rule: block
 ((s*C + c)*NQ + q) holds at byte 16*l (l = 16*g + n) the row-major bytes of
-row 16*s + n starting at NQ*(64*c + 16*g) + 16*q."""
+row 16*s + n starting at NQ*(64*c + 16*g) + 16*q.  Likewise the blocked row
+order of MXFP4 activations (tests/helpers.blocked_order against the rule of
+moe_mxfp4_quantize_blocked: row p's chunk c at ((p/16)*C + c)*1024 +
+(p%16)*64 for the codes, ((p/16)*C + c)*64 + (p%16)*4 for the scales)."""
 import numpy as np
 
-from tests.helpers import native_order
+from tests.helpers import blocked_order, native_order
 
 
 def _labelled(rows, row_bytes):
@@ -58,3 +61,22 @@ def test_is_a_permutation_of_pieces_and_keeps_experts_in_place():
     assert sorted(map(bytes, codes.reshape(-1, 16))) == sorted(map(bytes, nat.reshape(-1, 16)))
     for e in range(3):          # converting the stack = converting each expert on its own
         assert np.array_equal(nat[32 * e:32 * e + 32], native_order(codes[32 * e:32 * e + 32], 1))
+
+
+def test_blocked_activation_rows():
+    R, C = 32, 2                               # 32 rows of 256 codes: 128 code bytes, 8 scale bytes
+    codes, scales = _labelled(R, 64 * C), _labelled(R, 4 * C)
+    bc, bs = blocked_order(codes, scales)
+    fc, fs = bc.reshape(-1), bs.reshape(-1)
+    # row 0, chunk 0: code bytes 0..63 first, its scale bytes 0..3 first
+    assert list(fc[:64]) == list(range(64)) and list(fs[:4]) == [0, 1, 2, 3]
+    # row 1, chunk 0 right after row 0's: codes at 64, scales at 4
+    assert fc[64] == 1 * 128 and fs[4] == 1 * 8
+    # row 0, chunk 1 (code bytes 64..127, scale bytes 4..7): block (0, 1) at 1024 / 64
+    assert fc[1024] == 64 and fs[64] == 4
+    # row 17 = block 1, row 1; chunk 1: ((1*2 + 1)*1024 + 64), ((1*2 + 1)*64 + 4)
+    assert fc[3 * 1024 + 64] == 17 * 128 + 64 and fs[3 * 64 + 4] == 17 * 8 + 4
+    # row 31, chunk 1, last code byte / last scale byte: the arrays' last bytes
+    assert fc[-1] == 31 * 128 + 127 and fs[-1] == 31 * 8 + 7
+    # a permutation: every byte once
+    assert sorted(fc) == sorted(codes.reshape(-1)) and sorted(fs) == sorted(scales.reshape(-1))
