@@ -44,8 +44,9 @@ struct TileT {
 // G pairs later.  G = 1 is the plain tile-major order (an XCD runs all
 // slices of a tile back to back).  On the W4A4 batch (experts of ~128 rows,
 // about half of them with a second, nearly empty 128-row tile) the down GEMM
-// takes G = 4: fetched bytes 1.74 -> 1.36 GB per launch, 1-2% faster; its
-// gate/up keeps G = 1, which measured 2.5% faster than 4 at the same fetch.
+// takes G = 4: fetched bytes 1.74 -> 1.36 GB per launch, 1-2% faster.  The
+// gate/up GEMM takes G = 4 on blocked activations (1% faster than 1) and
+// G = 1 on gathered per-token rows (2.5% faster than 4 there).
 //
 // bf16 activations (bound by the MFMA work, which grows with a tile's rows):
 // runs of equal pair counts leave the XCD holding a hot expert's full tiles
@@ -553,7 +554,8 @@ __global__ __launch_bounds__(256, KV ? 2 : 1) void gate_up_tiled_kernel(
     uint16_t* __restrict__ h) {
   TileT ti;
   int s;
-  if (!tile_slice<BM, kFP4A>(blockIdx.x, tiles, offsets, *num_tiles, I / 128, &ti, &s)) return;
+  if (!tile_slice<BM, kFP4A, kBlk ? 4 : 1>(blockIdx.x, tiles, offsets, *num_tiles, I / 128, &ti, &s))
+    return;
   TiledGemm<BM, kFP4A, kW8, KV, kBlk> G;
   setup(G, ti, H, w13, w13s, 2 * I);
   const int nl = G.nl, g = G.g;
