@@ -42,6 +42,7 @@ constexpr int kTileM = 32;        // rows per workgroup (= the tile table's tile
 
 struct TileInfo {
   int expert, row0, rows;
+  bool single;    // the expert's only tile: nothing re-reads its weights
 };
 
 // Workgroups take the tile table from its end: block b works on tile
@@ -56,6 +57,7 @@ __device__ __forceinline__ bool load_tile(const int32_t* tiles, const int32_t* n
   ti->expert = tiles[2 * tile];
   ti->row0 = tiles[2 * tile + 1];
   ti->rows = min(kTileM, offsets[ti->expert + 1] - ti->row0);
+  ti->single = offsets[ti->expert + 1] - offsets[ti->expert] <= kTileM;
   return true;
 }
 
@@ -85,6 +87,7 @@ struct Operands {
   const uint8_t* lds;      // the workgroup's weight scales
   const uint8_t* ldx;      // bf16 activation rows staged in LDS (small tiles), lane row + 64 g
   bool xvalid;             // the lane's activation row exists (padded rows read zeros)
+  bool stream;             // weights read once (the expert's only tile): non-temporal loads
 };
 
 template <int PH, bool kFP4A, bool XL, bool kW8>
@@ -102,7 +105,8 @@ struct Phase {
       for (int si = 0; si < 2; ++si)
 #pragma unroll
         for (int hq = 0; hq < NQ; ++hq)
-          q[si][NQ * j + hq] = bload16(o.w, o.wo[si], wnat_chunk(c0 + j, NQ, hq));
+          q[si][NQ * j + hq] = o.stream ? bload16_nt(o.w, o.wo[si], wnat_chunk(c0 + j, NQ, hq))
+                                        : bload16(o.w, o.wo[si], wnat_chunk(c0 + j, NQ, hq));
 #pragma unroll
     for (int j = 0; j < PH; ++j) {
       if constexpr (kFP4A) {
@@ -218,6 +222,7 @@ __attribute__((amdgpu_waves_per_eu(MOE_GEMM_WAVES_PER_EU))) void gate_up_kernel(
   Operands o;
   o.lds = lds_scales;
   o.w = make_rsrc(w13 + ti.expert * wbytes, (uint32_t)wbytes);
+  o.stream = ti.single;
   constexpr int NQ = Phase<PH, kFP4A, false, kW8>::NQ;
   o.wo[0] = wnat_lane(i >> 4, H, NQ, lane);
   o.wo[1] = wnat_lane((I + i) >> 4, H, NQ, lane);
@@ -292,6 +297,7 @@ __attribute__((amdgpu_waves_per_eu(MOE_GEMM_WAVES_PER_EU))) void down_kernel(
   Operands o;
   o.lds = lds_scales;
   o.w = make_rsrc(w2 + ti.expert * wbytes, (uint32_t)wbytes);
+  o.stream = ti.single;
   constexpr int NQ = Phase<PH, kFP4A, false, kW8>::NQ;
   o.wo[0] = wnat_lane(j0 >> 4, I, NQ, lane);
   o.wo[1] = wnat_lane((j0 >> 4) + 1, I, NQ, lane);

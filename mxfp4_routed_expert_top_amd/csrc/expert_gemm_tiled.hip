@@ -31,6 +31,7 @@ constexpr uint32_t kOOR = 0x80000000u;   // out-of-range buffer offset: loads re
 
 struct TileT {
   int expert, row0, rows;
+  bool single;    // the expert's only tile: nothing re-reads its weights
 };
 
 // Block -> (tile, weight slice).  The hardware hands workgroup b to XCD
@@ -82,6 +83,7 @@ __device__ __forceinline__ bool tile_slice(int b, const int32_t* tiles, const in
     ti->expert = e;
     ti->row0 = o0 + k * BM;
     ti->rows = min(BM, o1 - ti->row0);
+    ti->single = o1 - o0 <= BM;
     return true;
   } else {
     const int q = j / (kDeal * nslices), p = j - q * kDeal * nslices;
@@ -92,6 +94,7 @@ __device__ __forceinline__ bool tile_slice(int b, const int32_t* tiles, const in
   ti->expert = tiles[2 * tile];
   ti->row0 = tiles[2 * tile + 1];
   ti->rows = min(BM, offsets[ti->expert + 1] - ti->row0);
+  ti->single = offsets[ti->expert + 1] - offsets[ti->expert] <= BM;
   return true;
 }
 
@@ -216,6 +219,7 @@ struct TiledGemm {
   uint32_t sro;                 // lane's scale byte offset in LDS for strip 0 (row 64 wave + nl, + g)
   uint32_t aso;                 // (kAS) lane's activation scale row offset, or kOOR
   int wave, lane, nl, g, nch, Q, swz;
+  bool stream;                  // weights read once: non-temporal loads
 
   // Scale rows (Q dwords each, whole K) into LDS: wave w fills rows
   // [RW w, RW w + RW), its region padded to whole 64-lane loads (size-4
@@ -264,7 +268,9 @@ struct TiledGemm {
 #pragma unroll
     for (int t = 0; t < 4; ++t)
 #pragma unroll
-      for (int hq = 0; hq < NQ; ++hq) q[NQ * t + hq] = bload16(w, wo[t] | oor, wnat_chunk(cc, NQ, hq));
+      for (int hq = 0; hq < NQ; ++hq)
+        q[NQ * t + hq] = stream ? bload16_nt(w, wo[t] | oor, wnat_chunk(cc, NQ, hq))
+                                : bload16(w, wo[t] | oor, wnat_chunk(cc, NQ, hq));
   }
 
   // MFMAs of one chunk on the first NMT 16-row sub-tiles (the live ones).
@@ -435,6 +441,10 @@ __device__ __forceinline__ void setup(TiledGemm<BM, kFP4A, kW8, KV, kBlk>& G, co
   G.sro = 4 * (64 * G.wave + G.nl) * G.Q + G.g;
   const size_t wbytes = (size_t)wrows * (kW8 ? K : K / 2), sbytes = (size_t)wrows * (K / 32);
   G.w = make_rsrc(wq + ti.expert * wbytes, (uint32_t)wbytes);
+  // The expert's only tile with bf16 activations streams its weights
+  // non-temporally; with MXFP4 activations (or several tiles) an expert's
+  // weight lines stay cacheable for the tiles that re-read them from L2.
+  G.stream = !kFP4A && ti.single;
   G.ws = make_rsrc(wsc + ti.expert * sbytes, (uint32_t)sbytes);
 }
 
