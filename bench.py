@@ -335,14 +335,16 @@ def main():
                                             topk_weights=rw_, workspace=rws)
         for _ in range(3):
             rcall()
-        re = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-              for _ in range(args.steps)]
-        for a, b in re:
-            a.record()
-            rcall()
-            b.record()
+        # one event pair around the back-to-back calls: per-call pairs would time
+        # the host whenever enqueueing a call takes longer than running it
+        ra, rb = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
-        rms = float(np.mean([a.elapsed_time(b) for a, b in re]))
+        ra.record()
+        for _ in range(args.steps):
+            rcall()
+        rb.record()
+        torch.cuda.synchronize()
+        rms = ra.elapsed_time(rb) / args.steps
         rbytes = cfg.Ep * cfg.H * 2 + cfg.T * cfg.H * 2
         router = {"call_ms": round(rms, 4), "algorithmic_bytes": rbytes,
                   "flops": 2 * cfg.T * cfg.Ep * cfg.H, "gbs": round(rbytes / (rms / 1e3) / 1e9, 1)}
