@@ -7,14 +7,19 @@ inputs already resident in HBM.  Prints one JSON line.
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload decode]
 
 The default workload is the decode batch (T=64, H=4096, I=1024, E=512,
-top-10 + shared expert, W4A16).  The cpu_baseline leg times the CPU oracle
-on a few tokens of the same batch.
+top-10 + shared expert, W4A16); its throughput is `value`.  The same run
+also times the prefill chunk (T=1536), the skewed prefill chunk (T=8192)
+and the W4A4 batch (T=4096, H=6144, I=1536, E=256, top-8 + shared) and
+reports each under `workloads` with its rooflines.  The cpu_baseline leg
+times the C++ CPU oracle on the whole decode batch on the host's cores.
 """
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
+import platform
 import sys
 import time
 
@@ -35,9 +40,12 @@ def parse():
     p.add_argument("--steps", type=int, default=50)
     p.add_argument("--warmup", type=int, default=10)
     p.add_argument("--workload", default="decode", choices=list(synth.CONFIGS))
-    p.add_argument("--cpu-tokens", type=int, default=40,
-                   help="tokens of the batch the CPU oracle is timed on")
     p.add_argument("--no-cpu", action="store_true", help="skip the cpu_baseline leg")
+    p.add_argument("--no-extras", action="store_true",
+                   help="time only the decode workload (by default the prefill, skewed prefill "
+                        "and W4A4 workloads are timed too, under 'workloads')")
+    p.add_argument("--no-sha", dest="sha", action="store_false",
+                   help="skip the SHA-256 of the input buffers")
     p.add_argument("--router", action="store_true",
                    help="route from x through the router GEMM (bf16 router rows [E + shared, H]) "
                         "instead of taking precomputed logits")
@@ -57,13 +65,18 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def make_inputs(cfg):
+def make_inputs(cfg, weights=None):
+    """x, logits, gate of the workload on the GPU, and its expert weights
+    (drawn and packed by the library's quantiser unless `weights` holds the
+    same draw's packing already)."""
     from mxfp4_routed_expert_top_amd import ops
     dev = "cuda"
     x = synth.activations(cfg).to(dev)
     logits = synth.router_logits(cfg).to(dev)
     gate = synth.gate_logits(cfg)
     gate = None if gate is None else gate.to(dev)
+    if weights is not None:
+        return (x, logits, gate, *weights)
     u8 = dict(dtype=torch.uint8, device=dev)
     per = 1 if cfg.wfmt == synth.W_MXFP8 else 2      # elements per code byte
     w13 = torch.empty(cfg.Ep, 2 * cfg.I, cfg.H // per, **u8)
@@ -118,32 +131,46 @@ def traffic_path(cfg):
                         f"{cfg.name}_T{cfg.T}_traffic.json")
 
 
-def _pack_expert(args):
-    """Draw one expert's float weights on the CPU and pack them with the
-    oracle's quantiser (input preparation for the cpu_baseline leg)."""
-    from oracle import mxfp4, mxfp8
-    cfg, e = args
-    torch.set_num_threads(1)
-    q = mxfp8.quantize if cfg.wfmt == synth.W_MXFP8 else mxfp4.quantize
-    a = q(synth.expert_w13(cfg, e).double().numpy())
-    b = q(synth.expert_w2(cfg, e).double().numpy())
-    return e, (a[0], a[1], b[0], b[1])
+def sha256_of(*tensors: torch.Tensor) -> str:
+    """SHA-256 of the tensors' bytes, one after another (copied to the host
+    in slices)."""
+    h = hashlib.sha256()
+    step = 64 << 20
+    for t in tensors:
+        flat = t.detach().contiguous().view(-1).view(torch.uint8)
+        for lo in range(0, flat.numel(), step):
+            h.update(flat[lo:lo + step].cpu().numpy().tobytes())
+    return h.hexdigest()
 
 
-def cpu_baseline(cfg, n_tokens, router=False):
-    """Time the oracle, as it stands, on the first n_tokens tokens of the
-    batch (route + align over all tokens, expert MLPs + combine for the
-    sample), single-threaded.  Its weights are the same distribution drawn on
-    the CPU and packed beforehand by the oracle's own quantiser in a process
-    pool (not timed)."""
-    import multiprocessing as mp
-    from threadpoolctl import threadpool_limits
-    from oracle import moe
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor() or "unknown"
+
+
+def cpu_baseline(cfg, router=False):
+    """Time the C++ oracle, as it stands, on the whole batch: routing and
+    grouping of every token, every touched expert's MLP in fp64, the
+    combine (oracle_forward's own wall time).  Threads: the CPUs of the
+    affinity mask (at most 16, one GPU's share of the host).  Its weights are
+    the same float draws (drawn on the GPU by the seeded generator, copied to
+    the host) packed by the oracle's own quantiser beforehand (not timed)."""
+    from oracle import _lib as olib
+    from oracle import moe, mxfp4, mxfp8
+    threads = olib.default_threads()
     x_bits = synth.activations(cfg).view(torch.int16).numpy().view(np.uint16)
-    tokens = np.arange(min(n_tokens, cfg.T))
+    t_router = 0.0
     if router:
         wr_bits = synth.router_weight(cfg).view(torch.int16).numpy().view(np.uint16)
-        lg = moe.router_logits(x_bits, wr_bits)          # all tokens (routing needs them), untimed
+        t0 = time.perf_counter()
+        lg = moe.router_logits(x_bits, wr_bits, threads=threads)
+        t_router = time.perf_counter() - t0
         logits = lg[:, :cfg.E].astype(np.float32)
         gate = lg[:, cfg.E].astype(np.float32) if cfg.shared else None
     else:
@@ -151,25 +178,25 @@ def cpu_baseline(cfg, n_tokens, router=False):
         gate = synth.gate_logits(cfg)
         gate = None if gate is None else gate.numpy()
     ids, _ = moe.route(logits, gate, cfg.K, cfg.shared)
-    need = sorted(set(ids[tokens].reshape(-1).tolist()))
-    procs = max(1, min(16, len(os.sched_getaffinity(0))))
-    log(f"cpu_baseline: packing {len(need)} experts with the oracle's quantiser ({procs} procs)")
-    with mp.get_context("spawn").Pool(procs) as pool:
-        packed = dict(pool.map(_pack_expert, [(cfg, e) for e in need], chunksize=4))
-    t_router = 0.0
-    with threadpool_limits(1):
-        if router:                 # the router GEMM over the sampled tokens, single-threaded too
-            t0 = time.perf_counter()
-            moe.router_logits(x_bits[tokens], wr_bits)
-            t_router = time.perf_counter() - t0
-        t0 = time.perf_counter()
-        moe.forward(x_bits, logits, gate, lambda e: packed[e], cfg.I, cfg.E, cfg.K, cfg.shared,
-                    cfg.act_fmt, tokens=tokens, wfmt=cfg.wfmt)
-        dt = time.perf_counter() - t0 + t_router
-    return {"value": round(len(tokens) / dt, 3), "unit": "tokens/s", "cores": 1, "kind": "oracle",
-            "seconds": round(dt, 2),
-            "sample": f"{len(tokens)} of the batch's {cfg.T} tokens ({len(need)} experts decoded); "
-                      "numpy fp64 oracle on one host core"}
+    need = sorted(set(ids.reshape(-1).tolist()))
+    q = mxfp8.quantize if cfg.wfmt == synth.W_MXFP8 else mxfp4.quantize
+    log(f"cpu_baseline: packing {len(need)} experts with the oracle's quantiser ({threads} threads)")
+    packed = {}
+    for e in need:
+        a = q(synth.expert_w13(cfg, e, "cuda").cpu().numpy(), threads=threads)
+        b = q(synth.expert_w2(cfg, e, "cuda").cpu().numpy(), threads=threads)
+        packed[e] = (a[0], a[1], b[0], b[1])
+    log("cpu_baseline: timing oracle_forward on the whole batch")
+    res = moe.forward(x_bits, logits, gate, lambda e: packed[e], cfg.I, cfg.E, cfg.K, cfg.shared,
+                      cfg.act_fmt, wfmt=cfg.wfmt, threads=threads)
+    dt = res["seconds"] + t_router
+    flops = cfg.A * 6 * cfg.H * cfg.I + (2 * cfg.T * cfg.Ep * cfg.H if router else 0)
+    return {"value": round(cfg.T / dt, 3), "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "seconds": round(dt, 3), "gflops_fp64": round(flops / dt / 1e9, 2),
+            "cpu": cpu_model(), "affinity_cpus": len(os.sched_getaffinity(0)),
+            "sample": f"the whole batch: {cfg.T} tokens, {cfg.A} assignments, {len(need)} experts "
+                      "decoded" + (", router GEMM included" if router else "")
+                      + "; C++ fp64 oracle (oracle_forward), one std::thread pool"}
 
 
 def bench_layers(cfg, args):
@@ -235,35 +262,28 @@ def bench_layers(cfg, args):
     print(json.dumps(res), flush=True)
 
 
-def main():
-    args = parse()
-    if args.gpus != 1:
-        print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
-              "(this layer is measured on a single MI355X)", file=sys.stderr)
-        sys.exit(2)
-    from mxfp4_routed_expert_top_amd import ops
-    cfg = synth.CONFIGS[args.workload]
-    if args.layers:
-        if cfg.wfmt == synth.W_MXFP8:
-            print("--layers is for MXFP4 weights", file=sys.stderr)
-            sys.exit(2)
-        return bench_layers(cfg, args)
+EXTRAS = ["prefill", "prefill_skewed", "w4a4"]      # timed beside the decode headline
+
+
+def pct(a, q):
+    return float(np.percentile(np.asarray(a), q))
+
+
+def measure(cfg, args, weights=None, router=False):
+    """One workload: whole-layer throughput over args.steps calls (wall
+    clock, synchronised on both sides), the per-call HIP-event distribution,
+    the GEMM kernels' durations from HIP events on their launch stream, and
+    the rooflines.  Returns (result dict, weights) so a later workload with
+    the same weight draw can reuse them."""
+    from mxfp4_routed_expert_top_amd import ops, profiling
     w8 = cfg.wfmt == synth.W_MXFP8
-    if args.router and w8:
-        print("--router is for MXFP4 weights", file=sys.stderr)
-        sys.exit(2)
     log(f"workload {cfg.name}: T={cfg.T} H={cfg.H} I={cfg.I} E={cfg.E} K={cfg.K} "
         f"shared={cfg.shared} act={'mxfp4' if cfg.act_fmt else 'bf16'} "
         f"weights={'mxfp8' if w8 else 'mxfp4'}")
-    if args.pmc_calibrate:
-        a = torch.zeros(1 << 28, dtype=torch.int32, device="cuda")      # 1 GiB
-        torch.bitwise_not(a, out=torch.empty_like(a))
-        torch.cuda.synchronize()
-        del a
-        torch.cuda.empty_cache()
-    x, logits, gate, w13, w13s, w2, w2s = make_inputs(cfg)
-    wr = synth.router_weight(cfg).to("cuda") if args.router else None
-    if args.router:
+    x, logits, gate, *wts = make_inputs(cfg, weights)
+    w13, w13s, w2, w2s = wts
+    wr = synth.router_weight(cfg).to("cuda") if router else None
+    if router:
         # the stage-by-stage pass routes on the logits the router GEMM gives
         lg = torch.empty(cfg.T, cfg.Ep, dtype=torch.float32, device="cuda")
         ops.route_topk_gemm(x, wr, cfg.K, cfg.shared, logits_out=lg)
@@ -275,12 +295,11 @@ def main():
     assert not w8 or ws.numel() >= ops.mxfp8_workspace_size(cfg.T, cfg.H, cfg.I, cfg.E, cfg.K,
                                                              cfg.shared)
     out = torch.empty(cfg.T, cfg.H, dtype=torch.bfloat16, device="cuda")
-    stream = torch.cuda.current_stream()
 
     def step():
         # the whole layer, one C call: [router GEMM,] route, align, [quant x], gate/up+SwiGLU,
         # [quant h], down, combine
-        if args.router:
+        if router:
             ops.mxfp4_forward_router(x, wr, w13, w13s, w2, w2s, cfg.I, cfg.E, cfg.K, cfg.shared,
                                      cfg.act_fmt, out=out, workspace=ws)
         elif w8:
@@ -297,7 +316,6 @@ def main():
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    log("warmup done")
 
     # timed region 1: whole-layer throughput (no events inside the steps)
     torch.cuda.synchronize()
@@ -305,12 +323,23 @@ def main():
     for _ in range(args.steps):
         step()
     torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    ms = (t1 - t0) * 1e3 / args.steps
+    ms = (time.perf_counter() - t0) * 1e3 / args.steps
 
-    # timed region 2: the same pass stage by stage, HIP events on the launch
+    # timed region 2: each call between its own pair of HIP events on the
+    # launch stream, for the distribution (median, p10, p90)
+    stream = torch.cuda.current_stream()
+    pairs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+             for _ in range(args.steps)]
+    for a, b in pairs:
+        a.record(stream)
+        step()
+        b.record(stream)
+    torch.cuda.synchronize()
+    call_ms = [a.elapsed_time(b) for a, b in pairs]
+
+    # timed region 3: the same pass stage by stage, HIP events on the launch
     # stream around the GEMM kernels (the dominant ones) for their durations
-    names = ["gate_up", "down"]
+    names = ["gate_up", "down", "combine"]
     ev = [{n: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
            for n in names} for _ in range(args.steps)]
     for _ in range(2):
@@ -320,13 +349,14 @@ def main():
         step_stages(ev[i])
     torch.cuda.synchronize()
     stage_ms = {n: float(np.mean([e[n][0].elapsed_time(e[n][1]) for e in ev])) for n in names}
-    log("kernel ms:", json.dumps({k: round(v, 4) for k, v in stage_ms.items()}),
-        "step ms:", round(ms, 4))
+    log(f"  step {ms:.4f} ms (events: median {pct(call_ms, 50):.4f}); kernel ms:",
+        json.dumps({k: round(v, 4) for k, v in stage_ms.items()}))
     if not torch.equal(out, bufs["out"]):
         raise RuntimeError("one-call forward and per-stage pass disagree")
-    router = None
-    if args.router:
-        # timed region 3: the router call alone (router GEMM + routing), HIP events
+
+    router_res = None
+    if router:
+        # timed region 4: the router call alone (router GEMM + routing), HIP events
         rws = torch.empty(ops.route_gemm_workspace_size(cfg.T, cfg.H, cfg.E, cfg.shared),
                           dtype=torch.uint8, device="cuda")
         rids = torch.empty(cfg.T, cfg.Kp, dtype=torch.int32, device="cuda")
@@ -346,16 +376,16 @@ def main():
         torch.cuda.synchronize()
         rms = ra.elapsed_time(rb) / args.steps
         rbytes = cfg.Ep * cfg.H * 2 + cfg.T * cfg.H * 2
-        router = {"call_ms": round(rms, 4), "algorithmic_bytes": rbytes,
-                  "flops": 2 * cfg.T * cfg.Ep * cfg.H, "gbs": round(rbytes / (rms / 1e3) / 1e9, 1)}
-        log("router call ms:", round(rms, 4))
+        router_res = {"call_ms": round(rms, 4), "algorithmic_bytes": rbytes,
+                      "flops": 2 * cfg.T * cfg.Ep * cfg.H,
+                      "gbs": round(rbytes / (rms / 1e3) / 1e9, 1)}
+        log("  router call ms:", round(rms, 4))
 
     counts = bufs["align"]["counts"].cpu().numpy()
     alg = algorithmic(cfg, counts)
-    if args.router:          # the router rows join the layer's bytes and FLOPs
+    if router:          # the router rows join the layer's bytes and FLOPs
         alg["layer_bytes"] += cfg.Ep * cfg.H * 2 - cfg.T * cfg.E * 4 - cfg.T * 4 * cfg.shared
         alg["flops"] += 2 * cfg.T * cfg.Ep * cfg.H
-    from mxfp4_routed_expert_top_amd import profiling
     tile_m = (ops.mxfp8_gemm_tile_m(cfg.T, cfg.Kp, cfg.Ep, cfg.H, cfg.I) if w8 else
               ops.gemm_tile_m(cfg.T, cfg.Kp, cfg.Ep, cfg.H, cfg.I, cfg.act_fmt))
     kname = gate_up_kernel_name(cfg, tile_m)
@@ -377,33 +407,97 @@ def main():
                      "algorithmic_flops": alg["gate_up_flops"],
                      "kernel_ms": round(stage_ms["gate_up"], 4)})
     layer_s = ms / 1e3
-    t_bind = max(alg["layer_bytes"] / (HBM_PEAK_GBS * 1e9), alg["flops"] / (mfma_peak * 1e12))
-    layer = {"bytes": alg["layer_bytes"], "flops": alg["flops"], "touched_experts": alg["touched"],
-             "hbm_gbs": round(alg["layer_bytes"] / layer_s / 1e9, 1),
-             "hbm_frac": round(alg["layer_bytes"] / layer_s / 1e9 / HBM_PEAK_GBS, 4),
-             "mxfp4_mfma_frac": round(alg["flops"] / layer_s / 1e12 / MXFP4_PEAK_TFLOPS, 5),
-             "bf16_mfma_frac": round(alg["flops"] / layer_s / 1e12 / BF16_PEAK_TFLOPS, 5),
-             "binding_roofline_frac": round(t_bind / layer_s, 4),
-             "kernel_ms": {k: round(v, 4) for k, v in stage_ms.items()},
-             "down_gbs": round(alg["w2_bytes"] / (stage_ms["down"] / 1e3) / 1e9, 1)}
+    t_l_hbm = alg["layer_bytes"] / (HBM_PEAK_GBS * 1e9)
+    t_l_mfma = alg["flops"] / (mfma_peak * 1e12)
+    t_bind = max(t_l_hbm, t_l_mfma)
+    t_mxfp4 = alg["flops"] / (MXFP4_PEAK_TFLOPS * 1e12)
+    routed = counts[:cfg.E]
+    res = {"workload": cfg.name, "T": cfg.T, "H": cfg.H, "I": cfg.I, "E": cfg.E, "K": cfg.K,
+           "shared": cfg.shared,
+           "format": ("W8A16 MXFP8" if w8 else ("W4A16" if cfg.act_fmt == 0 else "W4A4") + " MXFP4"),
+           "ms_per_step": round(ms, 4), "tokens_per_s": round(cfg.T / layer_s, 1),
+           "call_ms": {"median": round(pct(call_ms, 50), 4), "p10": round(pct(call_ms, 10), 4),
+                       "p90": round(pct(call_ms, 90), 4), "calls": len(call_ms)},
+           "kernel_ms": {k: round(v, 4) for k, v in stage_ms.items()},
+           "bytes": alg["layer_bytes"], "flops": alg["flops"],
+           "hbm_gbs": round(alg["layer_bytes"] / layer_s / 1e9, 1),
+           "hbm_frac": round(alg["layer_bytes"] / layer_s / 1e9 / HBM_PEAK_GBS, 4),
+           "bf16_mfma_frac": round(alg["flops"] / layer_s / 1e12 / BF16_PEAK_TFLOPS, 5),
+           "mxfp4_mfma_frac": round(alg["flops"] / layer_s / 1e12 / MXFP4_PEAK_TFLOPS, 5),
+           "mxfp4_mfma_frac_ceiling": round(t_mxfp4 / t_bind, 4),
+           "binding_roofline": "hbm" if t_l_hbm >= t_l_mfma else
+                               ("bf16_mfma" if cfg.act_fmt == 0 else "mxfp4_mfma"),
+           "binding_roofline_frac": round(t_bind / layer_s, 4),
+           "down_gbs": round(alg["w2_bytes"] / (stage_ms["down"] / 1e3) / 1e9, 1),
+           "experts": {"touched": alg["touched"], "routed_zero": int((routed == 0).sum()),
+                       "routed_rows_min": int(routed.min()), "routed_rows_max": int(routed.max()),
+                       "routed_rows_mean": round(float(routed.mean()), 2),
+                       "shared_rows": int(counts[cfg.E]) if cfg.shared else 0},
+           "roofline": roofline}
+    if router_res is not None:
+        res["router"] = router_res
+    if args.sha:
+        res["sha256"] = {"x": sha256_of(x), "logits": sha256_of(logits),
+                         "gate": None if gate is None else sha256_of(gate)}
+        if weights is None:         # the weight set is hashed once, where it is made
+            res["sha256"]["weights"] = sha256_of(*wts)
+    return res, wts
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
+              "(this layer is measured on a single MI355X)", file=sys.stderr)
+        sys.exit(2)
+    cfg = synth.CONFIGS[args.workload]
+    if args.layers:
+        if cfg.wfmt == synth.W_MXFP8:
+            print("--layers is for MXFP4 weights", file=sys.stderr)
+            sys.exit(2)
+        return bench_layers(cfg, args)
+    w8 = cfg.wfmt == synth.W_MXFP8
+    if args.router and w8:
+        print("--router is for MXFP4 weights", file=sys.stderr)
+        sys.exit(2)
+    if args.pmc_calibrate:
+        a = torch.zeros(1 << 28, dtype=torch.int32, device="cuda")      # 1 GiB
+        torch.bitwise_not(a, out=torch.empty_like(a))
+        torch.cuda.synchronize()
+        del a
+        torch.cuda.empty_cache()
+    head, head_w = measure(cfg, args, router=args.router)
+    extras = {}
+    want_extras = (not args.no_extras and args.workload == "decode" and not args.router)
+    if want_extras:
+        kept = {(cfg.seed_w, cfg.H, cfg.I, cfg.E, cfg.shared, cfg.wfmt): head_w}
+        for name in EXTRAS:
+            c = synth.CONFIGS[name]
+            key = (c.seed_w, c.H, c.I, c.E, c.shared, c.wfmt)
+            r, w = measure(c, args, weights=kept.get(key))
+            kept.setdefault(key, w)
+            extras[name] = r
     cpu = None
     if not args.no_cpu:
-        cpu = cpu_baseline(cfg, args.cpu_tokens, router=args.router)
-    res = {"metric": METRIC, "value": round(cfg.T / layer_s, 1), "unit": "tokens/s",
-           "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
+        cpu = cpu_baseline(cfg, router=args.router)
+        log("cpu_baseline:", json.dumps(cpu))
+    roofline = head.pop("roofline")
+    res = {"metric": METRIC, "value": head["tokens_per_s"], "unit": "tokens/s",
+           "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+           "ms_per_step": head["ms_per_step"],
            "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
            "dtype": "bf16" if cfg.act_fmt == 0 else "mxfp4",
            "data": "synthetic",
            "config": {"workload": f"{cfg.name}: T={cfg.T} H={cfg.H} I={cfg.I} E={cfg.E} "
-                                  f"K={cfg.K}+{cfg.shared} shared, "
-                                  + ("W8A16 MXFP8 weights" if w8 else
-                                     f"{'W4A16' if cfg.act_fmt == 0 else 'W4A4'} MXFP4 weights")
+                                  f"K={cfg.K}+{cfg.shared} shared, {head['format']} weights"
                                   + (", routed from x by the router GEMM" if args.router else ""),
                       "T": cfg.T, "H": cfg.H, "I": cfg.I, "E": cfg.E, "K": cfg.K,
                       "shared": cfg.shared, "parallelism": "none (1 GPU)"},
-           "roofline": roofline, "layer": layer, "cpu_baseline": cpu}
-    if router is not None:
-        res["router"] = router
+           "roofline": roofline, "layer": head, "cpu_baseline": cpu}
+    if extras:
+        res["workloads"] = extras
+    if "router" in head:
+        res["router"] = head.pop("router")
     print(json.dumps(res), flush=True)
 
 

@@ -1,8 +1,10 @@
-"""The MXFP4 routed-expert MoE layer, computed from its plain definition (fp64).
+"""The MXFP4 routed-expert MoE layer computed from its plain definition
+(fp64): Python access to the C++ oracle (oracle/moe_oracle.cpp).
 
 TEST INFRASTRUCTURE.  Only tests/, __graft_entry__.smoke() and bench.py's
 cpu_baseline leg may import this package.  It shares no code with the HIP
-path and never imports it.
+path and never imports it.  This module only marshals arrays and picks the
+experts a call needs; the arithmetic is the C++ oracle's.
 
 What the layer computes, per token t with router logits l_t, activations
 x_t and (when the shared expert is folded in) gate logit g_t:
@@ -20,36 +22,40 @@ x_t and (when the shared expert is folded in) gate logit g_t:
   MLP_e(a) = W2_e . bf16( silu(W13_e[gate] . a) * (W13_e[up] . a) )
   out_t = bf16( sum_k w_t,k * bf16(MLP_{e_k}(x_t)) ), summed in slot order.
 
-MXFP4 weights are decoded exactly; each dot product is an fp64 matmul over
-exact products; bf16 rounding happens where the GPU path stores bf16: h,
-each slot's expert output y (staged between the down GEMM and the combine;
-the pages fix no precision for it, and bf16 is the activations' type on the
-path) and out.  For W4A4 the activations and h are MXFP4-quantised then decoded
-before their GEMM (OpenRelay "Gemma 4 31B on MI355X" post, sections
+MXFP4 weights are decoded exactly; each dot product is an fp64 sum of exact
+products; bf16 rounding happens where the GPU path stores bf16: h, each
+slot's expert output y (staged between the down GEMM and the combine; the
+pages fix no precision for it, and bf16 is the activations' type on the
+path) and out.  For W4A4 the activations and h are MXFP4-quantised then
+decoded before their GEMM (OpenRelay "Gemma 4 31B on MI355X" post, sections
 "Optimisation 3" and "Optimisation 4": activation + MXFP4 quantisation
 fused into one kernel).
 
-Grouping by expert (align) is defined here as a stable sort of the flat
-assignment ids t*K'+k by expert id; the tile list is the 32-row tiles of
-each expert's group (VibeSys post, section "Prefill, cache and
-speculation": 32-row tiles in the MoE kernel).
+Grouping by expert (align) is a stable sort of the flat assignment ids
+t*K'+k by expert id; the tile list is the tile_m-row tiles of each
+expert's group (VibeSys post, section "Prefill, cache and speculation":
+32-row tiles in the MoE kernel).
 
 The router GEMM that produces the logits (the step before routing; the
 InferenceX post's fused_topk consumes a separately computed gating output)
 is logits = x . Wr^T over bf16 x and bf16 router rows, and with a shared
 expert the gate logit g = x . Wr[E] of one more row: router_logits computes
-it exactly (fp64 sums of exact products).
+it in fp64 over exact products.
 
 Expert weights may also be MXFP8 (oracle/mxfp8.py), with bf16 activations;
 everything else is unchanged.
 
-Pins: tests/test_oracle_moe.py, tests/golden/route_align.json.
+Pins: tests/test_oracle_moe.py, tests/golden/route_align.json,
+tests/golden/w4a4_worked.json.
 """
 from __future__ import annotations
+
+import ctypes
 
 import numpy as np
 
 from . import mxfp4, mxfp8
+from ._lib import check, default_threads, lib, ptr
 
 ACT_BF16 = 0
 ACT_MXFP4 = 1
@@ -75,34 +81,30 @@ def route(logits: np.ndarray, gate, K: int, shared: int, renormalize: bool = Tru
       renormalised: exp(l_k - l_max) / sum_{k' < K} exp(l_k' - l_max)
       otherwise:    exp(l_k - l_max) / sum_{all e} exp(l_e - l_max)
     Slot K (shared): id E, weight 1 / (1 + exp(-g))."""
-    l = np.asarray(logits, dtype=np.float32).astype(np.float64)
+    l = np.ascontiguousarray(logits, dtype=np.float32)
     T, E = l.shape
     Kp = K + shared
-    idx = np.broadcast_to(np.arange(E), (T, E))
-    order = np.lexsort((idx, -l), axis=-1)[:, :K]       # primary key -l, then index
+    g = np.ascontiguousarray(gate, dtype=np.float32) if shared else None
     ids = np.empty((T, Kp), dtype=np.int32)
     w = np.empty((T, Kp), dtype=np.float32)
-    ids[:, :K] = order
-    top = np.take_along_axis(l, order, axis=1)
-    lmax = l.max(axis=1, keepdims=True)
-    num = np.exp(top - lmax)
-    den = num.sum(axis=1, keepdims=True) if renormalize else np.exp(l - lmax).sum(axis=1, keepdims=True)
-    w[:, :K] = (num / den).astype(np.float32)
-    if shared:
-        g = np.asarray(gate, dtype=np.float32).astype(np.float64)
-        ids[:, K] = E
-        w[:, K] = (1.0 / (1.0 + np.exp(-g))).astype(np.float32)
+    check(lib().oracle_route(ptr(l), ptr(g), T, E, K, shared, int(bool(renormalize)), ptr(ids),
+                             ptr(w)), "route")
     return ids, w
 
 
-def router_logits(x_bits: np.ndarray, w_bits: np.ndarray) -> np.ndarray:
+def router_logits(x_bits: np.ndarray, w_bits: np.ndarray, threads: int | None = None) -> np.ndarray:
     """Router GEMM: x bf16 bits [T, H], router rows bf16 bits [R, H] ->
     fp64 [T, R] = x . W^T.  The inputs are decoded exactly and each product
-    of two bf16 values is exact in fp64; the sums are fp64 (exact unless a
-    row's products span more than fp64's 53 bits of magnitude)."""
-    x = mxfp4.bf16_to_f64(x_bits)
-    w = mxfp4.bf16_to_f64(w_bits)
-    return x @ w.T
+    of two bf16 values is exact in fp64; the sums are fp64."""
+    x = np.ascontiguousarray(x_bits, dtype=np.uint16)
+    wr = np.ascontiguousarray(w_bits, dtype=np.uint16)
+    T, H = x.shape
+    R = wr.shape[0]
+    assert wr.shape[1] == H
+    out = np.empty((T, R), dtype=np.float64)
+    check(lib().oracle_router_logits(ptr(x), ptr(wr), T, R, H, ptr(out),
+                                     threads or default_threads()), "router_logits")
+    return out
 
 
 def align(ids: np.ndarray, Ep: int, tile_m: int = 32):
@@ -113,39 +115,36 @@ def align(ids: np.ndarray, Ep: int, tile_m: int = 32):
     ascending inside a group), inv int32 [A] (position of each flat id in
     sorted), tiles int32 [n_tiles, 2] (expert, first row) for tile_m-row
     tiles, expert-major and ascending, and n_tiles."""
-    flat = np.asarray(ids, dtype=np.int64).reshape(-1)
+    flat = np.ascontiguousarray(np.asarray(ids).reshape(-1), dtype=np.int32)
     A = flat.size
-    counts = np.bincount(flat, minlength=Ep)[:Ep].astype(np.int32)
-    offsets = np.zeros(Ep + 1, dtype=np.int32)
-    offsets[1:] = np.cumsum(counts)
-    sorted_ = np.argsort(flat, kind="stable").astype(np.int32)
+    counts = np.empty(Ep, dtype=np.int32)
+    offsets = np.empty(Ep + 1, dtype=np.int32)
+    srt = np.empty(A, dtype=np.int32)
     inv = np.empty(A, dtype=np.int32)
-    inv[sorted_] = np.arange(A, dtype=np.int32)
-    tiles = [(e, offsets[e] + s) for e in range(Ep) for s in range(0, int(counts[e]), tile_m)]
-    tiles = np.array(tiles, dtype=np.int32).reshape(-1, 2)
-    return counts, offsets, sorted_, inv, tiles, len(tiles)
-
-
-def silu(z):
-    """z * sigmoid(z) in fp64."""
-    with np.errstate(over="ignore"):
-        return z / (1.0 + np.exp(-z))
+    n = ctypes.c_int64(0)
+    max_tiles = A // tile_m + Ep + 1
+    tiles = np.empty((max_tiles, 2), dtype=np.int32)
+    check(lib().oracle_align(ptr(flat), A, Ep, tile_m, ptr(counts), ptr(offsets), ptr(srt),
+                             ptr(inv), ptr(tiles), max_tiles, ctypes.addressof(n)), "align")
+    return counts, offsets, srt, inv, tiles[:n.value].copy(), int(n.value)
 
 
 def expert_mlp(a: np.ndarray, w13_e, w13s_e, w2_e, w2s_e, I: int, act_fmt: int,
-               return_h: bool = False, wfmt: int = W_MXFP4):
+               return_h: bool = False, wfmt: int = W_MXFP4, threads: int | None = None):
     """One expert on rows a (fp64 [n, H], already bf16 / MXFP4-exact values).
 
     acc = a . dq(W13)^T (fp64); h = bf16(silu(acc[:, :I]) * acc[:, I:]);
-    for W4A4 h is MXFP4-quantised along I and decoded; y = h . dq(W2)^T.
-    dq decodes MXFP4 or (wfmt = W_MXFP8) MXFP8 weights.  With return_h, also
-    returns the bf16 h (before any MXFP4 step)."""
-    W13 = decode_weights(w13_e, w13s_e, wfmt)      # [2I, H]
-    acc = a @ W13.T                                # [n, 2I]
-    h = mxfp4.round_bf16(silu(acc[:, :I]) * acc[:, I:])
-    hin = mxfp4.decode(*mxfp4.quantize(h)) if act_fmt == ACT_MXFP4 else h
-    W2 = decode_weights(w2_e, w2s_e, wfmt)         # [H, I]
-    y = hin @ W2.T                                 # [n, H]
+    for W4A4 h is MXFP4-quantised along I and decoded; y = h . dq(W2)^T
+    (fp64, not rounded).  dq decodes MXFP4 or (wfmt = W_MXFP8) MXFP8
+    weights.  With return_h, also returns the bf16 h (before any MXFP4
+    step)."""
+    a = np.ascontiguousarray(a, dtype=np.float64)
+    n, H = a.shape
+    arrs = [np.ascontiguousarray(v, dtype=np.uint8) for v in (w13_e, w13s_e, w2_e, w2s_e)]
+    y = np.empty((n, H), dtype=np.float64)
+    h = np.empty((n, I), dtype=np.float64)
+    check(lib().oracle_expert_mlp(ptr(a), n, H, I, *[ptr(v) for v in arrs], act_fmt, wfmt,
+                                  ptr(y), ptr(h), threads or default_threads()), "expert_mlp")
     return (y, h) if return_h else y
 
 
@@ -156,7 +155,8 @@ def quantize_activations(x_bits: np.ndarray):
 
 def forward(x_bits, logits, gate, weights, I: int, E: int, K: int, shared: int,
             act_fmt: int = ACT_BF16, tokens=None, renormalize: bool = True,
-            tile_m: int = 32, wfmt: int = W_MXFP4):
+            tile_m: int = 32, wfmt: int = W_MXFP4, threads: int | None = None,
+            return_h: bool = False):
     """The whole layer.
 
     x_bits uint16 [T, H] (bf16 bit patterns); logits fp32 [T, E]; gate fp32
@@ -164,42 +164,54 @@ def forward(x_bits, logits, gate, weights, I: int, E: int, K: int, shared: int,
     w2 uint8 [H, I/2], w2s uint8 [H, I/32]) for e in [0, E+shared), MXFP4;
     with wfmt = W_MXFP8 the code arrays hold one byte per element (w13
     [2I, H], w2 [H, I]).  MXFP8 weights come with bf16 activations.
+    weights(e) is called only for experts the selected tokens use.
     tokens: optional list of token indices; when given, only those tokens'
     outputs are computed (routing and grouping still cover all T tokens).
+    return_h (all tokens only): also the bf16 h of every assignment, rows in
+    the grouping's sorted order.
 
     Each slot's expert output y is rounded to bf16 before the combine (where
     the GPU path stores it).  Returns a dict: ids, w, counts, offsets,
     sorted, inv, tiles, n_tiles, out (uint16 bf16 bits [len(tokens) or T,
-    H]), out_f64 (before the last rounding), tokens."""
+    H]), out_f64 (before the last rounding), tokens, seconds (the C++
+    call's wall time) and, with return_h, h (uint16 bf16 bits [T*K', I])."""
     assert wfmt == W_MXFP4 or act_fmt == ACT_BF16
-    x_bits = np.asarray(x_bits, dtype=np.uint16)
+    x_bits = np.ascontiguousarray(x_bits, dtype=np.uint16)
     T, H = x_bits.shape
     Kp, Ep = K + shared, E + shared
-    ids, w = route(logits, gate, K, shared, renormalize)
-    counts, offsets, sorted_, inv, tiles, n_tiles = align(ids, Ep, tile_m)
-    tokens = np.arange(T) if tokens is None else np.asarray(tokens, dtype=np.int64)
+    logits = np.ascontiguousarray(logits, dtype=np.float32)
+    g = np.ascontiguousarray(gate, dtype=np.float32) if shared else None
+    ids, w = route(logits, g, K, shared, renormalize)
+    counts, offsets, srt, inv, tiles, n_tiles = align(ids, Ep, tile_m)
+    all_tokens = tokens is None
+    tokens = np.arange(T, dtype=np.int64) if all_tokens else np.asarray(tokens, dtype=np.int64)
+    assert not (return_h and not all_tokens)
+    need = sorted(set(ids[tokens].reshape(-1).tolist())) if len(tokens) else []
 
-    if act_fmt == ACT_MXFP4:
-        xq, xs = quantize_activations(x_bits[tokens])
-        a_all = mxfp4.decode(xq, xs)
-    else:
-        a_all = mxfp4.bf16_to_f64(x_bits[tokens])
-
-    # y[j, k] = MLP of slot k of token tokens[j]
-    y = np.zeros((len(tokens), Kp, H), dtype=np.float64)
-    sel_ids = ids[tokens]                          # [n, Kp]
-    for e in np.unique(sel_ids):
-        rows, slots = np.nonzero(sel_ids == e)
-        y[rows, slots] = mxfp4.round_bf16(expert_mlp(a_all[rows], *weights(int(e)), I, act_fmt,
-                                                     wfmt=wfmt))
-
-    acc = np.zeros((len(tokens), H), dtype=np.float64)
-    wt = w[tokens].astype(np.float64)
-    for k in range(Kp):                            # slot order
-        acc += wt[:, k, None] * y[:, k]
-    return dict(ids=ids, w=w, counts=counts, offsets=offsets, sorted=sorted_, inv=inv,
-                tiles=tiles, n_tiles=n_tiles, out=mxfp4.bf16_bits(acc), out_f64=acc,
-                tokens=tokens)
+    keep = []                                     # the arrays stay alive for the call
+    P = ctypes.c_void_p * Ep
+    p13, p13s, p2, p2s = P(), P(), P(), P()
+    for e in need:
+        arrs = [np.ascontiguousarray(v, dtype=np.uint8) for v in weights(int(e))]
+        keep.append(arrs)
+        for table, arr in zip((p13, p13s, p2, p2s), arrs):
+            table[e] = arr.ctypes.data
+    n = len(tokens)
+    out = np.empty((n, H), dtype=np.uint16)
+    out_f64 = np.empty((n, H), dtype=np.float64)
+    h = np.empty((T * Kp, I), dtype=np.uint16) if return_h else None
+    secs = ctypes.c_double(0.0)
+    tok_arg = None if all_tokens else np.ascontiguousarray(tokens)
+    check(lib().oracle_forward(ptr(x_bits), ptr(logits), ptr(g), p13, p13s, p2, p2s, T, H, I, E,
+                               K, shared, act_fmt, wfmt, int(bool(renormalize)), ptr(tok_arg),
+                               n if not all_tokens else 0, threads or default_threads(), None,
+                               None, ptr(out), ptr(out_f64), ptr(h), ctypes.addressof(secs)),
+          "forward")
+    res = dict(ids=ids, w=w, counts=counts, offsets=offsets, sorted=srt, inv=inv, tiles=tiles,
+               n_tiles=n_tiles, out=out, out_f64=out_f64, tokens=tokens, seconds=secs.value)
+    if return_h:
+        res["h"] = h
+    return res
 
 
 def weights_from_arrays(w13, w13s, w2, w2s):

@@ -1,8 +1,9 @@
-"""MXFP8 (E4M3 elements) written out from its definition (fp64).
+"""MXFP8 (E4M3 elements): Python access to the C++ oracle's definitions
+(oracle/moe_oracle.cpp).
 
 TEST INFRASTRUCTURE.  Only tests/, __graft_entry__.smoke() and bench.py's
 cpu_baseline leg may import this package.  It shares no code with the HIP
-path and never imports it.
+path and never imports it.  This module only marshals arrays.
 
 The pages serve MoE models in MXFP8 as well as MXFP4 (MiniMax M3 on MI355X
 post, section on its MI355X performance benchmarks: MXFP8 standard
@@ -25,10 +26,9 @@ from __future__ import annotations
 
 import numpy as np
 
-from . import mxfp4
+from ._lib import check, default_threads, lib, ptr
 
 BLOCK = 32          # elements per scale block
-E4M3_EMAX = 8       # exponent of the largest E4M3 value (448 = 1.75 * 2^8)
 NAN_CODE = 0x7F     # S.1111.111
 
 
@@ -36,13 +36,7 @@ def e4m3_value(code: int) -> float:
     """Value of an 8-bit E4M3 code s|eeee|mmm: (-1)^s * m/8 * 2^-6 for
     e == 0 (subnormal), NaN for e == 15 and m == 7, and
     (-1)^s * (1 + m/8) * 2^(e-7) otherwise."""
-    s = (code >> 7) & 1
-    e = (code >> 3) & 15
-    m = code & 7
-    if e == 15 and m == 7:
-        return float("nan")
-    mag = (m / 8.0) * 2.0 ** -6 if e == 0 else (1.0 + m / 8.0) * 2.0 ** (e - 7)
-    return -mag if s else mag
+    return lib().oracle_e4m3_value(int(code))
 
 
 E4M3 = np.array([e4m3_value(c) for c in range(256)], dtype=np.float64)
@@ -53,43 +47,33 @@ GRID = E4M3[:NAN_CODE].copy()
 def decode(codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
     """MXFP8 -> fp64: value = E4M3[code] * 2^(scale - 127).
     codes uint8 [..., K], scales uint8 [..., K/32] -> fp64 [..., K]."""
-    vals = E4M3[np.asarray(codes, dtype=np.uint8)]
-    sc = mxfp4.e8m0_value(scales)
-    return vals * np.repeat(sc, BLOCK, axis=-1)
+    codes = np.ascontiguousarray(codes, dtype=np.uint8)
+    scales = np.ascontiguousarray(scales, dtype=np.uint8)
+    K = codes.shape[-1]
+    rows = codes.size // max(K, 1)
+    assert scales.shape[-1] * BLOCK == K and scales.size == rows * (K // BLOCK)
+    out = np.empty(codes.shape, dtype=np.float64)
+    check(lib().oracle_mxfp8_decode(ptr(codes), ptr(scales), rows, K, ptr(out)), "mxfp8 decode")
+    return out
 
 
-def _nearest_code_magnitude(mag: np.ndarray) -> np.ndarray:
-    """Code 0..126 of the GRID value nearest to mag (mag >= 0); on a tie the
-    even code (mantissa bit 0) wins.  Values above 448 land on 448, the
-    nearest grid value, so saturation needs no separate rule.  The two
-    candidates are the grid neighbours of mag, found by binary search."""
-    hi = np.clip(np.searchsorted(GRID, mag, side="left"), 1, len(GRID) - 1)
-    lo = hi - 1
-    d_lo = mag - GRID[lo]
-    d_hi = GRID[hi] - mag
-    take_hi = (d_hi < d_lo) | ((d_hi == d_lo) & (hi % 2 == 0))
-    code = np.where(take_hi, hi, lo)
-    return np.where(mag >= GRID[-1], len(GRID) - 1, code).astype(np.uint8)
-
-
-def quantize(v: np.ndarray):
-    """fp64 [..., K] (K a multiple of 32) -> (codes uint8 [..., K],
-    scales uint8 [..., K/32]).
+def quantize(v: np.ndarray, threads: int | None = None):
+    """fp64 (or float32) [..., K] (K a multiple of 32) -> (codes uint8
+    [..., K], scales uint8 [..., K/32]).
 
     Per block: amax = max |v|; X = floor(log2 amax) - 8, clamped to
     [-127, 127] (X = -127 for an all-zero block); scale byte X + 127.  Each
     v / 2^X is rounded to the nearest E4M3 magnitude, ties to the even code,
     saturating at 448; the sign bit of v is kept (so -0.0 and negatives that
     round to zero give code 0x80)."""
-    v = np.asarray(v, dtype=np.float64)
+    v = np.asarray(v)
+    f32 = v.dtype == np.float32
+    v = np.ascontiguousarray(v, dtype=np.float32 if f32 else np.float64)
     K = v.shape[-1]
     assert K % BLOCK == 0
-    blocks = v.reshape(*v.shape[:-1], K // BLOCK, BLOCK)
-    amax = np.abs(blocks).max(axis=-1)
-    _, ex = np.frexp(amax)                 # amax = f * 2^ex, f in [0.5, 1)
-    X = np.where(amax > 0, (ex - 1) - E4M3_EMAX, -127)
-    X = np.clip(X, -127, 127)
-    scaled = blocks / np.ldexp(1.0, X)[..., None]
-    codes = _nearest_code_magnitude(np.abs(scaled))
-    codes = codes | (np.signbit(scaled).astype(np.uint8) << 7)
-    return codes.reshape(*v.shape[:-1], K), (X + 127).astype(np.uint8)
+    rows = v.size // K
+    codes = np.empty(v.shape, dtype=np.uint8)
+    scales = np.empty(v.shape[:-1] + (K // BLOCK,), dtype=np.uint8)
+    check(lib().oracle_mxfp8_quantize(ptr(v), int(f32), rows, K, ptr(codes), ptr(scales),
+                                      threads or default_threads()), "mxfp8 quantize")
+    return codes, scales

@@ -98,8 +98,8 @@ class Problem:
     def oracle_weights(self, e: int):
         """Expert e packed by the oracle's own quantiser from the same draws."""
         c = self.cfg
-        a = mxfp4.quantize(synth.expert_w13(c, e, DEV).cpu().double().numpy())
-        b = mxfp4.quantize(synth.expert_w2(c, e, DEV).cpu().double().numpy())
+        a = mxfp4.quantize(synth.expert_w13(c, e, DEV).cpu().numpy())
+        b = mxfp4.quantize(synth.expert_w2(c, e, DEV).cpu().numpy())
         return a[0], a[1], b[0], b[1]
 
     def oracle(self, tokens=None, act_fmt=None):

@@ -76,8 +76,8 @@ class Layers:
     def oracle_weights(self, l, e):
         if (l, e) not in self._ow:
             lc = synth.layer_config(self.cfg, l)
-            a = mxfp4.quantize(synth.expert_w13(lc, e, DEV).cpu().double().numpy())
-            b = mxfp4.quantize(synth.expert_w2(lc, e, DEV).cpu().double().numpy())
+            a = mxfp4.quantize(synth.expert_w13(lc, e, DEV).cpu().numpy())
+            b = mxfp4.quantize(synth.expert_w2(lc, e, DEV).cpu().numpy())
             self._ow[(l, e)] = (a[0], a[1], b[0], b[1])
         return self._ow[(l, e)]
 

@@ -59,8 +59,8 @@ class Problem8:
     @functools.lru_cache(maxsize=None)
     def oracle_weights(self, e: int):
         c = self.cfg
-        a = mxfp8.quantize(synth.expert_w13(c, e, DEV).cpu().double().numpy())
-        b = mxfp8.quantize(synth.expert_w2(c, e, DEV).cpu().double().numpy())
+        a = mxfp8.quantize(synth.expert_w13(c, e, DEV).cpu().numpy())
+        b = mxfp8.quantize(synth.expert_w2(c, e, DEV).cpu().numpy())
         return a[0], a[1], b[0], b[1]
 
     def oracle(self, tokens=None):
