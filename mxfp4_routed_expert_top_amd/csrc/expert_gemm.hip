@@ -283,7 +283,7 @@ __attribute__((amdgpu_waves_per_eu(MOE_GEMM_WAVES_PER_EU))) void down_kernel(
     const void* __restrict__ hin, const uint8_t* __restrict__ hscale,
     const int32_t* __restrict__ offsets, const int32_t* __restrict__ tiles,
     const int32_t* __restrict__ num_tiles, const uint8_t* __restrict__ w2,
-    const uint8_t* __restrict__ w2s, int A, int H, int I, int nsl, uint16_t* __restrict__ y) {
+    const uint8_t* __restrict__ w2s, int A, int H, int I, int nsl, float* __restrict__ y) {
   TileInfo ti;
   if (!load_tile(tiles, num_tiles, offsets, (int)(blockIdx.x / nsl), &ti)) return;
   const int s = blockIdx.x % nsl;
@@ -337,9 +337,9 @@ __attribute__((amdgpu_waves_per_eu(MOE_GEMM_WAVES_PER_EU))) void down_kernel(
     for (int r = 0; r < 4; ++r) {
       const int mm = 16 * mt + 4 * g + r;
       if (mm < ti.rows) {
-        uint16_t* yr = y + (size_t)(ti.row0 + mm) * H;
-        yr[j0] = f32_to_bf16_rne(acc[0][r]);
-        yr[j0 + 16] = f32_to_bf16_rne(acc[1][r]);
+        float* yr = y + (size_t)(ti.row0 + mm) * H;
+        yr[j0] = acc[0][r];
+        yr[j0 + 16] = acc[1][r];
       }
     }
   }
@@ -367,10 +367,11 @@ __device__ __forceinline__ void prefetch_ranges(const Prefetch& pf, int b) {
 }
 
 // out[t, j] = bf16( sum_k w[t, k] * y[inv[t*K' + k], j] ), slots in order,
-// fp32 sums; 8 outputs per thread (16-byte loads of y, a 16-byte store).
-// (Slot by slot, each y load waited for its row index: combine 167 -> 136
-// us on the skewed batch, 101 -> 88 us on the W4A4 one.)
-__global__ __launch_bounds__(256) void combine_kernel(const uint16_t* __restrict__ y,
+// fp32 y and sums; 8 outputs per thread (two 16-byte loads of each slot's y,
+// a 16-byte store).  The eight slots' row indices are read first, then their
+// y rows, so the loads are independent (waiting for each slot's index before
+// its y load cost 20% on the skewed batch).
+__global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ y,
                                                       const float* __restrict__ w,
                                                       const int32_t* __restrict__ inv, int H,
                                                       int Kp, int nbx, uint16_t* __restrict__ out,
@@ -395,19 +396,19 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint16_t* __restrict
       r[i] = ok ? inv[(size_t)t * Kp + k0 + i] : 0;
       wk[i] = ok ? w[(size_t)t * Kp + k0 + i] : 0.f;
     }
-    u32x4_t v[8];
+    floatx4_t v[8][2];
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      if (k0 + i < Kp) {
+        const floatx4_t* p = reinterpret_cast<const floatx4_t*>(y + (size_t)r[i] * H + j);
+        v[i][0] = __builtin_nontemporal_load(p);
+        v[i][1] = __builtin_nontemporal_load(p + 1);
+      }
 #pragma unroll
     for (int i = 0; i < 8; ++i)
       if (k0 + i < Kp)
-        v[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(y + (size_t)r[i] * H + j));
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
-      if (k0 + i < Kp)
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          acc[2 * q] += wk[i] * __uint_as_float(v[i][q] << 16);
-          acc[2 * q + 1] += wk[i] * __uint_as_float(v[i][q] & 0xFFFF0000u);
-        }
+        for (int q = 0; q < 8; ++q) acc[q] += wk[i] * v[i][q / 4][q % 4];
   }
   u32x4_t o;
 #pragma unroll
@@ -419,6 +420,12 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint16_t* __restrict
 }  // namespace
 
 int expert_gemm_tile_m() { return kTileM; }
+
+// Dynamic LDS of the 32-row kernels over a reduction of K: the weight scales
+// of 128 rows, plus (bf16 activations) kXR activation rows.
+size_t expert_gemm_lds_bytes(int K, int act_fmt) {
+  return (size_t)128 * (K / 32) + (act_fmt == 0 ? (size_t)kXR * K * 2 : 0);
+}
 
 // Phase width (chunks of 128 K-elements per pipeline stage): 2 when the chunk
 // count is even, else 1.  MXFP8 weights (32 bytes per lane per chunk) use 1,
@@ -445,7 +452,7 @@ struct DownLaunch {
   static hipError_t run(dim3 grid, hipStream_t stream, const void* hin, const uint8_t* hscale,
                         const int32_t* offsets, const int32_t* tiles, const int32_t* num_tiles,
                         const uint8_t* w2, const uint8_t* w2s, int A, int H, int I, int nsl,
-                        uint16_t* y) {
+                        float* y) {
     const size_t lds = (size_t)128 * (I / 32) + (kFP4A ? 0 : (size_t)kXR * I * 2);
     hipLaunchKernelGGL((down_kernel<PH, kFP4A, kW8>), grid, dim3(256), lds, stream,
                        hin, hscale, offsets,
@@ -480,14 +487,14 @@ hipError_t launch_gate_up(int act_fmt, int wfmt, const void* act, const uint8_t*
 hipError_t launch_down(int act_fmt, int wfmt, const void* h, const uint8_t* h_scale,
                        const int32_t* offsets, const int32_t* tiles, const int32_t* num_tiles,
                        int max_tiles, const uint8_t* w2, const uint8_t* w2s, int A, int H, int I,
-                       uint16_t* y, hipStream_t stream) {
+                       float* y, hipStream_t stream) {
   const int nsl = H / 128;
   dim3 grid((unsigned)(max_tiles * nsl));
   return dispatch<DownLaunch>(act_fmt, wfmt, I / 128, grid, stream, h, h_scale, offsets, tiles,
                               num_tiles, w2, w2s, A, H, I, nsl, y);
 }
 
-hipError_t launch_combine(const uint16_t* y, const float* w, const int32_t* inv, int T, int H, int Kp,
+hipError_t launch_combine(const float* y, const float* w, const int32_t* inv, int T, int H, int Kp,
                           uint16_t* out, hipStream_t stream, const Prefetch* pf) {
   const int nbx = (H / 8 + 255) / 256;
   Prefetch none{};

@@ -617,7 +617,7 @@ __global__ __launch_bounds__(256, KV ? 2 : 1) void down_tiled_kernel(
     const void* __restrict__ hin, const uint8_t* __restrict__ hscale,
     const int32_t* __restrict__ offsets, const int32_t* __restrict__ tiles,
     const int32_t* __restrict__ num_tiles, const uint8_t* __restrict__ w2,
-    const uint8_t* __restrict__ w2s, int A, int H, int I, uint16_t* __restrict__ y) {
+    const uint8_t* __restrict__ w2s, int A, int H, int I, float* __restrict__ y) {
   TileT ti;
   int s;
   if (!tile_slice<BM, kFP4A, 4>(blockIdx.x, tiles, offsets, *num_tiles, H / 256, &ti, &s)) return;
@@ -651,9 +651,9 @@ __global__ __launch_bounds__(256, KV ? 2 : 1) void down_tiled_kernel(
     for (int r = 0; r < 4; ++r) {
       const int m = 16 * mt + 4 * g + r;
       if (m < ti.rows) {
-        uint16_t* yr = y + (size_t)(ti.row0 + m) * H;
+        float* yr = y + (size_t)(ti.row0 + m) * H;
 #pragma unroll
-        for (int st = 0; st < 4; ++st) yr[j0 + 16 * st + nl] = f32_to_bf16_rne(acc[mt][st][r]);
+        for (int st = 0; st < 4; ++st) yr[j0 + 16 * st + nl] = acc[mt][st][r];
       }
     }
 }
@@ -673,7 +673,7 @@ hipError_t launch_gate_up_bm(const void* act, const uint8_t* act_scale, const in
 template <int BM, bool kFP4A, bool kW8 = false, int KV = 0, bool kBlk = false>
 hipError_t launch_down_bm(const void* h, const uint8_t* h_scale, const int32_t* offsets,
                           const int32_t* tiles, const int32_t* num_tiles, int max_tiles,
-                          const uint8_t* w2, const uint8_t* w2s, int A, int H, int I, uint16_t* y,
+                          const uint8_t* w2, const uint8_t* w2s, int A, int H, int I, float* y,
                           hipStream_t stream) {
   const unsigned grid = tile_slice_grid<kFP4A>(max_tiles, H / 256);
   hipLaunchKernelGGL((down_tiled_kernel<BM, kFP4A, kW8, KV, kBlk>), dim3(grid), dim3(256), 0, stream, h,
@@ -707,7 +707,7 @@ hipError_t gate_up_fp4(int tile_m, const void* act, const uint8_t* act_scale,
 template <bool kBlk>
 hipError_t down_fp4(int tile_m, const void* h, const uint8_t* h_scale, const int32_t* offsets,
                     const int32_t* tiles, const int32_t* num_tiles, int max_tiles,
-                    const uint8_t* w2, const uint8_t* w2s, int A, int H, int I, uint16_t* y,
+                    const uint8_t* w2, const uint8_t* w2s, int A, int H, int I, float* y,
                     hipStream_t stream) {
 #define MOE_DN_ARGS h, h_scale, offsets, tiles, num_tiles, max_tiles, w2, w2s, A, H, I, y, stream
   if (tile_m == 256) return launch_down_bm<256, true, false, 0, kBlk>(MOE_DN_ARGS);
@@ -766,7 +766,7 @@ hipError_t launch_down_tiled(int tile_m, int act_fmt, int wfmt, const void* h,
                              const uint8_t* h_scale,
                              const int32_t* offsets, const int32_t* tiles,
                              const int32_t* num_tiles, int max_tiles, const uint8_t* w2,
-                             const uint8_t* w2s, int A, int H, int I, uint16_t* y,
+                             const uint8_t* w2s, int A, int H, int I, float* y,
                              hipStream_t stream) {
   if (wfmt == 1)
     return tile_m == 128 ? launch_down_bm<128, false, true>(h, h_scale, offsets, tiles, num_tiles,

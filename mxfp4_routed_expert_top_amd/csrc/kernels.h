@@ -42,6 +42,10 @@ hipError_t launch_weights_native(const uint8_t* src, int nq, int64_t rows, int64
                                  uint8_t* dst, hipStream_t stream);
 
 int expert_gemm_tile_m();
+// Dynamic LDS bytes of the 32-row kernels for a reduction of K elements
+// (act_fmt 0: bf16 activations staged too); at most kMaxLdsBytes.
+size_t expert_gemm_lds_bytes(int K, int act_fmt);
+constexpr size_t kMaxLdsBytes = 160 * 1024;
 int expert_gemm_phase(int nch);
 // wfmt: 0 = MXFP4 weights, 1 = MXFP8 weights (bf16 activations only)
 hipError_t launch_gate_up(int act_fmt, int wfmt, const void* act, const uint8_t* act_scale,
@@ -49,10 +53,12 @@ hipError_t launch_gate_up(int act_fmt, int wfmt, const void* act, const uint8_t*
                           const int32_t* num_tiles, int max_tiles, const uint8_t* w13,
                           const uint8_t* w13s, int T, int H, int I, int Kp, uint16_t* h,
                           hipStream_t stream);
+// y fp32 [A, H]: each sorted row's down-projection, unrounded (the combine
+// sums the weighted rows in fp32 and rounds once, to the bf16 output)
 hipError_t launch_down(int act_fmt, int wfmt, const void* h, const uint8_t* h_scale,
                        const int32_t* offsets, const int32_t* tiles, const int32_t* num_tiles,
                        int max_tiles, const uint8_t* w2, const uint8_t* w2s, int A, int H, int I,
-                       uint16_t* y, hipStream_t stream);
+                       float* y, hipStream_t stream);
 // Byte ranges the combine's extra workgroups read into the caches (the next
 // layer's weights that are known before its routing); n = 0 for none.
 struct Prefetch {
@@ -61,7 +67,7 @@ struct Prefetch {
   uint32_t bytes[kMax];
   int n;
 };
-hipError_t launch_combine(const uint16_t* y, const float* w, const int32_t* inv, int T, int H, int Kp,
+hipError_t launch_combine(const float* y, const float* w, const int32_t* inv, int T, int H, int Kp,
                           uint16_t* out, hipStream_t stream, const Prefetch* pf = nullptr);
 
 bool expert_gemm_tiled_supported(int tile_m, int act_fmt, int H, int I, int wfmt = 0);
@@ -71,9 +77,10 @@ hipError_t launch_gate_up_tiled(int tile_m, int act_fmt, int wfmt, const void* a
                                 const int32_t* tiles, const int32_t* num_tiles, int max_tiles,
                                 const uint8_t* w13, const uint8_t* w13s, int T, int H, int I,
                                 int Kp, uint16_t* h, hipStream_t stream);
+// y fp32 [A, H] in sorted order (as launch_down)
 hipError_t launch_down_tiled(int tile_m, int act_fmt, int wfmt, const void* h,
                              const uint8_t* h_scale,
                              const int32_t* offsets, const int32_t* tiles,
                              const int32_t* num_tiles, int max_tiles, const uint8_t* w2,
-                             const uint8_t* w2s, int A, int H, int I, uint16_t* y,
+                             const uint8_t* w2s, int A, int H, int I, float* y,
                              hipStream_t stream);

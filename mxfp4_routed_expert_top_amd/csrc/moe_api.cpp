@@ -5,6 +5,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include "common.h"
 #include "kernels.h"
 
 namespace {
@@ -87,9 +88,10 @@ FwdLayout forward_layout(int64_t T, int64_t H, int64_t I, int64_t E, int64_t K, 
   L.h = take(A * I * 2);
   L.hq = take(q ? A16 * I / 2 : 0);
   L.hs = take(q ? A16 * I / 32 : 0);
-  // y; the router GEMM's partial sums (when the call routes from x) live in
-  // the same bytes: routing consumes them before the down GEMM writes y
-  L.y = take(std::max((size_t)(A * H * 2), router_workspace_bytes((int)T, (int)H, (int)Ep)));
+  // y fp32 [A, H]; the router GEMM's partial sums (when the call routes from
+  // x) live in the same bytes: routing consumes them before the down GEMM
+  // writes y
+  L.y = take(std::max((size_t)(A * H * 4), router_workspace_bytes((int)T, (int)H, (int)Ep)));
   L.total = p;
   return L;
 }
@@ -286,6 +288,8 @@ moe_status gate_up_impl(const void* act, const uint8_t* act_scale, int32_t act_f
     return MOE_ERR_UNSUPPORTED;
   if (!tile_m_ok(tile_m, act_fmt, H, I, wfmt) || (blk && tile_m == MOE_TILE_M))
     return MOE_ERR_UNSUPPORTED;
+  if (tile_m == MOE_TILE_M && expert_gemm_lds_bytes(H, act_fmt) > kMaxLdsBytes)
+    return MOE_ERR_UNSUPPORTED;
   if (T == 0) return MOE_OK;
   if (!act || !sorted_assign || !expert_offsets || !tile_table || !num_tiles || !w13 ||
       !w13_scale || !h || (act_fmt != MOE_ACT_BF16 && !act_scale))
@@ -308,7 +312,7 @@ moe_status down_impl(const void* h, const uint8_t* h_scale, int32_t act_fmt, int
                      const int32_t* expert_offsets, const int32_t* tile_table,
                      const int32_t* num_tiles, int32_t tile_m, const uint8_t* w2,
                      const uint8_t* w2_scale, int32_t T, int32_t H, int32_t I, int32_t Ep,
-                     int32_t Kp, uint16_t* y, void* stream) {
+                     int32_t Kp, float* y, void* stream) {
   if (T < 0 || Ep < 1 || Kp < 1 || !act_fmt_ok(act_fmt)) return MOE_ERR_INVALID_ARGUMENT;
   moe_status st = check_shape_HI(H, I);
   if (st != MOE_OK) return st;
@@ -316,6 +320,8 @@ moe_status down_impl(const void* h, const uint8_t* h_scale, int32_t act_fmt, int
   if (Ep > 2048 || !weights_fit(wfmt, H, I) || !acts_fit(act_fmt, (int64_t)T * Kp, I))
     return MOE_ERR_UNSUPPORTED;
   if (!tile_m_ok(tile_m, act_fmt, H, I, wfmt) || (blk && tile_m == MOE_TILE_M))
+    return MOE_ERR_UNSUPPORTED;
+  if (tile_m == MOE_TILE_M && expert_gemm_lds_bytes(I, act_fmt) > kMaxLdsBytes)
     return MOE_ERR_UNSUPPORTED;
   if (T == 0) return MOE_OK;
   if (!h || !expert_offsets || !tile_table || !num_tiles || !w2 || !w2_scale || !y ||
@@ -359,7 +365,7 @@ moe_status moe_expert_down(const void* h, const uint8_t* h_scale, int32_t act_fm
                            const int32_t* expert_offsets, const int32_t* tile_table,
                            const int32_t* num_tiles, int32_t tile_m, const uint8_t* w2,
                            const uint8_t* w2_scale, int32_t T, int32_t H, int32_t I, int32_t Ep,
-                           int32_t Kp, uint16_t* y, void* stream) {
+                           int32_t Kp, float* y, void* stream) {
   return down_impl(h, h_scale, act_fmt, 0, expert_offsets, tile_table, num_tiles, tile_m, w2,
                    w2_scale, T, H, I, Ep, Kp, y, stream);
 }
@@ -368,12 +374,12 @@ moe_status moe_mxfp8_expert_down(const uint16_t* h, const int32_t* expert_offset
                                  const int32_t* tile_table, const int32_t* num_tiles,
                                  int32_t tile_m, const uint8_t* w2, const uint8_t* w2_scale,
                                  int32_t T, int32_t H, int32_t I, int32_t Ep, int32_t Kp,
-                                 uint16_t* y, void* stream) {
+                                 float* y, void* stream) {
   return down_impl(h, nullptr, MOE_ACT_BF16, 1, expert_offsets, tile_table, num_tiles, tile_m, w2,
                    w2_scale, T, H, I, Ep, Kp, y, stream);
 }
 
-moe_status moe_combine(const uint16_t* y, const float* topk_weights, const int32_t* inv_assign,
+moe_status moe_combine(const float* y, const float* topk_weights, const int32_t* inv_assign,
                        int32_t T, int32_t H, int32_t Kp, uint16_t* out, void* stream) {
   if (T < 0 || H <= 0 || Kp < 1) return MOE_ERR_INVALID_ARGUMENT;
   if (H % 128) return MOE_ERR_UNSUPPORTED;
@@ -455,11 +461,15 @@ moe_status forward_impl(const uint16_t* x, const float* router_logits,
   uint16_t* h = (uint16_t*)(ws + L.h);
   uint8_t* hq = (uint8_t*)(ws + L.hq);
   uint8_t* hs = (uint8_t*)(ws + L.hs);
-  uint16_t* y = (uint16_t*)(ws + L.y);
+  float* y = (float*)(ws + L.y);
   float* rpart = (float*)(ws + L.y);                       // router partial sums (same bytes)
   hipStream_t s = as_stream(stream);
   const int tm = choose_tile_m(A, Ep, H, I, act_fmt, wfmt);
   const int mt = (int)max_tiles_for(A, Ep, tm);
+  // the 32-row kernels' LDS (weight scales, staged activation rows) must fit
+  if (tm == MOE_TILE_M && (expert_gemm_lds_bytes(H, act_fmt) > kMaxLdsBytes ||
+                           expert_gemm_lds_bytes(I, act_fmt) > kMaxLdsBytes))
+    return MOE_ERR_UNSUPPORTED;
 
   hipError_t e;
   if (router_w) {

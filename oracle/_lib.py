@@ -3,7 +3,7 @@
 TEST INFRASTRUCTURE.  The library is compiled with g++ (plain C++17, no GPU
 headers) into oracle/_build/: libmoe_oracle.so for the Python wrappers and
 moe_oracle, its command-line tool.  __graft_entry__.build() rebuilds both
-every time; lib() builds them only when they are missing.
+every time; lib() builds them when they are missing or older than a source.
 """
 from __future__ import annotations
 
@@ -61,7 +61,9 @@ def _declare(L):
         "oracle_expert_mlp": (c.c_int, [P, i64, i64, i64, P, P, P, P, c.c_int, c.c_int, P, P,
                                         c.c_int]),
         "oracle_forward": (c.c_int, [P, P, P, P, P, P, P, i64, i64, i64, i32, i32, i32, c.c_int,
-                                     c.c_int, i32, P, i64, c.c_int, P, P, P, P, P, P]),
+                                     c.c_int, i32, i32, P, i64, c.c_int, P, P, P, P, P, P]),
+        "oracle_forward_from_h": (c.c_int, [P, P, P, P, P, i64, i64, i64, i32, i32, i32, c.c_int,
+                                            c.c_int, i32, i32, c.c_int, P, P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(L, name)
@@ -70,12 +72,21 @@ def _declare(L):
     return L
 
 
+def _stale() -> bool:
+    """True when the library or the tool is missing or older than a source."""
+    if not os.path.exists(LIB_PATH) or not os.path.exists(CLI_PATH):
+        return True
+    built = min(os.path.getmtime(LIB_PATH), os.path.getmtime(CLI_PATH))
+    srcs = CLI_SOURCES + [os.path.join(HERE, "moe_oracle.h")]
+    return any(os.path.getmtime(p) > built for p in srcs)
+
+
 def lib():
-    """The loaded oracle library (built first if it is missing)."""
+    """The loaded oracle library (built first if it is missing or stale)."""
     global _lib
     with _lock:
         if _lib is None:
-            if not os.path.exists(LIB_PATH) or not os.path.exists(CLI_PATH):
+            if _stale():
                 build()
             _lib = _declare(ctypes.CDLL(LIB_PATH))
     return _lib

@@ -20,14 +20,14 @@ x_t and (when the shared expert is folded in) gate logit g_t:
           expert becomes expert top-K+1 of one MoE dispatch; MiniMax M3 on
           MI355X post, section "Shared expert fusion")
   MLP_e(a) = W2_e . bf16( silu(W13_e[gate] . a) * (W13_e[up] . a) )
-  out_t = bf16( sum_k w_t,k * bf16(MLP_{e_k}(x_t)) ), summed in slot order.
+  out_t = bf16( sum_k w_t,k * MLP_{e_k}(x_t) ), summed in slot order.
 
 MXFP4 weights are decoded exactly; each dot product is an fp64 sum of exact
-products; bf16 rounding happens where the GPU path stores bf16: h, each
-slot's expert output y (staged between the down GEMM and the combine; the
-pages fix no precision for it, and bf16 is the activations' type on the
-path) and out.  For W4A4 the activations and h are MXFP4-quantised then
-decoded before their GEMM (OpenRelay "Gemma 4 31B on MI355X" post, sections
+products; bf16 rounding happens where the GPU path stores bf16: h, out,
+and (round_y) each slot's expert output y where a path stages it in bf16
+between the down GEMM and the combine (the pages fix no precision for y).
+For W4A4 the activations and h are MXFP4-quantised then decoded before
+their GEMM (OpenRelay "Gemma 4 31B on MI355X" post, sections
 "Optimisation 3" and "Optimisation 4": activation + MXFP4 quantisation
 fused into one kernel).
 
@@ -156,7 +156,7 @@ def quantize_activations(x_bits: np.ndarray):
 def forward(x_bits, logits, gate, weights, I: int, E: int, K: int, shared: int,
             act_fmt: int = ACT_BF16, tokens=None, renormalize: bool = True,
             tile_m: int = 32, wfmt: int = W_MXFP4, threads: int | None = None,
-            return_h: bool = False):
+            return_h: bool = False, round_y: bool = False):
     """The whole layer.
 
     x_bits uint16 [T, H] (bf16 bit patterns); logits fp32 [T, E]; gate fp32
@@ -170,8 +170,10 @@ def forward(x_bits, logits, gate, weights, I: int, E: int, K: int, shared: int,
     return_h (all tokens only): also the bf16 h of every assignment, rows in
     the grouping's sorted order.
 
-    Each slot's expert output y is rounded to bf16 before the combine (where
-    the GPU path stores it).  Returns a dict: ids, w, counts, offsets,
+    round_y: each slot's expert output y is rounded to bf16 before the
+    combine (a path that stores y in bf16 between the down GEMM and the
+    combine); False (the default, as the GPU path) keeps it unrounded.
+    Returns a dict: ids, w, counts, offsets,
     sorted, inv, tiles, n_tiles, out (uint16 bf16 bits [len(tokens) or T,
     H]), out_f64 (before the last rounding), tokens, seconds (the C++
     call's wall time) and, with return_h, h (uint16 bf16 bits [T*K', I])."""
@@ -203,7 +205,8 @@ def forward(x_bits, logits, gate, weights, I: int, E: int, K: int, shared: int,
     secs = ctypes.c_double(0.0)
     tok_arg = None if all_tokens else np.ascontiguousarray(tokens)
     check(lib().oracle_forward(ptr(x_bits), ptr(logits), ptr(g), p13, p13s, p2, p2s, T, H, I, E,
-                               K, shared, act_fmt, wfmt, int(bool(renormalize)), ptr(tok_arg),
+                               K, shared, act_fmt, wfmt, int(bool(renormalize)),
+                               int(bool(round_y)), ptr(tok_arg),
                                n if not all_tokens else 0, threads or default_threads(), None,
                                None, ptr(out), ptr(out_f64), ptr(h), ctypes.addressof(secs)),
           "forward")
@@ -212,6 +215,38 @@ def forward(x_bits, logits, gate, weights, I: int, E: int, K: int, shared: int,
     if return_h:
         res["h"] = h
     return res
+
+
+def forward_from_h(h_bits, logits, gate, weights, I: int, E: int, K: int, shared: int,
+                   act_fmt: int = ACT_BF16, renormalize: bool = True, wfmt: int = W_MXFP4,
+                   threads: int | None = None, round_y: bool = False):
+    """The layer from a given h onward: routing and grouping as forward, then
+    each assignment's down projection of h_bits (uint16 bf16 [T*K', I], rows
+    in the grouping's sorted order; MXFP4-quantised and decoded first for
+    W4A4) and the combine.  weights(e) as in forward (only its W2 arrays
+    are read).  Returns out (bf16 bits [T, H]) and out_f64."""
+    h_bits = np.ascontiguousarray(h_bits, dtype=np.uint16)
+    logits = np.ascontiguousarray(logits, dtype=np.float32)
+    T = logits.shape[0]
+    Kp, Ep = K + shared, E + shared
+    assert h_bits.shape == (T * Kp, I)
+    g = np.ascontiguousarray(gate, dtype=np.float32) if shared else None
+    ids, _ = route(logits, g, K, shared, renormalize)
+    keep = []
+    P = ctypes.c_void_p * Ep
+    p2, p2s = P(), P()
+    for e in sorted(set(ids.reshape(-1).tolist())):
+        arrs = [np.ascontiguousarray(v, dtype=np.uint8) for v in weights(int(e))[2:4]]
+        keep.append(arrs)
+        p2[e], p2s[e] = arrs[0].ctypes.data, arrs[1].ctypes.data
+    H = keep[0][0].shape[0] if keep else 0
+    out = np.empty((T, H), dtype=np.uint16)
+    out_f64 = np.empty((T, H), dtype=np.float64)
+    check(lib().oracle_forward_from_h(ptr(h_bits), ptr(logits), ptr(g), p2, p2s, T, H, I, E, K,
+                                      shared, act_fmt, wfmt, int(bool(renormalize)),
+                                      int(bool(round_y)), threads or default_threads(), ptr(out),
+                                      ptr(out_f64)), "forward_from_h")
+    return dict(out=out, out_f64=out_f64)
 
 
 def weights_from_arrays(w13, w13s, w2, w2s):

@@ -302,13 +302,12 @@ void mxfp4_roundtrip_row(double *v, int64_t K) {
 // Columns of one expert's gate/up GEMM handled by one work item.
 constexpr int64_t kCols = 8;
 
-// One expert on n rows of a (see oracle_expert_mlp).  h (n x I) is always
-// written; y (n x H) gets the fp64 down-projection.
-void expert_mlp(const double *a, int64_t n, int64_t H, int64_t I, const uint8_t *w13,
-                const uint8_t *w13s, const uint8_t *w2, const uint8_t *w2s, int act_fmt, int wfmt,
-                double *y, double *h, Pool &pool) {
-  const int64_t rb13 = row_bytes(H, wfmt), rb2 = row_bytes(I, wfmt);
-  // gate/up + SwiGLU: a work item owns intermediate columns [i0, i0 + kCols)
+// Gate/up GEMM + SwiGLU of one expert on n rows of a: h (n x I) gets the
+// bf16-rounded values.
+void expert_gate_up(const double *a, int64_t n, int64_t H, int64_t I, const uint8_t *w13,
+                    const uint8_t *w13s, int wfmt, double *h, Pool &pool) {
+  const int64_t rb13 = row_bytes(H, wfmt);
+  // a work item owns intermediate columns [i0, i0 + kCols)
   pool.for_each((I + kCols - 1) / kCols, [&](int64_t item) {
     const int64_t i0 = item * kCols, ni = std::min(kCols, I - i0);
     std::vector<double> gate(ni * H), up(ni * H);
@@ -323,7 +322,13 @@ void expert_mlp(const double *a, int64_t n, int64_t H, int64_t I, const uint8_t 
         h[r * I + i0 + i] = round_bf16(silu(g) * u);
       }
   });
-  // W4A4: the down GEMM reads h quantised to MXFP4 (along I) and decoded
+}
+
+// Down GEMM of one expert on n rows of bf16 h: y (n x H), fp64, unrounded.
+// For W4A4 the rows of h are first quantised to MXFP4 (along I) and decoded.
+void expert_down(const double *h, int64_t n, int64_t H, int64_t I, const uint8_t *w2,
+                 const uint8_t *w2s, int act_fmt, int wfmt, double *y, Pool &pool) {
+  const int64_t rb2 = row_bytes(I, wfmt);
   std::vector<double> hq;
   const double *hin = h;
   if (act_fmt == ORACLE_ACT_MXFP4) {
@@ -331,7 +336,7 @@ void expert_mlp(const double *a, int64_t n, int64_t H, int64_t I, const uint8_t 
     pool.for_each(n, [&](int64_t r) { mxfp4_roundtrip_row(&hq[r * I], I); });
     hin = hq.data();
   }
-  // down: a work item owns output columns [j0, j0 + kCols)
+  // a work item owns output columns [j0, j0 + kCols)
   pool.for_each((H + kCols - 1) / kCols, [&](int64_t item) {
     const int64_t j0 = item * kCols, nj = std::min(kCols, H - j0);
     std::vector<double> wrow(nj * I);
@@ -340,6 +345,15 @@ void expert_mlp(const double *a, int64_t n, int64_t H, int64_t I, const uint8_t 
     for (int64_t r = 0; r < n; ++r)
       for (int64_t j = 0; j < nj; ++j) y[r * H + j0 + j] = dot(hin + r * I, &wrow[j * I], I);
   });
+}
+
+// One expert on n rows of a (see oracle_expert_mlp): h (n x I) always
+// written, y (n x H) the fp64 down-projection.
+void expert_mlp(const double *a, int64_t n, int64_t H, int64_t I, const uint8_t *w13,
+                const uint8_t *w13s, const uint8_t *w2, const uint8_t *w2s, int act_fmt, int wfmt,
+                double *y, double *h, Pool &pool) {
+  expert_gate_up(a, n, H, I, w13, w13s, wfmt, h, pool);
+  expert_down(h, n, H, I, w2, w2s, act_fmt, wfmt, y, pool);
 }
 
 void route(const float *logits, const float *gate, int64_t T, int32_t E, int32_t K, int32_t shared,
@@ -512,9 +526,9 @@ int oracle_forward(const uint16_t *x_bits, const float *logits, const float *gat
                    const uint8_t *const *w13, const uint8_t *const *w13s,
                    const uint8_t *const *w2, const uint8_t *const *w2s, int64_t T, int64_t H,
                    int64_t I, int32_t E, int32_t K, int32_t shared, int act_fmt, int wfmt,
-                   int32_t renormalize, const int64_t *tokens, int64_t n_tokens, int threads,
-                   int32_t *ids_out, float *w_out, uint16_t *out_bits, double *out_f64,
-                   uint16_t *h_bits, double *seconds) {
+                   int32_t renormalize, int32_t round_y, const int64_t *tokens,
+                   int64_t n_tokens, int threads, int32_t *ids_out, float *w_out,
+                   uint16_t *out_bits, double *out_f64, uint16_t *h_bits, double *seconds) {
   const auto t_start = std::chrono::steady_clock::now();
   if (T < 0 || H <= 0 || I <= 0 || H % kBlock || I % kBlock || E < 1 || K < 1 || K > E) return -1;
   if ((shared != 0 && shared != 1) || (shared && !gate)) return -1;
@@ -561,8 +575,9 @@ int oracle_forward(const uint16_t *x_bits, const float *logits, const float *gat
     if (act_fmt == ORACLE_ACT_MXFP4) mxfp4_roundtrip_row(row, H);
   });
 
-  // 4. every expert on its selected rows; y (bf16-rounded) per (token, slot)
-  std::vector<float> y(n * Kp * H);
+  // 4. every expert on its selected rows; y per (token, slot), rounded to
+  //    bf16 when round_y (where a path stores y in bf16 before the combine)
+  std::vector<double> y(n * Kp * H);
   std::vector<double> a_e, y_e, h_e;
   for (int32_t e = 0; e < Ep; ++e) {
     std::vector<int32_t> rows;                 // sorted positions of the expert's selected rows
@@ -582,8 +597,8 @@ int oracle_forward(const uint16_t *x_bits, const float *logits, const float *gat
     pool.for_each(R, [&](int64_t r) {
       const int32_t flat = sorted_ids[rows[r]];
       const int64_t j = sel[flat / Kp], k = flat % Kp;
-      float *dst = &y[(j * Kp + k) * H];
-      for (int64_t c = 0; c < H; ++c) dst[c] = static_cast<float>(round_bf16(y_e[r * H + c]));
+      double *dst = &y[(j * Kp + k) * H];
+      for (int64_t c = 0; c < H; ++c) dst[c] = round_y ? round_bf16(y_e[r * H + c]) : y_e[r * H + c];
       if (h_bits)
         for (int64_t i = 0; i < I; ++i) h_bits[static_cast<int64_t>(rows[r]) * I + i] = bf16_bits(h_e[r * I + i]);
     });
@@ -595,7 +610,7 @@ int oracle_forward(const uint16_t *x_bits, const float *logits, const float *gat
     for (int64_t c = 0; c < H; ++c) {
       double acc = 0.0;
       for (int32_t k = 0; k < Kp; ++k)
-        acc += static_cast<double>(w[t * Kp + k]) * static_cast<double>(y[(j * Kp + k) * H + c]);
+        acc += static_cast<double>(w[t * Kp + k]) * y[(j * Kp + k) * H + c];
       if (out_f64) out_f64[j * H + c] = acc;
       if (out_bits) out_bits[j * H + c] = bf16_bits(acc);
     }
@@ -605,6 +620,50 @@ int oracle_forward(const uint16_t *x_bits, const float *logits, const float *gat
   if (w_out) std::copy(w.begin(), w.end(), w_out);
   if (seconds)
     *seconds = std::chrono::duration<double>(std::chrono::steady_clock::now() - t_start).count();
+  return 0;
+}
+
+int oracle_forward_from_h(const uint16_t *h_bits, const float *logits, const float *gate,
+                          const uint8_t *const *w2, const uint8_t *const *w2s, int64_t T,
+                          int64_t H, int64_t I, int32_t E, int32_t K, int32_t shared, int act_fmt,
+                          int wfmt, int32_t renormalize, int32_t round_y, int threads,
+                          uint16_t *out_bits, double *out_f64) {
+  if (T < 0 || H <= 0 || I <= 0 || H % kBlock || I % kBlock || E < 1 || K < 1 || K > E) return -1;
+  if ((shared != 0 && shared != 1) || (shared && !gate)) return -1;
+  if (wfmt == ORACLE_W_MXFP8 && act_fmt != ORACLE_ACT_BF16) return -1;
+  if (T > 0 && (!h_bits || !logits || !w2 || !w2s)) return -1;
+  const int32_t Kp = K + shared, Ep = E + shared;
+  const int64_t A = T * Kp;
+  std::vector<int32_t> ids(A), counts(Ep), offsets(Ep + 1), sorted_ids(A), inv(A);
+  std::vector<float> w(A);
+  route(logits, gate, T, E, K, shared, renormalize, ids.data(), w.data());
+  align(ids.data(), A, Ep, 32, counts.data(), offsets.data(), sorted_ids.data(), inv.data(), nullptr);
+  for (int32_t e = 0; e < Ep; ++e)
+    if (counts[e] > 0 && (!w2[e] || !w2s[e])) return -2;
+  Pool pool(resolve_threads(threads));
+  std::vector<double> y(A * H);                // per flat assignment
+  std::vector<double> h_e, y_e;
+  for (int32_t e = 0; e < Ep; ++e) {
+    const int64_t R = counts[e], p0 = offsets[e];
+    if (R == 0) continue;
+    h_e.resize(R * I);
+    y_e.resize(R * H);
+    for (int64_t i = 0; i < R * I; ++i) h_e[i] = bf16_value(h_bits[p0 * I + i]);
+    expert_down(h_e.data(), R, H, I, w2[e], w2s[e], act_fmt, wfmt, y_e.data(), pool);
+    pool.for_each(R, [&](int64_t r) {
+      double *dst = &y[static_cast<int64_t>(sorted_ids[p0 + r]) * H];
+      for (int64_t c = 0; c < H; ++c) dst[c] = round_y ? round_bf16(y_e[r * H + c]) : y_e[r * H + c];
+    });
+  }
+  pool.for_each(T, [&](int64_t t) {
+    for (int64_t c = 0; c < H; ++c) {
+      double acc = 0.0;
+      for (int32_t k = 0; k < Kp; ++k)
+        acc += static_cast<double>(w[t * Kp + k]) * y[(t * Kp + k) * H + c];
+      if (out_f64) out_f64[t * H + c] = acc;
+      if (out_bits) out_bits[t * H + c] = bf16_bits(acc);
+    }
+  });
   return 0;
 }
 

@@ -23,8 +23,8 @@
  *           over exactly decoded MXFP4 (or MXFP8) weights, fp64 dot
  *           products (VibeSys post, section "Baseline": MXFP4 weights
  *           dequantised inside the MoE kernel; the SwiGLU expert MLP)
- *   forward out[t] = bf16( sum_k w[t,k] * bf16(MLP_{ids[t,k]}(x_t)) ), slots
- *           summed in order.  For W4A4 the activations and h go through
+ *   forward out[t] = bf16( sum_k w[t,k] * MLP_{ids[t,k]}(x_t) ), slots summed
+ *           in order (optionally each MLP output rounded to bf16 first).  For W4A4 the activations and h go through
  *           MXFP4 quantise-then-decode before their GEMM (OpenRelay "Gemma 4
  *           31B on MI355X" post, sections "Optimisation 3" and
  *           "Optimisation 4": activation + MXFP4 quantisation fused).
@@ -137,19 +137,34 @@ int oracle_expert_mlp(const double *a, int64_t n, int64_t H, int64_t I, const ui
  *     oracle_expert_mlp; an expert no selected token uses may be NULL
  *   tokens: n_tokens token indices whose outputs are computed (NULL: all T;
  *     routing and grouping always cover every token)
+ *   round_y: 1 rounds each slot's expert output y to bf16 before the
+ *     combine (a path that stores y in bf16 between the down GEMM and the
+ *     combine), 0 keeps it (a path whose combine adds the unrounded products)
  * Outputs (any may be NULL): ids int32 [T, K'], w float [T, K'];
  *   out_bits bf16 [n, H] and out_f64 [n, H] (the fp64 sum before its
  *   rounding), n = n_tokens or T; h_bits bf16 [T*K', I]: each assignment's
  *   h, rows in the grouping's sorted order (only with tokens = NULL).
- * Each slot's expert output y is rounded to bf16 before the combine.
  * seconds (may be NULL) receives the wall time of the call. */
 int oracle_forward(const uint16_t *x_bits, const float *logits, const float *gate,
                    const uint8_t *const *w13, const uint8_t *const *w13s,
                    const uint8_t *const *w2, const uint8_t *const *w2s, int64_t T, int64_t H,
                    int64_t I, int32_t E, int32_t K, int32_t shared, int act_fmt, int wfmt,
-                   int32_t renormalize, const int64_t *tokens, int64_t n_tokens, int threads,
-                   int32_t *ids, float *w, uint16_t *out_bits, double *out_f64, uint16_t *h_bits,
-                   double *seconds);
+                   int32_t renormalize, int32_t round_y, const int64_t *tokens, int64_t n_tokens,
+                   int threads, int32_t *ids, float *w, uint16_t *out_bits, double *out_f64,
+                   uint16_t *h_bits, double *seconds);
+
+/* The layer from a given h onward: routing and grouping as oracle_forward,
+ * then each assignment's down projection of h_bits [T*K', I] (bf16, rows in
+ * the grouping's sorted order; for W4A4 quantised to MXFP4 and decoded
+ * first) and the combine.  Only the W2 arrays are read.  Tests use it to
+ * take the h-dependent steps on the h a GPU produced, so that a rounding
+ * decision taken differently on the two sides upstream does not propagate.
+ * out_bits / out_f64 [T, H] as in oracle_forward (either may be NULL). */
+int oracle_forward_from_h(const uint16_t *h_bits, const float *logits, const float *gate,
+                          const uint8_t *const *w2, const uint8_t *const *w2s, int64_t T,
+                          int64_t H, int64_t I, int32_t E, int32_t K, int32_t shared, int act_fmt,
+                          int wfmt, int32_t renormalize, int32_t round_y, int threads,
+                          uint16_t *out_bits, double *out_f64);
 
 /* The thread count `threads` <= 0 resolves to. */
 int oracle_default_threads(void);

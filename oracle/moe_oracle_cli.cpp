@@ -3,9 +3,11 @@
 // Reads the layer's inputs from raw little-endian files, runs oracle_forward
 // on all tokens, writes the bf16 output and prints one JSON line with the
 // wall time, tokens/s, fp64 GFLOP/s of the expert MLPs, threads and CPU.
+// --round-y 1 rounds each slot's expert output to bf16 before the combine
+// (default 0: unrounded, as the GPU path).
 //
 //   moe_oracle --T 64 --H 4096 --I 1024 --E 512 --K 10 --shared 1
-//              [--act bf16|mxfp4] [--wfmt mxfp4|mxfp8] [--threads N]
+//              [--act bf16|mxfp4] [--wfmt mxfp4|mxfp8] [--threads N] [--round-y 1|0]
 //              --x x.bin --logits logits.bin [--gate gate.bin]
 //              --w13 w13.bin --w13s w13s.bin --w2 w2.bin --w2s w2s.bin
 //              [--out out.bin]
@@ -74,6 +76,7 @@ int main(int argc, char **argv) {
   const int act = arg.count("act") && arg["act"] == "mxfp4" ? ORACLE_ACT_MXFP4 : ORACLE_ACT_BF16;
   const int wfmt = arg.count("wfmt") && arg["wfmt"] == "mxfp8" ? ORACLE_W_MXFP8 : ORACLE_W_MXFP4;
   const int threads = arg.count("threads") ? std::atoi(arg["threads"].c_str()) : 0;
+  const int round_y = arg.count("round-y") ? std::atoi(arg["round-y"].c_str()) : 0;
   if (T < 1 || H < 32 || I < 32 || E < 1 || K < 1 || K > E || (shared != 0 && shared != 1))
     die("bad shape");
   const int64_t Ep = E + shared, Kp = K + shared;
@@ -100,7 +103,8 @@ int main(int argc, char **argv) {
   const int rc = oracle_forward(
       reinterpret_cast<const uint16_t *>(x.data()), reinterpret_cast<const float *>(logits.data()),
       shared ? reinterpret_cast<const float *>(gate.data()) : nullptr, p13.data(), p13s.data(),
-      p2.data(), p2s.data(), T, H, I, E, K, shared, act, wfmt, 1, nullptr, 0, threads, nullptr,
+      p2.data(), p2s.data(), T, H, I, E, K, shared, act, wfmt, 1, round_y, nullptr, 0, threads,
+      nullptr,
       nullptr, out.data(), nullptr, nullptr, &seconds);
   if (rc != 0) die("oracle_forward failed with " + std::to_string(rc));
   if (arg.count("out")) {

@@ -41,9 +41,14 @@ def e2m1_value(code: int) -> float:
     return lib().oracle_e2m1_value(int(code))
 
 
-E2M1 = np.array([e2m1_value(c) for c in range(16)], dtype=np.float64)
-# magnitudes of codes 0..7, ascending
-GRID = E2M1[:8].copy()
+def __getattr__(name):
+    """E2M1 (the 16 code values) and GRID (magnitudes of codes 0..7,
+    ascending), built from the C++ oracle on first use."""
+    if name == "E2M1":
+        return np.array([e2m1_value(c) for c in range(16)], dtype=np.float64)
+    if name == "GRID":
+        return np.array([e2m1_value(c) for c in range(8)], dtype=np.float64)
+    raise AttributeError(name)
 
 
 def e8m0_value(b):

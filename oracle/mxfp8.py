@@ -39,9 +39,15 @@ def e4m3_value(code: int) -> float:
     return lib().oracle_e4m3_value(int(code))
 
 
-E4M3 = np.array([e4m3_value(c) for c in range(256)], dtype=np.float64)
-# magnitudes of the finite non-negative codes 0..126, ascending with the code
-GRID = E4M3[:NAN_CODE].copy()
+def __getattr__(name):
+    """E4M3 (the 256 code values) and GRID (magnitudes of the finite
+    non-negative codes 0..126, ascending with the code), built from the C++
+    oracle on first use."""
+    if name == "E4M3":
+        return np.array([e4m3_value(c) for c in range(256)], dtype=np.float64)
+    if name == "GRID":
+        return np.array([e4m3_value(c) for c in range(NAN_CODE)], dtype=np.float64)
+    raise AttributeError(name)
 
 
 def decode(codes: np.ndarray, scales: np.ndarray) -> np.ndarray:

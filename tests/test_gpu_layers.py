@@ -9,14 +9,15 @@ input); the multi-layer call must equal the chain of single-layer router
 calls bit for bit, with and without the cache prefetch, and every graph
 replay must equal the eager result.
 
-Tolerance of a layer against the oracle: relative L2 as for one layer; the
-max-abs bound is taken per element against max(|want|, RMS(want)).  Both
-sides round y and out to bf16 at the same points, so they differ by rare
-one-ulp rounding flips, and a flip is proportional to the element it hits.
-A layer fed by another layer (no residual or norm in between) gives
-heavy-tailed outputs (max/RMS 6-9 by the third layer, against ~4 for
-N(0,1) inputs), where one flip at the largest element alone is 2.5-3.5% of
-the RMS."""
+Tolerance of a layer against the oracle: relative L2 as for one layer.
+Layer 0 (fed the N(0,1) activations) keeps the layer's max-abs bound,
+2e-2 x RMS of the oracle's output.  For later layers the max-abs bound is
+taken per element against max(|want|, RMS(want)): both sides round y and
+out to bf16 at the same points, so they differ by rare one-ulp rounding
+flips, and a flip is proportional to the element it hits.  A layer fed by
+another layer (no residual or norm in between) gives heavy-tailed outputs
+(max/RMS 6-9 by the third layer, against ~4 for N(0,1) inputs), where one
+flip at the largest element alone is 2.5-3.5% of the RMS."""
 import sys
 
 import numpy as np
@@ -25,7 +26,8 @@ import torch
 
 import synth
 from oracle import moe, mxfp4
-from tests.helpers import DEV, MAX_ABS_RMS, REL_L2, W_ATOL, bits, rel_l2
+from tests.helpers import (DEV, MAX_ABS_RMS, REL_L2, W_ATOL, bf16_ulp, bits, max_abs_over_rms,
+                           oracle_pack, oracle_pack_all, rel_l2)
 
 pytestmark = pytest.mark.gpu
 
@@ -40,12 +42,16 @@ def ops():
     return o
 
 
-def max_abs_elementwise(got_bits, want_bits) -> float:
-    """max_j |got_j - want_j| / max(|want_j|, RMS(want))."""
+def max_abs_elementwise(got_bits, want) -> float:
+    """max_j (|got_j - want_f64_j| - ulp(got_j) / 2) / max(|want_j|, RMS(want)):
+    as the layer's max-abs measure (beyond the output's own rounding), taken
+    per element against the element's own size."""
     g = mxfp4.bf16_to_f64(got_bits)
-    w = mxfp4.bf16_to_f64(want_bits)
+    w = mxfp4.bf16_to_f64(want["out"])
+    f = np.asarray(want["out_f64"], dtype=np.float64)
     rms = float(np.sqrt(np.mean(w * w)))
-    return float(np.max(np.abs(g - w) / np.maximum(np.abs(w), max(rms, 1e-300))))
+    err = np.maximum(np.abs(g - f) - 0.5 * bf16_ulp(g), 0.0)
+    return float(np.max(err / np.maximum(np.abs(w), max(rms, 1e-300))))
 
 
 class Layers:
@@ -71,15 +77,9 @@ class Layers:
                 ops().quantize_weights(synth.expert_w2(lc, e, DEV), w2[e], w2s[e])
             self.w.append((synth.router_weight(lc).to(DEV), w13, w13s, w2, w2s))
         torch.cuda.synchronize()
-        self._ow = {}
 
     def oracle_weights(self, l, e):
-        if (l, e) not in self._ow:
-            lc = synth.layer_config(self.cfg, l)
-            a = mxfp4.quantize(synth.expert_w13(lc, e, DEV).cpu().numpy())
-            b = mxfp4.quantize(synth.expert_w2(lc, e, DEV).cpu().numpy())
-            self._ow[(l, e)] = (a[0], a[1], b[0], b[1])
-        return self._ow[(l, e)]
+        return oracle_pack(synth.layer_config(self.cfg, l), e)
 
     def multi(self, prefetch, **kw):
         c = self.cfg
@@ -103,9 +103,25 @@ class Layers:
         """Layer l by the oracle on the GPU's input and fp32 logits of that layer."""
         c = self.cfg
         lg = logits.cpu().numpy()
-        return moe.forward(bits(x_in), lg[:, :c.E], lg[:, c.E] if c.shared else None,
+        gate = lg[:, c.E] if c.shared else None
+        ids, _ = moe.route(lg[:, :c.E], gate, c.K, c.shared)
+        oracle_pack_all(synth.layer_config(c, l), np.unique(ids if tokens is None else ids[tokens]))
+        return moe.forward(bits(x_in), lg[:, :c.E], gate,
                            lambda e: self.oracle_weights(l, e), c.I, c.E, c.K, c.shared,
                            c.act_fmt, tokens=tokens)
+
+
+def check_layer(l, got_bits, want, act_fmt):
+    """Layer 0 against the layer's bounds; later layers with the max-abs bound
+    per element (see the module's docstring)."""
+    e_rel = rel_l2(got_bits, want["out"])
+    if l == 0:
+        e_max = max_abs_over_rms(got_bits, want)
+        _say(f"  layer {l}: rel_l2 {e_rel:.2e}  max_abs/rms {e_max:.2e}")
+    else:
+        e_max = max_abs_elementwise(got_bits, want)
+        _say(f"  layer {l}: rel_l2 {e_rel:.2e}  max_abs (per element) {e_max:.2e}")
+    assert e_rel <= REL_L2[act_fmt] and e_max <= MAX_ABS_RMS
 
 
 SMALL = {
@@ -129,10 +145,7 @@ def test_layers_match_chain_and_oracle(name):
         assert np.array_equal(bits(out), bits(steps[-1][2])), prefetch
     for l, (x_in, lg, out) in enumerate(steps):
         want = P.oracle_layer(l, x_in, lg)
-        e_rel = rel_l2(bits(out), want["out"])
-        e_max = max_abs_elementwise(bits(out), want["out"])
-        _say(f"  layer {l}: rel_l2 {e_rel:.2e}  max_abs (per element) {e_max:.2e}")
-        assert e_rel <= REL_L2[c.act_fmt] and e_max <= MAX_ABS_RMS
+        check_layer(l, bits(out), want, c.act_fmt)
     assert not np.array_equal(bits(steps[0][2]), bits(steps[1][2]))   # the layers differ
 
 
@@ -160,10 +173,11 @@ def test_layers_graph_replays_equal_eager():
         assert torch.equal(out, eager), i
 
 
-def test_layers_full_decode_sampled():
+@pytest.mark.timeout(600)
+def test_layers_full_decode():
     """Two layers of the decode workload's shapes in the configuration the
     bench times: equal to the chained calls bit for bit (with the prefetch),
-    and the last layer's sampled tokens against the oracle."""
+    and every token of both layers against the oracle."""
     cfg = synth.CONFIGS["decode"]
     _say("layers full decode", cfg.T, cfg.H, cfg.I, cfg.E, cfg.K)
     P = Layers(cfg, 2)
@@ -172,11 +186,6 @@ def test_layers_full_decode_sampled():
     torch.cuda.synchronize()
     assert np.array_equal(bits(out), bits(steps[-1][2]))
     _say("  chain == multi-layer call")
-    x_in, lg, last = steps[-1]
-    tokens = np.sort(np.random.default_rng(cfg.seed_act).choice(cfg.T, size=2, replace=False))
-    want = P.oracle_layer(1, x_in, lg, tokens=tokens)
-    got = bits(last)[tokens]
-    e_rel = rel_l2(got, want["out"])
-    e_max = max_abs_elementwise(got, want["out"])
-    _say(f"  last layer: rel_l2 {e_rel:.2e}  max_abs (per element) {e_max:.2e}")
-    assert e_rel <= REL_L2[cfg.act_fmt] and e_max <= MAX_ABS_RMS
+    for l, (x_in, lg, got) in enumerate(steps):
+        want = P.oracle_layer(l, x_in, lg)
+        check_layer(l, bits(got), want, cfg.act_fmt)

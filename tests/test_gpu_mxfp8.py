@@ -5,7 +5,6 @@ and the grouping tables.  Within tolerance, as for W4A16 (the arithmetic is
 the same: exact dequantised weights times bf16 activations, fp32 sums, h
 and y rounded to bf16): routing weights 1e-6, layer output relative L2 <=
 5e-3 and max abs <= 2e-2 x RMS of the oracle output."""
-import functools
 import sys
 
 import numpy as np
@@ -15,7 +14,7 @@ import torch
 import synth
 from oracle import moe, mxfp4, mxfp8
 from tests.helpers import (DEV, MAX_ABS_RMS, REL_L2, W_ATOL, bits, max_abs_over_rms, native_order,
-                           rel_l2)
+                           oracle_pack, oracle_pack_all, rel_l2)
 
 pytestmark = pytest.mark.gpu
 
@@ -56,19 +55,19 @@ class Problem8:
                                    ops().W_MXFP8)
         torch.cuda.synchronize()
 
-    @functools.lru_cache(maxsize=None)
     def oracle_weights(self, e: int):
-        c = self.cfg
-        a = mxfp8.quantize(synth.expert_w13(c, e, DEV).cpu().numpy())
-        b = mxfp8.quantize(synth.expert_w2(c, e, DEV).cpu().numpy())
-        return a[0], a[1], b[0], b[1]
+        return oracle_pack(self.cfg, e, synth.W_MXFP8)
 
-    def oracle(self, tokens=None):
+    def oracle(self, tokens=None, return_h=False):
         c = self.cfg
-        return moe.forward(bits(self.x_cpu), self.logits_cpu.numpy(),
-                           None if self.gate_cpu is None else self.gate_cpu.numpy(),
-                           self.oracle_weights, c.I, c.E, c.K, c.shared, moe.ACT_BF16,
-                           tokens=tokens, wfmt=moe.W_MXFP8)
+        logits = self.logits_cpu.numpy()
+        gate = None if self.gate_cpu is None else self.gate_cpu.numpy()
+        ids, _ = moe.route(logits, gate, c.K, c.shared)
+        oracle_pack_all(c, np.unique(ids if tokens is None else ids[np.asarray(tokens)]),
+                        synth.W_MXFP8)
+        return moe.forward(bits(self.x_cpu), logits, gate, self.oracle_weights, c.I, c.E, c.K,
+                           c.shared, moe.ACT_BF16, tokens=tokens, wfmt=moe.W_MXFP8,
+                           return_h=return_h)
 
     def forward(self, **kw):
         c = self.cfg
@@ -165,7 +164,7 @@ def test_mxfp8_layer_small(name):
     assert np.max(np.abs(r["w"].cpu().numpy() - want["w"])) <= W_ATOL
     assert np.array_equal(r["align"]["sorted"].cpu().numpy(), want["sorted"])
     e_rel = rel_l2(bits(out), want["out"])
-    e_max = max_abs_over_rms(bits(out), want["out"])
+    e_max = max_abs_over_rms(bits(out), want)
     _say(f"  {name}: rel_l2 {e_rel:.2e}  max_abs/rms {e_max:.2e}")
     assert e_rel <= TOL
     assert e_max <= MAX_ABS_RMS
@@ -182,53 +181,38 @@ def test_mxfp8_layer_empty_batch():
     assert out.shape == (0, cfg.H)
 
 
-def test_mxfp8_layer_full_size_decode_sampled():
-    """The decode workload's shapes (T=64, H=4096, I=1024, E=512, top-10 +
-    shared) with MXFP8 weights, in the launch configuration the bench times:
-    routing bit-exact for every token, sampled tokens against the oracle."""
-    cfg = synth.CONFIGS["decode"]
-    _say("mxfp8 full decode", cfg.T, cfg.H, cfg.I, cfg.E, cfg.K)
-    prob = Problem8(cfg)
-    ids = torch.empty(cfg.T, cfg.Kp, dtype=torch.int32, device=DEV)
-    w = torch.empty(cfg.T, cfg.Kp, dtype=torch.float32, device=DEV)
-    out = prob.forward(topk_ids=ids, topk_weights=w)
-    torch.cuda.synchronize()
-    _say("  forward done")
-    tokens = np.sort(np.random.default_rng(cfg.seed_act).choice(cfg.T, size=2, replace=False))
-    want = prob.oracle(tokens=tokens)
-    _say("  oracle done for tokens", tokens.tolist())
-    assert np.array_equal(ids.cpu().numpy(), want["ids"])
-    assert np.max(np.abs(w.cpu().numpy() - want["w"])) <= W_ATOL
-    got = bits(out)[tokens]
-    e_rel = rel_l2(got, want["out"])
-    e_max = max_abs_over_rms(got, want["out"])
-    _say(f"  decode mxfp8: rel_l2 {e_rel:.2e}  max_abs/rms {e_max:.2e}")
-    assert e_rel <= TOL and e_max <= MAX_ABS_RMS
-    assert torch.isfinite(out.float()).all()
-
-
-def test_mxfp8_layer_full_size_prefill_sampled():
-    """The MXFP8 prefill workload (T=1536, 64-row LDS-tiled kernels) in the
-    launch configuration the bench times: routing bit-exact for every token,
-    sampled tokens against the oracle."""
-    cfg = synth.CONFIGS["prefill_mxfp8"]
-    _say("mxfp8 full prefill", cfg.T, "tile_m",
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("name", ["decode_mxfp8", "prefill_mxfp8"])
+def test_mxfp8_layer_full_size(name):
+    """The MXFP8 workloads (T = 64 on the weight-streaming kernels, T = 1536 on
+    the 64-row LDS-tiled ones) in the launch configuration the bench times:
+    routing and grouping bit-exact, h of every sorted row and every token's
+    output against the oracle."""
+    cfg = synth.CONFIGS[name]
+    _say("mxfp8 full", name, cfg.T, "tile_m",
          ops().mxfp8_gemm_tile_m(cfg.T, cfg.Kp, cfg.Ep, cfg.H, cfg.I))
     prob = Problem8(cfg)
     ids = torch.empty(cfg.T, cfg.Kp, dtype=torch.int32, device=DEV)
     w = torch.empty(cfg.T, cfg.Kp, dtype=torch.float32, device=DEV)
     out = prob.forward(topk_ids=ids, topk_weights=w)
+    r = prob.stages()
     torch.cuda.synchronize()
-    _say("  forward done")
-    tokens = np.sort(np.random.default_rng(cfg.seed_act).choice(cfg.T, size=2, replace=False))
-    want = prob.oracle(tokens=tokens)
-    _say("  oracle done for tokens", tokens.tolist())
+    assert torch.equal(out, r["out"])
+    _say("  GPU done")
+    want = prob.oracle(return_h=True)
+    _say(f"  oracle done ({want['seconds']:.1f} s)")
     assert np.array_equal(ids.cpu().numpy(), want["ids"])
     assert np.max(np.abs(w.cpu().numpy() - want["w"])) <= W_ATOL
-    got = bits(out)[tokens]
+    assert np.array_equal(r["align"]["sorted"].cpu().numpy(), want["sorted"])
+    hg, hw = bits(r["h"]), want["h"]
+    h_rel = rel_l2(hg, hw)
+    h_same = float(np.mean(hg == hw))
+    _say(f"  h rel_l2 {h_rel:.2e}, bit-identical {h_same:.5f}")
+    assert h_rel <= 2e-3 and h_same >= 0.99
+    got = bits(out)
     e_rel = rel_l2(got, want["out"])
-    e_max = max_abs_over_rms(got, want["out"])
-    _say(f"  prefill mxfp8: rel_l2 {e_rel:.2e}  max_abs/rms {e_max:.2e}")
+    e_max = max_abs_over_rms(got, want)
+    _say(f"  {name}: all {cfg.T} tokens: rel_l2 {e_rel:.2e}  max_abs/rms {e_max:.2e}")
     assert e_rel <= TOL and e_max <= MAX_ABS_RMS
     assert torch.isfinite(out.float()).all()
 
@@ -248,6 +232,6 @@ def test_mxfp8_gemm_kernels_for_every_tile_size(tile_m):
     torch.cuda.synchronize()
     want = prob.oracle()
     e_rel = rel_l2(bits(out), want["out"])
-    e_max = max_abs_over_rms(bits(out), want["out"])
+    e_max = max_abs_over_rms(bits(out), want)
     _say(f"  tile_m {tile_m}: rel_l2 {e_rel:.2e}  max_abs/rms {e_max:.2e}")
     assert e_rel <= TOL and e_max <= MAX_ABS_RMS

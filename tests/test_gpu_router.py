@@ -98,7 +98,8 @@ def test_forward_router_equals_forward_on_its_logits(name):
     GEMM produced (bit for bit: the same kernels after routing), and matches
     the oracle's layer on those logits."""
     from mxfp4_routed_expert_top_amd import ops
-    from tests.helpers import MAX_ABS_RMS, REL_L2, Problem, max_abs_over_rms, rel_l2
+    from tests.helpers import (MAX_ABS_RMS, REL_L2, Problem, max_abs_over_rms, oracle_pack_all,
+                               rel_l2)
     cfg = {"tiny": synth.CONFIGS["tiny"],
            "tiled128": synth.custom_config("r_tiled128", T=300, H=512, I=256, E=16, K=3, shared=1),
            "w4a4_small": synth.custom_config("r_w4a4", T=40, H=256, I=128, E=16, K=3, shared=1,
@@ -118,13 +119,13 @@ def test_forward_router_equals_forward_on_its_logits(name):
     torch.cuda.synchronize()
     assert torch.equal(out_r, out_l)
     l32 = logits.cpu().numpy()
-    # the oracle packs every expert a token touches: a few tokens of the big shapes
-    tokens = np.arange(cfg.T) if cfg.T <= 16 else np.sort(np.random.default_rng(1).choice(cfg.T, 3, replace=False))
-    _say("  GPU done; oracle on tokens", tokens.tolist())
-    want = moe.forward(bits(prob.x_cpu), l32[:, :cfg.E], l32[:, cfg.E] if cfg.shared else None,
-                       prob.oracle_weights, cfg.I, cfg.E, cfg.K, cfg.shared, cfg.act_fmt,
-                       tokens=tokens)
-    got = bits(out_r.cpu())[tokens]
-    e_rel, e_max = rel_l2(got, want["out"]), max_abs_over_rms(got, want["out"])
+    gate_np = l32[:, cfg.E] if cfg.shared else None
+    _say("  GPU done; oracle on every token")
+    ids_np, _ = moe.route(l32[:, :cfg.E], gate_np, cfg.K, cfg.shared)
+    oracle_pack_all(cfg, np.unique(ids_np))
+    want = moe.forward(bits(prob.x_cpu), l32[:, :cfg.E], gate_np, prob.oracle_weights, cfg.I,
+                       cfg.E, cfg.K, cfg.shared, cfg.act_fmt)
+    got = bits(out_r.cpu())
+    e_rel, e_max = rel_l2(got, want["out"]), max_abs_over_rms(got, want)
     _say(f"  {name}: rel_l2 {e_rel:.2e}  max_abs/rms {e_max:.2e}")
     assert e_rel <= REL_L2[cfg.act_fmt] and e_max <= MAX_ABS_RMS

@@ -23,7 +23,7 @@ import torch
 import synth
 from oracle import moe
 from tests.helpers import (DEV, MAX_ABS_RMS, REL_L2, W_ATOL, Problem, bits, max_abs_over_rms,
-                           rel_l2)
+                           oracle_pack_all, rel_l2)
 
 pytestmark = pytest.mark.gpu
 
@@ -74,9 +74,8 @@ def test_tensor_parallel_shards_sum_to_the_layer(name):
     c = cfg
     full = prob.stages()
     torch.cuda.synchronize()
-    big = c.T <= 64 and c.H >= 4096
-    tokens = (np.sort(np.random.default_rng(c.seed_act).choice(c.T, size=2, replace=False))
-              if big else None)
+    tokens = None                      # every token against the oracle
+    oracle_pack_all(c, np.unique(full["ids"].cpu().numpy()))
     acc = torch.zeros(c.T, c.H, dtype=torch.float32, device=DEV)
     for g in range(G):
         w13, w13s, w2, w2s, Ig = _shard(prob, g, G)
@@ -100,7 +99,7 @@ def test_tensor_parallel_shards_sum_to_the_layer(name):
                                None if prob.gate_cpu is None else prob.gate_cpu.numpy(), wsh,
                                Ig, c.E, c.K, c.shared, c.act_fmt, tokens=tokens)
             got = bits(r["out"]) if tokens is None else bits(r["out"])[tokens]
-            e_rel, e_max = rel_l2(got, want["out"]), max_abs_over_rms(got, want["out"])
+            e_rel, e_max = rel_l2(got, want["out"]), max_abs_over_rms(got, want)
             _say(f"  shard {g}: vs the oracle on its slices: rel_l2 {e_rel:.2e}  max_abs/rms {e_max:.2e}")
             assert e_rel <= REL_L2[c.act_fmt] and e_max <= MAX_ABS_RMS
     got, ref = bits(acc.to(torch.bfloat16)), bits(full["out"])

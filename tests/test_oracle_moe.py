@@ -116,10 +116,13 @@ def _decode_by_table(packed, scales):
 
 
 def test_one_expert_reduces_to_dense_swiglu_mlp():
+    """With y kept (the default) out_f64 is the dense MLP's output; with
+    round_y each output is that value rounded to bf16."""
     cfg = synth.custom_config(T=3, H=64, I=32, E=1, K=1, shared=0)
     W = _make_weights(cfg)
     x, l, _ = _inputs(cfg)
     res = moe.forward(x, l, None, W, cfg.I, cfg.E, cfg.K, 0)
+    res_r = moe.forward(x, l, None, W, cfg.I, cfg.E, cfg.K, 0, round_y=True)
     w13, w13s, w2, w2s = W(0)
     A = _decode_by_table(w13, w13s)        # [2I][H]
     B = _decode_by_table(w2, w2s)          # [H][I]
@@ -131,8 +134,10 @@ def test_one_expert_reduces_to_dense_swiglu_mlp():
             u = sum(A[cfg.I + i][k] * xv[t, k] for k in range(cfg.H))
             h.append(float(mxfp4.round_bf16(g / (1 + math.exp(-g)) * u)))
         for j in range(cfg.H):
-            y = float(mxfp4.round_bf16(sum(B[j][i] * h[i] for i in range(cfg.I))))
+            y = sum(B[j][i] * h[i] for i in range(cfg.I))
             assert abs(res["out_f64"][t, j] - y) <= 1e-12 * max(1.0, abs(y))
+            yr = float(mxfp4.round_bf16(y))
+            assert abs(res_r["out_f64"][t, j] - yr) <= 1e-12 * max(1.0, abs(yr))
     assert np.all(res["w"] == 1.0)
 
 
@@ -166,7 +171,7 @@ def test_one_expert_mxfp8_reduces_to_dense_swiglu_mlp():
             u = sum(A[cfg.I + i][k] * xv[t, k] for k in range(cfg.H))
             h.append(float(mxfp4.round_bf16(g / (1 + math.exp(-g)) * u)))
         for j in range(cfg.H):
-            y = float(mxfp4.round_bf16(sum(B[j][i] * h[i] for i in range(cfg.I))))
+            y = sum(B[j][i] * h[i] for i in range(cfg.I))
             assert abs(res["out_f64"][t, j] - y) <= 1e-12 * max(1.0, abs(y))
 
 
@@ -196,13 +201,15 @@ def test_shared_expert_fusion_equals_separate_dense_mlp():
     cfg = synth.custom_config(T=24, H=128, I=64, E=8, K=3, shared=1)
     W = _make_weights(cfg)
     x, l, g = _inputs(cfg)
-    fused = moe.forward(x, l, g, W, cfg.I, cfg.E, cfg.K, 1)
-    routed = moe.forward(x, l, None, W, cfg.I, cfg.E, cfg.K, 0)
-    dense = mxfp4.round_bf16(moe.expert_mlp(mxfp4.bf16_to_f64(x), *W(cfg.E), cfg.I, moe.ACT_BF16))
     sig = (1 / (1 + np.exp(-g.astype(np.float64)))).astype(np.float32).astype(np.float64)
-    want = routed["out_f64"] + sig[:, None] * dense
-    assert np.allclose(fused["out_f64"], want, rtol=1e-12, atol=1e-15)
-    assert np.all(fused["ids"][:, cfg.K] == cfg.E)
+    dense = moe.expert_mlp(mxfp4.bf16_to_f64(x), *W(cfg.E), cfg.I, moe.ACT_BF16)
+    for round_y in (False, True):
+        fused = moe.forward(x, l, g, W, cfg.I, cfg.E, cfg.K, 1, round_y=round_y)
+        routed = moe.forward(x, l, None, W, cfg.I, cfg.E, cfg.K, 0, round_y=round_y)
+        d = mxfp4.round_bf16(dense) if round_y else dense
+        want = routed["out_f64"] + sig[:, None] * d
+        assert np.allclose(fused["out_f64"], want, rtol=1e-12, atol=1e-15)
+        assert np.all(fused["ids"][:, cfg.K] == cfg.E)
 
 
 def test_down_scale_linearity():
@@ -287,3 +294,20 @@ def test_router_logits_triple_loop():
             for h in range(40):
                 acc += float(x[t, h]) * float(w[e, h])
             assert got[t, e] == acc
+
+
+def test_forward_from_h_continues_forward():
+    """The layer from h onward, fed the oracle's own h, is the forward bit for
+    bit (W4A16 and W4A4, y kept or rounded)."""
+    for act in (moe.ACT_BF16, moe.ACT_MXFP4):
+        cfg = synth.custom_config(T=20, H=128, I=64, E=8, K=3, shared=1, act_fmt=act,
+                                  outlier_p=0.02 if act else 0.0)
+        W = _make_weights(cfg)
+        x, l, g = _inputs(cfg)
+        for round_y in (False, True):
+            full = moe.forward(x, l, g, W, cfg.I, cfg.E, cfg.K, 1, act_fmt=act, return_h=True,
+                               round_y=round_y)
+            rest = moe.forward_from_h(full["h"], l, g, W, cfg.I, cfg.E, cfg.K, 1, act_fmt=act,
+                                      round_y=round_y)
+            assert np.array_equal(rest["out_f64"], full["out_f64"])
+            assert np.array_equal(rest["out"], full["out"])
