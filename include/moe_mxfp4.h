@@ -413,6 +413,34 @@ MOE_API moe_status moe_mxfp4_forward(const uint16_t *x, const float *router_logi
                              void *stream);
 
 /*
+ * moe_mxfp4_forward for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same layer, arguments and results, with no workspace
+ * argument.  The workspace is a library-owned device array of
+ * MOE_NOALLOC_SCRATCH_BYTES per GPU, held until the process ends; its
+ * address on the current device is looked up on the first call on that
+ * device (make that first call outside graph capture).  Nothing is
+ * allocated or freed by any call.
+ *   Limit: the call's workspace (moe_mxfp4_workspace_size) must fit the
+ *   scratch, else WORKSPACE_TOO_SMALL: e.g. T up to 330 at H = 4096,
+ *   I = 1024, E = 512, K' = 11 (about 203 KB of workspace per token there:
+ *   each assignment's bf16 h and fp32 y), enough for decode batches.
+ *   Every call on one GPU uses that GPU's one scratch: calls that overlap
+ *   on one GPU (different streams, or host threads) race; serialise them.
+ *   No part of the scratch needs to start at zero.
+ * Errors: as moe_mxfp4_forward; WORKSPACE_TOO_SMALL beyond the limit;
+ * DEVICE if the scratch's address cannot be looked up.
+ */
+#define MOE_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+MOE_API moe_status moe_mxfp4_forward_noalloc(const uint16_t *x, const float *router_logits,
+                                     const float *shared_gate_logits, const uint8_t *w13,
+                                     const uint8_t *w13_scale, const uint8_t *w2,
+                                     const uint8_t *w2_scale, int32_t T, int32_t H, int32_t I,
+                                     int32_t E, int32_t K, int32_t shared, int32_t act_fmt,
+                                     uint16_t *out, int32_t *topk_ids_out,
+                                     float *topk_weights_out, void *stream);
+
+/*
  * The whole layer routed from x: moe_route_topk_gemm's router GEMM and
  * routing, then everything moe_mxfp4_forward does after its routing.
  *   router_w     bf16 [E + shared, H] (16-byte aligned); row E = the shared

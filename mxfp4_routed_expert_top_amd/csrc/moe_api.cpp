@@ -5,6 +5,8 @@
 
 #include <hip/hip_runtime.h>
 
+#include <mutex>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -420,7 +422,7 @@ moe_status forward_impl(const uint16_t* x, const float* router_logits,
                         int32_t I, int32_t E, int32_t K, int32_t shared, int32_t act_fmt,
                         int wfmt, uint16_t* out, int32_t* topk_ids_out, float* topk_weights_out,
                         void* workspace, size_t workspace_bytes, void* stream,
-                        const Prefetch* pf = nullptr) {
+                        const Prefetch* pf = nullptr, bool check_only = false) {
   moe_status st = router_w ? check_route_shape(T, E, K, shared, 1)
                            : check_route(router_logits, shared_gate_logits, T, E, K, shared, 1);
   if (st != MOE_OK) return st;
@@ -443,7 +445,14 @@ moe_status forward_impl(const uint16_t* x, const float* router_logits,
   const int64_t A = (int64_t)T * Kp;
   if (A * (int64_t)H >= ((int64_t)1 << 40) || A > INT32_MAX / 2) return MOE_ERR_UNSUPPORTED;
   const FwdLayout L = forward_layout(T, H, I, E, K, shared, act_fmt);
+  const int tm = choose_tile_m(A, Ep, H, I, act_fmt, wfmt);
+  const int mt = (int)max_tiles_for(A, Ep, tm);
+  // the 32-row kernels' LDS (weight scales, staged activation rows) must fit
+  if (tm == MOE_TILE_M && (expert_gemm_lds_bytes(H, act_fmt) > kMaxLdsBytes ||
+                           expert_gemm_lds_bytes(I, act_fmt) > kMaxLdsBytes))
+    return MOE_ERR_UNSUPPORTED;
   if (workspace_bytes < L.total) return MOE_ERR_WORKSPACE_TOO_SMALL;
+  if (check_only) return MOE_OK;
   if (!workspace) return MOE_ERR_INVALID_ARGUMENT;
 
   char* ws = (char*)workspace;
@@ -464,12 +473,6 @@ moe_status forward_impl(const uint16_t* x, const float* router_logits,
   float* y = (float*)(ws + L.y);
   float* rpart = (float*)(ws + L.y);                       // router partial sums (same bytes)
   hipStream_t s = as_stream(stream);
-  const int tm = choose_tile_m(A, Ep, H, I, act_fmt, wfmt);
-  const int mt = (int)max_tiles_for(A, Ep, tm);
-  // the 32-row kernels' LDS (weight scales, staged activation rows) must fit
-  if (tm == MOE_TILE_M && (expert_gemm_lds_bytes(H, act_fmt) > kMaxLdsBytes ||
-                           expert_gemm_lds_bytes(I, act_fmt) > kMaxLdsBytes))
-    return MOE_ERR_UNSUPPORTED;
 
   hipError_t e;
   if (router_w) {
@@ -615,6 +618,63 @@ moe_status moe_mxfp4_forward_layers(const uint16_t* x, int32_t L, const moe_mxfp
     if (T == 0) return MOE_OK;
   }
   return MOE_OK;
+}
+
+}  // extern "C"
+
+// ---- the forward for callers that cannot allocate -------------------------
+
+namespace {
+
+// Workspace of moe_mxfp4_forward_noalloc: one copy per GPU the library runs
+// on, held until the process ends.  In host code `scratch` names a host-side
+// stand-in, not device memory: host code uses only the device address
+// hipGetSymbolAddress returns for the current device (noalloc_scratch).
+__device__ __align__(256) uint8_t scratch[MOE_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];        // per device, looked up on its first call
+
+// The current device's address of `scratch` (looked up once per device,
+// with that device current).
+moe_status noalloc_scratch(void** out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return MOE_ERR_DEVICE;
+  if (dev < 0 || dev >= kMaxDevices) return MOE_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> g(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return MOE_ERR_DEVICE;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+moe_status moe_mxfp4_forward_noalloc(const uint16_t* x, const float* router_logits,
+                                     const float* shared_gate_logits, const uint8_t* w13,
+                                     const uint8_t* w13_scale, const uint8_t* w2,
+                                     const uint8_t* w2_scale, int32_t T, int32_t H, int32_t I,
+                                     int32_t E, int32_t K, int32_t shared, int32_t act_fmt,
+                                     uint16_t* out, int32_t* topk_ids_out,
+                                     float* topk_weights_out, void* stream) {
+  // every argument check (and the scratch size) before any HIP call
+  moe_status st = forward_impl(x, router_logits, shared_gate_logits, nullptr, nullptr, w13,
+                               w13_scale, w2, w2_scale, T, H, I, E, K, shared, act_fmt, 0, out,
+                               topk_ids_out, topk_weights_out, nullptr,
+                               MOE_NOALLOC_SCRATCH_BYTES, stream, nullptr, true);
+  if (st != MOE_OK || T == 0) return st;
+  void* ws = nullptr;
+  st = noalloc_scratch(&ws);
+  if (st != MOE_OK) return st;
+  return forward_impl(x, router_logits, shared_gate_logits, nullptr, nullptr, w13, w13_scale, w2,
+                      w2_scale, T, H, I, E, K, shared, act_fmt, 0, out, topk_ids_out,
+                      topk_weights_out, ws, MOE_NOALLOC_SCRATCH_BYTES, stream);
 }
 
 }  // extern "C"

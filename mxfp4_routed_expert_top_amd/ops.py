@@ -62,6 +62,8 @@ _SIGS = {
     "moe_mxfp8_gemm_tile_m": (_I32, [_I32, _I32, _I32, _I32, _I32]),
     "moe_mxfp8_forward": (_I32, [_P, _P, _P, _P, _P, _P, _P, _I32, _I32, _I32, _I32, _I32, _I32,
                                  _P, _P, _P, _P, _SZ, _P]),
+    "moe_mxfp4_forward_noalloc": (_I32, [_P, _P, _P, _P, _P, _P, _P, _I32, _I32, _I32, _I32, _I32,
+                                         _I32, _I32, _P, _P, _P, _P]),
 }
 EXPORTS = tuple(_SIGS)
 
@@ -386,6 +388,26 @@ def mxfp4_forward(x, router_logits, shared_gate_logits, w13, w13_scale, w2, w2_s
         _ptr(w2), _ptr(w2_scale), T, H, I, E, K, shared, act_fmt, _ptr(out), _ptr(topk_ids),
         _ptr(topk_weights), _ptr(workspace), workspace.numel(), _stream(stream)))
     return out
+
+
+def mxfp4_forward_noalloc(x, router_logits, shared_gate_logits, w13, w13_scale, w2, w2_scale,
+                          I: int, E: int, K: int, shared: int, act_fmt: int = ACT_BF16, out=None,
+                          topk_ids=None, topk_weights=None, stream=None):
+    """moe_mxfp4_forward_noalloc: the whole layer with the library's own
+    device scratch instead of a workspace.  x bf16 [T, H] -> out bf16 [T, H]."""
+    _dt(x, torch.bfloat16, "x")
+    _dt(router_logits, torch.float32, "router_logits")
+    T, H = x.shape
+    if out is None:
+        out = torch.empty(T, H, dtype=torch.bfloat16, device=x.device)
+    _check("moe_mxfp4_forward_noalloc", lib().moe_mxfp4_forward_noalloc(
+        _ptr(x), _ptr(router_logits), _ptr(shared_gate_logits), _ptr(w13), _ptr(w13_scale),
+        _ptr(w2), _ptr(w2_scale), T, H, I, E, K, shared, act_fmt, _ptr(out), _ptr(topk_ids),
+        _ptr(topk_weights), _stream(stream)))
+    return out
+
+
+NOALLOC_SCRATCH_BYTES = 64 << 20      # MOE_NOALLOC_SCRATCH_BYTES
 
 
 def mxfp4_forward_router(x, router_w, w13, w13_scale, w2, w2_scale, I: int, E: int, K: int,

@@ -26,7 +26,7 @@ def declared_functions():
 def test_library_loads_and_exports_every_declared_symbol():
     lib = ops.lib()
     names = declared_functions()
-    assert len(names) == 23
+    assert len(names) == 24
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(ops.EXPORTS)
@@ -311,3 +311,18 @@ def test_forward_layers_argument_errors():
     assert call() == INVALID
     arr[1] = ops._Layer(FAKE, FAKE, FAKE, MIS, FAKE)   # a later layer's misaligned W2
     assert call() == INVALID
+
+
+def test_forward_noalloc_argument_errors():
+    """Every check of the no-allocation forward returns before any HIP call,
+    including the limit of its scratch."""
+    f = ops.lib().moe_mxfp4_forward_noalloc
+    a = [FAKE] * 7
+    assert f(None, *a[1:], 4, 256, 128, 16, 2, 0, 0, FAKE, None, None, None) == INVALID   # null x
+    assert f(*a, 4, 200, 128, 16, 2, 0, 0, FAKE, None, None, None) == UNSUPPORTED         # H % 128
+    assert f(*a, 4, 256, 128, 16, 2, 0, 5, FAKE, None, None, None) == INVALID             # act_fmt
+    assert f(*a, 0, 256, 128, 16, 2, 0, 0, FAKE, None, None, None) == OK                  # T = 0
+    # 331 decode tokens need more than the 64 MiB scratch; 330 fit
+    assert ops.lib().moe_mxfp4_workspace_size(331, 4096, 1024, 512, 10, 1, 0) > ops.NOALLOC_SCRATCH_BYTES
+    assert f(*a, 331, 4096, 1024, 512, 10, 1, 0, FAKE, None, None, None) == WS_SMALL
+    assert ops.lib().moe_mxfp4_workspace_size(330, 4096, 1024, 512, 10, 1, 0) <= ops.NOALLOC_SCRATCH_BYTES
