@@ -292,37 +292,44 @@ MOE_API moe_status moe_expert_gate_up(const void *act, const uint8_t *act_scale,
 
 /*
  * Grouped down GEMM: y[r, j] = sum_i h[r, i] * W2[e, j, i], fp32 accumulation,
- * stored as fp32 (unrounded: the combine adds the weighted rows in fp32 and
- * rounds once, to the bf16 output; a bf16 y measured up to 3 output ulps of
- * error where a token's slots cancel).  VibeSys "Qwen3.5-397B on 4x MI300A"
- * post, section "Baseline" (the down projection of the fused MoE kernel).
+ * staged for moe_combine (VibeSys "Qwen3.5-397B on 4x MI300A" post, section
+ * "Baseline": the down projection of the fused MoE kernel).
+ * Staged y format: fp16 [A, H] holding y / 2^e, then uint8 [A, H/32] holding
+ * e + 127, one e per row and 32-column group, chosen so that the group's
+ * largest magnitude lands in [2^14, 2^15): every element keeps 11
+ * significant bits (a bf16 y, 8 bits, measured up to 3 output ulps of error
+ * where a token's slots cancel) in MOE_STAGED_Y_BYTES(A, H) bytes, half of
+ * fp32's.
  *   act_fmt = MOE_ACT_BF16:  h bf16 [A, I], h_scale = NULL
  *   act_fmt = MOE_ACT_MXFP4: h packed uint8 [A, I/2], h_scale uint8 [A, I/32]
  *   act_fmt = MOE_ACT_MXFP4_BLOCKED (tile_m 64, 128, 256): h, h_scale in the
  *              blocked order, ceil(A/16)*16 rows; h_scale 16-byte aligned
  *   tile_m     as for moe_expert_gate_up
  *   w2         codes [E', H, I/2] in the native order; w2_scale [E', H, I/32]
- *   y          out fp32 [A, H], sorted row order (A = T*Kp), 16-byte aligned
+ *   y          out staged y of MOE_STAGED_Y_BYTES(A, H) bytes, rows in
+ *              sorted order (A = T*Kp), 16-byte aligned
  * Errors: INVALID_ARGUMENT, UNSUPPORTED (H or I not a multiple of 128, or a
  * tile_m / shape the kernels do not cover; with tile_m 32, I above 13,568 for
  * bf16 activations: the kernel's LDS would exceed 160 KiB).
  */
+#define MOE_STAGED_Y_BYTES(A, H) ((size_t)(A) * (size_t)(H) * 2 + (size_t)(A) * ((size_t)(H) / 32))
 MOE_API moe_status moe_expert_down(const void *h, const uint8_t *h_scale, int32_t act_fmt,
                            const int32_t *expert_offsets, const int32_t *tile_table,
                            const int32_t *num_tiles, int32_t tile_m, const uint8_t *w2,
                            const uint8_t *w2_scale, int32_t T, int32_t H, int32_t I, int32_t Ep,
-                           int32_t Kp, float *y, void *stream);
+                           int32_t Kp, void *y, void *stream);
 
 /*
  * Weighted combine back into token order (the shared expert is slot K, so
  * no separate dense MLP is added: MiniMax M3 post, section "Shared expert
  * fusion"):  out[t, j] = bf16( sum_{k < Kp} w[t, k] * y[inv[t*Kp + k], j] ),
- * slots summed in order in fp32, one rounding to bf16.
- *   y fp32 [T*Kp, H] (16-byte aligned); topk_weights fp32 [T, Kp];
- *   inv_assign int32 [T*Kp]; out bf16 [T, H]
+ * slots summed in order in fp32 (y decoded from its staged fp16 format), one
+ * rounding to bf16.
+ *   y staged y of T*Kp rows (moe_expert_down; 16-byte aligned);
+ *   topk_weights fp32 [T, Kp]; inv_assign int32 [T*Kp]; out bf16 [T, H]
  * Errors: INVALID_ARGUMENT, UNSUPPORTED (H not a multiple of 128).
  */
-MOE_API moe_status moe_combine(const float *y, const float *topk_weights, const int32_t *inv_assign,
+MOE_API moe_status moe_combine(const void *y, const float *topk_weights, const int32_t *inv_assign,
                        int32_t T, int32_t H, int32_t Kp, uint16_t *out, void *stream);
 
 /*
@@ -363,14 +370,14 @@ MOE_API moe_status moe_mxfp8_expert_gate_up(const uint16_t *x, const int32_t *so
  * act_fmt = MOE_ACT_BF16; tile_m as for moe_mxfp8_expert_gate_up.
  *   h          bf16 [T*Kp, I];  w2 uint8 [E', H, I] (native code order),
  *              w2_scale uint8 [E', H, I/32]
- *   y          out fp32 [T*Kp, H], sorted row order
+ *   y          out staged y (as moe_expert_down), sorted row order
  * Errors: as moe_mxfp8_expert_gate_up.
  */
 MOE_API moe_status moe_mxfp8_expert_down(const uint16_t *h, const int32_t *expert_offsets,
                                  const int32_t *tile_table, const int32_t *num_tiles,
                                  int32_t tile_m, const uint8_t *w2, const uint8_t *w2_scale,
                                  int32_t T, int32_t H, int32_t I, int32_t Ep, int32_t Kp,
-                                 float *y, void *stream);
+                                 void *y, void *stream);
 
 /* The tile_m moe_mxfp4_forward uses for these shapes and activation format
  * (A = T*Kp assignments over Ep experts): 32, 64 or 128 (see
@@ -422,9 +429,9 @@ MOE_API moe_status moe_mxfp4_forward(const uint16_t *x, const float *router_logi
  * device (make that first call outside graph capture).  Nothing is
  * allocated or freed by any call.
  *   Limit: the call's workspace (moe_mxfp4_workspace_size) must fit the
- *   scratch, else WORKSPACE_TOO_SMALL: e.g. T up to 330 at H = 4096,
- *   I = 1024, E = 512, K' = 11 (about 203 KB of workspace per token there:
- *   each assignment's bf16 h and fp32 y), enough for decode batches.
+ *   scratch, else WORKSPACE_TOO_SMALL: e.g. T up to 587 at H = 4096,
+ *   I = 1024, E = 512, K' = 11 (about 114 KB of workspace per token there:
+ *   each assignment's bf16 h and staged y), enough for decode batches.
  *   Every call on one GPU uses that GPU's one scratch: calls that overlap
  *   on one GPU (different streams, or host threads) race; serialise them.
  *   No part of the scratch needs to start at zero.

@@ -28,6 +28,59 @@ __device__ __forceinline__ float e8m0_to_f32(uint32_t b) {
   return b ? __uint_as_float(b << 23) : __uint_as_float(0x00400000u);
 }
 
+// Staged y (each sorted row's down-projection, between the down GEMM and the
+// combine): fp16 values scaled by a power of two per row and 32-column
+// group, the exponent e in a byte (e + 127) of its own; value = fp16 * 2^e.
+// The group's largest magnitude lands in [2^14, 2^15): 11 significant bits
+// for every element (bf16 has 8) at half the bytes of fp32.
+constexpr int kYGroup = 32;
+
+// Exponent fields (bits 23-30) of two fp32 values packed as two 16-bit
+// halves, for max reductions of both at once.
+__device__ __forceinline__ uint32_t pack_exponents(float a, float b) {
+  return ((__float_as_uint(a) >> 23) & 0xFFu) | (((__float_as_uint(b) >> 23) & 0xFFu) << 16);
+}
+
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_move_u32(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, CTRL, 0xF, 0xF, true);
+}
+
+typedef unsigned short u16x2_t __attribute__((ext_vector_type(2)));
+
+// Per-half maximum of packed 16-bit fields (one packed max).
+__device__ __forceinline__ uint32_t max_halves(uint32_t a, uint32_t b) {
+  return __builtin_bit_cast(uint32_t, __builtin_elementwise_max(__builtin_bit_cast(u16x2_t, a),
+                                                                __builtin_bit_cast(u16x2_t, b)));
+}
+
+// Maximum of each 16-bit half of v over the 16 lanes of each DPP row (lanes
+// 16 i .. 16 i + 15): quad_perm [1,0,3,2] and [2,3,0,1] (each quad),
+// row_half_mirror (each eight), row_mirror (the sixteen).  Every lane of the
+// wave must take part.
+__device__ __forceinline__ uint32_t row16_max_halves(uint32_t v) {
+  v = max_halves(v, dpp_move_u32<0xB1>(v));
+  v = max_halves(v, dpp_move_u32<0x4E>(v));
+  v = max_halves(v, dpp_move_u32<0x141>(v));
+  v = max_halves(v, dpp_move_u32<0x140>(v));
+  return v;
+}
+
+// Exponent of a group whose largest biased fp32 exponent field is f:
+// floor(log2 amax) - 14 = f - 141, clamped to [-127, 127] (an all-zero or
+// all-subnormal group gets -127).
+__device__ __forceinline__ int y_exponent_of_field(uint32_t f) {
+  return min(127, max(-127, (int)f - 141));
+}
+
+__device__ __forceinline__ uint16_t y_encode(float v, int e) {
+  return __builtin_bit_cast(uint16_t, (_Float16)__builtin_amdgcn_ldexpf(v, -e));
+}
+
+__device__ __forceinline__ float y_decode(uint16_t bits, int e) {
+  return __builtin_amdgcn_ldexpf((float)__builtin_bit_cast(_Float16, bits), e);
+}
+
 // SiLU(g) * u in fp32.
 __device__ __forceinline__ float swiglu(float g, float u) {
   return g / (1.0f + __expf(-g)) * u;

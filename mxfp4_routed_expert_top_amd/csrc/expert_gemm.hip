@@ -283,7 +283,8 @@ __attribute__((amdgpu_waves_per_eu(MOE_GEMM_WAVES_PER_EU))) void down_kernel(
     const void* __restrict__ hin, const uint8_t* __restrict__ hscale,
     const int32_t* __restrict__ offsets, const int32_t* __restrict__ tiles,
     const int32_t* __restrict__ num_tiles, const uint8_t* __restrict__ w2,
-    const uint8_t* __restrict__ w2s, int A, int H, int I, int nsl, float* __restrict__ y) {
+    const uint8_t* __restrict__ w2s, int A, int H, int I, int nsl, uint16_t* __restrict__ y,
+    uint8_t* __restrict__ ye) {
   TileInfo ti;
   if (!load_tile(tiles, num_tiles, offsets, (int)(blockIdx.x / nsl), &ti)) return;
   const int s = blockIdx.x % nsl;
@@ -333,13 +334,20 @@ __attribute__((amdgpu_waves_per_eu(MOE_GEMM_WAVES_PER_EU))) void down_kernel(
       o.aso = m >= ti.rows ? kOutOfRange : row * rs + g;
       wave_gemm<PH, kFP4A, false, kW8>(o, I / 128 / PH, acc);
     }
+    // y in the staged fp16 format: the wave's 32 columns of a row are one
+    // group, held by one 16-lane row of the wave
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int mm = 16 * mt + 4 * g + r;
+      const int e = y_exponent_of_field(
+          row16_max_halves(max_halves(pack_exponents(acc[0][r], 0.f), pack_exponents(acc[1][r], 0.f))) &
+          0xFFFFu);
       if (mm < ti.rows) {
-        float* yr = y + (size_t)(ti.row0 + mm) * H;
-        yr[j0] = acc[0][r];
-        yr[j0 + 16] = acc[1][r];
+        const size_t row = (size_t)(ti.row0 + mm);
+        uint16_t* yr = y + row * H;
+        yr[j0] = y_encode(acc[0][r], e);
+        yr[j0 + 16] = y_encode(acc[1][r], e);
+        if (nl == 0) ye[row * (H / kYGroup) + (j0 - nl) / kYGroup] = (uint8_t)(e + 127);
       }
     }
   }
@@ -367,11 +375,13 @@ __device__ __forceinline__ void prefetch_ranges(const Prefetch& pf, int b) {
 }
 
 // out[t, j] = bf16( sum_k w[t, k] * y[inv[t*K' + k], j] ), slots in order,
-// fp32 y and sums; 8 outputs per thread (two 16-byte loads of each slot's y,
-// a 16-byte store).  The eight slots' row indices are read first, then their
-// y rows, so the loads are independent (waiting for each slot's index before
+// fp32 sums of the staged fp16 y (times its group's power of two); 8 outputs
+// per thread (a 16-byte load of each slot's y and its group exponent byte, a
+// 16-byte store).  The eight slots' row indices are read first, then their y
+// rows, so the loads are independent (waiting for each slot's index before
 // its y load cost 20% on the skewed batch).
-__global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ y,
+__global__ __launch_bounds__(256) void combine_kernel(const uint16_t* __restrict__ y,
+                                                      const uint8_t* __restrict__ ye,
                                                       const float* __restrict__ w,
                                                       const int32_t* __restrict__ inv, int H,
                                                       int Kp, int nbx, uint16_t* __restrict__ out,
@@ -396,19 +406,22 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
       r[i] = ok ? inv[(size_t)t * Kp + k0 + i] : 0;
       wk[i] = ok ? w[(size_t)t * Kp + k0 + i] : 0.f;
     }
-    floatx4_t v[8][2];
+    u32x4_t v[8];
+    int ex[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i)
       if (k0 + i < Kp) {
-        const floatx4_t* p = reinterpret_cast<const floatx4_t*>(y + (size_t)r[i] * H + j);
-        v[i][0] = __builtin_nontemporal_load(p);
-        v[i][1] = __builtin_nontemporal_load(p + 1);
+        v[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(y + (size_t)r[i] * H + j));
+        ex[i] = (int)ye[(size_t)r[i] * (H / kYGroup) + j / kYGroup] - 127;
       }
 #pragma unroll
     for (int i = 0; i < 8; ++i)
       if (k0 + i < Kp)
 #pragma unroll
-        for (int q = 0; q < 8; ++q) acc[q] += wk[i] * v[i][q / 4][q % 4];
+        for (int q = 0; q < 4; ++q) {
+          acc[2 * q] += wk[i] * y_decode((uint16_t)(v[i][q] & 0xFFFFu), ex[i]);
+          acc[2 * q + 1] += wk[i] * y_decode((uint16_t)(v[i][q] >> 16), ex[i]);
+        }
   }
   u32x4_t o;
 #pragma unroll
@@ -452,11 +465,12 @@ struct DownLaunch {
   static hipError_t run(dim3 grid, hipStream_t stream, const void* hin, const uint8_t* hscale,
                         const int32_t* offsets, const int32_t* tiles, const int32_t* num_tiles,
                         const uint8_t* w2, const uint8_t* w2s, int A, int H, int I, int nsl,
-                        float* y) {
+                        uint16_t* y) {
     const size_t lds = (size_t)128 * (I / 32) + (kFP4A ? 0 : (size_t)kXR * I * 2);
+    uint8_t* ye = reinterpret_cast<uint8_t*>(y) + (size_t)A * H * 2;   // the group exponents
     hipLaunchKernelGGL((down_kernel<PH, kFP4A, kW8>), grid, dim3(256), lds, stream,
                        hin, hscale, offsets,
-                       tiles, num_tiles, w2, w2s, A, H, I, nsl, y);
+                       tiles, num_tiles, w2, w2s, A, H, I, nsl, y, ye);
     return hipGetLastError();
   }
 };
@@ -487,19 +501,20 @@ hipError_t launch_gate_up(int act_fmt, int wfmt, const void* act, const uint8_t*
 hipError_t launch_down(int act_fmt, int wfmt, const void* h, const uint8_t* h_scale,
                        const int32_t* offsets, const int32_t* tiles, const int32_t* num_tiles,
                        int max_tiles, const uint8_t* w2, const uint8_t* w2s, int A, int H, int I,
-                       float* y, hipStream_t stream) {
+                       uint16_t* y, hipStream_t stream) {
   const int nsl = H / 128;
   dim3 grid((unsigned)(max_tiles * nsl));
   return dispatch<DownLaunch>(act_fmt, wfmt, I / 128, grid, stream, h, h_scale, offsets, tiles,
                               num_tiles, w2, w2s, A, H, I, nsl, y);
 }
 
-hipError_t launch_combine(const float* y, const float* w, const int32_t* inv, int T, int H, int Kp,
-                          uint16_t* out, hipStream_t stream, const Prefetch* pf) {
+hipError_t launch_combine(const uint16_t* y, const float* w, const int32_t* inv, int T, int H,
+                          int Kp, uint16_t* out, hipStream_t stream, const Prefetch* pf) {
   const int nbx = (H / 8 + 255) / 256;
   Prefetch none{};
   const Prefetch& p = pf ? *pf : none;
+  const uint8_t* ye = reinterpret_cast<const uint8_t*>(y) + (size_t)T * Kp * H * 2;
   dim3 grid((unsigned)(nbx * T + (p.n > 0 ? kPrefetchBlocks : 0))), block(256);
-  hipLaunchKernelGGL(combine_kernel, grid, block, 0, stream, y, w, inv, H, Kp, nbx, out, T, p);
+  hipLaunchKernelGGL(combine_kernel, grid, block, 0, stream, y, ye, w, inv, H, Kp, nbx, out, T, p);
   return hipGetLastError();
 }

@@ -617,7 +617,8 @@ __global__ __launch_bounds__(256, KV ? 2 : 1) void down_tiled_kernel(
     const void* __restrict__ hin, const uint8_t* __restrict__ hscale,
     const int32_t* __restrict__ offsets, const int32_t* __restrict__ tiles,
     const int32_t* __restrict__ num_tiles, const uint8_t* __restrict__ w2,
-    const uint8_t* __restrict__ w2s, int A, int H, int I, float* __restrict__ y) {
+    const uint8_t* __restrict__ w2s, int A, int H, int I, uint16_t* __restrict__ y,
+    uint8_t* __restrict__ ye) {
   TileT ti;
   int s;
   if (!tile_slice<BM, kFP4A, 4>(blockIdx.x, tiles, offsets, *num_tiles, H / 256, &ti, &s)) return;
@@ -645,15 +646,28 @@ __global__ __launch_bounds__(256, KV ? 2 : 1) void down_tiled_kernel(
     for (int st = 0; st < 4; ++st) acc[mt][st] = (floatx4_t){0.f, 0.f, 0.f, 0.f};
   tile_loop<BM, kFP4A, kW8, KV, kBlk>(G, ti, srow, wrow, kFP4A ? rb : (uint32_t)I * 2, rs, acc);
 
+  // y in the staged fp16 format: the wave's 64 columns of a row are two
+  // 32-column groups (strips 0-1 and 2-3), each row held by one 16-lane row
+  // of the wave
 #pragma unroll
   for (int mt = 0; mt < BM / 16; ++mt)
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int m = 16 * mt + 4 * g + r;
+      const uint32_t f = row16_max_halves(max_halves(pack_exponents(acc[mt][0][r], acc[mt][2][r]),
+                                                     pack_exponents(acc[mt][1][r], acc[mt][3][r])));
+      const int e0 = y_exponent_of_field(f & 0xFFFFu), e1 = y_exponent_of_field(f >> 16);
       if (m < ti.rows) {
-        float* yr = y + (size_t)(ti.row0 + m) * H;
-#pragma unroll
-        for (int st = 0; st < 4; ++st) yr[j0 + 16 * st + nl] = acc[mt][st][r];
+        const size_t row = (size_t)(ti.row0 + m);
+        uint16_t* yr = y + row * H + j0 + nl;
+        yr[0] = y_encode(acc[mt][0][r], e0);
+        yr[16] = y_encode(acc[mt][1][r], e0);
+        yr[32] = y_encode(acc[mt][2][r], e1);
+        yr[48] = y_encode(acc[mt][3][r], e1);
+        if (nl == 0) {
+          ye[row * (H / kYGroup) + j0 / kYGroup] = (uint8_t)(e0 + 127);
+          ye[row * (H / kYGroup) + j0 / kYGroup + 1] = (uint8_t)(e1 + 127);
+        }
       }
     }
 }
@@ -673,11 +687,12 @@ hipError_t launch_gate_up_bm(const void* act, const uint8_t* act_scale, const in
 template <int BM, bool kFP4A, bool kW8 = false, int KV = 0, bool kBlk = false>
 hipError_t launch_down_bm(const void* h, const uint8_t* h_scale, const int32_t* offsets,
                           const int32_t* tiles, const int32_t* num_tiles, int max_tiles,
-                          const uint8_t* w2, const uint8_t* w2s, int A, int H, int I, float* y,
+                          const uint8_t* w2, const uint8_t* w2s, int A, int H, int I, uint16_t* y,
                           hipStream_t stream) {
   const unsigned grid = tile_slice_grid<kFP4A>(max_tiles, H / 256);
+  uint8_t* ye = reinterpret_cast<uint8_t*>(y) + (size_t)A * H * 2;   // the group exponents
   hipLaunchKernelGGL((down_tiled_kernel<BM, kFP4A, kW8, KV, kBlk>), dim3(grid), dim3(256), 0, stream, h,
-                     h_scale, offsets, tiles, num_tiles, w2, w2s, A, H, I, y);
+                     h_scale, offsets, tiles, num_tiles, w2, w2s, A, H, I, y, ye);
   return hipGetLastError();
 }
 
@@ -707,7 +722,7 @@ hipError_t gate_up_fp4(int tile_m, const void* act, const uint8_t* act_scale,
 template <bool kBlk>
 hipError_t down_fp4(int tile_m, const void* h, const uint8_t* h_scale, const int32_t* offsets,
                     const int32_t* tiles, const int32_t* num_tiles, int max_tiles,
-                    const uint8_t* w2, const uint8_t* w2s, int A, int H, int I, float* y,
+                    const uint8_t* w2, const uint8_t* w2s, int A, int H, int I, uint16_t* y,
                     hipStream_t stream) {
 #define MOE_DN_ARGS h, h_scale, offsets, tiles, num_tiles, max_tiles, w2, w2s, A, H, I, y, stream
   if (tile_m == 256) return launch_down_bm<256, true, false, 0, kBlk>(MOE_DN_ARGS);
@@ -766,7 +781,7 @@ hipError_t launch_down_tiled(int tile_m, int act_fmt, int wfmt, const void* h,
                              const uint8_t* h_scale,
                              const int32_t* offsets, const int32_t* tiles,
                              const int32_t* num_tiles, int max_tiles, const uint8_t* w2,
-                             const uint8_t* w2s, int A, int H, int I, float* y,
+                             const uint8_t* w2s, int A, int H, int I, uint16_t* y,
                              hipStream_t stream) {
   if (wfmt == 1)
     return tile_m == 128 ? launch_down_bm<128, false, true>(h, h_scale, offsets, tiles, num_tiles,

@@ -53,12 +53,14 @@ hipError_t launch_gate_up(int act_fmt, int wfmt, const void* act, const uint8_t*
                           const int32_t* num_tiles, int max_tiles, const uint8_t* w13,
                           const uint8_t* w13s, int T, int H, int I, int Kp, uint16_t* h,
                           hipStream_t stream);
-// y fp32 [A, H]: each sorted row's down-projection, unrounded (the combine
-// sums the weighted rows in fp32 and rounds once, to the bf16 output)
+// y: each sorted row's down-projection in the staged fp16 format of
+// common.h: fp16 [A, H] followed by the group exponent bytes [A, H / 32]
+// (staged_y_bytes(A, H) bytes in all)
+inline size_t staged_y_bytes(size_t A, size_t H) { return A * H * 2 + A * (H / 32); }
 hipError_t launch_down(int act_fmt, int wfmt, const void* h, const uint8_t* h_scale,
                        const int32_t* offsets, const int32_t* tiles, const int32_t* num_tiles,
                        int max_tiles, const uint8_t* w2, const uint8_t* w2s, int A, int H, int I,
-                       float* y, hipStream_t stream);
+                       uint16_t* y, hipStream_t stream);
 // Byte ranges the combine's extra workgroups read into the caches (the next
 // layer's weights that are known before its routing); n = 0 for none.
 struct Prefetch {
@@ -67,8 +69,9 @@ struct Prefetch {
   uint32_t bytes[kMax];
   int n;
 };
-hipError_t launch_combine(const float* y, const float* w, const int32_t* inv, int T, int H, int Kp,
-                          uint16_t* out, hipStream_t stream, const Prefetch* pf = nullptr);
+// y as written by launch_down / launch_down_tiled for A = T * Kp rows
+hipError_t launch_combine(const uint16_t* y, const float* w, const int32_t* inv, int T, int H,
+                          int Kp, uint16_t* out, hipStream_t stream, const Prefetch* pf = nullptr);
 
 bool expert_gemm_tiled_supported(int tile_m, int act_fmt, int H, int I, int wfmt = 0);
 hipError_t launch_gate_up_tiled(int tile_m, int act_fmt, int wfmt, const void* act,
@@ -77,10 +80,10 @@ hipError_t launch_gate_up_tiled(int tile_m, int act_fmt, int wfmt, const void* a
                                 const int32_t* tiles, const int32_t* num_tiles, int max_tiles,
                                 const uint8_t* w13, const uint8_t* w13s, int T, int H, int I,
                                 int Kp, uint16_t* h, hipStream_t stream);
-// y fp32 [A, H] in sorted order (as launch_down)
+// y in sorted order, as launch_down
 hipError_t launch_down_tiled(int tile_m, int act_fmt, int wfmt, const void* h,
                              const uint8_t* h_scale,
                              const int32_t* offsets, const int32_t* tiles,
                              const int32_t* num_tiles, int max_tiles, const uint8_t* w2,
-                             const uint8_t* w2s, int A, int H, int I, float* y,
+                             const uint8_t* w2s, int A, int H, int I, uint16_t* y,
                              hipStream_t stream);

@@ -90,10 +90,10 @@ FwdLayout forward_layout(int64_t T, int64_t H, int64_t I, int64_t E, int64_t K, 
   L.h = take(A * I * 2);
   L.hq = take(q ? A16 * I / 2 : 0);
   L.hs = take(q ? A16 * I / 32 : 0);
-  // y fp32 [A, H]; the router GEMM's partial sums (when the call routes from
-  // x) live in the same bytes: routing consumes them before the down GEMM
-  // writes y
-  L.y = take(std::max((size_t)(A * H * 4), router_workspace_bytes((int)T, (int)H, (int)Ep)));
+  // staged y (fp16 [A, H] + group exponents); the router GEMM's partial sums
+  // (when the call routes from x) live in the same bytes: routing consumes
+  // them before the down GEMM writes y
+  L.y = take(std::max(staged_y_bytes(A, H), router_workspace_bytes((int)T, (int)H, (int)Ep)));
   L.total = p;
   return L;
 }
@@ -314,7 +314,7 @@ moe_status down_impl(const void* h, const uint8_t* h_scale, int32_t act_fmt, int
                      const int32_t* expert_offsets, const int32_t* tile_table,
                      const int32_t* num_tiles, int32_t tile_m, const uint8_t* w2,
                      const uint8_t* w2_scale, int32_t T, int32_t H, int32_t I, int32_t Ep,
-                     int32_t Kp, float* y, void* stream) {
+                     int32_t Kp, void* y, void* stream) {
   if (T < 0 || Ep < 1 || Kp < 1 || !act_fmt_ok(act_fmt)) return MOE_ERR_INVALID_ARGUMENT;
   moe_status st = check_shape_HI(H, I);
   if (st != MOE_OK) return st;
@@ -329,16 +329,17 @@ moe_status down_impl(const void* h, const uint8_t* h_scale, int32_t act_fmt, int
   if (!h || !expert_offsets || !tile_table || !num_tiles || !w2 || !w2_scale || !y ||
       (act_fmt != MOE_ACT_BF16 && !h_scale))
     return MOE_ERR_INVALID_ARGUMENT;
-  if (!aligned16(h) || !aligned16(w2) || (blk && !aligned16(h_scale)))
+  if (!aligned16(h) || !aligned16(w2) || !aligned16(y) || (blk && !aligned16(h_scale)))
     return MOE_ERR_INVALID_ARGUMENT;
   const int64_t mt = max_tiles_for((int64_t)T * Kp, Ep, tile_m);
   if (mt * (H / 128) >= INT32_MAX) return MOE_ERR_UNSUPPORTED;
+  uint16_t* y16 = static_cast<uint16_t*>(y);
   hipStream_t s = as_stream(stream);
   if (tile_m != MOE_TILE_M)
     return from_hip(launch_down_tiled(tile_m, act_fmt, wfmt, h, h_scale, expert_offsets, tile_table,
-                                      num_tiles, (int)mt, w2, w2_scale, T * Kp, H, I, y, s));
+                                      num_tiles, (int)mt, w2, w2_scale, T * Kp, H, I, y16, s));
   return from_hip(launch_down(act_fmt, wfmt, h, h_scale, expert_offsets, tile_table, num_tiles,
-                              (int)mt, w2, w2_scale, T * Kp, H, I, y, s));
+                              (int)mt, w2, w2_scale, T * Kp, H, I, y16, s));
 }
 
 }  // namespace
@@ -367,7 +368,7 @@ moe_status moe_expert_down(const void* h, const uint8_t* h_scale, int32_t act_fm
                            const int32_t* expert_offsets, const int32_t* tile_table,
                            const int32_t* num_tiles, int32_t tile_m, const uint8_t* w2,
                            const uint8_t* w2_scale, int32_t T, int32_t H, int32_t I, int32_t Ep,
-                           int32_t Kp, float* y, void* stream) {
+                           int32_t Kp, void* y, void* stream) {
   return down_impl(h, h_scale, act_fmt, 0, expert_offsets, tile_table, num_tiles, tile_m, w2,
                    w2_scale, T, H, I, Ep, Kp, y, stream);
 }
@@ -376,19 +377,20 @@ moe_status moe_mxfp8_expert_down(const uint16_t* h, const int32_t* expert_offset
                                  const int32_t* tile_table, const int32_t* num_tiles,
                                  int32_t tile_m, const uint8_t* w2, const uint8_t* w2_scale,
                                  int32_t T, int32_t H, int32_t I, int32_t Ep, int32_t Kp,
-                                 float* y, void* stream) {
+                                 void* y, void* stream) {
   return down_impl(h, nullptr, MOE_ACT_BF16, 1, expert_offsets, tile_table, num_tiles, tile_m, w2,
                    w2_scale, T, H, I, Ep, Kp, y, stream);
 }
 
-moe_status moe_combine(const float* y, const float* topk_weights, const int32_t* inv_assign,
+moe_status moe_combine(const void* y, const float* topk_weights, const int32_t* inv_assign,
                        int32_t T, int32_t H, int32_t Kp, uint16_t* out, void* stream) {
   if (T < 0 || H <= 0 || Kp < 1) return MOE_ERR_INVALID_ARGUMENT;
   if (H % 128) return MOE_ERR_UNSUPPORTED;
   if (T == 0) return MOE_OK;
   if (!y || !topk_weights || !inv_assign || !out || !aligned16(y) || !aligned16(out))
     return MOE_ERR_INVALID_ARGUMENT;
-  return from_hip(launch_combine(y, topk_weights, inv_assign, T, H, Kp, out, as_stream(stream)));
+  return from_hip(launch_combine(static_cast<const uint16_t*>(y), topk_weights, inv_assign, T, H,
+                                 Kp, out, as_stream(stream)));
 }
 
 int32_t moe_gemm_tile_m(int32_t T, int32_t Kp, int32_t Ep, int32_t H, int32_t I,
@@ -470,7 +472,7 @@ moe_status forward_impl(const uint16_t* x, const float* router_logits,
   uint16_t* h = (uint16_t*)(ws + L.h);
   uint8_t* hq = (uint8_t*)(ws + L.hq);
   uint8_t* hs = (uint8_t*)(ws + L.hs);
-  float* y = (float*)(ws + L.y);
+  uint16_t* y = (uint16_t*)(ws + L.y);
   float* rpart = (float*)(ws + L.y);                       // router partial sums (same bytes)
   hipStream_t s = as_stream(stream);
 

@@ -313,10 +313,10 @@ def expert_gate_up(act, act_scale, act_fmt: int, align: dict, w13, w13_scale, T:
 
 def expert_down(h, h_scale, act_fmt: int, align: dict, w2, w2_scale, T: int, H: int, I: int,
                 Ep: int, Kp: int, y=None, stream=None):
-    """moe_expert_down -> y fp32 [T*Kp, H] in sorted row order."""
+    """moe_expert_down -> staged y (uint8 [staged_y_bytes(T*Kp, H)]), rows in sorted order."""
     if y is None:
-        y = torch.empty(T * Kp, H, dtype=torch.float32, device=w2.device)
-    _dt(y, torch.float32, "y")
+        y = torch.empty(staged_y_bytes(T * Kp, H), dtype=torch.uint8, device=w2.device)
+    _dt(y, torch.uint8, "y")
     _check("moe_expert_down", lib().moe_expert_down(
         _ptr(h), _ptr(h_scale), act_fmt, _ptr(align["offsets"]), _ptr(align["tiles"]),
         _ptr(align["num_tiles"]), align["tile_m"], _ptr(w2), _ptr(w2_scale), T, H, I, Ep, Kp,
@@ -344,11 +344,11 @@ def mxfp8_expert_gate_up(x, align: dict, w13, w13_scale, T: int, H: int, I: int,
 
 def mxfp8_expert_down(h, align: dict, w2, w2_scale, T: int, H: int, I: int, Ep: int, Kp: int,
                       y=None, stream=None):
-    """moe_mxfp8_expert_down (MXFP8 weights, bf16 h) -> y fp32 [T*Kp, H], sorted rows."""
+    """moe_mxfp8_expert_down (MXFP8 weights, bf16 h) -> staged y, sorted rows."""
     _dt(h, torch.bfloat16, "h")
     if y is None:
-        y = torch.empty(T * Kp, H, dtype=torch.float32, device=w2.device)
-    _dt(y, torch.float32, "y")
+        y = torch.empty(staged_y_bytes(T * Kp, H), dtype=torch.uint8, device=w2.device)
+    _dt(y, torch.uint8, "y")
     _check("moe_mxfp8_expert_down", lib().moe_mxfp8_expert_down(
         _ptr(h), _ptr(align["offsets"]), _ptr(align["tiles"]), _ptr(align["num_tiles"]),
         align["tile_m"], _ptr(w2), _ptr(w2_scale), T, H, I, Ep, Kp, _ptr(y), _stream(stream)))
@@ -356,8 +356,8 @@ def mxfp8_expert_down(h, align: dict, w2, w2_scale, T: int, H: int, I: int, Ep: 
 
 
 def combine(y, topk_weights, inv, T: int, H: int, Kp: int, out=None, stream=None):
-    """moe_combine: y fp32 [T*Kp, H] -> out bf16 [T, H]."""
-    _dt(y, torch.float32, "y")
+    """moe_combine: staged y of T*Kp rows -> out bf16 [T, H]."""
+    _dt(y, torch.uint8, "y")
     if out is None:
         out = torch.empty(T, H, dtype=torch.bfloat16, device=y.device)
     _check("moe_combine", lib().moe_combine(
@@ -366,6 +366,12 @@ def combine(y, topk_weights, inv, T: int, H: int, Kp: int, out=None, stream=None
 
 
 # ------------------------------------------------------------ whole layer --
+
+def staged_y_bytes(A: int, H: int) -> int:
+    """Bytes of the staged y between moe_expert_down and moe_combine
+    (MOE_STAGED_Y_BYTES): fp16 [A, H] and one exponent byte per 32 columns."""
+    return A * H * 2 + A * (H // 32)
+
 
 def workspace_size(T, H, I, E, K, shared, act_fmt) -> int:
     return int(lib().moe_mxfp4_workspace_size(T, H, I, E, K, shared, act_fmt))
@@ -489,7 +495,7 @@ def alloc_stages(T: int, H: int, I: int, E: int, K: int, shared: int, act_fmt: i
              w=torch.empty(T, Kp, dtype=torch.float32, device=device),
              align=alloc_align(T, Kp, Ep, device),
              h=torch.empty(A, I, dtype=torch.bfloat16, device=device),
-             y=torch.empty(A, H, dtype=torch.float32, device=device),
+             y=torch.empty(staged_y_bytes(A, H), dtype=torch.uint8, device=device),
              out=torch.empty(T, H, dtype=torch.bfloat16, device=device))
     if act_fmt == ACT_MXFP4:
         # per token / sorted row, or sorted rows in the blocked order (tiled GEMMs)

@@ -322,7 +322,7 @@ def test_forward_noalloc_argument_errors():
     assert f(*a, 4, 200, 128, 16, 2, 0, 0, FAKE, None, None, None) == UNSUPPORTED         # H % 128
     assert f(*a, 4, 256, 128, 16, 2, 0, 5, FAKE, None, None, None) == INVALID             # act_fmt
     assert f(*a, 0, 256, 128, 16, 2, 0, 0, FAKE, None, None, None) == OK                  # T = 0
-    # 331 decode tokens need more than the 64 MiB scratch; 330 fit
-    assert ops.lib().moe_mxfp4_workspace_size(331, 4096, 1024, 512, 10, 1, 0) > ops.NOALLOC_SCRATCH_BYTES
-    assert f(*a, 331, 4096, 1024, 512, 10, 1, 0, FAKE, None, None, None) == WS_SMALL
-    assert ops.lib().moe_mxfp4_workspace_size(330, 4096, 1024, 512, 10, 1, 0) <= ops.NOALLOC_SCRATCH_BYTES
+    # 588 decode tokens need more than the 64 MiB scratch; 587 fit
+    assert ops.lib().moe_mxfp4_workspace_size(588, 4096, 1024, 512, 10, 1, 0) > ops.NOALLOC_SCRATCH_BYTES
+    assert f(*a, 588, 4096, 1024, 512, 10, 1, 0, FAKE, None, None, None) == WS_SMALL
+    assert ops.lib().moe_mxfp4_workspace_size(587, 4096, 1024, 512, 10, 1, 0) <= ops.NOALLOC_SCRATCH_BYTES

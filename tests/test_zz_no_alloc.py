@@ -65,9 +65,10 @@ def test_noalloc_decode_shape_and_limit():
     assert np.array_equal(na, fw)
     (na, _, _), (fw, _, _) = _both(prob, 17)          # smaller, after the full batch
     assert np.array_equal(na, fw)
-    # beyond the scratch: rejected, outputs untouched
+    # beyond the scratch (588 decode tokens): rejected, outputs untouched
     c = cfg
-    T = 331
+    T = 588
+    assert ops().workspace_size(T, c.H, c.I, c.E, c.K, c.shared, c.act_fmt) > ops().NOALLOC_SCRATCH_BYTES
     x = torch.zeros(T, c.H, dtype=torch.bfloat16, device=DEV)
     lg = torch.zeros(T, c.E, dtype=torch.float32, device=DEV)
     g = torch.zeros(T, dtype=torch.float32, device=DEV)
