@@ -72,11 +72,14 @@
  * stay row-major.  Per expert, with K the reduction length (H for w13, I for
  * w2), NQ = 1 (MXFP4) or 2 (MXFP8) and C = K/128 chunks, the codes are
  * 1 KiB blocks: block ((s*C + c)*NQ + q) holds at byte 16*l (l < 64,
- * l = 16*g + n) the 16 row-major bytes of row 16*s + n starting at byte
+ * l = 16*g + n) the 16 row-major bytes of row
+ * 32*(s/2) + 8*(n/4) + 4*(s%2) + n%4 starting at byte
  * NQ*(64*c + 16*g) + 16*q.  An expert keeps its size and place (expert e
  * starts at e * rows * K * NQ / 2 bytes), so each expert's codes stay one
  * contiguous range.  (One MFMA operand load of 16 rows x 128 elements is
- * then one contiguous KiB instead of 16 half cache lines.)
+ * then one contiguous KiB instead of 16 half cache lines; the two 16-row
+ * strips of each 32-row group interleave their rows in runs of four so
+ * that a lane of the MFMA result holds eight consecutive output columns.)
  */
 #ifndef MOE_MXFP4_H
 #define MOE_MXFP4_H
@@ -250,7 +253,7 @@ MOE_API moe_status moe_mxfp4_quantize_blocked(const void *src, int32_t src_dtype
  *   wfmt       0 = MXFP4, 1 = MXFP8
  *   dst        out, same size, 16-byte aligned, not overlapping src
  * Errors: INVALID_ARGUMENT (null or misaligned pointers, rows < 0, cols < 0,
- * bad wfmt, overlapping buffers), UNSUPPORTED (rows not a multiple of 16,
+ * bad wfmt, overlapping buffers), UNSUPPORTED (rows not a multiple of 32,
  * cols not a multiple of 128).
  */
 MOE_API moe_status moe_weights_to_native(const uint8_t *src, int32_t wfmt, int64_t rows,

@@ -66,6 +66,17 @@ __device__ __forceinline__ uint32_t row16_max_halves(uint32_t v) {
   return v;
 }
 
+// Maximum of each 16-bit half of v over lanes n, n ^ 16, n ^ 32, n ^ 48 (the
+// same lane of the four DPP rows): each gfx950 permlane swap exchanges half
+// of the wave between two copies of v, so every lane ends up with its own
+// value and its partner's (at distance 32, then 16).
+__device__ __forceinline__ uint32_t xrow_max_halves(uint32_t v) {
+  const auto a = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+  v = max_halves(a[0], a[1]);
+  const auto b = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+  return max_halves(b[0], b[1]);
+}
+
 // Exponent of a group whose largest biased fp32 exponent field is f:
 // floor(log2 amax) - 14 = f - 141, clamped to [-127, 127] (an all-zero or
 // all-subnormal group gets -127).
@@ -152,14 +163,23 @@ __device__ __forceinline__ u32x4_t bload16_nt(rsrc_t r, uint32_t voff, uint32_t 
 }
 
 // Expert weight codes in the GEMM kernels' native order.  An expert's code
-// matrix (rows a multiple of 16, reduction length K a multiple of 128; NQ =
+// matrix (rows a multiple of 32, reduction length K a multiple of 128; NQ =
 // 1 byte per two MXFP4 codes -> 16 code bytes per lane and chunk, NQ = 2 for
 // MXFP8's byte per code -> 32) is a sequence of 1 KiB blocks: block
 // (s * (K / 128) + c) * NQ + hq holds, at byte 16 l, the 16 bytes lane
-// l = 16 g + n loads for row 16 s + n, chunk c (elements [128 c, 128 c + 128)),
-// K-group g, part hq: row-major code bytes [NQ (64 c + 16 g) + 16 hq, +16).
-// A wave's load of one strip chunk is then one contiguous KiB, where the
-// row-major layout touches 16 rows at half a 128-byte line each.
+// l = 16 g + n loads for strip s, slot n, chunk c (elements [128 c,
+// 128 c + 128)), K-group g, part hq: row-major code bytes [NQ (64 c + 16 g) +
+// 16 hq, +16) of row 32 (s / 2) + wnat_row(s % 2, n).  A wave's load of one
+// strip chunk is then one contiguous KiB, where the row-major layout touches
+// 16 rows at half a 128-byte line each.
+//
+// The slots of a strip pair interleave the pair's 32 rows in runs of four:
+// with the weights as the MFMA's A operand, lane 16 g + n holds D rows 4 g ..
+// 4 g + 3 of each strip, which are then weight rows 8 g .. 8 g + 7 of the
+// pair: eight consecutive output columns, one 16-byte store of fp16 / bf16.
+__host__ __device__ constexpr int wnat_row(int u, int n) {
+  return 8 * (n >> 2) + 4 * u + (n & 3);
+}
 __device__ __forceinline__ uint32_t wnat_lane(int strip, int K, int NQ, int lane) {
   return (uint32_t)strip * (uint32_t)(K / 128 * NQ) * 1024u + 16u * (uint32_t)lane;
 }

@@ -196,8 +196,9 @@ __device__ __forceinline__ void scales_to_lds(rsrc_t r, uint32_t off, uint32_t b
 }
 
 // gate_up: a workgroup (4 waves) owns one tile and 64 intermediate columns;
-// wave w owns columns i in [16 w, 16 w + 16) of them: 16 gate rows and 16 up
-// rows of W13 over the whole K = H.  The tile's 16-row subtiles run one after
+// wave w owns strip w of them (16 columns, every other run of four in its
+// strip pair's 32, in the native order): 16 gate rows and 16 up rows of W13
+// over the whole K = H.  The tile's 16-row subtiles run one after
 // the other (the second re-reads the weights, from L2): decode tiles mostly
 // have 1-3 rows and this keeps a single subtile's registers live.  SwiGLU in
 // registers, bf16 h stored in sorted row order.
@@ -214,7 +215,10 @@ __attribute__((amdgpu_waves_per_eu(MOE_GEMM_WAVES_PER_EU))) void gate_up_kernel(
   const int s = blockIdx.x % nsl;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int nl = lane & 15, g = lane >> 4;
-  const int i = s * 64 + wave * 16 + nl;
+  // the wave's strip of gate rows (and the matching up strip) and the
+  // intermediate column its lane's slot holds in the native order
+  const int st = s * 4 + wave;
+  const int i = s * 64 + (wave & ~1) * 16 + wnat_row(wave & 1, nl);
   const uint32_t rb = H / 2, rs = H / 32;
   const uint32_t wrb = kW8 ? H : H / 2;                    // weight code bytes per row
   const size_t wbytes = (size_t)2 * I * wrb, sbytes = (size_t)2 * I * rs;
@@ -224,10 +228,10 @@ __attribute__((amdgpu_waves_per_eu(MOE_GEMM_WAVES_PER_EU))) void gate_up_kernel(
   o.w = make_rsrc(w13 + ti.expert * wbytes, (uint32_t)wbytes);
   o.stream = ti.single;
   constexpr int NQ = Phase<PH, kFP4A, false, kW8>::NQ;
-  o.wo[0] = wnat_lane(i >> 4, H, NQ, lane);
-  o.wo[1] = wnat_lane((I + i) >> 4, H, NQ, lane);
-  o.lso[0] = (wave * 16 + nl) * rs + g;
-  o.lso[1] = (64 + wave * 16 + nl) * rs + g;
+  o.wo[0] = wnat_lane(st, H, NQ, lane);
+  o.wo[1] = wnat_lane(I / 16 + st, H, NQ, lane);
+  o.lso[0] = (i - s * 64) * rs + g;
+  o.lso[1] = (64 + i - s * 64) * rs + g;
   if (kFP4A) {
     o.a = make_rsrc(act, (uint32_t)((size_t)T * rb));
     o.as = make_rsrc(act_scale, (uint32_t)((size_t)T * rs));
@@ -275,8 +279,8 @@ __attribute__((amdgpu_waves_per_eu(MOE_GEMM_WAVES_PER_EU))) void gate_up_kernel(
 }
 
 // down: a workgroup (4 waves) owns one tile and 128 output columns j; wave w
-// owns [32 w, 32 w + 32) of them (two 16-row strips of W2) over K = I.  y is
-// stored as fp32 in sorted row order.
+// owns [32 w, 32 w + 32) of them (a strip pair of W2) over K = I.  y is
+// stored in the staged fp16 format in sorted row order.
 template <int PH, bool kFP4A, bool kW8>
 __global__ __launch_bounds__(256)
 __attribute__((amdgpu_waves_per_eu(MOE_GEMM_WAVES_PER_EU))) void down_kernel(
@@ -290,7 +294,10 @@ __attribute__((amdgpu_waves_per_eu(MOE_GEMM_WAVES_PER_EU))) void down_kernel(
   const int s = blockIdx.x % nsl;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int nl = lane & 15, g = lane >> 4;
-  const int j0 = s * 128 + wave * 32 + nl;                 // strip 0; strip 1 is j0 + 16
+  // the wave's strip pair 2 st, 2 st + 1 (columns jb .. jb + 31) and the
+  // columns its lane's slots hold in the native order
+  const int st = s * 4 + wave, jb = 32 * st;
+  const int jc[2] = {jb + wnat_row(0, nl), jb + wnat_row(1, nl)};
   const uint32_t rb = I / 2, rs = I / 32;
   const uint32_t wrb = kW8 ? I : I / 2;                    // weight code bytes per row
   const size_t wbytes = (size_t)H * wrb, sbytes = (size_t)H * rs;
@@ -300,10 +307,10 @@ __attribute__((amdgpu_waves_per_eu(MOE_GEMM_WAVES_PER_EU))) void down_kernel(
   o.w = make_rsrc(w2 + ti.expert * wbytes, (uint32_t)wbytes);
   o.stream = ti.single;
   constexpr int NQ = Phase<PH, kFP4A, false, kW8>::NQ;
-  o.wo[0] = wnat_lane(j0 >> 4, I, NQ, lane);
-  o.wo[1] = wnat_lane((j0 >> 4) + 1, I, NQ, lane);
-  o.lso[0] = (wave * 32 + nl) * rs + g;
-  o.lso[1] = (wave * 32 + 16 + nl) * rs + g;
+  o.wo[0] = wnat_lane(2 * st, I, NQ, lane);
+  o.wo[1] = wnat_lane(2 * st + 1, I, NQ, lane);
+  o.lso[0] = (jc[0] - s * 128) * rs + g;
+  o.lso[1] = (jc[1] - s * 128) * rs + g;
   if (kFP4A) {
     o.a = make_rsrc(hin, (uint32_t)((size_t)A * rb));
     o.as = make_rsrc(hscale, (uint32_t)((size_t)A * rs));
@@ -345,9 +352,9 @@ __attribute__((amdgpu_waves_per_eu(MOE_GEMM_WAVES_PER_EU))) void down_kernel(
       if (mm < ti.rows) {
         const size_t row = (size_t)(ti.row0 + mm);
         uint16_t* yr = y + row * H;
-        yr[j0] = y_encode(acc[0][r], e);
-        yr[j0 + 16] = y_encode(acc[1][r], e);
-        if (nl == 0) ye[row * (H / kYGroup) + (j0 - nl) / kYGroup] = (uint8_t)(e + 127);
+        yr[jc[0]] = y_encode(acc[0][r], e);
+        yr[jc[1]] = y_encode(acc[1][r], e);
+        if (nl == 0) ye[row * (H / kYGroup) + jb / kYGroup] = (uint8_t)(e + 127);
       }
     }
   }

@@ -21,7 +21,12 @@
 //          activations MXFP4 ([rows][64 B] codes + [rows][4] scales) in LDS.
 // Operand layout as in the streaming kernels: lane l supplies row / column
 // l % 16 and K group g = l / 16; its 16 bytes are K-elements [32 g, 32 g + 32)
-// of the chunk.
+// of the chunk.  Here the weights are the A operand and the activation rows
+// the B operand, so D lane l holds strip slots 4 g .. 4 g + 3 of tile row
+// l % 16, and with the native order's strip pairs that is eight consecutive
+// output columns: the epilogues write h and y in 16-byte stores (with the
+// activations as A a lane held one column of four rows, stored 2 bytes at a
+// time).
 #include "common.h"
 #include "kernels.h"
 
@@ -296,7 +301,7 @@ struct TiledGemm {
       for (int mt = 0; mt < NMT; ++mt)
 #pragma unroll
         for (int t = 0; t < 4; ++t)
-          acc[mt][t] = mfma_fp4_16x16x128(av[mt], sa[mt], q[t], s[t], acc[mt][t]);
+          acc[mt][t] = mfma_fp4_16x16x128(q[t], s[t], av[mt], sa[mt], acc[mt][t]);
     } else {
       float scf[4];
 #pragma unroll
@@ -322,7 +327,7 @@ struct TiledGemm {
 #pragma unroll
         for (int mt = 0; mt < NMT; ++mt)
 #pragma unroll
-          for (int t = 0; t < 4; ++t) acc[mt][t] = mfma_bf16_16x16x32(av[cur][mt], bv[cur][t], acc[mt][t]);
+          for (int t = 0; t < 4; ++t) acc[mt][t] = mfma_bf16_16x16x32(bv[cur][t], av[cur][mt], acc[mt][t]);
         if (j < 3) interleave<0, 4 * NMT, 16, NMT>();
         __builtin_amdgcn_sched_barrier(0);    // one scheduling region per K-step
       }
@@ -330,14 +335,18 @@ struct TiledGemm {
   }
 
   // Scheduling groups for one K-step: after each of its NM MFMAs, a share of
-  // the NV conversions and ND LDS reads that prepare the next step.
+  // the NV conversions that prepare the next step; the next step's ND LDS
+  // reads all go right after the first MFMA, so their latency (bank
+  // conflicts included) is covered by the step's remaining MFMAs (spread
+  // evenly they left the last read a few MFMAs before its use: skewed
+  // gate/up 1.401 -> 1.377 ms).
   template <int I, int NM, int NV, int ND>
   __device__ __forceinline__ static void interleave() {
     if constexpr (I < NM) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                 // MFMA
       constexpr int v = (I + 1) * NV / NM - I * NV / NM;
       if constexpr (v > 0) __builtin_amdgcn_sched_group_barrier(0x002, v, 0);   // VALU
-      constexpr int d = (I + 1) * ND / NM - I * ND / NM;
+      constexpr int d = I == 0 ? ND : 0;
       if constexpr (d > 0) __builtin_amdgcn_sched_group_barrier(0x100, d, 0);   // DS read
       interleave<I + 1, NM, NV, ND>();
     }
@@ -585,10 +594,10 @@ __global__ __launch_bounds__(256, KV ? 2 : 1) void gate_up_tiled_kernel(
   auto token = [&](int r) -> uint32_t {
     return min((unsigned)(sorted[ti.row0 + r] / Kp), (unsigned)(T - 1));
   };
-  // workgroup row r (wave r/64, strip (r/16)%4, lane row r%16) -> weight scale row
+  // workgroup row r (wave r/64, strip (r/16)%4, slot r%16) -> weight scale row
   auto wrow = [&](int r) -> uint32_t {
     const int t = (r >> 4) & 3;
-    return rs * (uint32_t)((t < 2 ? 0 : I) + s * 128 + 32 * (r >> 6) + 16 * (t & 1) + (r & 15));
+    return rs * (uint32_t)((t < 2 ? 0 : I) + s * 128 + 32 * (r >> 6) + wnat_row(t & 1, r & 15));
   };
 
   floatx4_t acc[BM / 16][4];
@@ -598,17 +607,23 @@ __global__ __launch_bounds__(256, KV ? 2 : 1) void gate_up_tiled_kernel(
     for (int st = 0; st < 4; ++st) acc[mt][st] = (floatx4_t){0.f, 0.f, 0.f, 0.f};
   tile_loop<BM, kFP4A, kW8, KV, kBlk>(G, ti, token, wrow, kFP4A ? rb : (uint32_t)H * 2, rs, acc);
 
+  // h (bf16): lane 16 g + n holds tile row 16 mt + n at intermediate
+  // columns i0 + 8 g .. i0 + 8 g + 7 (gate strips 0-1, up strips 2-3; strip
+  // u, D row 4 g + r -> column i0 + 8 g + 4 u + r): one 16-byte store.
 #pragma unroll
-  for (int mt = 0; mt < BM / 16; ++mt)
+  for (int mt = 0; mt < BM / 16; ++mt) {
+    const int m = 16 * mt + nl;
+    if (m < ti.rows) {
+      u32x4_t v;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int m = 16 * mt + 4 * g + r;
-      if (m < ti.rows) {
-        uint16_t* hr = h + (size_t)(ti.row0 + m) * I;
-        hr[i0 + nl] = f32_to_bf16_rne(swiglu(acc[mt][0][r], acc[mt][2][r]));
-        hr[i0 + 16 + nl] = f32_to_bf16_rne(swiglu(acc[mt][1][r], acc[mt][3][r]));
+      for (int k = 0; k < 4; ++k) {
+        const int u = k >> 1, r = 2 * (k & 1);
+        v[k] = (uint32_t)f32_to_bf16_rne(swiglu(acc[mt][u][r], acc[mt][2 + u][r])) |
+               (uint32_t)f32_to_bf16_rne(swiglu(acc[mt][u][r + 1], acc[mt][2 + u][r + 1])) << 16;
       }
+      *reinterpret_cast<u32x4_t*>(h + (size_t)(ti.row0 + m) * I + i0 + 8 * g) = v;
     }
+  }
 }
 
 // down: weight rows j in [256 s, 256 s + 256); wave w owns [256 s + 64 w, +64).
@@ -637,7 +652,10 @@ __global__ __launch_bounds__(256, KV ? 2 : 1) void down_tiled_kernel(
     G.a = make_rsrc(hin, (uint32_t)((size_t)A * I * 2));
   }
   auto srow = [&](int r) -> uint32_t { return (uint32_t)(ti.row0 + r); };
-  auto wrow = [&](int r) -> uint32_t { return rs * (uint32_t)(s * 256 + r); };
+  // workgroup row r (wave r/64, strip (r/16)%4, slot r%16) -> weight scale row
+  auto wrow = [&](int r) -> uint32_t {
+    return rs * (uint32_t)(s * 256 + (r & ~31) + wnat_row((r >> 4) & 1, r & 15));
+  };
 
   floatx4_t acc[BM / 16][4];
 #pragma unroll
@@ -646,30 +664,39 @@ __global__ __launch_bounds__(256, KV ? 2 : 1) void down_tiled_kernel(
     for (int st = 0; st < 4; ++st) acc[mt][st] = (floatx4_t){0.f, 0.f, 0.f, 0.f};
   tile_loop<BM, kFP4A, kW8, KV, kBlk>(G, ti, srow, wrow, kFP4A ? rb : (uint32_t)I * 2, rs, acc);
 
-  // y in the staged fp16 format: the wave's 64 columns of a row are two
-  // 32-column groups (strips 0-1 and 2-3), each row held by one 16-lane row
-  // of the wave
+  // y in the staged fp16 format.  Lane 16 g + n holds tile row 16 mt + n at
+  // columns j0 + 32 p + 8 g .. + 7 of strip pair p (strip 2 p + u, D row
+  // 4 g + r -> column j0 + 32 p + 8 g + 4 u + r): one 16-byte store per
+  // pair.  A pair's 32 columns are one exponent group, spread over lanes
+  // n, n + 16, n + 32 and n + 48.
 #pragma unroll
-  for (int mt = 0; mt < BM / 16; ++mt)
+  for (int mt = 0; mt < BM / 16; ++mt) {
+    uint32_t f = 0;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int m = 16 * mt + 4 * g + r;
-      const uint32_t f = row16_max_halves(max_halves(pack_exponents(acc[mt][0][r], acc[mt][2][r]),
-                                                     pack_exponents(acc[mt][1][r], acc[mt][3][r])));
-      const int e0 = y_exponent_of_field(f & 0xFFFFu), e1 = y_exponent_of_field(f >> 16);
-      if (m < ti.rows) {
-        const size_t row = (size_t)(ti.row0 + m);
-        uint16_t* yr = y + row * H + j0 + nl;
-        yr[0] = y_encode(acc[mt][0][r], e0);
-        yr[16] = y_encode(acc[mt][1][r], e0);
-        yr[32] = y_encode(acc[mt][2][r], e1);
-        yr[48] = y_encode(acc[mt][3][r], e1);
-        if (nl == 0) {
-          ye[row * (H / kYGroup) + j0 / kYGroup] = (uint8_t)(e0 + 127);
-          ye[row * (H / kYGroup) + j0 / kYGroup + 1] = (uint8_t)(e1 + 127);
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) f = max_halves(f, pack_exponents(acc[mt][u][r], acc[mt][2 + u][r]));
+    f = xrow_max_halves(f);
+    const int e[2] = {y_exponent_of_field(f & 0xFFFFu), y_exponent_of_field(f >> 16)};
+    const int m = 16 * mt + nl;
+    if (m < ti.rows) {
+      const size_t row = (size_t)(ti.row0 + m);
+#pragma unroll
+      for (int p = 0; p < 2; ++p) {
+        u32x4_t v;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const int u = k >> 1, r = 2 * (k & 1);
+          v[k] = (uint32_t)y_encode(acc[mt][2 * p + u][r], e[p]) |
+                 (uint32_t)y_encode(acc[mt][2 * p + u][r + 1], e[p]) << 16;
         }
+        *reinterpret_cast<u32x4_t*>(y + row * H + j0 + 32 * p + 8 * g) = v;
       }
+      if (g == 0)
+        *reinterpret_cast<uint16_t*>(ye + row * (H / kYGroup) + j0 / kYGroup) =
+            (uint16_t)((e[0] + 127) | (e[1] + 127) << 8);
     }
+  }
 }
 
 template <int BM, bool kFP4A, bool kW8 = false, int KV = 0, bool kBlk = false>

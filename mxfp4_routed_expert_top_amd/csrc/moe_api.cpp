@@ -246,7 +246,7 @@ moe_status moe_mxfp8_quantize(const void* src, int32_t src_dtype, int64_t rows, 
 moe_status moe_weights_to_native(const uint8_t* src, int32_t wfmt, int64_t rows, int64_t cols,
                                  uint8_t* dst, void* stream) {
   if (rows < 0 || cols < 0 || (wfmt != 0 && wfmt != 1)) return MOE_ERR_INVALID_ARGUMENT;
-  if (rows % 16 || cols % 128) return MOE_ERR_UNSUPPORTED;
+  if (rows % 32 || cols % 128) return MOE_ERR_UNSUPPORTED;
   if (rows == 0 || cols == 0) return MOE_OK;
   if (!src || !dst || !aligned16(src) || !aligned16(dst)) return MOE_ERR_INVALID_ARGUMENT;
   const int64_t bytes = rows * (wfmt == 1 ? cols : cols / 2);

@@ -7,8 +7,8 @@
 namespace {
 
 // One thread per destination piece p (16 bytes): p = ((s * nch + c) * NQ +
-// hq) * 64 + l comes from row 16 s + l % 16, code bytes
-// NQ * (64 c + 16 (l / 16)) + 16 hq of the row.
+// hq) * 64 + l comes from row 32 (s / 2) + wnat_row(s % 2, l % 16), code
+// bytes NQ * (64 c + 16 (l / 16)) + 16 hq of the row.
 __global__ __launch_bounds__(256) void weights_native_kernel(const u32x4_t* __restrict__ src,
                                                              int64_t npieces, int nch, int nq,
                                                              int64_t row_bytes,
@@ -21,7 +21,7 @@ __global__ __launch_bounds__(256) void weights_native_kernel(const u32x4_t* __re
     const int64_t sc = blk / nq;
     const int c = (int)(sc % nch);
     const int64_t s = sc / nch;
-    const int64_t row = 16 * s + (l & 15);
+    const int64_t row = 32 * (s >> 1) + wnat_row((int)(s & 1), l & 15);
     const int64_t byte = (int64_t)nq * (64 * c + 16 * (l >> 4)) + 16 * hq;
     dst[p] = src[(row * row_bytes + byte) >> 4];
   }
@@ -29,7 +29,7 @@ __global__ __launch_bounds__(256) void weights_native_kernel(const u32x4_t* __re
 
 }  // namespace
 
-// rows x cols codes (rows a multiple of 16, cols of 128); nq = 1 for MXFP4
+// rows x cols codes (rows a multiple of 32, cols of 128); nq = 1 for MXFP4
 // (cols / 2 bytes per row), 2 for MXFP8 (cols bytes per row).
 hipError_t launch_weights_native(const uint8_t* src, int nq, int64_t rows, int64_t cols,
                                  uint8_t* dst, hipStream_t stream) {

@@ -21,12 +21,13 @@ W_ATOL = 1e-6          # routing weights, absolute
 def native_order(codes: np.ndarray, nq: int) -> np.ndarray:
     """Row-major weight codes [rows, row_bytes] -> the GEMM kernels' native
     code order (the permutation include/moe_mxfp4.h defines), by reshapes:
-    row 16 s + n, byte nq (64 c + 16 g) + 16 q + b  ->  block (s, c, q),
-    lane 16 g + n, byte b.  nq = 1 (MXFP4) or 2 (MXFP8)."""
+    row 32 p + 8 a + 4 u + b, byte nq (64 c + 16 g) + 16 q + j  ->  block
+    (s = 2 p + u, c, q), lane 16 g + 4 a + b, byte j.  nq = 1 (MXFP4) or 2
+    (MXFP8)."""
     rows, rb = codes.shape
     C = rb // (64 * nq)
-    a = codes.reshape(rows // 16, 16, C, 4, nq, 16)      # s, n, c, g, q, b
-    return np.ascontiguousarray(a.transpose(0, 2, 4, 3, 1, 5)).reshape(rows, rb)
+    a = codes.reshape(rows // 32, 4, 2, 4, C, 4, nq, 16)   # p, a, u, b, c, g, q, j
+    return np.ascontiguousarray(a.transpose(0, 2, 4, 6, 5, 1, 3, 7)).reshape(rows, rb)
 
 
 def blocked_order(codes: np.ndarray, scales: np.ndarray):

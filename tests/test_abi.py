@@ -130,7 +130,8 @@ def test_quantize_blocked_argument_errors():
 def test_weights_to_native_argument_errors():
     f = ops.lib().moe_weights_to_native
     B = ctypes.c_void_p(0x200000)                                  # FAKE + 1 MiB
-    assert f(FAKE, 0, 24, 256, B, None) == UNSUPPORTED             # rows % 16
+    assert f(FAKE, 0, 24, 256, B, None) == UNSUPPORTED             # rows % 32
+    assert f(FAKE, 0, 48, 256, B, None) == UNSUPPORTED             # whole strips, not pairs
     assert f(FAKE, 0, 32, 192, B, None) == UNSUPPORTED             # cols % 128
     assert f(FAKE, 2, 32, 256, B, None) == INVALID                 # weight format
     assert f(FAKE, 0, -16, 256, B, None) == INVALID

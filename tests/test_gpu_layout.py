@@ -12,7 +12,7 @@ pytestmark = pytest.mark.gpu
 
 
 @pytest.mark.parametrize("wfmt,rows,cols", [
-    (0, 16, 128),            # one strip, one chunk
+    (0, 32, 128),            # one strip pair, one chunk
     (0, 3 * 64, 384),        # three experts of 64 rows, three chunks
     (1, 32, 256),            # MXFP8: two parts per chunk
     (1, 2 * 48, 640),

@@ -2,10 +2,11 @@
 as the tests' numpy definition (tests/helpers.native_order) writes it,
 against entries worked out by hand from the header's rule: block
 ((s*C + c)*NQ + q) holds at byte 16*l (l = 16*g + n) the row-major bytes of
-row 16*s + n starting at NQ*(64*c + 16*g) + 16*q.  Likewise the blocked row
-order of MXFP4 activations (tests/helpers.blocked_order against the rule of
-moe_mxfp4_quantize_blocked: row p's chunk c at ((p/16)*C + c)*1024 +
-(p%16)*64 for the codes, ((p/16)*C + c)*64 + (p%16)*4 for the scales)."""
+row 32*(s/2) + 8*(n/4) + 4*(s%2) + n%4 starting at NQ*(64*c + 16*g) + 16*q.
+Likewise the blocked row order of MXFP4 activations
+(tests/helpers.blocked_order against the rule of moe_mxfp4_quantize_blocked:
+row p's chunk c at ((p/16)*C + c)*1024 + (p%16)*64 for the codes,
+((p/16)*C + c)*64 + (p%16)*4 for the scales)."""
 import numpy as np
 
 from tests.helpers import blocked_order, native_order
@@ -24,14 +25,19 @@ def _piece(nat, rb, k):
     return divmod(int(flat[0]), rb)
 
 
-def test_mxfp4_one_strip_one_chunk():
+def test_mxfp4_one_strip_pair_one_chunk():
     rb = 64                                    # 128 MXFP4 codes per row: C = 1
-    nat = native_order(_labelled(16, rb), 1)
-    assert _piece(nat, rb, 0) == (0, 0)        # lane 0: n 0, g 0
-    assert _piece(nat, rb, 1) == (1, 0)        # lane 1: n 1, g 0
-    assert _piece(nat, rb, 15) == (15, 0)
+    nat = native_order(_labelled(32, rb), 1)
+    assert _piece(nat, rb, 0) == (0, 0)        # block 0 = strip 0; lane 0: n 0, g 0
+    assert _piece(nat, rb, 1) == (1, 0)        # lane 1: n 1 -> row 1
+    assert _piece(nat, rb, 3) == (3, 0)
+    assert _piece(nat, rb, 4) == (8, 0)        # lane 4: n 4 -> 8*1 + 0
+    assert _piece(nat, rb, 15) == (27, 0)      # n 15 -> 8*3 + 3
     assert _piece(nat, rb, 16) == (0, 16)      # lane 16: n 0, g 1
-    assert _piece(nat, rb, 63) == (15, 48)     # lane 63: n 15, g 3
+    assert _piece(nat, rb, 63) == (27, 48)     # lane 63: n 15, g 3
+    assert _piece(nat, rb, 64) == (4, 0)       # block 1 = strip 1; lane 0 -> 4*1
+    assert _piece(nat, rb, 64 + 5) == (13, 0)  # strip 1, n 5 -> 8 + 4 + 1
+    assert _piece(nat, rb, 64 + 63) == (31, 48)
 
 
 def test_mxfp4_two_strips_two_chunks():
@@ -39,18 +45,27 @@ def test_mxfp4_two_strips_two_chunks():
     nat = native_order(_labelled(32, rb), 1)
     assert _piece(nat, rb, 64) == (0, 64)      # block 1 = (s 0, c 1), lane 0
     assert _piece(nat, rb, 64 + 17) == (1, 80)  # block 1, lane 17: n 1, g 1
-    assert _piece(nat, rb, 128) == (16, 0)     # block 2 = (s 1, c 0), lane 0
+    assert _piece(nat, rb, 128) == (4, 0)      # block 2 = (s 1, c 0), lane 0
     assert _piece(nat, rb, 3 * 64 + 63) == (31, 112)   # block 3 = (s 1, c 1), lane 63
+
+
+def test_mxfp4_second_strip_pair():
+    rb = 64
+    nat = native_order(_labelled(64, rb), 1)
+    assert _piece(nat, rb, 2 * 64) == (32, 0)           # block 2 = strip 2, lane 0
+    assert _piece(nat, rb, 2 * 64 + 6) == (42, 0)       # n 6 -> 32 + 8 + 2
+    assert _piece(nat, rb, 3 * 64 + 32 + 12) == (60, 32)   # strip 3, lane 44: n 12, g 2
 
 
 def test_mxfp8_parts():
     rb = 256                                   # 256 E4M3 codes per row: C = 2, NQ = 2
-    nat = native_order(_labelled(16, rb), 2)
-    assert _piece(nat, rb, 0) == (0, 0)        # block 0 = (c 0, q 0), lane 0
+    nat = native_order(_labelled(32, rb), 2)
+    assert _piece(nat, rb, 0) == (0, 0)        # block 0 = (s 0, c 0, q 0), lane 0
     assert _piece(nat, rb, 64) == (0, 16)      # block 1 = (c 0, q 1), lane 0
     assert _piece(nat, rb, 16) == (0, 32)      # block 0, lane 16: g 1 -> byte 2*16
-    assert _piece(nat, rb, 2 * 64 + 5) == (5, 128)     # block 2 = (c 1, q 0), lane 5
+    assert _piece(nat, rb, 2 * 64 + 5) == (9, 128)     # block 2 = (c 1, q 0), lane 5: n 5
     assert _piece(nat, rb, 3 * 64 + 50) == (2, 128 + 96 + 16)   # block 3 (c 1, q 1), lane 50: n 2, g 3
+    assert _piece(nat, rb, 4 * 64) == (4, 0)   # block 4 = (s 1, c 0, q 0), lane 0
 
 
 def test_is_a_permutation_of_pieces_and_keeps_experts_in_place():
