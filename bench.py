@@ -118,8 +118,9 @@ def gate_up_kernel_name(cfg, tile_m):
         if cfg.act_fmt and tile_m == 128:
             kv = 1 if cfg.H <= 2048 else 2 if cfg.H <= 6144 else 0
         # the forward feeds MXFP4 activations to the tiled kernels in the blocked row order
+        # and then quantises h in the gate/up epilogue
         blk = "true" if cfg.act_fmt else "false"
-        return f"gate_up_tiled_kernel<{tile_m}, {a}, {w8}, {kv}, {blk}>"
+        return f"gate_up_tiled_kernel<{tile_m}, {a}, {w8}, {kv}, {blk}, {blk}>"
     if cfg.wfmt == synth.W_MXFP8:
         return "gate_up_kernel<1, false, true>"
     ph = 2 if (cfg.H // 128) % 2 == 0 else 1          # phase width of the 32-row kernel
@@ -311,7 +312,8 @@ def measure(cfg, args, weights=None, router=False):
 
     def step_stages(events):
         ops.forward_stages(x, logits, gate, w13, w13s, w2, w2s, cfg.I, cfg.E, cfg.K, cfg.shared,
-                           cfg.act_fmt, bufs=bufs, events=events, wfmt=cfg.wfmt)
+                           cfg.act_fmt, bufs=bufs, events=events, wfmt=cfg.wfmt,
+                           fuse_h_quant=True)
 
     for _ in range(args.warmup):
         step()

@@ -77,6 +77,50 @@ __device__ __forceinline__ uint32_t xrow_max_halves(uint32_t v) {
   return max_halves(b[0], b[1]);
 }
 
+// Maximum of v over lanes n, n ^ 16, n ^ 32, n ^ 48, as xrow_max_halves.
+__device__ __forceinline__ uint32_t xrow_max_u32(uint32_t v) {
+  const auto a = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+  v = max(a[0], a[1]);
+  const auto b = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+  return max(b[0], b[1]);
+}
+
+// MXFP4 quantisation (OCP MX v1.0 encoding), per block of 32 values: X =
+// floor(log2 amax) - 2 clamped to [-127, 127] (an all-zero block gives
+// -127); scale byte X + 127; each |v| / 2^X goes to the nearest E2M1
+// magnitude {0, .5, 1, 1.5, 2, 3, 4, 6}, ties to the even code, saturating
+// at 6; the sign bit of v is kept.  All steps are exact in fp32.
+//
+// |v| / 2^X -> E2M1 magnitude code by the midpoints between grid values; at
+// a midpoint the even code wins.
+__device__ __forceinline__ uint32_t e2m1_code(float a) {
+  uint32_t c = 7;
+  c = (a <= 5.0f) ? 6 : c;
+  c = (a < 3.5f) ? 5 : c;
+  c = (a <= 2.5f) ? 4 : c;
+  c = (a < 1.75f) ? 3 : c;
+  c = (a <= 1.25f) ? 2 : c;
+  c = (a < 0.75f) ? 1 : c;
+  c = (a <= 0.25f) ? 0 : c;
+  return c;
+}
+
+// X of a block whose largest magnitude is amax.
+__device__ __forceinline__ int mxfp4_block_exponent(float amax) {
+  return max((int)((__float_as_uint(amax) >> 23) & 0xFF) - 129, -127);
+}
+
+// Eight values of a block with exponent X -> four code bytes (element j in
+// nibble j, low nibble first).
+__device__ __forceinline__ uint32_t mxfp4_codes8(const float (&v)[8], int X) {
+  const float inv = __uint_as_float((uint32_t)(127 - X) << 23);   // 2^-X, a normal float
+  uint32_t w = 0;
+#pragma unroll
+  for (int j = 0; j < 8; ++j)
+    w |= (e2m1_code(fabsf(v[j]) * inv) | ((__float_as_uint(v[j]) >> 31) << 3)) << (4 * j);
+  return w;
+}
+
 // Exponent of a group whose largest biased fp32 exponent field is f:
 // floor(log2 amax) - 14 = f - 141, clamped to [-127, 127] (an all-zero or
 // all-subnormal group gets -127).

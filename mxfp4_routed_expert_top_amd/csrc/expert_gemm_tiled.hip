@@ -564,13 +564,15 @@ __device__ __forceinline__ void tile_loop(TiledGemm<BM, kFP4A, kW8, KV, kBlk>& G
 
 // gate/up + SwiGLU: weight rows gate [i0, i0 + 128) and up [I + i0, I + i0 + 128),
 // i0 = 128 s; wave w owns i in [i0 + 32 w, i0 + 32 w + 32): strips gate lo/hi, up lo/hi.
-template <int BM, bool kFP4A, bool kW8, int KV = 0, bool kBlk = false>
+// kQH: h is written MXFP4-quantised in the blocked row order (hq, hs)
+// instead of as bf16 h.
+template <int BM, bool kFP4A, bool kW8, int KV = 0, bool kBlk = false, bool kQH = false>
 __global__ __launch_bounds__(256, KV ? 2 : 1) void gate_up_tiled_kernel(
     const void* __restrict__ act, const uint8_t* __restrict__ act_scale,
     const int32_t* __restrict__ sorted, const int32_t* __restrict__ offsets,
     const int32_t* __restrict__ tiles, const int32_t* __restrict__ num_tiles,
     const uint8_t* __restrict__ w13, const uint8_t* __restrict__ w13s, int T, int H, int I, int Kp,
-    uint16_t* __restrict__ h) {
+    uint16_t* __restrict__ h, uint8_t* __restrict__ hq, uint8_t* __restrict__ hs) {
   TileT ti;
   int s;
   if (!tile_slice<BM, kFP4A, kBlk ? 4 : 1>(blockIdx.x, tiles, offsets, *num_tiles, I / 128, &ti, &s))
@@ -610,6 +612,35 @@ __global__ __launch_bounds__(256, KV ? 2 : 1) void gate_up_tiled_kernel(
   // h (bf16): lane 16 g + n holds tile row 16 mt + n at intermediate
   // columns i0 + 8 g .. i0 + 8 g + 7 (gate strips 0-1, up strips 2-3; strip
   // u, D row 4 g + r -> column i0 + 8 g + 4 u + r): one 16-byte store.
+  if constexpr (kQH) {
+    // MXFP4 h (the pages fuse the activation and its quantisation): the
+    // wave's 32 columns are one scale block (K-group `wave` of chunk s), its
+    // amax over the lanes n, n + 16, n + 32, n + 48 of the row; each lane
+    // writes the four code bytes of its eight values, lane n the scale.
+    const int C = I / 128;
+#pragma unroll
+    for (int mt = 0; mt < BM / 16; ++mt) {
+      float v[8];
+      uint32_t am = 0;
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const int u = k >> 2, r = k & 3;
+        v[k] = __uint_as_float((uint32_t)f32_to_bf16_rne(swiglu(acc[mt][u][r], acc[mt][2 + u][r]))
+                               << 16);
+        am = max(am, __float_as_uint(v[k]) & 0x7FFFFFFFu);
+      }
+      const int X = mxfp4_block_exponent(__uint_as_float(xrow_max_u32(am)));
+      const uint32_t codes = mxfp4_codes8(v, X);
+      const int m = 16 * mt + nl;
+      if (m < ti.rows) {
+        const size_t p = (size_t)(ti.row0 + m);
+        const size_t blk = (p >> 4) * C + s;
+        *reinterpret_cast<uint32_t*>(hq + blk * 1024 + (p & 15) * 64 + 16 * G.wave + 4 * g) = codes;
+        if (g == 0) hs[blk * 64 + (p & 15) * 4 + G.wave] = (uint8_t)(X + 127);
+      }
+    }
+    return;
+  }
 #pragma unroll
   for (int mt = 0; mt < BM / 16; ++mt) {
     const int m = 16 * mt + nl;
@@ -704,10 +735,18 @@ hipError_t launch_gate_up_bm(const void* act, const uint8_t* act_scale, const in
                              const int32_t* offsets, const int32_t* tiles,
                              const int32_t* num_tiles, int max_tiles, const uint8_t* w13,
                              const uint8_t* w13s, int T, int H, int I, int Kp, uint16_t* h,
-                             hipStream_t stream) {
+                             hipStream_t stream, uint8_t* hq = nullptr, uint8_t* hs = nullptr) {
   const unsigned grid = tile_slice_grid<kFP4A>(max_tiles, I / 128);
+  if constexpr (kBlk) {
+    if (hq) {
+      hipLaunchKernelGGL((gate_up_tiled_kernel<BM, kFP4A, kW8, KV, kBlk, true>), dim3(grid), dim3(256),
+                         0, stream, act, act_scale, sorted, offsets, tiles, num_tiles, w13, w13s, T,
+                         H, I, Kp, h, hq, hs);
+      return hipGetLastError();
+    }
+  }
   hipLaunchKernelGGL((gate_up_tiled_kernel<BM, kFP4A, kW8, KV, kBlk>), dim3(grid), dim3(256), 0, stream, act,
-                     act_scale, sorted, offsets, tiles, num_tiles, w13, w13s, T, H, I, Kp, h);
+                     act_scale, sorted, offsets, tiles, num_tiles, w13, w13s, T, H, I, Kp, h, hq, hs);
   return hipGetLastError();
 }
 
@@ -735,8 +774,8 @@ hipError_t gate_up_fp4(int tile_m, const void* act, const uint8_t* act_scale,
                        const int32_t* sorted, const int32_t* offsets, const int32_t* tiles,
                        const int32_t* num_tiles, int max_tiles, const uint8_t* w13,
                        const uint8_t* w13s, int T, int H, int I, int Kp, uint16_t* h,
-                       hipStream_t stream) {
-#define MOE_GU_ARGS act, act_scale, sorted, offsets, tiles, num_tiles, max_tiles, w13, w13s, T, H, I, Kp, h, stream
+                       hipStream_t stream, uint8_t* hq, uint8_t* hs) {
+#define MOE_GU_ARGS act, act_scale, sorted, offsets, tiles, num_tiles, max_tiles, w13, w13s, T, H, I, Kp, h, stream, hq, hs
   if (tile_m == 256) return launch_gate_up_bm<256, true, false, 0, kBlk>(MOE_GU_ARGS);
   if (tile_m == 128)
     return H <= 2048   ? launch_gate_up_bm<128, true, false, 1, kBlk>(MOE_GU_ARGS)
@@ -782,7 +821,9 @@ hipError_t launch_gate_up_tiled(int tile_m, int act_fmt, int wfmt, const void* a
                                 const int32_t* sorted, const int32_t* offsets,
                                 const int32_t* tiles, const int32_t* num_tiles, int max_tiles,
                                 const uint8_t* w13, const uint8_t* w13s, int T, int H, int I,
-                                int Kp, uint16_t* h, hipStream_t stream) {
+                                int Kp, uint16_t* h, hipStream_t stream, uint8_t* hq,
+                                uint8_t* hs) {
+  if (hq && act_fmt != 2) return hipErrorInvalidValue;
   if (wfmt == 1)
     return tile_m == 128 ? launch_gate_up_bm<128, false, true>(act, act_scale, sorted, offsets, tiles,
                                                                num_tiles, max_tiles, w13, w13s, T,
@@ -792,10 +833,10 @@ hipError_t launch_gate_up_tiled(int tile_m, int act_fmt, int wfmt, const void* a
                                                               I, Kp, h, stream);
   if (act_fmt == 2)
     return gate_up_fp4<true>(tile_m, act, act_scale, sorted, offsets, tiles, num_tiles, max_tiles,
-                             w13, w13s, T, H, I, Kp, h, stream);
+                             w13, w13s, T, H, I, Kp, h, stream, hq, hs);
   if (act_fmt)
     return gate_up_fp4<false>(tile_m, act, act_scale, sorted, offsets, tiles, num_tiles, max_tiles,
-                              w13, w13s, T, H, I, Kp, h, stream);
+                              w13, w13s, T, H, I, Kp, h, stream, nullptr, nullptr);
   return tile_m == 128 ? launch_gate_up_bm<128, false>(act, act_scale, sorted, offsets, tiles,
                                                        num_tiles, max_tiles, w13, w13s, T, H, I, Kp,
                                                        h, stream)

@@ -79,7 +79,11 @@ hipError_t launch_gate_up_tiled(int tile_m, int act_fmt, int wfmt, const void* a
                                 const int32_t* sorted, const int32_t* offsets,
                                 const int32_t* tiles, const int32_t* num_tiles, int max_tiles,
                                 const uint8_t* w13, const uint8_t* w13s, int T, int H, int I,
-                                int Kp, uint16_t* h, hipStream_t stream);
+                                int Kp, uint16_t* h, hipStream_t stream, uint8_t* hq = nullptr,
+                                uint8_t* hs = nullptr);
+// (hq, hs given, blocked MXFP4 activations only: h is written MXFP4-quantised
+// in the blocked row order, as launch_mxfp4_quant_blocked would write it from
+// the bf16 h, and h itself is not written)
 // y in sorted order, as launch_down
 hipError_t launch_down_tiled(int tile_m, int act_fmt, int wfmt, const void* h,
                              const uint8_t* h_scale,

@@ -280,8 +280,10 @@ moe_status gate_up_impl(const void* act, const uint8_t* act_scale, int32_t act_f
                         const int32_t* sorted_assign, const int32_t* expert_offsets,
                         const int32_t* tile_table, const int32_t* num_tiles, int32_t tile_m,
                         const uint8_t* w13, const uint8_t* w13_scale, int32_t T, int32_t H,
-                        int32_t I, int32_t Ep, int32_t Kp, uint16_t* h, void* stream) {
+                        int32_t I, int32_t Ep, int32_t Kp, uint16_t* h, void* stream,
+                        uint8_t* hq = nullptr, uint8_t* hs = nullptr) {
   if (T < 0 || Ep < 1 || Kp < 1 || !act_fmt_ok(act_fmt)) return MOE_ERR_INVALID_ARGUMENT;
+  const bool quant = hq || hs;                              // h written as blocked MXFP4
   moe_status st = check_shape_HI(H, I);
   if (st != MOE_OK) return st;
   const bool blk = act_fmt == MOE_ACT_MXFP4_BLOCKED;
@@ -294,17 +296,18 @@ moe_status gate_up_impl(const void* act, const uint8_t* act_scale, int32_t act_f
     return MOE_ERR_UNSUPPORTED;
   if (T == 0) return MOE_OK;
   if (!act || !sorted_assign || !expert_offsets || !tile_table || !num_tiles || !w13 ||
-      !w13_scale || !h || (act_fmt != MOE_ACT_BF16 && !act_scale))
+      !w13_scale || (quant ? (!hq || !hs) : !h) || (act_fmt != MOE_ACT_BF16 && !act_scale))
     return MOE_ERR_INVALID_ARGUMENT;
   if (!aligned16(act) || !aligned16(w13) || (blk && !aligned16(act_scale)))
     return MOE_ERR_INVALID_ARGUMENT;
+  if (quant && (!aligned16(hq) || !aligned16(hs))) return MOE_ERR_INVALID_ARGUMENT;
   const int64_t mt = max_tiles_for((int64_t)T * Kp, Ep, tile_m);
   if (mt * (I / 16) >= INT32_MAX) return MOE_ERR_UNSUPPORTED;
   hipStream_t s = as_stream(stream);
   if (tile_m != MOE_TILE_M)
     return from_hip(launch_gate_up_tiled(tile_m, act_fmt, wfmt, act, act_scale, sorted_assign,
                                          expert_offsets, tile_table, num_tiles, (int)mt, w13,
-                                         w13_scale, T, H, I, Kp, h, s));
+                                         w13_scale, T, H, I, Kp, h, s, hq, hs));
   return from_hip(launch_gate_up(act_fmt, wfmt, act, act_scale, sorted_assign, expert_offsets,
                                  tile_table, num_tiles, (int)mt, w13, w13_scale, T, H, I, Kp, h,
                                  s));
@@ -353,6 +356,17 @@ moe_status moe_expert_gate_up(const void* act, const uint8_t* act_scale, int32_t
                               int32_t I, int32_t Ep, int32_t Kp, uint16_t* h, void* stream) {
   return gate_up_impl(act, act_scale, act_fmt, 0, sorted_assign, expert_offsets, tile_table,
                       num_tiles, tile_m, w13, w13_scale, T, H, I, Ep, Kp, h, stream);
+}
+
+moe_status moe_expert_gate_up_quant(const void* act, const uint8_t* act_scale,
+                                    const int32_t* sorted_assign, const int32_t* expert_offsets,
+                                    const int32_t* tile_table, const int32_t* num_tiles,
+                                    int32_t tile_m, const uint8_t* w13, const uint8_t* w13_scale,
+                                    int32_t T, int32_t H, int32_t I, int32_t Ep, int32_t Kp,
+                                    uint8_t* h_packed, uint8_t* h_scale, void* stream) {
+  return gate_up_impl(act, act_scale, MOE_ACT_MXFP4_BLOCKED, 0, sorted_assign, expert_offsets,
+                      tile_table, num_tiles, tile_m, w13, w13_scale, T, H, I, Ep, Kp, nullptr,
+                      stream, h_packed, h_scale);
 }
 
 moe_status moe_mxfp8_expert_gate_up(const uint16_t* x, const int32_t* sorted_assign,
@@ -502,15 +516,16 @@ moe_status forward_impl(const uint16_t* x, const float* router_logits,
   }
   const void* a1 = q ? (const void*)xq : (const void*)x;
   const uint8_t* a1s = q ? xs : nullptr;
+  // (blocked W4A4: the gate/up epilogue writes h MXFP4-quantised, no bf16 h)
   e = tm != MOE_TILE_M
           ? launch_gate_up_tiled(tm, gemm_act, wfmt, a1, a1s, sorted, offsets, tiles, ntiles, mt, w13,
-                                 w13_scale, T, H, I, Kp, h, s)
+                                 w13_scale, T, H, I, Kp, h, s, blk ? hq : nullptr,
+                                 blk ? hs : nullptr)
           : launch_gate_up(act_fmt, wfmt, a1, a1s, sorted, offsets, tiles, ntiles, mt, w13,
                            w13_scale, T, H, I, Kp, h, s);
   if (e != hipSuccess) return MOE_ERR_DEVICE;
-  if (q) {
-    e = blk ? launch_mxfp4_quant_blocked(h, 1, A, I, nullptr, 1, A, hq, hs, s)
-            : launch_mxfp4_quant(h, 1, A, I, hq, hs, s);
+  if (q && !blk) {
+    e = launch_mxfp4_quant(h, 1, A, I, hq, hs, s);
     if (e != hipSuccess) return MOE_ERR_DEVICE;
   }
   const void* a2 = q ? (const void*)hq : (const void*)h;

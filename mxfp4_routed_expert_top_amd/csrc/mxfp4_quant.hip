@@ -5,42 +5,26 @@
 // "Optimisation 4": activation + MXFP4 quantisation in one kernel) and for
 // packing float weights.
 //
-// Rule, per block: X = floor(log2 amax) - 2 clamped to [-127, 127] (an
-// all-zero block gives -127); scale byte X + 127; each |v| / 2^X goes to the
-// nearest E2M1 magnitude {0, .5, 1, 1.5, 2, 3, 4, 6}, ties to the even code,
-// saturating at 6; the sign bit of v is kept.  All steps are exact in fp32.
+// Rule: mxfp4_block_exponent, e2m1_code and mxfp4_codes8 in common.h (the
+// tiled gate/up GEMM's fused h quantisation uses the same ones).
 #include "common.h"
 #include "kernels.h"
 
 namespace {
-
-// |v| / 2^X (exact) -> E2M1 magnitude code by the midpoints between grid
-// values; at a midpoint the even code wins.
-__device__ __forceinline__ uint32_t e2m1_code(float a) {
-  uint32_t c = 7;
-  c = (a <= 5.0f) ? 6 : c;
-  c = (a < 3.5f) ? 5 : c;
-  c = (a <= 2.5f) ? 4 : c;
-  c = (a < 1.75f) ? 3 : c;
-  c = (a <= 1.25f) ? 2 : c;
-  c = (a < 0.75f) ? 1 : c;
-  c = (a <= 0.25f) ? 0 : c;
-  return c;
-}
 
 // Quantise 32 values held by one thread.
 __device__ __forceinline__ void quant_block32(const float* v, u32x4_t* packed, uint8_t* scale) {
   float amax = 0.f;
 #pragma unroll
   for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(v[i]));
-  const int ebits = (int)((__float_as_uint(amax) >> 23) & 0xFF);
-  const int X = max(ebits - 129, -127);                       // floor(log2 amax) - 2
-  const float inv = __uint_as_float((uint32_t)(127 - X) << 23);  // 2^-X, a normal float
-  uint32_t w[4] = {0, 0, 0, 0};
+  const int X = mxfp4_block_exponent(amax);
+  uint32_t w[4];
 #pragma unroll
-  for (int i = 0; i < 32; ++i) {
-    uint32_t c = e2m1_code(fabsf(v[i]) * inv) | ((__float_as_uint(v[i]) >> 31) << 3);
-    w[i >> 3] |= c << (4 * (i & 7));
+  for (int q = 0; q < 4; ++q) {
+    float e[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) e[j] = v[8 * q + j];
+    w[q] = mxfp4_codes8(e, X);
   }
   *packed = (u32x4_t){w[0], w[1], w[2], w[3]};
   *scale = (uint8_t)(X + 127);
@@ -121,13 +105,8 @@ __device__ __forceinline__ uint32_t quant8_in_block(const void* src, int64_t e, 
   for (int j = 0; j < 8; ++j) amax = fmaxf(amax, fabsf(v[j]));
   amax = fmaxf(amax, __shfl_xor(amax, 1, MOE_WAVE));
   amax = fmaxf(amax, __shfl_xor(amax, 2, MOE_WAVE));
-  const int ebits = (int)((__float_as_uint(amax) >> 23) & 0xFF);
-  const int X = max(ebits - 129, -127);                       // floor(log2 amax) - 2
-  const float inv = __uint_as_float((uint32_t)(127 - X) << 23);  // 2^-X, a normal float
-  uint32_t w = 0;
-#pragma unroll
-  for (int j = 0; j < 8; ++j)
-    w |= (e2m1_code(fabsf(v[j]) * inv) | ((__float_as_uint(v[j]) >> 31) << 3)) << (4 * j);
+  const int X = mxfp4_block_exponent(amax);
+  const uint32_t w = mxfp4_codes8(v, X);
   *scale = (uint8_t)(X + 127);
   return w;
 }

@@ -43,6 +43,8 @@ _SIGS = {
     "moe_mxfp4_quantize_blocked": (_I32, [_P, _I32, _I64, _I64, _P, _I32, _I64, _P, _P, _P]),
     "moe_expert_gate_up": (_I32, [_P, _P, _I32, _P, _P, _P, _P, _I32, _P, _P, _I32, _I32, _I32,
                                   _I32, _I32, _P, _P]),
+    "moe_expert_gate_up_quant": (_I32, [_P, _P, _P, _P, _P, _P, _I32, _P, _P, _I32, _I32, _I32,
+                                        _I32, _I32, _P, _P, _P]),
     "moe_expert_down": (_I32, [_P, _P, _I32, _P, _P, _P, _I32, _P, _P, _I32, _I32, _I32, _I32,
                                _I32, _P, _P]),
     "moe_combine": (_I32, [_P, _P, _P, _I32, _I32, _I32, _P, _P]),
@@ -311,6 +313,25 @@ def expert_gate_up(act, act_scale, act_fmt: int, align: dict, w13, w13_scale, T:
     return h
 
 
+def expert_gate_up_quant(act, act_scale, align: dict, w13, w13_scale, T: int, H: int, I: int,
+                         Ep: int, Kp: int, h_packed=None, h_scale=None, stream=None):
+    """moe_expert_gate_up_quant (blocked MXFP4 activations) -> (h_packed uint8
+    [R, I/2], h_scale uint8 [R, I/32]) in the blocked row order, R = T*Kp
+    rounded up to 16."""
+    r16 = (T * Kp + 15) // 16 * 16
+    if h_packed is None:
+        h_packed = torch.empty(r16, I // 2, dtype=torch.uint8, device=w13.device)
+    if h_scale is None:
+        h_scale = torch.empty(r16, I // 32, dtype=torch.uint8, device=w13.device)
+    _dt(h_packed, torch.uint8, "h_packed")
+    _dt(h_scale, torch.uint8, "h_scale")
+    _check("moe_expert_gate_up_quant", lib().moe_expert_gate_up_quant(
+        _ptr(act), _ptr(act_scale), _ptr(align["sorted"]), _ptr(align["offsets"]),
+        _ptr(align["tiles"]), _ptr(align["num_tiles"]), align["tile_m"], _ptr(w13),
+        _ptr(w13_scale), T, H, I, Ep, Kp, _ptr(h_packed), _ptr(h_scale), _stream(stream)))
+    return h_packed, h_scale
+
+
 def expert_down(h, h_scale, act_fmt: int, align: dict, w2, w2_scale, T: int, H: int, I: int,
                 Ep: int, Kp: int, y=None, stream=None):
     """moe_expert_down -> staged y (uint8 [staged_y_bytes(T*Kp, H)]), rows in sorted order."""
@@ -508,12 +529,14 @@ def alloc_stages(T: int, H: int, I: int, E: int, K: int, shared: int, act_fmt: i
 
 def forward_stages(x, router_logits, shared_gate_logits, w13, w13_scale, w2, w2_scale, I: int,
                    E: int, K: int, shared: int, act_fmt: int = ACT_BF16, bufs=None, stream=None,
-                   events=None, wfmt: int = W_MXFP4):
+                   events=None, wfmt: int = W_MXFP4, fuse_h_quant: bool = False):
     """The same pass as mxfp4_forward (mxfp8_forward for wfmt = W_MXFP8), one
     C entry point per stage, keeping every intermediate (in `bufs` if given,
     see alloc_stages).  `events`, if given, maps a stage name (route, align,
     quant_x, gate_up, quant_h, down, combine) to a (start, end) pair of
-    torch.cuda.Event recorded around it."""
+    torch.cuda.Event recorded around it.  W4A4 on the tiled kernels writes
+    the bf16 h and quantises it as a stage of its own, unless fuse_h_quant
+    (the forward's own path: moe_expert_gate_up_quant, no bf16 h)."""
     if wfmt == W_MXFP8 and act_fmt != ACT_BF16:
         raise ValueError("MXFP8 weights take bf16 activations")
     T, H = x.shape
@@ -546,15 +569,21 @@ def forward_stages(x, router_logits, shared_gate_logits, w13, w13_scale, w2, w2_
             mxfp4_quantize(x, b["xq"][:T], b["xs"][:T], stream=stream)
         rec("quant_x", 1)
         act, act_s = b["xq"], b["xs"]
+    fused = blk and fuse_h_quant
     rec("gate_up", 0)
     if wfmt == W_MXFP8:
         mxfp8_expert_gate_up(x, b["align"], w13, w13_scale, T, H, I, Ep, Kp, h=b["h"], stream=stream)
+    elif fused:
+        expert_gate_up_quant(act, act_s, b["align"], w13, w13_scale, T, H, I, Ep, Kp,
+                             h_packed=b["hq"], h_scale=b["hs"], stream=stream)
     else:
         expert_gate_up(act, act_s, gemm_act, b["align"], w13, w13_scale, T, H, I, Ep, Kp, h=b["h"],
                        stream=stream)
     rec("gate_up", 1)
     hin, hin_s = b["h"], None
-    if act_fmt == ACT_MXFP4:
+    if fused:
+        hin, hin_s = b["hq"], b["hs"]
+    elif act_fmt == ACT_MXFP4:
         rec("quant_h", 0)
         if blk:
             mxfp4_quantize_blocked(b["h"], packed=b["hq"], scales=b["hs"], stream=stream)

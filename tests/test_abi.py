@@ -26,7 +26,7 @@ def declared_functions():
 def test_library_loads_and_exports_every_declared_symbol():
     lib = ops.lib()
     names = declared_functions()
-    assert len(names) == 24
+    assert len(names) == 25
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(ops.EXPORTS)
@@ -173,6 +173,17 @@ def test_gemm_and_combine_argument_errors():
     # blocked rows of T*K' sorted rows (rounded up to 16), not T tokens
     assert call(gu, base, a2=2, a7=128, a1=FAKE, a10=120000, a11=512, a14=80) == UNSUPPORTED
     assert call(gu, base, a2=1, a7=128, a1=FAKE, a10=120000, a11=512, a14=80, a15=None) == INVALID
+    # gate/up with h quantised in the epilogue: blocked MXFP4 activations, tiled kernels
+    gq = ops.lib().moe_expert_gate_up_quant
+    baseq = [FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 128, FAKE, FAKE, 8, 512, 128, 16, 2, FAKE, FAKE,
+             None]
+    assert call(gq, baseq, a6=32) == UNSUPPORTED                             # 32-row tiles
+    assert call(gq, baseq, a10=384) == UNSUPPORTED                           # H % 256
+    assert call(gq, baseq, a1=None) == INVALID                               # no scales
+    assert call(gq, baseq, a14=None) == INVALID and call(gq, baseq, a15=None) == INVALID
+    assert call(gq, baseq, a14=None, a15=None) == INVALID
+    assert call(gq, baseq, a14=MIS) == INVALID and call(gq, baseq, a15=MIS) == INVALID
+    assert call(gq, baseq, a9=0) == OK
     dn = ops.lib().moe_expert_down
     based = [FAKE, None, 0, FAKE, FAKE, FAKE, 32, FAKE, FAKE, 8, 256, 128, 16, 2, FAKE, None]
     assert call(dn, based, a14=None) == INVALID

@@ -6,7 +6,8 @@ blocked order by tests/helpers.blocked_order (with and without a row map;
 rows nothing maps to keep their bytes), and the tiled GEMMs on blocked
 activations against the same GEMMs on row-major ones (the same products in
 the same order: only where the bytes come from differs), for every tile
-size and reduction-length variant."""
+size and reduction-length variant; and the gate/up GEMM with h quantised in
+its epilogue against the blocked quantiser on its bf16 h."""
 import sys
 
 import numpy as np
@@ -128,6 +129,13 @@ def test_gemms_blocked_equal_row_major(tile_m, T, H, I, E, K):
                              c.I, c.Ep, c.Kp)
     torch.cuda.synchronize()
     assert np.array_equal(bits(h_blk), bits(h_row))
+    # h quantised in the gate/up epilogue == the blocked quantiser on the bf16 h
+    fq, fs = o.expert_gate_up_quant(xb, xbs, al, prob.w13, prob.w13s, c.T, c.H, c.I, c.Ep, c.Kp)
+    qq, qs = o.mxfp4_quantize_blocked(h_blk)
+    torch.cuda.synchronize()
+    fq, fs = unblocked_rows(fq.cpu().numpy(), fs.cpu().numpy())
+    qq, qs = unblocked_rows(qq.cpu().numpy(), qs.cpu().numpy())
+    assert np.array_equal(fq[:A], qq[:A]) and np.array_equal(fs[:A], qs[:A])
     hq, hs = o.mxfp4_quantize(h_row)
     y_row = o.expert_down(hq, hs, o.ACT_MXFP4, al, prob.w2, prob.w2s, c.T, c.H, c.I, c.Ep, c.Kp)
     hb, hbs = o.mxfp4_quantize_blocked(h_row)

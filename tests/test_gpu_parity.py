@@ -390,6 +390,14 @@ def test_layer_full_size(name):
     assert e_rel <= REL_L2[cfg.act_fmt]
     if cfg.act_fmt == synth.ACT_MXFP4:
         _w4a4_from_gpu_h(prob, r, want)
+        if tile_m != 32:       # the forward's own path: h quantised in the gate/up epilogue
+            rf = prob.stages(fuse_h_quant=True)
+            torch.cuda.synchronize()
+            A = cfg.T * cfg.Kp
+            fq, fs = unblocked_rows(rf["hq"].cpu().numpy(), rf["hs"].cpu().numpy())
+            sq, ss = unblocked_rows(r["hq"].cpu().numpy(), r["hs"].cpu().numpy())
+            assert np.array_equal(fq[:A], sq[:A]) and np.array_equal(fs[:A], ss[:A])
+            assert torch.equal(rf["out"], out)
     else:
         assert e_max <= MAX_ABS_RMS
     assert torch.isfinite(out.float()).all()
