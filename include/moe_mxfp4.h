@@ -297,22 +297,22 @@ MOE_API moe_status moe_expert_gate_up(const void *act, const uint8_t *act_scale,
  * The W4A4 gate/up GEMM with the MXFP4 quantisation of h in its epilogue
  * (OpenRelay "Gemma 4 31B on MI355X" post, section "Optimisation 4": one
  * kernel for the activation, the up projection and the MXFP4 quantisation).
- * Computes moe_expert_gate_up's h for act_fmt = MOE_ACT_MXFP4_BLOCKED and
- * writes, instead of the bf16 h, what moe_mxfp4_quantize_blocked (row_map
- * NULL) writes from it: the same bits, without h's round trip through HBM.
- * moe_mxfp4_forward takes this path whenever it runs W4A4 on the tiled
- * kernels.
- *   act ... w13_scale, T ... Kp   as moe_expert_gate_up with MOE_ACT_MXFP4_BLOCKED
+ * Computes moe_expert_gate_up's h and writes, instead of the bf16 h, what
+ * moe_mxfp4_quantize_blocked (row_map NULL) writes from it: the same bits,
+ * without h's round trip through HBM.  moe_mxfp4_forward takes this path
+ * whenever it runs W4A4 on the tiled kernels.
+ *   act_fmt    MOE_ACT_MXFP4 (per-token rows) or MOE_ACT_MXFP4_BLOCKED
+ *   act ... w13_scale, T ... Kp   as moe_expert_gate_up with that act_fmt
  *              (tile_m 64, 128 or 256)
  *   h_packed   out uint8, the blocked order, ceil(T*Kp/16)*16 rows of I/2
  *              bytes (rows from T*Kp on are not written), 16-byte aligned
  *   h_scale    out uint8, the blocked order, same rows of I/32 bytes,
  *              16-byte aligned
- * Errors: as moe_expert_gate_up; INVALID_ARGUMENT also for a null or
- * misaligned h_packed / h_scale.
+ * Errors: as moe_expert_gate_up; INVALID_ARGUMENT also for another act_fmt
+ * or a null or misaligned h_packed / h_scale; UNSUPPORTED for tile_m 32.
  */
 MOE_API moe_status moe_expert_gate_up_quant(const void *act, const uint8_t *act_scale,
-                                    const int32_t *sorted_assign, const int32_t *expert_offsets,
+                                    int32_t act_fmt, const int32_t *sorted_assign, const int32_t *expert_offsets,
                                     const int32_t *tile_table, const int32_t *num_tiles,
                                     int32_t tile_m, const uint8_t *w13, const uint8_t *w13_scale,
                                     int32_t T, int32_t H, int32_t I, int32_t Ep, int32_t Kp,

@@ -737,7 +737,7 @@ hipError_t launch_gate_up_bm(const void* act, const uint8_t* act_scale, const in
                              const uint8_t* w13s, int T, int H, int I, int Kp, uint16_t* h,
                              hipStream_t stream, uint8_t* hq = nullptr, uint8_t* hs = nullptr) {
   const unsigned grid = tile_slice_grid<kFP4A>(max_tiles, I / 128);
-  if constexpr (kBlk) {
+  if constexpr (kFP4A) {
     if (hq) {
       hipLaunchKernelGGL((gate_up_tiled_kernel<BM, kFP4A, kW8, KV, kBlk, true>), dim3(grid), dim3(256),
                          0, stream, act, act_scale, sorted, offsets, tiles, num_tiles, w13, w13s, T,
@@ -823,7 +823,7 @@ hipError_t launch_gate_up_tiled(int tile_m, int act_fmt, int wfmt, const void* a
                                 const uint8_t* w13, const uint8_t* w13s, int T, int H, int I,
                                 int Kp, uint16_t* h, hipStream_t stream, uint8_t* hq,
                                 uint8_t* hs) {
-  if (hq && act_fmt != 2) return hipErrorInvalidValue;
+  if (hq && !act_fmt) return hipErrorInvalidValue;
   if (wfmt == 1)
     return tile_m == 128 ? launch_gate_up_bm<128, false, true>(act, act_scale, sorted, offsets, tiles,
                                                                num_tiles, max_tiles, w13, w13s, T,
@@ -836,7 +836,7 @@ hipError_t launch_gate_up_tiled(int tile_m, int act_fmt, int wfmt, const void* a
                              w13, w13s, T, H, I, Kp, h, stream, hq, hs);
   if (act_fmt)
     return gate_up_fp4<false>(tile_m, act, act_scale, sorted, offsets, tiles, num_tiles, max_tiles,
-                              w13, w13s, T, H, I, Kp, h, stream, nullptr, nullptr);
+                              w13, w13s, T, H, I, Kp, h, stream, hq, hs);
   return tile_m == 128 ? launch_gate_up_bm<128, false>(act, act_scale, sorted, offsets, tiles,
                                                        num_tiles, max_tiles, w13, w13s, T, H, I, Kp,
                                                        h, stream)

@@ -81,7 +81,7 @@ hipError_t launch_gate_up_tiled(int tile_m, int act_fmt, int wfmt, const void* a
                                 const uint8_t* w13, const uint8_t* w13s, int T, int H, int I,
                                 int Kp, uint16_t* h, hipStream_t stream, uint8_t* hq = nullptr,
                                 uint8_t* hs = nullptr);
-// (hq, hs given, blocked MXFP4 activations only: h is written MXFP4-quantised
+// (hq, hs given, MXFP4 activations only: h is written MXFP4-quantised
 // in the blocked row order, as launch_mxfp4_quant_blocked would write it from
 // the bf16 h, and h itself is not written)
 // y in sorted order, as launch_down

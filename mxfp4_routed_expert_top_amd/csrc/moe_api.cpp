@@ -358,15 +358,17 @@ moe_status moe_expert_gate_up(const void* act, const uint8_t* act_scale, int32_t
                       num_tiles, tile_m, w13, w13_scale, T, H, I, Ep, Kp, h, stream);
 }
 
-moe_status moe_expert_gate_up_quant(const void* act, const uint8_t* act_scale,
+moe_status moe_expert_gate_up_quant(const void* act, const uint8_t* act_scale, int32_t act_fmt,
                                     const int32_t* sorted_assign, const int32_t* expert_offsets,
                                     const int32_t* tile_table, const int32_t* num_tiles,
                                     int32_t tile_m, const uint8_t* w13, const uint8_t* w13_scale,
                                     int32_t T, int32_t H, int32_t I, int32_t Ep, int32_t Kp,
                                     uint8_t* h_packed, uint8_t* h_scale, void* stream) {
-  return gate_up_impl(act, act_scale, MOE_ACT_MXFP4_BLOCKED, 0, sorted_assign, expert_offsets,
-                      tile_table, num_tiles, tile_m, w13, w13_scale, T, H, I, Ep, Kp, nullptr,
-                      stream, h_packed, h_scale);
+  if (act_fmt != MOE_ACT_MXFP4 && act_fmt != MOE_ACT_MXFP4_BLOCKED) return MOE_ERR_INVALID_ARGUMENT;
+  if (tile_m == MOE_TILE_M) return MOE_ERR_UNSUPPORTED;
+  return gate_up_impl(act, act_scale, act_fmt, 0, sorted_assign, expert_offsets, tile_table,
+                      num_tiles, tile_m, w13, w13_scale, T, H, I, Ep, Kp, nullptr, stream,
+                      h_packed, h_scale);
 }
 
 moe_status moe_mxfp8_expert_gate_up(const uint16_t* x, const int32_t* sorted_assign,

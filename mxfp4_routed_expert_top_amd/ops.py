@@ -43,8 +43,8 @@ _SIGS = {
     "moe_mxfp4_quantize_blocked": (_I32, [_P, _I32, _I64, _I64, _P, _I32, _I64, _P, _P, _P]),
     "moe_expert_gate_up": (_I32, [_P, _P, _I32, _P, _P, _P, _P, _I32, _P, _P, _I32, _I32, _I32,
                                   _I32, _I32, _P, _P]),
-    "moe_expert_gate_up_quant": (_I32, [_P, _P, _P, _P, _P, _P, _I32, _P, _P, _I32, _I32, _I32,
-                                        _I32, _I32, _P, _P, _P]),
+    "moe_expert_gate_up_quant": (_I32, [_P, _P, _I32, _P, _P, _P, _P, _I32, _P, _P, _I32, _I32,
+                                        _I32, _I32, _I32, _P, _P, _P]),
     "moe_expert_down": (_I32, [_P, _P, _I32, _P, _P, _P, _I32, _P, _P, _I32, _I32, _I32, _I32,
                                _I32, _P, _P]),
     "moe_combine": (_I32, [_P, _P, _P, _I32, _I32, _I32, _P, _P]),
@@ -314,10 +314,11 @@ def expert_gate_up(act, act_scale, act_fmt: int, align: dict, w13, w13_scale, T:
 
 
 def expert_gate_up_quant(act, act_scale, align: dict, w13, w13_scale, T: int, H: int, I: int,
-                         Ep: int, Kp: int, h_packed=None, h_scale=None, stream=None):
-    """moe_expert_gate_up_quant (blocked MXFP4 activations) -> (h_packed uint8
-    [R, I/2], h_scale uint8 [R, I/32]) in the blocked row order, R = T*Kp
-    rounded up to 16."""
+                         Ep: int, Kp: int, h_packed=None, h_scale=None, stream=None,
+                         act_fmt: int = ACT_MXFP4_BLOCKED):
+    """moe_expert_gate_up_quant (MXFP4 activations, blocked or per token) ->
+    (h_packed uint8 [R, I/2], h_scale uint8 [R, I/32]) in the blocked row
+    order, R = T*Kp rounded up to 16."""
     r16 = (T * Kp + 15) // 16 * 16
     if h_packed is None:
         h_packed = torch.empty(r16, I // 2, dtype=torch.uint8, device=w13.device)
@@ -326,7 +327,7 @@ def expert_gate_up_quant(act, act_scale, align: dict, w13, w13_scale, T: int, H:
     _dt(h_packed, torch.uint8, "h_packed")
     _dt(h_scale, torch.uint8, "h_scale")
     _check("moe_expert_gate_up_quant", lib().moe_expert_gate_up_quant(
-        _ptr(act), _ptr(act_scale), _ptr(align["sorted"]), _ptr(align["offsets"]),
+        _ptr(act), _ptr(act_scale), act_fmt, _ptr(align["sorted"]), _ptr(align["offsets"]),
         _ptr(align["tiles"]), _ptr(align["num_tiles"]), align["tile_m"], _ptr(w13),
         _ptr(w13_scale), T, H, I, Ep, Kp, _ptr(h_packed), _ptr(h_scale), _stream(stream)))
     return h_packed, h_scale

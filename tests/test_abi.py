@@ -175,15 +175,17 @@ def test_gemm_and_combine_argument_errors():
     assert call(gu, base, a2=1, a7=128, a1=FAKE, a10=120000, a11=512, a14=80, a15=None) == INVALID
     # gate/up with h quantised in the epilogue: blocked MXFP4 activations, tiled kernels
     gq = ops.lib().moe_expert_gate_up_quant
-    baseq = [FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 128, FAKE, FAKE, 8, 512, 128, 16, 2, FAKE, FAKE,
-             None]
-    assert call(gq, baseq, a6=32) == UNSUPPORTED                             # 32-row tiles
-    assert call(gq, baseq, a10=384) == UNSUPPORTED                           # H % 256
+    baseq = [FAKE, FAKE, 2, FAKE, FAKE, FAKE, FAKE, 128, FAKE, FAKE, 8, 512, 128, 16, 2, FAKE,
+             FAKE, None]
+    assert call(gq, baseq, a7=32) == UNSUPPORTED                             # 32-row tiles
+    assert call(gq, baseq, a7=32, a2=1) == UNSUPPORTED
+    assert call(gq, baseq, a2=0) == INVALID and call(gq, baseq, a2=3) == INVALID   # bf16 / none
+    assert call(gq, baseq, a11=384) == UNSUPPORTED                           # H % 256
     assert call(gq, baseq, a1=None) == INVALID                               # no scales
-    assert call(gq, baseq, a14=None) == INVALID and call(gq, baseq, a15=None) == INVALID
-    assert call(gq, baseq, a14=None, a15=None) == INVALID
-    assert call(gq, baseq, a14=MIS) == INVALID and call(gq, baseq, a15=MIS) == INVALID
-    assert call(gq, baseq, a9=0) == OK
+    assert call(gq, baseq, a15=None) == INVALID and call(gq, baseq, a16=None) == INVALID
+    assert call(gq, baseq, a15=None, a16=None) == INVALID
+    assert call(gq, baseq, a15=MIS) == INVALID and call(gq, baseq, a16=MIS) == INVALID
+    assert call(gq, baseq, a10=0) == OK and call(gq, baseq, a10=0, a2=1) == OK
     dn = ops.lib().moe_expert_down
     based = [FAKE, None, 0, FAKE, FAKE, FAKE, 32, FAKE, FAKE, 8, 256, 128, 16, 2, FAKE, None]
     assert call(dn, based, a14=None) == INVALID

@@ -133,9 +133,14 @@ def test_gemms_blocked_equal_row_major(tile_m, T, H, I, E, K):
     fq, fs = o.expert_gate_up_quant(xb, xbs, al, prob.w13, prob.w13s, c.T, c.H, c.I, c.Ep, c.Kp)
     qq, qs = o.mxfp4_quantize_blocked(h_blk)
     torch.cuda.synchronize()
+    pq, ps = o.expert_gate_up_quant(xq, xs, al, prob.w13, prob.w13s, c.T, c.H, c.I, c.Ep, c.Kp,
+                                    act_fmt=o.ACT_MXFP4)     # per-token activation rows
+    torch.cuda.synchronize()
     fq, fs = unblocked_rows(fq.cpu().numpy(), fs.cpu().numpy())
+    pq, ps = unblocked_rows(pq.cpu().numpy(), ps.cpu().numpy())
     qq, qs = unblocked_rows(qq.cpu().numpy(), qs.cpu().numpy())
     assert np.array_equal(fq[:A], qq[:A]) and np.array_equal(fs[:A], qs[:A])
+    assert np.array_equal(pq[:A], qq[:A]) and np.array_equal(ps[:A], qs[:A])
     hq, hs = o.mxfp4_quantize(h_row)
     y_row = o.expert_down(hq, hs, o.ACT_MXFP4, al, prob.w2, prob.w2s, c.T, c.H, c.I, c.Ep, c.Kp)
     hb, hbs = o.mxfp4_quantize_blocked(h_row)
