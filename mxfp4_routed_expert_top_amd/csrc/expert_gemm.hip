@@ -22,8 +22,9 @@
 // gate_up: rows [0, I) of W13 are the gate projection, rows [I, 2I) the up
 // projection; a wave owns 16 intermediate columns i and both projections, so
 // SwiGLU h = silu(gate) * up runs in registers and h is stored as bf16 in
-// the sorted row order.  down: a wave owns 32 output columns j; y is stored
-// as bf16 in the sorted row order.
+// the sorted row order.  down: a wave owns 32 output columns j (one
+// exponent group); y is stored in the staged fp16 format of common.h in the
+// sorted row order.
 #include "common.h"
 #include "kernels.h"
 
