@@ -113,8 +113,8 @@ unsigned tile_slice_grid(int max_tiles, int nslices) {
 // Per-configuration constants.  NS: pipeline stages.  KMAX: the largest
 // reduction length whose scales fit the LDS left over by the stages (256
 // weight rows x KMAX/32 bytes, plus the tile's activation rows for MXFP4).
-// Totals: bf16 128-row 160 KiB (one workgroup per CU), bf16 64-row 80 KiB
-// (two per CU), MXFP4 256-row 145 KiB (three stages), MXFP4 128-row
+// Totals: bf16 128-row 128 KiB (one 8-wave workgroup per CU; MXFP8 weights
+// 160 KiB), bf16 64-row 80 KiB (two per CU), MXFP4 256-row 145 KiB (three stages), MXFP4 128-row
 // 128 KiB (48.5 KiB for reductions up to 2048: two per CU), MXFP4 64-row
 // 76 KiB (two per CU).  256-row tiles exist for MXFP4
 // activations only: an expert of the W4A4 batch (~143 rows) then streams its
@@ -137,8 +137,14 @@ struct TileCfg {
   // blocks: per block and chunk 1 KiB of codes and 64 bytes of scales, each
   // contiguous); their scales then always come with each stage
   static_assert(!kBlk || kFP4A, "blocked rows: MXFP4 activations");
+  // bf16 activations and MXFP4 weights at 128 rows: two 64-row halves, each
+  // on four waves with the weight strips of the 64-row tile (8 waves, one
+  // workgroup per CU: the same two waves per SIMD as two 64-row workgroups,
+  // but one weight fetch for the 128 rows)
+  static constexpr bool kM2 = BM == 128 && !kFP4A && !kW8;
+  static constexpr int kThreads = kM2 ? 512 : 256;
   static constexpr int NS =
-      ((BM == 64 && !kFP4A) || BM == 256 || (kW8 && BM == 128) || (KV && BM == 128)) ? 3 : 4;
+      ((BM == 64 && !kFP4A) || BM == 256 || (kW8 && BM == 128) || (KV && BM == 128) || kM2) ? 3 : 4;
   static constexpr int KMAX =
       KV == 1 ? 2048 : KV == 2 ? 6144 : kFP4A ? (BM == 128 ? 8192 : 6144) : 4096;
   static constexpr int SCB = 256 * (KMAX / 32);             // weight scales
@@ -209,8 +215,10 @@ template <int BM, bool kFP4A, bool kW8 = false, int KV = 0, bool kBlk = false>
 struct TiledGemm {
   static constexpr int NS = TileCfg<BM, kFP4A, kW8, KV, kBlk>::NS;
   static constexpr int XB = TileCfg<BM, kFP4A, kW8, KV, kBlk>::XB;
-  static constexpr int MT = BM / 16;
-  static constexpr int XI = kFP4A ? BM / 64 : BM / 16;   // code / row loads per wave per stage
+  static constexpr bool kM2 = TileCfg<BM, kFP4A, kW8, KV, kBlk>::kM2;
+  static constexpr int MT = kM2 ? 4 : BM / 16;           // 16-row sub-tiles per wave
+  // code / row loads per wave per stage (kM2: the 128 rows over 8 waves)
+  static constexpr int XI = kFP4A ? BM / 64 : kM2 ? BM / 32 : BM / 16;
   // weight registers per strip and stage: 16 bytes (32 E2M1 codes) or 32 (32 E4M3 codes)
   static constexpr int NQ = kW8 ? 2 : 1;
   static constexpr bool kAS = KV == 2 || kBlk;            // activation scales per stage
@@ -221,9 +229,10 @@ struct TiledGemm {
   rsrc_t w, ws, a, as;
   uint32_t wo[4];               // lane's offsets in its four weight strips (native code order)
   uint32_t xo[XI];              // lane's activation source offsets (or kOOR)
-  uint32_t sro;                 // lane's scale byte offset in LDS for strip 0 (row 64 wave + nl, + g)
+  uint32_t sro;                 // lane's scale byte offset in LDS for strip 0 (row 64 wv + nl, + g)
   uint32_t aso;                 // (kAS) lane's activation scale row offset, or kOOR
   int wave, lane, nl, g, nch, Q, swz;
+  int wv, half;                 // weight rows [64 wv, 64 wv + 64); tile rows from 64 half (kM2)
   bool stream;                  // weights read once: non-temporal loads
 
   // Scale rows (Q dwords each, whole K) into LDS: wave w fills rows
@@ -379,7 +388,7 @@ struct TiledGemm {
   __device__ __forceinline__ void run(uint8_t* const (&stages)[NS], uint8_t* sc, uint8_t* asc,
                                       WRow wrow, ARow arow, floatx4_t (&acc)[MT][4]) {
     u32x4_t q[NS][4 * NQ];
-    stage_rows<64>(sc, ws, wrow);
+    if (wave < 4) stage_rows<64>(sc, ws, wrow);
     // kAS: slot u's activation scales at asc + 4 BM u (waves w < BM / 64
     // load rows 64 w + lane; the others write zeros past the slots)
     auto aslot = [&](int u) -> uint8_t* { return kAS ? asc + 4 * BM * u : asc; };
@@ -400,7 +409,7 @@ struct TiledGemm {
         wait_vmcnt<LPS * (NS - 2)>();
         stage_barrier();
         issue(stages[(u + NS - 1) % NS], c + NS - 1, q[(u + NS - 1) % NS], adst((u + NS - 1) % NS));
-        if (c < nch) compute<NMT>(stages[u], sc, aslot(u), c, q[u], acc);
+        if (c < nch) compute<NMT>(stages[u] + half * 64 * 256, sc, aslot(u), c, q[u], acc);
       }
     }
     wait_vmcnt<0>();
@@ -442,12 +451,14 @@ __device__ __forceinline__ void setup(TiledGemm<BM, kFP4A, kW8, KV, kBlk>& G, co
                                       const uint8_t* wq, const uint8_t* wsc, int wrows) {
   G.lane = threadIdx.x & 63;
   G.wave = threadIdx.x >> 6;
+  G.wv = G.wave & 3;
+  G.half = G.wave >> 2;                     // 0 unless kM2 (8 waves)
   G.nl = G.lane & 15;
   G.g = G.lane >> 4;
   G.nch = K / 128;
   G.Q = K / 128;
   G.swz = scale_swizzle(G.nl, G.Q);
-  G.sro = 4 * (64 * G.wave + G.nl) * G.Q + G.g;
+  G.sro = 4 * (64 * G.wv + G.nl) * G.Q + G.g;
   const size_t wbytes = (size_t)wrows * (kW8 ? K : K / 2), sbytes = (size_t)wrows * (K / 32);
   G.w = make_rsrc(wq + ti.expert * wbytes, (uint32_t)wbytes);
   // The expert's only tile with bf16 activations streams its weights
@@ -529,7 +540,7 @@ __device__ __forceinline__ void with_lds(Body&& body) {
 template <int BM, bool kFP4A, bool kW8, int KV, bool kBlk, class Direct, class WRow>
 __device__ __forceinline__ void tile_loop(TiledGemm<BM, kFP4A, kW8, KV, kBlk>& G, const TileT& ti, Direct direct,
                                           WRow wrow, uint32_t row_bytes, uint32_t arow_bytes,
-                                          floatx4_t (&acc)[BM / 16][4]) {
+                                          floatx4_t (&acc)[TiledGemm<BM, kFP4A, kW8, KV, kBlk>::MT][4]) {
   with_lds<BM, kFP4A, kW8, KV, kBlk>([&](auto& stages, uint8_t* sc, uint8_t* asc, int32_t* srow) {
     if constexpr (kBlk) {
       plan_x<BM, kFP4A, kW8, KV, kBlk>(G, ti, direct, row_bytes);
@@ -552,6 +563,13 @@ __device__ __forceinline__ void tile_loop(TiledGemm<BM, kFP4A, kW8, KV, kBlk>& G
       with_nmt<BM>(ti.rows, [&](auto n) {
         G.template run<decltype(n)::value>(stages, sc, asc, wrow, arow, acc);
       });
+    } else if constexpr (TiledGemm<BM, kFP4A, kW8, KV, kBlk>::kM2) {
+      plan_x<BM, kFP4A, kW8, KV, kBlk>(G, ti, direct, row_bytes);
+      auto arow = [](int) -> uint32_t { return kOOR; };
+      // each half's live sub-tiles (a half with no rows runs one on zeros)
+      with_nmt<64>(max(0, ti.rows - 64 * G.half), [&](auto n) {
+        G.template run<decltype(n)::value>(stages, sc, asc, wrow, arow, acc);
+      });
     } else {
       plan_x<BM, kFP4A, kW8, KV, kBlk>(G, ti, direct, row_bytes);
       auto arow = [](int) -> uint32_t { return kOOR; };
@@ -567,7 +585,7 @@ __device__ __forceinline__ void tile_loop(TiledGemm<BM, kFP4A, kW8, KV, kBlk>& G
 // kQH: h is written MXFP4-quantised in the blocked row order (hq, hs)
 // instead of as bf16 h.
 template <int BM, bool kFP4A, bool kW8, int KV = 0, bool kBlk = false, bool kQH = false>
-__global__ __launch_bounds__(256, KV ? 2 : 1) void gate_up_tiled_kernel(
+__global__ __launch_bounds__((TileCfg<BM, kFP4A, kW8, KV, kBlk>::kThreads), KV ? 2 : 1) void gate_up_tiled_kernel(
     const void* __restrict__ act, const uint8_t* __restrict__ act_scale,
     const int32_t* __restrict__ sorted, const int32_t* __restrict__ offsets,
     const int32_t* __restrict__ tiles, const int32_t* __restrict__ num_tiles,
@@ -581,10 +599,12 @@ __global__ __launch_bounds__(256, KV ? 2 : 1) void gate_up_tiled_kernel(
   setup(G, ti, H, w13, w13s, 2 * I);
   const int nl = G.nl, g = G.g;
   const uint32_t rb = H / 2, rs = H / 32;
-  const int i0 = s * 128 + G.wave * 32;
+  const int i0 = s * 128 + G.wv * 32;
   const int rows4[4] = {i0 + nl, i0 + 16 + nl, I + i0 + nl, I + i0 + 16 + nl};
+  // (a 128-row tile's upper half with no rows loads no weights)
+  const bool idle = G.kM2 && ti.rows <= 64 * G.half;
 #pragma unroll
-  for (int st = 0; st < 4; ++st) G.wo[st] = wnat_lane(rows4[st] >> 4, H, G.NQ, G.lane);
+  for (int st = 0; st < 4; ++st) G.wo[st] = idle ? kOOR : wnat_lane(rows4[st] >> 4, H, G.NQ, G.lane);
   if (kFP4A) {
     // per token, or (blocked) per sorted row in whole 16-row blocks
     const size_t nr = kBlk ? ((size_t)T * Kp + 15) / 16 * 16 : (size_t)T;
@@ -602,24 +622,26 @@ __global__ __launch_bounds__(256, KV ? 2 : 1) void gate_up_tiled_kernel(
     return rs * (uint32_t)((t < 2 ? 0 : I) + s * 128 + 32 * (r >> 6) + wnat_row(t & 1, r & 15));
   };
 
-  floatx4_t acc[BM / 16][4];
+  constexpr int MT = TiledGemm<BM, kFP4A, kW8, KV, kBlk>::MT;
+  floatx4_t acc[MT][4];
 #pragma unroll
-  for (int mt = 0; mt < BM / 16; ++mt)
+  for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
     for (int st = 0; st < 4; ++st) acc[mt][st] = (floatx4_t){0.f, 0.f, 0.f, 0.f};
   tile_loop<BM, kFP4A, kW8, KV, kBlk>(G, ti, token, wrow, kFP4A ? rb : (uint32_t)H * 2, rs, acc);
+  const int m0 = 64 * G.half;               // the wave's first tile row
 
   // h (bf16): lane 16 g + n holds tile row 16 mt + n at intermediate
   // columns i0 + 8 g .. i0 + 8 g + 7 (gate strips 0-1, up strips 2-3; strip
   // u, D row 4 g + r -> column i0 + 8 g + 4 u + r): one 16-byte store.
   if constexpr (kQH) {
     // MXFP4 h (the pages fuse the activation and its quantisation): the
-    // wave's 32 columns are one scale block (K-group `wave` of chunk s), its
+    // wave's 32 columns are one scale block (K-group `wv` of chunk s), its
     // amax over the lanes n, n + 16, n + 32, n + 48 of the row; each lane
     // writes the four code bytes of its eight values, lane n the scale.
     const int C = I / 128;
 #pragma unroll
-    for (int mt = 0; mt < BM / 16; ++mt) {
+    for (int mt = 0; mt < MT; ++mt) {
       float v[8];
       uint32_t am = 0;
 #pragma unroll
@@ -631,19 +653,19 @@ __global__ __launch_bounds__(256, KV ? 2 : 1) void gate_up_tiled_kernel(
       }
       const int X = mxfp4_block_exponent(__uint_as_float(xrow_max_u32(am)));
       const uint32_t codes = mxfp4_codes8(v, X);
-      const int m = 16 * mt + nl;
+      const int m = m0 + 16 * mt + nl;
       if (m < ti.rows) {
         const size_t p = (size_t)(ti.row0 + m);
         const size_t blk = (p >> 4) * C + s;
-        *reinterpret_cast<uint32_t*>(hq + blk * 1024 + (p & 15) * 64 + 16 * G.wave + 4 * g) = codes;
-        if (g == 0) hs[blk * 64 + (p & 15) * 4 + G.wave] = (uint8_t)(X + 127);
+        *reinterpret_cast<uint32_t*>(hq + blk * 1024 + (p & 15) * 64 + 16 * G.wv + 4 * g) = codes;
+        if (g == 0) hs[blk * 64 + (p & 15) * 4 + G.wv] = (uint8_t)(X + 127);
       }
     }
     return;
   }
 #pragma unroll
-  for (int mt = 0; mt < BM / 16; ++mt) {
-    const int m = 16 * mt + nl;
+  for (int mt = 0; mt < MT; ++mt) {
+    const int m = m0 + 16 * mt + nl;
     if (m < ti.rows) {
       u32x4_t v;
 #pragma unroll
@@ -659,7 +681,7 @@ __global__ __launch_bounds__(256, KV ? 2 : 1) void gate_up_tiled_kernel(
 
 // down: weight rows j in [256 s, 256 s + 256); wave w owns [256 s + 64 w, +64).
 template <int BM, bool kFP4A, bool kW8, int KV = 0, bool kBlk = false>
-__global__ __launch_bounds__(256, KV ? 2 : 1) void down_tiled_kernel(
+__global__ __launch_bounds__((TileCfg<BM, kFP4A, kW8, KV, kBlk>::kThreads), KV ? 2 : 1) void down_tiled_kernel(
     const void* __restrict__ hin, const uint8_t* __restrict__ hscale,
     const int32_t* __restrict__ offsets, const int32_t* __restrict__ tiles,
     const int32_t* __restrict__ num_tiles, const uint8_t* __restrict__ w2,
@@ -672,9 +694,10 @@ __global__ __launch_bounds__(256, KV ? 2 : 1) void down_tiled_kernel(
   setup(G, ti, I, w2, w2s, H);
   const int nl = G.nl, g = G.g;
   const uint32_t rb = I / 2, rs = I / 32;
-  const int j0 = s * 256 + G.wave * 64;
+  const int j0 = s * 256 + G.wv * 64;
+  const bool idle = G.kM2 && ti.rows <= 64 * G.half;   // an upper half with no rows
 #pragma unroll
-  for (int st = 0; st < 4; ++st) G.wo[st] = wnat_lane((j0 >> 4) + st, I, G.NQ, G.lane);
+  for (int st = 0; st < 4; ++st) G.wo[st] = idle ? kOOR : wnat_lane((j0 >> 4) + st, I, G.NQ, G.lane);
   if (kFP4A) {
     const size_t nr = kBlk ? ((size_t)A + 15) / 16 * 16 : (size_t)A;
     G.a = make_rsrc(hin, (uint32_t)(nr * rb));
@@ -688,12 +711,14 @@ __global__ __launch_bounds__(256, KV ? 2 : 1) void down_tiled_kernel(
     return rs * (uint32_t)(s * 256 + (r & ~31) + wnat_row((r >> 4) & 1, r & 15));
   };
 
-  floatx4_t acc[BM / 16][4];
+  constexpr int MT = TiledGemm<BM, kFP4A, kW8, KV, kBlk>::MT;
+  floatx4_t acc[MT][4];
 #pragma unroll
-  for (int mt = 0; mt < BM / 16; ++mt)
+  for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
     for (int st = 0; st < 4; ++st) acc[mt][st] = (floatx4_t){0.f, 0.f, 0.f, 0.f};
   tile_loop<BM, kFP4A, kW8, KV, kBlk>(G, ti, srow, wrow, kFP4A ? rb : (uint32_t)I * 2, rs, acc);
+  const int m0 = 64 * G.half;               // the wave's first tile row
 
   // y in the staged fp16 format.  Lane 16 g + n holds tile row 16 mt + n at
   // columns j0 + 32 p + 8 g .. + 7 of strip pair p (strip 2 p + u, D row
@@ -701,7 +726,7 @@ __global__ __launch_bounds__(256, KV ? 2 : 1) void down_tiled_kernel(
   // pair.  A pair's 32 columns are one exponent group, spread over lanes
   // n, n + 16, n + 32 and n + 48.
 #pragma unroll
-  for (int mt = 0; mt < BM / 16; ++mt) {
+  for (int mt = 0; mt < MT; ++mt) {
     uint32_t f = 0;
 #pragma unroll
     for (int u = 0; u < 2; ++u)
@@ -709,7 +734,7 @@ __global__ __launch_bounds__(256, KV ? 2 : 1) void down_tiled_kernel(
       for (int r = 0; r < 4; ++r) f = max_halves(f, pack_exponents(acc[mt][u][r], acc[mt][2 + u][r]));
     f = xrow_max_halves(f);
     const int e[2] = {y_exponent_of_field(f & 0xFFFFu), y_exponent_of_field(f >> 16)};
-    const int m = 16 * mt + nl;
+    const int m = m0 + 16 * mt + nl;
     if (m < ti.rows) {
       const size_t row = (size_t)(ti.row0 + m);
 #pragma unroll
@@ -739,13 +764,15 @@ hipError_t launch_gate_up_bm(const void* act, const uint8_t* act_scale, const in
   const unsigned grid = tile_slice_grid<kFP4A>(max_tiles, I / 128);
   if constexpr (kFP4A) {
     if (hq) {
-      hipLaunchKernelGGL((gate_up_tiled_kernel<BM, kFP4A, kW8, KV, kBlk, true>), dim3(grid), dim3(256),
+      hipLaunchKernelGGL((gate_up_tiled_kernel<BM, kFP4A, kW8, KV, kBlk, true>), dim3(grid),
+                         dim3(TileCfg<BM, kFP4A, kW8, KV, kBlk>::kThreads),
                          0, stream, act, act_scale, sorted, offsets, tiles, num_tiles, w13, w13s, T,
                          H, I, Kp, h, hq, hs);
       return hipGetLastError();
     }
   }
-  hipLaunchKernelGGL((gate_up_tiled_kernel<BM, kFP4A, kW8, KV, kBlk>), dim3(grid), dim3(256), 0, stream, act,
+  hipLaunchKernelGGL((gate_up_tiled_kernel<BM, kFP4A, kW8, KV, kBlk>), dim3(grid),
+                     dim3(TileCfg<BM, kFP4A, kW8, KV, kBlk>::kThreads), 0, stream, act,
                      act_scale, sorted, offsets, tiles, num_tiles, w13, w13s, T, H, I, Kp, h, hq, hs);
   return hipGetLastError();
 }
@@ -757,7 +784,8 @@ hipError_t launch_down_bm(const void* h, const uint8_t* h_scale, const int32_t* 
                           hipStream_t stream) {
   const unsigned grid = tile_slice_grid<kFP4A>(max_tiles, H / 256);
   uint8_t* ye = reinterpret_cast<uint8_t*>(y) + (size_t)A * H * 2;   // the group exponents
-  hipLaunchKernelGGL((down_tiled_kernel<BM, kFP4A, kW8, KV, kBlk>), dim3(grid), dim3(256), 0, stream, h,
+  hipLaunchKernelGGL((down_tiled_kernel<BM, kFP4A, kW8, KV, kBlk>), dim3(grid),
+                     dim3(TileCfg<BM, kFP4A, kW8, KV, kBlk>::kThreads), 0, stream, h,
                      h_scale, offsets, tiles, num_tiles, w2, w2s, A, H, I, y, ye);
   return hipGetLastError();
 }
