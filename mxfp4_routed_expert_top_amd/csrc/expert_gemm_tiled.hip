@@ -267,11 +267,22 @@ struct TiledGemm {
     return 4 * ((row / RW) * per * 64 + (row % RW) * Q + (c ^ scale_swizzle(row, Q))) + g;
   }
 
-  // Issue chunk c into a stage (weight codes into registers q: strip t's
-  // 16-byte pieces at q[NQ t .. NQ t + NQ)).
-  // (kAS: adst = where this wave's activation-scale load lands)
-  __device__ __forceinline__ void issue(uint8_t* base, int c, u32x4_t (&q)[4 * NQ],
-                                        uint8_t* adst = nullptr) const {
+  // Issue chunk c: the weight codes into this wave's registers q (strip t's
+  // 16-byte pieces at q[NQ t .. NQ t + NQ)), then the activations into a
+  // stage of LDS (kAS: adst = where this wave's activation-scale load lands).
+  // Past the last chunk both move no data.
+  __device__ __forceinline__ void issue_w(int c, u32x4_t (&q)[4 * NQ]) const {
+    const bool ok = c < nch;
+    const uint32_t oor = ok ? 0u : kOOR;
+    const uint32_t cc = ok ? (uint32_t)c : 0u;
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+      for (int hq = 0; hq < NQ; ++hq)
+        q[NQ * t + hq] = stream ? bload16_nt(w, wo[t] | oor, wnat_chunk(cc, NQ, hq))
+                                : bload16(w, wo[t] | oor, wnat_chunk(cc, NQ, hq));
+  }
+  __device__ __forceinline__ void issue_x(uint8_t* base, int c, uint8_t* adst = nullptr) const {
     const bool ok = c < nch;
     const uint32_t oor = ok ? 0u : kOOR;
     const uint32_t cc = ok ? (uint32_t)c : 0u;
@@ -279,12 +290,6 @@ struct TiledGemm {
 #pragma unroll
     for (int i = 0; i < XI; ++i)
       load_to_lds16(a, xo[i] | oor, kXStep * cc, base + (wave * XI + i) * 1024);
-#pragma unroll
-    for (int t = 0; t < 4; ++t)
-#pragma unroll
-      for (int hq = 0; hq < NQ; ++hq)
-        q[NQ * t + hq] = stream ? bload16_nt(w, wo[t] | oor, wnat_chunk(cc, NQ, hq))
-                                : bload16(w, wo[t] | oor, wnat_chunk(cc, NQ, hq));
   }
 
   // MFMAs of one chunk on the first NMT 16-row sub-tiles (the live ones).
@@ -401,14 +406,22 @@ struct TiledGemm {
       stage_rows<BM / 4>(asc, as, arow);
     }
 #pragma unroll
-    for (int u = 0; u < NS - 1; ++u) issue(stages[u], u, q[u], adst(u));
+    for (int u = 0; u < NS - 1; ++u) {
+      issue_w(u, q[u]);
+      issue_x(stages[u], u, adst(u));
+    }
     for (int c0 = 0; c0 < nch; c0 += NS) {
 #pragma unroll
       for (int u = 0; u < NS; ++u) {
         const int c = c0 + u;
         wait_vmcnt<LPS * (NS - 2)>();
+        // The weights of chunk c + NS - 1 go to registers this wave has
+        // finished with (chunk c - 1's): they need not wait for the other
+        // waves; the activations refill the stage chunk c - 1 was read
+        // from, after the barrier that retires every read of it.
+        issue_w(c + NS - 1, q[(u + NS - 1) % NS]);
         stage_barrier();
-        issue(stages[(u + NS - 1) % NS], c + NS - 1, q[(u + NS - 1) % NS], adst((u + NS - 1) % NS));
+        issue_x(stages[(u + NS - 1) % NS], c + NS - 1, adst((u + NS - 1) % NS));
         if (c < nch) compute<NMT>(stages[u] + half * 64 * 256, sc, aslot(u), c, q[u], acc);
       }
     }
