@@ -72,6 +72,16 @@ SMALL = {
     # the same reductions on the 32-row weight-streaming kernels (few rows per expert)
     "full_k_decode": synth.custom_config("full_k_decode", T=24, H=4096, I=1024, E=64, K=4,
                                          shared=1),
+    # the interface's maxima: E = 1024 experts (16 routing keys per lane), K + shared = 32
+    # slots per token, H and I at the 32-row bf16 kernels' LDS limit (13,568), and the
+    # longest reduction of the MXFP4 128-row kernels (8,192)
+    "max_e": synth.custom_config("max_e", T=16, H=256, I=128, E=1024, K=8, shared=1),
+    "max_slots": synth.custom_config("max_slots", T=12, H=256, I=128, E=64, K=31, shared=1),
+    "max_h_decode": synth.custom_config("max_h_decode", T=6, H=13568, I=128, E=4, K=2, shared=1),
+    "max_i_decode": synth.custom_config("max_i_decode", T=6, H=128, I=13568, E=4, K=2, shared=1),
+    "tiled128_w4a4_k8192": synth.custom_config("tiled128_w4a4_k8192", T=200, H=8192, I=8192,
+                                               E=2, K=1, shared=1, act_fmt=synth.ACT_MXFP4,
+                                               outlier_p=0.002),
 }
 
 
