@@ -120,7 +120,8 @@ typedef enum { MOE_SRC_F32 = 0, MOE_SRC_BF16 = 1 } moe_src_dtype;
  * (prefill) GEMMs take 64- or 128-row tiles. */
 #define MOE_TILE_M 32
 
-/* Human-readable name of a status code (static string). */
+/* Human-readable name of a status code (static string).  Not a step of the
+ * method: the pages describe no error conventions, these are the library's. */
 MOE_API const char *moe_status_string(moe_status s);
 
 /*
@@ -410,17 +411,32 @@ MOE_API moe_status moe_mxfp8_expert_down(const uint16_t *h, const int32_t *exper
 /* The tile_m moe_mxfp4_forward uses for these shapes and activation format
  * (A = T*Kp assignments over Ep experts): 32, 64 or 128 (see
  * moe_expert_gate_up; 256-row tiles are used only when a caller of the
- * per-step entry points asks for them). */
+ * per-step entry points asks for them).  The pages keep separate small-M
+ * (decode) and large-M (prefill) GEMM launchers chosen by the local shape
+ * (MiniMax M3 on MI355X post, section "Local shape and tiling") and use
+ * 32-row tiles for the MoE kernel (VibeSys post, section "Prefill, cache and
+ * speculation"). */
 MOE_API int32_t moe_gemm_tile_m(int32_t T, int32_t Kp, int32_t Ep, int32_t H, int32_t I,
                                 int32_t act_fmt);
 
-/* Workspace bytes moe_mxfp4_forward needs (0 for T = 0). */
+/* Workspace bytes moe_mxfp4_forward needs (0 for T = 0): the routing
+ * tables, the grouping, the quantised activations, h and the staged y.  The
+ * pages say nothing of memory management; a caller-owned workspace keeps
+ * every call free of allocation and so capturable in a HIP graph, which the
+ * pages' graph-captured decode steps need (VibeSys post, section "Kernels
+ * and graph capture"). */
 MOE_API size_t moe_mxfp4_workspace_size(int32_t T, int32_t H, int32_t I, int32_t E, int32_t K,
                                 int32_t shared, int32_t act_fmt);
 
 /*
- * The whole layer in one call: route, align, [quantise x], gate/up + SwiGLU,
- * [quantise h], down, combine, all enqueued on `stream`.  The GEMM kernels
+ * The whole layer in one call: the MoE layer of 512 routed experts with
+ * MXFP4 weights (VibeSys "Qwen3.5-397B on 4x MI300A" post, section "Goal")
+ * run as one MoE dispatch over the top-K routed experts plus the shared
+ * expert as slot K (InferenceX "MI355X Qwen3.5 SGLang v0.5.12" post, section
+ * on the specific optimisations, shared-expert fusion bullet; MiniMax M3 on
+ * MI355X post, section "Shared expert fusion"): route, align, [quantise x],
+ * gate/up + SwiGLU [+ the quantisation of h, in the tiled W4A4 GEMM's
+ * epilogue], down, combine, all enqueued on `stream`.  The GEMM kernels
  * are chosen on the host from the shapes alone (no device read): average
  * rows per expert T*K'/E' <= 8 -> 32-row weight-streaming tiles, else
  * 64-row LDS-tiled tiles (bf16 activations; MXFP4 activations: 64 up to 48
@@ -433,7 +449,8 @@ MOE_API size_t moe_mxfp4_workspace_size(int32_t T, int32_t H, int32_t I, int32_t
  *   act_fmt        MOE_ACT_BF16 (W4A16) or MOE_ACT_MXFP4 (W4A4: x and h are
  *                  MXFP4-quantised before their GEMM; with tiled GEMMs into
  *                  the blocked sorted-row order, x into each of its token's
- *                  slots)
+ *                  slots and h by the gate/up GEMM itself, as
+ *                  moe_expert_gate_up_quant)
  *   out            out bf16 [T, H]
  *   topk_ids_out, topk_weights_out: optional copies of the routing [T, K']
  *   workspace      caller-owned device scratch of moe_mxfp4_workspace_size bytes
