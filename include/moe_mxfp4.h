@@ -125,6 +125,25 @@ typedef enum { MOE_SRC_F32 = 0, MOE_SRC_BF16 = 1 } moe_src_dtype;
 MOE_API const char *moe_status_string(moe_status s);
 
 /*
+ * Bound-check results of a debug build of the library (compiled with
+ * MOE_DEBUG; libmoe_mxfp4_debug.so).  In such a build every kernel checks the
+ * indices it takes from device tables before using them; a failed check skips
+ * the access and sets a bit, never traps:
+ *   MOE_DEBUG_ALIGN    (1) a grouping position or a tile-table entry out of range
+ *   MOE_DEBUG_TILES    (2) a GEMM tile whose rows leave [0, T*Kp)
+ *   MOE_DEBUG_COMBINE  (4) a slot row at or past T*Kp read by the combine
+ * Returns the OR of the bits set since the last reset (bit 31: the flags
+ * could not be read) and clears them when reset != 0.  It synchronises with
+ * the device (a blocking copy), so it is for tests, not for captured work.
+ * Release builds compile the checks away and return 0 without touching the
+ * device.  Not a step of the method.
+ */
+#define MOE_DEBUG_ALIGN 1u
+#define MOE_DEBUG_TILES 2u
+#define MOE_DEBUG_COMBINE 4u
+MOE_API uint32_t moe_debug_flags(int32_t reset);
+
+/*
  * Softmax top-K routing (InferenceX Qwen3.5 post, fused_topk bullet:
  * softmax-scored top-K selection, E = 512, K = 10; shared-expert bullet: the
  * shared expert as expert top-K+1 of one dispatch).

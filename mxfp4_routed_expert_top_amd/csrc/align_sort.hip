@@ -23,6 +23,8 @@
 #include "common.h"
 #include "kernels.h"
 
+MOE_DEBUG_FLAGS(debug_flags_align)
+
 namespace {
 
 constexpr int kChunk = 512;       // assignments per block in passes 1 and 4
@@ -155,10 +157,11 @@ __global__ __launch_bounds__(kScanThreads) void align_offsets_kernel(
     if (e < Ep) {
       offsets[e] = off[q];
       if (tiles)
-        for (int j = 0; j < nt[q]; ++j) {
-          tiles[2 * (toff[q] + j)] = e;
-          tiles[2 * (toff[q] + j) + 1] = off[q] + j * tile_m;
-        }
+        for (int j = 0; j < nt[q]; ++j)
+          if (MOE_DOK(toff[q] + j < (A + tile_m - 1) / tile_m + Ep, kDbgAlign)) {
+            tiles[2 * (toff[q] + j)] = e;
+            tiles[2 * (toff[q] + j) + 1] = off[q] + j * tile_m;
+          }
     }
   }
   if (threadIdx.x == 0) {
@@ -186,8 +189,10 @@ __global__ __launch_bounds__(256) void align_scatter_kernel(
     for (int w = 0; w < 4; ++w) {
       if (w == wave && e >= 0) {
         int p = pos[e] + rank;
-        sorted[p] = a;
-        if (inv) inv[a] = p;
+        if (MOE_DOK(p >= 0 && p < A, kDbgAlign)) {
+          sorted[p] = a;
+          if (inv) inv[a] = p;
+        }
         if (rank == same - 1) pos[e] = p + 1;    // the last lane of this expert advances it
       }
       __syncthreads();
@@ -231,10 +236,11 @@ __global__ __launch_bounds__(kScanThreads) void align_small_kernel(
       offsets[e] = off[q];
       pos[e] = off[q];
       if (tiles)
-        for (int j = 0; j < nt[q]; ++j) {
-          tiles[2 * (toff[q] + j)] = e;
-          tiles[2 * (toff[q] + j) + 1] = off[q] + j * tile_m;
-        }
+        for (int j = 0; j < nt[q]; ++j)
+          if (MOE_DOK(toff[q] + j < (A + tile_m - 1) / tile_m + Ep, kDbgAlign)) {
+            tiles[2 * (toff[q] + j)] = e;
+            tiles[2 * (toff[q] + j) + 1] = off[q] + j * tile_m;
+          }
     }
   }
   if (threadIdx.x == 0) {
@@ -253,8 +259,10 @@ __global__ __launch_bounds__(kScanThreads) void align_small_kernel(
     for (int w = 0; w < nwr; ++w) {
       if (w == wave && e >= 0) {
         const int p = pos[e] + rank;
-        sorted[p] = a;
-        if (inv) inv[a] = p;
+        if (MOE_DOK(p >= 0 && p < A, kDbgAlign)) {
+          sorted[p] = a;
+          if (inv) inv[a] = p;
+        }
         if (rank == same - 1) pos[e] = p + 1;
       }
       __syncthreads();

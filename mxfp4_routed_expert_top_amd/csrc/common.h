@@ -11,6 +11,45 @@ typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
 
 #define MOE_WAVE 64
 
+// Debug builds (-DMOE_DEBUG): the kernels check every index that comes from a
+// device table (the grouping's positions, a tile's rows, the combine's slot
+// rows) against the sizes they were given.  A failed check skips the access
+// and sets a bit in the source file's device flag word, which the host reads
+// (and clears) through moe_debug_flags: a bad index is reported, not
+// executed, and no check traps.  Release builds compile the checks away.
+enum : uint32_t {
+  kDbgAlign = 1u,     // a sorted / inv position or a tile-table entry out of range
+  kDbgTiles = 2u,     // a GEMM tile's rows outside its expert's group or past A
+  kDbgCombine = 4u,   // a slot row read by the combine at or past A
+};
+#ifdef MOE_DEBUG
+// Defines the file's flag word and host_fn(reset), which returns it (ORed
+// with 0x80000000 when the copy fails) and clears it when reset is set.
+#define MOE_DEBUG_FLAGS(host_fn)                                                            \
+  namespace {                                                                               \
+  __device__ uint32_t g_moe_debug_flags;                                                    \
+  }                                                                                         \
+  uint32_t host_fn(bool reset) {                                                            \
+    uint32_t v = 0;                                                                         \
+    if (hipMemcpyFromSymbol(&v, HIP_SYMBOL(g_moe_debug_flags), sizeof v) != hipSuccess)     \
+      return 0x80000000u;                                                                   \
+    const uint32_t zero = 0;                                                                \
+    if (reset && hipMemcpyToSymbol(HIP_SYMBOL(g_moe_debug_flags), &zero, sizeof zero) !=   \
+                     hipSuccess)                                                            \
+      return v | 0x80000000u;                                                               \
+    return v;                                                                               \
+  }
+#define MOE_DOK(cond, bit) moe_dok((cond), (bit), &g_moe_debug_flags)
+__device__ __forceinline__ bool moe_dok(bool ok, uint32_t bit, uint32_t* flags) {
+  if (!ok) atomicOr(flags, bit);
+  return ok;
+}
+#else
+#define MOE_DEBUG_FLAGS(host_fn) \
+  uint32_t host_fn(bool) { return 0; }
+#define MOE_DOK(cond, bit) true
+#endif
+
 // float32 -> bf16 bits, round to nearest even (finite inputs).
 __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
   uint32_t u = __float_as_uint(f);

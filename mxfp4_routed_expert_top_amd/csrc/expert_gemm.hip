@@ -28,6 +28,8 @@
 #include "common.h"
 #include "kernels.h"
 
+MOE_DEBUG_FLAGS(debug_flags_expert_gemm)
+
 namespace {
 
 // Tuning constants: the widest pipeline phase (in 128-element chunks) and
@@ -213,6 +215,9 @@ __attribute__((amdgpu_waves_per_eu(MOE_GEMM_WAVES_PER_EU))) void gate_up_kernel(
     int nsl, uint16_t* __restrict__ h) {
   TileInfo ti;
   if (!load_tile(tiles, num_tiles, offsets, (int)(blockIdx.x / nsl), &ti)) return;
+  // (debug builds: a tile whose rows leave [0, A) stores nothing)
+  if (!MOE_DOK(ti.row0 >= 0 && ti.rows > 0 && (int64_t)ti.row0 + ti.rows <= (int64_t)T * Kp, kDbgTiles))
+    return;
   const int s = blockIdx.x % nsl;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int nl = lane & 15, g = lane >> 4;
@@ -292,6 +297,9 @@ __attribute__((amdgpu_waves_per_eu(MOE_GEMM_WAVES_PER_EU))) void down_kernel(
     uint8_t* __restrict__ ye) {
   TileInfo ti;
   if (!load_tile(tiles, num_tiles, offsets, (int)(blockIdx.x / nsl), &ti)) return;
+  // (debug builds: a tile whose rows leave [0, A) stores nothing)
+  if (!MOE_DOK(ti.row0 >= 0 && ti.rows > 0 && (int64_t)ti.row0 + ti.rows <= (int64_t)A, kDbgTiles))
+    return;
   const int s = blockIdx.x % nsl;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int nl = lane & 15, g = lane >> 4;
@@ -408,23 +416,25 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint16_t* __restrict
   for (int k0 = 0; k0 < Kp; k0 += 8) {
     int r[8];
     float wk[8];
+    bool live[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const bool ok = k0 + i < Kp;
       r[i] = ok ? inv[(size_t)t * Kp + k0 + i] : 0;
       wk[i] = ok ? w[(size_t)t * Kp + k0 + i] : 0.f;
+      live[i] = ok && MOE_DOK((unsigned)r[i] < (unsigned)(T * Kp), kDbgCombine);
     }
     u32x4_t v[8];
     int ex[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i)
-      if (k0 + i < Kp) {
+      if (live[i]) {
         v[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(y + (size_t)r[i] * H + j));
         ex[i] = (int)ye[(size_t)r[i] * (H / kYGroup) + j / kYGroup] - 127;
       }
 #pragma unroll
     for (int i = 0; i < 8; ++i)
-      if (k0 + i < Kp)
+      if (live[i])
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           acc[2 * q] += wk[i] * y_decode((uint16_t)(v[i][q] & 0xFFFFu), ex[i]);

@@ -30,6 +30,8 @@
 #include "common.h"
 #include "kernels.h"
 
+MOE_DEBUG_FLAGS(debug_flags_expert_gemm_tiled)
+
 namespace {
 
 constexpr uint32_t kOOR = 0x80000000u;   // out-of-range buffer offset: loads return 0
@@ -608,6 +610,10 @@ __global__ __launch_bounds__((TileCfg<BM, kFP4A, kW8, KV, kBlk>::kThreads), KV ?
   int s;
   if (!tile_slice<BM, kFP4A, kBlk ? 4 : 1>(blockIdx.x, tiles, offsets, *num_tiles, I / 128, &ti, &s))
     return;
+  // (debug builds: a tile whose rows leave [0, A) stores nothing)
+  if (!MOE_DOK(ti.row0 >= 0 && ti.rows > 0 && (int64_t)ti.row0 + ti.rows <= (int64_t)T * Kp,
+               kDbgTiles))
+    return;
   TiledGemm<BM, kFP4A, kW8, KV, kBlk> G;
   setup(G, ti, H, w13, w13s, 2 * I);
   const int nl = G.nl, g = G.g;
@@ -703,6 +709,9 @@ __global__ __launch_bounds__((TileCfg<BM, kFP4A, kW8, KV, kBlk>::kThreads), KV ?
   TileT ti;
   int s;
   if (!tile_slice<BM, kFP4A, 4>(blockIdx.x, tiles, offsets, *num_tiles, H / 256, &ti, &s)) return;
+  // (debug builds: a tile whose rows leave [0, A) stores nothing)
+  if (!MOE_DOK(ti.row0 >= 0 && ti.rows > 0 && (int64_t)ti.row0 + ti.rows <= (int64_t)A, kDbgTiles))
+    return;
   TiledGemm<BM, kFP4A, kW8, KV, kBlk> G;
   setup(G, ti, I, w2, w2s, H);
   const int nl = G.nl, g = G.g;

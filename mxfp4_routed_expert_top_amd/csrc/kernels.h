@@ -73,6 +73,11 @@ struct Prefetch {
 hipError_t launch_combine(const uint16_t* y, const float* w, const int32_t* inv, int T, int H,
                           int Kp, uint16_t* out, hipStream_t stream, const Prefetch* pf = nullptr);
 
+// Debug builds: each source file's bound-check flags (0 in release builds).
+uint32_t debug_flags_align(bool reset);
+uint32_t debug_flags_expert_gemm(bool reset);
+uint32_t debug_flags_expert_gemm_tiled(bool reset);
+
 bool expert_gemm_tiled_supported(int tile_m, int act_fmt, int H, int I, int wfmt = 0);
 hipError_t launch_gate_up_tiled(int tile_m, int act_fmt, int wfmt, const void* act,
                                 const uint8_t* act_scale,

@@ -135,6 +135,11 @@ const char* moe_status_string(moe_status s) {
   return "MOE_ERR_UNKNOWN";
 }
 
+uint32_t moe_debug_flags(int32_t reset) {
+  return debug_flags_align(reset != 0) | debug_flags_expert_gemm(reset != 0) |
+         debug_flags_expert_gemm_tiled(reset != 0);
+}
+
 moe_status moe_route_topk(const float* logits, const float* gate_logits, int32_t T, int32_t E,
                           int32_t K, int32_t shared, int32_t renormalize, int32_t* topk_ids,
                           float* topk_weights, void* stream) {

@@ -8,6 +8,7 @@ CPU fallback: if the library is missing, loading it raises.
 """
 from __future__ import annotations
 
+import contextlib
 import ctypes
 import os
 
@@ -15,6 +16,7 @@ import torch
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG, "libmoe_mxfp4.so")
+DEBUG_LIB_PATH = os.path.join(PKG, "libmoe_mxfp4_debug.so")   # the MOE_DEBUG build
 
 MOE_OK, MOE_ERR_INVALID_ARGUMENT, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE_TOO_SMALL, MOE_ERR_DEVICE = range(5)
 ACT_BF16, ACT_MXFP4, ACT_MXFP4_BLOCKED = 0, 1, 2
@@ -31,6 +33,7 @@ _SZ = ctypes.c_size_t
 
 _SIGS = {
     "moe_status_string": (ctypes.c_char_p, [_I32]),
+    "moe_debug_flags": (ctypes.c_uint32, [_I32]),
     "moe_route_topk": (_I32, [_P, _P, _I32, _I32, _I32, _I32, _I32, _P, _P, _P]),
     "moe_mxfp4_forward_router": (_I32, [_P, _P, _P, _P, _P, _P, _I32, _I32, _I32, _I32, _I32,
                                         _I32, _I32, _P, _P, _P, _P, _P, _SZ, _P]),
@@ -76,19 +79,43 @@ class MoeError(RuntimeError):
         super().__init__(f"{fn} returned {status_string(status)} ({status})")
 
 
+def _load(path: str) -> ctypes.CDLL:
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build it with "
+                           "`python -m mxfp4_routed_expert_top_amd.build --all`")
+    l = ctypes.CDLL(path)
+    for name, (res, args) in _SIGS.items():
+        f = getattr(l, name)
+        f.restype, f.argtypes = res, args
+    return l
+
+
 def lib() -> ctypes.CDLL:
     """Load libmoe_mxfp4.so once (raises if it has not been built)."""
     global _lib
     if _lib is None:
-        if not os.path.exists(LIB_PATH):
-            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
-                               "`python -m mxfp4_routed_expert_top_amd.build`")
-        l = ctypes.CDLL(LIB_PATH)
-        for name, (res, args) in _SIGS.items():
-            f = getattr(l, name)
-            f.restype, f.argtypes = res, args
-        _lib = l
+        _lib = _load(LIB_PATH)
     return _lib
+
+
+@contextlib.contextmanager
+def using_library(path: str = DEBUG_LIB_PATH):
+    """Inside the block every call of this module goes to another build of
+    the library (by default the bound-checking debug build); raises if it
+    has not been built."""
+    global _lib
+    saved = lib()
+    _lib = _load(path)
+    try:
+        yield _lib
+    finally:
+        _lib = saved
+
+
+def debug_flags(reset: bool = True) -> int:
+    """moe_debug_flags: the debug build's bound-check bits since the last
+    reset (0 in the release build)."""
+    return int(lib().moe_debug_flags(1 if reset else 0))
 
 
 def status_string(status: int) -> str:

@@ -26,10 +26,22 @@ def declared_functions():
 def test_library_loads_and_exports_every_declared_symbol():
     lib = ops.lib()
     names = declared_functions()
-    assert len(names) == 25
+    assert len(names) == 26
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(ops.EXPORTS)
+
+
+def test_debug_build_exports_the_same_symbols():
+    # the MOE_DEBUG build (built beside the release one) has the same interface
+    dbg = ctypes.CDLL(ops.DEBUG_LIB_PATH)
+    for n in declared_functions():
+        assert hasattr(dbg, n), n
+
+
+def test_release_build_debug_flags_are_zero():
+    # release builds compile the checks away and answer without touching a device
+    assert ops.lib().moe_debug_flags(1) == 0 and ops.debug_flags() == 0
 
 
 def test_status_strings():
