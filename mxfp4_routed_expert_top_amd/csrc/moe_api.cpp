@@ -227,7 +227,7 @@ moe_status moe_mxfp4_quantize_blocked(const void* src, int32_t src_dtype, int64_
   if (row_map ? Kp < 1 : out_rows < rows) return MOE_ERR_INVALID_ARGUMENT;
   if (cols % 128) return MOE_ERR_UNSUPPORTED;
   const int64_t out16 = (out_rows + 15) / 16 * 16;
-  const int64_t grid = row_map ? rows * ((cols / 8 + 255) / 256) : out16 / 16 * ((cols / 128 + 3) / 4);
+  const int64_t grid = row_map ? (rows * (cols / 32) + 255) / 256 : out16 / 16 * ((cols / 128 + 3) / 4);
   if (out16 * (cols / 2) >= kMaxBufferBytes || (row_map && rows * Kp >= INT32_MAX) ||
       cols > ((int64_t)1 << 30) || grid >= (int64_t)UINT32_MAX)
     return MOE_ERR_UNSUPPORTED;                          // 32-bit offsets, columns and grid

@@ -135,30 +135,63 @@ __global__ __launch_bounds__(256) void mxfp4_quant_blocked_kernel(
 }
 
 // Source row t to output rows map[t * Kp + k], k < Kp (a value outside
-// [0, out_rows) writes nothing): workgroup b covers 2048 elements of source
-// row t = b / bpr, lane j of it elements [8 j', 8 j' + 8), j' = 256 (b % bpr)
-// + j; each lane writes its four code bytes (and, for k % 4 = 0, the scale
-// byte) into every output row of its source row.
+// [0, out_rows) writes nothing): thread i quantises 32-block i of the source
+// (block i % (cols/32) of row i / (cols/32), loaded as in mxfp4_quant_kernel)
+// and writes its 16 code bytes and its scale byte into every output row of
+// its source row.  The four threads of a chunk are the lanes of one DPP
+// quad (cols is a multiple of 128), so each output row's 64 code bytes of the
+// chunk are written by adjacent lanes, one 16-byte store each, and the
+// chunk's four scale bytes are gathered into the quad's first lane and
+// written as one word.  (x of the W4A4 batch: 45 us; a lane per 8 elements
+// with 4-byte code stores and byte-wide scale stores took 47: the 64-byte
+// pieces of each slot's chunk, not the number of stores, bound it.)
 template <bool kBf16>
 __global__ __launch_bounds__(256) void mxfp4_quant_scatter_kernel(
-    const void* __restrict__ src, int bpr, int cols, const int32_t* __restrict__ map, int Kp,
-    int64_t out_rows, uint8_t* __restrict__ packed, uint8_t* __restrict__ scales) {
-  const int64_t t = blockIdx.x / bpr;
-  const int j8 = (int)(blockIdx.x - t * bpr) * 256 + (int)threadIdx.x;
-  const bool live = j8 < cols / 8;        // dead lanes come in aligned groups of four
+    const void* __restrict__ src, int64_t nblocks, int cols, const int32_t* __restrict__ map,
+    int Kp, int64_t out_rows, uint8_t* __restrict__ packed, uint8_t* __restrict__ scales) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= nblocks) return;
+  const int nb = cols / 32;
+  const int64_t t = i / nb;
+  const int b = (int)(i - t * nb);
+  float v[32];
+  if (kBf16) {
+    const u32x4_t* p = reinterpret_cast<const u32x4_t*>(src) + i * 4;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const u32x4_t d = p[q];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        v[8 * q + 2 * j] = __uint_as_float(d[j] << 16);
+        v[8 * q + 2 * j + 1] = __uint_as_float(d[j] & 0xFFFF0000u);
+      }
+    }
+  } else {
+    const float4* p = reinterpret_cast<const float4*>(src) + i * 8;
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      const float4 d = p[q];
+      v[4 * q] = d.x;
+      v[4 * q + 1] = d.y;
+      v[4 * q + 2] = d.z;
+      v[4 * q + 3] = d.w;
+    }
+  }
+  u32x4_t pk;
   uint8_t sc;
-  const uint32_t w = quant8_in_block<kBf16>(src, t * cols + 8 * (live ? j8 : 0), &sc);
-  if (!live) return;
-  const int col = 8 * j8;
+  quant_block32(v, &pk, &sc);
+  // the quad's scale bytes, K-group order, in its first lane (quad_perm
+  // [1,..], [2,..], [3,..] bring lanes 1, 2 and 3 to lane 0)
+  const uint32_t s4 = (uint32_t)sc | dpp_move_u32<0x01>(sc) << 8 | dpp_move_u32<0x02>(sc) << 16 |
+                      dpp_move_u32<0x03>(sc) << 24;
   const int64_t C = cols / 128;
-  const int64_t c = col >> 7;
-  const int g = (col >> 5) & 3, q = (col >> 3) & 3;
+  const int c = b >> 2, g = b & 3;
   for (int k = 0; k < Kp; ++k) {
     const int64_t p = map[t * Kp + k];
     if (p < 0 || p >= out_rows) continue;
     const int64_t blk = (p >> 4) * C + c;
-    *reinterpret_cast<uint32_t*>(packed + blk * 1024 + (p & 15) * 64 + 16 * g + 4 * q) = w;
-    if (q == 0) scales[blk * 64 + (p & 15) * 4 + g] = sc;
+    *reinterpret_cast<u32x4_t*>(packed + blk * 1024 + (p & 15) * 64 + 16 * g) = pk;
+    if (g == 0) *reinterpret_cast<uint32_t*>(scales + blk * 64 + (p & 15) * 4) = s4;
   }
 }
 
@@ -169,14 +202,14 @@ hipError_t launch_mxfp4_quant_blocked(const void* src, int src_is_bf16, int64_t 
                                       uint8_t* packed, uint8_t* scales, hipStream_t stream) {
   if (rows == 0 || cols == 0) return hipSuccess;
   if (map) {
-    const int bpr = (int)((cols / 8 + 255) / 256);
-    const unsigned grid = (unsigned)(rows * bpr);
+    const int64_t nblocks = rows * (cols / 32);
+    const unsigned grid = (unsigned)((nblocks + 255) / 256);
     if (src_is_bf16)
       hipLaunchKernelGGL(mxfp4_quant_scatter_kernel<true>, dim3(grid), dim3(256), 0, stream, src,
-                         bpr, (int)cols, map, Kp, out_rows, packed, scales);
+                         nblocks, (int)cols, map, Kp, out_rows, packed, scales);
     else
       hipLaunchKernelGGL(mxfp4_quant_scatter_kernel<false>, dim3(grid), dim3(256), 0, stream, src,
-                         bpr, (int)cols, map, Kp, out_rows, packed, scales);
+                         nblocks, (int)cols, map, Kp, out_rows, packed, scales);
     return hipGetLastError();
   }
   const int cgroups = (int)((cols / 128 + kChunksPerGroup - 1) / kChunksPerGroup);
