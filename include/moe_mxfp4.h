@@ -11,6 +11,7 @@
  *   1. softmax top-K routing over E experts, the shared expert folded in as
  *      expert E in slot K                              moe_route_topk
  *   2. permute: group the (token, slot) assignments by expert   moe_align_sort
+ *   1 and 2 in one call (one launch for a small batch)  moe_route_align
  *   3. (W4A4 only) MXFP4-quantise the activations      moe_mxfp4_quantize
  *   4. grouped gate/up GEMM on MXFP4 weights + SwiGLU  moe_expert_gate_up
  *   5. grouped down GEMM                               moe_expert_down
@@ -37,7 +38,8 @@
  *     at the caller's next synchronisation.
  *   - All argument checks happen before anything is enqueued; on an error
  *     nothing is enqueued and no output is touched.  T = 0 is valid and
- *     enqueues nothing (moe_align_sort still writes its zero tables).
+ *     enqueues nothing (moe_align_sort and moe_route_align still write
+ *     their zero tables).
  *   - Vector-loaded buffers (activations, packed weights, y, quantiser
  *     input and output) must be 16-byte aligned.
  *   - Shapes: H and I multiples of 128; E <= 1024; K + shared <= 32.
@@ -214,6 +216,31 @@ MOE_API moe_status moe_align_sort(const int32_t *topk_ids, int32_t T, int32_t Kp
                           int32_t *sorted_assign, int32_t *inv_assign, int32_t *tile_table,
                           int32_t *num_tiles, void *workspace, size_t workspace_bytes,
                           void *stream);
+
+/*
+ * Steps 1 and 2 in one call: exactly moe_route_topk followed by
+ * moe_align_sort on its ids (Kp = K + shared, Ep = E + shared), the same
+ * outputs bit for bit.  A small batch (T <= 32 at E <= 256, T <= 16 at
+ * E <= 512, T <= 8 at E <= 1024) runs as ONE launch, one workgroup that
+ * routes the tokens and then groups their assignments, the chosen experts
+ * passed on in LDS (InferenceX "MI355X Qwen3.5 SGLang v0.5.12" post, section
+ * on the specific optimisations: fused_topk, and the shared expert folded
+ * into the one MoE dispatch); larger batches run the two steps' kernels,
+ * which route their tokens across the whole chip.  The forwards route and
+ * group through the same path.
+ *   logits, gate_logits, renormalize, topk_ids, topk_weights  as moe_route_topk
+ *   tile_m, expert_counts ... num_tiles                       as moe_align_sort
+ *   workspace  >= moe_align_workspace_size(T, K + shared, E + shared) bytes
+ * Errors: those of moe_route_topk and of moe_align_sort (tile_m < 1, null
+ * output pointers: INVALID_ARGUMENT; WORKSPACE_TOO_SMALL).
+ */
+MOE_API moe_status moe_route_align(const float *logits, const float *gate_logits, int32_t T,
+                                   int32_t E, int32_t K, int32_t shared, int32_t renormalize,
+                                   int32_t tile_m, int32_t *topk_ids, float *topk_weights,
+                                   int32_t *expert_counts, int32_t *expert_offsets,
+                                   int32_t *sorted_assign, int32_t *inv_assign,
+                                   int32_t *tile_table, int32_t *num_tiles, void *workspace,
+                                   size_t workspace_bytes, void *stream);
 
 /*
  * MXFP4-quantise rows x cols values (OpenRelay "Gemma 4 31B on MI355X" post,

@@ -6,7 +6,8 @@
 // InferenceX Qwen3.5 post's shared-expert bullet: one MoE dispatch covers
 // the routed experts and the shared one).
 //
-// Up to kSmallA assignments: one workgroup does everything in LDS.  Beyond:
+// Up to kSmallA assignments: one workgroup does everything in LDS
+// (grouping.h: group_small).  Beyond:
 // four launches over chunks of kChunk assignments:
 //   1. per-chunk histograms            hist[b][e]
 //   2. column scans, one block per 64 experts, each of its 16 waves owning a
@@ -25,32 +26,17 @@
 
 MOE_DEBUG_FLAGS(debug_flags_align)
 
+#include "grouping.h"
+
 namespace {
 
+using namespace moe_grouping;
+
 constexpr int kChunk = 512;       // assignments per block in passes 1 and 4
-constexpr int kScanThreads = 1024;
+constexpr int kScanThreads = kGroupThreads;
 constexpr int kSmallA = 8192;     // single-workgroup path up to this many assignments
 constexpr int kSlices = kScanThreads / 64;   // chunk slices of a column scan: one per wave
 constexpr int kBatch = 12;        // histogram loads in flight per lane in a column scan
-
-// Rank of this lane among the lanes of its wave holding the same expert e
-// (lower lanes first) and the number of such lanes; e < 0 takes no part.
-__device__ __forceinline__ void wave_match_rank(int e, int* rank, int* same) {
-  const int lane = threadIdx.x & 63;
-  uint64_t todo = __ballot(e >= 0);
-  *rank = 0;
-  *same = 0;
-  while (todo) {
-    const int leader = __ffsll((unsigned long long)todo) - 1;
-    const int el = __builtin_amdgcn_readlane(e, leader);
-    const uint64_t m = __ballot(e == el);
-    if (e == el) {
-      *rank = __popcll(m & ((1ull << lane) - 1ull));
-      *same = __popcll(m);
-    }
-    todo &= ~m;
-  }
-}
 
 __global__ __launch_bounds__(256) void align_hist_kernel(const int32_t* __restrict__ ids, int A,
                                                          int Ep, int32_t* __restrict__ hist) {
@@ -65,33 +51,6 @@ __global__ __launch_bounds__(256) void align_hist_kernel(const int32_t* __restri
   }
   __syncthreads();
   for (int e = threadIdx.x; e < Ep; e += blockDim.x) hist[(size_t)blockIdx.x * Ep + e] = sh[e];
-}
-
-// Exclusive scan of one value per thread over a 1024-thread block.
-__device__ int block_exclusive_scan(int v, int* tmp /* >= 16 ints */, int* total) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  int x = v;
-#pragma unroll
-  for (int d = 1; d < 64; d <<= 1) {
-    int y = __shfl_up(x, d, MOE_WAVE);
-    if (lane >= d) x += y;
-  }
-  if (lane == 63) tmp[wave] = x;
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    int run = 0;
-    for (int w = 0; w < (int)(blockDim.x >> 6); ++w) {
-      int c = tmp[w];
-      tmp[w] = run;
-      run += c;
-    }
-    tmp[16] = run;
-  }
-  __syncthreads();
-  int r = x - v + tmp[wave];
-  *total = tmp[16];
-  __syncthreads();
-  return r;
 }
 
 // Lane's expert e = 64 * block + lane; wave w's slice of the chunks,
@@ -139,35 +98,8 @@ __global__ __launch_bounds__(kScanThreads) void align_offsets_kernel(
     const int32_t* __restrict__ counts, int A, int Ep, int tile_m, int32_t* __restrict__ offsets,
     int32_t* __restrict__ tiles, int32_t* __restrict__ num_tiles) {
   __shared__ int tmp[17];
-  // Each thread owns experts e = 2*tid and 2*tid + 1 (Ep <= 2048).
-  int cnt[2] = {0, 0};
-  for (int q = 0; q < 2; ++q) {
-    const int e = 2 * threadIdx.x + q;
-    if (e < Ep) cnt[q] = counts[e];
-  }
-  int total;
-  const int base = block_exclusive_scan(cnt[0] + cnt[1], tmp, &total);
-  const int off[2] = {base, base + cnt[0]};
-  const int nt[2] = {(cnt[0] + tile_m - 1) / tile_m, (cnt[1] + tile_m - 1) / tile_m};
-  int ttotal;
-  const int tbase = block_exclusive_scan(nt[0] + nt[1], tmp, &ttotal);
-  const int toff[2] = {tbase, tbase + nt[0]};
-  for (int q = 0; q < 2; ++q) {
-    const int e = 2 * threadIdx.x + q;
-    if (e < Ep) {
-      offsets[e] = off[q];
-      if (tiles)
-        for (int j = 0; j < nt[q]; ++j)
-          if (MOE_DOK(toff[q] + j < (A + tile_m - 1) / tile_m + Ep, kDbgAlign)) {
-            tiles[2 * (toff[q] + j)] = e;
-            tiles[2 * (toff[q] + j) + 1] = off[q] + j * tile_m;
-          }
-    }
-  }
-  if (threadIdx.x == 0) {
-    offsets[Ep] = A;
-    *num_tiles = ttotal;
-  }
+  group_offsets([&](int e) { return counts[e]; }, A, Ep, tile_m, offsets, tiles, num_tiles, tmp,
+                [](int, int, int) {});
 }
 
 __global__ __launch_bounds__(256) void align_scatter_kernel(
@@ -206,68 +138,10 @@ __global__ __launch_bounds__(kScanThreads) void align_small_kernel(
     const int32_t* __restrict__ ids, int A, int Ep, int tile_m, int32_t* __restrict__ counts,
     int32_t* __restrict__ offsets, int32_t* __restrict__ sorted, int32_t* __restrict__ inv,
     int32_t* __restrict__ tiles, int32_t* __restrict__ num_tiles) {
-  extern __shared__ int32_t sh[];          // cnt[Ep], then pos[Ep]
+  extern __shared__ int32_t sh[];          // group_small_lds_bytes(Ep)
   __shared__ int tmp[17];
-  int32_t* cnt = sh;
-  int32_t* pos = sh + Ep;
-  for (int e = threadIdx.x; e < Ep; e += blockDim.x) cnt[e] = 0;
-  __syncthreads();
-  for (int a = threadIdx.x; a < A; a += blockDim.x) {
-    const int e = ids[a];
-    if ((unsigned)e < (unsigned)Ep) atomicAdd(&cnt[e], 1);
-  }
-  __syncthreads();
-  int c[2] = {0, 0};
-  for (int q = 0; q < 2; ++q) {
-    const int e = 2 * threadIdx.x + q;
-    if (e < Ep) c[q] = cnt[e];
-  }
-  int total;
-  const int base = block_exclusive_scan(c[0] + c[1], tmp, &total);
-  const int off[2] = {base, base + c[0]};
-  const int nt[2] = {(c[0] + tile_m - 1) / tile_m, (c[1] + tile_m - 1) / tile_m};
-  int ttotal;
-  const int tbase = block_exclusive_scan(nt[0] + nt[1], tmp, &ttotal);
-  const int toff[2] = {tbase, tbase + nt[0]};
-  for (int q = 0; q < 2; ++q) {
-    const int e = 2 * threadIdx.x + q;
-    if (e < Ep) {
-      counts[e] = c[q];
-      offsets[e] = off[q];
-      pos[e] = off[q];
-      if (tiles)
-        for (int j = 0; j < nt[q]; ++j)
-          if (MOE_DOK(toff[q] + j < (A + tile_m - 1) / tile_m + Ep, kDbgAlign)) {
-            tiles[2 * (toff[q] + j)] = e;
-            tiles[2 * (toff[q] + j) + 1] = off[q] + j * tile_m;
-          }
-    }
-  }
-  if (threadIdx.x == 0) {
-    offsets[Ep] = A;
-    *num_tiles = ttotal;
-  }
-  __syncthreads();
-  const int wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
-  for (int r = 0; r < A; r += blockDim.x) {
-    const int a = r + threadIdx.x;
-    int e = (a < A) ? ids[a] : -1;
-    if ((unsigned)e >= (unsigned)Ep) e = -1;
-    int rank, same;
-    wave_match_rank(e, &rank, &same);
-    const int nwr = min(nw, (A - r + 63) / 64);            // waves holding elements this round
-    for (int w = 0; w < nwr; ++w) {
-      if (w == wave && e >= 0) {
-        const int p = pos[e] + rank;
-        if (MOE_DOK(p >= 0 && p < A, kDbgAlign)) {
-          sorted[p] = a;
-          if (inv) inv[a] = p;
-        }
-        if (rank == same - 1) pos[e] = p + 1;
-      }
-      __syncthreads();
-    }
-  }
+  group_small([&](int a) { return ids[a]; }, A, Ep, tile_m, counts, offsets, sorted, inv, tiles,
+              num_tiles, sh, tmp);
 }
 
 }  // namespace
@@ -281,9 +155,8 @@ hipError_t launch_align_sort(const int32_t* ids, int A, int Ep, int tile_m, int3
                              int32_t* offsets, int32_t* sorted, int32_t* inv, int32_t* tiles,
                              int32_t* num_tiles, int32_t* scratch, hipStream_t stream) {
   if (A <= kSmallA) {
-    hipLaunchKernelGGL(align_small_kernel, dim3(1), dim3(kScanThreads),
-                       (size_t)2 * Ep * sizeof(int32_t), stream, ids, A, Ep, tile_m, counts, offsets,
-                       sorted, inv, tiles, num_tiles);
+    hipLaunchKernelGGL(align_small_kernel, dim3(1), dim3(kScanThreads), group_small_lds_bytes(Ep),
+                       stream, ids, A, Ep, tile_m, counts, offsets, sorted, inv, tiles, num_tiles);
     return hipGetLastError();
   }
   const int nb = (A + kChunk - 1) / kChunk;

@@ -1,0 +1,181 @@
+// Device helpers of the grouping by expert (align_sort.hip, and the fused
+// small-batch routing + grouping of route_align.hip): a stable histogram /
+// prefix-scan permute of the flat assignments a = t*K' + k (ascending a
+// inside each expert's group) and the table of tile_m-row tiles that drive
+// the grouped GEMMs (VibeSys "Qwen3.5-397B on 4x MI300A" post, section
+// "Prefill, cache and speculation": 32-row tiles in the MoE kernel).
+//
+// A file that includes this header first defines its debug flag word with
+// MOE_DEBUG_FLAGS (the position checks below report into it).
+#pragma once
+#include "common.h"
+
+namespace moe_grouping {
+
+constexpr int kGroupThreads = 1024;           // one-workgroup grouping
+constexpr int kGroupWaves = kGroupThreads / 64;
+
+// Rank of this lane among the lanes of its wave holding the same expert e
+// (lower lanes first) and the number of such lanes; e < 0 takes no part.
+// One ballot round per distinct expert in the wave, no data exchange.
+__device__ __forceinline__ void wave_match_rank(int e, int* rank, int* same) {
+  const int lane = threadIdx.x & 63;
+  uint64_t todo = __ballot(e >= 0);
+  *rank = 0;
+  *same = 0;
+  while (todo) {
+    const int leader = __ffsll((unsigned long long)todo) - 1;
+    const int el = __builtin_amdgcn_readlane(e, leader);
+    const uint64_t m = __ballot(e == el);
+    if (e == el) {
+      *rank = __popcll(m & ((1ull << lane) - 1ull));
+      *same = __popcll(m);
+    }
+    todo &= ~m;
+  }
+}
+
+// Exclusive scan of one value per thread over a 1024-thread block.
+__device__ __forceinline__ int block_exclusive_scan(int v, int* tmp /* >= 17 ints */, int* total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int x = v;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    int y = __shfl_up(x, d, MOE_WAVE);
+    if (lane >= d) x += y;
+  }
+  if (lane == 63) tmp[wave] = x;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    int run = 0;
+    for (int w = 0; w < kGroupWaves; ++w) {
+      int c = tmp[w];
+      tmp[w] = run;
+      run += c;
+    }
+    tmp[16] = run;
+  }
+  __syncthreads();
+  int r = x - v + tmp[wave];
+  *total = tmp[16];
+  __syncthreads();
+  return r;
+}
+
+// Counts [Ep] -> offsets [Ep + 1] (offsets[Ep] = A) and the tile table; each
+// thread owns experts 2 tid and 2 tid + 1 (Ep <= 2048).  cnt_of(e) is the
+// count of expert e; first(e, count, offset) is called for each owned expert.
+template <class Cnt, class First>
+__device__ __forceinline__ void group_offsets(Cnt&& cnt_of, int A, int Ep, int tile_m,
+                                              int32_t* __restrict__ offsets,
+                                              int32_t* __restrict__ tiles,
+                                              int32_t* __restrict__ num_tiles, int* tmp,
+                                              First&& first) {
+  int c[2] = {0, 0};
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    const int e = 2 * threadIdx.x + q;
+    if (e < Ep) c[q] = cnt_of(e);
+  }
+  int total;
+  const int base = block_exclusive_scan(c[0] + c[1], tmp, &total);
+  const int off[2] = {base, base + c[0]};
+  const int nt[2] = {(c[0] + tile_m - 1) / tile_m, (c[1] + tile_m - 1) / tile_m};
+  int ttotal;
+  const int tbase = block_exclusive_scan(nt[0] + nt[1], tmp, &ttotal);
+  const int toff[2] = {tbase, tbase + nt[0]};
+  for (int q = 0; q < 2; ++q) {
+    const int e = 2 * threadIdx.x + q;
+    if (e < Ep) {
+      offsets[e] = off[q];
+      first(e, c[q], off[q]);
+      if (tiles)
+        for (int j = 0; j < nt[q]; ++j)
+          if (MOE_DOK(toff[q] + j < (A + tile_m - 1) / tile_m + Ep, kDbgAlign)) {
+            tiles[2 * (toff[q] + j)] = e;
+            tiles[2 * (toff[q] + j) + 1] = off[q] + j * tile_m;
+          }
+    }
+  }
+  if (threadIdx.x == 0) {
+    offsets[Ep] = A;
+    *num_tiles = ttotal;
+  }
+}
+
+// LDS bytes of group_small: cnt [Ep] and pos [Ep] ints, then a byte per
+// (wave, expert).
+__host__ __device__ constexpr size_t group_small_lds_bytes(int Ep) {
+  return (size_t)2 * Ep * 4 + (((size_t)kGroupWaves * Ep + 3) & ~(size_t)3);
+}
+
+// The whole grouping in one workgroup of kGroupThreads threads.  ids(a) is
+// the expert of assignment a (ids outside [0, Ep) take no part).  sh holds
+// group_small_lds_bytes(Ep) bytes of LDS, tmp >= 17 ints.
+//
+// The scatter goes in rounds of 1024 assignments, one per thread.  A
+// thread's position is its expert's running offset, plus the count of that
+// expert in the round's earlier waves (a byte per (wave, expert), written by
+// the first lane of each expert in each wave), plus its rank among the equal
+// lanes of its own wave.  Between rounds each expert's offset advances by its
+// count in the round.
+template <class Ids>
+__device__ __forceinline__ void group_small(Ids&& ids, int A, int Ep, int tile_m,
+                                            int32_t* __restrict__ counts,
+                                            int32_t* __restrict__ offsets,
+                                            int32_t* __restrict__ sorted, int32_t* __restrict__ inv,
+                                            int32_t* __restrict__ tiles,
+                                            int32_t* __restrict__ num_tiles, int32_t* sh,
+                                            int* tmp) {
+  int32_t* cnt = sh;
+  int32_t* pos = sh + Ep;
+  uint8_t* tab = (uint8_t*)(sh + 2 * Ep);             // [kGroupWaves][Ep]
+  const int tid = threadIdx.x;
+  for (int e = tid; e < Ep; e += kGroupThreads) cnt[e] = 0;
+  for (int i = tid; i < (kGroupWaves * Ep + 3) / 4; i += kGroupThreads) ((uint32_t*)tab)[i] = 0u;
+  __syncthreads();
+  for (int a = tid; a < A; a += kGroupThreads) {
+    const int e = ids(a);
+    if ((unsigned)e < (unsigned)Ep) atomicAdd(&cnt[e], 1);
+  }
+  __syncthreads();
+  group_offsets([&](int e) { return cnt[e]; }, A, Ep, tile_m, offsets, tiles, num_tiles, tmp,
+                [&](int e, int c, int off) {
+                  counts[e] = c;
+                  pos[e] = off;
+                });
+  // (pos is read only after the barrier that follows the table's writes)
+  const int wave = tid >> 6;
+  for (int r = 0; r < A; r += kGroupThreads) {
+    const int a = r + tid;
+    int e = (a < A) ? ids(a) : -1;
+    if ((unsigned)e >= (unsigned)Ep) e = -1;
+    int rank, same;
+    wave_match_rank(e, &rank, &same);
+    if (e >= 0 && rank == 0) tab[wave * Ep + e] = (uint8_t)same;
+    __syncthreads();
+    if (e >= 0) {
+      int before = 0;
+      for (int w = 0; w < wave; ++w) before += tab[w * Ep + e];
+      const int p = pos[e] + before + rank;
+      if (MOE_DOK(p >= 0 && p < A, kDbgAlign)) {
+        sorted[p] = a;
+        if (inv) inv[a] = p;
+      }
+    }
+    if (r + kGroupThreads < A) {                     // another round (block-uniform)
+      __syncthreads();
+      for (int x = tid; x < Ep; x += kGroupThreads) {
+        int s = 0;
+        for (int w = 0; w < kGroupWaves; ++w) {
+          s += tab[w * Ep + x];
+          tab[w * Ep + x] = 0;
+        }
+        pos[x] += s;
+      }
+      __syncthreads();
+    }
+  }
+}
+
+}  // namespace moe_grouping

@@ -7,6 +7,12 @@
 hipError_t launch_route_topk(const float* logits, const float* gate, int T, int E, int K,
                              int shared, int renormalize, int32_t* ids, float* weights,
                              hipStream_t stream);
+// The same on logits of row stride ld, the gate logit of token t at
+// gate[t * gate_stride].
+hipError_t launch_route_topk_rows(const float* logits, int ld, const float* gate,
+                                  int gate_stride, int T, int E, int K, int shared,
+                                  int renormalize, int32_t* ids, float* weights,
+                                  hipStream_t stream);
 
 // Adds the router GEMM's S partial sums into logits [T, E + shared] (in
 // split order), then routes on them (the gate logit is column E).
@@ -15,12 +21,26 @@ hipError_t launch_route_topk_split(const float* partial, int S, int T, int E, in
                                    int renormalize, int32_t* ids, float* weights, float* logits,
                                    hipStream_t stream);
 
+// Adds the router GEMM's S partial sums into logits [T, Ep] (nothing for S = 1).
+hipError_t launch_sum_splits(const float* partial, int S, int T, int Ep, float* logits,
+                             hipStream_t stream);
+
 int router_splits(int T, int H, int Ep);
 size_t router_workspace_bytes(int T, int H, int Ep);   // partial sums + summed logits
 // S = router_splits(...) > 1: partial sums into partial [S, T, Ep] (added by
 // launch_route_topk_split); S = 1: the logits straight into logits [T, Ep].
 hipError_t launch_router_gemm(const uint16_t* x, const uint16_t* w, int T, int H, int Ep,
                               float* partial, float* logits, hipStream_t stream);
+
+// Routing then grouping (route_align.hip): the results of
+// launch_route_topk_rows followed by launch_align_sort (scratch of
+// align_scratch_bytes), in one launch when route_align_fits (a small batch).
+bool route_align_fits(int T, int E, int K, int shared);
+hipError_t launch_route_align(const float* logits, int ld, const float* gate, int gate_stride,
+                              int T, int E, int K, int shared, int renormalize, int tile_m,
+                              int32_t* ids, float* weights, int32_t* counts, int32_t* offsets,
+                              int32_t* sorted, int32_t* inv, int32_t* tiles, int32_t* num_tiles,
+                              int32_t* scratch, hipStream_t stream);
 
 size_t align_scratch_bytes(int A, int Ep);
 hipError_t launch_align_sort(const int32_t* ids, int A, int Ep, int tile_m, int32_t* counts,
@@ -77,6 +97,7 @@ hipError_t launch_combine(const uint16_t* y, const float* w, const int32_t* inv,
 uint32_t debug_flags_align(bool reset);
 uint32_t debug_flags_expert_gemm(bool reset);
 uint32_t debug_flags_expert_gemm_tiled(bool reset);
+uint32_t debug_flags_route_align(bool reset);
 
 bool expert_gemm_tiled_supported(int tile_m, int act_fmt, int H, int I, int wfmt = 0);
 hipError_t launch_gate_up_tiled(int tile_m, int act_fmt, int wfmt, const void* act,

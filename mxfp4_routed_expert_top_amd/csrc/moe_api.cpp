@@ -137,7 +137,7 @@ const char* moe_status_string(moe_status s) {
 
 uint32_t moe_debug_flags(int32_t reset) {
   return debug_flags_align(reset != 0) | debug_flags_expert_gemm(reset != 0) |
-         debug_flags_expert_gemm_tiled(reset != 0);
+         debug_flags_expert_gemm_tiled(reset != 0) | debug_flags_route_align(reset != 0);
 }
 
 moe_status moe_route_topk(const float* logits, const float* gate_logits, int32_t T, int32_t E,
@@ -203,6 +203,35 @@ moe_status moe_align_sort(const int32_t* topk_ids, int32_t T, int32_t Kp, int32_
   return from_hip(launch_align_sort(topk_ids, (int)A, Ep, tile_m, expert_counts, expert_offsets,
                                     sorted_assign, inv_assign, tile_table, num_tiles,
                                     (int32_t*)workspace, as_stream(stream)));
+}
+
+moe_status moe_route_align(const float* logits, const float* gate_logits, int32_t T, int32_t E,
+                           int32_t K, int32_t shared, int32_t renormalize, int32_t tile_m,
+                           int32_t* topk_ids, float* topk_weights, int32_t* expert_counts,
+                           int32_t* expert_offsets, int32_t* sorted_assign, int32_t* inv_assign,
+                           int32_t* tile_table, int32_t* num_tiles, void* workspace,
+                           size_t workspace_bytes, void* stream) {
+  moe_status st = check_route(logits, gate_logits, T, E, K, shared, renormalize);
+  if (st != MOE_OK) return st;
+  if (tile_m < 1) return MOE_ERR_INVALID_ARGUMENT;
+  const int Kp = K + shared, Ep = E + shared;
+  const int64_t A = (int64_t)T * Kp;
+  if (A > INT32_MAX / 2) return MOE_ERR_UNSUPPORTED;
+  if (!expert_counts || !expert_offsets || !num_tiles ||
+      (T > 0 && (!topk_ids || !topk_weights || !sorted_assign)))
+    return MOE_ERR_INVALID_ARGUMENT;
+  const size_t need = align_scratch_bytes((int)A, Ep);
+  if (workspace_bytes < need) return MOE_ERR_WORKSPACE_TOO_SMALL;
+  if (!workspace) return MOE_ERR_INVALID_ARGUMENT;
+  hipStream_t s = as_stream(stream);
+  if (T == 0)     // no assignments: zero counts and offsets, no tiles
+    return from_hip(launch_align_sort(nullptr, 0, Ep, tile_m, expert_counts, expert_offsets,
+                                      sorted_assign, inv_assign, tile_table, num_tiles,
+                                      (int32_t*)workspace, s));
+  return from_hip(launch_route_align(logits, E, gate_logits, 1, T, E, K, shared, renormalize,
+                                     tile_m, topk_ids, topk_weights, expert_counts,
+                                     expert_offsets, sorted_assign, inv_assign, tile_table,
+                                     num_tiles, (int32_t*)workspace, s));
 }
 
 moe_status moe_mxfp4_quantize(const void* src, int32_t src_dtype, int64_t rows, int64_t cols,
@@ -501,18 +530,26 @@ moe_status forward_impl(const uint16_t* x, const float* router_logits,
   float* rpart = (float*)(ws + L.y);                       // router partial sums (same bytes)
   hipStream_t s = as_stream(stream);
 
+  // routing: logits of row stride ld, the shared gate logit of token t at
+  // gate[t * gate_stride]
   hipError_t e;
+  const float* lgt = router_logits;
+  const float* gate = shared_gate_logits;
+  int ld = E, gate_stride = 1;
   if (router_w) {
     const int S = router_splits(T, H, Ep);
     float* lg = logits_out ? logits_out : rpart + (size_t)S * T * Ep;
     e = launch_router_gemm(x, router_w, T, H, Ep, rpart, lg, s);
     if (e != hipSuccess) return MOE_ERR_DEVICE;
-    e = launch_route_topk_split(rpart, S, T, E, K, shared, 1, ids, wts, lg, s);
-  } else {
-    e = launch_route_topk(router_logits, shared_gate_logits, T, E, K, shared, 1, ids, wts, s);
+    e = launch_sum_splits(rpart, S, T, Ep, lg, s);
+    if (e != hipSuccess) return MOE_ERR_DEVICE;
+    lgt = lg;
+    gate = lg + E;
+    ld = gate_stride = Ep;
   }
-  if (e != hipSuccess) return MOE_ERR_DEVICE;
-  e = launch_align_sort(ids, (int)A, Ep, tm, counts, offsets, sorted, inv, tiles, ntiles, scratch, s);
+  // (a small batch, a decode step: routing and grouping in one workgroup)
+  e = launch_route_align(lgt, ld, gate, gate_stride, T, E, K, shared, 1, tm, ids, wts, counts,
+                         offsets, sorted, inv, tiles, ntiles, scratch, s);
   if (e != hipSuccess) return MOE_ERR_DEVICE;
   // W4A4 on the tiled kernels: x quantised once per token and written into
   // each of its sorted slots, h in its sorted rows, both in the blocked order

@@ -42,6 +42,8 @@ _SIGS = {
                                    _P]),
     "moe_align_workspace_size": (_SZ, [_I32, _I32, _I32]),
     "moe_align_sort": (_I32, [_P, _I32, _I32, _I32, _I32, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
+    "moe_route_align": (_I32, [_P, _P, _I32, _I32, _I32, _I32, _I32, _I32, _P, _P, _P, _P, _P, _P,
+                               _P, _P, _P, _SZ, _P]),
     "moe_mxfp4_quantize": (_I32, [_P, _I32, _I64, _I64, _P, _P, _P]),
     "moe_mxfp4_quantize_blocked": (_I32, [_P, _I32, _I64, _I64, _P, _I32, _I64, _P, _P, _P]),
     "moe_expert_gate_up": (_I32, [_P, _P, _I32, _P, _P, _P, _P, _I32, _P, _P, _I32, _I32, _I32,
@@ -213,6 +215,34 @@ def align_sort(topk_ids, Ep: int, tile_m: int = TILE_M, out=None, stream=None):
         _ptr(out["tiles"]), _ptr(out["num_tiles"]), _ptr(out["workspace"]),
         out["workspace"].numel(), _stream(stream)))
     return out
+
+
+def route_align(logits, gate_logits, K: int, shared: int, renormalize: int = 1,
+                tile_m: int = TILE_M, topk_ids=None, topk_weights=None, out=None, stream=None):
+    """moe_route_align: route_topk then align_sort on its ids in one call (one launch
+    for a small batch) -> (ids, w, dict as align_sort returns)."""
+    _dt(logits, torch.float32, "logits")
+    _dt(gate_logits, torch.float32, "gate_logits")
+    T, E = logits.shape
+    Kp, Ep = K + shared, E + shared
+    A = T * Kp
+    dev = logits.device
+    if topk_ids is None:
+        topk_ids = torch.empty(T, Kp, dtype=torch.int32, device=dev)
+    if topk_weights is None:
+        topk_weights = torch.empty(T, Kp, dtype=torch.float32, device=dev)
+    if out is None:
+        out = alloc_align(T, Kp, Ep, dev, tile_m)
+    if out["tiles"].shape[0] < (A + tile_m - 1) // tile_m + Ep:
+        raise ValueError("tile table too small for this tile_m")
+    out["tile_m"] = tile_m
+    _check("moe_route_align", lib().moe_route_align(
+        _ptr(logits), _ptr(gate_logits), T, E, K, shared, renormalize, tile_m, _ptr(topk_ids),
+        _ptr(topk_weights), _ptr(out["counts"]), _ptr(out["offsets"]),
+        _ptr(out["sorted"]) if A else None, _ptr(out["inv"]) if A else None,
+        _ptr(out["tiles"]), _ptr(out["num_tiles"]), _ptr(out["workspace"]),
+        out["workspace"].numel(), _stream(stream)))
+    return topk_ids, topk_weights, out
 
 
 def alloc_align(T: int, Kp: int, Ep: int, device, tile_m: int = TILE_M) -> dict:

@@ -26,7 +26,7 @@ def declared_functions():
 def test_library_loads_and_exports_every_declared_symbol():
     lib = ops.lib()
     names = declared_functions()
-    assert len(names) == 26
+    assert len(names) == 27
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(ops.EXPORTS)
@@ -112,6 +112,35 @@ def test_align_sort_argument_errors():
     assert f(*args(Ep=4096)) == UNSUPPORTED
     assert f(*args(wsb=ws - 1)) == WS_SMALL
     assert f(*args(ws=None)) == INVALID
+
+
+def test_route_align_argument_errors():
+    f = ops.lib().moe_route_align
+    ws = ops.align_workspace_size(10, 3, 9)
+    def call(**kw):
+        a = dict(lg=FAKE, g=FAKE, T=10, E=8, K=2, s=1, r=1, tm=32, ids=FAKE, wt=FAKE, cnt=FAKE,
+                 off=FAKE, srt=FAKE, inv=None, tiles=None, nt=FAKE, ws=FAKE, wsb=ws)
+        a.update(kw)
+        return f(a["lg"], a["g"], a["T"], a["E"], a["K"], a["s"], a["r"], a["tm"], a["ids"],
+                 a["wt"], a["cnt"], a["off"], a["srt"], a["inv"], a["tiles"], a["nt"], a["ws"],
+                 a["wsb"], None)
+    assert call(lg=None) == INVALID
+    assert call(g=None) == INVALID                       # shared without gate
+    assert call(T=-1) == INVALID
+    assert call(K=0) == INVALID
+    assert call(K=9) == INVALID                          # K > E
+    assert call(r=2) == INVALID
+    assert call(tm=0) == INVALID
+    assert call(ids=None) == INVALID
+    assert call(wt=None) == INVALID
+    assert call(cnt=None) == INVALID
+    assert call(off=None) == INVALID
+    assert call(srt=None) == INVALID
+    assert call(nt=None) == INVALID
+    assert call(ws=None) == INVALID
+    assert call(E=2048, K=4) == UNSUPPORTED              # E > 1024
+    assert call(E=64, K=32) == UNSUPPORTED               # K' = 33
+    assert call(wsb=ws - 1) == WS_SMALL
 
 
 def test_quantize_argument_errors():

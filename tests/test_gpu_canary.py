@@ -4,8 +4,9 @@ must be unchanged (nothing written outside its buffer) and each output must
 equal, bit for bit, what the same sequence of calls writes into plain
 buffers (nothing read from outside the inputs, nothing left unwritten that
 the result depends on).  Covers the one-call forwards (32-row, 64-row and
-128-row GEMM paths, W4A4 on both, MXFP8, routed from x) and every per-step
-entry point at every tile size the kernels offer."""
+128-row GEMM paths, W4A4 on both, MXFP8, routed from x), every per-step
+entry point at every tile size the kernels offer, and the one-call routing +
+grouping."""
 import sys
 
 import numpy as np
@@ -156,6 +157,41 @@ def test_stage_guards(name, tm):
     want = _stages(o, prob, tm, plain)
     torch.cuda.synchronize()
     assert len(got) == len(want)
+    for a, b in zip(got, want):
+        assert torch.equal(a, b)
+
+
+@pytest.mark.parametrize("T,E,K,tm", [(16, 512, 10, 32), (30, 16, 3, 64), (64, 512, 10, 32),
+                                      (300, 64, 4, 32)])
+def test_route_align_guards(T, E, K, tm):
+    """moe_route_align (one launch for the small batches, two beyond) with guarded
+    outputs."""
+    o = ops()
+    gen = torch.Generator(device=DEV).manual_seed(T + E)
+    logits = torch.randn(T, E, generator=gen, device=DEV)
+    gate = torch.randn(T, generator=gen, device=DEV)
+    Kp, Ep = K + 1, E + 1
+    A = T * Kp
+    _say("canary route_align", T, E, K, tm)
+
+    def run(alloc):
+        i32 = torch.int32
+        ids, w = alloc((T, Kp), i32), alloc((T, Kp), torch.float32)
+        al = dict(counts=alloc((Ep,), i32), offsets=alloc((Ep + 1,), i32), sorted=alloc((A,), i32),
+                  inv=alloc((A,), i32), tiles=alloc(((A + tm - 1) // tm + Ep, 2), i32),
+                  num_tiles=alloc((1,), i32),
+                  workspace=alloc((max(o.align_workspace_size(T, Kp, Ep), 1),), torch.uint8))
+        o.route_align(logits, gate, K, 1, tile_m=tm, topk_ids=ids, topk_weights=w, out=al)
+        n = al["num_tiles"]
+        return [ids, w, al["counts"], al["offsets"], al["sorted"], al["inv"], n, al["tiles"]]
+
+    g = Guarded()
+    got = run(g)
+    g.check()
+    want = run(plain)
+    torch.cuda.synchronize()
+    n = int(want[6].item())
+    got[-1], want[-1] = got[-1][:n], want[-1][:n]       # (the table's rows past num_tiles are unused)
     for a, b in zip(got, want):
         assert torch.equal(a, b)
 

@@ -175,12 +175,20 @@ def test_align_golden_tile_m_2():
 
 
 @pytest.mark.parametrize("name", ["tiny", "ragged", "sparse", "decode", "prefill",
-                                  "prefill_skewed", "w4a4", "one_hot", "big_a", "chunks19"])
+                                  "prefill_skewed", "w4a4", "one_hot", "big_a", "chunks19",
+                                  "small_max", "small_max_one_expert"])
 def test_align_sort(name):
     _say("align", name)
     if name == "one_hot":                  # every assignment to one expert: many tiles
         T, Kp, Ep = 3000, 1, 40
         ids = torch.full((T, Kp), 17, dtype=torch.int32)
+    elif name in ("small_max", "small_max_one_expert"):
+        # the one-workgroup path at its largest (8192 assignments: eight scatter rounds),
+        # random ids over 1025 experts or every id the same (64 per wave)
+        T, Kp, Ep = 256, 32, 1025
+        ids = (torch.randint(0, Ep, (T, Kp), generator=torch.Generator().manual_seed(10),
+                             dtype=torch.int32) if name == "small_max"
+               else torch.full((T, Kp), 1024, dtype=torch.int32))
     elif name in ("big_a", "chunks19"):    # many chunks, random ids, a ragged last chunk
         # (218 and 19 chunks of 512: histogram columns padded by 2 and 1)
         T, Kp, Ep = (12345, 9, 1025) if name == "big_a" else (1080, 9, 300)
@@ -218,6 +226,64 @@ def test_align_empty():
     assert got["counts"].cpu().tolist() == [0] * 5
     assert got["offsets"].cpu().tolist() == [0] * 6
     assert int(got["num_tiles"].item()) == 0
+
+
+# ---------------------------------------------------- routing + grouping --
+
+# (T, E, K, shared, renormalize, tile_m): every keys-per-lane / tokens-per-wave
+# instance of the one-launch path (4 keys per lane with one and two tokens per
+# wave, 8 and 16 keys), 1024 assignments, ties, the full softmax, other tile
+# sizes, and the sizes just past the one-launch limit (two launches)
+ROUTE_ALIGN_CASES = [
+    (1, 64, 6, 1, 1, 32), (16, 256, 8, 1, 1, 32), (17, 200, 4, 0, 1, 64),
+    (32, 96, 31, 1, 1, 2), (32, 32, 32, 0, 0, 32), (32, 96, 7, 1, 1, 32),
+    (16, 512, 10, 1, 1, 32), (16, 512, 10, 1, 1, 128), (3, 300, 2, 1, 1, 32),
+    (8, 1024, 8, 1, 1, 32), (8, 1024, 31, 1, 1, 32),
+    (33, 256, 8, 1, 1, 32), (17, 512, 10, 1, 1, 32), (64, 512, 10, 1, 1, 32),
+    (9, 1024, 8, 1, 1, 32),
+]
+
+
+@pytest.mark.parametrize("T,E,K,shared,renorm,tile_m", ROUTE_ALIGN_CASES)
+def test_route_align(T, E, K, shared, renorm, tile_m):
+    """moe_route_align: the oracle's routing and grouping bit for bit, and the
+    same bits as moe_route_topk followed by moe_align_sort."""
+    _say("route_align", T, E, K, shared, renorm, tile_m)
+    o = ops()
+    gen = torch.Generator().manual_seed(1000 + T + E + K)
+    if (T, E, K) == (32, 96, 7):
+        logits = synth.ties_logits(T, E, 3)
+    else:
+        logits = torch.randn(T, E, generator=gen) * 2
+    gate = torch.randn(T, generator=gen) if shared else None
+    lg, g = logits.to(DEV), None if gate is None else gate.to(DEV)
+    ids, w, al = o.route_align(lg, g, K, shared, renorm, tile_m=tile_m)
+    torch.cuda.synchronize()
+    want_ids, want_w = moe.route(logits.numpy(), None if gate is None else gate.numpy(), K,
+                                 shared, bool(renorm))
+    assert np.array_equal(ids.cpu().numpy(), want_ids)
+    assert np.max(np.abs(w.cpu().numpy() - want_w)) <= W_ATOL
+    _check_align(al, moe.align(want_ids, E + shared, tile_m))
+    ids2, w2 = o.route_topk(lg, g, K, shared, renorm)
+    al2 = o.align_sort(ids2, E + shared, tile_m=tile_m)
+    torch.cuda.synchronize()
+    assert torch.equal(ids, ids2) and torch.equal(w, w2)
+    for k in ("counts", "offsets", "sorted", "inv", "num_tiles"):
+        assert torch.equal(al[k], al2[k]), k
+    n = int(al["num_tiles"].item())
+    assert torch.equal(al["tiles"][:n], al2["tiles"][:n])
+
+
+def test_route_align_empty():
+    o = ops()
+    lg = torch.empty(0, 16, dtype=torch.float32, device=DEV)
+    g = torch.empty(0, dtype=torch.float32, device=DEV)
+    ids, w, al = o.route_align(lg, g, 3, 1)
+    torch.cuda.synchronize()
+    assert ids.shape == (0, 4)
+    assert al["counts"].cpu().tolist() == [0] * 17
+    assert al["offsets"].cpu().tolist() == [0] * 18
+    assert int(al["num_tiles"].item()) == 0
 
 
 # -------------------------------------------------------------- the layer --
