@@ -270,6 +270,35 @@ __device__ __forceinline__ uint32_t wnat_chunk(int c, int NQ, int hq) {
   return (uint32_t)(NQ * c + hq) * 1024u;
 }
 
+// s_waitcnt vmcnt(n) with the other counters left alone (gfx9 encoding).
+// Vector memory operations complete in issue order, so it waits for all but
+// the n most recent.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// Workgroup barrier without the release fence of __syncthreads: the fence
+// would wait for every load still in flight, i.e. for the stages being
+// prefetched.  Each wave waits for its own direct-to-LDS loads (wait_vmcnt)
+// before the barrier, and every LDS read of a buffer has returned before the
+// barrier that precedes its refill; the "memory" clobber keeps the compiler
+// from moving memory accesses across.
+__device__ __forceinline__ void stage_barrier() { asm volatile("s_barrier" ::: "memory"); }
+
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+// Direct-to-LDS buffer loads: lane l's 16 (4) bytes land at lds + 16 l (4 l);
+// lds is the same for the whole wave.
+__device__ __forceinline__ void load_to_lds16(rsrc_t r, uint32_t voff, uint32_t soff, void* lds) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)lds, 16, (int)voff, (int)soff, 0, 0);
+}
+
+__device__ __forceinline__ void load_to_lds4(rsrc_t r, uint32_t voff, uint32_t soff, void* lds) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)lds, 4, (int)voff, (int)soff, 0, 0);
+}
+
 __device__ __forceinline__ uint32_t bload1(rsrc_t r, uint32_t voff, uint32_t soff) {
   return (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(r, (int)voff, (int)soff, 0);
 }

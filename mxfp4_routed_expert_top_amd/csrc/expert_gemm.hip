@@ -190,6 +190,65 @@ __device__ __forceinline__ void wave_gemm(const Operands& o, int nph, floatx4_t 
 // cooperative copy per workgroup instead of 4 loads per lane per chunk).
 constexpr int kXR = 4;
 
+// Copy `bytes` (a multiple of 256) from byte off of resource r into LDS with
+// direct-to-LDS loads (no registers): 1 KiB per wave instruction when the
+// size allows, else 256 bytes; wave w takes every fourth piece.  src maps a
+// byte of the copy to its byte in the resource.
+template <class Src>
+__device__ __forceinline__ void copy_to_lds(rsrc_t r, uint32_t bytes, uint8_t* lds, Src src) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  if (bytes % 1024 == 0) {
+    for (uint32_t p = wave * 1024; p < bytes; p += 4 * 1024)
+      load_to_lds16(r, src(p + 16 * lane), 0, lds + p);
+  } else {
+    for (uint32_t p = wave * 256; p < bytes; p += 4 * 256)
+      load_to_lds4(r, src(p + 4 * lane), 0, lds + p);
+  }
+}
+
+// The common decode tile (bf16 activations, at most kXR rows: one 16-row
+// subtile, activations from LDS), with a shorter prologue: the weight scales
+// and the activation rows go straight into LDS, the first two phases' weight
+// loads go out right after, and the workgroup's barrier waits for the LDS
+// copies only (loads complete in issue order), so the scales' and the
+// weights' fetches overlap instead of following one another.  copies()
+// issues the LDS copies; returns acc for rows 4 g + r of the subtile.
+template <int PH, bool kW8, class Copies>
+__device__ __forceinline__ void small_tile_gemm(Operands& o, int nph, Copies&& copies,
+                                                floatx4_t (&acc)[2]) {
+  using PA = Phase<PH, false, true, kW8>;
+  constexpr int kOps = PH * 2 * PA::NQ;                  // one phase's weight loads
+  copies();
+  __builtin_amdgcn_sched_barrier(0);
+  PA A, B;
+  A.load(o, 0);
+  if (nph > 1) {
+    B.load(o, PH);
+    wait_vmcnt<2 * kOps>();
+  } else {
+    wait_vmcnt<kOps>();
+  }
+  stage_barrier();
+  int p = 0;
+  for (; p + 3 < nph; p += 2) {
+    A.compute(o, PH * p, acc);
+    A.load(o, PH * (p + 2));
+    B.compute(o, PH * (p + 1), acc);
+    B.load(o, PH * (p + 3));
+  }
+  if (nph - p == 3) {
+    A.compute(o, PH * p, acc);
+    A.load(o, PH * (p + 2));
+    B.compute(o, PH * (p + 1), acc);
+    A.compute(o, PH * (p + 2), acc);
+  } else if (nph - p == 2) {
+    A.compute(o, PH * p, acc);
+    B.compute(o, PH * (p + 1), acc);
+  } else {
+    A.compute(o, PH * p, acc);
+  }
+}
+
 // Copy `bytes` (a multiple of 16) of weight scales starting at byte `off` of
 // resource r into LDS, 16 bytes per lane per step.
 __device__ __forceinline__ void scales_to_lds(rsrc_t r, uint32_t off, uint32_t bytes,
@@ -243,6 +302,36 @@ __attribute__((amdgpu_waves_per_eu(MOE_GEMM_WAVES_PER_EU))) void gate_up_kernel(
     o.as = make_rsrc(act_scale, (uint32_t)((size_t)T * rs));
   } else {
     o.a = make_rsrc(act, (uint32_t)((size_t)T * H * 2));
+  }
+  if (!kFP4A && ti.rows <= kXR) {
+    // (the common decode tile; its tokens are wave-uniform loads)
+    uint8_t* lds_x = lds_scales + 128 * rs;
+    uint32_t tk[kXR];
+#pragma unroll
+    for (int r = 0; r < kXR; ++r)
+      tk[r] = r < ti.rows ? min((unsigned)(sorted[ti.row0 + r] / Kp), (unsigned)(T - 1)) : 0u;
+    const uint32_t rowb = (uint32_t)H * 2;
+    const rsrc_t rsc = make_rsrc(w13s + ti.expert * sbytes, (uint32_t)sbytes);
+    o.ldx = lds_x + min(nl, kXR - 1) * H * 2 + 64 * g;
+    o.xvalid = nl < ti.rows;
+    floatx4_t acc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+    small_tile_gemm<PH, kW8>(o, H / 128 / PH, [&] {
+      const uint32_t gs = (uint32_t)(s * 64) * rs, us = (uint32_t)(I + s * 64) * rs;
+      copy_to_lds(rsc, 64 * rs, lds_scales, [&](uint32_t b) { return gs + b; });
+      copy_to_lds(rsc, 64 * rs, lds_scales + 64 * rs, [&](uint32_t b) { return us + b; });
+      copy_to_lds(o.a, (uint32_t)ti.rows * rowb, lds_x, [&](uint32_t b) {
+        const uint32_t r = b / rowb;
+        const uint32_t t = r == 0 ? tk[0] : r == 1 ? tk[1] : r == 2 ? tk[2] : tk[3];
+        return t * rowb + (b - r * rowb);
+      });
+    }, acc);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int mm = 4 * g + r;
+      if (mm < ti.rows)
+        h[(size_t)(ti.row0 + mm) * I + i] = f32_to_bf16_rne(swiglu(acc[0][r], acc[1][r]));
+    }
+    return;
   }
   {
     const rsrc_t rsc = make_rsrc(w13s + ti.expert * sbytes, (uint32_t)sbytes);
@@ -325,6 +414,34 @@ __attribute__((amdgpu_waves_per_eu(MOE_GEMM_WAVES_PER_EU))) void down_kernel(
     o.as = make_rsrc(hscale, (uint32_t)((size_t)A * rs));
   } else {
     o.a = make_rsrc(hin, (uint32_t)((size_t)A * I * 2));
+  }
+  if (!kFP4A && ti.rows <= kXR) {
+    // (the common decode tile: see small_tile_gemm)
+    uint8_t* lds_x = lds_scales + 128 * rs;
+    const rsrc_t rsc = make_rsrc(w2s + ti.expert * sbytes, (uint32_t)sbytes);
+    o.ldx = lds_x + min(nl, kXR - 1) * I * 2 + 64 * g;
+    o.xvalid = nl < ti.rows;
+    floatx4_t acc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+    small_tile_gemm<PH, kW8>(o, I / 128 / PH, [&] {
+      const uint32_t so = (uint32_t)(s * 128) * rs, xo = (uint32_t)ti.row0 * I * 2;
+      copy_to_lds(rsc, 128 * rs, lds_scales, [&](uint32_t b) { return so + b; });
+      copy_to_lds(o.a, (uint32_t)ti.rows * I * 2, lds_x, [&](uint32_t b) { return xo + b; });
+    }, acc);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int mm = 4 * g + r;
+      const int e = y_exponent_of_field(
+          row16_max_halves(max_halves(pack_exponents(acc[0][r], 0.f), pack_exponents(acc[1][r], 0.f))) &
+          0xFFFFu);
+      if (mm < ti.rows) {
+        const size_t row = (size_t)(ti.row0 + mm);
+        uint16_t* yr = y + row * H;
+        yr[jc[0]] = y_encode(acc[0][r], e);
+        yr[jc[1]] = y_encode(acc[1][r], e);
+        if (nl == 0) ye[row * (H / kYGroup) + jb / kYGroup] = (uint8_t)(e + 127);
+      }
+    }
+    return;
   }
   scales_to_lds(make_rsrc(w2s + ti.expert * sbytes, (uint32_t)sbytes), (uint32_t)(s * 128) * rs,
                 128 * rs, lds_scales);

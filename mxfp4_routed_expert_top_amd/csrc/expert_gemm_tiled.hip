@@ -177,32 +177,6 @@ __device__ __forceinline__ int scale_swizzle(int r, int Q) {
   return v <= 2 ? 0 : (v < 6 ? rr >> (6 - v) : rr);
 }
 
-// s_waitcnt vmcnt(n) with the other counters left alone (gfx9 encoding).
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
-}
-
-// Workgroup barrier without the release fence of __syncthreads: the fence
-// would wait for every direct-to-LDS load still in flight, i.e. for the
-// stages being prefetched.  Each wave waits for its own loads of the stage
-// it is about to read (wait_vmcnt) before the barrier, and every LDS read of
-// a stage has returned (its MFMAs consumed it) before the barrier that
-// precedes the stage's refill; the "memory" clobber keeps the compiler from
-// moving memory accesses across.
-__device__ __forceinline__ void stage_barrier() { asm volatile("s_barrier" ::: "memory"); }
-
-typedef __attribute__((address_space(3))) void lds_void_t;
-
-__device__ __forceinline__ void load_to_lds16(rsrc_t r, uint32_t voff, uint32_t soff, void* lds) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)lds, 16, (int)voff, (int)soff, 0, 0);
-}
-
-__device__ __forceinline__ void load_to_lds4(rsrc_t r, uint32_t voff, uint32_t soff, void* lds) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)lds, 4, (int)voff, (int)soff, 0, 0);
-}
-
 // The K loop as an NS-stage pipeline.  Stage u holds one 128-element chunk:
 // the tile's activation rows in LDS (written by direct-to-LDS buffer loads,
 // no registers) and each wave's four weight strips (16 bytes per lane) in
