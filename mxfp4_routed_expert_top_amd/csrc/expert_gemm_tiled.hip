@@ -204,6 +204,7 @@ struct TiledGemm {
 
   rsrc_t w, ws, a, as;
   uint32_t wo[4];               // lane's offsets in its four weight strips (native code order)
+  uint32_t wsd, ssd;            // (two slices) code and scale-row byte distance of the next slice
   uint32_t xo[XI];              // lane's activation source offsets (or kOOR)
   uint32_t sro;                 // lane's scale byte offset in LDS for strip 0 (row 64 wv + nl, + g)
   uint32_t aso;                 // (kAS) lane's activation scale row offset, or kOOR
@@ -247,21 +248,28 @@ struct TiledGemm {
   // 16-byte pieces at q[NQ t .. NQ t + NQ)), then the activations into a
   // stage of LDS (kAS: adst = where this wave's activation-scale load lands).
   // Past the last chunk both move no data.
+  // With NSL weight slices per workgroup, chunk c of the run is chunk
+  // c % nch of slice c / nch (the next slice's weights sit wsd bytes further,
+  // the activation chunk is the same).
+  template <int NSL = 1>
   __device__ __forceinline__ void issue_w(int c, u32x4_t (&q)[4 * NQ]) const {
-    const bool ok = c < nch;
+    const bool ok = c < NSL * nch;
+    const bool hi = NSL > 1 && c >= nch;
     const uint32_t oor = ok ? 0u : kOOR;
-    const uint32_t cc = ok ? (uint32_t)c : 0u;
+    const uint32_t cc = ok ? (uint32_t)(hi ? c - nch : c) : 0u;
+    const uint32_t so = hi ? wsd : 0u;
 #pragma unroll
     for (int t = 0; t < 4; ++t)
 #pragma unroll
       for (int hq = 0; hq < NQ; ++hq)
-        q[NQ * t + hq] = stream ? bload16_nt(w, wo[t] | oor, wnat_chunk(cc, NQ, hq))
-                                : bload16(w, wo[t] | oor, wnat_chunk(cc, NQ, hq));
+        q[NQ * t + hq] = stream ? bload16_nt(w, wo[t] | oor, wnat_chunk(cc, NQ, hq) + so)
+                                : bload16(w, wo[t] | oor, wnat_chunk(cc, NQ, hq) + so);
   }
+  template <int NSL = 1>
   __device__ __forceinline__ void issue_x(uint8_t* base, int c, uint8_t* adst = nullptr) const {
-    const bool ok = c < nch;
+    const bool ok = c < NSL * nch;
     const uint32_t oor = ok ? 0u : kOOR;
-    const uint32_t cc = ok ? (uint32_t)c : 0u;
+    const uint32_t cc = ok ? (uint32_t)(NSL > 1 && c >= nch ? c - nch : c) : 0u;
     if constexpr (kAS) load_to_lds4(as, aso | oor, kSStep * cc, adst);
 #pragma unroll
     for (int i = 0; i < XI; ++i)
@@ -365,11 +373,24 @@ struct TiledGemm {
   // scale rows, issued first, are complete once the first stage is.
   // wrow(r): byte offset of weight scale row r; arow(r): of the tile's
   // activation scale row r (MXFP4) or kOOR.
-  template <int NMT, class WRow, class ARow>
+  //
+  // NSL = 2: the workgroup's two weight slices one after the other in one
+  // pipeline (the second slice's first chunks load while the first's last
+  // ones compute); both slices' scales are staged up front, the second's
+  // 1 KiB * ceil(Q) further; after the first slice's last chunk
+  // between(acc) stores its result and the accumulators restart at zero.
+  // BP = (nch - 1) % NS: the stage of the first slice's last chunk, so that
+  // one unrolled position holds the code between the slices.
+  template <int NMT, int NSL = 1, int BP = 0, class WRow, class ARow, class Between>
   __device__ __forceinline__ void run(uint8_t* const (&stages)[NS], uint8_t* sc, uint8_t* asc,
-                                      WRow wrow, ARow arow, floatx4_t (&acc)[MT][4]) {
+                                      WRow wrow, ARow arow, floatx4_t (&acc)[MT][4],
+                                      Between&& between) {
     u32x4_t q[NS][4 * NQ];
-    if (wave < 4) stage_rows<64>(sc, ws, wrow);
+    const int scs = 1024 * ((64 * Q + 63) / 64);
+    if (wave < 4) {
+      stage_rows<64>(sc, ws, wrow);
+      if constexpr (NSL > 1) stage_rows<64>(sc + scs, ws, [&](int r) { return wrow(r) + ssd; });
+    }
     // kAS: slot u's activation scales at asc + 4 BM u (waves w < BM / 64
     // load rows 64 w + lane; the others write zeros past the slots)
     auto aslot = [&](int u) -> uint8_t* { return kAS ? asc + 4 * BM * u : asc; };
@@ -383,10 +404,11 @@ struct TiledGemm {
     }
 #pragma unroll
     for (int u = 0; u < NS - 1; ++u) {
-      issue_w(u, q[u]);
-      issue_x(stages[u], u, adst(u));
+      issue_w<NSL>(u, q[u]);
+      issue_x<NSL>(stages[u], u, adst(u));
     }
-    for (int c0 = 0; c0 < nch; c0 += NS) {
+    const int ntot = NSL * nch;
+    for (int c0 = 0; c0 < ntot; c0 += NS) {
 #pragma unroll
       for (int u = 0; u < NS; ++u) {
         const int c = c0 + u;
@@ -395,13 +417,31 @@ struct TiledGemm {
         // finished with (chunk c - 1's): they need not wait for the other
         // waves; the activations refill the stage chunk c - 1 was read
         // from, after the barrier that retires every read of it.
-        issue_w(c + NS - 1, q[(u + NS - 1) % NS]);
+        issue_w<NSL>(c + NS - 1, q[(u + NS - 1) % NS]);
         stage_barrier();
-        issue_x(stages[(u + NS - 1) % NS], c + NS - 1, adst((u + NS - 1) % NS));
-        if (c < nch) compute<NMT>(stages[u] + half * 64 * 256, sc, aslot(u), c, q[u], acc);
+        issue_x<NSL>(stages[(u + NS - 1) % NS], c + NS - 1, adst((u + NS - 1) % NS));
+        if constexpr (NSL == 1) {
+          if (c < nch) compute<NMT>(stages[u] + half * 64 * 256, sc, aslot(u), c, q[u], acc);
+        } else if (c < ntot) {
+          const bool hi = c >= nch;
+          compute<NMT>(stages[u] + half * 64 * 256, hi ? sc + scs : sc, aslot(u),
+                       hi ? c - nch : c, q[u], acc);
+          if (u == BP && c == nch - 1) {
+            between(acc);
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+              for (int t = 0; t < 4; ++t) acc[mt][t] = (floatx4_t){0.f, 0.f, 0.f, 0.f};
+          }
+        }
       }
     }
     wait_vmcnt<0>();
+  }
+  template <int NMT, class WRow, class ARow>
+  __device__ __forceinline__ void run(uint8_t* const (&stages)[NS], uint8_t* sc, uint8_t* asc,
+                                      WRow wrow, ARow arow, floatx4_t (&acc)[MT][4]) {
+    run<NMT, 1>(stages, sc, asc, wrow, arow, acc, [](floatx4_t (&)[MT][4]) {});
   }
 };
 
@@ -526,10 +566,20 @@ __device__ __forceinline__ void with_lds(Body&& body) {
 // activation-code offsets and the activation-scale rows), then the pipeline.
 // direct(r) = source row of tile row r < rows; wrow(r) = byte offset of
 // weight scale row r; arow_bytes = activation scale bytes per source row.
-template <int BM, bool kFP4A, bool kW8, int KV, bool kBlk, class Direct, class WRow>
+// NSL, between: the weight slices per workgroup and what runs between them
+// (bf16 activations, 64-row tiles).
+struct NoBetween {
+  template <class A>
+  __device__ void operator()(A&) const {}
+};
+
+template <int BM, bool kFP4A, bool kW8, int KV, bool kBlk, int NSL = 1, class Direct, class WRow,
+          class Between = NoBetween>
 __device__ __forceinline__ void tile_loop(TiledGemm<BM, kFP4A, kW8, KV, kBlk>& G, const TileT& ti, Direct direct,
                                           WRow wrow, uint32_t row_bytes, uint32_t arow_bytes,
-                                          floatx4_t (&acc)[TiledGemm<BM, kFP4A, kW8, KV, kBlk>::MT][4]) {
+                                          floatx4_t (&acc)[TiledGemm<BM, kFP4A, kW8, KV, kBlk>::MT][4],
+                                          Between&& between = {}) {
+  static_assert(NSL == 1 || (BM == 64 && !kFP4A), "two slices: bf16 64-row tiles");
   with_lds<BM, kFP4A, kW8, KV, kBlk>([&](auto& stages, uint8_t* sc, uint8_t* asc, int32_t* srow) {
     if constexpr (kBlk) {
       plan_x<BM, kFP4A, kW8, KV, kBlk>(G, ti, direct, row_bytes);
@@ -563,7 +613,16 @@ __device__ __forceinline__ void tile_loop(TiledGemm<BM, kFP4A, kW8, KV, kBlk>& G
       plan_x<BM, kFP4A, kW8, KV, kBlk>(G, ti, direct, row_bytes);
       auto arow = [](int) -> uint32_t { return kOOR; };
       with_nmt<BM>(ti.rows, [&](auto n) {
-        G.template run<decltype(n)::value>(stages, sc, asc, wrow, arow, acc);
+        constexpr int NMT = decltype(n)::value;
+        if constexpr (NSL == 1) {
+          G.template run<NMT>(stages, sc, asc, wrow, arow, acc);
+        } else {
+          static_assert(TiledGemm<BM, kFP4A, kW8, KV, kBlk>::NS == 3, "three stages");
+          const int bp = (G.nch - 1) % 3;
+          if (bp == 0) G.template run<NMT, NSL, 0>(stages, sc, asc, wrow, arow, acc, between);
+          else if (bp == 1) G.template run<NMT, NSL, 1>(stages, sc, asc, wrow, arow, acc, between);
+          else G.template run<NMT, NSL, 2>(stages, sc, asc, wrow, arow, acc, between);
+        }
       });
     }
   });
@@ -673,7 +732,9 @@ __global__ __launch_bounds__((TileCfg<BM, kFP4A, kW8, KV, kBlk>::kThreads), KV ?
 }
 
 // down: weight rows j in [256 s, 256 s + 256); wave w owns [256 s + 64 w, +64).
-template <int BM, bool kFP4A, bool kW8, int KV = 0, bool kBlk = false>
+// NSL = 2 (bf16 64-row tiles): the workgroup takes slices 2 s and 2 s + 1 of
+// its tile in one pipeline, the first slice's y stored between them.
+template <int BM, bool kFP4A, bool kW8, int KV = 0, bool kBlk = false, int NSL = 1>
 __global__ __launch_bounds__((TileCfg<BM, kFP4A, kW8, KV, kBlk>::kThreads), KV ? 2 : 1) void down_tiled_kernel(
     const void* __restrict__ hin, const uint8_t* __restrict__ hscale,
     const int32_t* __restrict__ offsets, const int32_t* __restrict__ tiles,
@@ -682,7 +743,9 @@ __global__ __launch_bounds__((TileCfg<BM, kFP4A, kW8, KV, kBlk>::kThreads), KV ?
     uint8_t* __restrict__ ye) {
   TileT ti;
   int s;
-  if (!tile_slice<BM, kFP4A, 4>(blockIdx.x, tiles, offsets, *num_tiles, H / 256, &ti, &s)) return;
+  if (!tile_slice<BM, kFP4A, 4>(blockIdx.x, tiles, offsets, *num_tiles, H / 256 / NSL, &ti, &s))
+    return;
+  s *= NSL;
   // (debug builds: a tile whose rows leave [0, A) stores nothing)
   if (!MOE_DOK(ti.row0 >= 0 && ti.rows > 0 && (int64_t)ti.row0 + ti.rows <= (int64_t)A, kDbgTiles))
     return;
@@ -694,6 +757,8 @@ __global__ __launch_bounds__((TileCfg<BM, kFP4A, kW8, KV, kBlk>::kThreads), KV ?
   const bool idle = G.kM2 && ti.rows <= 64 * G.half;   // an upper half with no rows
 #pragma unroll
   for (int st = 0; st < 4; ++st) G.wo[st] = idle ? kOOR : wnat_lane((j0 >> 4) + st, I, G.NQ, G.lane);
+  G.wsd = wnat_lane(16, I, G.NQ, 0);                    // the next slice: 16 strips on
+  G.ssd = 256 * rs;
   if (kFP4A) {
     const size_t nr = kBlk ? ((size_t)A + 15) / 16 * 16 : (size_t)A;
     G.a = make_rsrc(hin, (uint32_t)(nr * rb));
@@ -713,7 +778,6 @@ __global__ __launch_bounds__((TileCfg<BM, kFP4A, kW8, KV, kBlk>::kThreads), KV ?
   for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
     for (int st = 0; st < 4; ++st) acc[mt][st] = (floatx4_t){0.f, 0.f, 0.f, 0.f};
-  tile_loop<BM, kFP4A, kW8, KV, kBlk>(G, ti, srow, wrow, kFP4A ? rb : (uint32_t)I * 2, rs, acc);
   const int m0 = 64 * G.half;               // the wave's first tile row
 
   // y in the staged fp16 format.  Lane 16 g + n holds tile row 16 mt + n at
@@ -721,6 +785,7 @@ __global__ __launch_bounds__((TileCfg<BM, kFP4A, kW8, KV, kBlk>::kThreads), KV ?
   // 4 g + r -> column j0 + 32 p + 8 g + 4 u + r): one 16-byte store per
   // pair.  A pair's 32 columns are one exponent group, spread over lanes
   // n, n + 16, n + 32 and n + 48.
+  auto store_y = [&](floatx4_t (&acc)[MT][4], int j0) {
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) {
     uint32_t f = 0;
@@ -749,6 +814,14 @@ __global__ __launch_bounds__((TileCfg<BM, kFP4A, kW8, KV, kBlk>::kThreads), KV ?
             (uint16_t)((e[0] + 127) | (e[1] + 127) << 8);
     }
   }
+  };
+  if constexpr (NSL == 1) {
+    tile_loop<BM, kFP4A, kW8, KV, kBlk>(G, ti, srow, wrow, kFP4A ? rb : (uint32_t)I * 2, rs, acc);
+  } else {
+    tile_loop<BM, kFP4A, kW8, KV, kBlk, NSL>(G, ti, srow, wrow, (uint32_t)I * 2, rs, acc,
+                                             [&](floatx4_t (&a)[MT][4]) { store_y(a, j0); });
+  }
+  store_y(acc, j0 + 256 * (NSL - 1));
 }
 
 template <int BM, bool kFP4A, bool kW8 = false, int KV = 0, bool kBlk = false>
@@ -773,14 +846,14 @@ hipError_t launch_gate_up_bm(const void* act, const uint8_t* act_scale, const in
   return hipGetLastError();
 }
 
-template <int BM, bool kFP4A, bool kW8 = false, int KV = 0, bool kBlk = false>
+template <int BM, bool kFP4A, bool kW8 = false, int KV = 0, bool kBlk = false, int NSL = 1>
 hipError_t launch_down_bm(const void* h, const uint8_t* h_scale, const int32_t* offsets,
                           const int32_t* tiles, const int32_t* num_tiles, int max_tiles,
                           const uint8_t* w2, const uint8_t* w2s, int A, int H, int I, uint16_t* y,
                           hipStream_t stream) {
-  const unsigned grid = tile_slice_grid<kFP4A>(max_tiles, H / 256);
+  const unsigned grid = tile_slice_grid<kFP4A>(max_tiles, H / 256 / NSL);
   uint8_t* ye = reinterpret_cast<uint8_t*>(y) + (size_t)A * H * 2;   // the group exponents
-  hipLaunchKernelGGL((down_tiled_kernel<BM, kFP4A, kW8, KV, kBlk>), dim3(grid),
+  hipLaunchKernelGGL((down_tiled_kernel<BM, kFP4A, kW8, KV, kBlk, NSL>), dim3(grid),
                      dim3(TileCfg<BM, kFP4A, kW8, KV, kBlk>::kThreads), 0, stream, h,
                      h_scale, offsets, tiles, num_tiles, w2, w2s, A, H, I, y, ye);
   return hipGetLastError();
@@ -886,8 +959,13 @@ hipError_t launch_down_tiled(int tile_m, int act_fmt, int wfmt, const void* h,
   if (act_fmt)
     return down_fp4<false>(tile_m, h, h_scale, offsets, tiles, num_tiles, max_tiles, w2, w2s, A, H,
                            I, y, stream);
-  return tile_m == 128 ? launch_down_bm<128, false>(h, h_scale, offsets, tiles, num_tiles, max_tiles,
-                                                    w2, w2s, A, H, I, y, stream)
-                       : launch_down_bm<64, false>(h, h_scale, offsets, tiles, num_tiles, max_tiles,
-                                                   w2, w2s, A, H, I, y, stream);
+  if (tile_m == 128)
+    return launch_down_bm<128, false>(h, h_scale, offsets, tiles, num_tiles, max_tiles, w2, w2s, A,
+                                      H, I, y, stream);
+  // two slices per workgroup where their scales fit beside each other
+  if ((H / 256) % 2 == 0 && 2 * I <= TileCfg<64, false>::KMAX)
+    return launch_down_bm<64, false, false, 0, false, 2>(h, h_scale, offsets, tiles, num_tiles,
+                                                         max_tiles, w2, w2s, A, H, I, y, stream);
+  return launch_down_bm<64, false>(h, h_scale, offsets, tiles, num_tiles, max_tiles, w2, w2s, A, H,
+                                   I, y, stream);
 }
