@@ -52,6 +52,15 @@ SMALL = {
     "tiled128": synth.custom_config("tiled128", T=300, H=512, I=256, E=16, K=3, shared=1),
     "tiled128_w4a4": synth.custom_config("tiled128_w4a4", T=300, H=512, I=256, E=16, K=3,
                                          shared=1, act_fmt=synth.ACT_MXFP4, outlier_p=0.002),
+    # the bf16 64-row down GEMM taking two weight slices per workgroup: the
+    # first slice's y is stored after chunk I/128 - 1, at pipeline stage
+    # (I/128 - 1) mod 3 (I = 256 and 1024 elsewhere give stage 1)
+    "two_slices_stage0_i128": synth.custom_config("two_slices_stage0_i128", T=200, H=512, I=128,
+                                                  E=16, K=4, shared=1),
+    "two_slices_stage0_i512": synth.custom_config("two_slices_stage0_i512", T=200, H=1024, I=512,
+                                                  E=16, K=4, shared=1),
+    "two_slices_stage2_i384": synth.custom_config("two_slices_stage2_i384", T=200, H=512, I=384,
+                                                  E=16, K=4, shared=1),
     # reductions in (2048, 6144]: the MXFP4 128-row kernels that bring the
     # activation scales with each stage (gate/up and down)
     "tiled128_w4a4_k2560": synth.custom_config("tiled128_w4a4_k2560", T=200, H=2560, I=2560,
