@@ -64,6 +64,7 @@ def _declare(L):
                                      c.c_int, i32, i32, P, i64, c.c_int, P, P, P, P, P, P]),
         "oracle_forward_from_h": (c.c_int, [P, P, P, P, P, i64, i64, i64, i32, i32, i32, c.c_int,
                                             c.c_int, i32, i32, c.c_int, P, P]),
+        "oracle_residual_rmsnorm": (c.c_int, [P, i32, P, P, dbl, i64, i64, P, P, P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(L, name)

@@ -45,6 +45,12 @@ it in fp64 over exact products.
 Expert weights may also be MXFP8 (oracle/mxfp8.py), with bf16 activations;
 everything else is unchanged.
 
+After the layer, a tensor-parallel decode sums the ranks' partial outputs,
+adds the residual stream and applies RMSNorm in one step (VibeSys post,
+section "Communication and concurrency": the all-reduce replaced by a
+one-shot one fused with the residual add and RMSNorm): residual_rmsnorm,
+with RMSNorm in its textbook form (the pages do not define it).
+
 Pins: tests/test_oracle_moe.py, tests/golden/route_align.json,
 tests/golden/w4a4_worked.json.
 """
@@ -90,6 +96,28 @@ def route(logits: np.ndarray, gate, K: int, shared: int, renormalize: bool = Tru
     check(lib().oracle_route(ptr(l), ptr(g), T, E, K, shared, int(bool(renormalize)), ptr(ids),
                              ptr(w)), "route")
     return ids, w
+
+
+def residual_rmsnorm(partials_bits: np.ndarray, residual_bits, gamma_bits: np.ndarray,
+                     eps: float):
+    """Partial outputs bf16 bits [G, T, H] summed, the residual [T, H] (bf16
+    bits, or None for zeros) added, then RMSNorm with gamma [H] (bf16 bits):
+    h = bf16(residual + sum_g partial_g) (fp64 sums of exact values),
+    y = bf16(h / sqrt(mean_j h^2 + eps) * gamma).  Returns (h bits, y bits,
+    rstd fp64 [T])."""
+    p = np.ascontiguousarray(partials_bits, dtype=np.uint16)
+    G, T, H = p.shape
+    gm = np.ascontiguousarray(gamma_bits, dtype=np.uint16)
+    assert gm.shape == (H,)
+    r = None if residual_bits is None else np.ascontiguousarray(residual_bits, dtype=np.uint16)
+    assert r is None or r.shape == (T, H)
+    h = np.empty((T, H), dtype=np.uint16)
+    y = np.empty((T, H), dtype=np.uint16)
+    rstd = np.empty(T, dtype=np.float64)
+    check(lib().oracle_residual_rmsnorm(ptr(p), G, None if r is None else ptr(r), ptr(gm),
+                                        float(eps), T, H, ptr(h), ptr(y), ptr(rstd)),
+          "residual_rmsnorm")
+    return h, y, rstd
 
 
 def router_logits(x_bits: np.ndarray, w_bits: np.ndarray, threads: int | None = None) -> np.ndarray:

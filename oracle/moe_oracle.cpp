@@ -667,4 +667,31 @@ int oracle_forward_from_h(const uint16_t *h_bits, const float *logits, const flo
   return 0;
 }
 
+// The partial outputs of G ranks summed, the residual added, then RMSNorm
+// (VibeSys post, section "Communication and concurrency": the all-reduce
+// fused with the residual add and RMSNorm; RMSNorm in its textbook form).
+// Each row: h = bf16(residual + sum of the partials), fp64 sums of exact
+// bf16 values; then the mean of h^2 over the row, and y = bf16(h * rstd * gamma).
+int oracle_residual_rmsnorm(const uint16_t *partials, int32_t G, const uint16_t *residual,
+                            const uint16_t *gamma, double eps, int64_t T, int64_t H,
+                            uint16_t *h_out, uint16_t *y_out, double *rstd_out) {
+  if (!partials || !gamma || !h_out || !y_out || G < 1 || T < 0 || H < 1 || !(eps >= 0.0))
+    return -1;
+  std::vector<double> h(H);
+  for (int64_t t = 0; t < T; ++t) {
+    double ss = 0.0;
+    for (int64_t j = 0; j < H; ++j) {
+      double s = residual ? bf16_value(residual[t * H + j]) : 0.0;
+      for (int32_t g = 0; g < G; ++g) s += bf16_value(partials[(g * T + t) * H + j]);
+      h[j] = round_bf16(s);
+      h_out[t * H + j] = bf16_bits(h[j]);
+      ss += h[j] * h[j];
+    }
+    const double rstd = 1.0 / std::sqrt(ss / static_cast<double>(H) + eps);
+    if (rstd_out) rstd_out[t] = rstd;
+    for (int64_t j = 0; j < H; ++j) y_out[t * H + j] = bf16_bits(h[j] * rstd * bf16_value(gamma[j]));
+  }
+  return 0;
+}
+
 }  // extern "C"

@@ -23,6 +23,8 @@
  *           over exactly decoded MXFP4 (or MXFP8) weights, fp64 dot
  *           products (VibeSys post, section "Baseline": MXFP4 weights
  *           dequantised inside the MoE kernel; the SwiGLU expert MLP)
+ *   norm    the residual add and RMSNorm after the layer's partial outputs
+ *           are summed (oracle_residual_rmsnorm below)
  *   forward out[t] = bf16( sum_k w[t,k] * MLP_{ids[t,k]}(x_t) ), slots summed
  *           in order (optionally each MLP output rounded to bf16 first).  For W4A4 the activations and h go through
  *           MXFP4 quantise-then-decode before their GEMM (OpenRelay "Gemma 4
@@ -165,6 +167,21 @@ int oracle_forward_from_h(const uint16_t *h_bits, const float *logits, const flo
                           int64_t H, int64_t I, int32_t E, int32_t K, int32_t shared, int act_fmt,
                           int wfmt, int32_t renormalize, int32_t round_y, int threads,
                           uint16_t *out_bits, double *out_f64);
+
+/* The step after the layer in a tensor-parallel decode: the G ranks' partial
+ * outputs summed (the all-reduce), the residual stream added, then RMSNorm;
+ * the pages replace the all-reduce with a one-shot one fused with the
+ * residual add and RMSNorm (VibeSys post, section "Communication and
+ * concurrency").  RMSNorm is not defined on the pages; the textbook form:
+ *   h[t, j] = bf16( residual[t, j] + sum_g partial[g][t, j] )   (new residual)
+ *   y[t, j] = bf16( h[t, j] / sqrt(mean_j h[t, j]^2 + eps) * gamma[j] )
+ * with the sum and the norm in fp64 on h's bf16 values.  partials: G arrays
+ * of T x H bf16 bits one after another ([G][T][H]); residual [T, H] and
+ * gamma [H] bf16 bits (residual may be NULL: zeros); G >= 1.  rstd_out [T]
+ * (may be NULL) receives 1 / sqrt(mean_j h^2 + eps). */
+int oracle_residual_rmsnorm(const uint16_t *partials, int32_t G, const uint16_t *residual,
+                            const uint16_t *gamma, double eps, int64_t T, int64_t H,
+                            uint16_t *h_out, uint16_t *y_out, double *rstd_out);
 
 /* The thread count `threads` <= 0 resolves to. */
 int oracle_default_threads(void);
