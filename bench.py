@@ -55,6 +55,10 @@ def parse():
     p.add_argument("--prefetch", action="store_true",
                    help="with --layers: each layer's combine prefetches the next layer's router "
                         "rows and shared expert into the caches")
+    p.add_argument("--epilogue", type=int, nargs="*", default=None, metavar="T",
+                   help="time only the step after the layer at tensor-parallel degree 8 "
+                        "(partials summed, residual added, RMSNorm) for these batch sizes "
+                        "(default: 64, 1536 and 8192 tokens) and print its record")
     p.add_argument("--pmc-calibrate", action="store_true",
                    help="first run a plain 1 GiB kernel (torch.bitwise_not) whose HBM bytes are "
                         "known, for scaling FETCH_SIZE / WRITE_SIZE counter passes")
@@ -266,6 +270,57 @@ def bench_layers(cfg, args):
 EXTRAS = ["prefill", "prefill_skewed", "w4a4"]      # timed beside the decode headline
 
 
+NORM_G, NORM_H, NORM_EPS = 8, 4096, 1e-6
+NORM_T = (64, 1536, 8192)          # the decode batch and the two prefill chunks
+
+
+def bench_residual_norm(args, sizes=NORM_T):
+    """The step after the layer at tensor-parallel degree 8, one GPU's share
+    of the pages' one-shot all-reduce with the residual add and RMSNorm fused
+    (VibeSys post, section "Communication and concurrency"): eight partial
+    outputs [T, H] summed, the residual added, RMSNorm, per batch size T.
+    args.steps back-to-back calls are captured in one HIP graph (the entry
+    point allocates and synchronises nothing, so it can be captured) and the
+    replay is timed with HIP events on its stream: the per-call time without
+    host launch overhead.  Algorithmic bytes: the G + 1 inputs read, h and y
+    written, gamma read once."""
+    from mxfp4_routed_expert_top_amd import ops
+    res = {}
+    for T in sizes:
+        p, r, g = synth.norm_inputs(NORM_G, T, NORM_H, seed=T)
+        parts = [p[i].to("cuda") for i in range(NORM_G)]
+        resid, gam = r.to("cuda"), g.to("cuda")
+        hout, y = torch.empty_like(resid), torch.empty_like(resid)
+
+        def call():
+            ops.residual_rmsnorm(parts, gam, NORM_EPS, residual=resid, residual_out=hout, out=y)
+
+        for _ in range(max(1, args.warmup)):
+            call()
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            for _ in range(args.steps):
+                call()
+        graph.replay()                       # the first replay uploads the graph
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s = torch.cuda.current_stream()
+        e0.record(s)
+        graph.replay()
+        e1.record(s)
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / args.steps
+        nbytes = (NORM_G + 1) * T * NORM_H * 2 + 2 * T * NORM_H * 2 + NORM_H * 2
+        gbs = nbytes / (us * 1e-6) / 1e9
+        res[f"T{T}"] = {"G": NORM_G, "T": T, "H": NORM_H, "us_per_call": round(us, 2),
+                        "algorithmic_bytes": nbytes, "gbs": round(gbs, 1),
+                        "hbm_frac": round(gbs / (HBM_PEAK_GBS), 4)}
+        log(f"residual_rmsnorm T={T}: {us:.2f} us per call, {gbs:.0f} GB/s")
+        del graph
+    return res
+
+
 def pct(a, q):
     return float(np.percentile(np.asarray(a), q))
 
@@ -468,6 +523,11 @@ def main():
         torch.cuda.synchronize()
         del a
         torch.cuda.empty_cache()
+    if args.epilogue is not None:
+        sizes = tuple(args.epilogue) or NORM_T
+        print(json.dumps({"epilogue_residual_rmsnorm": bench_residual_norm(args, sizes)}),
+              flush=True)
+        return
     head, head_w = measure(cfg, args, router=args.router)
     extras = {}
     want_extras = (not args.no_extras and args.workload == "decode" and not args.router)
@@ -479,6 +539,7 @@ def main():
             r, w = measure(c, args, weights=kept.get(key))
             kept.setdefault(key, w)
             extras[name] = r
+    epilogue = bench_residual_norm(args) if want_extras else None
     cpu = None
     if not args.no_cpu:
         cpu = cpu_baseline(cfg, router=args.router)
@@ -498,6 +559,8 @@ def main():
            "roofline": roofline, "layer": head, "cpu_baseline": cpu}
     if extras:
         res["workloads"] = extras
+    if epilogue:
+        res["epilogue_residual_rmsnorm"] = epilogue
     if "router" in head:
         res["router"] = head.pop("router")
     print(json.dumps(res), flush=True)

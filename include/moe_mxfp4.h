@@ -20,6 +20,8 @@
  *   0-6 in one call                                    moe_mxfp4_forward_router
  *   L layers of 0-6 in one call (a decode step's MoE layers)
  *                                                      moe_mxfp4_forward_layers
+ *   after the layer: partial outputs summed (tensor parallelism), residual
+ *   added, RMSNorm                                     moe_residual_rmsnorm
  *
  * The same layer over MXFP8 expert weights (bf16 activations; the pages
  * serve MoE models in MXFP8 next to MXFP4: MiniMax M3 on MI355X post,
@@ -406,6 +408,40 @@ MOE_API moe_status moe_expert_down(const void *h, const uint8_t *h_scale, int32_
  */
 MOE_API moe_status moe_combine(const void *y, const float *topk_weights, const int32_t *inv_assign,
                        int32_t T, int32_t H, int32_t Kp, uint16_t *out, void *stream);
+
+/*
+ * The step after the layer in a tensor-parallel decode, on one GPU's rows:
+ * the G ranks' partial outputs summed, the residual stream added, then
+ * RMSNorm.  The pages replace the per-layer all-reduce with a one-shot one
+ * fused with the residual add and RMSNorm (VibeSys "Qwen3.5-397B on 4x
+ * MI300A" post, section "Communication and concurrency"): each GPU reads
+ * every rank's partial output and normalises the rows itself.  This call is
+ * that epilogue over G buffers this GPU can address (on one GPU, the outputs
+ * of G shard layers; the library makes no inter-GPU mapping).  RMSNorm in
+ * its textbook form (the pages do not define it):
+ *   h[t, j] = bf16( residual[t, j] + sum_{g < G} partials[g][t, j] ),
+ *             summed in fp32 in that order;
+ *   out[t, j] = bf16( h[t, j] / sqrt(mean_j h[t, j]^2 + eps) * gamma[j] ),
+ *             the mean of squares in fp32 over h's bf16 values.
+ *   partials      HOST array of G (1..MOE_NORM_MAX_RANKS) device pointers,
+ *                 each bf16 [T, H], 16-byte aligned
+ *   residual      bf16 [T, H] or NULL (zeros)
+ *   gamma         bf16 [H]
+ *   eps           >= 0, finite
+ *   residual_out  out bf16 [T, H] = h, or NULL; may be `residual` itself
+ *   out           out bf16 [T, H]; may be partials[0] itself
+ * Buffers 16-byte aligned; H a multiple of 8, at most 16384.  T = 0 returns
+ * MOE_OK without reading any data pointer (the host array must still hold G).
+ * The kernel's fp32 arithmetic follows the definition while |h| <= 2^56 and
+ * mean_j h^2 + eps stays a normal fp32 number (eps > 0 keeps zero rows finite).
+ * Errors: INVALID_ARGUMENT (null or misaligned pointer, G outside
+ * 1..MOE_NORM_MAX_RANKS, negative T, bad eps), UNSUPPORTED (H).
+ */
+#define MOE_NORM_MAX_RANKS 8
+MOE_API moe_status moe_residual_rmsnorm(const uint16_t *const *partials, int32_t G,
+                                        const uint16_t *residual, const uint16_t *gamma,
+                                        float eps, int32_t T, int32_t H, uint16_t *residual_out,
+                                        uint16_t *out, void *stream);
 
 /*
  * MXFP8-quantise rows x cols values (packing float expert weights).  Per

@@ -117,3 +117,13 @@ hipError_t launch_down_tiled(int tile_m, int act_fmt, int wfmt, const void* h,
                              const int32_t* num_tiles, int max_tiles, const uint8_t* w2,
                              const uint8_t* w2s, int A, int H, int I, uint16_t* y,
                              hipStream_t stream);
+
+// G partial outputs summed, the residual added, RMSNorm (residual_norm.hip):
+// partials is a host array of G <= kMaxNormRanks device pointers (bf16
+// [T, H] each); H a multiple of 8, at most residual_rmsnorm_max_h();
+// residual and residual_out may be null.
+constexpr int kMaxNormRanks = 8;
+int residual_rmsnorm_max_h();
+hipError_t launch_residual_rmsnorm(const uint16_t* const* partials, int G, const uint16_t* residual,
+                                   const uint16_t* gamma, float eps, int T, int H,
+                                   uint16_t* residual_out, uint16_t* out, hipStream_t stream);

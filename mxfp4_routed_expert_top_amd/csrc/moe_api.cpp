@@ -5,6 +5,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <cmath>
 #include <mutex>
 
 #include "common.h"
@@ -445,6 +446,27 @@ moe_status moe_combine(const void* y, const float* topk_weights, const int32_t* 
     return MOE_ERR_INVALID_ARGUMENT;
   return from_hip(launch_combine(static_cast<const uint16_t*>(y), topk_weights, inv_assign, T, H,
                                  Kp, out, as_stream(stream)));
+}
+
+static_assert(MOE_NORM_MAX_RANKS == kMaxNormRanks, "the header's rank limit is the kernel's");
+
+moe_status moe_residual_rmsnorm(const uint16_t* const* partials, int32_t G,
+                                const uint16_t* residual, const uint16_t* gamma, float eps,
+                                int32_t T, int32_t H, uint16_t* residual_out, uint16_t* out,
+                                void* stream) {
+  if (!partials || G < 1 || G > MOE_NORM_MAX_RANKS || T < 0 || H <= 0 || !(eps >= 0.f) ||
+      !std::isfinite(eps))
+    return MOE_ERR_INVALID_ARGUMENT;
+  if (H % 8 || H > residual_rmsnorm_max_h()) return MOE_ERR_UNSUPPORTED;
+  if (T == 0) return MOE_OK;
+  if (!gamma || !out) return MOE_ERR_INVALID_ARGUMENT;
+  for (int32_t g = 0; g < G; ++g)
+    if (!partials[g] || !aligned16(partials[g])) return MOE_ERR_INVALID_ARGUMENT;
+  if (!aligned16(gamma) || !aligned16(out) || (residual && !aligned16(residual)) ||
+      (residual_out && !aligned16(residual_out)))
+    return MOE_ERR_INVALID_ARGUMENT;
+  return from_hip(launch_residual_rmsnorm(partials, G, residual, gamma, eps, T, H, residual_out,
+                                          out, as_stream(stream)));
 }
 
 int32_t moe_gemm_tile_m(int32_t T, int32_t Kp, int32_t Ep, int32_t H, int32_t I,

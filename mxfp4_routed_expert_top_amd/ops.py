@@ -53,6 +53,7 @@ _SIGS = {
     "moe_expert_down": (_I32, [_P, _P, _I32, _P, _P, _P, _I32, _P, _P, _I32, _I32, _I32, _I32,
                                _I32, _P, _P]),
     "moe_combine": (_I32, [_P, _P, _P, _I32, _I32, _I32, _P, _P]),
+    "moe_residual_rmsnorm": (_I32, [_P, _I32, _P, _P, ctypes.c_float, _I32, _I32, _P, _P, _P]),
     "moe_gemm_tile_m": (_I32, [_I32, _I32, _I32, _I32, _I32, _I32]),
     "moe_mxfp4_workspace_size": (_SZ, [_I32, _I32, _I32, _I32, _I32, _I32, _I32]),
     "moe_mxfp4_forward": (_I32, [_P, _P, _P, _P, _P, _P, _P, _I32, _I32, _I32, _I32, _I32, _I32,
@@ -442,6 +443,33 @@ def combine(y, topk_weights, inv, T: int, H: int, Kp: int, out=None, stream=None
     _check("moe_combine", lib().moe_combine(
         _ptr(y), _ptr(topk_weights), _ptr(inv), T, H, Kp, _ptr(out), _stream(stream)))
     return out
+
+
+NORM_MAX_RANKS = 8
+
+
+def residual_rmsnorm(partials, gamma, eps: float, residual=None, residual_out=None, out=None,
+                     stream=None):
+    """moe_residual_rmsnorm: the G partial outputs (a list of bf16 [T, H]
+    tensors) summed, residual added, RMSNorm with gamma (bf16 [H]).  Returns
+    (out, residual_out); residual_out may be the residual tensor itself
+    (updated in place) or None (not written)."""
+    G = len(partials)
+    T, H = partials[0].shape
+    for p in partials:
+        _dt(p, torch.bfloat16, "partials")
+        if tuple(p.shape) != (T, H):
+            raise ValueError("partials: every one of shape [T, H]")
+    _dt(gamma, torch.bfloat16, "gamma")
+    _dt(residual, torch.bfloat16, "residual")
+    _dt(residual_out, torch.bfloat16, "residual_out")
+    if out is None:
+        out = torch.empty(T, H, dtype=torch.bfloat16, device=partials[0].device)
+    ptrs = (ctypes.c_void_p * G)(*[_ptr(p) for p in partials])
+    _check("moe_residual_rmsnorm", lib().moe_residual_rmsnorm(
+        ptrs, G, _ptr(residual), _ptr(gamma), float(eps), T, H, _ptr(residual_out), _ptr(out),
+        _stream(stream)))
+    return out, residual_out
 
 
 # ------------------------------------------------------------ whole layer --

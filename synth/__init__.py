@@ -43,6 +43,7 @@ STREAM_W2 = 5
 STREAM_OUTLIER = 6
 STREAM_SKEW = 7
 STREAM_ROUTER = 8
+STREAM_NORM = 9
 
 ACT_BF16 = 0    # W4A16: bf16 activations
 ACT_MXFP4 = 1   # W4A4: activations quantised to MXFP4 on the fly
@@ -215,3 +216,16 @@ def ties_logits(T: int, E: int, seed: int) -> torch.Tensor:
     vals = torch.tensor([-0.0, 0.0, 0.5, -0.5, 1.0, -1.0], dtype=torch.float32)
     idx = torch.randint(0, vals.numel(), (T, E), generator=g)
     return vals[idx]
+
+
+def norm_inputs(G: int, T: int, H: int, seed: int, part_std: float = 0.5):
+    """Inputs of the step after the layer (partial outputs summed, residual
+    added, RMSNorm): G partial outputs bf16 [G, T, H] ~ N(0, part_std^2)
+    (one tensor-parallel rank's share of the layer output each), the residual
+    stream bf16 [T, H] ~ N(0, 1) and gamma bf16 [H] ~ U(0.5, 1.5)
+    (CPU tensors)."""
+    g = _gen(seed, STREAM_NORM)
+    p = torch.randn(G, T, H, generator=g, dtype=torch.float32).mul_(part_std)
+    r = torch.randn(T, H, generator=g, dtype=torch.float32)
+    gamma = torch.rand(H, generator=g, dtype=torch.float32).add_(0.5)
+    return p.to(torch.bfloat16), r.to(torch.bfloat16), gamma.to(torch.bfloat16)

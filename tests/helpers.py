@@ -203,3 +203,43 @@ class Problem:
         c = self.cfg
         return ops.forward_stages(self.x, self.logits, self.gate, self.w13, self.w13s, self.w2,
                                   self.w2s, c.I, c.E, c.K, c.shared, c.act_fmt, **kw)
+
+
+def bf16_ulp(v):
+    """Spacing of bf16 values at |v| (normal range; v != 0)."""
+    return np.ldexp(1.0, np.floor(np.log2(np.abs(v))).astype(np.int64) - 7)
+
+
+def check_residual_rmsnorm(p_bits, r_bits, g_bits, eps, h_gpu, y_gpu, what=""):
+    """The kernel's h and y (bf16 bits) against the oracle on the same inputs.
+
+    h: the kernel sums residual and partials in fp32, the oracle in fp64; for
+    bf16 inputs the fp32 sum is exact unless their exponents span more than
+    16 bits, and even then its bf16 rounding changes only when the sum lies
+    within an fp32 rounding of a bf16 midpoint.  So h must be equal, with at
+    most one element in 10^4 one bf16 ulp away.
+    y: the kernel's fp32 mean of squares, reciprocal square root and two
+    products carry a relative error of a few times 1e-7 (up to H * 2^-24 for
+    the sum), far below half a bf16 ulp (2^-9), so its bf16 y is one of the
+    two bf16 neighbours of the exact y = h * rstd * gamma: |y - y_exact| <=
+    one bf16 ulp of y_exact, and exact rounding almost everywhere (>= 99%).
+    Elements whose h differed are left out of the y check."""
+    want_h, _, rstd = moe.residual_rmsnorm(p_bits, r_bits, g_bits, eps)
+    hg, hw = mxfp4.bf16_to_f64(h_gpu), mxfp4.bf16_to_f64(want_h)
+    diff = hg != hw
+    n = hw.size
+    assert diff.sum() <= max(0, n // 10000), f"{what}: {diff.sum()} h elements differ"
+    if diff.any():
+        assert np.all(np.abs(hg[diff] - hw[diff]) <= bf16_ulp(hw[diff])), f"{what}: h off by > 1 ulp"
+    gam = mxfp4.bf16_to_f64(g_bits)
+    y_exact = hw * rstd[:, None] * gam[None, :]
+    yg = mxfp4.bf16_to_f64(y_gpu)
+    ok = ~diff
+    zero = ok & (y_exact == 0)
+    assert np.all(yg[zero] == 0), f"{what}: y of a zero h is not zero"
+    nz = ok & (y_exact != 0)
+    err = np.abs(yg[nz] - y_exact[nz])
+    assert np.all(err <= bf16_ulp(y_exact[nz])), f"{what}: y off by more than one bf16 ulp"
+    exact = np.mean(y_gpu[ok] == mxfp4.bf16_bits(y_exact[ok]))
+    assert exact >= 0.99, f"{what}: only {exact:.4f} of y rounded exactly"
+    return int(diff.sum()), float(exact)

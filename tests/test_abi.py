@@ -26,7 +26,7 @@ def declared_functions():
 def test_library_loads_and_exports_every_declared_symbol():
     lib = ops.lib()
     names = declared_functions()
-    assert len(names) == 27
+    assert len(names) == 28
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(ops.EXPORTS)
@@ -141,6 +141,33 @@ def test_route_align_argument_errors():
     assert call(E=2048, K=4) == UNSUPPORTED              # E > 1024
     assert call(E=64, K=32) == UNSUPPORTED               # K' = 33
     assert call(wsb=ws - 1) == WS_SMALL
+
+
+def test_residual_rmsnorm_argument_errors():
+    f = ops.lib().moe_residual_rmsnorm
+    two = (ctypes.c_void_p * 2)(FAKE, FAKE)
+    def call(**kw):
+        a = dict(p=two, G=2, r=FAKE, gm=FAKE, eps=1e-6, T=4, H=4096, ro=FAKE, o=FAKE)
+        a.update(kw)
+        return f(a["p"], a["G"], a["r"], a["gm"], a["eps"], a["T"], a["H"], a["ro"], a["o"], None)
+    assert call(p=None) == INVALID
+    assert call(G=0) == INVALID
+    assert call(G=9) == INVALID                                       # above MOE_NORM_MAX_RANKS
+    assert call(p=(ctypes.c_void_p * 2)(FAKE, None)) == INVALID       # a null partial
+    assert call(p=(ctypes.c_void_p * 2)(FAKE, MIS)) == INVALID        # a misaligned partial
+    assert call(gm=None) == INVALID
+    assert call(o=None) == INVALID
+    assert call(r=MIS) == INVALID
+    assert call(ro=MIS) == INVALID
+    assert call(T=-1) == INVALID
+    assert call(eps=-1.0) == INVALID
+    assert call(eps=float("nan")) == INVALID
+    assert call(eps=float("inf")) == INVALID
+    assert call(H=4100) == UNSUPPORTED                                # not a multiple of 8
+    assert call(H=16392) == UNSUPPORTED                               # above 16384
+    assert call(T=0) == OK                                            # nothing to do
+    assert call(T=0, r=None, ro=None, gm=None, o=None) == OK          # no data pointer read
+    assert call(T=0, H=4100) == UNSUPPORTED                           # the shape still checked
 
 
 def test_quantize_argument_errors():

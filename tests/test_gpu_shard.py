@@ -7,7 +7,11 @@ G shard layers run one after another on one GPU, from slices of the same
 packed weights: routing must be identical, each shard's h must be the exact
 column slice of the full layer's h, each shard's output must match the
 oracle's layer on the same weight slices (the layer's tolerance), and the
-sum of the shards' outputs must match the full layer.
+sum of the shards' outputs must match the full layer.  The step that
+follows the layer in such a split, the ranks' outputs summed with the
+residual added and RMSNorm applied (moe_residual_rmsnorm, the epilogue of
+the pages' one-shot all-reduce), then runs on the G shard outputs with x as
+the residual stream and is checked against the oracle on the same bits.
 
 The sum carries roundings the single layer does not: each shard rounds its
 own y and out to bf16 (relative error <= 2^-9 each), and the shards' parts
@@ -22,8 +26,8 @@ import torch
 
 import synth
 from oracle import moe
-from tests.helpers import (DEV, MAX_ABS_RMS, REL_L2, W_ATOL, Problem, bits, max_abs_over_rms,
-                           oracle_pack_all, rel_l2)
+from tests.helpers import (DEV, MAX_ABS_RMS, REL_L2, W_ATOL, Problem, bits,
+                           check_residual_rmsnorm, max_abs_over_rms, oracle_pack_all, rel_l2)
 
 pytestmark = pytest.mark.gpu
 
@@ -77,6 +81,7 @@ def test_tensor_parallel_shards_sum_to_the_layer(name):
     tokens = None                      # every token against the oracle
     oracle_pack_all(c, np.unique(full["ids"].cpu().numpy()))
     acc = torch.zeros(c.T, c.H, dtype=torch.float32, device=DEV)
+    outs = []
     for g in range(G):
         w13, w13s, w2, w2s, Ig = _shard(prob, g, G)
         r = ops.forward_stages(prob.x, prob.logits, prob.gate, w13, w13s, w2, w2s, Ig, c.E, c.K,
@@ -87,6 +92,7 @@ def test_tensor_parallel_shards_sum_to_the_layer(name):
             # each output column of gate/up + SwiGLU sums over K in the same order
             assert torch.equal(r["h"], full["h"][:, g * Ig:(g + 1) * Ig])
         acc += r["out"].float()
+        outs.append(r["out"].clone())
         if g < 2:                      # the oracle's layer on this shard's weight slices
             Ig2, b2, s2 = Ig, Ig // 2, Ig // 32
 
@@ -106,3 +112,11 @@ def test_tensor_parallel_shards_sum_to_the_layer(name):
     e_rel, e_max = rel_l2(got, ref), max_abs_over_rms(got, ref)
     _say(f"  {name}: sum of {G} shards vs the full layer: rel_l2 {e_rel:.2e}  max_abs/rms {e_max:.2e}")
     assert e_rel <= 1e-2 and e_max <= 5e-2
+    # the fused epilogue of the all-reduce: shard outputs + x, RMSNorm
+    _, _, gamma = synth.norm_inputs(1, 1, c.H, seed=11)
+    hres = torch.empty_like(prob.x)
+    y, _ = ops.residual_rmsnorm(outs, gamma.to(DEV), 1e-6, residual=prob.x, residual_out=hres)
+    torch.cuda.synchronize()
+    nd, ex = check_residual_rmsnorm(np.stack([bits(o) for o in outs]), bits(prob.x_cpu),
+                                    bits(gamma), 1e-6, bits(hres), bits(y), name)
+    _say(f"  {name}: residual + sum of shards, RMSNorm: h off by one ulp {nd}, y exact {ex:.5f}")
