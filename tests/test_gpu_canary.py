@@ -5,8 +5,9 @@ equal, bit for bit, what the same sequence of calls writes into plain
 buffers (nothing read from outside the inputs, nothing left unwritten that
 the result depends on).  Covers the one-call forwards (32-row, 64-row and
 128-row GEMM paths, W4A4 on both, MXFP8, routed from x), every per-step
-entry point at every tile size the kernels offer, and the one-call routing +
-grouping."""
+entry point at every tile size the kernels offer, the one-call routing +
+grouping, and the step after the layer (partials summed, residual added,
+RMSNorm)."""
 import sys
 
 import numpy as np
@@ -264,3 +265,40 @@ def test_mxfp8_and_router_forward_guards():
     torch.cuda.synchronize()
     for a, b in zip(got, want):
         assert torch.equal(a, b)
+
+
+@pytest.mark.parametrize("G,T,H", [(3, 37, 136), (8, 64, 4096), (2, 5, 16384)])
+def test_residual_rmsnorm_guards(G, T, H):
+    """moe_residual_rmsnorm: inputs, h and out in guarded buffers (in place
+    and not), against the same calls on plain buffers."""
+    o = ops()
+    _say("canary residual_rmsnorm", G, T, H)
+    p, r, g = synth.norm_inputs(G, T, H, seed=3 + G + H)
+
+    def run(alloc, inplace):
+        parts = []
+        for i in range(G):
+            t = alloc((T, H), torch.bfloat16)
+            t.copy_(p[i])
+            parts.append(t)
+        res = alloc((T, H), torch.bfloat16)
+        res.copy_(r)
+        gam = alloc((H,), torch.bfloat16)
+        gam.copy_(g)
+        if inplace:
+            out, _ = o.residual_rmsnorm(parts, gam, 1e-6, residual=res, residual_out=res,
+                                        out=parts[0])
+            return out, res
+        hout = alloc((T, H), torch.bfloat16)
+        out = alloc((T, H), torch.bfloat16)
+        o.residual_rmsnorm(parts, gam, 1e-6, residual=res, residual_out=hout, out=out)
+        return out, hout
+
+    for inplace in (False, True):
+        gd = Guarded()
+        got = run(gd, inplace)
+        gd.check()
+        want = run(plain, inplace)
+        torch.cuda.synchronize()
+        for a, b in zip(got, want):
+            assert torch.equal(a, b)
