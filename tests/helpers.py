@@ -205,11 +205,6 @@ class Problem:
                                   self.w2s, c.I, c.E, c.K, c.shared, c.act_fmt, **kw)
 
 
-def bf16_ulp(v):
-    """Spacing of bf16 values at |v| (normal range; v != 0)."""
-    return np.ldexp(1.0, np.floor(np.log2(np.abs(v))).astype(np.int64) - 7)
-
-
 def check_residual_rmsnorm(p_bits, r_bits, g_bits, eps, h_gpu, y_gpu, what=""):
     """The kernel's h and y (bf16 bits) against the oracle on the same inputs.
 

@@ -297,10 +297,49 @@ def test_route_align_empty():
 
 # -------------------------------------------------------------- the layer --
 
+def _random_shapes(n=24, seed=20261202, act_fmt=synth.ACT_BF16):
+    """n layer shapes drawn from a fixed seed: H and I any multiples of 128 (so
+    odd multiples take the 32-row kernels and every (I/128 - 1) mod 3 of the
+    two-slice down GEMM comes up), E from 1 to 512, K from 1 to 12, with and
+    without the shared expert, T from 1 to 400 (32-row and tiled paths).
+    Weight volume capped so the draws and the oracle stay quick."""
+    rng = np.random.default_rng(seed)
+    out = {}
+    for i in range(n):
+        E = int(rng.choice([1, 3, 8, 17, 64, 130, 300, 512]))
+        K = int(rng.integers(1, min(E, 12) + 1))
+        shared = int(rng.integers(0, 2))
+        T = int(rng.choice([1, 2, 5, 17, 33, 64, 100, 257, 400, 600]))
+        while True:
+            # (the tiled kernels take H a multiple of 256: most draws are)
+            H = 256 * int(rng.integers(1, 9)) if rng.random() < 0.7 else 128 * int(rng.integers(1, 17))
+            I = 128 * int(rng.integers(1, 13))
+            if (E + shared) * 3 * H * I <= 1.2e8:
+                break
+        tag = "q" if act_fmt == synth.ACT_MXFP4 else "r"
+        name = f"{tag}{i:02d}_T{T}_H{H}_I{I}_E{E}_K{K}_s{shared}"
+        kw = dict(act_fmt=act_fmt, outlier_p=0.002) if act_fmt == synth.ACT_MXFP4 else {}
+        out[name] = synth.custom_config(name, T=T, H=H, I=I, E=E, K=K, shared=shared,
+                                        seed_act=500 + i, seed_w=600 + i, **kw)
+    return out
+
+
+RANDOM = {**_random_shapes(), **_random_shapes(8, seed=20261203, act_fmt=synth.ACT_MXFP4)}
+
+
 @pytest.mark.parametrize("name", list(SMALL))
 def test_layer_small(name):
+    _check_layer(SMALL[name], name)
+
+
+@pytest.mark.parametrize("name", list(RANDOM))
+def test_layer_random_shapes(name):
+    _check_layer(RANDOM[name], name)
+
+
+def _check_layer(cfg, name):
     _say("layer", name)
-    prob = Problem(SMALL[name])
+    prob = Problem(cfg)
     c = prob.cfg
     r = prob.stages()
     out = prob.forward()
