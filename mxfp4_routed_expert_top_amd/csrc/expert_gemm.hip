@@ -264,6 +264,14 @@ __device__ __forceinline__ void scales_to_lds(rsrc_t r, uint32_t off, uint32_t b
 // the other (the second re-reads the weights, from L2): decode tiles mostly
 // have 1-3 rows and this keeps a single subtile's registers live.  SwiGLU in
 // registers, bf16 h stored in sorted row order.
+//
+// The shared expert's tiles (T rows, last in the tile table) are the only
+// full ones in a decode batch, and with two subtiles each in turn their
+// workgroups run twice as long as the rest: where the whole grid fits on the
+// GPU at once (one GPU's tensor-parallel share, I = 128) they alone set the
+// kernel's length.  So the first nx * nsl blocks take subtile 1 of the last
+// nx tiles (when such a tile has more than 16 rows) and the workgroups of
+// those tiles run subtile 0 only: the two halves run side by side.
 template <int PH, bool kFP4A, bool kW8>
 __global__ __launch_bounds__(256)
 __attribute__((amdgpu_waves_per_eu(MOE_GEMM_WAVES_PER_EU))) void gate_up_kernel(
@@ -271,9 +279,15 @@ __attribute__((amdgpu_waves_per_eu(MOE_GEMM_WAVES_PER_EU))) void gate_up_kernel(
     const int32_t* __restrict__ sorted, const int32_t* __restrict__ offsets,
     const int32_t* __restrict__ tiles, const int32_t* __restrict__ num_tiles,
     const uint8_t* __restrict__ w13, const uint8_t* __restrict__ w13s, int T, int H, int I, int Kp,
-    int nsl, uint16_t* __restrict__ h) {
+    int nsl, int nx, uint16_t* __restrict__ h) {
   TileInfo ti;
-  if (!load_tile(tiles, num_tiles, offsets, (int)(blockIdx.x / nsl), &ti)) return;
+  // blocks [0, nx * nsl): subtile 1 of tile num_tiles - 1 - r; then every tile
+  const int bt = (int)(blockIdx.x / nsl);
+  const bool second = bt < nx;
+  const int r = second ? bt : bt - nx;
+  if (!load_tile(tiles, num_tiles, offsets, r, &ti)) return;
+  const bool split = r < nx && ti.rows > 16;
+  if (second && !split) return;
   // (debug builds: a tile whose rows leave [0, A) stores nothing)
   if (!MOE_DOK(ti.row0 >= 0 && ti.rows > 0 && (int64_t)ti.row0 + ti.rows <= (int64_t)T * Kp, kDbgTiles))
     return;
@@ -291,7 +305,7 @@ __attribute__((amdgpu_waves_per_eu(MOE_GEMM_WAVES_PER_EU))) void gate_up_kernel(
   Operands o;
   o.lds = lds_scales;
   o.w = make_rsrc(w13 + ti.expert * wbytes, (uint32_t)wbytes);
-  o.stream = ti.single;
+  o.stream = ti.single && !split;   // (the halves of a split tile share the lines in L2)
   constexpr int NQ = Phase<PH, kFP4A, false, kW8>::NQ;
   o.wo[0] = wnat_lane(st, H, NQ, lane);
   o.wo[1] = wnat_lane(I / 16 + st, H, NQ, lane);
@@ -350,7 +364,7 @@ __attribute__((amdgpu_waves_per_eu(MOE_GEMM_WAVES_PER_EU))) void gate_up_kernel(
   }
   __syncthreads();
   const int mtn = (ti.rows + 15) / 16;
-  for (int mt = 0; mt < mtn; ++mt) {
+  for (int mt = second ? 1 : 0; mt < (split && !second ? 1 : mtn); ++mt) {
     const int m = 16 * mt + nl;
     floatx4_t acc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
     if (xl) {
@@ -586,11 +600,11 @@ struct GateUpLaunch {
   static hipError_t run(dim3 grid, hipStream_t stream, const void* act, const uint8_t* act_scale,
                         const int32_t* sorted, const int32_t* offsets, const int32_t* tiles,
                         const int32_t* num_tiles, const uint8_t* w13, const uint8_t* w13s, int T,
-                        int H, int I, int Kp, int nsl, uint16_t* h) {
+                        int H, int I, int Kp, int nsl, int nx, uint16_t* h) {
     const size_t lds = (size_t)128 * (H / 32) + (kFP4A ? 0 : (size_t)kXR * H * 2);
     hipLaunchKernelGGL((gate_up_kernel<PH, kFP4A, kW8>), grid, dim3(256), lds, stream,
                        act, act_scale,
-                       sorted, offsets, tiles, num_tiles, w13, w13s, T, H, I, Kp, nsl, h);
+                       sorted, offsets, tiles, num_tiles, w13, w13s, T, H, I, Kp, nsl, nx, h);
     return hipGetLastError();
   }
 };
@@ -628,9 +642,11 @@ hipError_t launch_gate_up(int act_fmt, int wfmt, const void* act, const uint8_t*
                           const uint8_t* w13s, int T, int H, int I, int Kp, uint16_t* h,
                           hipStream_t stream) {
   const int nsl = I / 64;
-  dim3 grid((unsigned)(max_tiles * nsl));
+  // the last tiles of a T-row group (the shared expert's) split in two
+  const int nx = max_tiles < (T + kTileM - 1) / kTileM ? max_tiles : (T + kTileM - 1) / kTileM;
+  dim3 grid((unsigned)((max_tiles + nx) * nsl));
   return dispatch<GateUpLaunch>(act_fmt, wfmt, H / 128, grid, stream, act, act_scale, sorted,
-                                offsets, tiles, num_tiles, w13, w13s, T, H, I, Kp, nsl, h);
+                                offsets, tiles, num_tiles, w13, w13s, T, H, I, Kp, nsl, nx, h);
 }
 
 hipError_t launch_down(int act_fmt, int wfmt, const void* h, const uint8_t* h_scale,
