@@ -381,6 +381,16 @@ def measure(cfg, args, weights=None, router=False):
         step()
     torch.cuda.synchronize()
     ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    # two more back-to-back repeats of region 1 in the same run (paired
+    # repeats show the run-to-run spread); ms_per_step stays the first
+    repeats = [ms]
+    for _ in range(2):
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        for _ in range(args.steps):
+            step()
+        torch.cuda.synchronize()
+        repeats.append((time.perf_counter() - t1) * 1e3 / args.steps)
 
     # timed region 2: each call between its own pair of HIP events on the
     # launch stream, for the distribution (median, p10, p90)
@@ -473,6 +483,8 @@ def measure(cfg, args, weights=None, router=False):
            "shared": cfg.shared,
            "format": ("W8A16 MXFP8" if w8 else ("W4A16" if cfg.act_fmt == 0 else "W4A4") + " MXFP4"),
            "ms_per_step": round(ms, 4), "tokens_per_s": round(cfg.T / layer_s, 1),
+           "repeats_ms": [round(r, 4) for r in repeats],
+           "repeat_spread": round(max(repeats) / min(repeats) - 1, 4),
            "call_ms": {"median": round(pct(call_ms, 50), 4), "p10": round(pct(call_ms, 10), 4),
                        "p90": round(pct(call_ms, 90), 4), "calls": len(call_ms)},
            "kernel_ms": {k: round(v, 4) for k, v in stage_ms.items()},
