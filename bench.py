@@ -52,6 +52,9 @@ def parse():
     p.add_argument("--layers", type=int, default=0,
                    help="time L layers of the workload (each its own weights and router rows) "
                         "in one moe_mxfp4_forward_layers call, eager and replayed from a HIP graph")
+    p.add_argument("--norm", action="store_true",
+                   help="with --layers: the residual add and RMSNorm after each layer "
+                        "(moe_mxfp4_forward_layers_norm)")
     p.add_argument("--prefetch", action="store_true",
                    help="with --layers: each layer's combine prefetches the next layer's router "
                         "rows and shared expert into the caches")
@@ -221,12 +224,28 @@ def bench_layers(cfg, args):
     out = torch.empty(cfg.T, cfg.H, dtype=torch.bfloat16, device=dev)
     pf = 1 if args.prefetch else 0
     s = torch.cuda.Stream()
-    call = lambda: ops.mxfp4_forward_layers(x, layers, cfg.I, cfg.E, cfg.K, cfg.shared,
-                                            cfg.act_fmt, prefetch=pf, out=out, workspace=ws)
+    norm = bool(args.norm)
+    if norm:
+        # the residual stream (updated in place by every call) and each
+        # layer's norm weights
+        _, r0, _ = synth.norm_inputs(1, cfg.T, cfg.H, seed=900)
+        r0 = r0.to(dev)
+        resid = r0.clone()
+        gammas = [synth.norm_inputs(1, 1, cfg.H, seed=901 + l)[2].to(dev) for l in range(L)]
+        call = lambda: ops.mxfp4_forward_layers_norm(x, layers, gammas, NORM_EPS, resid, cfg.I,
+                                                     cfg.E, cfg.K, cfg.shared, cfg.act_fmt,
+                                                     prefetch=pf, out=out, workspace=ws)
+    else:
+        call = lambda: ops.mxfp4_forward_layers(x, layers, cfg.I, cfg.E, cfg.K, cfg.shared,
+                                                cfg.act_fmt, prefetch=pf, out=out, workspace=ws)
     with torch.cuda.stream(s):
         for _ in range(args.warmup):
             call()
         torch.cuda.synchronize()
+        if norm:
+            resid.copy_(r0)
+            call()
+            torch.cuda.synchronize()
         eager_out = out.clone()
         t0 = time.perf_counter()
         for _ in range(args.steps):
@@ -245,6 +264,10 @@ def bench_layers(cfg, args):
         g.replay()
     torch.cuda.synchronize()
     graph_ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    if norm:                              # the same residual stream as the eager call
+        resid.copy_(r0)
+        g.replay()
+        torch.cuda.synchronize()
     if not torch.equal(out, eager_out):
         raise RuntimeError("graph replay and eager call disagree")
     log(f"{L} layers: eager {eager_ms:.4f} ms, graph {graph_ms:.4f} ms")
@@ -255,11 +278,13 @@ def bench_layers(cfg, args):
            "data": "synthetic",
            "config": {"workload": f"{cfg.name}: {L} MoE layers in one call (T={cfg.T} H={cfg.H} "
                                   f"I={cfg.I} E={cfg.E} K={cfg.K}+{cfg.shared} shared, each routed "
-                                  "from its input by its router GEMM), one HIP graph",
+                                  "from its input by its router GEMM"
+                                  + (", residual add + RMSNorm after each" if norm else "")
+                                  + "), one HIP graph",
                       "T": cfg.T, "H": cfg.H, "I": cfg.I, "E": cfg.E, "K": cfg.K,
-                      "shared": cfg.shared, "layers": L, "prefetch": bool(pf),
+                      "shared": cfg.shared, "layers": L, "prefetch": bool(pf), "norm": norm,
                       "parallelism": "none (1 GPU)"},
-           "layers": {"L": L, "prefetch": bool(pf), "eager_ms": round(eager_ms, 4),
+           "layers": {"L": L, "prefetch": bool(pf), "norm": norm, "eager_ms": round(eager_ms, 4),
                       "graph_ms": round(graph_ms, 4),
                       "eager_ms_per_layer": round(eager_ms / L, 4),
                       "graph_ms_per_layer": round(graph_ms / L, 4)},

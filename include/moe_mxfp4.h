@@ -20,6 +20,8 @@
  *   0-6 in one call                                    moe_mxfp4_forward_router
  *   L layers of 0-6 in one call (a decode step's MoE layers)
  *                                                      moe_mxfp4_forward_layers
+ *   the same with the residual add and RMSNorm after each layer
+ *                                                      moe_mxfp4_forward_layers_norm
  *   after the layer: partial outputs summed (tensor parallelism), residual
  *   added, RMSNorm                                     moe_residual_rmsnorm
  *
@@ -628,6 +630,32 @@ MOE_API moe_status moe_mxfp4_forward_layers(const uint16_t *x, int32_t L,
                                             int32_t I, int32_t E, int32_t K, int32_t shared,
                                             int32_t act_fmt, int32_t prefetch, uint16_t *out,
                                             void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * The same L layers as the MoE sub-layers of a pre-norm decode step: after
+ * each layer the residual stream is updated and normalised in one pass (the
+ * pages fuse the residual add and RMSNorm into the step after the layer:
+ * VibeSys post, section "Communication and concurrency"; see
+ * moe_residual_rmsnorm, here with the layer's output as the one partial):
+ *   y_l = layer l on x_l (x_0 = x);  residual += y_l (bf16);
+ *   x_{l+1} = RMSNorm(residual) * gammas[l]  (written to out)
+ * so out holds the last layer's normalised output and residual the stream
+ * after all L layers.  Layer l > 0 reads out; every step writes in place.
+ *   gammas     host array of L device pointers, bf16 [H] each, 16-byte aligned
+ *   eps        >= 0, finite
+ *   residual   in/out bf16 [T, H], 16-byte aligned
+ * Other arguments as moe_mxfp4_forward_layers.  Errors: those of
+ * moe_mxfp4_forward_layers and moe_residual_rmsnorm, all checked before the
+ * first enqueue.
+ */
+MOE_API moe_status moe_mxfp4_forward_layers_norm(const uint16_t *x, int32_t L,
+                                                 const moe_mxfp4_layer *layers,
+                                                 const uint16_t *const *gammas, float eps,
+                                                 uint16_t *residual, int32_t T, int32_t H,
+                                                 int32_t I, int32_t E, int32_t K, int32_t shared,
+                                                 int32_t act_fmt, int32_t prefetch, uint16_t *out,
+                                                 void *workspace, size_t workspace_bytes,
+                                                 void *stream);
 
 /* The tile_m moe_mxfp8_forward uses for these shapes: 32 or 64, by the rule
  * of moe_mxfp4_forward with bf16 activations (128-row tiles only when a

@@ -609,6 +609,12 @@ moe_status forward_impl(const uint16_t* x, const float* router_logits,
   return from_hip(launch_combine(y, wts, inv, T, H, Kp, out, s, pf));
 }
 
+moe_status layers_impl(const uint16_t* x, int32_t L, const moe_mxfp4_layer* layers,
+                       const uint16_t* const* gammas, float eps, uint16_t* residual, int32_t T,
+                       int32_t H, int32_t I, int32_t E, int32_t K, int32_t shared, int32_t act_fmt,
+                       int32_t prefetch, uint16_t* out, void* workspace, size_t workspace_bytes,
+                       void* stream);
+
 }  // namespace
 
 extern "C" {
@@ -660,6 +666,40 @@ moe_status moe_mxfp4_forward_layers(const uint16_t* x, int32_t L, const moe_mxfp
                                     int32_t shared, int32_t act_fmt, int32_t prefetch,
                                     uint16_t* out, void* workspace, size_t workspace_bytes,
                                     void* stream) {
+  return layers_impl(x, L, layers, nullptr, 0.f, nullptr, T, H, I, E, K, shared, act_fmt,
+                     prefetch, out, workspace, workspace_bytes, stream);
+}
+
+moe_status moe_mxfp4_forward_layers_norm(const uint16_t* x, int32_t L,
+                                         const moe_mxfp4_layer* layers,
+                                         const uint16_t* const* gammas, float eps,
+                                         uint16_t* residual, int32_t T, int32_t H, int32_t I,
+                                         int32_t E, int32_t K, int32_t shared, int32_t act_fmt,
+                                         int32_t prefetch, uint16_t* out, void* workspace,
+                                         size_t workspace_bytes, void* stream) {
+  if (L < 1 || !gammas || !(eps >= 0.f) || !std::isfinite(eps)) return MOE_ERR_INVALID_ARGUMENT;
+  if (H > 0 && (H % 8 || H > residual_rmsnorm_max_h())) return MOE_ERR_UNSUPPORTED;
+  if (T > 0) {
+    if (!residual || !aligned16(residual)) return MOE_ERR_INVALID_ARGUMENT;
+    for (int l = 0; l < L; ++l)
+      if (!gammas[l] || !aligned16(gammas[l])) return MOE_ERR_INVALID_ARGUMENT;
+  }
+  return layers_impl(x, L, layers, gammas, eps, residual, T, H, I, E, K, shared, act_fmt,
+                     prefetch, out, workspace, workspace_bytes, stream);
+}
+
+}  // extern "C"
+
+namespace {
+
+// The layers of a pass; with gammas, each layer's output then goes through
+// the residual add and RMSNorm (one partial: h += out, out = RMSNorm(h)),
+// both in place, before the next layer reads out.
+moe_status layers_impl(const uint16_t* x, int32_t L, const moe_mxfp4_layer* layers,
+                       const uint16_t* const* gammas, float eps, uint16_t* residual, int32_t T,
+                       int32_t H, int32_t I, int32_t E, int32_t K, int32_t shared, int32_t act_fmt,
+                       int32_t prefetch, uint16_t* out, void* workspace, size_t workspace_bytes,
+                       void* stream) {
   if (L < 1 || !layers || (prefetch != 0 && prefetch != 1)) return MOE_ERR_INVALID_ARGUMENT;
   // Every layer's pointers are checked before anything is enqueued; the shapes
   // (shared by all layers) are checked by the first layer's call, before its
@@ -703,11 +743,17 @@ moe_status moe_mxfp4_forward_layers(const uint16_t* x, int32_t L, const moe_mxfp
                                  workspace_bytes, stream, pf.n ? &pf : nullptr);
     if (st != MOE_OK) return st;
     if (T == 0) return MOE_OK;
+    if (gammas) {
+      const uint16_t* part = out;
+      if (launch_residual_rmsnorm(&part, 1, residual, gammas[l], eps, T, H, residual, out,
+                                  as_stream(stream)) != hipSuccess)
+        return MOE_ERR_DEVICE;
+    }
   }
   return MOE_OK;
 }
 
-}  // extern "C"
+}  // namespace
 
 // ---- the forward for callers that cannot allocate -------------------------
 

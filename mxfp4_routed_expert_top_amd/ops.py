@@ -60,6 +60,9 @@ _SIGS = {
                                  _I32, _P, _P, _P, _P, _SZ, _P]),
     "moe_mxfp4_forward_layers": (_I32, [_P, _I32, _P, _I32, _I32, _I32, _I32, _I32, _I32, _I32,
                                         _I32, _P, _P, _SZ, _P]),
+    "moe_mxfp4_forward_layers_norm": (_I32, [_P, _I32, _P, _P, ctypes.c_float, _P, _I32, _I32,
+                                             _I32, _I32, _I32, _I32, _I32, _I32, _P, _P, _SZ,
+                                             _P]),
     "moe_mxfp8_quantize": (_I32, [_P, _I32, _I64, _I64, _P, _P, _P]),
     "moe_weights_to_native": (_I32, [_P, _I32, _I64, _I64, _P, _P]),
     "moe_mxfp8_expert_gate_up": (_I32, [_P, _P, _P, _P, _P, _I32, _P, _P, _I32, _I32, _I32, _I32,
@@ -591,6 +594,36 @@ def mxfp4_forward_layers(x, layers, I: int, E: int, K: int, shared: int,
     _check("moe_mxfp4_forward_layers", lib().moe_mxfp4_forward_layers(
         _ptr(x), len(layers), ctypes.cast(arr, _P), T, H, I, E, K, shared, act_fmt, prefetch,
         _ptr(out), _ptr(workspace), workspace.numel(), _stream(stream)))
+    return out
+
+
+def mxfp4_forward_layers_norm(x, layers, gammas, eps: float, residual, I: int, E: int, K: int,
+                              shared: int, act_fmt: int = ACT_BF16, prefetch: int = 0, out=None,
+                              workspace=None, stream=None):
+    """moe_mxfp4_forward_layers_norm: the layers of mxfp4_forward_layers with
+    residual += layer output and out = RMSNorm(residual) * gammas[l] after
+    each (residual, bf16 [T, H], updated in place).  -> out bf16 [T, H]."""
+    _dt(x, torch.bfloat16, "x")
+    _dt(residual, torch.bfloat16, "residual")
+    T, H = x.shape
+    if len(gammas) != len(layers):
+        raise ValueError("one gamma per layer")
+    if out is None:
+        out = torch.empty(T, H, dtype=torch.bfloat16, device=x.device)
+    need = workspace_size(T, H, I, E, K, shared, act_fmt)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=x.device)
+    arr = (_Layer * max(len(layers), 1))()
+    for i, (wr, w13, w13s, w2, w2s) in enumerate(layers):
+        _dt(wr, torch.bfloat16, "router_w")
+        arr[i] = _Layer(_ptr(wr), _ptr(w13), _ptr(w13s), _ptr(w2), _ptr(w2s))
+    for g in gammas:
+        _dt(g, torch.bfloat16, "gammas")
+    garr = (ctypes.c_void_p * max(len(gammas), 1))(*[_ptr(g) for g in gammas])
+    _check("moe_mxfp4_forward_layers_norm", lib().moe_mxfp4_forward_layers_norm(
+        _ptr(x), len(layers), ctypes.cast(arr, _P), garr, float(eps), _ptr(residual), T, H, I, E,
+        K, shared, act_fmt, prefetch, _ptr(out), _ptr(workspace), workspace.numel(),
+        _stream(stream)))
     return out
 
 

@@ -26,7 +26,7 @@ def declared_functions():
 def test_library_loads_and_exports_every_declared_symbol():
     lib = ops.lib()
     names = declared_functions()
-    assert len(names) == 28
+    assert len(names) == 29
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(ops.EXPORTS)
@@ -168,6 +168,31 @@ def test_residual_rmsnorm_argument_errors():
     assert call(T=0) == OK                                            # nothing to do
     assert call(T=0, r=None, ro=None, gm=None, o=None) == OK          # no data pointer read
     assert call(T=0, H=4100) == UNSUPPORTED                           # the shape still checked
+
+
+def test_forward_layers_norm_argument_errors():
+    f = ops.lib().moe_mxfp4_forward_layers_norm
+    lay = (ops._Layer * 2)(ops._Layer(FAKE, FAKE, FAKE, FAKE, FAKE),
+                           ops._Layer(FAKE, FAKE, FAKE, FAKE, FAKE))
+    gam = (ctypes.c_void_p * 2)(FAKE, FAKE)
+    def call(**kw):
+        a = dict(x=FAKE, L=2, lay=ctypes.cast(lay, ctypes.c_void_p), g=gam, eps=1e-6, r=FAKE,
+                 T=4, H=512, I=256, E=8, K=2, s=1, act=0, pf=0, o=FAKE, ws=FAKE, wsb=1 << 30)
+        a.update(kw)
+        return f(a["x"], a["L"], a["lay"], a["g"], a["eps"], a["r"], a["T"], a["H"], a["I"],
+                 a["E"], a["K"], a["s"], a["act"], a["pf"], a["o"], a["ws"], a["wsb"], None)
+    assert call(g=None) == INVALID
+    assert call(L=0) == INVALID
+    assert call(eps=-1.0) == INVALID
+    assert call(eps=float("nan")) == INVALID
+    assert call(r=None) == INVALID
+    assert call(r=MIS) == INVALID
+    assert call(g=(ctypes.c_void_p * 2)(FAKE, None)) == INVALID       # a null gamma
+    assert call(g=(ctypes.c_void_p * 2)(FAKE, MIS)) == INVALID        # a misaligned gamma
+    assert call(H=32768) == UNSUPPORTED                               # beyond the norm's rows
+    assert call(pf=2) == INVALID                                      # checks of the layers pass
+    assert call(lay=None) == INVALID
+    assert call(I=100) == UNSUPPORTED                                 # the layer's own checks
 
 
 def test_quantize_argument_errors():

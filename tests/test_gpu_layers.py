@@ -26,8 +26,9 @@ import torch
 
 import synth
 from oracle import moe, mxfp4
-from tests.helpers import (DEV, MAX_ABS_RMS, REL_L2, W_ATOL, bf16_ulp, bits, max_abs_over_rms,
-                           oracle_pack, oracle_pack_all, rel_l2)
+from tests.helpers import (DEV, MAX_ABS_RMS, REL_L2, W_ATOL, bf16_ulp, bits,
+                           check_residual_rmsnorm, max_abs_over_rms, oracle_pack, oracle_pack_all,
+                           rel_l2)
 
 pytestmark = pytest.mark.gpu
 
@@ -111,11 +112,12 @@ class Layers:
                            c.act_fmt, tokens=tokens)
 
 
-def check_layer(l, got_bits, want, act_fmt):
-    """Layer 0 against the layer's bounds; later layers with the max-abs bound
-    per element (see the module's docstring)."""
+def check_layer(l, got_bits, want, act_fmt, strict=False):
+    """Layer 0 (or every layer, strict) against the layer's bounds; later
+    layers of an unnormalised chain with the max-abs bound per element (see
+    the module's docstring)."""
     e_rel = rel_l2(got_bits, want["out"])
-    if l == 0:
+    if l == 0 or strict:
         e_max = max_abs_over_rms(got_bits, want)
         _say(f"  layer {l}: rel_l2 {e_rel:.2e}  max_abs/rms {e_max:.2e}")
     else:
@@ -189,3 +191,117 @@ def test_layers_full_decode():
     for l, (x_in, lg, got) in enumerate(steps):
         want = P.oracle_layer(l, x_in, lg)
         check_layer(l, bits(got), want, cfg.act_fmt)
+
+
+# ---- the same layers with the residual add and RMSNorm after each ----------
+
+EPS = 1e-6
+
+
+def _norm_inputs(cfg, L):
+    """The residual stream entering layer 0 (N(0, 1)) and each layer's norm
+    weights (U(0.5, 1.5)), bf16."""
+    _, r0, _ = synth.norm_inputs(1, cfg.T, cfg.H, seed=900)
+    gammas = [synth.norm_inputs(1, 1, cfg.H, seed=901 + l)[2] for l in range(L)]
+    return r0, gammas
+
+
+def chain_norm(P, r0, gammas):
+    """One call per step: the layer from its input, then the residual add and
+    RMSNorm of its output.  Returns per layer (input, logits, layer output,
+    residual before, residual after, normalised output) and the last residual."""
+    c = P.cfg
+    cur, h = P.x, r0.to(DEV).clone()
+    steps = []
+    for l in range(P.L):
+        lg = torch.empty(c.T, c.Ep, dtype=torch.float32, device=DEV)
+        y = ops().mxfp4_forward_router(cur, P.w[l][0], *P.w[l][1:], c.I, c.E, c.K, c.shared,
+                                       c.act_fmt, logits_out=lg)
+        h_in = h.clone()
+        out, _ = ops().residual_rmsnorm([y], gammas[l].to(DEV), EPS, residual=h, residual_out=h)
+        steps.append((cur, lg, y, h_in, h.clone(), out))
+        cur = out
+    torch.cuda.synchronize()
+    return steps, h
+
+
+def _multi_norm(P, r0, gammas, prefetch, **kw):
+    c = P.cfg
+    res = r0.to(DEV).clone()
+    out = ops().mxfp4_forward_layers_norm(P.x, P.w, [g.to(DEV) for g in gammas], EPS, res, c.I,
+                                          c.E, c.K, c.shared, c.act_fmt, prefetch=prefetch, **kw)
+    torch.cuda.synchronize()
+    return out, res
+
+
+def _check_norm_steps(P, steps, gammas):
+    c = P.cfg
+    for l, (x_in, lg, y, h_in, h_out, out) in enumerate(steps):
+        want = P.oracle_layer(l, x_in, lg)
+        # every layer's input is normalised: the layer's own bounds for each
+        check_layer(l, bits(y), want, c.act_fmt, strict=True)
+        nd, ex = check_residual_rmsnorm(bits(y)[None], bits(h_in), bits(gammas[l]), EPS,
+                                        bits(h_out), bits(out), f"norm after layer {l}")
+        _say(f"  norm after layer {l}: h off by one ulp {nd}, y exact {ex:.5f}")
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+def test_layers_norm_match_chain_and_oracle(name):
+    _say("layers + residual RMSNorm", name)
+    P = Layers(SMALL[name], 3)
+    r0, gammas = _norm_inputs(P.cfg, 3)
+    steps, h_last = chain_norm(P, r0, gammas)
+    for prefetch in (0, 1):
+        out, res = _multi_norm(P, r0, gammas, prefetch)
+        assert np.array_equal(bits(out), bits(steps[-1][5])), prefetch
+        assert np.array_equal(bits(res), bits(h_last)), prefetch
+    _check_norm_steps(P, steps, gammas)
+
+
+def test_layers_norm_graph_replays_equal_eager():
+    P = Layers(SMALL["ragged"], 2)
+    c = P.cfg
+    r0, gammas = _norm_inputs(c, 2)
+    g_dev = [g.to(DEV) for g in gammas]
+    ws = torch.empty(ops().workspace_size(c.T, c.H, c.I, c.E, c.K, c.shared, c.act_fmt),
+                     dtype=torch.uint8, device=DEV)
+    out = torch.empty(c.T, c.H, dtype=torch.bfloat16, device=DEV)
+    res = torch.empty(c.T, c.H, dtype=torch.bfloat16, device=DEV)
+    r0d = r0.to(DEV)
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        res.copy_(r0d)
+        ops().mxfp4_forward_layers_norm(P.x, P.w, g_dev, EPS, res, c.I, c.E, c.K, c.shared,
+                                        c.act_fmt, prefetch=1, out=out, workspace=ws)
+        torch.cuda.synchronize()
+        eager_out, eager_res = out.clone(), res.clone()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=s):
+            ops().mxfp4_forward_layers_norm(P.x, P.w, g_dev, EPS, res, c.I, c.E, c.K, c.shared,
+                                            c.act_fmt, prefetch=1, out=out, workspace=ws)
+    torch.cuda.synchronize()
+    for i in range(4):
+        out.fill_(0)
+        ws.fill_(0xFF)                     # eager work between replays
+        res.copy_(r0d)                     # the residual stream is updated in place
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, eager_out) and torch.equal(res, eager_res), i
+
+
+@pytest.mark.timeout(600)
+def test_layers_norm_full_decode():
+    """Two layers of the decode workload's shapes with the residual add and
+    RMSNorm after each: equal to the chained calls bit for bit, every token of
+    both layers and both norm steps against the oracle."""
+    cfg = synth.CONFIGS["decode"]
+    _say("layers + residual RMSNorm, full decode", cfg.T, cfg.H, cfg.I, cfg.E, cfg.K)
+    P = Layers(cfg, 2)
+    r0, gammas = _norm_inputs(cfg, 2)
+    steps, h_last = chain_norm(P, r0, gammas)
+    out, res = _multi_norm(P, r0, gammas, 1)
+    assert np.array_equal(bits(out), bits(steps[-1][5]))
+    assert np.array_equal(bits(res), bits(h_last))
+    _say("  chain == multi-layer call")
+    _check_norm_steps(P, steps, gammas)
