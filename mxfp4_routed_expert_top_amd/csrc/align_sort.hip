@@ -35,6 +35,7 @@ using namespace moe_grouping;
 constexpr int kChunk = 512;       // assignments per block in passes 1 and 4
 constexpr int kScanThreads = kGroupThreads;
 constexpr int kSmallA = 8192;     // single-workgroup path up to this many assignments
+static_assert(kSmallA <= moe_grouping::kGroupMaxA, "group_small's register-held ids");
 constexpr int kSlices = kScanThreads / 64;   // chunk slices of a column scan: one per wave
 constexpr int kBatch = 12;        // histogram loads in flight per lane in a column scan
 
@@ -140,7 +141,7 @@ __global__ __launch_bounds__(kScanThreads) void align_small_kernel(
     int32_t* __restrict__ tiles, int32_t* __restrict__ num_tiles) {
   extern __shared__ int32_t sh[];          // group_small_lds_bytes(Ep)
   __shared__ int tmp[17];
-  group_small([&](int a) { return ids[a]; }, A, Ep, tile_m, counts, offsets, sorted, inv, tiles,
+  group_small<true>([&](int a) { return ids[a]; }, A, Ep, tile_m, counts, offsets, sorted, inv, tiles,
               num_tiles, sh, tmp);
 }
 

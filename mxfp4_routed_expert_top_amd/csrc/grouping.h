@@ -109,8 +109,19 @@ __host__ __device__ constexpr size_t group_small_lds_bytes(int Ep) {
   return (size_t)2 * Ep * 4 + (((size_t)kGroupWaves * Ep + 3) & ~(size_t)3);
 }
 
-// The whole grouping in one workgroup of kGroupThreads threads.  ids(a) is
-// the expert of assignment a (ids outside [0, Ep) take no part).  sh holds
+// Largest A of group_small: a thread keeps the ids of its assignments
+// a = tid + 1024 i in registers (loaded once and used by both the histogram
+// and the scatter).
+constexpr int kGroupRounds = 8;
+constexpr int kGroupMaxA = kGroupRounds * kGroupThreads;
+
+// The whole grouping in one workgroup of kGroupThreads threads, A <=
+// kGroupMaxA.  ids(a) is the expert of assignment a (ids outside [0, Ep)
+// take no part).  kEarly: the ids are read on entry, so their loads overlap
+// the clearing of the count table (ids in global memory; 2,816 and 7,700
+// assignments: 20.1 -> 19.2 and 49.8 -> 46.4 us); otherwise after the barrier that follows the
+// clearing, which then also publishes ids that other threads of the
+// workgroup have just written (the fused routing's LDS).  sh holds
 // group_small_lds_bytes(Ep) bytes of LDS, tmp >= 17 ints.
 //
 // The scatter goes in rounds of 1024 assignments, one per thread.  A
@@ -119,7 +130,7 @@ __host__ __device__ constexpr size_t group_small_lds_bytes(int Ep) {
 // the first lane of each expert in each wave), plus its rank among the equal
 // lanes of its own wave.  Between rounds each expert's offset advances by its
 // count in the round.
-template <class Ids>
+template <bool kEarly, class Ids>
 __device__ __forceinline__ void group_small(Ids&& ids, int A, int Ep, int tile_m,
                                             int32_t* __restrict__ counts,
                                             int32_t* __restrict__ offsets,
@@ -131,12 +142,28 @@ __device__ __forceinline__ void group_small(Ids&& ids, int A, int Ep, int tile_m
   int32_t* pos = sh + Ep;
   uint8_t* tab = (uint8_t*)(sh + 2 * Ep);             // [kGroupWaves][Ep]
   const int tid = threadIdx.x;
+  // the expert of assignment a, -1 for none or one outside [0, Ep)
+  auto id_at = [&](int a) -> int {
+    const int e = a < A ? ids(a) : -1;
+    return (unsigned)e < (unsigned)Ep ? e : -1;
+  };
+  int ev[kEarly ? kGroupRounds : 1];                 // (kEarly) the thread's ids, round by round
+  if constexpr (kEarly) {
+#pragma unroll
+    for (int i = 0; i < kGroupRounds; ++i) ev[i] = id_at(i * kGroupThreads + tid);
+  }
   for (int e = tid; e < Ep; e += kGroupThreads) cnt[e] = 0;
   for (int i = tid; i < (kGroupWaves * Ep + 3) / 4; i += kGroupThreads) ((uint32_t*)tab)[i] = 0u;
   __syncthreads();
-  for (int a = tid; a < A; a += kGroupThreads) {
-    const int e = ids(a);
-    if ((unsigned)e < (unsigned)Ep) atomicAdd(&cnt[e], 1);
+  if constexpr (kEarly) {
+#pragma unroll
+    for (int i = 0; i < kGroupRounds; ++i)
+      if (ev[i] >= 0) atomicAdd(&cnt[ev[i]], 1);
+  } else {
+    for (int a = tid; a < A; a += kGroupThreads) {
+      const int e = id_at(a);
+      if (e >= 0) atomicAdd(&cnt[e], 1);
+    }
   }
   __syncthreads();
   group_offsets([&](int e) { return cnt[e]; }, A, Ep, tile_m, offsets, tiles, num_tiles, tmp,
@@ -146,10 +173,9 @@ __device__ __forceinline__ void group_small(Ids&& ids, int A, int Ep, int tile_m
                 });
   // (pos is read only after the barrier that follows the table's writes)
   const int wave = tid >> 6;
-  for (int r = 0; r < A; r += kGroupThreads) {
+  // one round: assignment a = r + tid of expert e (or -1)
+  auto scatter = [&](int r, int e) {
     const int a = r + tid;
-    int e = (a < A) ? ids(a) : -1;
-    if ((unsigned)e >= (unsigned)Ep) e = -1;
     int rank, same;
     wave_match_rank(e, &rank, &same);
     if (e >= 0 && rank == 0) tab[wave * Ep + e] = (uint8_t)same;
@@ -175,6 +201,15 @@ __device__ __forceinline__ void group_small(Ids&& ids, int A, int Ep, int tile_m
       }
       __syncthreads();
     }
+  };
+  if constexpr (kEarly) {
+#pragma unroll
+    for (int i = 0; i < kGroupRounds; ++i) {
+      if (i * kGroupThreads >= A) break;             // block-uniform
+      scatter(i * kGroupThreads, ev[i]);
+    }
+  } else {
+    for (int r = 0; r < A; r += kGroupThreads) scatter(r, id_at(r + tid));
   }
 }
 

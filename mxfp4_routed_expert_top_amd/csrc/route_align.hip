@@ -48,8 +48,9 @@ __global__ __launch_bounds__(kGroupThreads) void route_align_kernel(
                           weights[a] = w;
                           chosen[a] = e;
                         });
-  // (group_small's first barrier, after it clears its own LDS, publishes chosen)
-  group_small([&](int a) { return chosen[a]; }, A, Ep, tile_m, counts, offsets, sorted, inv, tiles,
+  // (group_small's barrier after it clears its own LDS publishes chosen,
+  // which it reads only then)
+  group_small<false>([&](int a) { return chosen[a]; }, A, Ep, tile_m, counts, offsets, sorted, inv, tiles,
               num_tiles, sh, tmp);
 }
 
@@ -75,6 +76,7 @@ void launch(const float* logits, int ld, const float* gate, int gate_stride, int
 bool route_align_fits(int T, int E, int K, int shared) {
   if (T < 1 || E < 1 || E > 64 * kMaxPerLane) return false;
   if (keys_per_lane(E) * T > kMaxKeyTokens) return false;
+  if ((int64_t)T * (K + shared) > moe_grouping::kGroupMaxA) return false;
   const int Kp = K + shared, Ep = E + shared;
   return Ep <= 2 * kGroupThreads && lds_bytes(T, Kp, Ep) <= kMaxLds;
 }
