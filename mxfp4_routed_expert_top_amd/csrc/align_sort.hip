@@ -34,7 +34,10 @@ using namespace moe_grouping;
 
 constexpr int kChunk = 512;       // assignments per block in passes 1 and 4
 constexpr int kScanThreads = kGroupThreads;
-constexpr int kSmallA = 8192;     // single-workgroup path up to this many assignments
+// Single-workgroup path up to this many assignments.  Above it the chunked
+// kernels take ~18 us whatever A (E = 512); the one workgroup takes 10 us at
+// 704 assignments, 17.6 at 2,112, 19.3 at 2,816 and 46.5 at 7,700.
+constexpr int kSmallA = 2048;
 static_assert(kSmallA <= moe_grouping::kGroupMaxA, "group_small's register-held ids");
 constexpr int kSlices = kScanThreads / 64;   // chunk slices of a column scan: one per wave
 constexpr int kBatch = 12;        // histogram loads in flight per lane in a column scan

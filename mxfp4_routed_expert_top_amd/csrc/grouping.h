@@ -112,14 +112,13 @@ __host__ __device__ constexpr size_t group_small_lds_bytes(int Ep) {
 // Largest A of group_small: a thread keeps the ids of its assignments
 // a = tid + 1024 i in registers (loaded once and used by both the histogram
 // and the scatter).
-constexpr int kGroupRounds = 8;
+constexpr int kGroupRounds = 2;
 constexpr int kGroupMaxA = kGroupRounds * kGroupThreads;
 
 // The whole grouping in one workgroup of kGroupThreads threads, A <=
 // kGroupMaxA.  ids(a) is the expert of assignment a (ids outside [0, Ep)
 // take no part).  kEarly: the ids are read on entry, so their loads overlap
-// the clearing of the count table (ids in global memory; 2,816 and 7,700
-// assignments: 20.1 -> 19.2 and 49.8 -> 46.4 us); otherwise after the barrier that follows the
+// the clearing of the count table (ids in global memory); otherwise after the barrier that follows the
 // clearing, which then also publishes ids that other threads of the
 // workgroup have just written (the fused routing's LDS).  sh holds
 // group_small_lds_bytes(Ep) bytes of LDS, tmp >= 17 ints.
