@@ -493,9 +493,10 @@ MOE_API moe_status moe_mxfp8_expert_down(const uint16_t *h, const int32_t *exper
                                  void *y, void *stream);
 
 /* The tile_m moe_mxfp4_forward uses for these shapes and activation format
- * (A = T*Kp assignments over Ep experts): 32, 64 or 128 (see
- * moe_expert_gate_up; 256-row tiles are used only when a caller of the
- * per-step entry points asks for them).  The pages keep separate small-M
+ * (A = T*Kp assignments over Ep experts): 32 up to an average of 3 rows per
+ * expert (W4A16; 8 for W4A4), else 64 or 128 (see moe_expert_gate_up;
+ * 256-row tiles are used only when a caller of the per-step entry points
+ * asks for them).  The pages keep separate small-M
  * (decode) and large-M (prefill) GEMM launchers chosen by the local shape
  * (MiniMax M3 on MI355X post, section "Local shape and tiling") and use
  * 32-row tiles for the MoE kernel (VibeSys post, section "Prefill, cache and
@@ -657,9 +658,9 @@ MOE_API moe_status moe_mxfp4_forward_layers_norm(const uint16_t *x, int32_t L,
                                                  void *workspace, size_t workspace_bytes,
                                                  void *stream);
 
-/* The tile_m moe_mxfp8_forward uses for these shapes: 32 or 64, by the rule
- * of moe_mxfp4_forward with bf16 activations (128-row tiles only when a
- * caller of the per-step entry points asks for them). */
+/* The tile_m moe_mxfp8_forward uses for these shapes: 32 up to an average
+ * of 4 rows per expert, else 64 (128-row tiles only when a caller of the
+ * per-step entry points asks for them). */
 MOE_API int32_t moe_mxfp8_gemm_tile_m(int32_t T, int32_t Kp, int32_t Ep, int32_t H, int32_t I);
 
 /* Workspace bytes moe_mxfp8_forward needs (0 for T = 0). */

@@ -38,9 +38,15 @@ inline int64_t max_tiles_for(int64_t A, int64_t Ep, int64_t tile_m = MOE_TILE_M)
 // weight reuse of 128-row tiles even on the skewed T = 8192 batch (~176
 // rows per expert: step 2.92 -> 2.53 ms).  MXFP4 activations keep 128-row
 // tiles above 48 rows (64-row tiles are 5% slower on the W4A4 batch).
+// The 32-row weight-streaming kernels up to an average group of `small`
+// rows (whole passes at E = 512, H = 4096, I = 1024 cross over at ~3.4 rows
+// for W4A16: 64-row tiles 5% faster at 4.1 rows and 10% at 5.5; at ~5 rows
+// with MXFP8 weights; at ~9.6 rows for W4A4, 6% faster at 11.8), the tiled
+// kernels above.
 int choose_tile_m(int64_t A, int64_t Ep, int H, int I, int act_fmt, int wfmt = 0) {
   const int64_t avg = A / Ep;
-  if (avg <= 8) return MOE_TILE_M;
+  const int64_t small = act_fmt != MOE_ACT_BF16 ? 8 : wfmt == 1 ? 4 : 3;
+  if (avg <= small) return MOE_TILE_M;
   // (256-row tiles, MXFP4 activations only, are taken on request: on the
   // W4A4 batch, ~143 rows per expert, 128-row tiles are faster even though
   // they stream most experts' weights twice, the second time mostly from L2.

@@ -297,6 +297,10 @@ def test_gemm_and_combine_argument_errors():
 def test_gemm_tile_choice():
     # decode-like groups stream weights; larger groups use the LDS-tiled kernels
     assert ops.gemm_tile_m(64, 11, 513, 4096, 1024) == 32
+    assert ops.gemm_tile_m(160, 11, 513, 4096, 1024) == 32     # 3 rows per expert
+    assert ops.gemm_tile_m(192, 11, 513, 4096, 1024) == 64     # 4: the tiled kernels
+    assert ops.gemm_tile_m(372, 11, 513, 4096, 1024, ops.ACT_MXFP4) == 32   # W4A4: 7
+    assert ops.gemm_tile_m(450, 11, 513, 4096, 1024, ops.ACT_MXFP4) == 64   # W4A4: 9
     assert ops.gemm_tile_m(1536, 11, 513, 4096, 1024) == 64
     assert ops.gemm_tile_m(8192, 11, 513, 4096, 1024) == 64     # bf16: two workgroups per CU
     assert ops.gemm_tile_m(8192, 11, 513, 384, 1024) == 32      # H % 256 != 0
@@ -376,6 +380,8 @@ def test_mxfp8_argument_errors():
     based = [FAKE, FAKE, FAKE, FAKE, 32, FAKE, FAKE, 4, 256, 128, 9, 3, FAKE, None]
     assert call(dn, based, a4=256) == UNSUPPORTED
     assert ops.mxfp8_gemm_tile_m(64, 11, 513, 4096, 1024) == 32
+    assert ops.mxfp8_gemm_tile_m(192, 11, 513, 4096, 1024) == 32   # 4 rows per expert
+    assert ops.mxfp8_gemm_tile_m(256, 11, 513, 4096, 1024) == 64   # 5
     assert ops.mxfp8_gemm_tile_m(1536, 11, 513, 4096, 1024) == 64
     assert ops.mxfp8_gemm_tile_m(8192, 11, 513, 4096, 1024) == 64
     assert ops.mxfp8_gemm_tile_m(8192, 11, 513, 4096, 4608) == 32   # I above the tiled limit

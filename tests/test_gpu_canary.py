@@ -58,7 +58,7 @@ def plain(shape, dtype):
 
 
 CASES = {
-    "ragged": synth.custom_config("canary_ragged", T=50, H=512, I=256, E=32, K=4, shared=1),
+    "ragged": synth.custom_config("canary_ragged", T=50, H=512, I=256, E=64, K=4, shared=1),
     "tiled": synth.custom_config("canary_tiled", T=300, H=512, I=256, E=8, K=3, shared=1),
     "w4a4": synth.custom_config("canary_w4a4", T=40, H=256, I=128, E=16, K=3, shared=1,
                                 act_fmt=synth.ACT_MXFP4, outlier_p=0.01),

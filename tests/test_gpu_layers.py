@@ -127,8 +127,8 @@ def check_layer(l, got_bits, want, act_fmt, strict=False):
 
 
 SMALL = {
-    "ragged": synth.custom_config("layers_ragged", T=50, H=512, I=256, E=32, K=4, shared=1),
-    "no_shared": synth.custom_config("layers_no_shared", T=33, H=256, I=128, E=8, K=2, shared=0),
+    "ragged": synth.custom_config("layers_ragged", T=50, H=512, I=256, E=64, K=4, shared=1),
+    "no_shared": synth.custom_config("layers_no_shared", T=33, H=256, I=128, E=24, K=2, shared=0),
     "w4a4": synth.custom_config("layers_w4a4", T=40, H=256, I=128, E=16, K=3, shared=1,
                                 act_fmt=synth.ACT_MXFP4, outlier_p=0.01),
     "tiled": synth.custom_config("layers_tiled", T=300, H=512, I=256, E=16, K=3, shared=1),

@@ -131,7 +131,7 @@ def test_mxfp8_quantize_bit_exact(kind):
 
 SMALL = {
     "tiny": synth.CONFIGS["tiny"],
-    "ragged": synth.custom_config("ragged8", T=50, H=512, I=256, E=32, K=4, shared=1),
+    "ragged": synth.custom_config("ragged8", T=50, H=512, I=256, E=64, K=4, shared=1),
     "no_shared_k1": synth.custom_config("no_shared_k1_8", T=33, H=256, I=128, E=8, K=1, shared=0),
     "one_expert": synth.custom_config("one_expert8", T=7, H=128, I=128, E=1, K=1, shared=0),
     "single_token": synth.custom_config("single_token8", T=1, H=384, I=256, E=64, K=6, shared=1),

@@ -38,8 +38,8 @@ def ops():
 SMALL = {
     "tiny": synth.CONFIGS["tiny"],
     # several 32-row tiles per expert with ragged tails; H, I span several K steps
-    "ragged": synth.custom_config("ragged", T=50, H=512, I=256, E=32, K=4, shared=1),
-    "no_shared_k1": synth.custom_config("no_shared_k1", T=33, H=256, I=128, E=8, K=1, shared=0),
+    "ragged": synth.custom_config("ragged", T=50, H=512, I=256, E=64, K=4, shared=1),
+    "no_shared_k1": synth.custom_config("no_shared_k1", T=24, H=256, I=128, E=8, K=1, shared=0),
     "one_expert": synth.custom_config("one_expert", T=7, H=128, I=128, E=1, K=1, shared=0),
     "single_token": synth.custom_config("single_token", T=1, H=384, I=256, E=64, K=6, shared=1),
     "sparse": synth.custom_config("sparse", T=3, H=256, I=128, E=300, K=2, shared=1),
@@ -85,7 +85,7 @@ SMALL = {
     # slots per token, H and I at the 32-row bf16 kernels' LDS limit (13,568), and the
     # longest reduction of the MXFP4 128-row kernels (8,192)
     "max_e": synth.custom_config("max_e", T=16, H=256, I=128, E=1024, K=8, shared=1),
-    "max_slots": synth.custom_config("max_slots", T=12, H=256, I=128, E=64, K=31, shared=1),
+    "max_slots": synth.custom_config("max_slots", T=12, H=256, I=128, E=128, K=31, shared=1),
     "max_h_decode": synth.custom_config("max_h_decode", T=6, H=13568, I=128, E=4, K=2, shared=1),
     "max_i_decode": synth.custom_config("max_i_decode", T=6, H=128, I=13568, E=4, K=2, shared=1),
     "tiled128_w4a4_k8192": synth.custom_config("tiled128_w4a4_k8192", T=200, H=8192, I=8192,

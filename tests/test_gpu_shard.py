@@ -61,7 +61,7 @@ def _shard(prob, g, G):
 
 
 CASES = {
-    "tp4_small": (synth.custom_config("tp4_small", T=50, H=512, I=512, E=32, K=4, shared=1), 4),
+    "tp4_small": (synth.custom_config("tp4_small", T=50, H=512, I=512, E=64, K=4, shared=1), 4),
     "tp4_tiled": (synth.custom_config("tp4_tiled", T=300, H=512, I=512, E=16, K=3, shared=1), 4),
     "tp2_w4a4": (synth.custom_config("tp2_w4a4", T=40, H=256, I=256, E=16, K=3, shared=1,
                                      act_fmt=synth.ACT_MXFP4, outlier_p=0.01), 2),
