@@ -308,6 +308,8 @@ def test_gemm_tile_choice():
     # MXFP4 activations: 128-row tiles above 48 rows (256-row tiles only on request)
     assert ops.gemm_tile_m(4096, 9, 257, 6144, 1536, ops.ACT_MXFP4) == 128
     assert ops.gemm_tile_m(2048, 9, 257, 6144, 1536, ops.ACT_MXFP4) == 128
+    assert ops.gemm_tile_m(914, 9, 257, 6144, 1536, ops.ACT_MXFP4) == 64     # 32 rows per expert
+    assert ops.gemm_tile_m(945, 9, 257, 6144, 1536, ops.ACT_MXFP4) == 128    # 33
     assert ops.gemm_tile_m(4096, 9, 257, 8192, 1536, ops.ACT_MXFP4) == 128
     assert ops.gemm_tile_m(4096, 9, 257, 6144, 1536, ops.ACT_BF16) == 32
     assert ops.gemm_tile_m(8192, 11, 513, 4096, 4608, ops.ACT_BF16) == 32
