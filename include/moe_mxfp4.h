@@ -644,7 +644,7 @@ MOE_API moe_status moe_mxfp4_forward_layers(const uint16_t *x, int32_t L,
  * after all L layers.  Layer l > 0 reads out; every step writes in place.
  *   gammas     host array of L device pointers, bf16 [H] each, 16-byte aligned
  *   eps        >= 0, finite
- *   residual   in/out bf16 [T, H], 16-byte aligned
+ *   residual   in/out bf16 [T, H], 16-byte aligned, not overlapping out
  * Other arguments as moe_mxfp4_forward_layers.  Errors: those of
  * moe_mxfp4_forward_layers and moe_residual_rmsnorm, all checked before the
  * first enqueue.

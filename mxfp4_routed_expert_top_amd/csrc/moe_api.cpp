@@ -688,7 +688,8 @@ moe_status moe_mxfp4_forward_layers_norm(const uint16_t* x, int32_t L,
   if (L < 1 || !gammas || !(eps >= 0.f) || !std::isfinite(eps)) return MOE_ERR_INVALID_ARGUMENT;
   if (H > 0 && (H % 8 || H > residual_rmsnorm_max_h())) return MOE_ERR_UNSUPPORTED;
   if (T > 0) {
-    if (!residual || !aligned16(residual)) return MOE_ERR_INVALID_ARGUMENT;
+    // (the norm reads out as its partial and updates residual: two buffers)
+    if (!residual || !aligned16(residual) || residual == out) return MOE_ERR_INVALID_ARGUMENT;
     for (int l = 0; l < L; ++l)
       if (!gammas[l] || !aligned16(gammas[l])) return MOE_ERR_INVALID_ARGUMENT;
   }

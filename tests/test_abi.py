@@ -16,6 +16,7 @@ OK, INVALID, UNSUPPORTED, WS_SMALL = (ops.MOE_OK, ops.MOE_ERR_INVALID_ARGUMENT,
                                       ops.MOE_ERR_UNSUPPORTED, ops.MOE_ERR_WORKSPACE_TOO_SMALL)
 FAKE = ctypes.c_void_p(0x100000)        # never dereferenced: every call below fails validation
 MIS = ctypes.c_void_p(0x100004)          # not 16-byte aligned
+FAKE2 = ctypes.c_void_p(0x200000)       # a second, distinct fake buffer
 
 
 def declared_functions():
@@ -177,7 +178,7 @@ def test_forward_layers_norm_argument_errors():
     gam = (ctypes.c_void_p * 2)(FAKE, FAKE)
     def call(**kw):
         a = dict(x=FAKE, L=2, lay=ctypes.cast(lay, ctypes.c_void_p), g=gam, eps=1e-6, r=FAKE,
-                 T=4, H=512, I=256, E=8, K=2, s=1, act=0, pf=0, o=FAKE, ws=FAKE, wsb=1 << 30)
+                 T=4, H=512, I=256, E=8, K=2, s=1, act=0, pf=0, o=FAKE2, ws=FAKE, wsb=1 << 30)
         a.update(kw)
         return f(a["x"], a["L"], a["lay"], a["g"], a["eps"], a["r"], a["T"], a["H"], a["I"],
                  a["E"], a["K"], a["s"], a["act"], a["pf"], a["o"], a["ws"], a["wsb"], None)
@@ -187,6 +188,7 @@ def test_forward_layers_norm_argument_errors():
     assert call(eps=float("nan")) == INVALID
     assert call(r=None) == INVALID
     assert call(r=MIS) == INVALID
+    assert call(r=FAKE, o=FAKE) == INVALID                            # residual is out
     assert call(g=(ctypes.c_void_p * 2)(FAKE, None)) == INVALID       # a null gamma
     assert call(g=(ctypes.c_void_p * 2)(FAKE, MIS)) == INVALID        # a misaligned gamma
     assert call(H=32768) == UNSUPPORTED                               # beyond the norm's rows
