@@ -227,7 +227,8 @@ MOE_API moe_status moe_align_sort(const int32_t *topk_ids, int32_t T, int32_t Kp
  * outputs bit for bit.  A small batch (T <= 32 at E <= 256, T <= 16 at
  * E <= 512, T <= 8 at E <= 1024) runs as ONE launch, one workgroup that
  * routes the tokens and then groups their assignments, the chosen experts
- * passed on in LDS (InferenceX "MI355X Qwen3.5 SGLang v0.5.12" post, section
+ * passed on in LDS (at most 64 assignments and 16 tokens: one wave per
+ * token, the first wave grouping) (InferenceX "MI355X Qwen3.5 SGLang v0.5.12" post, section
  * on the specific optimisations: fused_topk, and the shared expert folded
  * into the one MoE dispatch); larger batches run the two steps' kernels,
  * which route their tokens across the whole chip.  The forwards route and

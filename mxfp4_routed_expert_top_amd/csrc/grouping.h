@@ -212,4 +212,92 @@ __device__ __forceinline__ void group_small(Ids&& ids, int A, int Ep, int tile_m
   }
 }
 
+// The grouping of at most kWaveMaxA assignments by the first wave of a
+// workgroup (the other waves, if any, only clear the count table and take
+// the barriers): the same counts, offsets, sorted order, inverse map and tile
+// table as group_small.  Lane a takes assignment a; the expert counts go
+// through LDS atomics; lane l owns the experts [l * epl, l * epl + epl)
+// (epl = ceil(Ep / 64) <= kWaveEPL) and wave scans of their counts and tile
+// counts give the offsets and the tile table; each assignment lands at its
+// expert's offset plus its rank among the lanes of the same expert.  ids(a)
+// is read after the first barrier (which publishes ids that the workgroup
+// has just written to LDS).  cnt: LDS of Ep ints.
+constexpr int kWaveMaxA = 64;
+constexpr int kWaveEPL = 17;                          // Ep <= 64 * 17
+
+__device__ __forceinline__ int wave_exclusive_scan(int v) {
+  const int lane = threadIdx.x & 63;
+  int x = v;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int y = __shfl_up(x, d, MOE_WAVE);
+    if (lane >= d) x += y;
+  }
+  return x - v;
+}
+
+template <class Ids>
+__device__ __forceinline__ void group_wave(Ids&& ids, int A, int Ep, int tile_m,
+                                           int32_t* __restrict__ counts,
+                                           int32_t* __restrict__ offsets,
+                                           int32_t* __restrict__ sorted, int32_t* __restrict__ inv,
+                                           int32_t* __restrict__ tiles,
+                                           int32_t* __restrict__ num_tiles, int32_t* cnt) {
+  const int lane = threadIdx.x & 63;
+  const bool first = threadIdx.x < 64;                // (a wave-uniform condition)
+  for (int x = threadIdx.x; x < Ep; x += blockDim.x) cnt[x] = 0;
+  __syncthreads();
+  int e = first && lane < A ? ids(lane) : -1;
+  if ((unsigned)e >= (unsigned)Ep) e = -1;
+  if (e >= 0) atomicAdd(&cnt[e], 1);
+  __syncthreads();
+  if (first) {
+    const int epl = (Ep + 63) / 64, e0 = lane * epl;
+    int c[kWaveEPL];
+    int sum = 0, tsum = 0;
+#pragma unroll
+    for (int j = 0; j < kWaveEPL; ++j) {
+      c[j] = (j < epl && e0 + j < Ep) ? cnt[e0 + j] : 0;
+      sum += c[j];
+      tsum += (c[j] + tile_m - 1) / tile_m;
+    }
+    int off = wave_exclusive_scan(sum), toff = wave_exclusive_scan(tsum);
+    const int ntiles = __builtin_amdgcn_readlane(toff + tsum, 63);
+    const int max_tiles = (A + tile_m - 1) / tile_m + Ep;
+#pragma unroll
+    for (int j = 0; j < kWaveEPL; ++j) {
+      const int x = e0 + j;
+      if (j < epl && x < Ep) {
+        counts[x] = c[j];
+        offsets[x] = off;
+        cnt[x] = off;                                 // (the scatter's positions)
+        if (tiles)
+          for (int q = 0; q * tile_m < c[j]; ++q)
+            if (MOE_DOK(toff + q < max_tiles, kDbgAlign)) {
+              tiles[2 * (toff + q)] = x;
+              tiles[2 * (toff + q) + 1] = off + q * tile_m;
+            }
+        off += c[j];
+        toff += (c[j] + tile_m - 1) / tile_m;
+      }
+    }
+    if (lane == 0) {
+      offsets[Ep] = A;
+      *num_tiles = ntiles;
+    }
+  }
+  __syncthreads();
+  if (first) {
+    int rank, same;
+    wave_match_rank(e, &rank, &same);
+    if (e >= 0) {
+      const int p = cnt[e] + rank;
+      if (MOE_DOK(p >= 0 && p < A, kDbgAlign)) {
+        sorted[p] = lane;
+        if (inv) inv[lane] = p;
+      }
+    }
+  }
+}
+
 }  // namespace moe_grouping

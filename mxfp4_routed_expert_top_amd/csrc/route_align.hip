@@ -8,7 +8,8 @@
 //
 // Wave w of the 16 routes tokens w and w + 16 (NT of them, their dependency
 // chains interleaved); after one barrier all 1024 threads group the T*K'
-// assignments.  Used up to 128 / NPL tokens (32 at E <= 256, 16 at E <= 512,
+// assignments.  The smallest batches (at most 64 assignments) take a
+// workgroup of one wave per token instead, whose first wave groups them.  Used up to 128 / NPL tokens (32 at E <= 256, 16 at E <= 512,
 // 8 at E <= 1024): there the one launch took 10-16 us against 16.5-18.5 us
 // for the two.  Beyond, the routing of many tokens on one CU's four SIMDs
 // (about 35 wave instructions per token and slot) costs more than the
@@ -60,6 +61,53 @@ int tokens_per_wave(int T) { return T <= kGroupWaves ? 1 : 2; }
 
 size_t lds_bytes(int T, int Kp, int Ep) { return group_small_lds_bytes(Ep) + (size_t)T * Kp * 4; }
 
+// The smallest batches (T <= 16 tokens, T * K' <= 64 assignments): a
+// workgroup of T waves, wave t routing token t, then the first wave groups
+// the assignments (group_wave).  Dynamic LDS: the counts [Ep], then the
+// chosen experts [64].  At T = 1 this took 6.7 us against 8.5 for the
+// 1024-thread workgroup (E = 512, K' = 11) and 8.6 against 13.5 at E = 1024:
+// the grouping's synchronisation of 16 waves over Ep experts is gone.
+constexpr int kWaveMaxTokens = 16;
+static_assert(64 * kMaxPerLane + 1 <= 64 * kWaveEPL, "group_wave's experts per lane");
+
+template <int NPL>
+__global__ __launch_bounds__(64 * kWaveMaxTokens) void route_align_wave_kernel(
+    const float* __restrict__ logits, int ld, const float* __restrict__ gate, int gate_stride,
+    int T, int E, int K, int shared, int renormalize, int tile_m, int32_t* __restrict__ ids,
+    float* __restrict__ weights, int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
+    int32_t* __restrict__ sorted, int32_t* __restrict__ inv, int32_t* __restrict__ tiles,
+    int32_t* __restrict__ num_tiles) {
+  extern __shared__ int32_t sh[];
+  const int Kp = K + shared, Ep = E + shared, A = T * Kp;
+  int32_t* chosen = sh + Ep;
+  route_tokens<NPL, 1>(RowLogits{logits, ld}, GateLogit{gate, gate_stride}, threadIdx.x >> 6,
+                       kWaveMaxTokens, T, E, K, shared, renormalize,
+                       [&](int t, int k, int e, float w) {
+                         const int a = t * Kp + k;
+                         ids[a] = e;
+                         weights[a] = w;
+                         chosen[a] = e;
+                       });
+  // (group_wave's first barrier publishes chosen, which it reads only then)
+  group_wave([&](int a) { return chosen[a]; }, A, Ep, tile_m, counts, offsets, sorted, inv, tiles,
+             num_tiles, sh);
+}
+
+bool wave_fits(int T, int K, int shared) {
+  return T >= 1 && T <= kWaveMaxTokens && (int64_t)T * (K + shared) <= kWaveMaxA;
+}
+
+template <int NPL>
+void launch_wave(const float* logits, int ld, const float* gate, int gate_stride, int T, int E,
+                 int K, int shared, int renormalize, int tile_m, int32_t* ids, float* weights,
+                 int32_t* counts, int32_t* offsets, int32_t* sorted, int32_t* inv, int32_t* tiles,
+                 int32_t* num_tiles, hipStream_t stream) {
+  hipLaunchKernelGGL((route_align_wave_kernel<NPL>), dim3(1), dim3(64 * T),
+                     (size_t)(E + shared + kWaveMaxA) * 4, stream, logits, ld, gate, gate_stride,
+                     T, E, K, shared, renormalize, tile_m, ids, weights, counts, offsets, sorted,
+                     inv, tiles, num_tiles);
+}
+
 template <int NPL, int NT>
 void launch(const float* logits, int ld, const float* gate, int gate_stride, int T, int E, int K,
             int shared, int renormalize, int tile_m, int32_t* ids, float* weights, int32_t* counts,
@@ -92,6 +140,17 @@ hipError_t launch_route_align(const float* logits, int ld, const float* gate, in
     if (e != hipSuccess) return e;
     return launch_align_sort(ids, T * (K + shared), E + shared, tile_m, counts, offsets, sorted,
                              inv, tiles, num_tiles, scratch, stream);
+  }
+  if (wave_fits(T, K, shared)) {
+#define MOE_RW_LAUNCH(P)                                                                         \
+  launch_wave<P>(logits, ld, gate, gate_stride, T, E, K, shared, renormalize, tile_m, ids,        \
+                 weights, counts, offsets, sorted, inv, tiles, num_tiles, stream)
+    const int npl = keys_per_lane(E);
+    if (npl == 4) MOE_RW_LAUNCH(4);
+    else if (npl == 8) MOE_RW_LAUNCH(8);
+    else MOE_RW_LAUNCH(kMaxPerLane);
+#undef MOE_RW_LAUNCH
+    return hipGetLastError();
   }
   const int npl = keys_per_lane(E), nt = tokens_per_wave(T);
 #define MOE_RA_LAUNCH(P, N)                                                                      \

@@ -162,11 +162,12 @@ def test_stage_guards(name, tm):
         assert torch.equal(a, b)
 
 
-@pytest.mark.parametrize("T,E,K,tm", [(16, 512, 10, 32), (30, 16, 3, 64), (64, 512, 10, 32),
-                                      (300, 64, 4, 32)])
+@pytest.mark.parametrize("T,E,K,tm", [(1, 512, 10, 32), (4, 512, 14, 32), (16, 64, 3, 32),
+                                      (16, 512, 10, 32),
+                                      (30, 16, 3, 64), (64, 512, 10, 32), (300, 64, 4, 32)])
 def test_route_align_guards(T, E, K, tm):
-    """moe_route_align (one launch for the small batches, two beyond) with guarded
-    outputs."""
+    """moe_route_align (a wave per token for the smallest batches, one 16-wave
+    workgroup for the small ones, two launches beyond) with guarded outputs."""
     o = ops()
     gen = torch.Generator(device=DEV).manual_seed(T + E)
     logits = torch.randn(T, E, generator=gen, device=DEV)

@@ -246,8 +246,16 @@ def test_align_empty():
 # (T, E, K, shared, renormalize, tile_m): every keys-per-lane / tokens-per-wave
 # instance of the one-launch path (4 keys per lane with one and two tokens per
 # wave, 8 and 16 keys), 1024 assignments, ties, the full softmax, other tile
-# sizes, and the sizes just past the one-launch limit (two launches)
+# sizes, and the sizes just past the one-launch limit (two launches).  The
+# wave-per-token kernel (at most 64 assignments): each keys per lane, exactly
+# 64 assignments, 16 tokens (its most waves), ties, a
+# two-row tile
 ROUTE_ALIGN_CASES = [
+    (1, 512, 10, 1, 1, 32), (2, 512, 10, 1, 1, 32), (4, 512, 10, 1, 1, 32),
+    (16, 128, 3, 1, 1, 32), (16, 1024, 1, 1, 0, 2),
+    (5, 256, 8, 1, 1, 32), (8, 64, 7, 1, 1, 32), (4, 512, 15, 1, 1, 2), (6, 200, 4, 0, 0, 64),
+    (1, 1024, 8, 1, 1, 128), (2, 1024, 31, 1, 1, 32), (1, 1024, 31, 1, 0, 32),
+    (4, 96, 7, 1, 1, 32), (2, 24, 24, 0, 0, 32),
     (1, 64, 6, 1, 1, 32), (16, 256, 8, 1, 1, 32), (17, 200, 4, 0, 1, 64),
     (32, 96, 31, 1, 1, 2), (32, 32, 32, 0, 0, 32), (32, 96, 7, 1, 1, 32),
     (16, 512, 10, 1, 1, 32), (16, 512, 10, 1, 1, 128), (3, 300, 2, 1, 1, 32),
@@ -264,7 +272,7 @@ def test_route_align(T, E, K, shared, renorm, tile_m):
     _say("route_align", T, E, K, shared, renorm, tile_m)
     o = ops()
     gen = torch.Generator().manual_seed(1000 + T + E + K)
-    if (T, E, K) == (32, 96, 7):
+    if (E, K) == (96, 7):
         logits = synth.ties_logits(T, E, 3)
     else:
         logits = torch.randn(T, E, generator=gen) * 2
