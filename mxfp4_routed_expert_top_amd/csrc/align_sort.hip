@@ -102,8 +102,9 @@ __global__ __launch_bounds__(kScanThreads) void align_offsets_kernel(
     const int32_t* __restrict__ counts, int A, int Ep, int tile_m, int32_t* __restrict__ offsets,
     int32_t* __restrict__ tiles, int32_t* __restrict__ num_tiles) {
   __shared__ int tmp[17];
-  group_offsets([&](int e) { return counts[e]; }, A, Ep, tile_m, offsets, tiles, num_tiles, tmp,
-                [](int, int, int) {});
+  __shared__ int tstart[2 * kScanThreads + 1], roff[2 * kScanThreads];
+  group_offsets<true>([&](int e) { return counts[e]; }, A, Ep, tile_m, offsets, tiles, num_tiles,
+                      tmp, tstart, roff, [](int, int, int) {});
 }
 
 __global__ __launch_bounds__(256) void align_scatter_kernel(

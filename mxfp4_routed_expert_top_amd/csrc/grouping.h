@@ -65,12 +65,21 @@ __device__ __forceinline__ int block_exclusive_scan(int v, int* tmp /* >= 17 int
 // Counts [Ep] -> offsets [Ep + 1] (offsets[Ep] = A) and the tile table; each
 // thread owns experts 2 tid and 2 tid + 1 (Ep <= 2048).  cnt_of(e) is the
 // count of expert e; first(e, count, offset) is called for each owned expert.
-template <class Cnt, class First>
+// The table (expert-major, row start ascending) is written either by the
+// owner of each expert, entry after entry, or (kByEntry) entry by entry,
+// thread q taking entry q: its expert is the last one whose first entry
+// tstart[e] is <= q, found by a binary search in LDS, so that a wave's stores
+// are contiguous.  With many entries per expert the owners' stores touch 64
+// cache lines each (3,060 entries: 11.3 us, by entry 5.1); with about one
+// per expert (the decode batch) the search and its barrier cost more
+// (6.95 -> 7.21 us).  kByEntry: tstart is LDS of Ep + 1 ints and roff LDS of
+// Ep ints (the experts' row offsets); otherwise both unused.
+template <bool kByEntry, class Cnt, class First>
 __device__ __forceinline__ void group_offsets(Cnt&& cnt_of, int A, int Ep, int tile_m,
                                               int32_t* __restrict__ offsets,
                                               int32_t* __restrict__ tiles,
                                               int32_t* __restrict__ num_tiles, int* tmp,
-                                              First&& first) {
+                                              int* tstart, int* roff, First&& first) {
   int c[2] = {0, 0};
 #pragma unroll
   for (int q = 0; q < 2; ++q) {
@@ -84,22 +93,42 @@ __device__ __forceinline__ void group_offsets(Cnt&& cnt_of, int A, int Ep, int t
   int ttotal;
   const int tbase = block_exclusive_scan(nt[0] + nt[1], tmp, &ttotal);
   const int toff[2] = {tbase, tbase + nt[0]};
+  const int max_tiles = (A + tile_m - 1) / tile_m + Ep;
   for (int q = 0; q < 2; ++q) {
     const int e = 2 * threadIdx.x + q;
     if (e < Ep) {
       offsets[e] = off[q];
       first(e, c[q], off[q]);
-      if (tiles)
+      if constexpr (kByEntry) {
+        tstart[e] = toff[q];
+        roff[e] = off[q];
+      } else if (tiles) {
         for (int j = 0; j < nt[q]; ++j)
-          if (MOE_DOK(toff[q] + j < (A + tile_m - 1) / tile_m + Ep, kDbgAlign)) {
+          if (MOE_DOK(toff[q] + j < max_tiles, kDbgAlign)) {
             tiles[2 * (toff[q] + j)] = e;
             tiles[2 * (toff[q] + j) + 1] = off[q] + j * tile_m;
           }
+      }
     }
   }
   if (threadIdx.x == 0) {
     offsets[Ep] = A;
     *num_tiles = ttotal;
+    if constexpr (kByEntry) tstart[Ep] = ttotal;
+  }
+  if (!kByEntry || !tiles) return;                    // (uniform in the block)
+  __syncthreads();
+  for (int q = threadIdx.x; q < ttotal; q += blockDim.x) {
+    int lo = 0, hi = Ep;                              // tstart[lo] <= q < tstart[hi]
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (tstart[mid] <= q) lo = mid;
+      else hi = mid;
+    }
+    if (MOE_DOK(q < max_tiles, kDbgAlign)) {
+      tiles[2 * q] = lo;
+      tiles[2 * q + 1] = roff[lo] + (q - tstart[lo]) * tile_m;
+    }
   }
 }
 
@@ -165,11 +194,11 @@ __device__ __forceinline__ void group_small(Ids&& ids, int A, int Ep, int tile_m
     }
   }
   __syncthreads();
-  group_offsets([&](int e) { return cnt[e]; }, A, Ep, tile_m, offsets, tiles, num_tiles, tmp,
-                [&](int e, int c, int off) {
-                  counts[e] = c;
-                  pos[e] = off;
-                });
+  group_offsets<false>([&](int e) { return cnt[e]; }, A, Ep, tile_m, offsets, tiles, num_tiles,
+                       tmp, nullptr, nullptr, [&](int e, int c, int off) {
+                         counts[e] = c;
+                         pos[e] = off;
+                       });
   // (pos is read only after the barrier that follows the table's writes)
   const int wave = tid >> 6;
   // one round: assignment a = r + tid of expert e (or -1)
