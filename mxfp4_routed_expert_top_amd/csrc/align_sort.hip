@@ -19,8 +19,8 @@
 //   4. per-chunk stable scatter from offsets[e] + hist[b][e]: inside a
 //      chunk, wave by wave in order, each lane's rank among the earlier
 //      lanes with the same expert
-// A lane's rank among equal experts in its wave comes from ballots: one
-// round per distinct expert in the wave (at most 64), no data exchange.
+// A lane's rank among equal experts in its wave comes from ballots: one per
+// bit of the expert index, no data exchange.
 #include "common.h"
 #include "kernels.h"
 
@@ -35,9 +35,10 @@ using namespace moe_grouping;
 constexpr int kChunk = 512;       // assignments per block in passes 1 and 4
 constexpr int kScanThreads = kGroupThreads;
 // Single-workgroup path up to this many assignments.  Above it the chunked
-// kernels take ~18 us whatever A (E = 512); the one workgroup takes 10 us at
-// 704 assignments, 17.6 at 2,112, 19.3 at 2,816 and 46.5 at 7,700.
-constexpr int kSmallA = 2048;
+// kernels take ~13-14.5 us whatever A (E = 512, kernel trace); the one
+// workgroup takes 4.1 us at 704 assignments, 8.1 at 2,112, 8.6 at 2,816,
+// 12.3 at 4,224, 14.6 at 5,632 and 19.2 at 8,184.
+constexpr int kSmallA = 5120;
 static_assert(kSmallA <= moe_grouping::kGroupMaxA, "group_small's register-held ids");
 constexpr int kSlices = kScanThreads / 64;   // chunk slices of a column scan: one per wave
 constexpr int kBatch = 12;        // histogram loads in flight per lane in a column scan
@@ -122,7 +123,7 @@ __global__ __launch_bounds__(256) void align_scatter_kernel(
     int e = (a < A) ? ids[a] : -1;
     if ((unsigned)e >= (unsigned)Ep) e = -1;
     int rank, same;
-    wave_match_rank(e, &rank, &same);
+    wave_match_rank(e, expert_bits(Ep), &rank, &same);
     for (int w = 0; w < 4; ++w) {
       if (w == wave && e >= 0) {
         int p = pos[e] + rank;

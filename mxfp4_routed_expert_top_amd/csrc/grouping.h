@@ -16,24 +16,27 @@ constexpr int kGroupThreads = 1024;           // one-workgroup grouping
 constexpr int kGroupWaves = kGroupThreads / 64;
 
 // Rank of this lane among the lanes of its wave holding the same expert e
-// (lower lanes first) and the number of such lanes; e < 0 takes no part.
-// One ballot round per distinct expert in the wave, no data exchange.
-__device__ __forceinline__ void wave_match_rank(int e, int* rank, int* same) {
+// (lower lanes first) and the number of such lanes; e < 0 takes no part
+// (rank = same = 0).  Experts are below 2^nbits (expert_bits).  One ballot
+// per bit of the expert index: each lane keeps the lanes that agree with it
+// on every bit, which are exactly the lanes holding its own expert.  A fixed
+// cost, where one ballot round per distinct expert in the wave took ~60
+// rounds under near-uniform routing.
+__device__ __forceinline__ void wave_match_rank(int e, int nbits, int* rank, int* same) {
   const int lane = threadIdx.x & 63;
-  uint64_t todo = __ballot(e >= 0);
-  *rank = 0;
-  *same = 0;
-  while (todo) {
-    const int leader = __ffsll((unsigned long long)todo) - 1;
-    const int el = __builtin_amdgcn_readlane(e, leader);
-    const uint64_t m = __ballot(e == el);
-    if (e == el) {
-      *rank = __popcll(m & ((1ull << lane) - 1ull));
-      *same = __popcll(m);
-    }
-    todo &= ~m;
+  uint64_t m = __ballot(e >= 0);
+  for (int b = 0; b < nbits; ++b) {
+    const bool bit = (e >> b) & 1;
+    const uint64_t ones = __ballot(bit);
+    m &= bit ? ones : ~ones;
   }
+  const bool ok = e >= 0;
+  *rank = ok ? __popcll(m & ((1ull << lane) - 1ull)) : 0;
+  *same = ok ? __popcll(m) : 0;
 }
+
+// Bits of an expert index below Ep.
+__device__ __forceinline__ int expert_bits(int Ep) { return Ep <= 1 ? 0 : 32 - __clz(Ep - 1); }
 
 // Exclusive scan of one value per thread over a 1024-thread block.
 __device__ __forceinline__ int block_exclusive_scan(int v, int* tmp /* >= 17 ints */, int* total) {
@@ -141,7 +144,7 @@ __host__ __device__ constexpr size_t group_small_lds_bytes(int Ep) {
 // Largest A of group_small: a thread keeps the ids of its assignments
 // a = tid + 1024 i in registers (loaded once and used by both the histogram
 // and the scatter).
-constexpr int kGroupRounds = 2;
+constexpr int kGroupRounds = 5;
 constexpr int kGroupMaxA = kGroupRounds * kGroupThreads;
 
 // The whole grouping in one workgroup of kGroupThreads threads, A <=
@@ -205,7 +208,7 @@ __device__ __forceinline__ void group_small(Ids&& ids, int A, int Ep, int tile_m
   auto scatter = [&](int r, int e) {
     const int a = r + tid;
     int rank, same;
-    wave_match_rank(e, &rank, &same);
+    wave_match_rank(e, expert_bits(Ep), &rank, &same);
     if (e >= 0 && rank == 0) tab[wave * Ep + e] = (uint8_t)same;
     __syncthreads();
     if (e >= 0) {
@@ -318,7 +321,7 @@ __device__ __forceinline__ void group_wave(Ids&& ids, int A, int Ep, int tile_m,
   __syncthreads();
   if (first) {
     int rank, same;
-    wave_match_rank(e, &rank, &same);
+    wave_match_rank(e, expert_bits(Ep), &rank, &same);
     if (e >= 0) {
       const int p = cnt[e] + rank;
       if (MOE_DOK(p >= 0 && p < A, kDbgAlign)) {

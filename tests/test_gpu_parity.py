@@ -185,21 +185,23 @@ def test_align_golden_tile_m_2():
 
 @pytest.mark.parametrize("name", ["tiny", "ragged", "sparse", "decode", "prefill",
                                   "prefill_skewed", "w4a4", "one_hot", "big_a", "chunks19",
-                                  "small_max", "small_max_one_expert", "chunked_min"])
+                                  "two_rounds", "small_max", "small_max_one_expert",
+                                  "chunked_min"])
 def test_align_sort(name):
     _say("align", name)
     if name == "one_hot":                  # every assignment to one expert: many tiles
         T, Kp, Ep = 3000, 1, 40
         ids = torch.full((T, Kp), 17, dtype=torch.int32)
-    elif name in ("small_max", "small_max_one_expert"):
-        # the one-workgroup path at its largest (2048 assignments: two scatter rounds),
-        # random ids over 1025 experts or every id the same (64 per wave)
-        T, Kp, Ep = 64, 32, 1025
+    elif name in ("two_rounds", "small_max", "small_max_one_expert"):
+        # the one-workgroup path over two scatter rounds (2048 assignments) and
+        # at its largest (5120: five rounds), random ids over 1025 experts or
+        # every id the same (64 per wave)
+        T, Kp, Ep = (64 if name == "two_rounds" else 160), 32, 1025
         ids = (torch.randint(0, Ep, (T, Kp), generator=torch.Generator().manual_seed(10),
-                             dtype=torch.int32) if name == "small_max"
+                             dtype=torch.int32) if name != "small_max_one_expert"
                else torch.full((T, Kp), 1024, dtype=torch.int32))
-    elif name == "chunked_min":            # one past the one-workgroup path: 5 chunks, the last of 1
-        T, Kp, Ep = 683, 3, 513
+    elif name == "chunked_min":            # one past the one-workgroup path: 11 chunks, the last of 1
+        T, Kp, Ep = 1707, 3, 513
         ids = torch.randint(0, Ep, (T, Kp), generator=torch.Generator().manual_seed(11),
                             dtype=torch.int32)
     elif name in ("big_a", "chunks19"):    # many chunks, random ids, a ragged last chunk
