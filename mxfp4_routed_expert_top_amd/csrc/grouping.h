@@ -38,15 +38,32 @@ __device__ __forceinline__ void wave_match_rank(int e, int nbits, int* rank, int
 // Bits of an expert index below Ep.
 __device__ __forceinline__ int expert_bits(int Ep) { return Ep <= 1 ? 0 : 32 - __clz(Ep - 1); }
 
+// x plus the value DPP control CTRL moves into this lane (0 where it moves
+// none: rows outside ROWMASK, or a row shift's first lanes)
+template <int CTRL, int ROWMASK>
+__device__ __forceinline__ int dpp_add(int x) {
+  return x + __builtin_amdgcn_update_dpp(0, x, CTRL, ROWMASK, 0xF, false);
+}
+
+// Inclusive sum over the lanes of a wave, lane order, all in DPP lane moves
+// (no LDS round trips, where a __shfl_up step is an LDS permute and a wait):
+// shifts by 1, 2, 4 and 8 inside each 16-lane row, then row 0's total into
+// row 1 and row 2's into row 3 (row_bcast:15), then lane 31's into rows 2
+// and 3 (row_bcast:31).
+__device__ __forceinline__ int wave_inclusive_scan(int x) {
+  x = dpp_add<0x111, 0xF>(x);                         // row_shr:1
+  x = dpp_add<0x112, 0xF>(x);                         // row_shr:2
+  x = dpp_add<0x114, 0xF>(x);                         // row_shr:4
+  x = dpp_add<0x118, 0xF>(x);                         // row_shr:8
+  x = dpp_add<0x142, 0xA>(x);                         // row_bcast:15 into rows 1, 3
+  x = dpp_add<0x143, 0xC>(x);                         // row_bcast:31 into rows 2, 3
+  return x;
+}
+
 // Exclusive scan of one value per thread over a 1024-thread block.
 __device__ __forceinline__ int block_exclusive_scan(int v, int* tmp /* >= 17 ints */, int* total) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  int x = v;
-#pragma unroll
-  for (int d = 1; d < 64; d <<= 1) {
-    int y = __shfl_up(x, d, MOE_WAVE);
-    if (lane >= d) x += y;
-  }
+  const int x = wave_inclusive_scan(v);
   if (lane == 63) tmp[wave] = x;
   __syncthreads();
   if (threadIdx.x == 0) {
@@ -257,16 +274,7 @@ __device__ __forceinline__ void group_small(Ids&& ids, int A, int Ep, int tile_m
 constexpr int kWaveMaxA = 64;
 constexpr int kWaveEPL = 17;                          // Ep <= 64 * 17
 
-__device__ __forceinline__ int wave_exclusive_scan(int v) {
-  const int lane = threadIdx.x & 63;
-  int x = v;
-#pragma unroll
-  for (int d = 1; d < 64; d <<= 1) {
-    const int y = __shfl_up(x, d, MOE_WAVE);
-    if (lane >= d) x += y;
-  }
-  return x - v;
-}
+__device__ __forceinline__ int wave_exclusive_scan(int v) { return wave_inclusive_scan(v) - v; }
 
 template <class Ids>
 __device__ __forceinline__ void group_wave(Ids&& ids, int A, int Ep, int tile_m,
