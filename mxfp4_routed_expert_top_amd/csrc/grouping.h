@@ -113,7 +113,7 @@ __device__ __forceinline__ void group_offsets(Cnt&& cnt_of, int A, int Ep, int t
   int ttotal;
   const int tbase = block_exclusive_scan(nt[0] + nt[1], tmp, &ttotal);
   const int toff[2] = {tbase, tbase + nt[0]};
-  const int max_tiles = (A + tile_m - 1) / tile_m + Ep;
+  [[maybe_unused]] const int max_tiles = (A + tile_m - 1) / tile_m + Ep;
   for (int q = 0; q < 2; ++q) {
     const int e = 2 * threadIdx.x + q;
     if (e < Ep) {
@@ -303,7 +303,7 @@ __device__ __forceinline__ void group_wave(Ids&& ids, int A, int Ep, int tile_m,
     }
     int off = wave_exclusive_scan(sum), toff = wave_exclusive_scan(tsum);
     const int ntiles = __builtin_amdgcn_readlane(toff + tsum, 63);
-    const int max_tiles = (A + tile_m - 1) / tile_m + Ep;
+    [[maybe_unused]] const int max_tiles = (A + tile_m - 1) / tile_m + Ep;
 #pragma unroll
     for (int j = 0; j < kWaveEPL; ++j) {
       const int x = e0 + j;
