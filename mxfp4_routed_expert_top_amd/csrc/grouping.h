@@ -167,10 +167,10 @@ constexpr int kGroupMaxA = kGroupRounds * kGroupThreads;
 // The whole grouping in one workgroup of kGroupThreads threads, A <=
 // kGroupMaxA.  ids(a) is the expert of assignment a (ids outside [0, Ep)
 // take no part).  kEarly: the ids are read on entry, so their loads overlap
-// the clearing of the count table (ids in global memory); otherwise after the barrier that follows the
-// clearing, which then also publishes ids that other threads of the
-// workgroup have just written (the fused routing's LDS).  sh holds
-// group_small_lds_bytes(Ep) bytes of LDS, tmp >= 17 ints.
+// the clearing of the count table (ids in global memory); otherwise after
+// the barrier that follows the clearing, which then also publishes ids that
+// other threads of the workgroup have just written (the fused routing's
+// LDS).  sh holds group_small_lds_bytes(Ep) bytes of LDS, tmp >= 17 ints.
 //
 // The scatter goes in rounds of 1024 assignments, one per thread.  A
 // thread's position is its expert's running offset, plus the count of that

@@ -9,11 +9,12 @@
 // Wave w of the 16 routes tokens w and w + 16 (NT of them, their dependency
 // chains interleaved); after one barrier all 1024 threads group the T*K'
 // assignments.  The smallest batches (at most 64 assignments) take a
-// workgroup of one wave per token instead, whose first wave groups them.  Used up to 128 / NPL tokens (32 at E <= 256, 16 at E <= 512,
-// 8 at E <= 1024): there the one launch took 10-16 us against 16.5-18.5 us
-// for the two.  Beyond, the routing of many tokens on one CU's four SIMDs
-// (about 35 wave instructions per token and slot) costs more than the
-// second launch, and the per-token route kernel spread over the chip wins.
+// workgroup of one wave per token instead, whose first wave groups them.
+// Used up to 128 / NPL tokens (32 at E <= 256, 16 at E <= 512, 8 at
+// E <= 1024): there the one launch took 10-16 us against 16.5-18.5 us for
+// the two.  Beyond, the routing of many tokens on one CU's four SIMDs (about
+// 35 wave instructions per token and slot) costs more than the second
+// launch, and the per-token route kernel spread over the chip wins.
 #include "common.h"
 #include "kernels.h"
 
