@@ -219,6 +219,21 @@ def test_align_sort(name):
     _check_align(got, moe.align(ids.numpy(), Ep, 32))
 
 
+@pytest.mark.parametrize("Ep", [1, 2, 3, 1024, 2048])
+@pytest.mark.parametrize("T,Kp", [(37, 5), (700, 9)])
+def test_align_sort_expert_counts(Ep, T, Kp):
+    """The grouping at the edges of the expert index's bit count (a lane's
+    rank among its wave's equal experts is built bit by bit): one expert
+    (no bits), two, three, a power of two and the largest count (eleven
+    bits), on the one-workgroup path (185 assignments) and the chunked one
+    (6,300), bit-exact against the oracle."""
+    _say("align experts", Ep, "T", T, "Kp", Kp)
+    ids = torch.randint(0, Ep, (T, Kp), generator=torch.Generator().manual_seed(Ep + T),
+                        dtype=torch.int32)
+    got = ops().align_sort(ids.to(DEV), Ep, tile_m=32)
+    _check_align(got, moe.align(ids.numpy(), Ep, 32))
+
+
 @pytest.mark.parametrize("name", ["prefill", "prefill_skewed", "w4a4", "prefill_mxfp8"])
 def test_align_sort_with_the_forwards_tile_size(name):
     """The grouping tables at full size with the tile rows the forward picks
