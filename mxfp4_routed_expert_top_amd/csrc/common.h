@@ -237,11 +237,8 @@ __device__ __forceinline__ u32x4_t bload16(rsrc_t r, uint32_t voff, uint32_t sof
 // through the caches rather than kept for reuse), for weight codes read once:
 // an expert's only tile.  Streaming the decode step's expert weights this way
 // raised its GEMMs from ~6.1 to ~6.8 TB/s; where other tiles of the expert
-// re-read the weights from L2 it costs 7-26% instead.  The policy also sets
-// SC0 (a wider coherence scope, harmless for read-only weights): decode down
-// 133.1-134.1 -> 131.8-132.5 us and gate/up ~1 us lower (kernel trace, runs
-// alternated on one GPU); SC1 or both scope bits measured no better.
-constexpr int kCacheNT = 2 | 1;
+// re-read the weights from L2 it costs 7-26% instead.
+constexpr int kCacheNT = 2;
 
 __device__ __forceinline__ u32x4_t bload16_nt(rsrc_t r, uint32_t voff, uint32_t soff) {
   return __builtin_bit_cast(u32x4_t,
